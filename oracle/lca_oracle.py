@@ -1,0 +1,419 @@
+"""Plain float64 CPU oracle of the CSA/HCA attention path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the library imports this module; only
+the tests, the package smoke check and the benchmark's CPU-baseline leg use it.
+It shares no code with the HIP path: every decoder, rounding rule and step of
+the method below is written here, from the pages' descriptions, in float64.
+
+Sources (all pages discuss the DeepSeek-V4 report):
+  [XT]  "[DeepSeek-5] DeepSeek-V4 Technical Report: Hybrid Attention and
+        Post-Training for Million-Token Contexts" (xutianle.me), sections
+        "3. CSA", "4. HCA", "5. From MLA to CSA/HCA".
+  [QB]  QbitAI article on DeepSeek-V4 (m.admirer.cn), section
+        "混合注意力机制" (hybrid attention mechanism).
+  [PT]  "DeepSeek V4 Architecture Tricks" (pinktalk.online), sections
+        "CSA: Compressed Sparse Attention", "HCA: Heavily Compressed
+        Attention", "压缩 KV 的具体 trick" (compressed-KV tricks),
+        "Sliding Window Branch", "Partial RoPE 和 Attention Sink",
+        "FP4 / FP8 Quantization-Aware Training", "Heterogeneous KV Cache Layout".
+
+Readings where the pages are silent (each also listed in the design notes):
+  * gate softmax is per channel over the candidate window; bias row i goes with
+    the i-th candidate in time order; a CSA entry with no previous block masks
+    the missing candidates;
+  * entry s is visible to a query at position t iff its last token
+    (s+1)*m - 1 <= t;
+  * the window is the query's own token and the n_win-1 before it; the window
+    KV of token j is RMSNorm(C[j]) stored in the KV format;
+  * RMSNorm has unit gain and eps = 1e-6; softmax scale 1/sqrt(c);
+  * indexer score I[t,s] = sum_h w[t,h] * relu(q_I[t,h] . k_I[s]);
+  * top-k keeps the min(k, visible) largest scores, ties to the lower index,
+    -0 counted as +0, NaN counted as -inf, output ascending, padded with -1;
+  * the two branches form one softmax, merged by log-sum-exp; an optional
+    per-head sink logit joins the denominator only.
+"""
+from collections import deque
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# exact decoders of the stored formats
+
+
+def decode_bf16(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64, exact (bf16 is the top half of fp32)."""
+    b = np.asarray(bits).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+def _e4m3_table() -> np.ndarray:
+    """All 256 OCP fp8 e4m3fn values: 1 sign, 4 exponent (bias 7), 3 mantissa bits;
+    exponent 0 is subnormal; S.1111.111 is NaN; no infinities."""
+    t = np.empty(256, np.float64)
+    for v in range(256):
+        s = -1.0 if v & 0x80 else 1.0
+        e = (v >> 3) & 0xF
+        f = v & 0x7
+        if e == 0xF and f == 0x7:
+            t[v] = np.nan
+        elif e == 0:
+            t[v] = s * (f / 8.0) * 2.0 ** -6
+        else:
+            t[v] = s * (1.0 + f / 8.0) * 2.0 ** (e - 7)
+    return t
+
+
+E4M3 = _e4m3_table()
+# e2m1 (fp4): 1 sign, 2 exponent (bias 1), 1 mantissa bit; exponent 0 subnormal.
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+                 -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0])
+
+
+def decode_e4m3(bits) -> np.ndarray:
+    return E4M3[np.asarray(bits, dtype=np.uint8)]
+
+
+def decode_mxfp4(packed, scales, block: int = 32) -> np.ndarray:
+    """OCP MXFP4: two e2m1 codes per byte (element 2i in the low nibble), one E8M0
+    scale byte 2^(e-127) per `block` elements along the last dim."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    lo = E2M1[packed & 0xF]
+    hi = E2M1[packed >> 4]
+    x = np.stack([lo, hi], -1).reshape(*packed.shape[:-1], packed.shape[-1] * 2)
+    sc = np.exp2(np.asarray(scales, dtype=np.float64) - 127.0)
+    return (x.reshape(*x.shape[:-1], -1, block) * sc[..., None]).reshape(x.shape)
+
+
+def decode(arr, fmt: str, scales=None) -> np.ndarray:
+    """Stored rows -> float64.  fmt: f32 | bf16 | fp8 | fp8_bf16rope | mxfp4."""
+    if fmt == "f32":
+        return np.asarray(arr, dtype=np.float32).astype(np.float64)
+    if fmt == "bf16":
+        return decode_bf16(arr)
+    if fmt == "fp8":
+        return decode_e4m3(arr)
+    if fmt == "mxfp4":
+        return decode_mxfp4(arr, scales)
+    if fmt == "fp8_bf16rope":
+        a = np.asarray(arr, dtype=np.uint8)
+        nope = a.shape[-1] - 128          # 64 bf16 rope dims take the last 128 bytes
+        lo = decode_e4m3(a[..., :nope])
+        hi = decode_bf16(np.ascontiguousarray(a[..., nope:]).view(np.uint16))
+        return np.concatenate([lo, hi], -1)
+    raise ValueError(fmt)
+
+
+# ---------------------------------------------------------------------------
+# rounding to a stored format (round to nearest, ties to even)
+
+
+def _round_binary(x, mbits: int, emin: int, maxval: float, saturate: bool) -> np.ndarray:
+    """Round to the binary format with `mbits` fraction bits, smallest normal exponent
+    `emin` (gradual underflow below it) and largest finite value `maxval`."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, E = np.frexp(a)                       # a = f * 2^E, f in [0.5, 1)
+    e = np.maximum(E - 1, emin)              # exponent of the leading bit, clamped
+    ulp = np.exp2(e - mbits)
+    r = np.round(a / ulp) * ulp              # np.round: half to even; a/ulp is exact
+    if saturate:
+        r = np.minimum(r, maxval)
+    else:
+        r = np.where(r > maxval, np.inf, r)
+    r = np.where(np.isnan(a), np.nan, r)
+    return np.copysign(r, x)
+
+
+def round_to(x, fmt: str, rope_dims: int = 64) -> np.ndarray:
+    """Value of x after the storage cast to `fmt` (as float64)."""
+    if fmt == "f32":
+        return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    if fmt == "bf16":
+        return _round_binary(x, 7, -126, float.fromhex("0x1.fep127"), saturate=False)
+    if fmt == "fp8":
+        return _round_binary(x, 3, -6, 448.0, saturate=True)
+    if fmt == "fp8_bf16rope":
+        x = np.asarray(x, dtype=np.float64)
+        c = x.shape[-1]
+        return np.concatenate([round_to(x[..., : c - rope_dims], "fp8"),
+                               round_to(x[..., c - rope_dims:], "bf16")], -1)
+    raise ValueError(fmt)
+
+
+# ---------------------------------------------------------------------------
+# the method
+
+
+def rmsnorm(x, eps: float = 1e-6) -> np.ndarray:
+    """Unit-gain RMSNorm over the last dim; [QB] applies it to queries and KV
+    entries before core attention."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def gate_softmax(logits) -> np.ndarray:
+    """Softmax over axis 1 (the candidate axis), independently per channel."""
+    mx = np.max(logits, axis=1, keepdims=True)
+    e = np.exp(logits - mx)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def compress(C, Z, P, m: int, overlap: bool, prevC=None, prevZ=None) -> np.ndarray:
+    """Softmax-gated pooling of every m tokens into one entry ([PT] compressed-KV
+    tricks; [XT] 3/4; [QB]).
+
+    C, Z: [n, c] KV candidates and gate logits of n = nb*m consecutive tokens that
+    start on a block boundary.  P: positional bias, one row per candidate slot.
+    overlap=True (CSA): entry s pools the 2m tokens of blocks s-1 and s, with
+    candidate slot i in time order taking bias row i; block -1 of the first entry
+    is prevC/prevZ, or masked out when those are None.  overlap=False (HCA): entry
+    s pools its own m tokens.  Returns the pooled, un-normalised entries [nb, c].
+    """
+    C = np.asarray(C, np.float64)
+    Z = np.asarray(Z, np.float64)
+    P = np.asarray(P, np.float64)
+    n, c = C.shape
+    assert n % m == 0
+    nb = n // m
+    Cb = C.reshape(nb, m, c)
+    Zb = Z.reshape(nb, m, c)
+    if overlap:
+        if prevC is None:
+            pC = np.zeros((1, m, c))
+            pZ = np.zeros((1, m, c))
+        else:
+            pC = np.asarray(prevC, np.float64)[None]
+            pZ = np.asarray(prevZ, np.float64)[None]
+        cand = np.concatenate([np.concatenate([pC, Cb[:-1]], 0), Cb], 1)       # [nb, 2m, c]
+        logits = np.concatenate([np.concatenate([pZ, Zb[:-1]], 0), Zb], 1) + P[None, :2 * m]
+        if prevC is None:
+            logits[0, :m] = -np.inf
+    else:
+        cand = Cb
+        logits = Zb + P[None, :m]
+    return (gate_softmax(logits) * cand).sum(axis=1)
+
+
+def visible(q_pos, m: int, n_entries) -> np.ndarray:
+    """Number of entries visible at position t: entry s needs (s+1)*m-1 <= t."""
+    return np.minimum((np.asarray(q_pos, np.int64) + 1) // m, n_entries)
+
+
+def index_scores(qI, kI, w, vis) -> np.ndarray:
+    """Lightning-indexer scores ([QB]: inherited from V3.2's DSA; [PT] CSA section):
+    I[t,s] = sum_h w[t,h] * max(0, qI[t,h] . kI[s]) for s < vis[t], else -inf.
+
+    qI [nq, H_I, d_I], kI [N, d_I] (one key per entry, shared by the heads),
+    w [nq, H_I]."""
+    qI = np.asarray(qI, np.float64)
+    kI = np.asarray(kI, np.float64)
+    dots = np.einsum("thd,sd->ths", qI, kI)
+    I = np.einsum("th,ths->ts", np.asarray(w, np.float64), np.maximum(dots, 0.0))
+    cols = np.arange(kI.shape[0])[None, :]
+    return np.where(cols < np.asarray(vis)[:, None], I, -np.inf)
+
+
+def score_error_bound(qI, kI, w, d_terms: int = 0) -> np.ndarray:
+    """Bound on |I_fp32 - I_exact| for any fp32 evaluation order: the standard
+    gamma_n = n*u/(1-n*u) (u = 2^-24) summation bound with n = d_I + H_I + 2,
+    applied to sum_h w_h sum_d |q_hd k_d|."""
+    qI = np.abs(np.asarray(qI, np.float64))
+    kI = np.abs(np.asarray(kI, np.float64))
+    n = qI.shape[-1] + qI.shape[-2] + 2 + d_terms
+    u = 2.0 ** -24
+    gamma = n * u / (1 - n * u)
+    return gamma * np.einsum("th,thd,sd->ts", np.asarray(w, np.float64), qI, kI)
+
+
+def _select_key(s) -> np.ndarray:
+    s = np.asarray(s, np.float64)
+    s = np.where(np.isnan(s), -np.inf, s)
+    return s + 0.0                       # -0.0 + 0.0 == +0.0
+
+
+def topk(scores, vis, k: int) -> np.ndarray:
+    """Top-k selection ([PT] CSA section: k=1024; [QB]): for each row, the indices of
+    the min(k, vis) largest of scores[:vis], larger score first and lower index
+    first among equal scores, returned in ascending index order, padded with -1."""
+    scores = np.atleast_2d(scores)
+    out = np.full((scores.shape[0], k), -1, np.int32)
+    for r in range(scores.shape[0]):
+        v = int(vis[r])
+        key = _select_key(scores[r, :v])
+        order = np.lexsort((np.arange(v), -key))          # primary: -key, then index
+        sel = np.sort(order[: min(k, v)])
+        out[r, : sel.size] = sel
+    return out
+
+
+def attend(qhat, rows, tau: float):
+    """Softmax attention of H query heads over R rows that are both key and value
+    (MQA, [QB]).  Returns (o [H, c], lse [H]); no rows gives lse = -inf, o = 0."""
+    qhat = np.asarray(qhat, np.float64)
+    rows = np.asarray(rows, np.float64)
+    H, c = qhat.shape
+    if rows.shape[0] == 0:
+        return np.zeros((H, c)), np.full(H, -np.inf)
+    logits = tau * (qhat @ rows.T)
+    mx = logits.max(axis=1, keepdims=True)
+    p = np.exp(logits - mx)
+    l = p.sum(axis=1, keepdims=True)
+    return (p @ rows) / l, (mx + np.log(l))[:, 0]
+
+
+def merge(parts, sink=None):
+    """Log-sum-exp merge of branch partials (o_i, lse_i) into one softmax over the
+    union of their rows; an optional per-head sink logit only enlarges the
+    denominator ([QB] attention sink)."""
+    lses = np.stack([p[1] for p in parts])                  # [n_parts, H]
+    if sink is not None:
+        lses_all = np.concatenate([lses, np.asarray(sink, np.float64)[None]])
+    else:
+        lses_all = lses
+    mx = np.max(lses_all, axis=0)
+    mx = np.where(np.isfinite(mx), mx, 0.0)
+    tot = mx + np.log(np.exp(lses_all - mx).sum(axis=0))
+    o = sum(np.exp(lse - tot)[:, None] * o_i for o_i, lse in parts)
+    return o, tot
+
+
+def window_positions(t: int, n_win: int) -> np.ndarray:
+    """The query's own position and the n_win-1 before it ([PT] Sliding Window
+    Branch, n_win = 128), clipped at 0."""
+    return np.arange(max(0, t - n_win + 1), t + 1)
+
+
+# ---------------------------------------------------------------------------
+# a whole layer: prefill of new tokens after an optional prefix
+
+
+def prefill_layer(*, mode, m, k, n_win, tau, eps, kv_fmt, out_fmt, pos0,
+                  C, Z, P, q, cache_prefix, prevC=None, prevZ=None, win_prefix=None,
+                  qI=None, kI=None, w=None, queries=None, sink=None):
+    """One sequence of CSA ("csa") or HCA ("hca") prefill.
+
+    New tokens occupy positions pos0 .. pos0+n-1 (pos0 % m == 0).  cache_prefix
+    [pos0/m, c] holds the stored entries of the prefix, win_prefix the stored
+    window KV of the n_win-1 prefix positions before pos0.  `queries` selects which
+    new tokens to evaluate (default all).  Returns a dict of float64 results.
+    """
+    C = np.asarray(C, np.float64)
+    n, c = C.shape
+    E = compress(C, Z, P, m, overlap=(mode == "csa"), prevC=prevC, prevZ=prevZ)
+    entries_new = round_to(rmsnorm(E, eps), kv_fmt)
+    Khat = np.concatenate([np.asarray(cache_prefix, np.float64).reshape(-1, c), entries_new], 0)
+    U_new = round_to(rmsnorm(C, eps), kv_fmt)
+    n_pre_win = 0 if win_prefix is None else len(win_prefix)
+    U = U_new if win_prefix is None else np.concatenate([np.asarray(win_prefix, np.float64), U_new], 0)
+    win_origin = pos0 - n_pre_win
+    qhat = rmsnorm(np.asarray(q, np.float64), eps)             # [n, H, c], per head
+    queries = np.arange(n) if queries is None else np.asarray(queries)
+    H = qhat.shape[1]
+    res = {"entries": entries_new, "out": np.zeros((len(queries), H, c)),
+           "lse": np.zeros((len(queries), H)), "idx": None, "scores": None}
+    if mode == "csa":
+        res["idx"] = np.full((len(queries), k), -1, np.int32)
+        res["scores"] = []
+    for r, i in enumerate(queries):
+        t = pos0 + int(i)
+        vis = int(visible([t], m, len(Khat))[0])
+        if mode == "csa":
+            I = index_scores(np.asarray(qI, np.float64)[i][None], kI[:vis], np.asarray(w)[i][None],
+                             [vis])
+            sel = topk(I, [vis], k)[0]
+            res["idx"][r] = sel
+            res["scores"].append(I[0])
+            S = sel[sel >= 0]
+        else:
+            S = np.arange(vis)
+        W = window_positions(t, n_win) - win_origin
+        assert W.min() >= 0, "window reaches before the provided window KV"
+        part_c = attend(qhat[i], Khat[S], tau)
+        part_w = attend(qhat[i], U[W], tau)
+        o, lse = merge([part_c, part_w], sink)
+        res["out"][r] = round_to(o, out_fmt)
+        res["lse"][r] = lse
+    return res
+
+
+# ---------------------------------------------------------------------------
+# decode: state of uncompressed tokens, one token per step
+
+
+class DecodeState:
+    """Per-sequence decode state ([PT] Heterogeneous KV Cache Layout: a state cache
+    holds the window KV and the tail tokens of the block not yet compressed; the
+    classical cache holds compressed entries).
+
+    L: tokens seen.  cur: (C, Z) rows of the incomplete block (L % m rows).
+    prev: (C, Z) rows of the last complete block (CSA overlap) or None.
+    window: the stored window KV of the last n_win-1 or fewer tokens.
+    entries: stored compressed entries, [N, c].
+    """
+
+    def __init__(self, *, mode, m, n_win, c, L=0, cur=None, prev=None, window=None, entries=None):
+        self.mode, self.m, self.n_win, self.c = mode, m, n_win, c
+        self.L = L
+        self.cur = cur if cur is not None else (np.zeros((0, c)), np.zeros((0, c)))
+        self.prev = prev
+        self.window = deque(list(window) if window is not None else [], maxlen=n_win - 1 if n_win > 1 else 0)
+        self.entries = np.zeros((0, c)) if entries is None else np.asarray(entries, np.float64)
+
+
+def decode_step(st: DecodeState, *, tokC, tokZ, P, q, tau, eps, kv_fmt, out_fmt, k=0,
+                qI=None, kI=None, w=None, sink=None):
+    """Append one token and answer its query (the step of a decode loop).
+
+    The token goes to the incomplete block and its normalised KV to the window;
+    when its block completes, the block is compressed into a new entry (with the
+    previous block as overlap for CSA).  The query at the token's position then
+    attends top-k (CSA) or all (HCA) visible entries plus the window.
+    kI holds the indexer keys of all entries including a new one."""
+    m, c = st.m, st.c
+    t = st.L
+    tokC = np.asarray(tokC, np.float64).reshape(c)
+    tokZ = np.asarray(tokZ, np.float64).reshape(c)
+    curC = np.concatenate([st.cur[0], tokC[None]], 0)
+    curZ = np.concatenate([st.cur[1], tokZ[None]], 0)
+    u_t = round_to(rmsnorm(tokC, eps), kv_fmt)
+    win_rows = np.array(list(st.window) + [u_t]).reshape(-1, c)
+    new_entry = None
+    if (t + 1) % m == 0:
+        if st.mode == "csa":
+            pc, pz = (None, None) if st.prev is None else st.prev
+            E = compress(curC, curZ, P, m, True, pc, pz)
+        else:
+            E = compress(curC, curZ, P, m, False)
+        new_entry = round_to(rmsnorm(E, eps), kv_fmt)[0]
+        st.entries = np.concatenate([st.entries, new_entry[None]], 0)
+        st.prev = (curC, curZ)
+        st.cur = (np.zeros((0, c)), np.zeros((0, c)))
+    else:
+        st.cur = (curC, curZ)
+    if st.window.maxlen:
+        st.window.append(u_t)
+    st.L = t + 1
+    vis = int(visible([t], m, len(st.entries))[0])
+    qhat = rmsnorm(np.asarray(q, np.float64), eps)
+    res = {"new_entry": new_entry, "window_row": u_t, "idx": None, "scores": None}
+    if st.mode == "csa":
+        I = index_scores(np.asarray(qI, np.float64)[None], np.asarray(kI, np.float64)[:vis],
+                         np.asarray(w, np.float64)[None], [vis])
+        sel = topk(I, [vis], k)[0]
+        res["idx"], res["scores"] = sel, I[0]
+        S = sel[sel >= 0]
+    else:
+        S = np.arange(vis)
+    part_c = attend(qhat, st.entries[S], tau)
+    part_w = attend(qhat, win_rows, tau)
+    o, lse = merge([part_c, part_w], sink)
+    res["out"] = round_to(o, out_fmt)
+    res["out_exact"] = o
+    res["lse"] = lse
+    return res
+
+
+def gamma(n: int) -> float:
+    u = 2.0 ** -24
+    return n * u / (1 - n * u)

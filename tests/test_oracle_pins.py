@@ -1,0 +1,428 @@
+"""Pins of the float64 oracle against things other than itself: closed forms,
+library routines, brute force on tiny inputs and the invariants the method must
+satisfy.  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import brute
+from oracle import lca_oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------
+# stored formats
+
+
+def test_decode_bf16_matches_torch_all_patterns():
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = O.decode_bf16(bits)
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+
+
+def test_decode_e4m3_matches_torch_all_patterns():
+    bits = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(bits).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.decode_e4m3(bits)
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+    assert np.nanmax(got) == 448.0 and got[1] == 2.0 ** -9      # format limits
+
+
+def test_e2m1_table_from_format_definition():
+    # value = 2^(e-1) * (1 + f/2) for e > 0, f/2 for e = 0 (bias 1, 1 mantissa bit)
+    for code in range(16):
+        s, e, f = code >> 3, (code >> 1) & 3, code & 1
+        v = (2.0 ** (e - 1)) * (1 + f / 2) if e else f / 2
+        assert O.E2M1[code] == (-v if s else v)
+
+
+@pytest.mark.parametrize("fmt,tdt", [("bf16", torch.bfloat16), ("fp8", torch.float8_e4m3fn)])
+def test_round_to_matches_torch_cast(fmt, tdt):
+    r = rng(1)
+    x = np.concatenate([r.standard_normal(20000) * s for s in (1e-3, 1, 30, 300)]).astype(np.float32)
+    if fmt == "fp8":
+        # exact halfway points between neighbouring e4m3 values (ties to even)
+        vals = np.unique(np.abs(O.E4M3[np.isfinite(O.E4M3)]))
+        x = np.concatenate([x, ((vals[1:] + vals[:-1]) / 2).astype(np.float32)])
+        x = np.clip(x, -448, 448)
+    else:
+        # bf16 halfway points: fp32 patterns with exactly the 0x8000 low half
+        hb = (r.integers(0x3000, 0x4f00, 5000).astype(np.uint32) << 16) | 0x8000
+        x = np.concatenate([x, hb.view(np.float32)])
+    ref = torch.from_numpy(x).to(tdt).to(torch.float64).numpy()
+    assert np.array_equal(O.round_to(x.astype(np.float64), fmt), ref)
+
+
+def test_fp8_saturates():
+    assert O.round_to(np.array([1e6, -500.0]), "fp8").tolist() == [448.0, -448.0]
+
+
+def test_mxfp4_decode_closed_form():
+    # byte 0x21: low nibble code 1 (0.5), high nibble code 2 (1.0); scale 2^(130-127)=8
+    packed = np.full((1, 16), 0x21, np.uint8)
+    scales = np.array([[130]], np.uint8)
+    x = O.decode_mxfp4(packed, scales)
+    assert x.shape == (1, 32)
+    assert np.all(x[0, 0::2] == 4.0) and np.all(x[0, 1::2] == 8.0)
+
+
+def test_mxfp4_generator_roundtrip():
+    from synth import encode as enc
+    r = rng(2)
+    x = r.standard_normal((64, 128))
+    p, s = enc.to_mxfp4(x)
+    y = O.decode_mxfp4(p, s)
+    # error per element <= half an e2m1 step at the block scale, i.e. amax/8 ... /4
+    blk = np.abs(x.reshape(64, 4, 32)).max(-1)
+    err = np.abs(y - x).reshape(64, 4, 32).max(-1)
+    assert np.all(err <= blk / 4 + 1e-12)
+    # exactly representable inputs come back exactly
+    z = O.E2M1[r.integers(0, 16, (8, 64))] * 0.25
+    z[:, ::32] = 1.5                       # amax 1.5 in every block -> scale 2^-2
+    p, s = enc.to_mxfp4(z)
+    assert np.array_equal(O.decode_mxfp4(p, s), z)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm and the compressor
+
+
+def test_rmsnorm_closed_form():
+    x = rng(3).standard_normal((10, 64)) * 3
+    y = O.rmsnorm(x, 1e-6)
+    ms = np.mean(x * x, -1)
+    assert np.allclose(np.sqrt(np.mean(y * y, -1)), np.sqrt(ms / (ms + 1e-6)), rtol=1e-14)
+    assert np.allclose(y / x, (1 / np.sqrt(ms + 1e-6))[:, None])
+
+
+def test_compress_hand_example():
+    # HCA, m=4, c=1: zero gates, bias ln(1..4) -> weights 1:2:3:4, E = (1+4+9+16)/10 = 3
+    C = np.array([[1.0], [2.0], [3.0], [4.0]])
+    P = np.log(np.array([[1.0], [2.0], [3.0], [4.0]]))
+    assert np.isclose(O.compress(C, np.zeros_like(C), P, 4, False)[0, 0], 3.0, rtol=1e-15)
+    # CSA entry 1 pools blocks 0 and 1 (8 candidates), uniform gate -> mean of 1..8
+    C8 = np.arange(1.0, 9.0)[:, None]
+    E = O.compress(C8, np.zeros_like(C8), np.zeros((8, 1)), 4, True)
+    assert np.isclose(E[0, 0], 2.5) and np.isclose(E[1, 0], 4.5)
+
+
+@pytest.mark.parametrize("overlap,m", [(True, 4), (False, 4), (False, 128), (True, 2)])
+def test_compress_uniform_gate_is_block_mean(overlap, m):
+    r = rng(4)
+    n, c = 4 * m, 16
+    C = r.standard_normal((n, c))
+    const = r.standard_normal(c)
+    Z = np.tile(const, (n, 1))
+    P = np.zeros((2 * m if overlap else m, c))
+    E = O.compress(C, Z, P, m, overlap)
+    Cb = C.reshape(-1, m, c)
+    if overlap:
+        # entry 0 has no previous block: mean of its own m tokens; later: mean of 2m
+        want = np.concatenate([Cb[:1].mean(1), np.concatenate([Cb[:-1], Cb[1:]], 1).mean(1)], 0)
+    else:
+        want = Cb.mean(1)
+    assert np.allclose(E, want, rtol=1e-13, atol=1e-14)
+
+
+def test_compress_one_hot_and_shift_invariance():
+    r = rng(5)
+    m, c = 4, 8
+    C = r.standard_normal((3 * m, c))
+    Z = r.standard_normal((3 * m, c))
+    P = r.standard_normal((2 * m, c)) * 0.1
+    # one-hot: make candidate slot 5 (own block, token 1) dominate channel 3 of entry 2
+    Z2 = Z.copy()
+    Z2[2 * m + 1, 3] += 60.0
+    E = O.compress(C, Z2, P, m, True)
+    assert np.isclose(E[2, 3], C[2 * m + 1, 3], rtol=1e-12)
+    # adding a per-channel constant to all gate logits changes nothing
+    E0 = O.compress(C, Z, P, m, True)
+    E1 = O.compress(C, Z + r.standard_normal(c)[None], P, m, True)
+    assert np.allclose(E0, E1, rtol=1e-12, atol=1e-14)
+    # m=1 without overlap is the identity
+    assert np.allclose(O.compress(C, Z, P[:1], 1, False), C)
+
+
+def test_compress_matches_brute_force():
+    r = rng(6)
+    for overlap, m in [(True, 4), (False, 8)]:
+        n, c = 4 * m, 6
+        C, Z = r.standard_normal((n, c)), r.standard_normal((n, c))
+        P = r.standard_normal((2 * m if overlap else m, c)) * 0.1
+        pc, pz = r.standard_normal((m, c)), r.standard_normal((m, c))
+        E = O.compress(C, Z, P, m, overlap, pc if overlap else None, pz if overlap else None)
+        for s in range(n // m):
+            b = brute.compress_entry(C.tolist(), Z.tolist(), P.tolist(), m, s, overlap,
+                                     pc.tolist() if overlap else None, pz.tolist() if overlap else None)
+            assert np.allclose(E[s], b, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# indexer scores and top-k
+
+
+def test_index_scores_single_head_is_relu_matmul():
+    r = rng(7)
+    q = r.standard_normal((5, 1, 16))
+    k = r.standard_normal((40, 16))
+    I = O.index_scores(q, k, np.ones((5, 1)), np.full(5, 40))
+    assert np.allclose(I, np.maximum(q[:, 0] @ k.T, 0), rtol=1e-13, atol=1e-13)
+
+
+def test_index_scores_brute_force_and_mask():
+    r = rng(8)
+    q = r.standard_normal((3, 4, 8))
+    k = r.standard_normal((20, 8))
+    w = r.random((3, 4))
+    vis = np.array([0, 7, 20])
+    I = O.index_scores(q, k, w, vis)
+    for t in range(3):
+        for s in range(20):
+            if s < vis[t]:
+                assert np.isclose(I[t, s], brute.score(q[t].tolist(), k[s].tolist(), w[t].tolist()),
+                                  rtol=1e-12)
+            else:
+                assert I[t, s] == -np.inf
+
+
+def test_index_scores_zero_when_all_dots_negative():
+    q = -np.abs(rng(9).standard_normal((1, 3, 8)))
+    k = np.abs(rng(10).standard_normal((6, 8)))
+    assert np.all(O.index_scores(q, k, np.ones((1, 3)), [6]) == 0.0)
+
+
+def test_topk_matches_brute_force_with_ties():
+    r = rng(11)
+    for trial in range(30):
+        n = int(r.integers(1, 60))
+        s = r.integers(-3, 4, n).astype(np.float64)        # heavy ties
+        if trial % 3 == 0:
+            s[r.integers(0, n)] = -0.0
+        k = int(r.integers(1, 70))
+        got = O.topk(s[None], [n], k)[0]
+        assert got.tolist() == brute.select(list(s + 0.0), k)
+
+
+def test_topk_edge_cases():
+    s = np.array([[1.0, np.nan, -0.0, 0.0, 5.0, 5.0]])
+    # NaN counts as -inf; -0 equals +0 so index 2 wins the tie against 3
+    assert O.topk(s, [6], 3)[0].tolist() == [0, 4, 5]
+    assert O.topk(s, [6], 4)[0].tolist() == [0, 2, 4, 5]
+    assert O.topk(s, [6], 10)[0].tolist() == [0, 1, 2, 3, 4, 5, -1, -1, -1, -1]
+    assert O.topk(s, [0], 2)[0].tolist() == [-1, -1]
+    assert O.topk(s, [2], 1)[0].tolist() == [0]
+
+
+def test_topk_invariant_under_increasing_transform_and_scaling():
+    r = rng(12)
+    q = r.standard_normal((4, 4, 16))
+    k = r.standard_normal((300, 16))
+    w = r.random((4, 4))
+    vis = np.array([10, 100, 250, 300])
+    a = O.topk(O.index_scores(q, k, w, vis), vis, 32)
+    b = O.topk(O.index_scores(q * 3.7, k, w, vis), vis, 32)
+    c = O.topk(np.exp(O.index_scores(q, k, w, vis) / 50.0), vis, 32)
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+
+
+# ---------------------------------------------------------------------------
+# attention and merge
+
+
+def test_attention_constant_rows_and_single_row():
+    r = rng(13)
+    q = r.standard_normal((3, 8))
+    v = r.standard_normal(8)
+    o, lse = O.attend(q, np.tile(v, (5, 1)), 0.3)
+    assert np.allclose(o, v[None], rtol=1e-13)
+    assert np.allclose(lse, 0.3 * q @ v + np.log(5))
+    o1, _ = O.attend(q, v[None], 0.3)
+    assert np.allclose(o1, v[None])
+    oe, le = O.attend(q, np.zeros((0, 8)), 0.3)
+    assert np.all(le == -np.inf) and np.all(oe == 0)
+
+
+def test_merge_split_invariance_and_order():
+    r = rng(14)
+    q = r.standard_normal((4, 16))
+    rows = r.standard_normal((23, 16))
+    whole = O.attend(q, rows, 0.25)
+    for _ in range(5):
+        perm = r.permutation(23)
+        cuts = np.sort(r.choice(np.arange(1, 23), 3, replace=False))
+        parts = [O.attend(q, rows[p], 0.25) for p in np.split(perm, cuts)]
+        o, lse = O.merge(parts)
+        assert np.allclose(o, whole[0], rtol=1e-12, atol=1e-13)
+        assert np.allclose(lse, whole[1], rtol=1e-13)
+    # an empty part changes nothing
+    o, lse = O.merge([whole, O.attend(q, rows[:0], 0.25)])
+    assert np.allclose(o, whole[0]) and np.allclose(lse, whole[1])
+
+
+def test_merge_sink_closed_form():
+    r = rng(15)
+    q = r.standard_normal((2, 8))
+    rows = r.standard_normal((5, 8))
+    sink = np.array([0.5, -1.0])
+    o, lse = O.merge([O.attend(q, rows, 0.5)], sink)
+    o_ns, lse_ns = O.attend(q, rows, 0.5)
+    scale = np.exp(lse_ns) / (np.exp(lse_ns) + np.exp(sink))
+    assert np.allclose(o, o_ns * scale[:, None])
+    for h in range(2):
+        b = brute.attention(q[h].tolist(), rows.tolist(), 0.5, sink[h])
+        assert np.allclose(o[h], b, rtol=1e-12)
+
+
+def _tiny_layer_inputs(seed, n=48, c=16, H=2, HI=3, dI=8, m=4):
+    r = rng(seed)
+    return dict(C=r.standard_normal((n, c)), Z=r.standard_normal((n, c)),
+                P=r.standard_normal((2 * m, c)) * 0.1, q=r.standard_normal((n, H, c)),
+                qI=r.standard_normal((n, HI, dI)), kI=r.standard_normal((n // m, dI)),
+                w=r.random((n, HI)))
+
+
+@pytest.mark.parametrize("mode,m,k,n_win,kv", [("csa", 4, 5, 6, "f32"), ("csa", 4, 3, 1, "bf16"),
+                                               ("hca", 8, 0, 5, "fp8"), ("csa", 2, 4, 3, "fp8_bf16rope")])
+def test_layer_matches_brute_force(mode, m, k, n_win, kv):
+    c = 80 if kv == "fp8_bf16rope" else 16
+    d = _tiny_layer_inputs(20 + m + k, n=32, c=c, m=m)
+    tau = 1 / math.sqrt(c)
+    sink = np.array([0.3, -0.7])
+    res = O.prefill_layer(mode=mode, m=m, k=k, n_win=n_win, tau=tau, eps=1e-6, kv_fmt=kv,
+                          out_fmt="f32", pos0=0, C=d["C"], Z=d["Z"], P=d["P"][: 2 * m if mode == "csa" else m],
+                          q=d["q"], cache_prefix=np.zeros((0, c)), qI=d["qI"], kI=d["kI"], w=d["w"],
+                          sink=sink)
+    rk = (lambda row: O.round_to(np.array(row), kv).tolist())
+    outs, idxs, entries = brute.layer(mode=mode, m=m, k=k, n_win=n_win, tau=tau, eps=1e-6,
+                                      C=d["C"].tolist(), Z=d["Z"].tolist(),
+                                      P=d["P"][: 2 * m if mode == "csa" else m].tolist(),
+                                      q=d["q"].tolist(), qI=d["qI"].tolist(), kI=d["kI"].tolist(),
+                                      w=d["w"].tolist(), round_kv=rk, sink=sink.tolist())
+    assert np.allclose(res["entries"], entries, rtol=1e-12, atol=1e-12)
+    if mode == "csa":
+        assert np.array_equal(res["idx"], np.array(idxs))
+    assert np.allclose(res["out"], np.array(outs), rtol=1e-6, atol=1e-6)   # out rounded to f32
+
+
+def test_dense_limit_equals_sdpa():
+    """With k >= number of entries, CSA is dense attention over [entries; window]
+    under the causal masks; checked against torch's scaled_dot_product_attention."""
+    m, n, c, H, n_win = 4, 64, 16, 2, 5
+    d = _tiny_layer_inputs(30, n=n, c=c, H=H, m=m)
+    tau = 1 / math.sqrt(c)
+    res = O.prefill_layer(mode="csa", m=m, k=10 ** 6 // 10 ** 4, n_win=n_win, tau=tau, eps=1e-6,
+                          kv_fmt="f32", out_fmt="f32", pos0=0, C=d["C"], Z=d["Z"], P=d["P"], q=d["q"],
+                          cache_prefix=np.zeros((0, c)), qI=d["qI"], kI=d["kI"], w=d["w"])
+    K = np.concatenate([res["entries"], O.round_to(O.rmsnorm(d["C"]), "f32")], 0)   # [N + n, c]
+    N = n // m
+    t = np.arange(n)[:, None]
+    mask = np.concatenate([(np.arange(N)[None] + 1) * m - 1 <= t,
+                           (np.arange(n)[None] <= t) & (np.arange(n)[None] > t - n_win)], 1)
+    qh = torch.from_numpy(O.rmsnorm(d["q"]).transpose(1, 0, 2))              # [H, n, c]
+    kv = torch.from_numpy(K)[None].expand(H, -1, -1)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qh, kv, kv, attn_mask=torch.from_numpy(mask)[None], scale=tau).numpy().transpose(1, 0, 2)
+    assert np.allclose(res["out"], ref, rtol=1e-6, atol=1e-6)
+
+
+def test_empty_selection_is_pure_window():
+    # queries at t < m-1 see no entry: output is the window alone
+    m, c = 4, 16
+    d = _tiny_layer_inputs(31, n=16, c=c, m=m)
+    res = O.prefill_layer(mode="csa", m=m, k=2, n_win=3, tau=0.25, eps=1e-6, kv_fmt="f32",
+                          out_fmt="f32", pos0=0, C=d["C"], Z=d["Z"], P=d["P"], q=d["q"],
+                          cache_prefix=np.zeros((0, c)), qI=d["qI"], kI=d["kI"], w=d["w"],
+                          queries=[0, 1, 2])
+    U = O.round_to(O.rmsnorm(d["C"]), "f32")
+    for r, t in enumerate([0, 1, 2]):
+        assert np.all(res["idx"][r] == -1)
+        o, _ = O.attend(O.rmsnorm(d["q"][t]), U[max(0, t - 2): t + 1], 0.25)
+        assert np.allclose(res["out"][r], o, atol=1e-6)
+
+
+def test_causality_future_perturbation():
+    m, n, c = 4, 40, 16
+    d = _tiny_layer_inputs(32, n=n, c=c, m=m)
+    kw = dict(mode="csa", m=m, k=3, n_win=4, tau=0.25, eps=1e-6, kv_fmt="bf16", out_fmt="f32",
+              pos0=0, P=d["P"], cache_prefix=np.zeros((0, c)))
+    a = O.prefill_layer(C=d["C"], Z=d["Z"], q=d["q"], qI=d["qI"], kI=d["kI"], w=d["w"], **kw)
+    cut = 21                                     # perturb tokens > cut (and their entries)
+    e = {key: v.copy() for key, v in d.items()}
+    r = rng(33)
+    e["C"][cut + 1:] += r.standard_normal(e["C"][cut + 1:].shape)
+    e["Z"][cut + 1:] += 5
+    e["q"][cut + 1:] *= -1
+    e["qI"][cut + 1:] += 1
+    e["kI"][(cut + 1) // m:] += r.standard_normal(e["kI"][(cut + 1) // m:].shape)
+    b = O.prefill_layer(C=e["C"], Z=e["Z"], q=e["q"], qI=e["qI"], kI=e["kI"], w=e["w"], **kw)
+    assert np.array_equal(a["out"][: cut + 1], b["out"][: cut + 1])
+    assert np.array_equal(a["idx"][: cut + 1], b["idx"][: cut + 1])
+
+
+# ---------------------------------------------------------------------------
+# decode: incremental steps reproduce the prefill
+
+
+@pytest.mark.parametrize("mode,m", [("csa", 4), ("hca", 8)])
+def test_incremental_decode_equals_prefill(mode, m):
+    n, c, H = 40, 16, 2
+    d = _tiny_layer_inputs(40 + m, n=n, c=c, H=H, m=m)
+    P = d["P"][: 2 * m if mode == "csa" else m]
+    kw = dict(tau=0.25, eps=1e-6, kv_fmt="bf16", out_fmt="f32")
+    pre = O.prefill_layer(mode=mode, m=m, k=3, n_win=5, pos0=0, C=d["C"], Z=d["Z"], P=P, q=d["q"],
+                          cache_prefix=np.zeros((0, c)), qI=d["qI"], kI=d["kI"], w=d["w"], **kw)
+    st = O.DecodeState(mode=mode, m=m, n_win=5, c=c)
+    for t in range(n):
+        r = O.decode_step(st, tokC=d["C"][t], tokZ=d["Z"][t], P=P, q=d["q"][t], k=3,
+                          qI=d["qI"][t], kI=d["kI"], w=d["w"][t], **kw)
+        assert np.array_equal(r["out"], pre["out"][t])
+        if mode == "csa":
+            assert np.array_equal(r["idx"], pre["idx"][t])
+    assert np.array_equal(st.entries, pre["entries"])
+
+
+# ---------------------------------------------------------------------------
+# score error bound and the pages' hyperparameters
+
+
+def test_score_error_bound_covers_fp32_evaluation():
+    r = rng(50)
+    q = r.standard_normal((3, 64, 128))
+    k = r.standard_normal((200, 128))
+    w = r.random((3, 64))
+    exact = O.index_scores(q, k, w, np.full(3, 200))
+    q32, k32, w32 = (torch.from_numpy(a.astype(np.float32)) for a in (q, k, w))
+    dots = torch.einsum("thd,sd->ths", q32, k32)
+    f32 = torch.einsum("th,ths->ts", w32, torch.relu(dots)).double().numpy()
+    q32d, k32d = q32.double().numpy(), k32.double().numpy()
+    bound = O.score_error_bound(q32d, k32d, w32.double().numpy())
+    exact32 = O.index_scores(q32d, k32d, w32.double().numpy(), np.full(3, 200))
+    assert np.all(np.abs(f32 - exact32) <= bound)
+    assert np.all(bound < 1e-3 * np.abs(exact).max())
+
+
+def test_pages_hyperparameters():
+    from synth.configs import CSA_DECODE_1M, HCA_DECODE, HYBRID_DECODE_1M
+    g = json.load(open(os.path.join(GOLD, "hyperparams.json")))
+    cfg = CSA_DECODE_1M
+    assert cfg.m == g["csa_rate_m"]["value"] and cfg.k == g["csa_topk"]["value"]
+    assert cfg.H_I == g["indexer_heads"]["value"] and cfg.d_I == g["indexer_head_dim"]["value"]
+    assert cfg.n_win == g["window_n_win"]["value"] and cfg.c == g["head_dim_c"]["value"]
+    assert HCA_DECODE.m == g["hca_rate_m_prime"]["value"] == HYBRID_DECODE_1M.m_hca
+    assert HYBRID_DECODE_1M.rope_dims == g["rope_dims"]["value"]
+    assert cfg.ctx == g["context_tokens"]["value"]
+    assert np.lcm(cfg.m, HCA_DECODE.m) == g["cache_block_tokens_lcm"]["value"]
+    assert cfg.k == g["entries_attended_at_1m"]["value"]
+    assert int(O.visible([cfg.ctx - 1], cfg.m, 10 ** 9)[0]) == 262144
