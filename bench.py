@@ -1,0 +1,174 @@
+"""Benchmark: CSA decode at 1M context on one MI355X.
+
+Workload: CSA decode step, batch 16 sequences of 2^20 + T_b tokens (m = 4 ->
+262144 compressed entries each), fp8 indexer keys (64 heads x 128), top-1024,
+multi-query attention over the selected bf16 entries (64 heads x 512) plus a
+128-token window, bf16 in / fp32 accumulate.  One step = one decode token per
+sequence through every stage of the path: state append (window KV, tail
+block, compression of a block the token completes), indexer scores, top-k,
+sparse attention with the window branch and the log-sum-exp merge.  Steps run
+back to back, so the state advances (blocks complete every 4 steps).
+
+Prints ONE JSON line.  Per-stage times come from HIP events recorded on the
+stream the kernels run on, over the timed region itself.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU time budget of the oracle baseline sample")
+    ap.add_argument("--detail", default=None, help="write per-stage timings (JSON) to this file")
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg, d, budget_s):
+    """The float64 oracle (as is) on a bounded sample: whole decode steps of the
+    first sequences of the same batch, until about budget_s of CPU time."""
+    import numpy as np
+    from oracle.workloads import oracle_decode
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    done, t0 = 0, time.perf_counter()
+    while done < cfg.B:
+        oracle_decode(cfg, d, done)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "query-tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {cfg.B} sequences, one full decode step each "
+                      f"({el:.1f} s, float64 numpy)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
+              "multi-GPU path; batch sharding across GPUs is described in the design notes.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from long_context_attention_14_amd import ops, pipeline
+    from synth import gen
+    from synth.configs import CSA_DECODE_1M
+
+    cfg = CSA_DECODE_1M
+    dev = "cuda"
+    total_steps = args.warmup + args.steps
+    d = gen.decode_inputs(cfg, extra_entries=total_steps // cfg.m + 2)
+    layer = pipeline.DecodeLayer(cfg, d, dev)
+    B, m = cfg.B, cfg.m
+    q_pos = torch.empty(B, dtype=torch.int32, device=dev)
+    n_ent = torch.empty(B, dtype=torch.int32, device=dev)
+    scores = torch.empty((B, layer.N_cap), dtype=torch.float32, device=dev)
+    ws_topk = torch.empty(max(1, ops.lca_topk_workspace_size(B, 1, layer.N_cap, cfg.k)),
+                          dtype=torch.uint8, device=dev)
+    ws_mqa = torch.empty(max(1, ops.lca_sparse_mqa_workspace_size(
+        B, 1, cfg.H, cfg.c, cfg.kv_dtype, cfg.k, layer.N_cap, cfg.n_win, False)),
+        dtype=torch.uint8, device=dev)
+    stages = ["append", "indexer", "topk", "attention"]
+
+    def step(ev=None):
+        # the same library calls lca_decode_step makes, with events between stages
+        if ev:
+            ev[0].record()
+        ops.lca_state_append("csa", m, B, cfg.c, cfg.n_win, layer.tokC, layer.tokZ, cfg.io_dtype,
+                             layer.tailC, layer.tailZ, layer.ring, cfg.kv_dtype, layer.P,
+                             layer.cache, layer.N_cap, layer.n_tokens, q_pos, n_ent, cfg.eps)
+        if ev:
+            ev[1].record()
+        ops.lca_indexer_scores(B, 1, cfg.H_I, cfg.d_I, cfg.idx_dtype, layer.qI, None, layer.kI, None,
+                               layer.N_cap, layer.w, q_pos, m, n_ent, scores)
+        if ev:
+            ev[2].record()
+        ops.lca_topk(B, 1, layer.N_cap, scores, q_pos, m, n_ent, cfg.k, layer.idx, ws_topk)
+        if ev:
+            ev[3].record()
+        ops.lca_sparse_mqa(B, 1, cfg.H, cfg.c, layer.q, cfg.io_dtype, layer.cache, cfg.kv_dtype,
+                           layer.N_cap, layer.idx, cfg.k, q_pos, m, n_ent, layer.ring, cfg.n_win, 0,
+                           cfg.n_win, cfg.tau, cfg.eps, None, layer.out, cfg.io_dtype, layer.lse,
+                           ws_mqa)
+        if ev:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per_stage = {s: [] for s in stages}
+    for ev in events:
+        for j, s in enumerate(stages):
+            per_stage[s].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)
+    avg = {s: float(np.mean(v)) for s, v in per_stage.items()}
+    ms_per_step = elapsed / args.steps * 1e3
+    value = B * args.steps / elapsed
+
+    # dominant kernel: the indexer.  Algorithmic bytes per launch: every visible
+    # entry's 128-byte fp8 key, plus the 64x128 fp8 query and 64 fp32 weights of
+    # each sequence (the fp32 score output is not counted).
+    n_vis_mean = float(np.mean([((d["lengths"] + args.warmup + i) // m).sum() for i in range(args.steps)]))
+    idx_bytes = n_vis_mean * cfg.d_I + B * cfg.H_I * (cfg.d_I + 4)
+    achieved = idx_bytes / avg["indexer"] / 1e9
+    # traffic from the committed rocprofv3 counter summary of this kernel, if current
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "indexer_fp8_decode_b16_1m_counters.txt")
+    if os.path.exists(tfile):
+        kv = dict(l.split(":", 1) for l in open(tfile) if ":" in l and not l.startswith("#"))
+        src = os.path.join(ROOT, "long_context_attention_14_amd", "csrc", "indexer.hip")
+        import hashlib
+        cur = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        if kv.get("indexer_source_sha256_16", "").strip() == cur and "hbm_bytes_per_launch" in kv:
+            traffic = float(kv["hbm_bytes_per_launch"])
+    step_bytes = idx_bytes + B * (cfg.k * cfg.c * 2 + cfg.n_win * cfg.c * 2 + 2 * cfg.H * cfg.c * 2)
+    result = {
+        "metric": "CSA/HCA decode query-tokens/s at 1M ctx + achieved HBM GB/s vs peak",
+        "value": value, "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8 indexer / bf16 KV / fp32 accumulate",
+        "data": "synthetic (seeded; N(0,1) and RMS-normalised rows)",
+        "config": {"workload": "csa_decode_b16_1m: batch 16, context 2^20 + U{0..3}, m=4 "
+                               "(262144 entries), fp8 indexer 64x128, top-1024, MQA 64x512 bf16, "
+                               "window 128",
+                   "global_batch": B, "seq_len": int(cfg.ctx), "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "indexer_mfma_kernel<fp8>"},
+        "stages_us": {s: v * 1e6 for s, v in avg.items()},
+        "step_algorithmic_GBs": step_bytes / (ms_per_step * 1e-3) / 1e9,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_seconds)
+    if args.detail:
+        with open(args.detail, "w") as f:
+            json.dump({"per_stage_s": per_stage, "result": result}, f)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,283 @@
+/*
+ * lca.h -- C ABI of the MI355X (gfx950) CSA/HCA long-context attention path.
+ *
+ * The method (DeepSeek-V4's hybrid attention, as described on the pages
+ * "DeepSeek V4 Architecture Tricks" (pinktalk.online), the QbitAI article on
+ * DeepSeek-V4 (m.admirer.cn) and "[DeepSeek-5] DeepSeek-V4 Technical Report:
+ * Hybrid Attention and Post-Training for Million-Token Contexts"
+ * (xutianle.me)):
+ *   - every m tokens' KV candidates are pooled into one compressed entry by a
+ *     per-channel softmax over gate logits plus a learned positional bias;
+ *     CSA (m = 4) also pools the previous block (overlap), HCA (m' = 128)
+ *     does not;
+ *   - CSA scores each query against every visible entry with the lightning
+ *     indexer and keeps the top-k (k = 1024) entries;
+ *   - multi-query attention (one KV row is both key and value, head dim
+ *     c = 512) runs over the kept entries (CSA) or all visible entries (HCA),
+ *     plus a sliding window over the last n_win = 128 tokens' uncompressed
+ *     KV; both branches form one softmax, merged by log-sum-exp;
+ *   - queries and KV are RMS-normalised before attention.
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates or frees device memory and keeps no pointer after a
+ *     call returns.  Scratch space is a caller-provided device workspace whose
+ *     size the matching *_workspace_size call returns.
+ *   - Tensors are dense and row-major in the shapes given; the innermost
+ *     dimension is contiguous.  Every pointer must be 16-byte aligned.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     default stream).  No call synchronises the host.
+ *   - Arguments are validated on the host before any HIP call; a call that
+ *     returns an error has enqueued nothing.  A HIP launch failure returns
+ *     LCA_ERR_HIP.  lca_last_error() gives a per-thread message for the last
+ *     failing call.  No call aborts, prints or throws.
+ *   - Results are deterministic: the same inputs give bitwise-identical
+ *     outputs, independent of the other sequences in the batch.
+ *
+ * Stored formats (enum lca_dtype)
+ *   LCA_F32              IEEE float32.
+ *   LCA_BF16             bfloat16 (upper half of float32), round to nearest even.
+ *   LCA_FP8_E4M3         OCP fp8 e4m3fn (bias 7, no inf, max 448), one byte.
+ *   LCA_MXFP4            OCP MXFP4: e2m1 codes, two per byte (element 2i in the
+ *                        low nibble), plus a separate uint8 E8M0 scale
+ *                        (2^(s-127)) per 32 consecutive elements of the row.
+ *   LCA_KV_FP8_BF16ROPE  a KV row of c dims stored as c-64 e4m3 bytes followed
+ *                        by the last 64 dims (the RoPE dims) as bf16: c+64 bytes
+ *                        ("DeepSeek V4 Architecture Tricks", section
+ *                        "Partial RoPE 和 Attention Sink").
+ *
+ * Positions and visibility
+ *   Tokens of a sequence have positions 0, 1, 2, ...  Compressed entry s covers
+ *   tokens [s*m, (s+1)*m).  A query at position t sees entry s iff
+ *   (s+1)*m - 1 <= t and s < n_entries[b] (strict causality of compressed
+ *   attention: an entry that covers a future token is never visible).  Its
+ *   window is positions max(0, t-n_win+1) .. t.
+ */
+#ifndef LCA_H
+#define LCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LCA_ABI_VERSION 1
+
+/* A hipStream_t. */
+typedef struct ihipStream_t* lca_stream_t;
+
+enum lca_status {
+  LCA_OK = 0,
+  LCA_ERR_INVALID_ARG = -1, /* a NULL pointer, bad size, shape or enum value      */
+  LCA_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype/shape combination) */
+  LCA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required          */
+  LCA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed          */
+};
+
+enum lca_dtype {
+  LCA_F32 = 0,
+  LCA_BF16 = 1,
+  LCA_FP8_E4M3 = 2,
+  LCA_MXFP4 = 3,
+  LCA_KV_FP8_BF16ROPE = 4
+};
+
+enum lca_mode {
+  LCA_CSA = 0, /* compressed sparse attention: overlapped m-token blocks, top-k */
+  LCA_HCA = 1  /* heavily compressed attention: disjoint m'-token blocks, dense */
+};
+
+/* ABI version (LCA_ABI_VERSION of the built library). */
+int lca_version(void);
+
+/* Static text for a status code. */
+const char* lca_status_string(int status);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* lca_last_error(void);
+
+/* Bytes of one stored KV row of c dims in format kv_dtype (F32, BF16 or
+ * KV_FP8_BF16ROPE), or 0 if the combination is invalid. */
+size_t lca_kv_row_bytes(int kv_dtype, int c);
+
+/* ---------------------------------------------------------------------------
+ * lca_compress -- the KV compressor on a prefill chunk.
+ * "DeepSeek V4 Architecture Tricks", section "压缩 KV 的具体 trick": KV
+ * candidates and compression weights come from the hidden states; weights
+ * plus a learnable positional bias go through a softmax; the weighted sum is
+ * the compressed entry; CSA also looks at the previous block's candidates.
+ *
+ * For entry s of the chunk (s = 0 .. n_new/m - 1) and channel ch:
+ *   E[s,ch] = sum_j softmax_j(Z[j,ch] + P[slot(j),ch]) * C[j,ch]
+ * over candidates j: CSA -- the m tokens of the previous block then the m
+ * tokens of block s (slots 0 .. 2m-1 in time order; for s = 0 the previous
+ * block is prevC/prevZ, or absent (masked) when those are NULL); HCA -- the m
+ * tokens of block s (slots 0 .. m-1).  The stored entry is
+ * cast(E / sqrt(mean(E^2) + eps)) (unit-gain RMSNorm, QbitAI article, hybrid
+ * attention section), written to cache[b, first_entry + s].
+ *
+ *   mode         LCA_CSA or LCA_HCA
+ *   m            tokens per entry (>= 1); n_new % m == 0
+ *   B, n_new, c  sequences, new tokens per sequence, channels (c % 64 == 0, c <= 1024)
+ *   C, Z         [B, n_new, c] candidates / gate logits, format io_dtype (F32|BF16)
+ *   prevC,prevZ  [B, m, c] previous block (CSA only) or both NULL
+ *   P            [2m, c] (CSA) or [m, c] (HCA) float32 positional bias
+ *   cache        [B, N_cap, row] stored entries, format kv_dtype; rows
+ *                first_entry .. first_entry + n_new/m - 1 are written
+ *   N_cap        rows per sequence in cache; first_entry + n_new/m <= N_cap
+ *   eps          RMSNorm epsilon
+ * ------------------------------------------------------------------------- */
+int lca_compress(int mode, int m, int B, int n_new, int c, const void* C, const void* Z,
+                 int io_dtype, const void* prevC, const void* prevZ, const float* P,
+                 void* cache, int kv_dtype, int N_cap, int first_entry, float eps,
+                 lca_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * lca_rmsnorm_rows -- y[b, i] = cast(x[b, i] / sqrt(mean(x[b, i]^2) + eps)):
+ * the window (uncompressed) KV of new tokens, RMSNorm of their KV candidates
+ * (QbitAI article, hybrid attention section: Q/KV RMSNorm; sliding-window
+ * branch over uncompressed KV).
+ *   x  [B, n, c] format x_dtype (F32|BF16)
+ *   y  rows (b, i) at y + (b*y_seq_rows + i) * row_bytes(y_dtype, c)
+ * ------------------------------------------------------------------------- */
+int lca_rmsnorm_rows(int B, int n, int c, const void* x, int x_dtype, void* y, int y_dtype,
+                     int y_seq_rows, float eps, lca_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * lca_indexer_scores -- lightning-indexer scores (QbitAI article, hybrid
+ * attention section: inherited from V3.2's DSA; "DeepSeek V4 Architecture
+ * Tricks", section "CSA": 64 indexer heads of dim 128; section "FP4 / FP8
+ * Quantization-Aware Training": the indexer QK path in FP4):
+ *   I[b,t,s] = sum_h w[b,t,h] * max(0, sum_d qI[b,t,h,d] * kI[b,s,d])
+ * for s < vis(b,t) = min((q_pos[b,t]+1)/m, n_entries[b]).  Entries s >=
+ * vis(b,t) are not written.  Products accumulate in float32.
+ *
+ *   idx_dtype  F32, FP8_E4M3 or MXFP4 (for both qI and kI)
+ *   qI         [B, n_q, H_I, d_I] (MXFP4: [B, n_q, H_I, d_I/2] bytes + qI_scale
+ *              [B, n_q, H_I, d_I/32]); qI_scale NULL otherwise
+ *   kI         [B, N_cap, d_I] (MXFP4: bytes + kI_scale [B, N_cap, d_I/32])
+ *   w          [B, n_q, H_I] float32 head weights
+ *   q_pos      [B, n_q] int32 positions; n_entries [B] int32 (both device)
+ *   scores     [B, n_q, N_cap] float32
+ * FP8/MXFP4 need H_I == 64 and d_I == 128; F32 needs d_I <= 256, H_I <= 64.
+ * ------------------------------------------------------------------------- */
+int lca_indexer_scores(int B, int n_q, int H_I, int d_I, int idx_dtype, const void* qI,
+                       const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale,
+                       int N_cap, const float* w, const int32_t* q_pos, int m,
+                       const int32_t* n_entries, float* scores, lca_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * lca_topk -- per-query top-k selection ("DeepSeek V4 Architecture Tricks",
+ * section "CSA": top-k = 1024; QbitAI article: 1M tokens attend 1024
+ * compressed blocks).  idx[b,t,:] holds the min(k, vis) indices s < vis(b,t)
+ * with the largest scores[b,t,s] (equal scores: lower index first; -0 counts
+ * as +0 and NaN as -inf), in ascending order, followed by -1 padding.
+ *   scores [B, n_q, N_cap] float32, idx [B, n_q, k] int32, 1 <= k <= 4096.
+ * Workspace: lca_topk_workspace_size(B, n_q, N_cap, k) bytes.
+ * ------------------------------------------------------------------------- */
+size_t lca_topk_workspace_size(int B, int n_q, int N_cap, int k);
+int lca_topk(int B, int n_q, int N_cap, const float* scores, const int32_t* q_pos, int m,
+             const int32_t* n_entries, int k, int32_t* idx, void* workspace,
+             size_t workspace_bytes, lca_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * lca_sparse_mqa -- core attention of CSA (over idx) or HCA (idx == NULL: all
+ * visible entries) plus the sliding-window branch, merged into one softmax
+ * (QbitAI article, hybrid attention section: MQA over the selected compressed
+ * entries, KV entries act as both key and value; Q/KV RMSNorm; the window
+ * branch over the most recent tokens' uncompressed KV; the attention sink as
+ * an extra logit in the denominator).  For head h of query (b,t):
+ *   qh  = q[b,t,h] / sqrt(mean(q[b,t,h]^2) + eps)
+ *   rows = {cache[b,s] : s in S(b,t)} u {win[b, slot(j)] : j in window(t)}
+ *   out[b,t,h] = sum_x softmax_x(tau * qh . row_x) * row_x, where the softmax
+ *   denominator also holds exp(sink[h]) when sink != NULL;
+ *   lse[b,t,h]  = log of that denominator.
+ *   q        [B, n_q, H, c] format q_dtype (F32|BF16), not normalised
+ *   cache    [B, N_cap, row] format kv_dtype (F32|BF16|KV_FP8_BF16ROPE), rows
+ *            already RMS-normalised
+ *   idx      [B, n_q, k] int32 ascending, -1 padded (lca_topk output), or NULL
+ *   q_pos    [B, n_q], n_entries [B] int32 device
+ *   win      [B, W_cap, row] window KV in kv_dtype; position j lives in slot
+ *            (j - win_origin) mod W_cap.  A decode ring is W_cap = n_win,
+ *            win_origin = 0; a prefill buffer of positions p0 .. p0+W_cap-1 is
+ *            win_origin = p0.  Every window position must be present.
+ *   out      [B, n_q, H, c] format out_dtype (F32|BF16); lse [B, n_q, H] or NULL
+ * Workspace: lca_sparse_mqa_workspace_size(...) bytes (split partials).
+ * ------------------------------------------------------------------------- */
+size_t lca_sparse_mqa_workspace_size(int B, int n_q, int H, int c, int kv_dtype, int k,
+                                     int N_cap, int n_win, int dense);
+int lca_sparse_mqa(int B, int n_q, int H, int c, const void* q, int q_dtype, const void* cache,
+                   int kv_dtype, int N_cap, const int32_t* idx, int k, const int32_t* q_pos,
+                   int m, const int32_t* n_entries, const void* win, int W_cap,
+                   int64_t win_origin, int n_win, float tau, float eps, const float* sink,
+                   void* out, int out_dtype, float* lse, void* workspace,
+                   size_t workspace_bytes, lca_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * lca_state_append -- decode-time state of uncompressed tokens ("DeepSeek V4
+ * Architecture Tricks", section "Heterogeneous KV Cache Layout": the state
+ * cache keeps the window KV and the tail tokens of the block not yet
+ * compressed; the classical cache keeps compressed entries).  For each
+ * sequence b with L = n_tokens[b] tokens so far, the new token gets position
+ * p = L:
+ *   - tokC/tokZ go to tail row  ((p/m)%2)*m + p%m  (CSA: two-block ring that
+ *     also keeps the previous block for the overlap) or p%m (HCA);
+ *   - ring[b, p % n_win] = cast(RMSNorm(tokC[b]));
+ *   - if (p+1) % m == 0 the block is compressed (as lca_compress) into
+ *     cache[b, (p+1)/m - 1] (skipped if that row is >= N_cap);
+ *   - n_tokens[b] = p+1, q_pos[b] = p, n_entries[b] = (p+1)/m.
+ *   tailC, tailZ [B, 2m or m, c] io_dtype; ring [B, n_win, row] kv_dtype;
+ *   cache [B, N_cap, row]; n_tokens, q_pos, n_entries [B] int32 device.
+ * ------------------------------------------------------------------------- */
+int lca_state_append(int mode, int m, int B, int c, int n_win, const void* tokC, const void* tokZ,
+                     int io_dtype, void* tailC, void* tailZ, void* ring, int kv_dtype,
+                     const float* P, void* cache, int N_cap, int32_t* n_tokens, int32_t* q_pos,
+                     int32_t* n_entries, float eps, lca_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * lca_decode_step -- one decode step of one CSA or HCA layer for B sequences:
+ * lca_state_append, then (CSA) lca_indexer_scores + lca_topk, then
+ * lca_sparse_mqa over the ring window (W_cap = n_win, win_origin = 0).
+ * ------------------------------------------------------------------------- */
+typedef struct lca_decode_layer {
+  size_t struct_size;   /* sizeof(lca_decode_layer) */
+  int mode, m, B, c, H, n_win, N_cap;
+  int io_dtype, kv_dtype;
+  void* tailC;          /* [B, 2m|m, c]   */
+  void* tailZ;
+  void* ring;           /* [B, n_win, row] */
+  void* cache;          /* [B, N_cap, row] */
+  int32_t* n_tokens;    /* [B]            */
+  const float* P;       /* [2m|m, c]      */
+  const float* sink;    /* [H] or NULL    */
+  float tau, eps;
+  /* CSA only */
+  int k, H_I, d_I, idx_dtype;
+  const void* kI;       /* [B, N_cap, d_I] (+ kI_scale for MXFP4) */
+  const uint8_t* kI_scale;
+} lca_decode_layer;
+
+typedef struct lca_decode_io {
+  size_t struct_size;   /* sizeof(lca_decode_io) */
+  const void* tokC;     /* [B, c] io_dtype */
+  const void* tokZ;
+  const void* q;        /* [B, H, c] io_dtype */
+  const void* qI;       /* CSA: [B, H_I, d_I] (+ qI_scale) */
+  const uint8_t* qI_scale;
+  const float* w;       /* CSA: [B, H_I] */
+  void* out;            /* [B, H, c] out_dtype */
+  float* lse;           /* [B, H] or NULL */
+  int out_dtype;
+  int32_t* idx_out;     /* CSA: [B, k] selected entries, or NULL (kept in workspace) */
+} lca_decode_io;
+
+size_t lca_decode_workspace_size(const lca_decode_layer* layer);
+int lca_decode_step(const lca_decode_layer* layer, const lca_decode_io* io, void* workspace,
+                    size_t workspace_bytes, lca_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LCA_H */

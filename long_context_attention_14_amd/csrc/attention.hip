@@ -1,0 +1,307 @@
+// Core attention of CSA/HCA plus the sliding-window branch, as one softmax
+// merged by log-sum-exp (QbitAI article on DeepSeek-V4, hybrid attention
+// section: multi-query attention over the selected compressed entries, each
+// entry being both key and value; RMSNorm of queries and KV before attention;
+// a sliding-window branch over the most recent tokens' uncompressed KV; an
+// attention-sink logit that only enlarges the softmax denominator.  "DeepSeek
+// V4 Architecture Tricks", section "Sliding Window Branch": n_win = 128).
+//
+// Work decomposition (flash-decoding): for a query row, the list of candidate
+// rows is [compressed slots (top-k indices, or all visible entries for HCA);
+// n_win window slots].  The list is cut into splits of kSplitRows slots when
+// there are few query rows (decode), so that enough workgroups fill the 256
+// CUs; each (query row, head group, split) workgroup streams its rows through
+// LDS in tiles, keeps an online softmax per head, and writes a normalised
+// partial (o, lse).  A merge kernel combines the splits of a row in a fixed
+// order (deterministic).  With a single split (prefill: many query rows) the
+// workgroup writes the final output directly.
+#include "common.h"
+
+namespace lca {
+namespace {
+
+constexpr int kAttnThreads = 256;
+constexpr int kHG = 8;          // heads per workgroup
+constexpr int kRT = 16;         // rows per LDS tile
+constexpr int kSplitRows = 64;  // slots per split in decode
+
+struct SlotCtx {
+  const int32_t* idx;  // [k] for this row, or nullptr (dense)
+  int NS;              // compressed slots
+  int vis;             // visible entries
+  int N_cap;
+  int t;               // query position
+  int n_win;
+  const uint8_t* cache_b;
+  const uint8_t* win_b;
+  int W_cap;
+  long long win_origin;
+  size_t kv_row;
+};
+
+// Row pointer of slot i of the candidate list, or nullptr if the slot is empty.
+__device__ __forceinline__ const uint8_t* slot_row(const SlotCtx& s, int i) {
+  if (i < s.NS) {
+    int e = s.idx ? s.idx[i] : i;
+    const int lim = s.vis < s.N_cap ? s.vis : s.N_cap;
+    if (e < 0 || e >= lim) return nullptr;
+    return s.cache_b + static_cast<size_t>(e) * s.kv_row;
+  }
+  const int w = i - s.NS;
+  const long long j = static_cast<long long>(s.t) - s.n_win + 1 + w;
+  if (j < 0) return nullptr;
+  long long slot = (j - s.win_origin) % s.W_cap;
+  if (slot < 0) slot += s.W_cap;
+  return s.win_b + static_cast<size_t>(slot) * s.kv_row;
+}
+
+template <int CPL>
+__global__ __launch_bounds__(kAttnThreads) void attn_generic_kernel(
+    int n_q, int H, int c, const uint8_t* __restrict__ q, int q_fmt, const uint8_t* __restrict__ cache,
+    int kv_fmt, int N_cap, const int32_t* __restrict__ idx, int k, const int32_t* __restrict__ q_pos,
+    int m, const int32_t* __restrict__ n_entries, const uint8_t* __restrict__ win, int W_cap,
+    long long win_origin, int n_win, float tau, float eps, const float* __restrict__ sink,
+    int n_splits, int split_rows, uint8_t* __restrict__ out, int out_fmt, float* __restrict__ lse,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
+  constexpr int C = CPL * 64;
+  constexpr int CP = C + 1;                    // padded LDS row stride (floats)
+  constexpr int OPT = kHG * C / kAttnThreads;  // outputs per thread
+  constexpr int TPH = kAttnThreads / kHG;      // threads per head
+  __shared__ float qs[kHG * CP];
+  __shared__ float rows_s[kRT * CP];
+  __shared__ float logit_s[kHG * kRT];
+  __shared__ int valid_s[kRT];
+
+  const int n_hg = H / kHG;
+  long long bid = blockIdx.x;
+  const int split = static_cast<int>(bid % n_splits);
+  bid /= n_splits;
+  const int hg = static_cast<int>(bid % n_hg);
+  const long long row = bid / n_hg;
+  const int b = static_cast<int>(row / n_q);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+
+  SlotCtx sc;
+  sc.t = q_pos[row];
+  sc.vis = visible_entries(sc.t, m, n_entries[b], N_cap);
+  sc.idx = idx ? idx + row * k : nullptr;
+  sc.NS = idx ? k : N_cap;
+  sc.N_cap = N_cap;
+  sc.n_win = n_win;
+  sc.kv_row = row_bytes(kv_fmt, c);
+  sc.cache_b = cache + static_cast<size_t>(b) * N_cap * sc.kv_row;
+  sc.win_b = win + static_cast<size_t>(b) * W_cap * sc.kv_row;
+  sc.W_cap = W_cap;
+  sc.win_origin = win_origin;
+  const int NT = sc.NS + n_win;
+  const int s_begin = split * split_rows;
+  const int s_end = min(s_begin + split_rows, NT);
+
+  // normalised queries of this head group (wave wv handles heads wv, wv+4)
+  const size_t q_row = row_bytes(q_fmt, c);
+  for (int hh = wv; hh < kHG; hh += kAttnThreads / 64) {
+    float v[CPL];
+    load_row<CPL>(q + (static_cast<size_t>(row) * H + hg * kHG + hh) * q_row, q_fmt, c, lane, v);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) ss += v[i] * v[i];
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / static_cast<float>(c) + eps);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) qs[hh * CP + lane * CPL + i] = v[i] * r;
+  }
+
+  const int my_h = tid / TPH;
+  const int my_d0 = tid % TPH;
+  float o[OPT];
+#pragma unroll
+  for (int i = 0; i < OPT; ++i) o[i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int base = s_begin; base < s_end; base += kRT) {
+    __syncthreads();
+    // stage kRT rows (each wave 4 rows) as fp32
+    for (int r = wv; r < kRT; r += kAttnThreads / 64) {
+      const int slot = base + r;
+      const uint8_t* rp = slot < s_end ? slot_row(sc, slot) : nullptr;
+      float v[CPL];
+      if (rp) {
+        load_row<CPL>(rp, kv_fmt, c, lane, v);
+      } else {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) v[i] = 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) rows_s[r * CP + lane * CPL + i] = v[i];
+      if (lane == 0) valid_s[r] = rp != nullptr;
+    }
+    __syncthreads();
+    if (tid < kHG * kRT) {
+      const int h = tid / kRT, r = tid % kRT;
+      float d = 0.f;
+      const float* qp = qs + h * CP;
+      const float* rp = rows_s + r * CP;
+      for (int i = 0; i < C; ++i) d = fmaf(qp[i], rp[i], d);
+      logit_s[h * kRT + r] = valid_s[r] ? d * tau : -INFINITY;
+    }
+    __syncthreads();
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < kRT; ++r) tmax = fmaxf(tmax, logit_s[my_h * kRT + r]);
+    const float m_new = fmaxf(m_run, tmax);
+    if (m_new == -INFINITY) continue;
+    const float scale = __expf(m_run - m_new);
+    l_run *= scale;
+#pragma unroll
+    for (int i = 0; i < OPT; ++i) o[i] *= scale;
+#pragma unroll 4
+    for (int r = 0; r < kRT; ++r) {
+      const float lg = logit_s[my_h * kRT + r];
+      const float p = lg == -INFINITY ? 0.f : __expf(lg - m_new);
+      l_run += p;
+      const float* rp = rows_s + r * CP + my_d0;
+#pragma unroll
+      for (int i = 0; i < OPT; ++i) o[i] = fmaf(p, rp[i * TPH], o[i]);
+    }
+    m_run = m_new;
+  }
+
+  const int h = hg * kHG + my_h;
+  float lse_v = l_run > 0.f ? m_run + __logf(l_run) : -INFINITY;
+  const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+  if (n_splits == 1) {
+    float f = 1.f;
+    if (sink && lse_v != -INFINITY) {
+      const float sk = sink[h];
+      const float mx = fmaxf(lse_v, sk);
+      const float tot = mx + __logf(__expf(lse_v - mx) + __expf(sk - mx));
+      f = __expf(lse_v - tot);
+      lse_v = tot;
+    } else if (sink) {
+      lse_v = sink[h];
+    }
+    const size_t orow = (static_cast<size_t>(row) * H + h) * row_bytes(out_fmt, c);
+    for (int i = 0; i < OPT; ++i) {
+      const int d = my_d0 + i * TPH;
+      const float v = o[i] * inv * f;
+      if (out_fmt == LCA_F32)
+        reinterpret_cast<float*>(out + orow)[d] = v;
+      else
+        reinterpret_cast<uint16_t*>(out + orow)[d] = f32_to_bf16(v);
+    }
+    if (lse && my_d0 == 0) lse[static_cast<size_t>(row) * H + h] = lse_v;
+  } else {
+    const size_t prow = (static_cast<size_t>(row) * n_splits + split) * H + h;
+    for (int i = 0; i < OPT; ++i) part_o[prow * c + my_d0 + i * TPH] = o[i] * inv;
+    if (my_d0 == 0) part_lse[prow] = lse_v;
+  }
+}
+
+// One wave per (query row, head): combine the splits in order.
+template <int CPL>
+__global__ __launch_bounds__(256) void attn_merge_kernel(
+    long long rows, int H, int c, int n_splits, const float* __restrict__ part_o,
+    const float* __restrict__ part_lse, const float* __restrict__ sink, uint8_t* __restrict__ out,
+    int out_fmt, float* __restrict__ lse) {
+  const long long rh = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (rh >= rows * H) return;
+  const int lane = threadIdx.x & 63;
+  const long long row = rh / H;
+  const int h = static_cast<int>(rh % H);
+  float mx = sink ? sink[h] : -INFINITY;
+  for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, part_lse[(row * n_splits + s) * H + h]);
+  float acc[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
+  float den = 0.f;
+  if (mx != -INFINITY) {
+    if (sink) den = __expf(sink[h] - mx);
+    for (int s = 0; s < n_splits; ++s) {
+      const long long pr = (row * n_splits + s) * H + h;
+      const float ls = part_lse[pr];
+      if (ls == -INFINITY) continue;
+      const float wgt = __expf(ls - mx);
+      den += wgt;
+      float v[CPL];
+      load_row<CPL>(part_o + pr * c, LCA_F32, c, lane, v);
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) acc[i] = fmaf(wgt, v[i], acc[i]);
+    }
+  }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) acc[i] *= inv;
+  store_row<CPL>(out + rh * row_bytes(out_fmt, c), out_fmt, c, lane, acc);
+  if (lse && lane == 0) lse[rh] = den > 0.f ? mx + __logf(den) : -INFINITY;
+}
+
+struct Plan {
+  int n_splits, split_rows;
+};
+
+Plan make_plan(long long rows, int k, int N_cap, int n_win, int dense) {
+  const int NT = (dense ? N_cap : k) + n_win;
+  Plan p;
+  if (rows >= 512) {
+    p.n_splits = 1;
+    p.split_rows = NT;
+  } else {
+    p.split_rows = kSplitRows;
+    p.n_splits = (NT + kSplitRows - 1) / kSplitRows;
+  }
+  return p;
+}
+
+}  // namespace
+
+size_t mqa_workspace_bytes(int B, int n_q, int H, int c, int kv_fmt, int k, int N_cap, int n_win,
+                           int dense) {
+  (void)kv_fmt;
+  const long long rows = static_cast<long long>(B) * n_q;
+  const Plan p = make_plan(rows, k, N_cap, n_win, dense);
+  if (p.n_splits == 1) return 0;
+  const size_t n = static_cast<size_t>(rows) * p.n_splits * H;
+  return n * c * sizeof(float) + ((n * sizeof(float) + 255) & ~static_cast<size_t>(255)) + 256;
+}
+
+#define LCA_ATTN_CPL(c, KERNEL, GRID, BLOCK, ...)                                         \
+  do {                                                                                    \
+    switch ((c) / 64) {                                                                   \
+      case 2: hipLaunchKernelGGL(KERNEL<2>, GRID, BLOCK, 0, s, __VA_ARGS__); break;       \
+      case 4: hipLaunchKernelGGL(KERNEL<4>, GRID, BLOCK, 0, s, __VA_ARGS__); break;       \
+      case 8: hipLaunchKernelGGL(KERNEL<8>, GRID, BLOCK, 0, s, __VA_ARGS__); break;       \
+      default: return hipErrorInvalidValue;                                               \
+    }                                                                                     \
+  } while (0)
+
+hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, const void* cache,
+                      int kv_fmt, int N_cap, const int32_t* idx, int k, const int32_t* q_pos, int m,
+                      const int32_t* n_entries, const void* win, int W_cap, int64_t win_origin,
+                      int n_win, float tau, float eps, const float* sink, void* out, int out_fmt,
+                      float* lse, void* ws, hipStream_t s) {
+  const long long rows = static_cast<long long>(B) * n_q;
+  if (rows == 0) return hipSuccess;
+  const int dense = idx == nullptr;
+  const Plan p = make_plan(rows, k, N_cap, n_win, dense);
+  float* part_o = nullptr;
+  float* part_lse = nullptr;
+  if (p.n_splits > 1) {
+    const size_t n = static_cast<size_t>(rows) * p.n_splits * H;
+    part_o = static_cast<float*>(ws);
+    part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + n * c * sizeof(float));
+  }
+  const dim3 grid(static_cast<unsigned>(rows * (H / kHG) * p.n_splits));
+  LCA_ATTN_CPL(c, attn_generic_kernel, grid, dim3(kAttnThreads), n_q, H, c,
+               static_cast<const uint8_t*>(q), q_fmt, static_cast<const uint8_t*>(cache), kv_fmt,
+               N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
+               static_cast<long long>(win_origin), n_win, tau, eps, sink, p.n_splits, p.split_rows,
+               static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_splits == 1) return e;
+  const dim3 g2(static_cast<unsigned>((rows * H + 3) / 4));
+  LCA_ATTN_CPL(c, attn_merge_kernel, g2, dim3(256), rows, H, c, p.n_splits, part_o, part_lse, sink,
+               static_cast<uint8_t*>(out), out_fmt, lse);
+  return hipGetLastError();
+}
+
+}  // namespace lca

@@ -1,0 +1,182 @@
+// Shared device helpers and internal launcher declarations of the CSA/HCA
+// attention library for gfx950 (CDNA4, 64-wide wavefronts).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/lca.h"
+
+namespace lca {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// stored formats
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// float32 -> bfloat16, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// OCP e4m3fn byte -> float32 (exact).  Exponent bias 7, exponent 0 is
+// subnormal (f * 2^-9), S.1111.111 is NaN.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t v) {
+  const uint32_t s = (v & 0x80u) << 24;
+  const uint32_t e = (v >> 3) & 0xfu;
+  const uint32_t f = v & 0x7u;
+  if (e == 0) return __uint_as_float(s | __float_as_uint(static_cast<float>(f) * 0.001953125f));
+  if (e == 0xf && f == 0x7) return __uint_as_float(0x7fc00000u);
+  return __uint_as_float(s | ((e + 120u) << 23) | (f << 20));
+}
+
+// float32 -> OCP e4m3fn byte, round to nearest even, saturating at +-448.
+// With E = max(exponent(|x|), -6) the quantum is 2^(E-3), and the code of
+// q = rint(|x| / 2^(E-3)) is (E + 6) * 8 + q for every E (subnormals included).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t s = (__float_as_uint(x) >> 24) & 0x80u;
+  float a = fabsf(x);
+  if (!(a == a)) return 0x7fu;
+  a = fminf(a, 448.0f);
+  int E = static_cast<int>((__float_as_uint(a) >> 23) & 0xffu) - 127;
+  E = E < -6 ? -6 : E;
+  const float inv_q = __uint_as_float(static_cast<uint32_t>(127 - (E - 3)) << 23);  // 2^(3-E)
+  const float q = rintf(a * inv_q);
+  uint32_t code = static_cast<uint32_t>((E + 6) * 8 + static_cast<int>(q));
+  code = code > 126u ? 126u : code;
+  return s | code;
+}
+
+// ---------------------------------------------------------------------------
+// row I/O: a lane owns CPL consecutive channels [lane*CPL, lane*CPL + CPL)
+
+template <int CPL>
+__device__ __forceinline__ void load_row(const void* base, int fmt, int c, int lane, float* v) {
+  const int ch0 = lane * CPL;
+  if (fmt == LCA_F32) {
+    const float* p = static_cast<const float*>(base) + ch0;
+#pragma unroll
+    for (int i = 0; i < CPL; i += 2) {
+      const float2 t = *reinterpret_cast<const float2*>(p + i);
+      v[i] = t.x;
+      v[i + 1] = t.y;
+    }
+  } else if (fmt == LCA_BF16) {
+    const uint16_t* p = static_cast<const uint16_t*>(base) + ch0;
+#pragma unroll
+    for (int i = 0; i < CPL; i += 2) {
+      const uint32_t t = *reinterpret_cast<const uint32_t*>(p + i);
+      v[i] = bf16_to_f32(static_cast<uint16_t>(t & 0xffffu));
+      v[i + 1] = bf16_to_f32(static_cast<uint16_t>(t >> 16));
+    }
+  } else {  // LCA_KV_FP8_BF16ROPE
+    const uint8_t* p = static_cast<const uint8_t*>(base);
+    const int nope = c - 64;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int ch = ch0 + i;
+      v[i] = ch < nope ? e4m3_to_f32(p[ch])
+                       : bf16_to_f32(reinterpret_cast<const uint16_t*>(p + nope)[ch - nope]);
+    }
+  }
+}
+
+template <int CPL>
+__device__ __forceinline__ void store_row(void* base, int fmt, int c, int lane, const float* v) {
+  const int ch0 = lane * CPL;
+  if (fmt == LCA_F32) {
+    float* p = static_cast<float*>(base) + ch0;
+#pragma unroll
+    for (int i = 0; i < CPL; i += 2) *reinterpret_cast<float2*>(p + i) = make_float2(v[i], v[i + 1]);
+  } else if (fmt == LCA_BF16) {
+    uint16_t* p = static_cast<uint16_t*>(base) + ch0;
+#pragma unroll
+    for (int i = 0; i < CPL; i += 2)
+      *reinterpret_cast<uint32_t*>(p + i) =
+          static_cast<uint32_t>(f32_to_bf16(v[i])) | (static_cast<uint32_t>(f32_to_bf16(v[i + 1])) << 16);
+  } else {  // LCA_KV_FP8_BF16ROPE
+    uint8_t* p = static_cast<uint8_t*>(base);
+    const int nope = c - 64;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int ch = ch0 + i;
+      if (ch < nope)
+        p[ch] = static_cast<uint8_t>(f32_to_e4m3(v[i]));
+      else
+        reinterpret_cast<uint16_t*>(p + nope)[ch - nope] = f32_to_bf16(v[i]);
+    }
+  }
+}
+
+__host__ __device__ inline size_t row_bytes(int fmt, int c) {
+  switch (fmt) {
+    case LCA_F32: return 4 * static_cast<size_t>(c);
+    case LCA_BF16: return 2 * static_cast<size_t>(c);
+    case LCA_FP8_E4M3: return static_cast<size_t>(c);
+    case LCA_KV_FP8_BF16ROPE: return static_cast<size_t>(c) + 64;
+    default: return 0;
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  return x;
+}
+
+// Visible compressed entries for a query at position t: entry s needs
+// (s+1)*m - 1 <= t, and s < n_entries.
+// n_entries is also clamped to the cache capacity N_cap, and a negative
+// position sees nothing.
+__device__ __forceinline__ int visible_entries(int t, int m, int n_entries, int N_cap) {
+  if (t < 0) return 0;
+  int v = (t + 1) / m;
+  v = v < n_entries ? v : n_entries;
+  v = v < N_cap ? v : N_cap;
+  return v < 0 ? 0 : v;
+}
+
+// ---------------------------------------------------------------------------
+// internal launchers (defined next to their kernels, called by the C ABI)
+
+hipError_t launch_compress(int mode, int m, int B, int n_new, int c, const void* C, const void* Z,
+                           int io_fmt, const void* prevC, const void* prevZ, const float* P,
+                           void* cache, int kv_fmt, int N_cap, int first_entry, float eps,
+                           hipStream_t s);
+hipError_t launch_rmsnorm_rows(int B, int n, int c, const void* x, int x_fmt, void* y, int y_fmt,
+                               int y_seq_rows, float eps, hipStream_t s);
+hipError_t launch_state_append(int mode, int m, int B, int c, int n_win, const void* tokC,
+                               const void* tokZ, int io_fmt, void* tailC, void* tailZ, void* ring,
+                               int kv_fmt, const float* P, void* cache, int N_cap,
+                               int32_t* n_tokens, int32_t* q_pos, int32_t* n_entries, float eps,
+                               hipStream_t s);
+hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const void* qI,
+                          const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale,
+                          int N_cap, const float* w, const int32_t* q_pos, int m,
+                          const int32_t* n_entries, float* scores, hipStream_t s);
+size_t topk_workspace_bytes(int B, int n_q, int N_cap, int k);
+hipError_t launch_topk(int B, int n_q, int N_cap, const float* scores, const int32_t* q_pos, int m,
+                       const int32_t* n_entries, int k, int32_t* idx, void* ws, hipStream_t s);
+size_t mqa_workspace_bytes(int B, int n_q, int H, int c, int kv_fmt, int k, int N_cap, int n_win,
+                           int dense);
+hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, const void* cache,
+                      int kv_fmt, int N_cap, const int32_t* idx, int k, const int32_t* q_pos, int m,
+                      const int32_t* n_entries, const void* win, int W_cap, int64_t win_origin,
+                      int n_win, float tau, float eps, const float* sink, void* out, int out_fmt,
+                      float* lse, void* ws, hipStream_t s);
+
+}  // namespace lca

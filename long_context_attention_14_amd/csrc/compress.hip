@@ -1,0 +1,286 @@
+// KV compressor, window-KV normalisation and decode-time state append.
+//
+// Compressor ("DeepSeek V4 Architecture Tricks", section "压缩 KV 的具体 trick";
+// QbitAI article on DeepSeek-V4, hybrid attention section): each compressed
+// entry is a per-channel softmax over the gate logits plus a learned
+// positional bias of its candidate tokens, applied to their KV candidates;
+// CSA's candidates are the previous block and the own block (2m tokens), HCA's
+// the own block (m' tokens).  The entry is RMS-normalised (unit gain) and cast
+// to the cache format.
+//
+// Mapping: one 64-lane wavefront per entry; lane l owns channels
+// [l*CPL, (l+1)*CPL) with CPL = c/64, so every candidate row is one coalesced
+// c-wide load per wave; the softmax is computed online per channel in
+// registers and the RMSNorm sum of squares is a wavefront reduction.
+#include "common.h"
+
+namespace lca {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+
+struct Pool {
+  float mx, sum, acc;
+};
+
+template <int CPL>
+__device__ __forceinline__ void pool_init(Pool* p) {
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) p[i] = {-INFINITY, 0.f, 0.f};
+}
+
+// Online softmax update of one candidate (KV values c, logits z).
+template <int CPL>
+__device__ __forceinline__ void pool_add(Pool* p, const float* cv, const float* zv) {
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const float nm = fmaxf(p[i].mx, zv[i]);
+    const float sc = __expf(p[i].mx - nm);
+    const float e = __expf(zv[i] - nm);
+    p[i].sum = p[i].sum * sc + e;
+    p[i].acc = p[i].acc * sc + e * cv[i];
+    p[i].mx = nm;
+  }
+}
+
+// E / sqrt(mean(E^2) + eps) across the wave's c channels.
+template <int CPL>
+__device__ __forceinline__ void pool_finish_norm(const Pool* p, int c, float eps, float* out) {
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    out[i] = p[i].acc / p[i].sum;
+    ss += out[i] * out[i];
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / static_cast<float>(c) + eps);
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) out[i] *= r;
+}
+
+template <int CPL>
+__device__ __forceinline__ void load_bias(const float* P, int slot, int c, int lane, float* pv) {
+  load_row<CPL>(P + static_cast<size_t>(slot) * c, LCA_F32, c, lane, pv);
+}
+
+template <int CPL>
+__global__ __launch_bounds__(kWave * kWavesPerBlock) void compress_kernel(
+    int csa, int m, int B, int n_new, int c, const uint8_t* C, const uint8_t* Z, int io_fmt,
+    const uint8_t* prevC, const uint8_t* prevZ, const float* P, uint8_t* cache, int kv_fmt,
+    int N_cap, int first_entry, float eps) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int n_ent = n_new / m;
+  const long long e = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+  if (e >= static_cast<long long>(B) * n_ent) return;
+  const int b = static_cast<int>(e / n_ent);
+  const int s = static_cast<int>(e % n_ent);
+  const size_t io_row = row_bytes(io_fmt, c);
+  const uint8_t* Cb = C + static_cast<size_t>(b) * n_new * io_row;
+  const uint8_t* Zb = Z + static_cast<size_t>(b) * n_new * io_row;
+
+  Pool pool[CPL];
+  pool_init<CPL>(pool);
+  float cv[CPL], zv[CPL], pv[CPL];
+  if (csa) {
+    // slots 0..m-1: previous block (absent for the first entry without prevC)
+    const bool have_prev = s > 0 || prevC != nullptr;
+    if (have_prev) {
+      for (int i = 0; i < m; ++i) {
+        const uint8_t* rc = s > 0 ? Cb + (static_cast<size_t>(s - 1) * m + i) * io_row
+                                  : prevC + (static_cast<size_t>(b) * m + i) * io_row;
+        const uint8_t* rz = s > 0 ? Zb + (static_cast<size_t>(s - 1) * m + i) * io_row
+                                  : prevZ + (static_cast<size_t>(b) * m + i) * io_row;
+        load_row<CPL>(rc, io_fmt, c, lane, cv);
+        load_row<CPL>(rz, io_fmt, c, lane, zv);
+        load_bias<CPL>(P, i, c, lane, pv);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) zv[j] += pv[j];
+        pool_add<CPL>(pool, cv, zv);
+      }
+    }
+  }
+  const int slot0 = csa ? m : 0;
+  for (int i = 0; i < m; ++i) {
+    const size_t r = static_cast<size_t>(s) * m + i;
+    load_row<CPL>(Cb + r * io_row, io_fmt, c, lane, cv);
+    load_row<CPL>(Zb + r * io_row, io_fmt, c, lane, zv);
+    load_bias<CPL>(P, slot0 + i, c, lane, pv);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) zv[j] += pv[j];
+    pool_add<CPL>(pool, cv, zv);
+  }
+  float out[CPL];
+  pool_finish_norm<CPL>(pool, c, eps, out);
+  const size_t kv_row = row_bytes(kv_fmt, c);
+  store_row<CPL>(cache + (static_cast<size_t>(b) * N_cap + first_entry + s) * kv_row, kv_fmt, c,
+                 lane, out);
+}
+
+template <int CPL>
+__global__ __launch_bounds__(kWave * kWavesPerBlock) void rmsnorm_rows_kernel(
+    int B, int n, int c, const uint8_t* x, int x_fmt, uint8_t* y, int y_fmt, int y_seq_rows,
+    float eps) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const long long r = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+  if (r >= static_cast<long long>(B) * n) return;
+  const int b = static_cast<int>(r / n);
+  const int i = static_cast<int>(r % n);
+  float v[CPL];
+  load_row<CPL>(x + static_cast<size_t>(r) * row_bytes(x_fmt, c), x_fmt, c, lane, v);
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) ss += v[j] * v[j];
+  ss = wave_sum(ss);
+  const float rs = 1.0f / sqrtf(ss / static_cast<float>(c) + eps);
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) v[j] *= rs;
+  store_row<CPL>(y + (static_cast<size_t>(b) * y_seq_rows + i) * row_bytes(y_fmt, c), y_fmt, c, lane,
+                 v);
+}
+
+// One wave per sequence: append the token, and compress its block when the
+// token completes it.  Rows of the tail other than the new token were written
+// by earlier steps; the new token's row is used from registers.
+template <int CPL>
+__global__ __launch_bounds__(kWave * kWavesPerBlock) void state_append_kernel(
+    int csa, int m, int B, int c, int n_win, const uint8_t* tokC, const uint8_t* tokZ, int io_fmt,
+    uint8_t* tailC, uint8_t* tailZ, uint8_t* ring, int kv_fmt, const float* P, uint8_t* cache,
+    int N_cap, int32_t* n_tokens, int32_t* q_pos, int32_t* n_entries, float eps) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int b = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (b >= B) return;
+  const int p = n_tokens[b];
+  if (p < 0) return;
+  const size_t io_row = row_bytes(io_fmt, c);
+  const size_t kv_row = row_bytes(kv_fmt, c);
+  const int T_cap = csa ? 2 * m : m;
+  const int blk = p / m;
+  const int half = csa ? (blk & 1) : 0;
+  const int row = half * m + p % m;
+
+  float tc[CPL], tz[CPL];
+  load_row<CPL>(tokC + static_cast<size_t>(b) * io_row, io_fmt, c, lane, tc);
+  load_row<CPL>(tokZ + static_cast<size_t>(b) * io_row, io_fmt, c, lane, tz);
+  uint8_t* tCb = tailC + static_cast<size_t>(b) * T_cap * io_row;
+  uint8_t* tZb = tailZ + static_cast<size_t>(b) * T_cap * io_row;
+  store_row<CPL>(tCb + row * io_row, io_fmt, c, lane, tc);
+  store_row<CPL>(tZb + row * io_row, io_fmt, c, lane, tz);
+
+  // window KV of the new token
+  {
+    float u[CPL];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      u[j] = tc[j];
+      ss += u[j] * u[j];
+    }
+    ss = wave_sum(ss);
+    const float rs = 1.0f / sqrtf(ss / static_cast<float>(c) + eps);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) u[j] *= rs;
+    store_row<CPL>(ring + (static_cast<size_t>(b) * n_win + p % n_win) * kv_row, kv_fmt, c, lane, u);
+  }
+
+  if ((p + 1) % m == 0) {
+    const int s = (p + 1) / m - 1;
+    Pool pool[CPL];
+    pool_init<CPL>(pool);
+    float cv[CPL], zv[CPL], pv[CPL];
+    if (csa && s > 0) {
+      const int ph = (blk - 1) & 1;
+      for (int i = 0; i < m; ++i) {
+        load_row<CPL>(tCb + (ph * m + i) * io_row, io_fmt, c, lane, cv);
+        load_row<CPL>(tZb + (ph * m + i) * io_row, io_fmt, c, lane, zv);
+        load_bias<CPL>(P, i, c, lane, pv);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) zv[j] += pv[j];
+        pool_add<CPL>(pool, cv, zv);
+      }
+    }
+    const int slot0 = csa ? m : 0;
+    for (int i = 0; i < m; ++i) {
+      if (i == m - 1) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          cv[j] = tc[j];
+          zv[j] = tz[j];
+        }
+      } else {
+        load_row<CPL>(tCb + (half * m + i) * io_row, io_fmt, c, lane, cv);
+        load_row<CPL>(tZb + (half * m + i) * io_row, io_fmt, c, lane, zv);
+      }
+      load_bias<CPL>(P, slot0 + i, c, lane, pv);
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) zv[j] += pv[j];
+      pool_add<CPL>(pool, cv, zv);
+    }
+    float out[CPL];
+    pool_finish_norm<CPL>(pool, c, eps, out);
+    if (s < N_cap) store_row<CPL>(cache + (static_cast<size_t>(b) * N_cap + s) * kv_row, kv_fmt, c, lane, out);
+  }
+  if (lane == 0) {
+    n_tokens[b] = p + 1;
+    q_pos[b] = p;
+    const int ne = (p + 1) / m;
+    n_entries[b] = ne < N_cap ? ne : N_cap;
+  }
+}
+
+}  // namespace
+
+#define LCA_DISPATCH_CPL(c, KERNEL, GRID, ...)                                              \
+  do {                                                                                      \
+    const int cpl_ = (c) / kWave;                                                           \
+    if (cpl_ == 2)                                                                          \
+      hipLaunchKernelGGL(KERNEL<2>, GRID, dim3(kWave * kWavesPerBlock), 0, s, __VA_ARGS__); \
+    else if (cpl_ == 4)                                                                     \
+      hipLaunchKernelGGL(KERNEL<4>, GRID, dim3(kWave * kWavesPerBlock), 0, s, __VA_ARGS__); \
+    else if (cpl_ == 8)                                                                     \
+      hipLaunchKernelGGL(KERNEL<8>, GRID, dim3(kWave * kWavesPerBlock), 0, s, __VA_ARGS__); \
+    else if (cpl_ == 16)                                                                    \
+      hipLaunchKernelGGL(KERNEL<16>, GRID, dim3(kWave * kWavesPerBlock), 0, s, __VA_ARGS__); \
+    else                                                                                    \
+      return hipErrorInvalidValue;                                                          \
+  } while (0)
+
+hipError_t launch_compress(int mode, int m, int B, int n_new, int c, const void* C, const void* Z,
+                           int io_fmt, const void* prevC, const void* prevZ, const float* P,
+                           void* cache, int kv_fmt, int N_cap, int first_entry, float eps,
+                           hipStream_t s) {
+  const long long n = static_cast<long long>(B) * (n_new / m);
+  if (n == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((n + kWavesPerBlock - 1) / kWavesPerBlock));
+  LCA_DISPATCH_CPL(c, compress_kernel, grid, mode == LCA_CSA ? 1 : 0, m, B, n_new, c,
+                   static_cast<const uint8_t*>(C), static_cast<const uint8_t*>(Z), io_fmt,
+                   static_cast<const uint8_t*>(prevC), static_cast<const uint8_t*>(prevZ), P,
+                   static_cast<uint8_t*>(cache), kv_fmt, N_cap, first_entry, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_rows(int B, int n, int c, const void* x, int x_fmt, void* y, int y_fmt,
+                               int y_seq_rows, float eps, hipStream_t s) {
+  const long long rows = static_cast<long long>(B) * n;
+  if (rows == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((rows + kWavesPerBlock - 1) / kWavesPerBlock));
+  LCA_DISPATCH_CPL(c, rmsnorm_rows_kernel, grid, B, n, c, static_cast<const uint8_t*>(x), x_fmt,
+                   static_cast<uint8_t*>(y), y_fmt, y_seq_rows, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_append(int mode, int m, int B, int c, int n_win, const void* tokC,
+                               const void* tokZ, int io_fmt, void* tailC, void* tailZ, void* ring,
+                               int kv_fmt, const float* P, void* cache, int N_cap,
+                               int32_t* n_tokens, int32_t* q_pos, int32_t* n_entries, float eps,
+                               hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const dim3 grid((B + kWavesPerBlock - 1) / kWavesPerBlock);
+  LCA_DISPATCH_CPL(c, state_append_kernel, grid, mode == LCA_CSA ? 1 : 0, m, B, c, n_win,
+                   static_cast<const uint8_t*>(tokC), static_cast<const uint8_t*>(tokZ), io_fmt,
+                   static_cast<uint8_t*>(tailC), static_cast<uint8_t*>(tailZ),
+                   static_cast<uint8_t*>(ring), kv_fmt, P, static_cast<uint8_t*>(cache), N_cap,
+                   n_tokens, q_pos, n_entries, eps);
+  return hipGetLastError();
+}
+
+}  // namespace lca

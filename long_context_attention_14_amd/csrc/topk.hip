@@ -1,0 +1,459 @@
+// Per-query top-k selection of indexer scores ("DeepSeek V4 Architecture
+// Tricks", section "CSA": top-k = 1024; QbitAI article on DeepSeek-V4, hybrid
+// attention section: at 1M tokens a query attends 1024 compressed blocks).
+//
+// Scores become order-preserving uint32 keys (-0 -> +0, NaN -> -inf first), so
+// "largest score, lower index first among equals" is "largest key, lowest index
+// first".  The k-th largest key T is found by MSB-first radix select on integer
+// histograms (no floating-point atomics: the result is deterministic), then the
+// selected indices are compacted in index order: every key > T, plus the first
+// (k - #{key > T}) keys equal to T.  The output is therefore ascending.
+//
+// Two paths:
+//  * rows of at most kLdsMaxRow entries (prefill): one 1024-thread workgroup
+//    per row keeps the whole row's keys in LDS (up to 144 KiB of gfx950's
+//    160 KiB) and runs four 8-bit radix passes there;
+//  * longer rows (decode at 1M context: 262144 entries): many workgroups per
+//    row build a 4096-bin histogram of the top 12 key bits; the bin holding the
+//    k-th key splits the row into "surely selected" (higher bins) and
+//    "candidates" (that bin); a second pass compacts both per segment in index
+//    order; a last one-workgroup-per-row pass radix-selects among the
+//    candidates on the remaining 20 bits and merges the two sorted lists.
+#include "common.h"
+
+namespace lca {
+namespace {
+
+constexpr int kLdsMaxRow = 36864;
+constexpr int kRowThreads = 1024;
+constexpr int kSeg = 8192;
+constexpr int kSegThreads = 256;
+constexpr int kHistBins = 4096;
+
+__device__ __forceinline__ uint32_t score_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) u = 0xff800000u;  // NaN -> -inf
+  if (u == 0x80000000u) u = 0u;                          // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
+}
+
+// Given a histogram of `nbins` bins (bin index order == key order), find the bin
+// d holding the `want`-th largest element (1-based), and the number of elements
+// in bins above d.  Run by one full wave (all 64 lanes); nbins % 64 == 0.
+// Lane l owns bins nbins-1-l*per .. nbins-per-l*per (descending).
+__device__ void find_bin_wave(const uint32_t* hist, int nbins, int want, int* out_bin,
+                              int* out_above) {
+  const int lane = threadIdx.x & 63;
+  const int per = nbins / 64;
+  const int top = nbins - 1 - lane * per;
+  uint32_t local = 0;
+  for (int i = 0; i < per; ++i) local += hist[top - i];
+  // exclusive prefix over lanes (lane 0 holds the highest bins)
+  uint32_t incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  uint32_t run = incl - local;
+  if (run < static_cast<uint32_t>(want) && incl >= static_cast<uint32_t>(want)) {
+    for (int i = 0; i < per; ++i) {
+      const uint32_t h = hist[top - i];
+      if (run + h >= static_cast<uint32_t>(want)) {
+        *out_bin = top - i;
+        *out_above = static_cast<int>(run);
+        break;
+      }
+      run += h;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LDS path
+
+__global__ __launch_bounds__(kRowThreads) void topk_lds_kernel(
+    const float* __restrict__ scores, int N_cap, int n_q, const int32_t* __restrict__ q_pos, int m,
+    const int32_t* __restrict__ n_entries, int k, int32_t* __restrict__ idx) {
+  extern __shared__ uint32_t keys[];
+  __shared__ uint32_t hist[256];
+  __shared__ int sh_bin, sh_above;
+  __shared__ uint32_t wgt[kRowThreads / 64], weq[kRowThreads / 64];
+  const long long row = blockIdx.x;
+  const int b = static_cast<int>(row / n_q);
+  const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
+  int32_t* out = idx + row * k;
+  const int tid = threadIdx.x;
+  if (vis <= k) {
+    for (int i = tid; i < k; i += kRowThreads) out[i] = i < vis ? i : -1;
+    return;
+  }
+  const float* src = scores + row * N_cap;
+  for (int i = tid; i < vis; i += kRowThreads) keys[i] = score_key(src[i]);
+
+  uint32_t prefix = 0, mask = 0;
+  int remaining = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += kRowThreads) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < vis; i += kRowThreads) {
+      const uint32_t key = keys[i];
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xffu], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) find_bin_wave(hist, 256, remaining, &sh_bin, &sh_above);
+    __syncthreads();
+    prefix |= static_cast<uint32_t>(sh_bin) << shift;
+    mask |= 0xffu << shift;
+    remaining -= sh_above;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  const int need_eq = remaining;
+
+  // compaction in index order
+  const int lane = tid & 63, wv = tid >> 6;
+  int run_gt = 0, run_eq = 0;
+  for (int base = 0; base < vis; base += kRowThreads) {
+    const int i = base + tid;
+    const uint32_t key = i < vis ? keys[i] : 0u;
+    const bool gt = i < vis && key > T;
+    const bool eq = i < vis && key == T;
+    const uint64_t bg = __ballot(gt), be = __ballot(eq);
+    if (lane == 0) {
+      wgt[wv] = __popcll(bg);
+      weq[wv] = __popcll(be);
+    }
+    __syncthreads();
+    int off_gt = run_gt, off_eq = run_eq, tot_gt = 0, tot_eq = 0;
+    for (int x = 0; x < kRowThreads / 64; ++x) {
+      if (x < wv) {
+        off_gt += wgt[x];
+        off_eq += weq[x];
+      }
+      tot_gt += wgt[x];
+      tot_eq += weq[x];
+    }
+    const int gt_before = off_gt + lanes_below(bg);
+    const int eq_before = off_eq + lanes_below(be);
+    const int pos = gt_before + min(eq_before, need_eq);
+    if ((gt || (eq && eq_before < need_eq)) && pos < k) out[pos] = i;
+    run_gt += tot_gt;
+    run_eq += tot_eq;
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// histogram path for long rows
+
+struct WideWs {
+  uint32_t* hist;      // [rows, 4096]
+  int32_t* sure;       // [rows, n_seg, k]
+  uint32_t* cand_key;  // [rows, n_seg, kSeg]
+  int32_t* cand_idx;   // [rows, n_seg, kSeg]
+  int32_t* sure_cnt;   // [rows, n_seg]
+  int32_t* cand_cnt;   // [rows, n_seg]
+};
+
+// Workspace carve-up; every array starts on a 256-byte boundary.
+struct WideLayout {
+  size_t hist, sure, cand_key, cand_idx, sure_cnt, cand_cnt, total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+inline WideLayout wide_layout(long long rows, int n_seg, int k) {
+  WideLayout L;
+  const size_t r = static_cast<size_t>(rows), ns = static_cast<size_t>(n_seg);
+  size_t off = 0;
+  L.hist = off;     off += align256(r * kHistBins * 4);
+  L.sure = off;     off += align256(r * ns * static_cast<size_t>(k) * 4);
+  L.cand_key = off; off += align256(r * ns * kSeg * 4);
+  L.cand_idx = off; off += align256(r * ns * kSeg * 4);
+  L.sure_cnt = off; off += align256(r * ns * 4);
+  L.cand_cnt = off; off += align256(r * ns * 4);
+  L.total = off;
+  return L;
+}
+
+inline WideWs wide_ws(void* base, long long rows, int n_seg, int k) {
+  const WideLayout L = wide_layout(rows, n_seg, k);
+  char* p = static_cast<char*>(base);
+  WideWs w;
+  w.hist = reinterpret_cast<uint32_t*>(p + L.hist);
+  w.sure = reinterpret_cast<int32_t*>(p + L.sure);
+  w.cand_key = reinterpret_cast<uint32_t*>(p + L.cand_key);
+  w.cand_idx = reinterpret_cast<int32_t*>(p + L.cand_idx);
+  w.sure_cnt = reinterpret_cast<int32_t*>(p + L.sure_cnt);
+  w.cand_cnt = reinterpret_cast<int32_t*>(p + L.cand_cnt);
+  return w;
+}
+
+__global__ void zero_u32_kernel(uint32_t* p, long long n) {
+  const long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+__global__ __launch_bounds__(kSegThreads) void topk_hist_kernel(
+    const float* __restrict__ scores, int N_cap, int n_q, const int32_t* __restrict__ q_pos, int m,
+    const int32_t* __restrict__ n_entries, int k, int n_seg, uint32_t* __restrict__ ghist) {
+  __shared__ uint32_t h[kHistBins];
+  const long long row = blockIdx.x / n_seg;
+  const int seg = blockIdx.x % n_seg;
+  const int b = static_cast<int>(row / n_q);
+  const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
+  if (vis <= k) return;
+  const int s0 = seg * kSeg;
+  if (s0 >= vis) return;
+  const int s1 = min(s0 + kSeg, vis);
+  for (int i = threadIdx.x; i < kHistBins; i += kSegThreads) h[i] = 0;
+  __syncthreads();
+  const float* src = scores + row * N_cap;
+  for (int i = s0 + threadIdx.x; i < s1; i += kSegThreads) atomicAdd(&h[score_key(src[i]) >> 20], 1u);
+  __syncthreads();
+  uint32_t* gh = ghist + row * kHistBins;
+  for (int i = threadIdx.x; i < kHistBins; i += kSegThreads)
+    if (h[i]) atomicAdd(&gh[i], h[i]);
+}
+
+// (bin, count above bin) of the k-th largest key of a row; bin = -1 when every
+// visible entry is selected.
+__device__ void row_threshold(const uint32_t* gh, int vis, int k, int* sh_bin, int* sh_above) {
+  if (vis <= k) {
+    if (threadIdx.x == 0) {
+      *sh_bin = -1;
+      *sh_above = vis;
+    }
+    return;
+  }
+  if (threadIdx.x < 64) find_bin_wave(gh, kHistBins, k, sh_bin, sh_above);
+}
+
+__global__ __launch_bounds__(kSegThreads) void topk_collect_kernel(
+    const float* __restrict__ scores, int N_cap, int n_q, const int32_t* __restrict__ q_pos, int m,
+    const int32_t* __restrict__ n_entries, int k, int n_seg, WideWs ws) {
+  __shared__ int sh_bin, sh_above;
+  __shared__ uint32_t wsure[kSegThreads / 64], wcand[kSegThreads / 64];
+  const long long row = blockIdx.x / n_seg;
+  const int seg = blockIdx.x % n_seg;
+  const int b = static_cast<int>(row / n_q);
+  const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
+  const int s0 = seg * kSeg;
+  const int s1 = min(s0 + kSeg, vis);
+  const long long rs = row * n_seg + seg;
+  row_threshold(ws.hist + row * kHistBins, vis, k, &sh_bin, &sh_above);
+  __syncthreads();
+  const int bstar = sh_bin;
+  const float* src = scores + row * N_cap;
+  int32_t* sure = ws.sure + rs * k;
+  uint32_t* ckey = ws.cand_key + rs * kSeg;
+  int32_t* cidx = ws.cand_idx + rs * kSeg;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int run_s = 0, run_c = 0;
+  for (int base = s0; base < s1; base += kSegThreads) {
+    const int i = base + tid;
+    const uint32_t key = i < s1 ? score_key(src[i]) : 0u;
+    const int bin = static_cast<int>(key >> 20);
+    const bool is_s = i < s1 && bin > bstar;
+    const bool is_c = i < s1 && bin == bstar;
+    const uint64_t bs = __ballot(is_s), bc = __ballot(is_c);
+    if (lane == 0) {
+      wsure[wv] = __popcll(bs);
+      wcand[wv] = __popcll(bc);
+    }
+    __syncthreads();
+    int os = run_s, oc = run_c, ts = 0, tc = 0;
+    for (int x = 0; x < kSegThreads / 64; ++x) {
+      if (x < wv) {
+        os += wsure[x];
+        oc += wcand[x];
+      }
+      ts += wsure[x];
+      tc += wcand[x];
+    }
+    const int ps = os + lanes_below(bs);
+    if (is_s && ps < k) sure[ps] = i;
+    if (is_c) {
+      const int p = oc + lanes_below(bc);
+      ckey[p] = key;
+      cidx[p] = i;
+    }
+    run_s += ts;
+    run_c += tc;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    ws.sure_cnt[rs] = s0 < vis ? run_s : 0;
+    ws.cand_cnt[rs] = s0 < vis ? run_c : 0;
+  }
+}
+
+__device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+constexpr int kMaxK = 4096;
+constexpr int kMaxSeg = 1024;
+
+__global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
+    int N_cap, int n_q, const int32_t* __restrict__ q_pos, int m, const int32_t* __restrict__ n_entries, int k,
+    int n_seg, WideWs ws, int32_t* __restrict__ idx) {
+  __shared__ int32_t S[kMaxK], Ch[kMaxK];
+  __shared__ int seg_s[kMaxSeg + 1], seg_c[kMaxSeg + 1];
+  __shared__ uint32_t hist[256];
+  __shared__ int sh_bin, sh_above, sh_b2, sh_a2;
+  __shared__ uint32_t wgt[kRowThreads / 64], weq[kRowThreads / 64];
+  const long long row = blockIdx.x;
+  const int b = static_cast<int>(row / n_q);
+  const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int32_t* out = idx + row * k;
+  row_threshold(ws.hist + row * kHistBins, vis, k, &sh_bin, &sh_above);
+  if (tid == 0) {
+    int a = 0, c = 0;
+    for (int s = 0; s < n_seg; ++s) {
+      seg_s[s] = a;
+      seg_c[s] = c;
+      a += ws.sure_cnt[row * n_seg + s];
+      c += ws.cand_cnt[row * n_seg + s];
+    }
+    seg_s[n_seg] = a;
+    seg_c[n_seg] = c;
+  }
+  __syncthreads();
+  const int nS = seg_s[n_seg];
+  // gather the surely selected indices (already ascending per segment)
+  for (int s = 0; s < n_seg; ++s) {
+    const int cnt = seg_s[s + 1] - seg_s[s];
+    const int32_t* src = ws.sure + (row * n_seg + s) * k;
+    for (int i = tid; i < cnt; i += kRowThreads)
+      if (seg_s[s] + i < kMaxK) S[seg_s[s] + i] = src[i];
+  }
+  const int need = vis <= k ? 0 : k - sh_above;
+  int nC = 0;
+  if (need > 0) {
+    // radix select among the candidates on the low 20 key bits (8, 8, 4)
+    uint32_t prefix = 0, mask = 0;
+    int remaining = need;
+    const int shifts[3] = {12, 4, 0};
+    const int widths[3] = {8, 8, 4};
+    for (int p = 0; p < 3; ++p) {
+      const int sh = shifts[p];
+      const uint32_t dm = (1u << widths[p]) - 1u;
+      for (int i = tid; i < 256; i += kRowThreads) hist[i] = 0;
+      __syncthreads();
+      for (int s = 0; s < n_seg; ++s) {
+        const int cnt = seg_c[s + 1] - seg_c[s];
+        const uint32_t* ck = ws.cand_key + (row * n_seg + s) * kSeg;
+        for (int i = tid; i < cnt; i += kRowThreads) {
+          const uint32_t key = ck[i];
+          if ((key & mask) == prefix) atomicAdd(&hist[(key >> sh) & dm], 1u);
+        }
+      }
+      __syncthreads();
+      if (tid < 64) find_bin_wave(hist, 256, remaining, &sh_b2, &sh_a2);
+      __syncthreads();
+      prefix |= static_cast<uint32_t>(sh_b2) << sh;
+      mask |= dm << sh;
+      remaining -= sh_a2;
+      __syncthreads();
+    }
+    // every candidate shares the top 12 bits, so compare the low 20 only
+    const uint32_t T = prefix;
+    const int need_eq = remaining;
+    int run_gt = 0, run_eq = 0;
+    for (int s = 0; s < n_seg; ++s) {
+      const int cnt = seg_c[s + 1] - seg_c[s];
+      const uint32_t* ck = ws.cand_key + (row * n_seg + s) * kSeg;
+      const int32_t* ci = ws.cand_idx + (row * n_seg + s) * kSeg;
+      for (int base = 0; base < cnt; base += kRowThreads) {
+        const int i = base + tid;
+        const uint32_t key = i < cnt ? (ck[i] & 0xfffffu) : 0u;
+        const bool gt = i < cnt && key > T;
+        const bool eq = i < cnt && key == T;
+        const uint64_t bg = __ballot(gt), be = __ballot(eq);
+        if (lane == 0) {
+          wgt[wv] = __popcll(bg);
+          weq[wv] = __popcll(be);
+        }
+        __syncthreads();
+        int og = run_gt, oe = run_eq, tg = 0, te = 0;
+        for (int x = 0; x < kRowThreads / 64; ++x) {
+          if (x < wv) {
+            og += wgt[x];
+            oe += weq[x];
+          }
+          tg += wgt[x];
+          te += weq[x];
+        }
+        const int gb = og + lanes_below(bg), eb = oe + lanes_below(be);
+        const int pc = gb + min(eb, need_eq);
+        if ((gt || (eq && eb < need_eq)) && pc < need) Ch[pc] = ci[i];
+        run_gt += tg;
+        run_eq += te;
+        __syncthreads();
+      }
+    }
+    nC = need;
+  }
+  __syncthreads();
+  // merge the two ascending lists
+  const int nSc = min(nS, k);
+  for (int i = tid; i < nSc; i += kRowThreads) {
+    const int pos = i + lower_bound_i32(Ch, nC, S[i]);
+    if (pos < k) out[pos] = S[i];
+  }
+  for (int i = tid; i < nC; i += kRowThreads) {
+    const int pos = i + lower_bound_i32(S, nSc, Ch[i]);
+    if (pos < k) out[pos] = Ch[i];
+  }
+  for (int i = nSc + nC + tid; i < k; i += kRowThreads) out[i] = -1;
+}
+
+}  // namespace
+
+static int n_segments(int N_cap) { return (N_cap + kSeg - 1) / kSeg; }
+
+size_t topk_workspace_bytes(int B, int n_q, int N_cap, int k) {
+  if (N_cap <= kLdsMaxRow) return 0;
+  return wide_layout(static_cast<long long>(B) * n_q, n_segments(N_cap), k).total;
+}
+
+hipError_t launch_topk(int B, int n_q, int N_cap, const float* scores, const int32_t* q_pos, int m,
+                       const int32_t* n_entries, int k, int32_t* idx, void* ws, hipStream_t s) {
+  const long long rows = static_cast<long long>(B) * n_q;
+  if (rows == 0) return hipSuccess;
+  if (N_cap <= kLdsMaxRow) {
+    const size_t lds = sizeof(uint32_t) * static_cast<size_t>(N_cap > 0 ? N_cap : 1);
+    hipLaunchKernelGGL(topk_lds_kernel, dim3(static_cast<unsigned>(rows)), dim3(kRowThreads), lds, s,
+                       scores, N_cap, n_q, q_pos, m, n_entries, k, idx);
+    return hipGetLastError();
+  }
+  const int n_seg = n_segments(N_cap);
+  if (n_seg > kMaxSeg || k > kMaxK) return hipErrorInvalidValue;
+  WideWs w = wide_ws(ws, rows, n_seg, k);
+  const long long nh = rows * kHistBins;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(static_cast<unsigned>((nh + 255) / 256)), dim3(256), 0, s,
+                     w.hist, nh);
+  const dim3 g2(static_cast<unsigned>(rows * n_seg));
+  hipLaunchKernelGGL(topk_hist_kernel, g2, dim3(kSegThreads), 0, s, scores, N_cap, n_q, q_pos, m,
+                     n_entries, k, n_seg, w.hist);
+  hipLaunchKernelGGL(topk_collect_kernel, g2, dim3(kSegThreads), 0, s, scores, N_cap, n_q, q_pos, m,
+                     n_entries, k, n_seg, w);
+  hipLaunchKernelGGL(topk_finish_kernel, dim3(static_cast<unsigned>(rows)), dim3(kRowThreads), 0, s,
+                     N_cap, n_q, q_pos, m, n_entries, k, n_seg, w, idx);
+  return hipGetLastError();
+}
+
+}  // namespace lca

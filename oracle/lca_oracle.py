@@ -195,6 +195,22 @@ def compress(C, Z, P, m: int, overlap: bool, prevC=None, prevZ=None) -> np.ndarr
     return (gate_softmax(logits) * cand).sum(axis=1)
 
 
+def compress_error_bound(C, Z, P, m: int, overlap: bool, prevC=None, prevZ=None,
+                         eps: float = 1e-6) -> np.ndarray:
+    """Bound on the error of an fp32 evaluation of rmsnorm(compress(...)), before
+    the storage cast.  The pooled value sum_j p_j C_j is a sum of W terms whose
+    weights carry a few ulps of exp/division error, so its absolute error is at
+    most gamma(2W + 32) * sum_j p_j |C_j|; the RMSNorm scale multiplies it.  Near
+    zero (cancelling terms) this exceeds an ulp of the stored value."""
+    C = np.asarray(C, np.float64)
+    E = compress(C, Z, P, m, overlap, prevC, prevZ)
+    E_abs = compress(np.abs(C), Z, P, m, overlap,
+                     None if prevC is None else np.abs(np.asarray(prevC, np.float64)), prevZ)
+    W = 2 * m if overlap else m
+    r = 1.0 / np.sqrt(np.mean(E * E, axis=-1, keepdims=True) + eps)
+    return gamma(2 * W + 32) * E_abs * r
+
+
 def visible(q_pos, m: int, n_entries) -> np.ndarray:
     """Number of entries visible at position t: entry s needs (s+1)*m-1 <= t."""
     return np.minimum((np.asarray(q_pos, np.int64) + 1) // m, n_entries)
@@ -208,8 +224,8 @@ def index_scores(qI, kI, w, vis) -> np.ndarray:
     w [nq, H_I]."""
     qI = np.asarray(qI, np.float64)
     kI = np.asarray(kI, np.float64)
-    dots = np.einsum("thd,sd->ths", qI, kI)
-    I = np.einsum("th,ths->ts", np.asarray(w, np.float64), np.maximum(dots, 0.0))
+    dots = qI @ kI.T                                          # [nq, H_I, N]
+    I = (np.asarray(w, np.float64)[:, None, :] @ np.maximum(dots, 0.0))[:, 0, :]
     cols = np.arange(kI.shape[0])[None, :]
     return np.where(cols < np.asarray(vis)[:, None], I, -np.inf)
 
@@ -223,7 +239,9 @@ def score_error_bound(qI, kI, w, d_terms: int = 0) -> np.ndarray:
     n = qI.shape[-1] + qI.shape[-2] + 2 + d_terms
     u = 2.0 ** -24
     gamma = n * u / (1 - n * u)
-    return gamma * np.einsum("th,thd,sd->ts", np.asarray(w, np.float64), qI, kI)
+    # sum_h w_h sum_d |q_hd| |k_sd| = sum_d (sum_h w_h |q_hd|) |k_sd|
+    wq = (np.asarray(w, np.float64)[:, None, :] @ qI)[:, 0, :]  # [nq, d_I]
+    return gamma * (wq @ kI.T)
 
 
 def _select_key(s) -> np.ndarray:
@@ -290,13 +308,16 @@ def window_positions(t: int, n_win: int) -> np.ndarray:
 
 def prefill_layer(*, mode, m, k, n_win, tau, eps, kv_fmt, out_fmt, pos0,
                   C, Z, P, q, cache_prefix, prevC=None, prevZ=None, win_prefix=None,
-                  qI=None, kI=None, w=None, queries=None, sink=None):
+                  qI=None, kI=None, w=None, queries=None, sink=None, idx_given=None):
     """One sequence of CSA ("csa") or HCA ("hca") prefill.
 
     New tokens occupy positions pos0 .. pos0+n-1 (pos0 % m == 0).  cache_prefix
     [pos0/m, c] holds the stored entries of the prefix, win_prefix the stored
     window KV of the n_win-1 prefix positions before pos0.  `queries` selects which
-    new tokens to evaluate (default all).  Returns a dict of float64 results.
+    new tokens to evaluate (default all); q, qI and w are indexed per query, so
+    they may be lazy row accessors.  idx_given ([len(queries), k]) makes the
+    attention use those selections instead of the oracle's own (the oracle's
+    scores and selections are still returned).  Returns float64 results.
     """
     C = np.asarray(C, np.float64)
     n, c = C.shape
@@ -305,12 +326,13 @@ def prefill_layer(*, mode, m, k, n_win, tau, eps, kv_fmt, out_fmt, pos0,
     Khat = np.concatenate([np.asarray(cache_prefix, np.float64).reshape(-1, c), entries_new], 0)
     U_new = round_to(rmsnorm(C, eps), kv_fmt)
     n_pre_win = 0 if win_prefix is None else len(win_prefix)
+    bound = compress_error_bound(C, Z, P, m, mode == "csa", prevC, prevZ, eps)
     U = U_new if win_prefix is None else np.concatenate([np.asarray(win_prefix, np.float64), U_new], 0)
     win_origin = pos0 - n_pre_win
-    qhat = rmsnorm(np.asarray(q, np.float64), eps)             # [n, H, c], per head
     queries = np.arange(n) if queries is None else np.asarray(queries)
-    H = qhat.shape[1]
-    res = {"entries": entries_new, "out": np.zeros((len(queries), H, c)),
+    H = np.asarray(q[int(queries[0])]).shape[0] if len(queries) else 0
+    res = {"entries": entries_new, "entries_bound": bound, "window": U_new,
+           "out": np.zeros((len(queries), H, c)),
            "lse": np.zeros((len(queries), H)), "idx": None, "scores": None}
     if mode == "csa":
         res["idx"] = np.full((len(queries), k), -1, np.int32)
@@ -319,18 +341,20 @@ def prefill_layer(*, mode, m, k, n_win, tau, eps, kv_fmt, out_fmt, pos0,
         t = pos0 + int(i)
         vis = int(visible([t], m, len(Khat))[0])
         if mode == "csa":
-            I = index_scores(np.asarray(qI, np.float64)[i][None], kI[:vis], np.asarray(w)[i][None],
-                             [vis])
+            I = index_scores(np.asarray(qI[i], np.float64)[None], kI[:vis],
+                             np.asarray(w[i], np.float64)[None], [vis])
             sel = topk(I, [vis], k)[0]
             res["idx"][r] = sel
             res["scores"].append(I[0])
-            S = sel[sel >= 0]
+            use = sel if idx_given is None else np.asarray(idx_given[r])
+            S = use[use >= 0]
         else:
             S = np.arange(vis)
         W = window_positions(t, n_win) - win_origin
         assert W.min() >= 0, "window reaches before the provided window KV"
-        part_c = attend(qhat[i], Khat[S], tau)
-        part_w = attend(qhat[i], U[W], tau)
+        qhat = rmsnorm(np.asarray(q[i], np.float64), eps)          # per head
+        part_c = attend(qhat, Khat[S], tau)
+        part_w = attend(qhat, U[W], tau)
         o, lse = merge([part_c, part_w], sink)
         res["out"][r] = round_to(o, out_fmt)
         res["lse"][r] = lse
@@ -349,7 +373,9 @@ class DecodeState:
     L: tokens seen.  cur: (C, Z) rows of the incomplete block (L % m rows).
     prev: (C, Z) rows of the last complete block (CSA overlap) or None.
     window: the stored window KV of the last n_win-1 or fewer tokens.
-    entries: stored compressed entries, [N, c].
+    entries: stored compressed entries present before the first step -- any
+    object with len() whose [index array] gives float64 rows; entries that
+    decode steps create are kept in `new`.
     """
 
     def __init__(self, *, mode, m, n_win, c, L=0, cur=None, prev=None, window=None, entries=None):
@@ -357,19 +383,38 @@ class DecodeState:
         self.L = L
         self.cur = cur if cur is not None else (np.zeros((0, c)), np.zeros((0, c)))
         self.prev = prev
-        self.window = deque(list(window) if window is not None else [], maxlen=n_win - 1 if n_win > 1 else 0)
-        self.entries = np.zeros((0, c)) if entries is None else np.asarray(entries, np.float64)
+        self.window = deque(list(window) if window is not None else [],
+                            maxlen=n_win - 1 if n_win > 1 else 0)
+        self.base = np.zeros((0, c)) if entries is None else entries
+        self.new = []
+
+    @property
+    def n_entries(self) -> int:
+        return len(self.base) + len(self.new)
+
+    def rows(self, S) -> np.ndarray:
+        """Stored entries at the indices S, float64 [len(S), c]."""
+        S = np.asarray(S, np.int64)
+        nb = len(self.base)
+        out = np.zeros((len(S), self.c))
+        old = S < nb
+        if old.any():
+            out[old] = np.asarray(self.base[S[old]], np.float64).reshape(-1, self.c)
+        for r in np.nonzero(~old)[0]:
+            out[r] = self.new[S[r] - nb]
+        return out
 
 
 def decode_step(st: DecodeState, *, tokC, tokZ, P, q, tau, eps, kv_fmt, out_fmt, k=0,
-                qI=None, kI=None, w=None, sink=None):
+                qI=None, kI=None, w=None, sink=None, idx_given=None):
     """Append one token and answer its query (the step of a decode loop).
 
     The token goes to the incomplete block and its normalised KV to the window;
     when its block completes, the block is compressed into a new entry (with the
     previous block as overlap for CSA).  The query at the token's position then
     attends top-k (CSA) or all (HCA) visible entries plus the window.
-    kI holds the indexer keys of all entries including a new one."""
+    kI holds the indexer keys of all entries including a new one.  idx_given makes
+    the attention use that selection instead of the oracle's own."""
     m, c = st.m, st.c
     t = st.L
     tokC = np.asarray(tokC, np.float64).reshape(c)
@@ -378,7 +423,7 @@ def decode_step(st: DecodeState, *, tokC, tokZ, P, q, tau, eps, kv_fmt, out_fmt,
     curZ = np.concatenate([st.cur[1], tokZ[None]], 0)
     u_t = round_to(rmsnorm(tokC, eps), kv_fmt)
     win_rows = np.array(list(st.window) + [u_t]).reshape(-1, c)
-    new_entry = None
+    new_entry = new_bound = None
     if (t + 1) % m == 0:
         if st.mode == "csa":
             pc, pz = (None, None) if st.prev is None else st.prev
@@ -386,7 +431,11 @@ def decode_step(st: DecodeState, *, tokC, tokZ, P, q, tau, eps, kv_fmt, out_fmt,
         else:
             E = compress(curC, curZ, P, m, False)
         new_entry = round_to(rmsnorm(E, eps), kv_fmt)[0]
-        st.entries = np.concatenate([st.entries, new_entry[None]], 0)
+        if st.mode == "csa":
+            new_bound = compress_error_bound(curC, curZ, P, m, True, pc, pz, eps)[0]
+        else:
+            new_bound = compress_error_bound(curC, curZ, P, m, False, eps=eps)[0]
+        st.new.append(new_entry)
         st.prev = (curC, curZ)
         st.cur = (np.zeros((0, c)), np.zeros((0, c)))
     else:
@@ -394,18 +443,20 @@ def decode_step(st: DecodeState, *, tokC, tokZ, P, q, tau, eps, kv_fmt, out_fmt,
     if st.window.maxlen:
         st.window.append(u_t)
     st.L = t + 1
-    vis = int(visible([t], m, len(st.entries))[0])
+    vis = int(visible([t], m, st.n_entries)[0])
     qhat = rmsnorm(np.asarray(q, np.float64), eps)
-    res = {"new_entry": new_entry, "window_row": u_t, "idx": None, "scores": None}
+    res = {"new_entry": new_entry, "new_entry_bound": new_bound, "window_row": u_t, "idx": None,
+           "scores": None}
     if st.mode == "csa":
         I = index_scores(np.asarray(qI, np.float64)[None], np.asarray(kI, np.float64)[:vis],
                          np.asarray(w, np.float64)[None], [vis])
         sel = topk(I, [vis], k)[0]
         res["idx"], res["scores"] = sel, I[0]
-        S = sel[sel >= 0]
+        use = sel if idx_given is None else np.asarray(idx_given)
+        S = use[use >= 0]
     else:
         S = np.arange(vis)
-    part_c = attend(qhat, st.entries[S], tau)
+    part_c = attend(qhat, st.rows(S), tau)
     part_w = attend(qhat, win_rows, tau)
     o, lse = merge([part_c, part_w], sink)
     res["out"] = round_to(o, out_fmt)

@@ -1,0 +1,134 @@
+"""The C ABI library: it loads without a GPU, exports every function that
+include/lca.h declares, and rejects bad arguments with a status code before any
+HIP call (so these run on a CPU-only machine)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_attention_14_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lca.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lca_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("liblca.so is not built; run __graft_entry__.build()")
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in lca.h but not exported"
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_version_and_strings(L):
+    assert L.lca_version() == 1
+    for st in (0, -1, -2, -3, -4):
+        assert L.lca_status_string(st)
+    assert L.lca_status_string(7) == b"unknown status"
+    assert L.lca_kv_row_bytes(_lib.FMT["bf16"], 512) == 1024
+    assert L.lca_kv_row_bytes(_lib.FMT["fp8_bf16rope"], 512) == 576
+    assert L.lca_kv_row_bytes(_lib.FMT["f32"], 128) == 512
+    assert L.lca_kv_row_bytes(99, 128) == 0
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def test_compress_validation(L):
+    base = dict(mode=0, m=4, B=1, n_new=8, c=128, C=FAKE, Z=FAKE, io=0, pc=None, pz=None, P=FAKE,
+                cache=FAKE, kv=0, N_cap=2, first=0)
+
+    def call(**kw):
+        a = {**base, **kw}
+        return L.lca_compress(a["mode"], a["m"], a["B"], a["n_new"], a["c"], a["C"], a["Z"], a["io"],
+                              a["pc"], a["pz"], a["P"], a["cache"], a["kv"], a["N_cap"], a["first"],
+                              1e-6, None)
+
+    assert call(mode=5) == _lib.LCA_ERR_INVALID_ARG
+    assert call(n_new=6) == _lib.LCA_ERR_INVALID_ARG
+    assert b"multiple" in L.lca_last_error()
+    assert call(c=100) == _lib.LCA_ERR_UNSUPPORTED
+    assert call(io=2) == _lib.LCA_ERR_UNSUPPORTED
+    assert call(pc=FAKE) == _lib.LCA_ERR_INVALID_ARG
+    assert call(N_cap=1) == _lib.LCA_ERR_INVALID_ARG
+    assert call(C=None) == _lib.LCA_ERR_INVALID_ARG
+    assert call(B=0) == _lib.LCA_OK            # nothing to do: no launch
+    assert call(mode=1, pc=FAKE, pz=FAKE) == _lib.LCA_ERR_INVALID_ARG
+
+
+def test_indexer_topk_mqa_validation(L):
+    F = _lib.FMT
+    # fp8 indexer only for 64 x 128
+    assert L.lca_indexer_scores(1, 1, 32, 128, F["fp8"], FAKE, None, FAKE, None, 8, FAKE, FAKE, 4,
+                                FAKE, FAKE, None) == _lib.LCA_ERR_UNSUPPORTED
+    assert L.lca_indexer_scores(1, 1, 64, 128, F["mxfp4"], FAKE, None, FAKE, None, 8, FAKE, FAKE, 4,
+                                FAKE, FAKE, None) == _lib.LCA_ERR_INVALID_ARG
+    assert L.lca_indexer_scores(1, 1, 4, 32, 7, FAKE, None, FAKE, None, 8, FAKE, FAKE, 4, FAKE, FAKE,
+                                None) == _lib.LCA_ERR_UNSUPPORTED
+    # top-k: k range and workspace
+    assert L.lca_topk(1, 1, 100, FAKE, FAKE, 4, FAKE, 0, FAKE, None, 0, None) == _lib.LCA_ERR_INVALID_ARG
+    assert L.lca_topk(1, 1, 100, FAKE, FAKE, 4, FAKE, 5000, FAKE, None, 0, None) == _lib.LCA_ERR_INVALID_ARG
+    need = L.lca_topk_workspace_size(16, 1, 262148, 1024)
+    assert need > 0 and L.lca_topk_workspace_size(1, 8, 30000, 1024) == 0
+    assert L.lca_topk(16, 1, 262148, FAKE, FAKE, 4, FAKE, 1024, FAKE, FAKE, need - 1,
+                      None) == _lib.LCA_ERR_WORKSPACE
+    # attention: shape support and workspace
+    args = [1, 1, 64, 512, FAKE, F["bf16"], FAKE, F["bf16"], 1024, FAKE, 1024, FAKE, 4, FAKE, FAKE,
+            128, 0, 128, 0.04, 1e-6, None, FAKE, F["bf16"], None]
+    need = L.lca_sparse_mqa_workspace_size(1, 1, 64, 512, F["bf16"], 1024, 1024, 128, 0)
+    assert need > 0
+    assert L.lca_sparse_mqa(*args, None, 0, None) == _lib.LCA_ERR_WORKSPACE
+    bad = list(args)
+    bad[2] = 12
+    assert L.lca_sparse_mqa(*bad, FAKE, need, None) == _lib.LCA_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[3] = 384
+    assert L.lca_sparse_mqa(*bad, FAKE, need, None) == _lib.LCA_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[14] = None          # window buffer missing with n_win > 0
+    assert L.lca_sparse_mqa(*bad, FAKE, need, None) == _lib.LCA_ERR_INVALID_ARG
+
+
+def test_state_and_decode_validation(L):
+    F = _lib.FMT
+    assert L.lca_state_append(0, 4, 1, 512, 0, FAKE, FAKE, F["bf16"], FAKE, FAKE, FAKE, F["bf16"],
+                              FAKE, FAKE, 8, FAKE, FAKE, FAKE, 1e-6, None) == _lib.LCA_ERR_INVALID_ARG
+    lay = _lib.DecodeLayer()
+    lay.struct_size = 3                          # wrong struct size
+    assert L.lca_decode_workspace_size(ctypes.byref(lay)) == 0
+    lay.struct_size = ctypes.sizeof(_lib.DecodeLayer)
+    lay.mode, lay.m, lay.B, lay.c, lay.H, lay.n_win, lay.N_cap = 0, 4, 2, 512, 64, 128, 70000
+    lay.io_dtype, lay.kv_dtype, lay.k, lay.H_I, lay.d_I, lay.idx_dtype = 1, 1, 1024, 64, 128, 2
+    need = L.lca_decode_workspace_size(ctypes.byref(lay))
+    assert need > 2 * 70000 * 4
+    io = _lib.DecodeIO()
+    io.struct_size = ctypes.sizeof(_lib.DecodeIO)
+    assert L.lca_decode_step(ctypes.byref(lay), ctypes.byref(io), FAKE, need - 1,
+                             None) == _lib.LCA_ERR_WORKSPACE
+    assert L.lca_decode_step(ctypes.byref(lay), ctypes.byref(io), FAKE, need,
+                             None) == _lib.LCA_ERR_INVALID_ARG       # CSA without kI/qI/w
+    lay.k = 0
+    assert L.lca_decode_workspace_size(ctypes.byref(lay)) == 0
+
+
+def test_no_cpu_fallback_in_binding():
+    """The binding must raise when the library is missing, never compute on the CPU."""
+    src = open(os.path.join(ROOT, "long_context_attention_14_amd", "ops.py")).read()
+    for name in ("oracle", "numpy", "np."):
+        assert name not in src
+    src = open(os.path.join(ROOT, "long_context_attention_14_amd", "_lib.py")).read()
+    assert "no fallback" in src

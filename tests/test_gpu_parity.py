@@ -1,0 +1,389 @@
+"""GPU parity of every step of the path against the float64 oracle, through the
+C ABI.  Tolerances: outputs within 1e-4 (fp32 I/O) or 2e-2 (bf16 I/O) max
+absolute error; stored entries and window rows within one ulp of their storage
+format plus the oracle's fp32-evaluation bound (fp32: 1e-5); indexer scores within the fp32 evaluation bound; top-k
+indices bit-exact on the select stage and on every certified row."""
+import numpy as np
+import pytest
+import torch
+
+import oracle_side as OS
+from long_context_attention_14_amd import ops, pipeline
+from oracle import lca_oracle as O
+from synth import encode as enc
+from synth import gen
+from synth.configs import (CSA_DECODE_1M, CSA_PREFILL_CHUNK, HCA_DECODE, HYBRID_DECODE_1M,
+                           TINY_CSA_PREFILL)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+OUT_TOL = {"f32": 1e-4, "bf16": 2e-2}
+LSE_TOL = {"f32": 1e-5, "bf16": 2e-3}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def T(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def out_f64(t):
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return host(t).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# top-k on adversarial score arrays (select stage, bit-exact)
+
+
+def _scores(kind, rows, N, rng):
+    if kind == "ties":
+        s = rng.integers(-3, 4, (rows, N)).astype(np.float32)
+        s[:, ::7] = -0.0
+    elif kind == "normal":
+        s = rng.standard_normal((rows, N)).astype(np.float32)
+    elif kind == "constant":
+        s = np.full((rows, N), 1.5, np.float32)
+    elif kind == "special":
+        s = rng.standard_normal((rows, N)).astype(np.float32)
+        s[:, ::5] = np.nan
+        s[:, 1::11] = -np.inf
+        s[:, 2::13] = np.inf
+        s[:, 3::17] = -0.0
+        s[:, 4::17] = 0.0
+        s[:, 6::19] = np.float32(1e-45)     # denormal
+    else:
+        raise ValueError(kind)
+    return s
+
+
+@pytest.mark.parametrize("N,k,kind", [
+    (300, 32, "ties"), (4097, 1024, "normal"), (36864, 1024, "ties"), (20000, 4096, "special"),
+    (36865, 1024, "normal"), (100003, 1024, "ties"), (262148, 1024, "special"),
+    (262148, 1024, "constant"), (70000, 1, "normal")])
+def test_topk_select_stage_bit_exact(N, k, kind):
+    say(f"topk N={N} k={k} kind={kind}")
+    rng = np.random.default_rng(N + k)
+    B, n_q = 2, 3
+    s = _scores(kind, B * n_q, N, rng)
+    vis = np.array([0, max(0, k - 1), k, min(N, k + 1), N, N - 3])[: B * n_q]
+    q_pos = T((vis - 1).astype(np.int32).reshape(B, n_q))
+    n_ent = T(np.full(B, N, np.int32))
+    idx = torch.full((B, n_q, k), -7, dtype=torch.int32, device=DEV)
+    ops.lca_topk(B, n_q, N, T(s.reshape(B, n_q, N)), q_pos, 1, n_ent, k, idx)
+    got = host(idx).reshape(B * n_q, k)
+    for r in range(B * n_q):
+        want = O.topk(s[r:r + 1].astype(np.float64), [vis[r]], k)[0]
+        assert np.array_equal(got[r], want), f"row {r} vis {vis[r]}"
+
+
+# ---------------------------------------------------------------------------
+# indexer
+
+
+@pytest.mark.parametrize("fmt,HI,dI", [("f32", 4, 32), ("f32", 16, 64), ("fp8", 64, 128),
+                                       ("mxfp4", 64, 128)])
+def test_indexer_scores_within_bound(fmt, HI, dI):
+    say(f"indexer {fmt} {HI}x{dI}")
+    rng = np.random.default_rng(7)
+    B, n_q, N, m = 2, 3, 5003, 4
+    qf = rng.standard_normal((B, n_q, HI, dI))
+    kf = rng.standard_normal((B, N, dI))
+    w = rng.random((B, n_q, HI)).astype(np.float32)
+    if fmt == "mxfp4":
+        qb, qs = enc.to_mxfp4(qf)
+        kb, ks = enc.to_mxfp4(kf)
+        qd, kd = O.decode_mxfp4(qb, qs), O.decode_mxfp4(kb, ks)
+        qs_t, ks_t = T(qs), T(ks)
+    else:
+        qb, kb = enc.encode(qf, fmt), enc.encode(kf, fmt)
+        qd, kd = O.decode(qb, fmt), O.decode(kb, fmt)
+        qs_t = ks_t = None
+    pos = np.array([[3, 100, 20011], [4 * N + 50, 0, 9999]], np.int32)[:, :n_q]
+    n_ent = np.array([N, N - 17], np.int32)
+    scores = torch.full((B, n_q, N), 12345.0, dtype=torch.float32, device=DEV)
+    ops.lca_indexer_scores(B, n_q, HI, dI, fmt, T(qb), qs_t, T(kb), ks_t, N, T(w), T(pos), m,
+                           T(n_ent), scores)
+    got = host(scores)
+    for b in range(B):
+        for t in range(n_q):
+            vis = int(O.visible([pos[b, t]], m, n_ent[b])[0])
+            ref = O.index_scores(qd[b, t][None], kd[b, :vis], w[b, t][None].astype(np.float64), [vis])[0]
+            bnd = O.score_error_bound(qd[b, t][None], kd[b, :vis], w[b, t][None].astype(np.float64))[0]
+            err = np.abs(got[b, t, :vis] - ref)
+            assert np.all(err <= bnd + 1e-30), f"b{b} t{t}: err {err.max():.3g}"
+            assert np.all(got[b, t, vis:] == 12345.0), "entries past vis were written"
+
+
+# ---------------------------------------------------------------------------
+# compressor and window KV
+
+
+@pytest.mark.parametrize("mode,m,io,kv,prev", [("csa", 4, "bf16", "bf16", True),
+                                               ("csa", 4, "f32", "f32", False),
+                                               ("hca", 128, "bf16", "bf16", False),
+                                               ("csa", 4, "bf16", "fp8_bf16rope", True),
+                                               ("hca", 8, "f32", "fp8_bf16rope", False)])
+def test_compress_entries(mode, m, io, kv, prev):
+    say(f"compress {mode} m={m} {io}->{kv} prev={prev}")
+    rng = np.random.default_rng(11)
+    B, c, n = 2, 512 if kv != "f32" else 128, 4 * m if m > 4 else 1028
+    C = enc.encode(rng.standard_normal((B, n, c)), io)
+    Z = enc.encode(rng.standard_normal((B, n, c)), io)
+    W = 2 * m if mode == "csa" else m
+    P = (rng.standard_normal((W, c)) * 0.1).astype(np.float32)
+    pC = enc.encode(rng.standard_normal((B, m, c)), io) if prev else None
+    pZ = enc.encode(rng.standard_normal((B, m, c)), io) if prev else None
+    first, N_cap = 3, 3 + n // m + 2
+    rb = ops.row_bytes(kv, c)
+    cache = torch.zeros(B * N_cap * rb, dtype=torch.uint8, device=DEV)
+    ops.lca_compress(mode, m, B, n, c, T(C), T(Z), io, T(pC) if prev else None,
+                     T(pZ) if prev else None, T(P), cache, kv, N_cap, first)
+    got = host(cache).reshape(B, N_cap, rb)
+    assert np.all(got[:, :first] == 0) and np.all(got[:, first + n // m:] == 0)
+    for b in range(B):
+        E = O.compress(O.decode(C[b], io), O.decode(Z[b], io), P, m, mode == "csa",
+                       O.decode(pC[b], io) if prev else None, O.decode(pZ[b], io) if prev else None)
+        want = O.round_to(O.rmsnorm(E), kv)
+        bound = O.compress_error_bound(O.decode(C[b], io), O.decode(Z[b], io), P, m, mode == "csa",
+                                       O.decode(pC[b], io) if prev else None,
+                                       O.decode(pZ[b], io) if prev else None)
+        gb = got[b, first:first + n // m]
+        g = O.decode(gb.view(np.float32) if kv == "f32" else gb.view(np.uint16) if kv == "bf16" else gb, kv)
+        OS.assert_within_ulp(g, want, kv, slack=bound, what=f"entries b{b}")
+
+
+@pytest.mark.parametrize("io,kv", [("bf16", "bf16"), ("f32", "f32"), ("bf16", "fp8_bf16rope")])
+def test_rmsnorm_rows(io, kv):
+    say(f"rmsnorm rows {io}->{kv}")
+    rng = np.random.default_rng(12)
+    B, n, c, ys = 3, 37, 512, 50
+    x = enc.encode(rng.standard_normal((B, n, c)) * 3, io)
+    rb = ops.row_bytes(kv, c)
+    y = torch.zeros(B * ys * rb, dtype=torch.uint8, device=DEV)
+    ops.lca_rmsnorm_rows(B, n, c, T(x), io, y, kv, ys)
+    got = host(y).reshape(B, ys, rb)
+    for b in range(B):
+        gb = got[b, :n]
+        g = O.decode(gb.view(np.float32) if kv == "f32" else gb.view(np.uint16) if kv == "bf16" else gb, kv)
+        OS.assert_within_ulp(g, O.round_to(O.rmsnorm(O.decode(x[b], io)), kv), kv, what=f"rows b{b}")
+        assert np.all(got[b, n:] == 0)
+
+
+# ---------------------------------------------------------------------------
+# whole prefill layers
+
+
+def _stored(arr_u8, fmt):
+    return arr_u8.view(np.float32) if fmt == "f32" else arr_u8.view(np.uint16) if fmt == "bf16" else arr_u8
+
+
+def run_prefill_parity(cfg, queries, check_entries=True):
+    d = gen.prefill_inputs(cfg)
+    layer = pipeline.PrefillLayer(cfg, d, DEV)
+    layer.run()
+    torch.cuda.synchronize()
+    scores = host(layer.scores)
+    idx = host(layer.idx)
+    out = out_f64(layer.out)
+    lse = host(layer.lse)
+    kv, io = cfg.kv_dtype, cfg.io_dtype
+    rb = ops.row_bytes(kv, cfg.c)
+    cache = host(layer.cache).view(np.uint8).reshape(cfg.B, layer.N_cap, rb)
+    n_cert = 0
+    for b in range(cfg.B):
+        ref = OS.oracle_prefill(cfg, d, b, queries)
+        if check_entries:
+            g = O.decode(_stored(cache[b, d["n_prefix"]:], kv), kv)
+            OS.assert_within_ulp(g, ref["entries"], kv, slack=ref["entries_bound"], what="new entries")
+        kI_sc = d.get("kI_scale")
+        kI = O.decode(d["kI"][b], cfg.idx_dtype, None if kI_sc is None else kI_sc[b])
+        qI_rows = OS.LazyRows(d["qI"][b], cfg.idx_dtype,
+                              None if d.get("qI_scale") is None else d["qI_scale"][b])
+        for r, i in enumerate(queries):
+            t = d["pos0"] + int(i)
+            vis = int(O.visible([t], cfg.m, layer.N_cap)[0])
+            bnd = O.score_error_bound(qI_rows[int(i)][None], kI[:vis], d["w"][b, i][None].astype(np.float64))[0]
+            n_cert += OS.check_selection(idx[b, i], scores[b, i], ref["scores"][r], bnd, vis, cfg.k,
+                                         what=f"b{b} q{i}")
+        ref2 = OS.oracle_prefill(cfg, d, b, queries, idx_given=idx[b, queries])
+        err = np.abs(out[b, queries] - ref2["out"])
+        assert err.max() <= OUT_TOL[io], f"out err {err.max():.3g}"
+        lerr = np.abs(lse[b, queries] - ref2["lse"])
+        assert lerr.max() <= LSE_TOL[io], f"lse err {lerr.max():.3g}"
+    say(f"{cfg.name}: {n_cert} of {cfg.B * len(queries)} rows certified")
+    return layer
+
+
+def test_tiny_csa_prefill_end_to_end():
+    say("tiny CSA prefill fp32")
+    run_prefill_parity(TINY_CSA_PREFILL, np.arange(TINY_CSA_PREFILL.n_new))
+
+
+def test_csa_prefill_chunk_reduced():
+    cfg = CSA_PREFILL_CHUNK.with_(ctx=8192, n_new=1024)
+    say(f"prefill {cfg.ctx}+{cfg.n_new}")
+    q = np.concatenate([np.arange(0, 1024, 37), [1023]])
+    run_prefill_parity(cfg, q)
+
+
+def test_csa_prefill_chunk_full_size_sampled():
+    cfg = CSA_PREFILL_CHUNK
+    say("prefill chunk 8192 on 131072, sampled rows")
+    q = np.array([0, 1, 2, 3, 1000, 4095, 4096, 8188, 8189, 8190, 8191])
+    run_prefill_parity(cfg, q, check_entries=True)
+
+
+# ---------------------------------------------------------------------------
+# decode steps
+
+
+def _decode_parity(cfg, d, seqs, layer=None):
+    if layer is None:
+        layer = pipeline.DecodeLayer(cfg, d, DEV)
+    layer.step()
+    torch.cuda.synchronize()
+    out = out_f64(layer.out)
+    lse = host(layer.lse)
+    idx = host(layer.idx)
+    ntok = host(layer.n_tokens)
+    io, kv, m = cfg.io_dtype, cfg.kv_dtype, d["m"]
+    rb = ops.row_bytes(kv, cfg.c)
+    cache = host(layer.cache).view(np.uint8).reshape(cfg.B, d["n_cap"], rb)
+    ring = host(layer.ring).view(np.uint8).reshape(cfg.B, cfg.n_win, rb)
+    assert np.array_equal(ntok, d["n_tokens"] + 1)
+    n_cert = 0
+    for b in seqs:
+        ref = OS.oracle_decode(cfg, d, b)
+        p = int(d["n_tokens"][b])
+        OS.assert_within_ulp(O.decode(_stored(ring[b, p % cfg.n_win], kv), kv), ref["window_row"], kv,
+                             what="ring row")
+        if ref["new_entry"] is not None:
+            s = (p + 1) // m - 1
+            OS.assert_within_ulp(O.decode(_stored(cache[b, s], kv), kv), ref["new_entry"], kv,
+                                 slack=ref["new_entry_bound"], what="new entry")
+        if d["kind"] == "C":
+            vis = (p + 1) // m
+            sel = idx[b]
+            # selection: certified rows bit-exact against the oracle's own top-k
+            st = ref["state"]
+            sc = d.get("kI_scale")
+            kI = O.decode(d["kI"][b, :vis], cfg.idx_dtype, None if sc is None else sc[b, :vis])
+            qI = O.decode(d["qI"][b], cfg.idx_dtype, None if d.get("qI_scale") is None else d["qI_scale"][b])
+            bnd = O.score_error_bound(qI[None], kI, d["w"][b][None].astype(np.float64))[0]
+            osel = ref["idx"]
+            if OS.certified(ref["scores"], bnd, vis, cfg.k):
+                assert np.array_equal(sel, osel), f"b{b}: certified row selects differently"
+                n_cert += 1
+            ref = OS.oracle_decode(cfg, d, b, idx_given=sel)
+        err = np.abs(out[b] - ref["out"])
+        assert err.max() <= OUT_TOL[io], f"b{b}: out err {err.max():.3g}"
+        lerr = np.abs(lse[b] - ref["lse"])
+        assert lerr.max() <= LSE_TOL[io], f"b{b}: lse err {lerr.max():.3g}"
+    say(f"{cfg.name}: {n_cert} of {len(seqs)} CSA rows certified")
+    return layer
+
+
+@pytest.mark.parametrize("ctx", [1 << 14, 1 << 18])
+def test_csa_decode_reduced(ctx):
+    cfg = CSA_DECODE_1M.with_(B=4, ctx=ctx)
+    say(f"CSA decode B=4 ctx={ctx}")
+    d = gen.decode_inputs(cfg)
+    _decode_parity(cfg, d, range(cfg.B))
+
+
+def test_csa_decode_1m_full_size_sampled():
+    cfg = CSA_DECODE_1M
+    say("CSA decode 1M B=16 (sampled sequences)")
+    d = gen.decode_inputs(cfg)
+    _decode_parity(cfg, d, [0, 7, 15])
+
+
+def test_hca_decode_full_size():
+    cfg = HCA_DECODE
+    say("HCA decode B=32 131072")
+    d = gen.decode_inputs(cfg)
+    _decode_parity(cfg, d, range(cfg.B))
+
+
+def test_hybrid_decode_reduced_all_layers():
+    cfg = HYBRID_DECODE_1M.with_(ctx=1 << 16)
+    say("hybrid decode 8 layers ctx 65536")
+    for i, d in enumerate(gen.hybrid_inputs(cfg)):
+        say(f"  layer {i} {d['kind']}")
+        lc = cfg.with_(m=d["m"]) if d["kind"] == "H" else cfg
+        _decode_parity(lc, d, range(cfg.B))
+
+
+def test_decode_multi_step_matches_oracle_stepping():
+    """Nine steps of a CSA and an HCA layer (blocks complete along the way)."""
+    for cfg in (CSA_DECODE_1M.with_(B=2, ctx=4096), HCA_DECODE.with_(B=2, ctx=1024, m=8)):
+        say(f"multi-step {cfg.name}")
+        d = gen.decode_inputs(cfg, extra_entries=4)
+        layer = pipeline.DecodeLayer(cfg, d, DEV)
+        states = [OS.oracle_decode_state(cfg, d, b) for b in range(cfg.B)]
+        rng = np.random.default_rng(3)
+        for step in range(9):
+            if step:
+                for name in ("tokC", "tokZ", "q"):
+                    new = enc.encode(rng.standard_normal(d[name].shape), cfg.io_dtype)
+                    d[name] = new
+                    getattr(layer, name).copy_(T(new))
+            layer.step()
+            out = out_f64(layer.out)
+            idx = host(layer.idx)
+            for b in range(cfg.B):
+                kw = {}
+                if d["kind"] == "C":
+                    L = states[b].L + 1
+                    kw = dict(k=cfg.k, qI=O.decode(d["qI"][b], cfg.idx_dtype),
+                              kI=O.decode(d["kI"][b, :L // d["m"]], cfg.idx_dtype), w=d["w"][b],
+                              idx_given=idx[b])
+                r = O.decode_step(states[b], tokC=O.decode(d["tokC"][b], cfg.io_dtype),
+                                  tokZ=O.decode(d["tokZ"][b], cfg.io_dtype), P=d["P"],
+                                  q=O.decode(d["q"][b], cfg.io_dtype), tau=cfg.tau, eps=cfg.eps,
+                                  kv_fmt=cfg.kv_dtype, out_fmt=cfg.io_dtype, **kw)
+                err = np.abs(out[b] - r["out"]).max()
+                assert err <= OUT_TOL[cfg.io_dtype], f"step {step} b{b}: {err:.3g}"
+
+
+def test_decode_deterministic_and_batch_invariant():
+    cfg = CSA_DECODE_1M.with_(B=3, ctx=1 << 16)
+    say("determinism / batch invariance")
+    d = gen.decode_inputs(cfg)
+    outs = []
+    for _ in range(2):
+        layer = pipeline.DecodeLayer(cfg, d, DEV)
+        layer.step()
+        outs.append((host(layer.out.view(torch.int16)), host(layer.idx), host(layer.lse)))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
+    # sequence 1 alone
+    one = {k: (v[1:2] if isinstance(v, np.ndarray) and v.ndim >= 1 and v.shape[0] == cfg.B else v)
+           for k, v in d.items()}
+    layer1 = pipeline.DecodeLayer(cfg.with_(B=1), one, DEV)
+    layer1.step()
+    assert np.array_equal(host(layer1.out.view(torch.int16))[0], outs[0][0][1])
+    assert np.array_equal(host(layer1.idx)[0], outs[0][1][1])
+
+
+def test_sink_logit():
+    cfg = HCA_DECODE.with_(B=2, ctx=4096, m=128)
+    say("sink")
+    d = gen.decode_inputs(cfg)
+    sink = np.linspace(-2, 3, cfg.H).astype(np.float32)
+    layer = pipeline.DecodeLayer(cfg, d, DEV, sink=sink)
+    layer.step()
+    out = out_f64(layer.out)
+    for b in range(cfg.B):
+        ref = OS.oracle_decode(cfg, d, b, sink=sink.astype(np.float64))
+        assert np.abs(out[b] - ref["out"]).max() <= OUT_TOL["bf16"]

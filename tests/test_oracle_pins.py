@@ -390,7 +390,7 @@ def test_incremental_decode_equals_prefill(mode, m):
         assert np.array_equal(r["out"], pre["out"][t])
         if mode == "csa":
             assert np.array_equal(r["idx"], pre["idx"][t])
-    assert np.array_equal(st.entries, pre["entries"])
+    assert np.array_equal(st.rows(np.arange(st.n_entries)), pre["entries"])
 
 
 # ---------------------------------------------------------------------------
@@ -426,3 +426,24 @@ def test_pages_hyperparameters():
     assert np.lcm(cfg.m, HCA_DECODE.m) == g["cache_block_tokens_lcm"]["value"]
     assert cfg.k == g["entries_attended_at_1m"]["value"]
     assert int(O.visible([cfg.ctx - 1], cfg.m, 10 ** 9)[0]) == 262144
+
+
+def test_compress_error_bound_covers_fp32_pooling():
+    """The bound covers an fp32 evaluation of the pooling + RMSNorm (emulated with
+    numpy float32 arithmetic) and is far below an ulp of bf16 at unit scale."""
+    r = rng(60)
+    m, c = 4, 256
+    C, Z = r.standard_normal((64, c)), r.standard_normal((64, c))
+    P = r.standard_normal((8, c)) * 0.1
+    exact = O.rmsnorm(O.compress(C, Z, P, m, True))
+    bound = O.compress_error_bound(C, Z, P, m, True)
+    C32, Z32, P32 = (a.astype(np.float32) for a in (C, Z, P))
+    cand = np.concatenate([np.concatenate([np.zeros((1, m, c), np.float32), C32.reshape(-1, m, c)[:-1]], 0),
+                           C32.reshape(-1, m, c)], 1)
+    lg = np.concatenate([np.concatenate([np.full((1, m, c), -np.inf, np.float32), Z32.reshape(-1, m, c)[:-1]], 0),
+                         Z32.reshape(-1, m, c)], 1) + P32[None]
+    e = np.exp(lg - lg.max(1, keepdims=True)).astype(np.float32)
+    E32 = ((e * cand).sum(1, dtype=np.float32) / e.sum(1, dtype=np.float32)).astype(np.float32)
+    y32 = E32 / np.sqrt((E32 * E32).mean(-1, keepdims=True, dtype=np.float32) + np.float32(1e-6))
+    assert np.all(np.abs(y32 - exact) <= bound)
+    assert bound.max() < 1e-4
