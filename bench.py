@@ -9,8 +9,9 @@ block, compression of a block the token completes), indexer scores, top-k,
 sparse attention with the window branch and the log-sum-exp merge.  Steps run
 back to back, so the state advances (blocks complete every 4 steps).
 
-Prints ONE JSON line.  Per-stage times come from HIP events recorded on the
-stream the kernels run on, over the timed region itself.
+Prints ONE JSON line.  The timed loop calls lca_decode_step; per-stage times
+come from HIP events that the library records on the stream its kernels run on
+(lca_decode_io.stage_events), over the timed region itself.
 """
 import argparse
 import json
@@ -22,6 +23,29 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime, recorded by the library itself on
+    the stream its kernels run on."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.lib = ctypes.CDLL("libamdhip64.so")
+
+    def create(self):
+        e = self.ct.c_void_p()
+        assert self.lib.hipEventCreate(self.ct.byref(e)) == 0
+        return e.value
+
+    def elapsed_s(self, a, b):
+        ms = self.ct.c_float()
+        assert self.lib.hipEventElapsedTime(self.ct.byref(ms), self.ct.c_void_p(a), self.ct.c_void_p(b)) == 0
+        return ms.value * 1e-3
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(self.ct.c_void_p(e))
 
 
 def parse():
@@ -78,43 +102,18 @@ def main():
     d = gen.decode_inputs(cfg, extra_entries=total_steps // cfg.m + 2)
     layer = pipeline.DecodeLayer(cfg, d, dev)
     B, m = cfg.B, cfg.m
-    q_pos = torch.empty(B, dtype=torch.int32, device=dev)
-    n_ent = torch.empty(B, dtype=torch.int32, device=dev)
-    scores = torch.empty((B, layer.N_cap), dtype=torch.float32, device=dev)
-    ws_topk = torch.empty(max(1, ops.lca_topk_workspace_size(B, 1, layer.N_cap, cfg.k)),
-                          dtype=torch.uint8, device=dev)
-    ws_mqa = torch.empty(max(1, ops.lca_sparse_mqa_workspace_size(
-        B, 1, cfg.H, cfg.c, cfg.kv_dtype, cfg.k, layer.N_cap, cfg.n_win, False)),
-        dtype=torch.uint8, device=dev)
     stages = ["append", "indexer", "topk", "attention"]
+    hip = HipEvents()
 
     def step(ev=None):
-        # the same library calls lca_decode_step makes, with events between stages
-        if ev:
-            ev[0].record()
-        ops.lca_state_append("csa", m, B, cfg.c, cfg.n_win, layer.tokC, layer.tokZ, cfg.io_dtype,
-                             layer.tailC, layer.tailZ, layer.ring, cfg.kv_dtype, layer.P,
-                             layer.cache, layer.N_cap, layer.n_tokens, q_pos, n_ent, cfg.eps)
-        if ev:
-            ev[1].record()
-        ops.lca_indexer_scores(B, 1, cfg.H_I, cfg.d_I, cfg.idx_dtype, layer.qI, None, layer.kI, None,
-                               layer.N_cap, layer.w, q_pos, m, n_ent, scores)
-        if ev:
-            ev[2].record()
-        ops.lca_topk(B, 1, layer.N_cap, scores, q_pos, m, n_ent, cfg.k, layer.idx, ws_topk)
-        if ev:
-            ev[3].record()
-        ops.lca_sparse_mqa(B, 1, cfg.H, cfg.c, layer.q, cfg.io_dtype, layer.cache, cfg.kv_dtype,
-                           layer.N_cap, layer.idx, cfg.k, q_pos, m, n_ent, layer.ring, cfg.n_win, 0,
-                           cfg.n_win, cfg.tau, cfg.eps, None, layer.out, cfg.io_dtype, layer.lse,
-                           ws_mqa)
-        if ev:
-            ev[4].record()
+        ops.lca_decode_step(layer.state, layer.tokC, layer.tokZ, layer.q, layer.out, cfg.io_dtype,
+                            qI=layer.qI, w=layer.w, lse=layer.lse, idx_out=layer.idx,
+                            workspace=layer.workspace, stage_events=ev)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[hip.create() for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -124,7 +123,10 @@ def main():
     per_stage = {s: [] for s in stages}
     for ev in events:
         for j, s in enumerate(stages):
-            per_stage[s].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)
+            per_stage[s].append(hip.elapsed_s(ev[j], ev[j + 1]))
+    for ev in events:
+        for e in ev:
+            hip.destroy(e)
     avg = {s: float(np.mean(v)) for s, v in per_stage.items()}
     ms_per_step = elapsed / args.steps * 1e3
     value = B * args.steps / elapsed

@@ -239,7 +239,10 @@ int lca_state_append(int mode, int m, int B, int c, int n_win, const void* tokC,
 /* ---------------------------------------------------------------------------
  * lca_decode_step -- one decode step of one CSA or HCA layer for B sequences:
  * lca_state_append, then (CSA) lca_indexer_scores + lca_topk, then
- * lca_sparse_mqa over the ring window (W_cap = n_win, win_origin = 0).
+ * lca_sparse_mqa over the ring window (W_cap = n_win, win_origin = 0).  For
+ * CSA rows longer than 36864 entries with an FP8/MXFP4 indexer, the indexer
+ * also builds the top-k's score histogram (the append clears it), so the
+ * top-k skips its own histogram pass; results are identical.
  * ------------------------------------------------------------------------- */
 typedef struct lca_decode_layer {
   size_t struct_size;   /* sizeof(lca_decode_layer) */
@@ -271,6 +274,10 @@ typedef struct lca_decode_io {
   float* lse;           /* [B, H] or NULL */
   int out_dtype;
   int32_t* idx_out;     /* CSA: [B, k] selected entries, or NULL (kept in workspace) */
+  /* Optional hipEvent_t handles (NULL = skip), recorded on `stream` before the
+   * state append, after it, after the indexer, after the top-k and after the
+   * attention; an HCA layer records [2] and [3] right after the append. */
+  void* stage_events[5];
 } lca_decode_io;
 
 size_t lca_decode_workspace_size(const lca_decode_layer* layer);

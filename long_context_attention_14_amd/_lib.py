@@ -31,7 +31,7 @@ class DecodeLayer(ctypes.Structure):
 class DecodeIO(ctypes.Structure):
     _fields_ = [("struct_size", c_size_t), ("tokC", P), ("tokZ", P), ("q", P), ("qI", P),
                 ("qI_scale", P), ("w", P), ("out", P), ("lse", P), ("out_dtype", c_int),
-                ("idx_out", P)]
+                ("idx_out", P), ("stage_events", P * 5)]
 
 
 SIGNATURES = {

@@ -286,30 +286,56 @@ int lca_decode_step(const lca_decode_layer* L, const lca_decode_io* io, void* wo
   }
   REQUIRE(io->tokC && io->tokZ && io->q && io->out, "NULL io tensor");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  st = lca_state_append(L->mode, L->m, L->B, L->c, L->n_win, io->tokC, io->tokZ, L->io_dtype,
-                        L->tailC, L->tailZ, L->ring, L->kv_dtype, L->P, L->cache, L->N_cap,
-                        L->n_tokens, q_pos, n_ent, L->eps, stream);
+  auto mark = [&](int i) -> int {
+    if (io->stage_events[i] == nullptr) return LCA_OK;
+    return hip_status(hipEventRecord(reinterpret_cast<hipEvent_t>(io->stage_events[i]), s),
+                      "lca_decode_step/event");
+  };
+  // the fused histogram path: the indexer accumulates the top-k's row histogram
+  uint32_t* hist = nullptr;
+  if (csa && L->idx_dtype != LCA_F32)
+    hist = lca::topk_hist_in_workspace(ws + d.topk, L->B, 1, L->N_cap, L->k);
+  if ((st = mark(0)) != LCA_OK) return st;
+  st = hip_status(lca::launch_state_append(L->mode, L->m, L->B, L->c, L->n_win, io->tokC, io->tokZ,
+                                           L->io_dtype, L->tailC, L->tailZ, L->ring, L->kv_dtype,
+                                           L->P, L->cache, L->N_cap, L->n_tokens, q_pos, n_ent,
+                                           L->eps, s, hist,
+                                           hist ? static_cast<long long>(L->B) * lca::kScoreHistBins : 0),
+                  "lca_decode_step/append");
   if (st != LCA_OK) return st;
+  if ((st = mark(1)) != LCA_OK) return st;
   const int32_t* sel = nullptr;
   if (csa) {
     float* scores = reinterpret_cast<float*>(ws + d.scores);
     int32_t* idx = io->idx_out ? io->idx_out : reinterpret_cast<int32_t*>(ws + d.idx);
     st = hip_status(lca::launch_indexer(L->B, 1, L->H_I, L->d_I, L->idx_dtype, io->qI, io->qI_scale,
                                         L->kI, L->kI_scale, L->N_cap, io->w, q_pos, L->m, n_ent,
-                                        scores, s),
+                                        scores, s, hist),
                     "lca_decode_step/indexer");
     if (st != LCA_OK) return st;
-    st = hip_status(lca::launch_topk(L->B, 1, L->N_cap, scores, q_pos, L->m, n_ent, L->k, idx,
-                                     ws + d.topk, s),
-                    "lca_decode_step/topk");
+    if ((st = mark(2)) != LCA_OK) return st;
+    if (hist)
+      st = hip_status(lca::launch_topk_from_hist(L->B, 1, L->N_cap, scores, q_pos, L->m, n_ent, L->k,
+                                                 idx, ws + d.topk, s),
+                      "lca_decode_step/topk");
+    else
+      st = hip_status(lca::launch_topk(L->B, 1, L->N_cap, scores, q_pos, L->m, n_ent, L->k, idx,
+                                       ws + d.topk, s),
+                      "lca_decode_step/topk");
     if (st != LCA_OK) return st;
+    if ((st = mark(3)) != LCA_OK) return st;
     sel = idx;
+  } else {
+    if ((st = mark(2)) != LCA_OK) return st;
+    if ((st = mark(3)) != LCA_OK) return st;
   }
-  return hip_status(lca::launch_mqa(L->B, 1, L->H, L->c, io->q, L->io_dtype, L->cache, L->kv_dtype,
-                                    L->N_cap, sel, csa ? L->k : 0, q_pos, L->m, n_ent, L->ring,
-                                    L->n_win, 0, L->n_win, L->tau, L->eps, L->sink, io->out,
-                                    io->out_dtype, io->lse, ws + d.mqa, s),
-                    "lca_decode_step/mqa");
+  st = hip_status(lca::launch_mqa(L->B, 1, L->H, L->c, io->q, L->io_dtype, L->cache, L->kv_dtype,
+                                  L->N_cap, sel, csa ? L->k : 0, q_pos, L->m, n_ent, L->ring,
+                                  L->n_win, 0, L->n_win, L->tau, L->eps, L->sink, io->out,
+                                  io->out_dtype, io->lse, ws + d.mqa, s),
+                  "lca_decode_step/mqa");
+  if (st != LCA_OK) return st;
+  return mark(4);
 }
 
 }  // extern "C"

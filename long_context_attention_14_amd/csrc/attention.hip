@@ -197,6 +197,271 @@ __global__ __launch_bounds__(kAttnThreads) void attn_generic_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// MFMA path: c = 512, H = 64, bf16 (or fp8 + bf16 RoPE dims) KV.
+//
+// A workgroup (4 waves) owns one query row and one split of its candidate list
+// and all 64 heads, so each gathered KV row is read from HBM once and serves
+// every head as both key and value.  Per 64-row tile: the rows are staged in
+// LDS as bf16; S = Qn K^T runs on the 32x32x16 bf16 MFMA (wave w: heads
+// [32*(w/2), +32) x rows [32*(w%2), +32), K = 512); the online softmax updates
+// per-head max / sum in LDS and writes P as bf16; O += P V runs on the same
+// MFMA (wave w: all heads x dims [128w, 128w+128), K = 64 rows), with the V
+// operand read from the same LDS tile.  The softmax denominator sums the
+// bf16-rounded P that the PV product uses.
+
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
+
+constexpr int kMT = 64;            // rows per tile
+constexpr int kMC = 512;           // head dim
+constexpr int kMH = 64;            // heads
+constexpr int kQS = kMC + 8;       // LDS row stride of Q and KV tiles (bf16 elements)
+constexpr int kPS = kMT + 8;       // LDS row stride of P (bf16 elements)
+constexpr int kSS = kMT + 1;       // LDS row stride of S (floats)
+constexpr int kMfmaSplitRows = 128;
+
+__device__ __forceinline__ v8bf_t as_v8bf(uint4 u) { return __builtin_bit_cast(v8bf_t, u); }
+
+__device__ __forceinline__ v16f_t mfma_bf16(const v8bf_t& a, const v8bf_t& b, const v16f_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+template <int KVFMT>
+__global__ __launch_bounds__(256) void attn_mfma_kernel(
+    int n_q, const uint8_t* __restrict__ q, int q_fmt, const uint8_t* __restrict__ cache,
+    int N_cap, const int32_t* __restrict__ idx, int k, const int32_t* __restrict__ q_pos, int m,
+    const int32_t* __restrict__ n_entries, const uint8_t* __restrict__ win, int W_cap,
+    long long win_origin, int n_win, float tau, float eps, const float* __restrict__ sink,
+    int n_splits, int split_rows, uint8_t* __restrict__ out, int out_fmt, float* __restrict__ lse,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
+  __shared__ __attribute__((aligned(16))) uint16_t q_s[kMH * kQS];
+  __shared__ __attribute__((aligned(16))) uint16_t kv_s[kMT * kQS];
+  __shared__ float s_s[kMH * kSS];
+  __shared__ __attribute__((aligned(16))) uint16_t p_s[kMH * kPS];
+  __shared__ float m_s[kMH], l_s[kMH], a_s[kMH];
+  __shared__ const uint8_t* rowp_s[kMT];
+
+  const int split = blockIdx.x % n_splits;
+  const long long row = blockIdx.x / n_splits;
+  const int b = static_cast<int>(row / n_q);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int j32 = lane & 31, g = lane >> 5;
+
+  SlotCtx sc;
+  sc.t = q_pos[row];
+  sc.vis = visible_entries(sc.t, m, n_entries[b], N_cap);
+  sc.idx = idx ? idx + row * k : nullptr;
+  sc.NS = idx ? k : N_cap;
+  sc.N_cap = N_cap;
+  sc.n_win = n_win;
+  sc.kv_row = row_bytes(KVFMT, kMC);
+  sc.cache_b = cache + static_cast<size_t>(b) * N_cap * sc.kv_row;
+  sc.win_b = win + static_cast<size_t>(b) * W_cap * sc.kv_row;
+  sc.W_cap = W_cap;
+  sc.win_origin = win_origin;
+  const int NT = sc.NS + n_win;
+  const int s_begin = split * split_rows;
+  const int s_end = min(s_begin + split_rows, NT);
+
+  // normalised queries -> bf16 in LDS (wave wv: heads wv, wv+4, ...)
+  const size_t q_row = row_bytes(q_fmt, kMC);
+  for (int h = wv; h < kMH; h += 4) {
+    float v[8];
+    load_row<8>(q + (static_cast<size_t>(row) * kMH + h) * q_row, q_fmt, kMC, lane, v);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / static_cast<float>(kMC) + eps);
+    uint4 pk;
+    pk.x = pack_bf16(v[0] * r, v[1] * r);
+    pk.y = pack_bf16(v[2] * r, v[3] * r);
+    pk.z = pack_bf16(v[4] * r, v[5] * r);
+    pk.w = pack_bf16(v[6] * r, v[7] * r);
+    *reinterpret_cast<uint4*>(&q_s[h * kQS + lane * 8]) = pk;
+  }
+  if (tid < kMH) {
+    m_s[tid] = -INFINITY;
+    l_s[tid] = 0.f;
+  }
+
+  v16f_t o[2][4];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[ht][dt] = v16f_t{0};
+
+  const int sh = wv >> 1, sr = wv & 1;  // this wave's S tile
+  for (int base = s_begin; base < s_end; base += kMT) {
+    __syncthreads();  // previous tile fully consumed
+    if (tid < kMT) rowp_s[tid] = base + tid < s_end ? slot_row(sc, base + tid) : nullptr;
+    __syncthreads();
+    // stage the tile: wave wv loads rows wv, wv+4, ... (one 1 KiB row per load)
+    for (int r = wv; r < kMT; r += 4) {
+      const uint8_t* rp = rowp_s[r];
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (rp) {
+        if (KVFMT == LCA_BF16) {
+          v = *reinterpret_cast<const uint4*>(rp + lane * 16);
+        } else if (lane < 56) {  // 8 fp8 dims -> bf16
+          const uint2 f = *reinterpret_cast<const uint2*>(rp + lane * 8);
+          float x[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[i] = e4m3_to_f32((f.x >> (8 * i)) & 0xffu);
+            x[4 + i] = e4m3_to_f32((f.y >> (8 * i)) & 0xffu);
+          }
+          v.x = pack_bf16(x[0], x[1]);
+          v.y = pack_bf16(x[2], x[3]);
+          v.z = pack_bf16(x[4], x[5]);
+          v.w = pack_bf16(x[6], x[7]);
+        } else {  // bf16 rope dims
+          v = *reinterpret_cast<const uint4*>(rp + 448 + (lane - 56) * 16);
+        }
+      }
+      *reinterpret_cast<uint4*>(&kv_s[r * kQS + lane * 8]) = v;
+    }
+    __syncthreads();
+    // S tile of this wave
+    {
+      v16f_t acc = v16f_t{0};
+      const uint16_t* qa = &q_s[(32 * sh + j32) * kQS + 8 * g];
+      const uint16_t* kb = &kv_s[(32 * sr + j32) * kQS + 8 * g];
+#pragma unroll 8
+      for (int ks = 0; ks < kMC / 16; ++ks) {
+        const uint4 a = *reinterpret_cast<const uint4*>(qa + 16 * ks);
+        const uint4 bb = *reinterpret_cast<const uint4*>(kb + 16 * ks);
+        acc = mfma_bf16(as_v8bf(a), as_v8bf(bb), acc);
+      }
+      const bool valid = rowp_s[32 * sr + j32] != nullptr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int h = 32 * sh + 8 * (r >> 2) + 4 * g + (r & 3);
+        s_s[h * kSS + 32 * sr + j32] = valid ? acc[r] * tau : -INFINITY;
+      }
+    }
+    __syncthreads();
+    // online softmax: thread -> (head tid/4, rows 16*(tid%4) .. +16)
+    {
+      const int h = tid >> 2, q4 = tid & 3;
+      const float* srow = &s_s[h * kSS + 16 * q4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, srow[r]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 1, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 2, 64));
+      const float m_old = m_s[h];
+      const float m_new = fmaxf(m_old, tmax);
+      float psum = 0.f;
+      uint32_t pk[8];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float p0 = 0.f, p1 = 0.f;
+        if (m_new != -INFINITY) {
+          p0 = srow[r] == -INFINITY ? 0.f : __expf(srow[r] - m_new);
+          p1 = srow[r + 1] == -INFINITY ? 0.f : __expf(srow[r + 1] - m_new);
+        }
+        pk[r / 2] = pack_bf16(p0, p1);
+        psum += bf16_to_f32(static_cast<uint16_t>(pk[r / 2] & 0xffffu)) +
+                bf16_to_f32(static_cast<uint16_t>(pk[r / 2] >> 16));
+      }
+      uint4* pd = reinterpret_cast<uint4*>(&p_s[h * kPS + 16 * q4]);
+      pd[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      pd[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+      psum += __shfl_xor(psum, 1, 64);
+      psum += __shfl_xor(psum, 2, 64);
+      if (q4 == 0) {
+        const float alpha = (m_new == -INFINITY || m_old == -INFINITY) ? (m_old == -INFINITY ? 0.f : 1.f)
+                                                                       : __expf(m_old - m_new);
+        l_s[h] = l_s[h] * alpha + psum;
+        a_s[h] = alpha;
+        m_s[h] = m_new;
+      }
+    }
+    __syncthreads();
+    // O = O * alpha + P V   (wave wv: dims [128 wv, +128))
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float al = a_s[32 * ht + 8 * (r >> 2) + 4 * g + (r & 3)];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[ht][dt][r] *= al;
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < kMT / 16; ++ks) {
+      v8bf_t A[2];
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht)
+        A[ht] = as_v8bf(*reinterpret_cast<const uint4*>(&p_s[(32 * ht + j32) * kPS + 16 * ks + 8 * g]));
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int dim = 128 * wv + 32 * dt + j32;
+        const uint16_t* vp = &kv_s[(16 * ks + 8 * g) * kQS + dim];
+        uint4 bv;
+        bv.x = static_cast<uint32_t>(vp[0]) | (static_cast<uint32_t>(vp[kQS]) << 16);
+        bv.y = static_cast<uint32_t>(vp[2 * kQS]) | (static_cast<uint32_t>(vp[3 * kQS]) << 16);
+        bv.z = static_cast<uint32_t>(vp[4 * kQS]) | (static_cast<uint32_t>(vp[5 * kQS]) << 16);
+        bv.w = static_cast<uint32_t>(vp[6 * kQS]) | (static_cast<uint32_t>(vp[7 * kQS]) << 16);
+        const v8bf_t Bv = as_v8bf(bv);
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) o[ht][dt] = mfma_bf16(A[ht], Bv, o[ht][dt]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // epilogue: O / l; lse = m + log l
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int h = 32 * ht + 8 * (r >> 2) + 4 * g + (r & 3);
+      const float l = l_s[h];
+      float lse_v = l > 0.f ? m_s[h] + __logf(l) : -INFINITY;
+      float f = l > 0.f ? 1.0f / l : 0.f;
+      if (n_splits == 1 && sink) {
+        const float sk = sink[h];
+        if (lse_v == -INFINITY) {
+          lse_v = sk;
+        } else {
+          const float mx = fmaxf(lse_v, sk);
+          const float tot = mx + __logf(__expf(lse_v - mx) + __expf(sk - mx));
+          f *= __expf(lse_v - tot);
+          lse_v = tot;
+        }
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int dim = 128 * wv + 32 * dt + j32;
+        const float v = o[ht][dt][r] * f;
+        if (n_splits == 1) {
+          const size_t oi = (static_cast<size_t>(row) * kMH + h) * kMC + dim;
+          if (out_fmt == LCA_F32)
+            reinterpret_cast<float*>(out)[oi] = v;
+          else
+            reinterpret_cast<uint16_t*>(out)[oi] = f32_to_bf16(v);
+        } else {
+          part_o[((static_cast<size_t>(row) * n_splits + split) * kMH + h) * kMC + dim] = v;
+        }
+      }
+      if (wv == 0 && j32 == 0) {
+        if (n_splits == 1) {
+          if (lse) lse[static_cast<size_t>(row) * kMH + h] = lse_v;
+        } else {
+          part_lse[(static_cast<size_t>(row) * n_splits + split) * kMH + h] = lse_v;
+        }
+      }
+    }
+  }
+}
+
 // One wave per (query row, head): combine the splits in order.
 template <int CPL>
 __global__ __launch_bounds__(256) void attn_merge_kernel(
@@ -237,17 +502,26 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
 
 struct Plan {
   int n_splits, split_rows;
+  bool mfma;
 };
 
-Plan make_plan(long long rows, int k, int N_cap, int n_win, int dense) {
+bool use_mfma(int H, int c, int q_fmt, int kv_fmt) {
+  return H == kMH && c == kMC && (q_fmt == LCA_BF16 || q_fmt == LCA_F32) &&
+         (kv_fmt == LCA_BF16 || kv_fmt == LCA_KV_FP8_BF16ROPE);
+}
+
+Plan make_plan(long long rows, int H, int c, int q_fmt, int kv_fmt, int k, int N_cap, int n_win,
+               int dense) {
   const int NT = (dense ? N_cap : k) + n_win;
   Plan p;
+  p.mfma = use_mfma(H, c, q_fmt, kv_fmt);
+  const int split_rows = p.mfma ? kMfmaSplitRows : kSplitRows;
   if (rows >= 512) {
     p.n_splits = 1;
     p.split_rows = NT;
   } else {
-    p.split_rows = kSplitRows;
-    p.n_splits = (NT + kSplitRows - 1) / kSplitRows;
+    p.split_rows = split_rows;
+    p.n_splits = (NT + split_rows - 1) / split_rows;
   }
   return p;
 }
@@ -256,9 +530,9 @@ Plan make_plan(long long rows, int k, int N_cap, int n_win, int dense) {
 
 size_t mqa_workspace_bytes(int B, int n_q, int H, int c, int kv_fmt, int k, int N_cap, int n_win,
                            int dense) {
-  (void)kv_fmt;
   const long long rows = static_cast<long long>(B) * n_q;
-  const Plan p = make_plan(rows, k, N_cap, n_win, dense);
+  // the plan does not depend on q_fmt beyond F32/BF16, which both allow the MFMA path
+  const Plan p = make_plan(rows, H, c, LCA_BF16, kv_fmt, k, N_cap, n_win, dense);
   if (p.n_splits == 1) return 0;
   const size_t n = static_cast<size_t>(rows) * p.n_splits * H;
   return n * c * sizeof(float) + ((n * sizeof(float) + 255) & ~static_cast<size_t>(255)) + 256;
@@ -282,7 +556,7 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
   const long long rows = static_cast<long long>(B) * n_q;
   if (rows == 0) return hipSuccess;
   const int dense = idx == nullptr;
-  const Plan p = make_plan(rows, k, N_cap, n_win, dense);
+  const Plan p = make_plan(rows, H, c, q_fmt, kv_fmt, k, N_cap, n_win, dense);
   float* part_o = nullptr;
   float* part_lse = nullptr;
   if (p.n_splits > 1) {
@@ -290,12 +564,28 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
     part_o = static_cast<float*>(ws);
     part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + n * c * sizeof(float));
   }
+  if (p.mfma) {
+    const dim3 grid(static_cast<unsigned>(rows * p.n_splits));
+    if (kv_fmt == LCA_BF16)
+      hipLaunchKernelGGL(attn_mfma_kernel<LCA_BF16>, grid, dim3(256), 0, s, n_q,
+                         static_cast<const uint8_t*>(q), q_fmt, static_cast<const uint8_t*>(cache),
+                         N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
+                         static_cast<long long>(win_origin), n_win, tau, eps, sink, p.n_splits,
+                         p.split_rows, static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
+    else
+      hipLaunchKernelGGL(attn_mfma_kernel<LCA_KV_FP8_BF16ROPE>, grid, dim3(256), 0, s, n_q,
+                         static_cast<const uint8_t*>(q), q_fmt, static_cast<const uint8_t*>(cache),
+                         N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
+                         static_cast<long long>(win_origin), n_win, tau, eps, sink, p.n_splits,
+                         p.split_rows, static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
+  } else {
   const dim3 grid(static_cast<unsigned>(rows * (H / kHG) * p.n_splits));
   LCA_ATTN_CPL(c, attn_generic_kernel, grid, dim3(kAttnThreads), n_q, H, c,
                static_cast<const uint8_t*>(q), q_fmt, static_cast<const uint8_t*>(cache), kv_fmt,
                N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
                static_cast<long long>(win_origin), n_win, tau, eps, sink, p.n_splits, p.split_rows,
                static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
   const dim3 g2(static_cast<unsigned>((rows * H + 3) / 4));

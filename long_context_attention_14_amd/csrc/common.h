@@ -150,6 +150,18 @@ __device__ __forceinline__ int visible_entries(int t, int m, int n_entries, int 
   return v < 0 ? 0 : v;
 }
 
+// Order-preserving uint32 key of a score: larger score <-> larger key; -0 is
+// counted as +0 and NaN as -inf.  The top 12 bits are the histogram bin of the
+// multi-workgroup top-k.
+__device__ __forceinline__ uint32_t score_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) u = 0xff800000u;  // NaN -> -inf
+  if (u == 0x80000000u) u = 0u;                          // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+constexpr int kScoreHistBins = 4096;
+__device__ __forceinline__ uint32_t score_bin(uint32_t key) { return key >> 20; }
+
 // ---------------------------------------------------------------------------
 // internal launchers (defined next to their kernels, called by the C ABI)
 
@@ -159,18 +171,30 @@ hipError_t launch_compress(int mode, int m, int B, int n_new, int c, const void*
                            hipStream_t s);
 hipError_t launch_rmsnorm_rows(int B, int n, int c, const void* x, int x_fmt, void* y, int y_fmt,
                                int y_seq_rows, float eps, hipStream_t s);
+// zero_buf (optional): zero_words uint32 words the kernel clears as a side job.
 hipError_t launch_state_append(int mode, int m, int B, int c, int n_win, const void* tokC,
                                const void* tokZ, int io_fmt, void* tailC, void* tailZ, void* ring,
                                int kv_fmt, const float* P, void* cache, int N_cap,
                                int32_t* n_tokens, int32_t* q_pos, int32_t* n_entries, float eps,
-                               hipStream_t s);
+                               hipStream_t s, uint32_t* zero_buf = nullptr,
+                               long long zero_words = 0);
+// hist (optional, [B*n_q, 4096], zeroed by the caller): the MFMA path adds the
+// score_bin histogram of every row's visible scores into it.
 hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const void* qI,
                           const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale,
                           int N_cap, const float* w, const int32_t* q_pos, int m,
-                          const int32_t* n_entries, float* scores, hipStream_t s);
+                          const int32_t* n_entries, float* scores, hipStream_t s,
+                          uint32_t* hist = nullptr);
 size_t topk_workspace_bytes(int B, int n_q, int N_cap, int k);
 hipError_t launch_topk(int B, int n_q, int N_cap, const float* scores, const int32_t* q_pos, int m,
                        const int32_t* n_entries, int k, int32_t* idx, void* ws, hipStream_t s);
+// For rows longer than the LDS path takes: the row histogram inside the top-k
+// workspace (nullptr when the LDS path applies), and the selection from a
+// histogram that the indexer already accumulated there.
+uint32_t* topk_hist_in_workspace(void* ws, int B, int n_q, int N_cap, int k);
+hipError_t launch_topk_from_hist(int B, int n_q, int N_cap, const float* scores,
+                                 const int32_t* q_pos, int m, const int32_t* n_entries, int k,
+                                 int32_t* idx, void* ws, hipStream_t s);
 size_t mqa_workspace_bytes(int B, int n_q, int H, int c, int kv_fmt, int k, int N_cap, int n_win,
                            int dense);
 hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, const void* cache,

@@ -138,17 +138,28 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void rmsnorm_rows_kernel(
                  v);
 }
 
-// One wave per sequence: append the token, and compress its block when the
-// token completes it.  Rows of the tail other than the new token were written
-// by earlier steps; the new token's row is used from registers.
+// One workgroup of kAppendWaves waves per sequence: append the token, and
+// compress its block when the token completes it.  The block's candidates are
+// spread over the waves (candidate j goes to wave j % kAppendWaves), each wave
+// keeping an online per-channel softmax; the partial states are combined in
+// wave order through LDS, so the result does not depend on timing.  Tail rows
+// other than the new token were written by earlier steps; the new token's row is
+// used from registers.  As a side job the workgroups clear zero_buf.
+constexpr int kAppendWaves = 8;
+
 template <int CPL>
-__global__ __launch_bounds__(kWave * kWavesPerBlock) void state_append_kernel(
+__global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
     int csa, int m, int B, int c, int n_win, const uint8_t* tokC, const uint8_t* tokZ, int io_fmt,
     uint8_t* tailC, uint8_t* tailZ, uint8_t* ring, int kv_fmt, const float* P, uint8_t* cache,
-    int N_cap, int32_t* n_tokens, int32_t* q_pos, int32_t* n_entries, float eps) {
+    int N_cap, int32_t* n_tokens, int32_t* q_pos, int32_t* n_entries, float eps,
+    uint32_t* zero_buf, long long zero_words) {
+  __shared__ float part[kAppendWaves][3][CPL * kWave];
   const int lane = threadIdx.x & (kWave - 1);
-  const int b = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (b >= B) return;
+  const int wv = threadIdx.x >> 6;
+  const int b = blockIdx.x;
+  for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; i < zero_words;
+       i += static_cast<long long>(gridDim.x) * blockDim.x)
+    zero_buf[i] = 0u;
   const int p = n_tokens[b];
   if (p < 0) return;
   const size_t io_row = row_bytes(io_fmt, c);
@@ -163,11 +174,10 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void state_append_kernel(
   load_row<CPL>(tokZ + static_cast<size_t>(b) * io_row, io_fmt, c, lane, tz);
   uint8_t* tCb = tailC + static_cast<size_t>(b) * T_cap * io_row;
   uint8_t* tZb = tailZ + static_cast<size_t>(b) * T_cap * io_row;
-  store_row<CPL>(tCb + row * io_row, io_fmt, c, lane, tc);
-  store_row<CPL>(tZb + row * io_row, io_fmt, c, lane, tz);
-
-  // window KV of the new token
-  {
+  if (wv == 0) {
+    store_row<CPL>(tCb + row * io_row, io_fmt, c, lane, tc);
+    store_row<CPL>(tZb + row * io_row, io_fmt, c, lane, tz);
+    // window KV of the new token
     float u[CPL];
     float ss = 0.f;
 #pragma unroll
@@ -180,51 +190,68 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void state_append_kernel(
 #pragma unroll
     for (int j = 0; j < CPL; ++j) u[j] *= rs;
     store_row<CPL>(ring + (static_cast<size_t>(b) * n_win + p % n_win) * kv_row, kv_fmt, c, lane, u);
+    if (lane == 0) {
+      n_tokens[b] = p + 1;
+      q_pos[b] = p;
+      const int ne = (p + 1) / m;
+      n_entries[b] = ne < N_cap ? ne : N_cap;
+    }
   }
+  if ((p + 1) % m != 0) return;
 
-  if ((p + 1) % m == 0) {
-    const int s = (p + 1) / m - 1;
-    Pool pool[CPL];
-    pool_init<CPL>(pool);
-    float cv[CPL], zv[CPL], pv[CPL];
-    if (csa && s > 0) {
-      const int ph = (blk - 1) & 1;
-      for (int i = 0; i < m; ++i) {
-        load_row<CPL>(tCb + (ph * m + i) * io_row, io_fmt, c, lane, cv);
-        load_row<CPL>(tZb + (ph * m + i) * io_row, io_fmt, c, lane, zv);
-        load_bias<CPL>(P, i, c, lane, pv);
+  // candidate slots: CSA 0..m-1 previous block (absent for the first entry),
+  // m..2m-1 own block; HCA 0..m-1 own block.  The own block's last slot is the
+  // new token.
+  const int s = (p + 1) / m - 1;
+  const int W = csa ? 2 * m : m;
+  const int first_slot = (csa && s == 0) ? m : 0;
+  const int ph = (blk - 1) & 1;
+  Pool pool[CPL];
+  pool_init<CPL>(pool);
+  float cv[CPL], zv[CPL], pv[CPL];
+  for (int slot = first_slot + wv; slot < W; slot += kAppendWaves) {
+    if (slot == W - 1) {
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) zv[j] += pv[j];
-        pool_add<CPL>(pool, cv, zv);
+      for (int j = 0; j < CPL; ++j) {
+        cv[j] = tc[j];
+        zv[j] = tz[j];
       }
+    } else {
+      const int r = (csa && slot < m) ? ph * m + slot : half * m + (slot - (csa ? m : 0));
+      load_row<CPL>(tCb + r * io_row, io_fmt, c, lane, cv);
+      load_row<CPL>(tZb + r * io_row, io_fmt, c, lane, zv);
     }
-    const int slot0 = csa ? m : 0;
-    for (int i = 0; i < m; ++i) {
-      if (i == m - 1) {
+    load_bias<CPL>(P, slot, c, lane, pv);
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          cv[j] = tc[j];
-          zv[j] = tz[j];
-        }
-      } else {
-        load_row<CPL>(tCb + (half * m + i) * io_row, io_fmt, c, lane, cv);
-        load_row<CPL>(tZb + (half * m + i) * io_row, io_fmt, c, lane, zv);
-      }
-      load_bias<CPL>(P, slot0 + i, c, lane, pv);
+    for (int j = 0; j < CPL; ++j) zv[j] += pv[j];
+    pool_add<CPL>(pool, cv, zv);
+  }
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) zv[j] += pv[j];
-      pool_add<CPL>(pool, cv, zv);
+  for (int j = 0; j < CPL; ++j) {
+    part[wv][0][lane * CPL + j] = pool[j].mx;
+    part[wv][1][lane * CPL + j] = pool[j].sum;
+    part[wv][2][lane * CPL + j] = pool[j].acc;
+  }
+  __syncthreads();
+  if (wv != 0) return;
+  Pool tot[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    float M = -INFINITY;
+    for (int x = 0; x < kAppendWaves; ++x) M = fmaxf(M, part[x][0][lane * CPL + j]);
+    float sum = 0.f, acc = 0.f;
+    for (int x = 0; x < kAppendWaves; ++x) {
+      const float mx = part[x][0][lane * CPL + j];
+      if (mx == -INFINITY) continue;
+      const float f = __expf(mx - M);
+      sum += part[x][1][lane * CPL + j] * f;
+      acc += part[x][2][lane * CPL + j] * f;
     }
-    float out[CPL];
-    pool_finish_norm<CPL>(pool, c, eps, out);
-    if (s < N_cap) store_row<CPL>(cache + (static_cast<size_t>(b) * N_cap + s) * kv_row, kv_fmt, c, lane, out);
+    tot[j] = {M, sum, acc};
   }
-  if (lane == 0) {
-    n_tokens[b] = p + 1;
-    q_pos[b] = p;
-    const int ne = (p + 1) / m;
-    n_entries[b] = ne < N_cap ? ne : N_cap;
-  }
+  float out[CPL];
+  pool_finish_norm<CPL>(tot, c, eps, out);
+  if (s < N_cap) store_row<CPL>(cache + (static_cast<size_t>(b) * N_cap + s) * kv_row, kv_fmt, c, lane, out);
 }
 
 }  // namespace
@@ -272,14 +299,23 @@ hipError_t launch_state_append(int mode, int m, int B, int c, int n_win, const v
                                const void* tokZ, int io_fmt, void* tailC, void* tailZ, void* ring,
                                int kv_fmt, const float* P, void* cache, int N_cap,
                                int32_t* n_tokens, int32_t* q_pos, int32_t* n_entries, float eps,
-                               hipStream_t s) {
+                               hipStream_t s, uint32_t* zero_buf, long long zero_words) {
   if (B == 0) return hipSuccess;
-  const dim3 grid((B + kWavesPerBlock - 1) / kWavesPerBlock);
-  LCA_DISPATCH_CPL(c, state_append_kernel, grid, mode == LCA_CSA ? 1 : 0, m, B, c, n_win,
-                   static_cast<const uint8_t*>(tokC), static_cast<const uint8_t*>(tokZ), io_fmt,
-                   static_cast<uint8_t*>(tailC), static_cast<uint8_t*>(tailZ),
-                   static_cast<uint8_t*>(ring), kv_fmt, P, static_cast<uint8_t*>(cache), N_cap,
-                   n_tokens, q_pos, n_entries, eps);
+  const dim3 grid(B), block(kWave * kAppendWaves);
+  const int csa = mode == LCA_CSA ? 1 : 0;
+  const uint8_t* tc = static_cast<const uint8_t*>(tokC);
+  const uint8_t* tz = static_cast<const uint8_t*>(tokZ);
+  uint8_t* tC = static_cast<uint8_t*>(tailC);
+  uint8_t* tZ = static_cast<uint8_t*>(tailZ);
+  uint8_t* rg = static_cast<uint8_t*>(ring);
+  uint8_t* ch = static_cast<uint8_t*>(cache);
+  switch (c / kWave) {
+    case 2: hipLaunchKernelGGL(state_append_kernel<2>, grid, block, 0, s, csa, m, B, c, n_win, tc, tz, io_fmt, tC, tZ, rg, kv_fmt, P, ch, N_cap, n_tokens, q_pos, n_entries, eps, zero_buf, zero_words); break;
+    case 4: hipLaunchKernelGGL(state_append_kernel<4>, grid, block, 0, s, csa, m, B, c, n_win, tc, tz, io_fmt, tC, tZ, rg, kv_fmt, P, ch, N_cap, n_tokens, q_pos, n_entries, eps, zero_buf, zero_words); break;
+    case 8: hipLaunchKernelGGL(state_append_kernel<8>, grid, block, 0, s, csa, m, B, c, n_win, tc, tz, io_fmt, tC, tZ, rg, kv_fmt, P, ch, N_cap, n_tokens, q_pos, n_entries, eps, zero_buf, zero_words); break;
+    case 16: hipLaunchKernelGGL(state_append_kernel<16>, grid, block, 0, s, csa, m, B, c, n_win, tc, tz, io_fmt, tC, tZ, rg, kv_fmt, P, ch, N_cap, n_tokens, q_pos, n_entries, eps, zero_buf, zero_words); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -56,13 +56,46 @@ __device__ __forceinline__ v16f mfma(const v8i& a, const v8i& b, const v16f& c, 
 }
 
 template <bool MX>
+struct KeyGroup {
+  v8i b[2];
+  int sb[2];
+};
+
+// B operand (32 keys) of one key group for this lane: key row `key`.
+template <bool MX>
+__device__ __forceinline__ void load_group(const uint8_t* kb_base, const uint8_t* ks_base, int key,
+                                           int g, KeyGroup<MX>& G) {
+  constexpr int kRowBytes = MX ? 64 : 128;
+  const uint8_t* kp = kb_base + static_cast<size_t>(key) * kRowBytes;
+  if (MX) {
+    const uint32_t sc = *reinterpret_cast<const uint32_t*>(ks_base + static_cast<size_t>(key) * 4);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int blk = 2 * g + ks;
+      G.b[ks] = load16(kp + 16 * blk);
+      G.sb[ks] = (sc >> (8 * blk)) & 0xff;
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      G.b[ks] = load32(kp + 64 * g + 32 * ks);
+      G.sb[ks] = 127;
+    }
+  }
+}
+
+// HIST: also accumulate the score_bin histogram of the written scores into
+// hist[row] (global, zeroed by the caller) through a per-workgroup LDS histogram.
+template <bool MX, bool HIST>
 __global__ __launch_bounds__(kWave * kIdxWaves) void indexer_mfma_kernel(
     const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qI_scale,
     const uint8_t* __restrict__ kI, const uint8_t* __restrict__ kI_scale, int n_q, int N_cap,
     int n_chunks, const float* __restrict__ w, const int32_t* __restrict__ q_pos, int m,
-    const int32_t* __restrict__ n_entries, float* __restrict__ scores) {
+    const int32_t* __restrict__ n_entries, float* __restrict__ scores,
+    uint32_t* __restrict__ hist) {
   constexpr int kFmt = MX ? 4 : 0;
   constexpr int kRowBytes = MX ? 64 : 128;  // bytes of one 128-dim vector
+  __shared__ uint32_t lh[HIST ? kScoreHistBins : 1];
   const long long row = blockIdx.x / n_chunks;
   const int chunk = blockIdx.x % n_chunks;
   const int b = static_cast<int>(row / n_q);
@@ -75,6 +108,9 @@ __global__ __launch_bounds__(kWave * kIdxWaves) void indexer_mfma_kernel(
   const int wave = threadIdx.x >> 6;
   const int j = lane & 31;
   const int g = lane >> 5;
+  if (HIST) {
+    for (int i = threadIdx.x; i < kScoreHistBins; i += kWave * kIdxWaves) lh[i] = 0;
+  }
 
   // A operand: query heads 32*ht + j, K-steps ks = 0, 1
   v8i A[2][2];
@@ -107,39 +143,39 @@ __global__ __launch_bounds__(kWave * kIdxWaves) void indexer_mfma_kernel(
   const uint8_t* kb_base = kI + static_cast<size_t>(b) * N_cap * kRowBytes;
   const uint8_t* ks_base = MX ? kI_scale + static_cast<size_t>(b) * N_cap * 4 : nullptr;
   float* out = scores + static_cast<size_t>(row) * N_cap;
+  if (HIST) __syncthreads();
 
-  for (int kb = key0 + wave * kKeysPerGroup; kb < key_end; kb += kIdxWaves * kKeysPerGroup) {
-    const int key = min(kb + j, vis - 1);  // clamp the ragged tail to a valid row
-    const uint8_t* kp = kb_base + static_cast<size_t>(key) * kRowBytes;
-    v8i Bk[2];
-    int sB[2];
-    if (MX) {
-      const uint32_t sc = *reinterpret_cast<const uint32_t*>(ks_base + static_cast<size_t>(key) * 4);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int blk = 2 * g + ks;
-        Bk[ks] = load16(kp + 16 * blk);
-        sB[ks] = (sc >> (8 * blk)) & 0xff;
-      }
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        Bk[ks] = load32(kp + 64 * g + 32 * ks);
-        sB[ks] = 127;
-      }
-    }
+  constexpr int kStride = kIdxWaves * kKeysPerGroup;
+  int kb = key0 + wave * kKeysPerGroup;
+  KeyGroup<MX> cur;
+  if (kb < key_end) load_group<MX>(kb_base, ks_base, min(kb + j, vis - 1), g, cur);
+  for (; kb < key_end; kb += kStride) {
+    // prefetch the next group of this wave while the current one is reduced
+    KeyGroup<MX> nxt;
+    const int kn = kb + kStride;
+    if (kn < key_end) load_group<MX>(kb_base, ks_base, min(kn + j, vis - 1), g, nxt);
     v16f acc0 = {0}, acc1 = {0};
-    acc0 = mfma<kFmt>(A[0][0], Bk[0], acc0, sA[0][0], sB[0]);
-    acc0 = mfma<kFmt>(A[0][1], Bk[1], acc0, sA[0][1], sB[1]);
-    acc1 = mfma<kFmt>(A[1][0], Bk[0], acc1, sA[1][0], sB[0]);
-    acc1 = mfma<kFmt>(A[1][1], Bk[1], acc1, sA[1][1], sB[1]);
+    acc0 = mfma<kFmt>(A[0][0], cur.b[0], acc0, sA[0][0], cur.sb[0]);
+    acc0 = mfma<kFmt>(A[0][1], cur.b[1], acc0, sA[0][1], cur.sb[1]);
+    acc1 = mfma<kFmt>(A[1][0], cur.b[0], acc1, sA[1][0], cur.sb[0]);
+    acc1 = mfma<kFmt>(A[1][1], cur.b[1], acc1, sA[1][1], cur.sb[1]);
     float s = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s += wr[0][r] * fmaxf(acc0[r], 0.f);
 #pragma unroll
     for (int r = 0; r < 16; ++r) s += wr[1][r] * fmaxf(acc1[r], 0.f);
     s += __shfl_xor(s, 32, kWave);
-    if (g == 0 && kb + j < key_end) out[kb + j] = s;
+    if (g == 0 && kb + j < key_end) {
+      out[kb + j] = s;
+      if (HIST) atomicAdd(&lh[score_bin(score_key(s))], 1u);
+    }
+    cur = nxt;
+  }
+  if (HIST) {
+    __syncthreads();
+    uint32_t* gh = hist + row * kScoreHistBins;
+    for (int i = threadIdx.x; i < kScoreHistBins; i += kWave * kIdxWaves)
+      if (lh[i]) atomicAdd(&gh[i], lh[i]);
   }
 }
 
@@ -179,7 +215,8 @@ __global__ __launch_bounds__(kF32Threads) void indexer_f32_kernel(
 hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const void* qI,
                           const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale,
                           int N_cap, const float* w, const int32_t* q_pos, int m,
-                          const int32_t* n_entries, float* scores, hipStream_t s) {
+                          const int32_t* n_entries, float* scores, hipStream_t s,
+                          uint32_t* hist) {
   const long long rows = static_cast<long long>(B) * n_q;
   if (rows == 0 || N_cap == 0) return hipSuccess;
   if (idx_fmt == LCA_F32) {
@@ -193,14 +230,22 @@ hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const v
   }
   const int n_chunks = (N_cap + kKeysPerBlock - 1) / kKeysPerBlock;
   const dim3 grid(static_cast<unsigned>(rows * n_chunks));
-  if (idx_fmt == LCA_FP8_E4M3)
-    hipLaunchKernelGGL(indexer_mfma_kernel<false>, grid, dim3(kWave * kIdxWaves), 0, s,
-                       static_cast<const uint8_t*>(qI), qI_scale, static_cast<const uint8_t*>(kI),
-                       kI_scale, n_q, N_cap, n_chunks, w, q_pos, m, n_entries, scores);
+  const dim3 block(kWave * kIdxWaves);
+  const uint8_t* q8 = static_cast<const uint8_t*>(qI);
+  const uint8_t* k8 = static_cast<const uint8_t*>(kI);
+  const bool mx = idx_fmt == LCA_MXFP4;
+  if (!mx && !hist)
+    hipLaunchKernelGGL((indexer_mfma_kernel<false, false>), grid, block, 0, s, q8, qI_scale, k8,
+                       kI_scale, n_q, N_cap, n_chunks, w, q_pos, m, n_entries, scores, hist);
+  else if (!mx)
+    hipLaunchKernelGGL((indexer_mfma_kernel<false, true>), grid, block, 0, s, q8, qI_scale, k8,
+                       kI_scale, n_q, N_cap, n_chunks, w, q_pos, m, n_entries, scores, hist);
+  else if (!hist)
+    hipLaunchKernelGGL((indexer_mfma_kernel<true, false>), grid, block, 0, s, q8, qI_scale, k8,
+                       kI_scale, n_q, N_cap, n_chunks, w, q_pos, m, n_entries, scores, hist);
   else
-    hipLaunchKernelGGL(indexer_mfma_kernel<true>, grid, dim3(kWave * kIdxWaves), 0, s,
-                       static_cast<const uint8_t*>(qI), qI_scale, static_cast<const uint8_t*>(kI),
-                       kI_scale, n_q, N_cap, n_chunks, w, q_pos, m, n_entries, scores);
+    hipLaunchKernelGGL((indexer_mfma_kernel<true, true>), grid, block, 0, s, q8, qI_scale, k8,
+                       kI_scale, n_q, N_cap, n_chunks, w, q_pos, m, n_entries, scores, hist);
   return hipGetLastError();
 }
 

@@ -28,14 +28,7 @@ constexpr int kLdsMaxRow = 36864;
 constexpr int kRowThreads = 1024;
 constexpr int kSeg = 8192;
 constexpr int kSegThreads = 256;
-constexpr int kHistBins = 4096;
-
-__device__ __forceinline__ uint32_t score_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) u = 0xff800000u;  // NaN -> -inf
-  if (u == 0x80000000u) u = 0u;                          // -0 -> +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
+constexpr int kHistBins = kScoreHistBins;
 
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
@@ -215,7 +208,7 @@ __global__ __launch_bounds__(kSegThreads) void topk_hist_kernel(
   for (int i = threadIdx.x; i < kHistBins; i += kSegThreads) h[i] = 0;
   __syncthreads();
   const float* src = scores + row * N_cap;
-  for (int i = s0 + threadIdx.x; i < s1; i += kSegThreads) atomicAdd(&h[score_key(src[i]) >> 20], 1u);
+  for (int i = s0 + threadIdx.x; i < s1; i += kSegThreads) atomicAdd(&h[score_bin(score_key(src[i]))], 1u);
   __syncthreads();
   uint32_t* gh = ghist + row * kHistBins;
   for (int i = threadIdx.x; i < kHistBins; i += kSegThreads)
@@ -223,8 +216,10 @@ __global__ __launch_bounds__(kSegThreads) void topk_hist_kernel(
 }
 
 // (bin, count above bin) of the k-th largest key of a row; bin = -1 when every
-// visible entry is selected.
-__device__ void row_threshold(const uint32_t* gh, int vis, int k, int* sh_bin, int* sh_above) {
+// visible entry is selected.  The row histogram is first copied to LDS with
+// coalesced loads (lh: kHistBins words of shared memory); call from all threads.
+__device__ void row_threshold(const uint32_t* gh, uint32_t* lh, int vis, int k, int* sh_bin,
+                              int* sh_above) {
   if (vis <= k) {
     if (threadIdx.x == 0) {
       *sh_bin = -1;
@@ -232,14 +227,62 @@ __device__ void row_threshold(const uint32_t* gh, int vis, int k, int* sh_bin, i
     }
     return;
   }
-  if (threadIdx.x < 64) find_bin_wave(gh, kHistBins, k, sh_bin, sh_above);
+  const uint4* g4 = reinterpret_cast<const uint4*>(gh);
+  uint4* l4 = reinterpret_cast<uint4*>(lh);
+  for (int i = threadIdx.x; i < kHistBins / 4; i += blockDim.x) l4[i] = g4[i];
+  __syncthreads();
+  if (threadIdx.x < 64) find_bin_wave(lh, kHistBins, k, sh_bin, sh_above);
 }
+
+// Exclusive prefix sums of two counters over the workgroup (thread order);
+// also returns the totals.  All threads must call it.
+template <int NT>
+__device__ __forceinline__ void block_scan2(int a, int b, int* ex_a, int* ex_b, int* tot_a,
+                                            int* tot_b, int* sh /* 2 * NT/64 ints */) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int ia = a, ib = b;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int ta = __shfl_up(ia, o, 64), tb = __shfl_up(ib, o, 64);
+    if (lane >= o) {
+      ia += ta;
+      ib += tb;
+    }
+  }
+  if (lane == 63) {
+    sh[wv] = ia;
+    sh[NT / 64 + wv] = ib;
+  }
+  __syncthreads();
+  int oa = 0, ob = 0, ta = 0, tb = 0;
+#pragma unroll
+  for (int x = 0; x < NT / 64; ++x) {
+    const int va = sh[x], vb = sh[NT / 64 + x];
+    if (x < wv) {
+      oa += va;
+      ob += vb;
+    }
+    ta += va;
+    tb += vb;
+  }
+  *ex_a = oa + ia - a;
+  *ex_b = ob + ib - b;
+  *tot_a = ta;
+  *tot_b = tb;
+}
+
+// One workgroup per (row, segment of kSeg scores): thread t owns the contiguous
+// chunk [s0 + kChunk*t, +kChunk) and loads it all before compacting, so the
+// memory latency is paid once; one block scan gives every thread its output
+// offsets in index order.
+constexpr int kChunk = kSeg / kSegThreads;  // 32
 
 __global__ __launch_bounds__(kSegThreads) void topk_collect_kernel(
     const float* __restrict__ scores, int N_cap, int n_q, const int32_t* __restrict__ q_pos, int m,
     const int32_t* __restrict__ n_entries, int k, int n_seg, WideWs ws) {
   __shared__ int sh_bin, sh_above;
-  __shared__ uint32_t wsure[kSegThreads / 64], wcand[kSegThreads / 64];
+  __shared__ int scan_sh[2 * kSegThreads / 64];
+  __shared__ uint32_t lh[kHistBins];
   const long long row = blockIdx.x / n_seg;
   const int seg = blockIdx.x % n_seg;
   const int b = static_cast<int>(row / n_q);
@@ -247,50 +290,47 @@ __global__ __launch_bounds__(kSegThreads) void topk_collect_kernel(
   const int s0 = seg * kSeg;
   const int s1 = min(s0 + kSeg, vis);
   const long long rs = row * n_seg + seg;
-  row_threshold(ws.hist + row * kHistBins, vis, k, &sh_bin, &sh_above);
+  const int tid = threadIdx.x;
+  // issue the chunk's loads first
+  const int c0 = s0 + kChunk * tid;
+  const float* src = scores + row * N_cap;
+  float v[kChunk];
+#pragma unroll
+  for (int i = 0; i < kChunk; ++i) v[i] = c0 + i < s1 ? src[c0 + i] : 0.f;
+  row_threshold(ws.hist + row * kHistBins, lh, vis, k, &sh_bin, &sh_above);
   __syncthreads();
   const int bstar = sh_bin;
-  const float* src = scores + row * N_cap;
+  uint32_t key[kChunk];
+  int ns = 0, nc = 0;
+#pragma unroll
+  for (int i = 0; i < kChunk; ++i) {
+    key[i] = score_key(v[i]);
+    const int bin = static_cast<int>(score_bin(key[i]));
+    const bool in = c0 + i < s1;
+    ns += (in && bin > bstar);
+    nc += (in && bin == bstar);
+  }
+  int os, oc, ts, tc;
+  block_scan2<kSegThreads>(ns, nc, &os, &oc, &ts, &tc, scan_sh);
   int32_t* sure = ws.sure + rs * k;
   uint32_t* ckey = ws.cand_key + rs * kSeg;
   int32_t* cidx = ws.cand_idx + rs * kSeg;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int run_s = 0, run_c = 0;
-  for (int base = s0; base < s1; base += kSegThreads) {
-    const int i = base + tid;
-    const uint32_t key = i < s1 ? score_key(src[i]) : 0u;
-    const int bin = static_cast<int>(key >> 20);
-    const bool is_s = i < s1 && bin > bstar;
-    const bool is_c = i < s1 && bin == bstar;
-    const uint64_t bs = __ballot(is_s), bc = __ballot(is_c);
-    if (lane == 0) {
-      wsure[wv] = __popcll(bs);
-      wcand[wv] = __popcll(bc);
+#pragma unroll
+  for (int i = 0; i < kChunk; ++i) {
+    const int bin = static_cast<int>(score_bin(key[i]));
+    const bool in = c0 + i < s1;
+    if (in && bin > bstar) {
+      if (os < k) sure[os] = c0 + i;
+      ++os;
+    } else if (in && bin == bstar) {
+      ckey[oc] = key[i];
+      cidx[oc] = c0 + i;
+      ++oc;
     }
-    __syncthreads();
-    int os = run_s, oc = run_c, ts = 0, tc = 0;
-    for (int x = 0; x < kSegThreads / 64; ++x) {
-      if (x < wv) {
-        os += wsure[x];
-        oc += wcand[x];
-      }
-      ts += wsure[x];
-      tc += wcand[x];
-    }
-    const int ps = os + lanes_below(bs);
-    if (is_s && ps < k) sure[ps] = i;
-    if (is_c) {
-      const int p = oc + lanes_below(bc);
-      ckey[p] = key;
-      cidx[p] = i;
-    }
-    run_s += ts;
-    run_c += tc;
-    __syncthreads();
   }
   if (tid == 0) {
-    ws.sure_cnt[rs] = s0 < vis ? run_s : 0;
-    ws.cand_cnt[rs] = s0 < vis ? run_c : 0;
+    ws.sure_cnt[rs] = s0 < vis ? ts : 0;
+    ws.cand_cnt[rs] = s0 < vis ? tc : 0;
   }
 }
 
@@ -305,41 +345,99 @@ __device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int x) {
 
 constexpr int kMaxK = 4096;
 constexpr int kMaxSeg = 1024;
+constexpr int kCandLds = 8192;
 
+// segment containing flat position p of a concatenation with exclusive
+// prefix offsets off[0..n] (off[n] = total)
+__device__ __forceinline__ int seg_of(const int* off, int n, int p) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= p) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// One workgroup per row: gather the surely selected indices and the candidate
+// (key, index) pairs of all segments into LDS with independent loads, radix-
+// select the remaining `need` among the candidates on the low 20 key bits, and
+// merge the two ascending lists into the row's output.
 __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
-    int N_cap, int n_q, const int32_t* __restrict__ q_pos, int m, const int32_t* __restrict__ n_entries, int k,
-    int n_seg, WideWs ws, int32_t* __restrict__ idx) {
+    int N_cap, int n_q, const int32_t* __restrict__ q_pos, int m, const int32_t* __restrict__ n_entries,
+    int k, int n_seg, WideWs ws, int32_t* __restrict__ idx) {
   __shared__ int32_t S[kMaxK], Ch[kMaxK];
   __shared__ int seg_s[kMaxSeg + 1], seg_c[kMaxSeg + 1];
   __shared__ uint32_t hist[256];
   __shared__ int sh_bin, sh_above, sh_b2, sh_a2;
   __shared__ uint32_t wgt[kRowThreads / 64], weq[kRowThreads / 64];
+  __shared__ uint32_t lh[kHistBins];
+  __shared__ uint32_t ck_s[kCandLds];
+  __shared__ int32_t ci_s[kCandLds];
   const long long row = blockIdx.x;
   const int b = static_cast<int>(row / n_q);
   const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int32_t* out = idx + row * k;
-  row_threshold(ws.hist + row * kHistBins, vis, k, &sh_bin, &sh_above);
-  if (tid == 0) {
-    int a = 0, c = 0;
-    for (int s = 0; s < n_seg; ++s) {
-      seg_s[s] = a;
-      seg_c[s] = c;
-      a += ws.sure_cnt[row * n_seg + s];
-      c += ws.cand_cnt[row * n_seg + s];
-    }
-    seg_s[n_seg] = a;
-    seg_c[n_seg] = c;
+  row_threshold(ws.hist + row * kHistBins, lh, vis, k, &sh_bin, &sh_above);
+  for (int s = tid; s < n_seg; s += kRowThreads) {
+    seg_s[s] = ws.sure_cnt[row * n_seg + s];
+    seg_c[s] = ws.cand_cnt[row * n_seg + s];
   }
   __syncthreads();
-  const int nS = seg_s[n_seg];
-  // gather the surely selected indices (already ascending per segment)
-  for (int s = 0; s < n_seg; ++s) {
-    const int cnt = seg_s[s + 1] - seg_s[s];
-    const int32_t* src = ws.sure + (row * n_seg + s) * k;
-    for (int i = tid; i < cnt; i += kRowThreads)
-      if (seg_s[s] + i < kMaxK) S[seg_s[s] + i] = src[i];
+  if (wv == 0) {  // exclusive prefix sums, 64 segments a round
+    int run_s = 0, run_c = 0;
+    for (int base = 0; base < n_seg; base += 64) {
+      const int s = base + lane;
+      const int vs = s < n_seg ? seg_s[s] : 0, vc = s < n_seg ? seg_c[s] : 0;
+      int is = vs, ic = vc;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int ts = __shfl_up(is, o, 64), tc = __shfl_up(ic, o, 64);
+        if (lane >= o) {
+          is += ts;
+          ic += tc;
+        }
+      }
+      if (s < n_seg) {
+        seg_s[s] = run_s + is - vs;
+        seg_c[s] = run_c + ic - vc;
+      }
+      run_s += __shfl(is, 63, 64);
+      run_c += __shfl(ic, 63, 64);
+    }
+    if (lane == 0) {
+      seg_s[n_seg] = run_s;
+      seg_c[n_seg] = run_c;
+    }
   }
+  __syncthreads();
+  const int nS = min(seg_s[n_seg], k);
+  const int nCand = seg_c[n_seg];
+  const bool cand_in_lds = nCand <= kCandLds;
+  // parallel gathers (ascending index order is the concatenation order)
+  for (int p = tid; p < nS; p += kRowThreads) {
+    const int s = seg_of(seg_s, n_seg, p);
+    S[p] = ws.sure[(row * n_seg + s) * k + (p - seg_s[s])];
+  }
+  if (cand_in_lds) {
+    for (int p = tid; p < nCand; p += kRowThreads) {
+      const int s = seg_of(seg_c, n_seg, p);
+      const long long off = (row * n_seg + s) * kSeg + (p - seg_c[s]);
+      ck_s[p] = ws.cand_key[off];
+      ci_s[p] = ws.cand_idx[off];
+    }
+  }
+  __syncthreads();
+  auto cand_key = [&](int p) -> uint32_t {
+    if (cand_in_lds) return ck_s[p];
+    const int s = seg_of(seg_c, n_seg, p);
+    return ws.cand_key[(row * n_seg + s) * kSeg + (p - seg_c[s])];
+  };
+  auto cand_idx = [&](int p) -> int32_t {
+    if (cand_in_lds) return ci_s[p];
+    const int s = seg_of(seg_c, n_seg, p);
+    return ws.cand_idx[(row * n_seg + s) * kSeg + (p - seg_c[s])];
+  };
   const int need = vis <= k ? 0 : k - sh_above;
   int nC = 0;
   if (need > 0) {
@@ -348,18 +446,14 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
     int remaining = need;
     const int shifts[3] = {12, 4, 0};
     const int widths[3] = {8, 8, 4};
-    for (int p = 0; p < 3; ++p) {
-      const int sh = shifts[p];
-      const uint32_t dm = (1u << widths[p]) - 1u;
+    for (int pass = 0; pass < 3; ++pass) {
+      const int sh = shifts[pass];
+      const uint32_t dm = (1u << widths[pass]) - 1u;
       for (int i = tid; i < 256; i += kRowThreads) hist[i] = 0;
       __syncthreads();
-      for (int s = 0; s < n_seg; ++s) {
-        const int cnt = seg_c[s + 1] - seg_c[s];
-        const uint32_t* ck = ws.cand_key + (row * n_seg + s) * kSeg;
-        for (int i = tid; i < cnt; i += kRowThreads) {
-          const uint32_t key = ck[i];
-          if ((key & mask) == prefix) atomicAdd(&hist[(key >> sh) & dm], 1u);
-        }
+      for (int p = tid; p < nCand; p += kRowThreads) {
+        const uint32_t key = cand_key(p);
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> sh) & dm], 1u);
       }
       __syncthreads();
       if (tid < 64) find_bin_wave(hist, 256, remaining, &sh_b2, &sh_a2);
@@ -373,57 +467,73 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
     const uint32_t T = prefix;
     const int need_eq = remaining;
     int run_gt = 0, run_eq = 0;
-    for (int s = 0; s < n_seg; ++s) {
-      const int cnt = seg_c[s + 1] - seg_c[s];
-      const uint32_t* ck = ws.cand_key + (row * n_seg + s) * kSeg;
-      const int32_t* ci = ws.cand_idx + (row * n_seg + s) * kSeg;
-      for (int base = 0; base < cnt; base += kRowThreads) {
-        const int i = base + tid;
-        const uint32_t key = i < cnt ? (ck[i] & 0xfffffu) : 0u;
-        const bool gt = i < cnt && key > T;
-        const bool eq = i < cnt && key == T;
-        const uint64_t bg = __ballot(gt), be = __ballot(eq);
-        if (lane == 0) {
-          wgt[wv] = __popcll(bg);
-          weq[wv] = __popcll(be);
-        }
-        __syncthreads();
-        int og = run_gt, oe = run_eq, tg = 0, te = 0;
-        for (int x = 0; x < kRowThreads / 64; ++x) {
-          if (x < wv) {
-            og += wgt[x];
-            oe += weq[x];
-          }
-          tg += wgt[x];
-          te += weq[x];
-        }
-        const int gb = og + lanes_below(bg), eb = oe + lanes_below(be);
-        const int pc = gb + min(eb, need_eq);
-        if ((gt || (eq && eb < need_eq)) && pc < need) Ch[pc] = ci[i];
-        run_gt += tg;
-        run_eq += te;
-        __syncthreads();
+    for (int base = 0; base < nCand; base += kRowThreads) {
+      const int p = base + tid;
+      const uint32_t key = p < nCand ? (cand_key(p) & 0xfffffu) : 0u;
+      const bool gt = p < nCand && key > T;
+      const bool eq = p < nCand && key == T;
+      const uint64_t bg = __ballot(gt), be = __ballot(eq);
+      if (lane == 0) {
+        wgt[wv] = __popcll(bg);
+        weq[wv] = __popcll(be);
       }
+      __syncthreads();
+      int og = run_gt, oe = run_eq, tg = 0, te = 0;
+      for (int x = 0; x < kRowThreads / 64; ++x) {
+        if (x < wv) {
+          og += wgt[x];
+          oe += weq[x];
+        }
+        tg += wgt[x];
+        te += weq[x];
+      }
+      const int gb = og + lanes_below(bg), eb = oe + lanes_below(be);
+      const int pc = gb + min(eb, need_eq);
+      if ((gt || (eq && eb < need_eq)) && pc < need) Ch[pc] = cand_idx(p);
+      run_gt += tg;
+      run_eq += te;
+      __syncthreads();
     }
     nC = need;
   }
   __syncthreads();
   // merge the two ascending lists
-  const int nSc = min(nS, k);
-  for (int i = tid; i < nSc; i += kRowThreads) {
+  for (int i = tid; i < nS; i += kRowThreads) {
     const int pos = i + lower_bound_i32(Ch, nC, S[i]);
     if (pos < k) out[pos] = S[i];
   }
   for (int i = tid; i < nC; i += kRowThreads) {
-    const int pos = i + lower_bound_i32(S, nSc, Ch[i]);
+    const int pos = i + lower_bound_i32(S, nS, Ch[i]);
     if (pos < k) out[pos] = Ch[i];
   }
-  for (int i = nSc + nC + tid; i < k; i += kRowThreads) out[i] = -1;
+  for (int i = nS + nC + tid; i < k; i += kRowThreads) out[i] = -1;
 }
 
 }  // namespace
 
 static int n_segments(int N_cap) { return (N_cap + kSeg - 1) / kSeg; }
+
+uint32_t* topk_hist_in_workspace(void* ws, int B, int n_q, int N_cap, int k) {
+  if (N_cap <= kLdsMaxRow || ws == nullptr) return nullptr;
+  return wide_ws(ws, static_cast<long long>(B) * n_q, n_segments(N_cap), k).hist;
+}
+
+hipError_t launch_topk_from_hist(int B, int n_q, int N_cap, const float* scores,
+                                 const int32_t* q_pos, int m, const int32_t* n_entries, int k,
+                                 int32_t* idx, void* ws, hipStream_t s) {
+  const long long rows = static_cast<long long>(B) * n_q;
+  if (rows == 0) return hipSuccess;
+  if (N_cap <= kLdsMaxRow) return launch_topk(B, n_q, N_cap, scores, q_pos, m, n_entries, k, idx, ws, s);
+  const int n_seg = n_segments(N_cap);
+  if (n_seg > kMaxSeg || k > kMaxK) return hipErrorInvalidValue;
+  WideWs w = wide_ws(ws, rows, n_seg, k);
+  const dim3 g2(static_cast<unsigned>(rows * n_seg));
+  hipLaunchKernelGGL(topk_collect_kernel, g2, dim3(kSegThreads), 0, s, scores, N_cap, n_q, q_pos, m,
+                     n_entries, k, n_seg, w);
+  hipLaunchKernelGGL(topk_finish_kernel, dim3(static_cast<unsigned>(rows)), dim3(kRowThreads), 0, s,
+                     N_cap, n_q, q_pos, m, n_entries, k, n_seg, w, idx);
+  return hipGetLastError();
+}
 
 size_t topk_workspace_bytes(int B, int n_q, int N_cap, int k) {
   if (N_cap <= kLdsMaxRow) return 0;

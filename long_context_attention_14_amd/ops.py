@@ -175,7 +175,8 @@ class DecodeLayerState:
 
 
 def lca_decode_step(layer: DecodeLayerState, tokC, tokZ, q, out, out_fmt, qI=None, qI_scale=None,
-                    w=None, lse=None, idx_out=None, workspace=None, stream=None):
+                    w=None, lse=None, idx_out=None, workspace=None, stream=None, stage_events=None):
+    """stage_events: optional sequence of 5 raw hipEvent_t handles (ints or None)."""
     need = layer.workspace_size()
     if workspace is None:
         if layer.workspace is None or layer.workspace.numel() < need:
@@ -197,6 +198,9 @@ def lca_decode_step(layer: DecodeLayerState, tokC, tokZ, q, out, out_fmt, qI=Non
     io.out = _ptr(out, row_bytes(out_fmt, c) * B * H, "out")
     io.lse = _ptr(lse, 4 * B * H, "lse", True)
     io.out_dtype = FMT[out_fmt]
+    if stage_events is not None:
+        for i, e in enumerate(stage_events):
+            io.stage_events[i] = e
     return check("lca_decode_step", lib().lca_decode_step(
         ctypes.byref(layer.struct), ctypes.byref(io), _ptr(workspace, need, "workspace"), need,
         _stream(stream)))

@@ -18,7 +18,11 @@ from synth.configs import (CSA_DECODE_1M, CSA_PREFILL_CHUNK, HCA_DECODE, HYBRID_
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 OUT_TOL = {"f32": 1e-4, "bf16": 2e-2}
-LSE_TOL = {"f32": 1e-5, "bf16": 2e-3}
+# lse: the fp32 path is exact to rounding; the bf16 path feeds the MFMA with the
+# normalised query rounded to bf16, which moves each logit tau*q.k by at most
+# 2^-9 * tau * |q| |k| = 2^-9 * sqrt(c) for RMS-normalised q and k (c = 512),
+# and rounds P to bf16 (at most 2^-9 relative in the denominator).
+LSE_TOL = {"f32": 1e-5, "bf16": 2.0 ** -9 * 512 ** 0.5 * 1.01 + 2.0 ** -8}
 
 
 def say(*a):
