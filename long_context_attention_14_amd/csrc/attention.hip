@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_generic_kernel(
 #pragma unroll
     for (int i = 0; i < CPL; ++i) ss += v[i] * v[i];
     ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss / static_cast<float>(c) + eps);
+    const float r = rsqrt_hw(ss / static_cast<float>(c) + eps);
 #pragma unroll
     for (int i = 0; i < CPL; ++i) qs[hh * CP + lane * CPL + i] = v[i] * r;
   }
@@ -219,16 +219,12 @@ constexpr int kMH = 64;            // heads
 constexpr int kQS = kMC + 8;       // LDS row stride of Q and KV tiles (bf16 elements)
 constexpr int kPS = kMT + 8;       // LDS row stride of P (bf16 elements)
 constexpr int kSS = kMT + 1;       // LDS row stride of S (floats)
-constexpr int kMfmaSplitRows = 128;
+constexpr int kMfmaSplitRows = 64;
 
 __device__ __forceinline__ v8bf_t as_v8bf(uint4 u) { return __builtin_bit_cast(v8bf_t, u); }
 
 __device__ __forceinline__ v16f_t mfma_bf16(const v8bf_t& a, const v8bf_t& b, const v16f_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
 }
 
 template <int KVFMT>
@@ -244,7 +240,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
   __shared__ float s_s[kMH * kSS];
   __shared__ __attribute__((aligned(16))) uint16_t p_s[kMH * kPS];
   __shared__ float m_s[kMH], l_s[kMH], a_s[kMH];
-  __shared__ const uint8_t* rowp_s[kMT];
+  __shared__ const uint8_t* rowp_s[2][kMT];
 
   const int split = blockIdx.x % n_splits;
   const long long row = blockIdx.x / n_splits;
@@ -268,22 +264,54 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
   const int s_begin = split * split_rows;
   const int s_end = min(s_begin + split_rows, NT);
 
-  // normalised queries -> bf16 in LDS (wave wv: heads wv, wv+4, ...)
+  // row pointers of the first tile (its index loads overlap the query phase)
+  if (tid < kMT) rowp_s[0][tid] = s_begin + tid < s_end ? slot_row(sc, s_begin + tid) : nullptr;
+  // normalised queries -> bf16 in LDS (wave wv: heads wv, wv+4, ...); all of a
+  // wave's loads are issued before the first reduction
   const size_t q_row = row_bytes(q_fmt, kMC);
-  for (int h = wv; h < kMH; h += 4) {
-    float v[8];
-    load_row<8>(q + (static_cast<size_t>(row) * kMH + h) * q_row, q_fmt, kMC, lane, v);
-    float ss = 0.f;
+  if (q_fmt == LCA_BF16) {
+    uint4 raw[kMH / 4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
-    ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss / static_cast<float>(kMC) + eps);
-    uint4 pk;
-    pk.x = pack_bf16(v[0] * r, v[1] * r);
-    pk.y = pack_bf16(v[2] * r, v[3] * r);
-    pk.z = pack_bf16(v[4] * r, v[5] * r);
-    pk.w = pack_bf16(v[6] * r, v[7] * r);
-    *reinterpret_cast<uint4*>(&q_s[h * kQS + lane * 8]) = pk;
+    for (int i = 0; i < kMH / 4; ++i)
+      raw[i] = *reinterpret_cast<const uint4*>(q + (static_cast<size_t>(row) * kMH + wv + 4 * i) * q_row +
+                                               lane * 16);
+#pragma unroll
+    for (int i = 0; i < kMH / 4; ++i) {
+      const uint32_t w4[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = bf16_to_f32(static_cast<uint16_t>(w4[e] & 0xffffu));
+        v[2 * e + 1] = bf16_to_f32(static_cast<uint16_t>(w4[e] >> 16));
+      }
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+      ss = wave_sum(ss);
+      const float r = rsqrt_hw(ss / static_cast<float>(kMC) + eps);
+      uint4 pk;
+      pk.x = pack_bf16(v[0] * r, v[1] * r);
+      pk.y = pack_bf16(v[2] * r, v[3] * r);
+      pk.z = pack_bf16(v[4] * r, v[5] * r);
+      pk.w = pack_bf16(v[6] * r, v[7] * r);
+      *reinterpret_cast<uint4*>(&q_s[(wv + 4 * i) * kQS + lane * 8]) = pk;
+    }
+  } else {
+    for (int h = wv; h < kMH; h += 4) {
+      float v[8];
+      load_row<8>(q + (static_cast<size_t>(row) * kMH + h) * q_row, q_fmt, kMC, lane, v);
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
+      ss = wave_sum(ss);
+      const float r = rsqrt_hw(ss / static_cast<float>(kMC) + eps);
+      uint4 pk;
+      pk.x = pack_bf16(v[0] * r, v[1] * r);
+      pk.y = pack_bf16(v[2] * r, v[3] * r);
+      pk.z = pack_bf16(v[4] * r, v[5] * r);
+      pk.w = pack_bf16(v[6] * r, v[7] * r);
+      *reinterpret_cast<uint4*>(&q_s[h * kQS + lane * 8]) = pk;
+    }
   }
   if (tid < kMH) {
     m_s[tid] = -INFINITY;
@@ -297,52 +325,71 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     for (int dt = 0; dt < 4; ++dt) o[ht][dt] = v16f_t{0};
 
   const int sh = wv >> 1, sr = wv & 1;  // this wave's S tile
-  for (int base = s_begin; base < s_end; base += kMT) {
-    __syncthreads();  // previous tile fully consumed
-    if (tid < kMT) rowp_s[tid] = base + tid < s_end ? slot_row(sc, base + tid) : nullptr;
-    __syncthreads();
-    // stage the tile: wave wv loads rows wv, wv+4, ... (one 1 KiB row per load)
-    for (int r = wv; r < kMT; r += 4) {
-      const uint8_t* rp = rowp_s[r];
-      uint4 v = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+  // raw rows of a tile, wave wv holding rows wv, wv+4, ...: issued one tile ahead
+  uint4 raw[kMT / 4];
+  auto load_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kMT / 4; ++i) {
+      const uint8_t* rp = rowp_s[buf][wv + 4 * i];
+      raw[i] = make_uint4(0, 0, 0, 0);
       if (rp) {
         if (KVFMT == LCA_BF16) {
-          v = *reinterpret_cast<const uint4*>(rp + lane * 16);
-        } else if (lane < 56) {  // 8 fp8 dims -> bf16
+          raw[i] = *reinterpret_cast<const uint4*>(rp + lane * 16);
+        } else if (lane < 56) {
           const uint2 f = *reinterpret_cast<const uint2*>(rp + lane * 8);
-          float x[8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x[i] = e4m3_to_f32((f.x >> (8 * i)) & 0xffu);
-            x[4 + i] = e4m3_to_f32((f.y >> (8 * i)) & 0xffu);
-          }
-          v.x = pack_bf16(x[0], x[1]);
-          v.y = pack_bf16(x[2], x[3]);
-          v.z = pack_bf16(x[4], x[5]);
-          v.w = pack_bf16(x[6], x[7]);
-        } else {  // bf16 rope dims
-          v = *reinterpret_cast<const uint4*>(rp + 448 + (lane - 56) * 16);
+          raw[i].x = f.x;
+          raw[i].y = f.y;
+        } else {
+          raw[i] = *reinterpret_cast<const uint4*>(rp + 448 + (lane - 56) * 16);
         }
       }
-      *reinterpret_cast<uint4*>(&kv_s[r * kQS + lane * 8]) = v;
     }
+  };
+  load_tile(0);
+  int cur = 0;
+  for (int base = s_begin; base < s_end; base += kMT, cur ^= 1) {
+    // stage this tile's rows as bf16 and resolve the next tile's row pointers
+#pragma unroll
+    for (int i = 0; i < kMT / 4; ++i) {
+      uint4 v = raw[i];
+      if (KVFMT != LCA_BF16 && lane < 56) {  // 8 fp8 dims -> bf16
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = e4m3_to_f32((raw[i].x >> (8 * e)) & 0xffu);
+          x[4 + e] = e4m3_to_f32((raw[i].y >> (8 * e)) & 0xffu);
+        }
+        v.x = pack_bf16(x[0], x[1]);
+        v.y = pack_bf16(x[2], x[3]);
+        v.z = pack_bf16(x[4], x[5]);
+        v.w = pack_bf16(x[6], x[7]);
+      }
+      *reinterpret_cast<uint4*>(&kv_s[(wv + 4 * i) * kQS + lane * 8]) = v;
+    }
+    const int nbase = base + kMT;
+    if (tid < kMT) rowp_s[cur ^ 1][tid] = nbase + tid < s_end ? slot_row(sc, nbase + tid) : nullptr;
     __syncthreads();
-    // S tile of this wave
+    if (nbase < s_end) load_tile(cur ^ 1);  // in flight during this tile's compute
+    // S tile of this wave (two accumulator chains)
     {
-      v16f_t acc = v16f_t{0};
+      v16f_t acc0 = v16f_t{0}, acc1 = v16f_t{0};
       const uint16_t* qa = &q_s[(32 * sh + j32) * kQS + 8 * g];
       const uint16_t* kb = &kv_s[(32 * sr + j32) * kQS + 8 * g];
 #pragma unroll 8
-      for (int ks = 0; ks < kMC / 16; ++ks) {
-        const uint4 a = *reinterpret_cast<const uint4*>(qa + 16 * ks);
-        const uint4 bb = *reinterpret_cast<const uint4*>(kb + 16 * ks);
-        acc = mfma_bf16(as_v8bf(a), as_v8bf(bb), acc);
+      for (int ks = 0; ks < kMC / 16; ks += 2) {
+        const uint4 a0 = *reinterpret_cast<const uint4*>(qa + 16 * ks);
+        const uint4 b0 = *reinterpret_cast<const uint4*>(kb + 16 * ks);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(qa + 16 * ks + 16);
+        const uint4 b1 = *reinterpret_cast<const uint4*>(kb + 16 * ks + 16);
+        acc0 = mfma_bf16(as_v8bf(a0), as_v8bf(b0), acc0);
+        acc1 = mfma_bf16(as_v8bf(a1), as_v8bf(b1), acc1);
       }
-      const bool valid = rowp_s[32 * sr + j32] != nullptr;
+      const bool valid = rowp_s[cur][32 * sr + j32] != nullptr;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int h = 32 * sh + 8 * (r >> 2) + 4 * g + (r & 3);
-        s_s[h * kSS + 32 * sr + j32] = valid ? acc[r] * tau : -INFINITY;
+        s_s[h * kSS + 32 * sr + j32] = valid ? (acc0[r] + acc1[r]) * tau : -INFINITY;
       }
     }
     __syncthreads();
@@ -414,55 +461,78 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
         for (int ht = 0; ht < 2; ++ht) o[ht][dt] = mfma_bf16(A[ht], Bv, o[ht][dt]);
       }
     }
+    __syncthreads();  // kv_s, p_s and rowp_s[cur] are rewritten by the next tile
+  }
+
+  // epilogue: O / l (with the sink when this is the only split); lse = m + log l.
+  // Per-head factors go to LDS, then O is written through LDS (32 heads at a
+  // time, fp32, reusing the KV tile buffer) so that the global stores are
+  // contiguous 16-byte chunks.
+  float* fac_s = s_s;  // [kMH] output factors (S is no longer needed)
+  if (tid < kMH) {
+    const int h = tid;
+    const float l = l_s[h];
+    float lse_v = l > 0.f ? m_s[h] + __logf(l) : -INFINITY;
+    float f = l > 0.f ? 1.0f / l : 0.f;
+    if (n_splits == 1 && sink) {
+      const float sk = sink[h];
+      if (lse_v == -INFINITY) {
+        lse_v = sk;
+      } else {
+        const float mx = fmaxf(lse_v, sk);
+        const float tot = mx + __logf(__expf(lse_v - mx) + __expf(sk - mx));
+        f *= __expf(lse_v - tot);
+        lse_v = tot;
+      }
+    }
+    fac_s[h] = f;
+    if (n_splits == 1) {
+      if (lse) lse[static_cast<size_t>(row) * kMH + h] = lse_v;
+    } else {
+      part_lse[(static_cast<size_t>(row) * n_splits + split) * kMH + h] = lse_v;
+    }
   }
   __syncthreads();
-
-  // epilogue: O / l; lse = m + log l
+  float* ost = reinterpret_cast<float*>(kv_s);  // [32 heads][kMC] fp32 = 64 KiB
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int h = 32 * ht + 8 * (r >> 2) + 4 * g + (r & 3);
-      const float l = l_s[h];
-      float lse_v = l > 0.f ? m_s[h] + __logf(l) : -INFINITY;
-      float f = l > 0.f ? 1.0f / l : 0.f;
-      if (n_splits == 1 && sink) {
-        const float sk = sink[h];
-        if (lse_v == -INFINITY) {
-          lse_v = sk;
-        } else {
-          const float mx = fmaxf(lse_v, sk);
-          const float tot = mx + __logf(__expf(lse_v - mx) + __expf(sk - mx));
-          f *= __expf(lse_v - tot);
-          lse_v = tot;
-        }
-      }
+      const int hl = 8 * (r >> 2) + 4 * g + (r & 3);
+      const float f = fac_s[32 * ht + hl];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int dim = 128 * wv + 32 * dt + j32;
-        const float v = o[ht][dt][r] * f;
-        if (n_splits == 1) {
-          const size_t oi = (static_cast<size_t>(row) * kMH + h) * kMC + dim;
-          if (out_fmt == LCA_F32)
-            reinterpret_cast<float*>(out)[oi] = v;
-          else
-            reinterpret_cast<uint16_t*>(out)[oi] = f32_to_bf16(v);
+      for (int dt = 0; dt < 4; ++dt) ost[hl * kMC + 128 * wv + 32 * dt + j32] = o[ht][dt][r] * f;
+    }
+    __syncthreads();
+    // 32 heads x 512 fp32 = 4096 chunks of 16 B; thread tid writes chunks tid + 256 i
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int chunk = tid + 256 * i;
+      const int hl = chunk >> 7, d4 = (chunk & 127) * 4;
+      const float4 v = *reinterpret_cast<const float4*>(&ost[hl * kMC + d4]);
+      const int h = 32 * ht + hl;
+      if (n_splits == 1) {
+        const size_t oi = (static_cast<size_t>(row) * kMH + h) * kMC + d4;
+        if (out_fmt == LCA_F32) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + oi) = v;
         } else {
-          part_o[((static_cast<size_t>(row) * n_splits + split) * kMH + h) * kMC + dim] = v;
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + oi) =
+              make_uint2(pack_bf16(v.x, v.y), pack_bf16(v.z, v.w));
         }
-      }
-      if (wv == 0 && j32 == 0) {
-        if (n_splits == 1) {
-          if (lse) lse[static_cast<size_t>(row) * kMH + h] = lse_v;
-        } else {
-          part_lse[(static_cast<size_t>(row) * n_splits + split) * kMH + h] = lse_v;
-        }
+      } else {
+        *reinterpret_cast<float4*>(
+            &part_o[((static_cast<size_t>(row) * n_splits + split) * kMH + h) * kMC + d4]) = v;
       }
     }
+    __syncthreads();
   }
 }
 
-// One wave per (query row, head): combine the splits in order.
+// One wave per (query row, head): combine the splits in split order.  Lane s
+// reads split s's lse (wave-wide max and weights by shuffles), and every
+// split's partial row is loaded before the weighted sum.
+constexpr int kMaxMergeSplits = 64;
+
 template <int CPL>
 __global__ __launch_bounds__(256) void attn_merge_kernel(
     long long rows, int H, int c, int n_splits, const float* __restrict__ part_o,
@@ -473,24 +543,34 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
   const int lane = threadIdx.x & 63;
   const long long row = rh / H;
   const int h = static_cast<int>(rh % H);
-  float mx = sink ? sink[h] : -INFINITY;
-  for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, part_lse[(row * n_splits + s) * H + h]);
+  const float my_lse = lane < n_splits ? part_lse[(row * n_splits + lane) * H + h] : -INFINITY;
+  float mx = fmaxf(wave_max(my_lse), sink ? sink[h] : -INFINITY);
   float acc[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
   float den = 0.f;
   if (mx != -INFINITY) {
+    const float my_w = my_lse == -INFINITY ? 0.f : __expf(my_lse - mx);
     if (sink) den = __expf(sink[h] - mx);
-    for (int s = 0; s < n_splits; ++s) {
-      const long long pr = (row * n_splits + s) * H + h;
-      const float ls = part_lse[pr];
-      if (ls == -INFINITY) continue;
-      const float wgt = __expf(ls - mx);
-      den += wgt;
-      float v[CPL];
-      load_row<CPL>(part_o + pr * c, LCA_F32, c, lane, v);
+    for (int s0 = 0; s0 < n_splits; s0 += 8) {
+      float v[8][CPL];
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) acc[i] = fmaf(wgt, v[i], acc[i]);
+      for (int u = 0; u < 8; ++u) {
+        if (s0 + u < n_splits) {
+          load_row<CPL>(part_o + ((row * n_splits + s0 + u) * H + h) * c, LCA_F32, c, lane, v[u]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) v[u][i] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wgt = __shfl(my_w, s0 + u < n_splits ? s0 + u : 0, 64);
+        if (s0 + u >= n_splits) continue;
+        den += wgt;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) acc[i] = fmaf(wgt, v[u][i], acc[i]);
+      }
     }
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
@@ -515,11 +595,14 @@ Plan make_plan(long long rows, int H, int c, int q_fmt, int kv_fmt, int k, int N
   const int NT = (dense ? N_cap : k) + n_win;
   Plan p;
   p.mfma = use_mfma(H, c, q_fmt, kv_fmt);
-  const int split_rows = p.mfma ? kMfmaSplitRows : kSplitRows;
+  int split_rows = p.mfma ? kMfmaSplitRows : kSplitRows;
   if (rows >= 512) {
     p.n_splits = 1;
     p.split_rows = NT;
   } else {
+    // at most kMaxMergeSplits splits (the merge gives each split one lane)
+    const int min_rows = (NT + kMaxMergeSplits - 1) / kMaxMergeSplits;
+    while (split_rows < min_rows) split_rows *= 2;
     p.split_rows = split_rows;
     p.n_splits = (NT + split_rows - 1) / split_rows;
   }

@@ -19,13 +19,20 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// float32 -> bfloat16, round to nearest even (NaN stays a quiet NaN).
+// float32 -> bfloat16, round to nearest even: gfx950's v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
+
+// Two float32 -> packed bfloat16 pair (a in the low half), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 1/sqrt(x) with the hardware reciprocal square root (v_rsq_f32, ~1 ulp).
+__device__ __forceinline__ float rsqrt_hw(float x) { return __builtin_amdgcn_rsqf(x); }
 
 // OCP e4m3fn byte -> float32 (exact).  Exponent bias 7, exponent 0 is
 // subnormal (f * 2^-9), S.1111.111 is NaN.
@@ -99,9 +106,7 @@ __device__ __forceinline__ void store_row(void* base, int fmt, int c, int lane, 
   } else if (fmt == LCA_BF16) {
     uint16_t* p = static_cast<uint16_t*>(base) + ch0;
 #pragma unroll
-    for (int i = 0; i < CPL; i += 2)
-      *reinterpret_cast<uint32_t*>(p + i) =
-          static_cast<uint32_t>(f32_to_bf16(v[i])) | (static_cast<uint32_t>(f32_to_bf16(v[i + 1])) << 16);
+    for (int i = 0; i < CPL; i += 2) *reinterpret_cast<uint32_t*>(p + i) = pack_bf16(v[i], v[i + 1]);
   } else {  // LCA_KV_FP8_BF16ROPE
     uint8_t* p = static_cast<uint8_t*>(base);
     const int nope = c - 64;
@@ -126,10 +131,27 @@ __host__ __device__ inline size_t row_bytes(int fmt, int c) {
   }
 }
 
+// DPP move of a float (row-level lane permutation, no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 64 lanes, returned in every lane.  Each 16-lane row is reduced
+// with DPP (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror: every lane of a row ends with the same value, since each step
+// adds a commuted pair), then the four row sums are read with readlane and
+// added in a fixed order.  Deterministic; no LDS traffic.
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
-  return x;
+  x += dpp_f<0xb1>(x);
+  x += dpp_f<0x4e>(x);
+  x += dpp_f<0x141>(x);
+  x += dpp_f<0x140>(x);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 __device__ __forceinline__ float wave_max(float x) {

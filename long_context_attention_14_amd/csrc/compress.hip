@@ -53,7 +53,7 @@ __device__ __forceinline__ void pool_finish_norm(const Pool* p, int c, float eps
     ss += out[i] * out[i];
   }
   ss = wave_sum(ss);
-  const float r = 1.0f / sqrtf(ss / static_cast<float>(c) + eps);
+  const float r = rsqrt_hw(ss / static_cast<float>(c) + eps);
 #pragma unroll
   for (int i = 0; i < CPL; ++i) out[i] *= r;
 }
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void rmsnorm_rows_kernel(
 #pragma unroll
   for (int j = 0; j < CPL; ++j) ss += v[j] * v[j];
   ss = wave_sum(ss);
-  const float rs = 1.0f / sqrtf(ss / static_cast<float>(c) + eps);
+  const float rs = rsqrt_hw(ss / static_cast<float>(c) + eps);
 #pragma unroll
   for (int j = 0; j < CPL; ++j) v[j] *= rs;
   store_row<CPL>(y + (static_cast<size_t>(b) * y_seq_rows + i) * row_bytes(y_fmt, c), y_fmt, c, lane,
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
       ss += u[j] * u[j];
     }
     ss = wave_sum(ss);
-    const float rs = 1.0f / sqrtf(ss / static_cast<float>(c) + eps);
+    const float rs = rsqrt_hw(ss / static_cast<float>(c) + eps);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) u[j] *= rs;
     store_row<CPL>(ring + (static_cast<size_t>(b) * n_win + p % n_win) * kv_row, kv_fmt, c, lane, u);

@@ -29,8 +29,14 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kIdxWaves = 4;
 constexpr int kKeysPerGroup = 32;
-constexpr int kGroupsPerWave = 16;
-constexpr int kKeysPerBlock = kIdxWaves * kGroupsPerWave * kKeysPerGroup;  // 2048
+constexpr int kBlockKeys = kIdxWaves * kKeysPerGroup;  // 128 keys per workgroup step
+// Workgroups per query row: the row's 128-key blocks are dealt round-robin to
+// the row's workgroups, so the workgroups of a row sweep its keys together
+// (a few MiB apart at most) instead of each streaming a separate chunk; this
+// keeps HBM row-buffer locality.  Chosen so that a decode batch has about
+// 1536 workgroups (6 per CU).
+constexpr int kTargetBlocks = 1536;
+constexpr int kPrefetch = 2;
 
 __device__ __forceinline__ v8i load32(const uint8_t* p) {
   const uint4 a = *reinterpret_cast<const uint4*>(p);
@@ -90,19 +96,17 @@ template <bool MX, bool HIST>
 __global__ __launch_bounds__(kWave * kIdxWaves) void indexer_mfma_kernel(
     const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qI_scale,
     const uint8_t* __restrict__ kI, const uint8_t* __restrict__ kI_scale, int n_q, int N_cap,
-    int n_chunks, const float* __restrict__ w, const int32_t* __restrict__ q_pos, int m,
+    int wpr, const float* __restrict__ w, const int32_t* __restrict__ q_pos, int m,
     const int32_t* __restrict__ n_entries, float* __restrict__ scores,
     uint32_t* __restrict__ hist) {
   constexpr int kFmt = MX ? 4 : 0;
   constexpr int kRowBytes = MX ? 64 : 128;  // bytes of one 128-dim vector
   __shared__ uint32_t lh[HIST ? kScoreHistBins : 1];
-  const long long row = blockIdx.x / n_chunks;
-  const int chunk = blockIdx.x % n_chunks;
+  const long long row = blockIdx.x / wpr;
+  const int wi = blockIdx.x % wpr;
   const int b = static_cast<int>(row / n_q);
   const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
-  const int key0 = chunk * kKeysPerBlock;
-  if (key0 >= vis) return;
-  const int key_end = min(key0 + kKeysPerBlock, vis);
+  if (wi * kBlockKeys >= vis) return;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
@@ -145,15 +149,20 @@ __global__ __launch_bounds__(kWave * kIdxWaves) void indexer_mfma_kernel(
   float* out = scores + static_cast<size_t>(row) * N_cap;
   if (HIST) __syncthreads();
 
-  constexpr int kStride = kIdxWaves * kKeysPerGroup;
-  int kb = key0 + wave * kKeysPerGroup;
-  KeyGroup<MX> cur;
-  if (kb < key_end) load_group<MX>(kb_base, ks_base, min(kb + j, vis - 1), g, cur);
-  for (; kb < key_end; kb += kStride) {
-    // prefetch the next group of this wave while the current one is reduced
+  // this wave's groups: keys [kb, kb + 32) for kb = wi*128 + 32*wave + t*stride
+  const int stride = kBlockKeys * wpr;
+  int kb = wi * kBlockKeys + wave * kKeysPerGroup;
+  KeyGroup<MX> buf[kPrefetch];
+#pragma unroll
+  for (int p = 0; p < kPrefetch; ++p) {
+    const int kk = kb + p * stride;
+    if (kk < vis) load_group<MX>(kb_base, ks_base, min(kk + j, vis - 1), g, buf[p]);
+  }
+  for (; kb < vis; kb += stride) {
     KeyGroup<MX> nxt;
-    const int kn = kb + kStride;
-    if (kn < key_end) load_group<MX>(kb_base, ks_base, min(kn + j, vis - 1), g, nxt);
+    const int kn = kb + kPrefetch * stride;
+    if (kn < vis) load_group<MX>(kb_base, ks_base, min(kn + j, vis - 1), g, nxt);
+    const KeyGroup<MX>& cur = buf[0];
     v16f acc0 = {0}, acc1 = {0};
     acc0 = mfma<kFmt>(A[0][0], cur.b[0], acc0, sA[0][0], cur.sb[0]);
     acc0 = mfma<kFmt>(A[0][1], cur.b[1], acc0, sA[0][1], cur.sb[1]);
@@ -165,11 +174,13 @@ __global__ __launch_bounds__(kWave * kIdxWaves) void indexer_mfma_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) s += wr[1][r] * fmaxf(acc1[r], 0.f);
     s += __shfl_xor(s, 32, kWave);
-    if (g == 0 && kb + j < key_end) {
+    if (g == 0 && kb + j < vis) {
       out[kb + j] = s;
       if (HIST) atomicAdd(&lh[score_bin(score_key(s))], 1u);
     }
-    cur = nxt;
+#pragma unroll
+    for (int p = 0; p < kPrefetch - 1; ++p) buf[p] = buf[p + 1];
+    buf[kPrefetch - 1] = nxt;
   }
   if (HIST) {
     __syncthreads();
@@ -228,8 +239,11 @@ hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const v
                        n_entries, scores);
     return hipGetLastError();
   }
-  const int n_chunks = (N_cap + kKeysPerBlock - 1) / kKeysPerBlock;
-  const dim3 grid(static_cast<unsigned>(rows * n_chunks));
+  const long long max_blocks = (N_cap + kBlockKeys - 1) / kBlockKeys;
+  long long wpr = (kTargetBlocks + rows - 1) / rows;
+  wpr = wpr < 1 ? 1 : (wpr > max_blocks ? max_blocks : wpr);
+  const dim3 grid(static_cast<unsigned>(rows * wpr));
+  const int n_chunks = static_cast<int>(wpr);
   const dim3 block(kWave * kIdxWaves);
   const uint8_t* q8 = static_cast<const uint8_t*>(qI);
   const uint8_t* k8 = static_cast<const uint8_t*>(kI);
