@@ -299,8 +299,7 @@ int lca_decode_step(const lca_decode_layer* L, const lca_decode_io* io, void* wo
   st = hip_status(lca::launch_state_append(L->mode, L->m, L->B, L->c, L->n_win, io->tokC, io->tokZ,
                                            L->io_dtype, L->tailC, L->tailZ, L->ring, L->kv_dtype,
                                            L->P, L->cache, L->N_cap, L->n_tokens, q_pos, n_ent,
-                                           L->eps, s, hist,
-                                           hist ? static_cast<long long>(L->B) * lca::kScoreHistBins : 0),
+                                           L->eps, s, hist, hist ? lca::topk_hist_words(L->B) : 0),
                   "lca_decode_step/append");
   if (st != LCA_OK) return st;
   if ((st = mark(1)) != LCA_OK) return st;

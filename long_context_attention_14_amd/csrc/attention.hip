@@ -219,7 +219,7 @@ constexpr int kMH = 64;            // heads
 constexpr int kQS = kMC + 8;       // LDS row stride of Q and KV tiles (bf16 elements)
 constexpr int kPS = kMT + 8;       // LDS row stride of P (bf16 elements)
 constexpr int kSS = kMT + 1;       // LDS row stride of S (floats)
-constexpr int kMfmaSplitRows = 64;
+constexpr int kMfmaSplitRows = 128;
 
 __device__ __forceinline__ v8bf_t as_v8bf(uint4 u) { return __builtin_bit_cast(v8bf_t, u); }
 
@@ -264,8 +264,30 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
   const int s_begin = split * split_rows;
   const int s_end = min(s_begin + split_rows, NT);
 
-  // row pointers of the first tile (its index loads overlap the query phase)
+  // row pointers of the first tile; its row loads are issued before the query
+  // phase so that both latencies overlap
   if (tid < kMT) rowp_s[0][tid] = s_begin + tid < s_end ? slot_row(sc, s_begin + tid) : nullptr;
+  __syncthreads();
+  uint4 raw[kMT / 4];
+  auto load_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kMT / 4; ++i) {
+      const uint8_t* rp = rowp_s[buf][wv + 4 * i];
+      raw[i] = make_uint4(0, 0, 0, 0);
+      if (rp) {
+        if (KVFMT == LCA_BF16) {
+          raw[i] = *reinterpret_cast<const uint4*>(rp + lane * 16);
+        } else if (lane < 56) {
+          const uint2 f = *reinterpret_cast<const uint2*>(rp + lane * 8);
+          raw[i].x = f.x;
+          raw[i].y = f.y;
+        } else {
+          raw[i] = *reinterpret_cast<const uint4*>(rp + 448 + (lane - 56) * 16);
+        }
+      }
+    }
+  };
+  load_tile(0);
   // normalised queries -> bf16 in LDS (wave wv: heads wv, wv+4, ...); all of a
   // wave's loads are issued before the first reduction
   const size_t q_row = row_bytes(q_fmt, kMC);
@@ -326,27 +348,6 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
 
   const int sh = wv >> 1, sr = wv & 1;  // this wave's S tile
   __syncthreads();
-  // raw rows of a tile, wave wv holding rows wv, wv+4, ...: issued one tile ahead
-  uint4 raw[kMT / 4];
-  auto load_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kMT / 4; ++i) {
-      const uint8_t* rp = rowp_s[buf][wv + 4 * i];
-      raw[i] = make_uint4(0, 0, 0, 0);
-      if (rp) {
-        if (KVFMT == LCA_BF16) {
-          raw[i] = *reinterpret_cast<const uint4*>(rp + lane * 16);
-        } else if (lane < 56) {
-          const uint2 f = *reinterpret_cast<const uint2*>(rp + lane * 8);
-          raw[i].x = f.x;
-          raw[i].y = f.y;
-        } else {
-          raw[i] = *reinterpret_cast<const uint4*>(rp + 448 + (lane - 56) * 16);
-        }
-      }
-    }
-  };
-  load_tile(0);
   int cur = 0;
   for (int base = s_begin; base < s_end; base += kMT, cur ^= 1) {
     // stage this tile's rows as bf16 and resolve the next tile's row pointers

@@ -184,6 +184,43 @@ __device__ __forceinline__ uint32_t score_key(float x) {
 constexpr int kScoreHistBins = 4096;
 __device__ __forceinline__ uint32_t score_bin(uint32_t key) { return key >> 20; }
 
+// Threshold of a row from its histogram in LDS (kScoreHistBins bins, bin
+// order == key order): the bin holding the want-th largest key and the count
+// of keys in higher bins.  All threads of the block call it; blockDim.x must
+// divide kScoreHistBins and be a multiple of 64; scan_sh holds blockDim.x/64
+// ints.  Thread t owns bins [4095 - per*t - per + 1, 4095 - per*t].
+__device__ inline void find_threshold_block(const uint32_t* lh, int want, int* sh_bin,
+                                            int* sh_above, int* scan_sh) {
+  const int nt = blockDim.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int per = kScoreHistBins / nt;
+  const int top = kScoreHistBins - 1 - per * t;
+  int local = 0;
+  for (int i = 0; i < per; ++i) local += static_cast<int>(lh[top - i]);
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) scan_sh[wv] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int x = 0; x < wv; ++x) before += scan_sh[x];
+  int run = before + incl - local;
+  if (run < want && run + local >= want) {
+    for (int i = 0; i < per; ++i) {
+      const int h = static_cast<int>(lh[top - i]);
+      if (run + h >= want) {
+        *sh_bin = top - i;
+        *sh_above = run;
+        break;
+      }
+      run += h;
+    }
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // internal launchers (defined next to their kernels, called by the C ABI)
 
@@ -211,8 +248,10 @@ size_t topk_workspace_bytes(int B, int n_q, int N_cap, int k);
 hipError_t launch_topk(int B, int n_q, int N_cap, const float* scores, const int32_t* q_pos, int m,
                        const int32_t* n_entries, int k, int32_t* idx, void* ws, hipStream_t s);
 // For rows longer than the LDS path takes: the row histogram inside the top-k
-// workspace (nullptr when the LDS path applies), and the selection from a
-// histogram that the indexer already accumulated there.
+// workspace (nullptr when the LDS path applies; its zero region is
+// topk_hist_words(rows) words), and the selection from a histogram that the
+// indexer already accumulated there.
+long long topk_hist_words(long long rows);
 uint32_t* topk_hist_in_workspace(void* ws, int B, int n_q, int N_cap, int k);
 hipError_t launch_topk_from_hist(int B, int n_q, int N_cap, const float* scores,
                                  const int32_t* q_pos, int m, const int32_t* n_entries, int k,

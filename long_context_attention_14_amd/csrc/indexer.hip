@@ -93,7 +93,7 @@ __device__ __forceinline__ void load_group(const uint8_t* kb_base, const uint8_t
 // HIST: also accumulate the score_bin histogram of the written scores into
 // hist[row] (global, zeroed by the caller) through a per-workgroup LDS histogram.
 template <bool MX, bool HIST>
-__global__ __launch_bounds__(kWave * kIdxWaves) void indexer_mfma_kernel(
+__global__ __launch_bounds__(kWave * kIdxWaves, 3) void indexer_mfma_kernel(
     const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qI_scale,
     const uint8_t* __restrict__ kI, const uint8_t* __restrict__ kI_scale, int n_q, int N_cap,
     int wpr, const float* __restrict__ w, const int32_t* __restrict__ q_pos, int m,
@@ -135,19 +135,15 @@ __global__ __launch_bounds__(kWave * kIdxWaves) void indexer_mfma_kernel(
       }
     }
   }
-  // head weights of the accumulator rows this lane holds:
-  // register r of tile ht is head 32*ht + 8*(r/4) + 4*g + (r%4)
-  float wr[2][16];
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      wr[ht][r] = w[static_cast<size_t>(row) * 64 + 32 * ht + 8 * (r >> 2) + 4 * g + (r & 3)];
+  // head weights in LDS: register r of accumulator tile ht is head
+  // 32*ht + 8*(r/4) + 4*g + (r%4), so four consecutive registers read one float4
+  __shared__ __attribute__((aligned(16))) float w_s[64];
+  if (threadIdx.x < 64) w_s[threadIdx.x] = w[static_cast<size_t>(row) * 64 + threadIdx.x];
 
   const uint8_t* kb_base = kI + static_cast<size_t>(b) * N_cap * kRowBytes;
   const uint8_t* ks_base = MX ? kI_scale + static_cast<size_t>(b) * N_cap * 4 : nullptr;
   float* out = scores + static_cast<size_t>(row) * N_cap;
-  if (HIST) __syncthreads();
+  __syncthreads();
 
   // this wave's groups: keys [kb, kb + 32) for kb = wi*128 + 32*wave + t*stride
   const int stride = kBlockKeys * wpr;
@@ -170,9 +166,21 @@ __global__ __launch_bounds__(kWave * kIdxWaves) void indexer_mfma_kernel(
     acc1 = mfma<kFmt>(A[1][1], cur.b[1], acc1, sA[1][1], cur.sb[1]);
     float s = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s += wr[0][r] * fmaxf(acc0[r], 0.f);
+    for (int a = 0; a < 4; ++a) {
+      const float4 w4 = *reinterpret_cast<const float4*>(&w_s[8 * a + 4 * g]);
+      s += w4.x * fmaxf(acc0[4 * a], 0.f);
+      s += w4.y * fmaxf(acc0[4 * a + 1], 0.f);
+      s += w4.z * fmaxf(acc0[4 * a + 2], 0.f);
+      s += w4.w * fmaxf(acc0[4 * a + 3], 0.f);
+    }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s += wr[1][r] * fmaxf(acc1[r], 0.f);
+    for (int a = 0; a < 4; ++a) {
+      const float4 w4 = *reinterpret_cast<const float4*>(&w_s[32 + 8 * a + 4 * g]);
+      s += w4.x * fmaxf(acc1[4 * a], 0.f);
+      s += w4.y * fmaxf(acc1[4 * a + 1], 0.f);
+      s += w4.z * fmaxf(acc1[4 * a + 2], 0.f);
+      s += w4.w * fmaxf(acc1[4 * a + 3], 0.f);
+    }
     s += __shfl_xor(s, 32, kWave);
     if (g == 0 && kb + j < vis) {
       out[kb + j] = s;

@@ -215,74 +215,40 @@ __global__ __launch_bounds__(kSegThreads) void topk_hist_kernel(
     if (h[i]) atomicAdd(&gh[i], h[i]);
 }
 
-// (bin, count above bin) of the k-th largest key of a row; bin = -1 when every
-// visible entry is selected.  The row histogram is first copied to LDS with
-// coalesced loads (lh: kHistBins words of shared memory); call from all threads.
+// Threshold of a row: (bin of the k-th largest key, count of keys in higher
+// bins), or (-1, vis) when every visible entry is kept.  The row histogram is
+// copied to LDS (lh) with coalesced loads and searched by the whole block.
+// All threads call it; the result is valid after it returns.
 __device__ void row_threshold(const uint32_t* gh, uint32_t* lh, int vis, int k, int* sh_bin,
-                              int* sh_above) {
+                              int* sh_above, int* scan_sh) {
   if (vis <= k) {
     if (threadIdx.x == 0) {
       *sh_bin = -1;
       *sh_above = vis;
     }
+    __syncthreads();
     return;
   }
   const uint4* g4 = reinterpret_cast<const uint4*>(gh);
-  uint4* l4 = reinterpret_cast<uint4*>(lh);
-  for (int i = threadIdx.x; i < kHistBins / 4; i += blockDim.x) l4[i] = g4[i];
+  for (int i = threadIdx.x; i < kHistBins / 4; i += blockDim.x) reinterpret_cast<uint4*>(lh)[i] = g4[i];
   __syncthreads();
-  if (threadIdx.x < 64) find_bin_wave(lh, kHistBins, k, sh_bin, sh_above);
+  find_threshold_block(lh, k, sh_bin, sh_above, scan_sh);
 }
 
-// Exclusive prefix sums of two counters over the workgroup (thread order);
-// also returns the totals.  All threads must call it.
-template <int NT>
-__device__ __forceinline__ void block_scan2(int a, int b, int* ex_a, int* ex_b, int* tot_a,
-                                            int* tot_b, int* sh /* 2 * NT/64 ints */) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int ia = a, ib = b;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int ta = __shfl_up(ia, o, 64), tb = __shfl_up(ib, o, 64);
-    if (lane >= o) {
-      ia += ta;
-      ib += tb;
-    }
-  }
-  if (lane == 63) {
-    sh[wv] = ia;
-    sh[NT / 64 + wv] = ib;
-  }
-  __syncthreads();
-  int oa = 0, ob = 0, ta = 0, tb = 0;
-#pragma unroll
-  for (int x = 0; x < NT / 64; ++x) {
-    const int va = sh[x], vb = sh[NT / 64 + x];
-    if (x < wv) {
-      oa += va;
-      ob += vb;
-    }
-    ta += va;
-    tb += vb;
-  }
-  *ex_a = oa + ia - a;
-  *ex_b = ob + ib - b;
-  *tot_a = ta;
-  *tot_b = tb;
-}
-
-// One workgroup per (row, segment of kSeg scores): thread t owns the contiguous
-// chunk [s0 + kChunk*t, +kChunk) and loads it all before compacting, so the
-// memory latency is paid once; one block scan gives every thread its output
-// offsets in index order.
-constexpr int kChunk = kSeg / kSegThreads;  // 32
+// One workgroup per (row, segment of kSeg scores); wave wv owns the quarter
+// [s0 + wv*kSeg/4, +kSeg/4) and loads it with coalesced loads (element
+// base + 64 r + lane in register r).  Pass 1 counts the surely selected and the
+// candidate entries of each wave with ballots; a scan of the four wave totals
+// gives every wave its output offsets; pass 2 writes the indices in order.
+constexpr int kQuarter = kSeg / (kSegThreads / 64);  // 2048
+constexpr int kPerLane = kQuarter / 64;                // 32
 
 __global__ __launch_bounds__(kSegThreads) void topk_collect_kernel(
     const float* __restrict__ scores, int N_cap, int n_q, const int32_t* __restrict__ q_pos, int m,
     const int32_t* __restrict__ n_entries, int k, int n_seg, WideWs ws) {
-  __shared__ int sh_bin, sh_above;
-  __shared__ int scan_sh[2 * kSegThreads / 64];
+  __shared__ int wtot_s[kSegThreads / 64], wtot_c[kSegThreads / 64];
   __shared__ uint32_t lh[kHistBins];
+  __shared__ int sh_bin, sh_above, scan_sh[kSegThreads / 64];
   const long long row = blockIdx.x / n_seg;
   const int seg = blockIdx.x % n_seg;
   const int b = static_cast<int>(row / n_q);
@@ -290,43 +256,59 @@ __global__ __launch_bounds__(kSegThreads) void topk_collect_kernel(
   const int s0 = seg * kSeg;
   const int s1 = min(s0 + kSeg, vis);
   const long long rs = row * n_seg + seg;
-  const int tid = threadIdx.x;
-  // issue the chunk's loads first
-  const int c0 = s0 + kChunk * tid;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wbase = s0 + wv * kQuarter;
   const float* src = scores + row * N_cap;
-  float v[kChunk];
+  float v[kPerLane];
 #pragma unroll
-  for (int i = 0; i < kChunk; ++i) v[i] = c0 + i < s1 ? src[c0 + i] : 0.f;
-  row_threshold(ws.hist + row * kHistBins, lh, vis, k, &sh_bin, &sh_above);
-  __syncthreads();
+  for (int r = 0; r < kPerLane; ++r) {
+    const int i = wbase + 64 * r + lane;
+    v[r] = i < s1 ? src[i] : 0.f;
+  }
+  row_threshold(ws.hist + row * kHistBins, lh, vis, k, &sh_bin, &sh_above, scan_sh);
   const int bstar = sh_bin;
-  uint32_t key[kChunk];
   int ns = 0, nc = 0;
 #pragma unroll
-  for (int i = 0; i < kChunk; ++i) {
-    key[i] = score_key(v[i]);
-    const int bin = static_cast<int>(score_bin(key[i]));
-    const bool in = c0 + i < s1;
-    ns += (in && bin > bstar);
-    nc += (in && bin == bstar);
+  for (int r = 0; r < kPerLane; ++r) {
+    const int i = wbase + 64 * r + lane;
+    const int bin = static_cast<int>(score_bin(score_key(v[r])));
+    ns += __popcll(__ballot(i < s1 && bin > bstar));
+    nc += __popcll(__ballot(i < s1 && bin == bstar));
   }
-  int os, oc, ts, tc;
-  block_scan2<kSegThreads>(ns, nc, &os, &oc, &ts, &tc, scan_sh);
+  if (lane == 0) {
+    wtot_s[wv] = ns;
+    wtot_c[wv] = nc;
+  }
+  __syncthreads();
+  int os = 0, oc = 0, ts = 0, tc = 0;
+#pragma unroll
+  for (int x = 0; x < kSegThreads / 64; ++x) {
+    if (x < wv) {
+      os += wtot_s[x];
+      oc += wtot_c[x];
+    }
+    ts += wtot_s[x];
+    tc += wtot_c[x];
+  }
   int32_t* sure = ws.sure + rs * k;
   uint32_t* ckey = ws.cand_key + rs * kSeg;
   int32_t* cidx = ws.cand_idx + rs * kSeg;
 #pragma unroll
-  for (int i = 0; i < kChunk; ++i) {
-    const int bin = static_cast<int>(score_bin(key[i]));
-    const bool in = c0 + i < s1;
-    if (in && bin > bstar) {
-      if (os < k) sure[os] = c0 + i;
-      ++os;
-    } else if (in && bin == bstar) {
-      ckey[oc] = key[i];
-      cidx[oc] = c0 + i;
-      ++oc;
+  for (int r = 0; r < kPerLane; ++r) {
+    const int i = wbase + 64 * r + lane;
+    const uint32_t key = score_key(v[r]);
+    const int bin = static_cast<int>(score_bin(key));
+    const bool is_s = i < s1 && bin > bstar;
+    const bool is_c = i < s1 && bin == bstar;
+    const uint64_t bs = __ballot(is_s), bc = __ballot(is_c);
+    const int ps = os + lanes_below(bs), pc = oc + lanes_below(bc);
+    if (is_s && ps < k) sure[ps] = i;
+    if (is_c) {
+      ckey[pc] = key;
+      cidx[pc] = i;
     }
+    os += __popcll(bs);
+    oc += __popcll(bc);
   }
   if (tid == 0) {
     ws.sure_cnt[rs] = s0 < vis ? ts : 0;
@@ -371,6 +353,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
   __shared__ int sh_bin, sh_above, sh_b2, sh_a2;
   __shared__ uint32_t wgt[kRowThreads / 64], weq[kRowThreads / 64];
   __shared__ uint32_t lh[kHistBins];
+  __shared__ int scan_sh[kRowThreads / 64];
   __shared__ uint32_t ck_s[kCandLds];
   __shared__ int32_t ci_s[kCandLds];
   const long long row = blockIdx.x;
@@ -378,7 +361,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
   const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int32_t* out = idx + row * k;
-  row_threshold(ws.hist + row * kHistBins, lh, vis, k, &sh_bin, &sh_above);
+  row_threshold(ws.hist + row * kHistBins, lh, vis, k, &sh_bin, &sh_above, scan_sh);
   for (int s = tid; s < n_seg; s += kRowThreads) {
     seg_s[s] = ws.sure_cnt[row * n_seg + s];
     seg_c[s] = ws.cand_cnt[row * n_seg + s];
@@ -513,9 +496,22 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
 
 static int n_segments(int N_cap) { return (N_cap + kSeg - 1) / kSeg; }
 
+long long topk_hist_words(long long rows) { return rows * kHistBins; }
+
 uint32_t* topk_hist_in_workspace(void* ws, int B, int n_q, int N_cap, int k) {
   if (N_cap <= kLdsMaxRow || ws == nullptr) return nullptr;
   return wide_ws(ws, static_cast<long long>(B) * n_q, n_segments(N_cap), k).hist;
+}
+
+static hipError_t launch_collect_finish(long long rows, int N_cap, const float* scores, int n_q,
+                                        const int32_t* q_pos, int m, const int32_t* n_entries, int k,
+                                        int32_t* idx, const WideWs& w, int n_seg, hipStream_t s) {
+  const dim3 g2(static_cast<unsigned>(rows * n_seg));
+  hipLaunchKernelGGL(topk_collect_kernel, g2, dim3(kSegThreads), 0, s, scores, N_cap, n_q, q_pos, m,
+                     n_entries, k, n_seg, w);
+  hipLaunchKernelGGL(topk_finish_kernel, dim3(static_cast<unsigned>(rows)), dim3(kRowThreads), 0, s,
+                     N_cap, n_q, q_pos, m, n_entries, k, n_seg, w, idx);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk_from_hist(int B, int n_q, int N_cap, const float* scores,
@@ -526,13 +522,8 @@ hipError_t launch_topk_from_hist(int B, int n_q, int N_cap, const float* scores,
   if (N_cap <= kLdsMaxRow) return launch_topk(B, n_q, N_cap, scores, q_pos, m, n_entries, k, idx, ws, s);
   const int n_seg = n_segments(N_cap);
   if (n_seg > kMaxSeg || k > kMaxK) return hipErrorInvalidValue;
-  WideWs w = wide_ws(ws, rows, n_seg, k);
-  const dim3 g2(static_cast<unsigned>(rows * n_seg));
-  hipLaunchKernelGGL(topk_collect_kernel, g2, dim3(kSegThreads), 0, s, scores, N_cap, n_q, q_pos, m,
-                     n_entries, k, n_seg, w);
-  hipLaunchKernelGGL(topk_finish_kernel, dim3(static_cast<unsigned>(rows)), dim3(kRowThreads), 0, s,
-                     N_cap, n_q, q_pos, m, n_entries, k, n_seg, w, idx);
-  return hipGetLastError();
+  return launch_collect_finish(rows, N_cap, scores, n_q, q_pos, m, n_entries, k, idx,
+                               wide_ws(ws, rows, n_seg, k), n_seg, s);
 }
 
 size_t topk_workspace_bytes(int B, int n_q, int N_cap, int k) {
@@ -553,17 +544,13 @@ hipError_t launch_topk(int B, int n_q, int N_cap, const float* scores, const int
   const int n_seg = n_segments(N_cap);
   if (n_seg > kMaxSeg || k > kMaxK) return hipErrorInvalidValue;
   WideWs w = wide_ws(ws, rows, n_seg, k);
-  const long long nh = rows * kHistBins;
+  const long long nh = topk_hist_words(rows);
   hipLaunchKernelGGL(zero_u32_kernel, dim3(static_cast<unsigned>((nh + 255) / 256)), dim3(256), 0, s,
                      w.hist, nh);
   const dim3 g2(static_cast<unsigned>(rows * n_seg));
   hipLaunchKernelGGL(topk_hist_kernel, g2, dim3(kSegThreads), 0, s, scores, N_cap, n_q, q_pos, m,
                      n_entries, k, n_seg, w.hist);
-  hipLaunchKernelGGL(topk_collect_kernel, g2, dim3(kSegThreads), 0, s, scores, N_cap, n_q, q_pos, m,
-                     n_entries, k, n_seg, w);
-  hipLaunchKernelGGL(topk_finish_kernel, dim3(static_cast<unsigned>(rows)), dim3(kRowThreads), 0, s,
-                     N_cap, n_q, q_pos, m, n_entries, k, n_seg, w, idx);
-  return hipGetLastError();
+  return launch_collect_finish(rows, N_cap, scores, n_q, q_pos, m, n_entries, k, idx, w, n_seg, s);
 }
 
 }  // namespace lca
