@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--detail", default=None, help="write per-stage timings (JSON) to this file")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="before warmup, run one plain device-to-device copy of MIB MiB (a "
+                         "kernel of known traffic for scaling rocprofv3 byte counters)")
     return ap.parse_args()
 
 
@@ -110,6 +113,13 @@ def main():
                             qI=layer.qI, w=layer.w, lse=layer.lse, idx_out=layer.idx,
                             workspace=layer.workspace, stage_events=ev)
 
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

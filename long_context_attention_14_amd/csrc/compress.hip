@@ -49,7 +49,7 @@ __device__ __forceinline__ void pool_finish_norm(const Pool* p, int c, float eps
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
-    out[i] = p[i].acc / p[i].sum;
+    out[i] = p[i].acc * __builtin_amdgcn_rcpf(p[i].sum);
     ss += out[i] * out[i];
   }
   ss = wave_sum(ss);
@@ -153,27 +153,37 @@ __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
     uint8_t* tailC, uint8_t* tailZ, uint8_t* ring, int kv_fmt, const float* P, uint8_t* cache,
     int N_cap, int32_t* n_tokens, int32_t* q_pos, int32_t* n_entries, float eps,
     uint32_t* zero_buf, long long zero_words) {
-  __shared__ float part[kAppendWaves][3][CPL * kWave];
+  __shared__ float part[kAppendWaves][3][CPL][kWave];  // lane-contiguous: no bank conflicts
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x >> 6;
   const int b = blockIdx.x;
   for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; i < zero_words;
        i += static_cast<long long>(gridDim.x) * blockDim.x)
     zero_buf[i] = 0u;
-  const int p = n_tokens[b];
-  if (p < 0) return;
   const size_t io_row = row_bytes(io_fmt, c);
   const size_t kv_row = row_bytes(kv_fmt, c);
   const int T_cap = csa ? 2 * m : m;
-  const int blk = p / m;
-  const int half = csa ? (blk & 1) : 0;
-  const int row = half * m + p % m;
-
+  uint8_t* tCb = tailC + static_cast<size_t>(b) * T_cap * io_row;
+  uint8_t* tZb = tailZ + static_cast<size_t>(b) * T_cap * io_row;
+  // A CSA tail of at most kAppendWaves rows is read speculatively (one row per
+  // wave, with the bias rows of both slots that row can take) before the token
+  // count arrives, so that the step pays one memory latency.
+  const bool spec = CPL <= 8 && csa && T_cap <= kAppendWaves;
+  float sc[CPL], sz[CPL], sp0[CPL], sp1[CPL];
+  if (spec && wv < T_cap) {
+    load_row<CPL>(tCb + wv * io_row, io_fmt, c, lane, sc);
+    load_row<CPL>(tZb + wv * io_row, io_fmt, c, lane, sz);
+    load_bias<CPL>(P, wv % m, c, lane, sp0);
+    load_bias<CPL>(P, m + wv % m, c, lane, sp1);
+  }
   float tc[CPL], tz[CPL];
   load_row<CPL>(tokC + static_cast<size_t>(b) * io_row, io_fmt, c, lane, tc);
   load_row<CPL>(tokZ + static_cast<size_t>(b) * io_row, io_fmt, c, lane, tz);
-  uint8_t* tCb = tailC + static_cast<size_t>(b) * T_cap * io_row;
-  uint8_t* tZb = tailZ + static_cast<size_t>(b) * T_cap * io_row;
+  const int p = n_tokens[b];
+  if (p < 0) return;
+  const int blk = p / m;
+  const int half = csa ? (blk & 1) : 0;
+  const int row = half * m + p % m;
   if (wv == 0) {
     store_row<CPL>(tCb + row * io_row, io_fmt, c, lane, tc);
     store_row<CPL>(tZb + row * io_row, io_fmt, c, lane, tz);
@@ -199,38 +209,53 @@ __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
   }
   if ((p + 1) % m != 0) return;
 
-  // candidate slots: CSA 0..m-1 previous block (absent for the first entry),
-  // m..2m-1 own block; HCA 0..m-1 own block.  The own block's last slot is the
-  // new token.
+  // candidates, by physical tail row r: CSA rows of the current half are slots
+  // m..2m-1 (own block), the other half slots 0..m-1 (previous block, absent
+  // for the first entry); HCA row r is slot r.  The new token's row is taken
+  // from registers.
   const int s = (p + 1) / m - 1;
-  const int W = csa ? 2 * m : m;
-  const int first_slot = (csa && s == 0) ? m : 0;
-  const int ph = (blk - 1) & 1;
   Pool pool[CPL];
   pool_init<CPL>(pool);
   float cv[CPL], zv[CPL], pv[CPL];
-  for (int slot = first_slot + wv; slot < W; slot += kAppendWaves) {
-    if (slot == W - 1) {
+  auto add_row = [&](int r, const float* rc, const float* rz, const float* bias) {
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        cv[j] = tc[j];
-        zv[j] = tz[j];
+    for (int j = 0; j < CPL; ++j) zv[j] = rz[j] + bias[j];
+    pool_add<CPL>(pool, rc, zv);
+  };
+  if (spec) {
+    if (wv < T_cap) {
+      const bool own = (wv / m) == half;
+      if (own || s > 0) {
+        const float* rc = wv == row ? tc : sc;
+        const float* rz = wv == row ? tz : sz;
+        add_row(wv, rc, rz, own ? sp1 : sp0);
       }
-    } else {
-      const int r = (csa && slot < m) ? ph * m + slot : half * m + (slot - (csa ? m : 0));
-      load_row<CPL>(tCb + r * io_row, io_fmt, c, lane, cv);
-      load_row<CPL>(tZb + r * io_row, io_fmt, c, lane, zv);
     }
-    load_bias<CPL>(P, slot, c, lane, pv);
+  } else {
+    for (int r = wv; r < T_cap; r += kAppendWaves) {
+      const bool own = !csa || (r / m) == half;
+      if (!own && s == 0) continue;
+      const int slot = csa ? (own ? m + r % m : r % m) : r;
+      if (r == row) {
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) zv[j] += pv[j];
-    pool_add<CPL>(pool, cv, zv);
+        for (int j = 0; j < CPL; ++j) {
+          cv[j] = tc[j];
+          pv[j] = tz[j];
+        }
+      } else {
+        load_row<CPL>(tCb + r * io_row, io_fmt, c, lane, cv);
+        load_row<CPL>(tZb + r * io_row, io_fmt, c, lane, pv);
+      }
+      float bias[CPL];
+      load_bias<CPL>(P, slot, c, lane, bias);
+      add_row(r, cv, pv, bias);
+    }
   }
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
-    part[wv][0][lane * CPL + j] = pool[j].mx;
-    part[wv][1][lane * CPL + j] = pool[j].sum;
-    part[wv][2][lane * CPL + j] = pool[j].acc;
+    part[wv][0][j][lane] = pool[j].mx;
+    part[wv][1][j][lane] = pool[j].sum;
+    part[wv][2][j][lane] = pool[j].acc;
   }
   __syncthreads();
   if (wv != 0) return;
@@ -238,14 +263,15 @@ __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     float M = -INFINITY;
-    for (int x = 0; x < kAppendWaves; ++x) M = fmaxf(M, part[x][0][lane * CPL + j]);
+#pragma unroll
+    for (int x = 0; x < kAppendWaves; ++x) M = fmaxf(M, part[x][0][j][lane]);
     float sum = 0.f, acc = 0.f;
+#pragma unroll
     for (int x = 0; x < kAppendWaves; ++x) {
-      const float mx = part[x][0][lane * CPL + j];
-      if (mx == -INFINITY) continue;
-      const float f = __expf(mx - M);
-      sum += part[x][1][lane * CPL + j] * f;
-      acc += part[x][2][lane * CPL + j] * f;
+      const float mx = part[x][0][j][lane];
+      const float f = mx == -INFINITY ? 0.f : __expf(mx - M);
+      sum += part[x][1][j][lane] * f;
+      acc += part[x][2][j][lane] * f;
     }
     tot[j] = {M, sum, acc};
   }
