@@ -9,9 +9,16 @@ block, compression of a block the token completes), indexer scores, top-k,
 sparse attention with the window branch and the log-sum-exp merge.  Steps run
 back to back, so the state advances (blocks complete every 4 steps).
 
-Prints ONE JSON line.  The timed loop calls lca_decode_step; per-stage times
-come from HIP events that the library records on the stream its kernels run on
-(lca_decode_io.stage_events), over the timed region itself.
+Other workloads (--workload): HCA decode at 128K (batch 32), the 8-layer hybrid
+decode stack at 1M (batch 4, MXFP4 indexer, fp8+bf16 KV) and the CSA prefill
+chunk (8192 tokens on a 131072 prefix); the default line is the 1M CSA decode.
+
+Prints ONE JSON line.  The timed loop calls lca_decode_step; on every 4th step
+the library records two HIP events (lca_decode_io.stage_events) around the
+dominant kernel on the stream its kernels run on, which gives that kernel's
+duration for the roofline.  The per-stage breakdown ("stages_us") comes from an
+untimed diagnostic loop that records all five events (each event record adds
+a few microseconds of GPU time, so those stage times include them).
 """
 import argparse
 import json
@@ -23,6 +30,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+WORKLOADS = ("csa_decode_1m", "hca_decode", "hybrid_decode_1m", "csa_prefill_chunk")
 
 
 class HipEvents:
@@ -51,6 +60,9 @@ class HipEvents:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", default="csa_decode_1m", choices=WORKLOADS,
+                    help="the default is the headline workload; the others are reported in the "
+                         "design notes")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -63,26 +75,283 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(cfg, d, budget_s):
-    """The float64 oracle (as is) on a bounded sample: whole decode steps of the
-    first sequences of the same batch, until about budget_s of CPU time."""
-    import numpy as np
-    from oracle.workloads import oracle_decode
+def _cores():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] + [1]))
     except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline_decode(cfgs, ds, budget_s):
+    """The float64 oracle (as is) on a bounded sample: whole decode steps (every
+    layer) of the first sequences of the same batch, until about budget_s."""
+    from oracle.workloads import oracle_decode
+    B = cfgs[0].B
     done, t0 = 0, time.perf_counter()
-    while done < cfg.B:
-        oracle_decode(cfg, d, done)
+    while done < B:
+        for c, d in zip(cfgs, ds):
+            oracle_decode(c, d, done)
         done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "query-tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} of {cfg.B} sequences, one full decode step each "
-                      f"({el:.1f} s, float64 numpy)"}
+    return {"value": done / el, "unit": "query-tokens/s", "cores": _cores(), "kind": "oracle",
+            "sample": f"{done} of {B} sequences, one full decode step each through "
+                      f"{len(cfgs)} layer(s) ({el:.1f} s, float64 numpy)"}
+
+
+def cpu_baseline_prefill(cfg, d, budget_s):
+    """The float64 oracle on a bounded sample of query rows of the same chunk (the
+    chunk's compression is computed once per call and included in the time)."""
+    import numpy as np
+    from oracle.workloads import oracle_prefill
+    rows, t0, q0 = 0, time.perf_counter(), 0
+    while rows < cfg.n_new:
+        qs = np.arange(q0, min(q0 + 16, cfg.n_new))
+        oracle_prefill(cfg, d, 0, qs)
+        rows += len(qs)
+        q0 = (q0 + 997) % max(1, cfg.n_new - 16)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": rows / el, "unit": "query-tokens/s", "cores": _cores(), "kind": "oracle",
+            "sample": f"{rows} of {cfg.n_new} query rows in blocks of 16, each block with the "
+                      f"chunk's compression ({el:.1f} s, float64 numpy)"}
+
+
+def _calibrate_copy(mib, dev):
+    import torch
+    if mib:
+        src = torch.ones(mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+
+def _indexer_traffic():
+    """HBM bytes per fp8 indexer launch from the committed counter summary, if it
+    was taken with the current kernel source."""
+    import hashlib
+    tfile = os.path.join(ROOT, "profiles", "indexer_fp8_decode_b16_1m_counters.txt")
+    if not os.path.exists(tfile):
+        return None
+    kv = dict(l.split(":", 1) for l in open(tfile) if ":" in l and not l.startswith("#"))
+    src = os.path.join(ROOT, "long_context_attention_14_amd", "csrc", "indexer.hip")
+    cur = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if kv.get("indexer_source_sha256_16", "").strip() == cur and "hbm_bytes_per_launch" in kv:
+        return float(kv["hbm_bytes_per_launch"])
+    return None
+
+
+DECODE_STAGES = ["append", "indexer", "topk", "attention"]
+
+
+def run_decode(args, workload):
+    import numpy as np
+    import torch
+
+    from long_context_attention_14_amd import ops, pipeline
+    from synth import gen
+    from synth.configs import CSA_DECODE_1M, HCA_DECODE, HYBRID_DECODE_1M
+
+    dev = "cuda"
+    total_steps = args.warmup + args.steps
+    if workload == "hybrid_decode_1m":
+        base = HYBRID_DECODE_1M
+        ds = gen.hybrid_inputs(base, extra_entries=total_steps // base.m + 2)
+        cfgs = [base if d["kind"] == "C" else base.with_(m=d["m"]) for d in ds]
+    else:
+        base = CSA_DECODE_1M if workload == "csa_decode_1m" else HCA_DECODE
+        ds = [gen.decode_inputs(base, extra_entries=total_steps // base.m + 2)]
+        cfgs = [base]
+    layers = [pipeline.DecodeLayer(c, d, dev) for c, d in zip(cfgs, ds)]
+    B = base.B
+    hip = HipEvents()
+
+    def step(evs=None):
+        for i, (c, L) in enumerate(zip(cfgs, layers)):
+            csa = L.mode == "csa"
+            ops.lca_decode_step(L.state, L.tokC, L.tokZ, L.q, L.out, c.io_dtype,
+                                qI=L.qI if csa else None, qI_scale=L.qI_scale if csa else None,
+                                w=L.w if csa else None, lse=L.lse, idx_out=L.idx if csa else None,
+                                workspace=L.workspace, stage_events=evs[i] if evs else None)
+
+    _calibrate_copy(args.calibrate_copy, dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # Timed region: every SAMPLE-th step records two events around the dominant
+    # kernel (an event record costs GPU time, so the other steps record none).
+    csa_layers = [i for i, L in enumerate(layers) if L.mode == "csa"]
+    dom_layers = csa_layers if csa_layers else [0]
+    dom = (1, 2) if csa_layers else (3, 4)          # indexer or attention stage
+    SAMPLE = 4
+    sampled = {}
+    for i in range(0, args.steps, SAMPLE):
+        sampled[i] = {li: (hip.create(), hip.create()) for li in dom_layers}
+
+    def evs_for(i):
+        if i not in sampled:
+            return None
+        out = []
+        for li in range(len(layers)):
+            e = [None] * 5
+            if li in sampled[i]:
+                e[dom[0]], e[dom[1]] = sampled[i][li]
+            out.append(e)
+        return out
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs_for(i))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    dom_time = float(np.mean([hip.elapsed_s(*sampled[i][li]) for i in sampled for li in dom_layers]))
+    for i in sampled:
+        for a, b in sampled[i].values():
+            hip.destroy(a)
+            hip.destroy(b)
+    # per-(layer, stage) breakdown from an untimed diagnostic loop with all events
+    n_diag = min(args.steps, 10)
+    events = [[[hip.create() for _ in range(5)] for _ in layers] for _ in range(n_diag)]
+    for i in range(n_diag):
+        step(events[i])
+    torch.cuda.synchronize()
+    per = np.zeros((len(layers), 4))
+    for ev in events:
+        for li, le in enumerate(ev):
+            for j in range(4):
+                per[li, j] += hip.elapsed_s(le[j], le[j + 1])
+    per /= n_diag
+    for ev in events:
+        for le in ev:
+            for e in le:
+                hip.destroy(e)
+    ms_per_step = elapsed / args.steps * 1e3
+    value = B * args.steps / elapsed
+    steps_done = np.arange(args.steps) + args.warmup
+
+    def vis_mean(d):
+        return float(np.mean([((d["lengths"] + s) // d["m"]).sum() for s in steps_done]))
+
+    step_bytes = 0.0
+    for c, d, L in zip(cfgs, ds, layers):
+        rb = ops.row_bytes(c.kv_dtype, c.c)
+        nsel = B * c.k if L.mode == "csa" else vis_mean(d)
+        step_bytes += (nsel + B * c.n_win) * rb + 2 * B * c.H * c.c * 2
+        if L.mode == "csa":
+            step_bytes += vis_mean(d) * ops.row_bytes(c.idx_dtype, c.d_I) * (1 + (4 / 64 if c.idx_dtype == "mxfp4" else 0))
+    if csa_layers:
+        # dominant kernel: the indexer; algorithmic bytes per launch = every visible
+        # key (+ its E8M0 scales for MXFP4) + queries and head weights
+        c0 = cfgs[csa_layers[0]]
+        key_b = ops.row_bytes(c0.idx_dtype, c0.d_I) + (4 if c0.idx_dtype == "mxfp4" else 0)
+        idx_bytes = np.mean([vis_mean(ds[i]) * key_b + B * c0.H_I * (key_b + 4) for i in csa_layers])
+        achieved = idx_bytes / dom_time / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS,
+                "traffic": _indexer_traffic() if workload == "csa_decode_1m" else None,
+                "kernel": f"indexer_mfma_kernel<{c0.idx_dtype}>"}
+    else:
+        # HCA only: dominant kernel is the attention over all visible entries + window
+        c0, d0 = cfgs[0], ds[0]
+        rb = ops.row_bytes(c0.kv_dtype, c0.c)
+        att_bytes = (vis_mean(d0) + B * c0.n_win) * rb + 2 * B * c0.H * c0.c * 2
+        achieved = att_bytes / dom_time / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "attn_mfma_kernel"}
+    desc = {
+        "csa_decode_1m": "csa_decode_b16_1m: batch 16, context 2^20 + U{0..3}, m=4 (262144 entries), "
+                         "fp8 indexer 64x128, top-1024, MQA 64x512 bf16, window 128",
+        "hca_decode": "hca_decode_b32_128k: batch 32, context 131072 + U{0..127}, m'=128 (1024 "
+                      "entries), dense MQA 64x512 bf16, window 128",
+        "hybrid_decode_1m": "hybrid8_decode_b4_1m: batch 4, context 2^20 + U{0..127}, layers "
+                            "H,H,C,H,C,H,C,H, MXFP4 indexer 64x128, top-1024, KV fp8 + bf16 rope "
+                            "dims, MQA 64x512, window 128",
+    }[workload]
+    result = {
+        "metric": "CSA/HCA decode query-tokens/s at 1M ctx + achieved HBM GB/s vs peak",
+        "value": value, "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": {"csa_decode_1m": "fp8 indexer / bf16 KV / fp32 accumulate",
+                  "hca_decode": "bf16 KV / fp32 accumulate",
+                  "hybrid_decode_1m": "mxfp4 indexer / fp8+bf16 KV / fp32 accumulate"}[workload],
+        "data": "synthetic (seeded; N(0,1) and RMS-normalised rows)",
+        "config": {"workload": desc, "global_batch": B, "seq_len": int(base.ctx),
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "dominant_kernel_us": dom_time * 1e6,
+        "stages_us": {s: float(per[:, j].sum()) * 1e6 for j, s in enumerate(DECODE_STAGES)},
+        "step_algorithmic_GBs": step_bytes / (ms_per_step * 1e-3) / 1e9,
+    }
+    if len(layers) > 1:
+        result["layers_us"] = [{"kind": L.mode, **{s: float(per[i, j]) * 1e6 for j, s in
+                                                   enumerate(DECODE_STAGES)}}
+                               for i, L in enumerate(layers)]
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_decode(cfgs, ds, args.cpu_seconds)
+    return result, per
+
+
+def run_prefill(args):
+    import numpy as np
+    import torch
+
+    from long_context_attention_14_amd import pipeline
+    from synth import gen
+    from synth.configs import CSA_PREFILL_CHUNK
+
+    cfg = CSA_PREFILL_CHUNK
+    dev = "cuda"
+    d = gen.prefill_inputs(cfg)
+    layer = pipeline.PrefillLayer(cfg, d, dev)
+    stages = [("compress", layer.compress), ("window", layer.window_kv), ("indexer", layer.indexer),
+              ("topk", layer.topk), ("attention", layer.attention)]
+    _calibrate_copy(args.calibrate_copy, dev)
+    for _ in range(args.warmup):
+        layer.run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record()
+        for j, (_, f) in enumerate(stages):
+            f()
+            evs[i][j + 1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e-3
+           for j, (n, _) in enumerate(stages)}
+    ms_per_step = elapsed / args.steps * 1e3
+    # dominant kernel: the indexer, MFMA-bound; algorithmic flops = every visible
+    # (query, entry) pair x 64 heads x 128 dims x 2
+    pos = cfg.ctx + np.arange(cfg.n_new)
+    pairs = float(np.minimum((pos + 1) // cfg.m, layer.N_cap).sum())
+    flops = pairs * cfg.H_I * cfg.d_I * 2
+    achieved = flops / per["indexer"] / 1e12
+    result = {
+        "metric": "CSA prefill query-tokens/s + indexer MFMA TFLOP/s vs peak",
+        "value": cfg.n_new * args.steps / elapsed, "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8 indexer / bf16 KV / fp32 accumulate",
+        "data": "synthetic (seeded; N(0,1) and RMS-normalised rows)",
+        "config": {"workload": "csa_prefill_8k_on_128k: 8192 new tokens after a 131072-token "
+                               "prefix, m=4 (34816 entries), fp8 indexer 64x128, top-1024, MQA "
+                               "64x512 bf16, window 128",
+                   "global_batch": 1, "seq_len": cfg.ctx + cfg.n_new, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / FP8_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "indexer_mfma_kernel<fp8>"},
+        "stages_us": {k: v * 1e6 for k, v in per.items()},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_prefill(cfg, d, args.cpu_seconds)
+    return result, per
 
 
 def main():
@@ -92,93 +361,13 @@ def main():
               "multi-GPU path; batch sharding across GPUs is described in the design notes.",
               file=sys.stderr)
         sys.exit(2)
-    import numpy as np
-    import torch
-
-    from long_context_attention_14_amd import ops, pipeline
-    from synth import gen
-    from synth.configs import CSA_DECODE_1M
-
-    cfg = CSA_DECODE_1M
-    dev = "cuda"
-    total_steps = args.warmup + args.steps
-    d = gen.decode_inputs(cfg, extra_entries=total_steps // cfg.m + 2)
-    layer = pipeline.DecodeLayer(cfg, d, dev)
-    B, m = cfg.B, cfg.m
-    stages = ["append", "indexer", "topk", "attention"]
-    hip = HipEvents()
-
-    def step(ev=None):
-        ops.lca_decode_step(layer.state, layer.tokC, layer.tokZ, layer.q, layer.out, cfg.io_dtype,
-                            qI=layer.qI, w=layer.w, lse=layer.lse, idx_out=layer.idx,
-                            workspace=layer.workspace, stage_events=ev)
-
-    if args.calibrate_copy:
-        n = args.calibrate_copy << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[hip.create() for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    per_stage = {s: [] for s in stages}
-    for ev in events:
-        for j, s in enumerate(stages):
-            per_stage[s].append(hip.elapsed_s(ev[j], ev[j + 1]))
-    for ev in events:
-        for e in ev:
-            hip.destroy(e)
-    avg = {s: float(np.mean(v)) for s, v in per_stage.items()}
-    ms_per_step = elapsed / args.steps * 1e3
-    value = B * args.steps / elapsed
-
-    # dominant kernel: the indexer.  Algorithmic bytes per launch: every visible
-    # entry's 128-byte fp8 key, plus the 64x128 fp8 query and 64 fp32 weights of
-    # each sequence (the fp32 score output is not counted).
-    n_vis_mean = float(np.mean([((d["lengths"] + args.warmup + i) // m).sum() for i in range(args.steps)]))
-    idx_bytes = n_vis_mean * cfg.d_I + B * cfg.H_I * (cfg.d_I + 4)
-    achieved = idx_bytes / avg["indexer"] / 1e9
-    # traffic from the committed rocprofv3 counter summary of this kernel, if current
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", "indexer_fp8_decode_b16_1m_counters.txt")
-    if os.path.exists(tfile):
-        kv = dict(l.split(":", 1) for l in open(tfile) if ":" in l and not l.startswith("#"))
-        src = os.path.join(ROOT, "long_context_attention_14_amd", "csrc", "indexer.hip")
-        import hashlib
-        cur = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-        if kv.get("indexer_source_sha256_16", "").strip() == cur and "hbm_bytes_per_launch" in kv:
-            traffic = float(kv["hbm_bytes_per_launch"])
-    step_bytes = idx_bytes + B * (cfg.k * cfg.c * 2 + cfg.n_win * cfg.c * 2 + 2 * cfg.H * cfg.c * 2)
-    result = {
-        "metric": "CSA/HCA decode query-tokens/s at 1M ctx + achieved HBM GB/s vs peak",
-        "value": value, "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8 indexer / bf16 KV / fp32 accumulate",
-        "data": "synthetic (seeded; N(0,1) and RMS-normalised rows)",
-        "config": {"workload": "csa_decode_b16_1m: batch 16, context 2^20 + U{0..3}, m=4 "
-                               "(262144 entries), fp8 indexer 64x128, top-1024, MQA 64x512 bf16, "
-                               "window 128",
-                   "global_batch": B, "seq_len": int(cfg.ctx), "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "indexer_mfma_kernel<fp8>"},
-        "stages_us": {s: v * 1e6 for s, v in avg.items()},
-        "step_algorithmic_GBs": step_bytes / (ms_per_step * 1e-3) / 1e9,
-    }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_seconds)
+    if args.workload == "csa_prefill_chunk":
+        result, per = run_prefill(args)
+    else:
+        result, per = run_decode(args, args.workload)
     if args.detail:
         with open(args.detail, "w") as f:
-            json.dump({"per_stage_s": per_stage, "result": result}, f)
+            json.dump({"per_stage": per if isinstance(per, dict) else per.tolist(), "result": result}, f)
     print(json.dumps(result), flush=True)
 
 

@@ -219,9 +219,15 @@ constexpr int kMH = 64;            // heads
 constexpr int kQS = kMC + 8;       // LDS row stride of Q and KV tiles (bf16 elements)
 constexpr int kPS = kMT + 8;       // LDS row stride of P (bf16 elements)
 constexpr int kSS = kMT + 1;       // LDS row stride of S (floats)
-constexpr int kMfmaSplitRows = 128;
 
 __device__ __forceinline__ v8bf_t as_v8bf(uint4 u) { return __builtin_bit_cast(v8bf_t, u); }
+
+// Two OCP e4m3 bytes (the low or the high 16 bits of w) -> packed bf16 pair, with
+// gfx950's scaled conversion at scale 1 (every e4m3 value is a bf16 value).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
 
 __device__ __forceinline__ v16f_t mfma_bf16(const v8bf_t& a, const v8bf_t& b, const v16f_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -354,17 +360,11 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < kMT / 4; ++i) {
       uint4 v = raw[i];
-      if (KVFMT != LCA_BF16 && lane < 56) {  // 8 fp8 dims -> bf16
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[e] = e4m3_to_f32((raw[i].x >> (8 * e)) & 0xffu);
-          x[4 + e] = e4m3_to_f32((raw[i].y >> (8 * e)) & 0xffu);
-        }
-        v.x = pack_bf16(x[0], x[1]);
-        v.y = pack_bf16(x[2], x[3]);
-        v.z = pack_bf16(x[4], x[5]);
-        v.w = pack_bf16(x[6], x[7]);
+      if (KVFMT != LCA_BF16 && lane < 56) {  // 8 OCP e4m3 dims -> bf16 (exact)
+        v.x = fp8x2_to_bf16x2<false>(raw[i].x);
+        v.y = fp8x2_to_bf16x2<true>(raw[i].x);
+        v.z = fp8x2_to_bf16x2<false>(raw[i].y);
+        v.w = fp8x2_to_bf16x2<true>(raw[i].y);
       }
       *reinterpret_cast<uint4*>(&kv_s[(wv + 4 * i) * kQS + lane * 8]) = v;
     }
@@ -532,7 +532,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
 // One wave per (query row, head): combine the splits in split order.  Lane s
 // reads split s's lse (wave-wide max and weights by shuffles), and every
 // split's partial row is loaded before the weighted sum.
-constexpr int kMaxMergeSplits = 64;
+constexpr int kMaxMergeSplits = 256;
 
 template <int CPL>
 __global__ __launch_bounds__(256) void attn_merge_kernel(
@@ -544,14 +544,25 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
   const int lane = threadIdx.x & 63;
   const long long row = rh / H;
   const int h = static_cast<int>(rh % H);
-  const float my_lse = lane < n_splits ? part_lse[(row * n_splits + lane) * H + h] : -INFINITY;
-  float mx = fmaxf(wave_max(my_lse), sink ? sink[h] : -INFINITY);
+  // lane holds the lse of splits lane, lane + 64, ... (at most kMaxMergeSplits)
+  float my_lse[kMaxMergeSplits / 64];
+  float lmax = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kMaxMergeSplits / 64; ++u) {
+    const int sp = lane + 64 * u;
+    my_lse[u] = sp < n_splits ? part_lse[(row * n_splits + sp) * H + h] : -INFINITY;
+    lmax = fmaxf(lmax, my_lse[u]);
+  }
+  float mx = fmaxf(wave_max(lmax), sink ? sink[h] : -INFINITY);
   float acc[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
   float den = 0.f;
   if (mx != -INFINITY) {
-    const float my_w = my_lse == -INFINITY ? 0.f : __expf(my_lse - mx);
+    float my_w[kMaxMergeSplits / 64];
+#pragma unroll
+    for (int u = 0; u < kMaxMergeSplits / 64; ++u)
+      my_w[u] = my_lse[u] == -INFINITY ? 0.f : __expf(my_lse[u] - mx);
     if (sink) den = __expf(sink[h] - mx);
     for (int s0 = 0; s0 < n_splits; s0 += 8) {
       float v[8][CPL];
@@ -566,7 +577,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const float wgt = __shfl(my_w, s0 + u < n_splits ? s0 + u : 0, 64);
+        const int sp = s0 + u < n_splits ? s0 + u : 0;
+        float wsel = my_w[0];
+#pragma unroll
+        for (int q = 1; q < kMaxMergeSplits / 64; ++q) wsel = (sp >> 6) == q ? my_w[q] : wsel;
+        const float wgt = __shfl(wsel, sp & 63, 64);
         if (s0 + u >= n_splits) continue;
         den += wgt;
 #pragma unroll
@@ -596,17 +611,26 @@ Plan make_plan(long long rows, int H, int c, int q_fmt, int kv_fmt, int k, int N
   const int NT = (dense ? N_cap : k) + n_win;
   Plan p;
   p.mfma = use_mfma(H, c, q_fmt, kv_fmt);
-  int split_rows = p.mfma ? kMfmaSplitRows : kSplitRows;
   if (rows >= 512) {
     p.n_splits = 1;
     p.split_rows = NT;
-  } else {
-    // at most kMaxMergeSplits splits (the merge gives each split one lane)
-    const int min_rows = (NT + kMaxMergeSplits - 1) / kMaxMergeSplits;
-    while (split_rows < min_rows) split_rows *= 2;
-    p.split_rows = split_rows;
-    p.n_splits = (NT + split_rows - 1) / split_rows;
+    return p;
   }
+  int split_rows;
+  if (p.mfma) {
+    // one workgroup per CU and one round: about 256 / rows splits per row, each a
+    // whole number of 64-row tiles
+    const long long want = rows >= 256 ? 1 : 256 / rows;
+    const long long per = (NT + want - 1) / want;
+    split_rows = static_cast<int>(((per + kMT - 1) / kMT) * kMT);
+  } else {
+    split_rows = kSplitRows;
+  }
+  if (split_rows < kMT) split_rows = kMT;
+  const int min_rows = (NT + kMaxMergeSplits - 1) / kMaxMergeSplits;
+  if (split_rows < min_rows) split_rows = ((min_rows + kMT - 1) / kMT) * kMT;
+  p.split_rows = split_rows;
+  p.n_splits = (NT + split_rows - 1) / split_rows;
   return p;
 }
 
