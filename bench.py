@@ -13,12 +13,15 @@ Other workloads (--workload): HCA decode at 128K (batch 32), the 8-layer hybrid
 decode stack at 1M (batch 4, MXFP4 indexer, fp8+bf16 KV) and the CSA prefill
 chunk (8192 tokens on a 131072 prefix); the default line is the 1M CSA decode.
 
-Prints ONE JSON line.  The timed loop calls lca_decode_step; on every 4th step
-the library records two HIP events (lca_decode_io.stage_events) around the
-dominant kernel on the stream its kernels run on, which gives that kernel's
-duration for the roofline.  The per-stage breakdown ("stages_us") comes from an
-untimed diagnostic loop that records all five events (each event record adds
-a few microseconds of GPU time, so those stage times include them).
+Prints ONE JSON line.  The timed loop calls lca_decode_step.  For a CSA layer
+the library launches the indexer (the dominant kernel) with two HIP events
+(lca_decode_io.stage_events[1], [2]) as its dispatch's own start and end
+stamps, on every timed step, which gives that kernel's duration for the
+roofline without extra packets on the stream.  For HCA alone the dominant kernel
+is the attention: every 4th step records two events around its stage (an event
+record costs a few microseconds of GPU time, so the other steps record none).
+The per-stage breakdown ("stages_us") comes from an untimed diagnostic loop
+that sets all five events (the recorded ones include that cost).
 """
 import argparse
 import json
@@ -181,12 +184,12 @@ def run_decode(args, workload):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # Timed region: every SAMPLE-th step records two events around the dominant
-    # kernel (an event record costs GPU time, so the other steps record none).
+    # Timed region: the indexer's events are its dispatch stamps (every step);
+    # the HCA attention stage is bracketed by recorded events on every 4th step.
     csa_layers = [i for i, L in enumerate(layers) if L.mode == "csa"]
     dom_layers = csa_layers if csa_layers else [0]
     dom = (1, 2) if csa_layers else (3, 4)          # indexer or attention stage
-    SAMPLE = 4
+    SAMPLE = 1 if csa_layers else 4
     sampled = {}
     for i in range(0, args.steps, SAMPLE):
         sampled[i] = {li: (hip.create(), hip.create()) for li in dom_layers}

@@ -274,9 +274,11 @@ typedef struct lca_decode_io {
   float* lse;           /* [B, H] or NULL */
   int out_dtype;
   int32_t* idx_out;     /* CSA: [B, k] selected entries, or NULL (kept in workspace) */
-  /* Optional hipEvent_t handles (NULL = skip), recorded on `stream` before the
-   * state append, after it, after the indexer, after the top-k and after the
-   * attention; an HCA layer records [2] and [3] right after the append. */
+  /* Optional hipEvent_t handles (NULL = skip) on `stream`: [0] is recorded before
+   * the state append; in a CSA layer [1] and [2] are the start and end stamps of
+   * the indexer's own dispatch (no separate event packet, so [2] - [1] is the
+   * indexer kernel's duration); [3] is recorded after the top-k and [4] after the
+   * attention.  An HCA layer records [1], [2] and [3] right after the append. */
   void* stage_events[5];
 } lca_decode_io;
 

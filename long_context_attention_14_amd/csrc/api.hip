@@ -302,17 +302,18 @@ int lca_decode_step(const lca_decode_layer* L, const lca_decode_io* io, void* wo
                                            L->eps, s, hist, hist ? lca::topk_hist_words(L->B) : 0),
                   "lca_decode_step/append");
   if (st != LCA_OK) return st;
-  if ((st = mark(1)) != LCA_OK) return st;
   const int32_t* sel = nullptr;
   if (csa) {
     float* scores = reinterpret_cast<float*>(ws + d.scores);
     int32_t* idx = io->idx_out ? io->idx_out : reinterpret_cast<int32_t*>(ws + d.idx);
+    // events 1 and 2 are the indexer dispatch's own start and end stamps
     st = hip_status(lca::launch_indexer(L->B, 1, L->H_I, L->d_I, L->idx_dtype, io->qI, io->qI_scale,
                                         L->kI, L->kI_scale, L->N_cap, io->w, q_pos, L->m, n_ent,
-                                        scores, s, hist),
+                                        scores, s, hist,
+                                        reinterpret_cast<hipEvent_t>(io->stage_events[1]),
+                                        reinterpret_cast<hipEvent_t>(io->stage_events[2])),
                     "lca_decode_step/indexer");
     if (st != LCA_OK) return st;
-    if ((st = mark(2)) != LCA_OK) return st;
     if (hist)
       st = hip_status(lca::launch_topk_from_hist(L->B, 1, L->N_cap, scores, q_pos, L->m, n_ent, L->k,
                                                  idx, ws + d.topk, s),
@@ -325,6 +326,7 @@ int lca_decode_step(const lca_decode_layer* L, const lca_decode_io* io, void* wo
     if ((st = mark(3)) != LCA_OK) return st;
     sel = idx;
   } else {
+    if ((st = mark(1)) != LCA_OK) return st;
     if ((st = mark(2)) != LCA_OK) return st;
     if ((st = mark(3)) != LCA_OK) return st;
   }

@@ -243,7 +243,8 @@ hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const v
                           const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale,
                           int N_cap, const float* w, const int32_t* q_pos, int m,
                           const int32_t* n_entries, float* scores, hipStream_t s,
-                          uint32_t* hist = nullptr);
+                          uint32_t* hist = nullptr, hipEvent_t ev_start = nullptr,
+                          hipEvent_t ev_stop = nullptr);
 size_t topk_workspace_bytes(int B, int n_q, int N_cap, int k);
 hipError_t launch_topk(int B, int n_q, int N_cap, const float* scores, const int32_t* q_pos, int m,
                        const int32_t* n_entries, int k, int32_t* idx, void* ws, hipStream_t s);

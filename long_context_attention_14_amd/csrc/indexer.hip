@@ -19,6 +19,8 @@
 // contiguous bytes per lane and key.  For MXFP4 each lane's 32 values must be
 // exactly one 32-element scale block, so lane group g takes block 2g + ks
 // together with that block's E8M0 scale.
+#include <hip/hip_ext.h>
+
 #include "common.h"
 
 namespace lca {
@@ -235,16 +237,21 @@ hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const v
                           const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale,
                           int N_cap, const float* w, const int32_t* q_pos, int m,
                           const int32_t* n_entries, float* scores, hipStream_t s,
-                          uint32_t* hist) {
+                          uint32_t* hist, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const long long rows = static_cast<long long>(B) * n_q;
   if (rows == 0 || N_cap == 0) return hipSuccess;
   if (idx_fmt == LCA_F32) {
     const int n_chunks = (N_cap + kF32Threads - 1) / kF32Threads;
     const size_t lds = sizeof(float) * (static_cast<size_t>(H_I) * d_I + H_I);
-    hipLaunchKernelGGL(indexer_f32_kernel, dim3(static_cast<unsigned>(rows * n_chunks)),
-                       dim3(kF32Threads), lds, s, static_cast<const float*>(qI),
-                       static_cast<const float*>(kI), n_q, H_I, d_I, N_cap, n_chunks, w, q_pos, m,
-                       n_entries, scores);
+    const dim3 g(static_cast<unsigned>(rows * n_chunks));
+    if (ev_start || ev_stop)
+      hipExtLaunchKernelGGL(indexer_f32_kernel, g, dim3(kF32Threads), lds, s, ev_start, ev_stop, 0,
+                            static_cast<const float*>(qI), static_cast<const float*>(kI), n_q, H_I,
+                            d_I, N_cap, n_chunks, w, q_pos, m, n_entries, scores);
+    else
+      hipLaunchKernelGGL(indexer_f32_kernel, g, dim3(kF32Threads), lds, s,
+                         static_cast<const float*>(qI), static_cast<const float*>(kI), n_q, H_I, d_I,
+                         N_cap, n_chunks, w, q_pos, m, n_entries, scores);
     return hipGetLastError();
   }
   const long long max_blocks = (N_cap + kBlockKeys - 1) / kBlockKeys;
@@ -256,18 +263,23 @@ hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const v
   const uint8_t* q8 = static_cast<const uint8_t*>(qI);
   const uint8_t* k8 = static_cast<const uint8_t*>(kI);
   const bool mx = idx_fmt == LCA_MXFP4;
+  // start/stop events, when given, are stamped by the dispatch itself
+  auto go = [&](auto kern) {
+    if (ev_start || ev_stop)
+      hipExtLaunchKernelGGL(kern, grid, block, 0, s, ev_start, ev_stop, 0, q8, qI_scale, k8, kI_scale,
+                            n_q, N_cap, n_chunks, w, q_pos, m, n_entries, scores, hist);
+    else
+      hipLaunchKernelGGL(kern, grid, block, 0, s, q8, qI_scale, k8, kI_scale, n_q, N_cap, n_chunks, w,
+                         q_pos, m, n_entries, scores, hist);
+  };
   if (!mx && !hist)
-    hipLaunchKernelGGL((indexer_mfma_kernel<false, false>), grid, block, 0, s, q8, qI_scale, k8,
-                       kI_scale, n_q, N_cap, n_chunks, w, q_pos, m, n_entries, scores, hist);
+    go(indexer_mfma_kernel<false, false>);
   else if (!mx)
-    hipLaunchKernelGGL((indexer_mfma_kernel<false, true>), grid, block, 0, s, q8, qI_scale, k8,
-                       kI_scale, n_q, N_cap, n_chunks, w, q_pos, m, n_entries, scores, hist);
+    go(indexer_mfma_kernel<false, true>);
   else if (!hist)
-    hipLaunchKernelGGL((indexer_mfma_kernel<true, false>), grid, block, 0, s, q8, qI_scale, k8,
-                       kI_scale, n_q, N_cap, n_chunks, w, q_pos, m, n_entries, scores, hist);
+    go(indexer_mfma_kernel<true, false>);
   else
-    hipLaunchKernelGGL((indexer_mfma_kernel<true, true>), grid, block, 0, s, q8, qI_scale, k8,
-                       kI_scale, n_q, N_cap, n_chunks, w, q_pos, m, n_entries, scores, hist);
+    go(indexer_mfma_kernel<true, true>);
   return hipGetLastError();
 }
 
