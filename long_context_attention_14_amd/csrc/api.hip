@@ -219,16 +219,25 @@ struct DecodeLayout {
 
 size_t al(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// A CSA layer with an MFMA indexer format on rows too long for the LDS top-k
+// fuses the top-k into the indexer (no score array): see SelectWs.
+bool fused_select(const lca_decode_layer* L) {
+  return L->mode == LCA_CSA && L->idx_dtype != LCA_F32 && lca::select_supported(L->N_cap, L->k);
+}
+
 DecodeLayout decode_layout(const lca_decode_layer* L) {
   DecodeLayout d;
   const size_t B = static_cast<size_t>(L->B);
   const bool csa = L->mode == LCA_CSA;
+  const bool fused = fused_select(L);
   size_t off = 0;
   d.q_pos = off; off += al(B * 4);
   d.n_entries = off; off += al(B * 4);
-  d.scores = off; off += csa ? al(B * static_cast<size_t>(L->N_cap) * 4) : 0;
+  d.scores = off; off += csa && !fused ? al(B * static_cast<size_t>(L->N_cap) * 4) : 0;
   d.idx = off; off += csa ? al(B * static_cast<size_t>(L->k) * 4) : 0;
-  d.topk = off; off += csa ? al(lca::topk_workspace_bytes(L->B, 1, L->N_cap, L->k)) : 0;
+  d.topk = off;
+  if (fused) off += al(lca::select_workspace_bytes(L->B, L->N_cap));
+  else if (csa) off += al(lca::topk_workspace_bytes(L->B, 1, L->N_cap, L->k));
   d.mqa = off;
   off += al(lca::mqa_workspace_bytes(L->B, 1, L->H, L->c, L->kv_dtype, csa ? L->k : 0, L->N_cap,
                                      L->n_win, csa ? 0 : 1));
@@ -291,30 +300,47 @@ int lca_decode_step(const lca_decode_layer* L, const lca_decode_io* io, void* wo
     return hip_status(hipEventRecord(reinterpret_cast<hipEvent_t>(io->stage_events[i]), s),
                       "lca_decode_step/event");
   };
-  // the fused histogram path: the indexer accumulates the top-k's row histogram
+  // Long CSA rows: either the fused selection (the indexer keeps its scores on
+  // chip and emits a superset of the top k; a finish pass selects) or the
+  // histogram path (the indexer writes scores and accumulates the top-k's row
+  // histogram).  Either way the append clears the histogram as a side job.
+  const bool fused = fused_select(L);
+  lca::SelectWs sw{};
   uint32_t* hist = nullptr;
-  if (csa && L->idx_dtype != LCA_F32)
+  long long zero_words = 0;
+  if (fused) {
+    sw = lca::select_ws_in(ws + d.topk, L->B, L->N_cap);
+    hist = sw.hist;
+    zero_words = lca::select_zero_words(L->B);
+  } else if (csa && L->idx_dtype != LCA_F32) {
     hist = lca::topk_hist_in_workspace(ws + d.topk, L->B, 1, L->N_cap, L->k);
+    zero_words = hist ? lca::topk_hist_words(L->B) : 0;
+  }
   if ((st = mark(0)) != LCA_OK) return st;
   st = hip_status(lca::launch_state_append(L->mode, L->m, L->B, L->c, L->n_win, io->tokC, io->tokZ,
                                            L->io_dtype, L->tailC, L->tailZ, L->ring, L->kv_dtype,
                                            L->P, L->cache, L->N_cap, L->n_tokens, q_pos, n_ent,
-                                           L->eps, s, hist, hist ? lca::topk_hist_words(L->B) : 0),
+                                           L->eps, s, hist, zero_words),
                   "lca_decode_step/append");
   if (st != LCA_OK) return st;
   const int32_t* sel = nullptr;
   if (csa) {
-    float* scores = reinterpret_cast<float*>(ws + d.scores);
+    float* scores = fused ? nullptr : reinterpret_cast<float*>(ws + d.scores);
     int32_t* idx = io->idx_out ? io->idx_out : reinterpret_cast<int32_t*>(ws + d.idx);
     // events 1 and 2 are the indexer dispatch's own start and end stamps
     st = hip_status(lca::launch_indexer(L->B, 1, L->H_I, L->d_I, L->idx_dtype, io->qI, io->qI_scale,
                                         L->kI, L->kI_scale, L->N_cap, io->w, q_pos, L->m, n_ent,
-                                        scores, s, hist,
+                                        scores, s, fused ? nullptr : hist,
                                         reinterpret_cast<hipEvent_t>(io->stage_events[1]),
-                                        reinterpret_cast<hipEvent_t>(io->stage_events[2])),
+                                        reinterpret_cast<hipEvent_t>(io->stage_events[2]),
+                                        fused ? &sw : nullptr, L->k),
                     "lca_decode_step/indexer");
     if (st != LCA_OK) return st;
-    if (hist)
+    if (fused)
+      st = hip_status(lca::launch_select_finish(L->B, 1, L->N_cap, q_pos, L->m, n_ent, L->k, idx, sw,
+                                                s),
+                      "lca_decode_step/topk");
+    else if (hist)
       st = hip_status(lca::launch_topk_from_hist(L->B, 1, L->N_cap, scores, q_pos, L->m, n_ent, L->k,
                                                  idx, ws + d.topk, s),
                       "lca_decode_step/topk");

@@ -183,6 +183,10 @@ __device__ __forceinline__ uint32_t score_key(float x) {
 }
 constexpr int kScoreHistBins = 4096;
 __device__ __forceinline__ uint32_t score_bin(uint32_t key) { return key >> 20; }
+// Word of bin b in a row's histogram in global memory: neighbouring bins sit in
+// different 128-byte lines (bin b -> line b % 32), so the few dozen bins a row's
+// scores fall in do not make one hot line for the atomics of many workgroups.
+__device__ __forceinline__ int hist_slot(int b) { return ((b & 31) << 7) | (b >> 5); }
 
 // Threshold of a row from its histogram in LDS (kScoreHistBins bins, bin
 // order == key order): the bin holding the want-th largest key and the count
@@ -237,14 +241,38 @@ hipError_t launch_state_append(int mode, int m, int B, int c, int n_win, const v
                                int32_t* n_tokens, int32_t* q_pos, int32_t* n_entries, float eps,
                                hipStream_t s, uint32_t* zero_buf = nullptr,
                                long long zero_words = 0);
+// Fused indexer + selection workspace (rows = B * n_q, n_blk = ceil(N_cap / 128)).
+// hist must be zero before the indexer runs (select_zero_words(rows) words).  The indexer writes, for every
+// 128-entry block that holds visible entries, the (key, index) pairs of that
+// block which can still be among the row's k largest, in index order, and their
+// count; the finish pass selects the top k from them.
+constexpr int kSelBlock = 128;
+struct SelectWs {
+  uint32_t* hist;      // [rows, 4096] score_bin histogram (hist_slot order)
+  int32_t* emit_cnt;   // [rows, n_blk]
+  uint2* emit;         // [rows, n_blk, 128] (score key, entry index) pairs
+  uint32_t* cand_key;  // [rows, N_cap] finish pass: threshold-bin keys when LDS overflows
+  int32_t* cand_idx;   // [rows, N_cap]
+  int n_blk;
+};
+size_t select_workspace_bytes(long long rows, int N_cap);
+long long select_zero_words(long long rows);
+SelectWs select_ws_in(void* ws, long long rows, int N_cap);
+// whether the fused path takes rows of N_cap entries and this k
+bool select_supported(int N_cap, int k);
+hipError_t launch_select_finish(int B, int n_q, int N_cap, const int32_t* q_pos, int m,
+                                const int32_t* n_entries, int k, int32_t* idx, const SelectWs& w,
+                                hipStream_t s);
+
 // hist (optional, [B*n_q, 4096], zeroed by the caller): the MFMA path adds the
-// score_bin histogram of every row's visible scores into it.
+// score_bin histogram of every row's visible scores into it.  sel (optional,
+// MFMA formats only): the fused selecting sink; scores is then not written.
 hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const void* qI,
                           const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale,
                           int N_cap, const float* w, const int32_t* q_pos, int m,
                           const int32_t* n_entries, float* scores, hipStream_t s,
                           uint32_t* hist = nullptr, hipEvent_t ev_start = nullptr,
-                          hipEvent_t ev_stop = nullptr);
+                          hipEvent_t ev_stop = nullptr, const SelectWs* sel = nullptr, int k = 0);
 size_t topk_workspace_bytes(int B, int n_q, int N_cap, int k);
 hipError_t launch_topk(int B, int n_q, int N_cap, const float* scores, const int32_t* q_pos, int m,
                        const int32_t* n_entries, int k, int32_t* idx, void* ws, hipStream_t s);

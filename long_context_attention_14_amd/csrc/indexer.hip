@@ -21,6 +21,8 @@
 // together with that block's E8M0 scale.
 #include <hip/hip_ext.h>
 
+#include <algorithm>
+
 #include "common.h"
 
 namespace lca {
@@ -38,7 +40,6 @@ constexpr int kBlockKeys = kIdxWaves * kKeysPerGroup;  // 128 keys per workgroup
 // keeps HBM row-buffer locality.  Chosen so that a decode batch has about
 // 1536 workgroups (6 per CU).
 constexpr int kTargetBlocks = 1536;
-constexpr int kPrefetch = 2;
 
 __device__ __forceinline__ v8i load32(const uint8_t* p) {
   const uint4 a = *reinterpret_cast<const uint4*>(p);
@@ -61,6 +62,11 @@ __device__ __forceinline__ v8i load16(const uint8_t* p) {
 template <int FMT>
 __device__ __forceinline__ v16f mfma(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 0, sa, 0, sb);
+}
+
+__device__ __forceinline__ int lanes_below64(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
 }
 
 template <bool MX>
@@ -92,35 +98,11 @@ __device__ __forceinline__ void load_group(const uint8_t* kb_base, const uint8_t
   }
 }
 
-// HIST: also accumulate the score_bin histogram of the written scores into
-// hist[row] (global, zeroed by the caller) through a per-workgroup LDS histogram.
-template <bool MX, bool HIST>
-__global__ __launch_bounds__(kWave * kIdxWaves, 3) void indexer_mfma_kernel(
-    const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qI_scale,
-    const uint8_t* __restrict__ kI, const uint8_t* __restrict__ kI_scale, int n_q, int N_cap,
-    int wpr, const float* __restrict__ w, const int32_t* __restrict__ q_pos, int m,
-    const int32_t* __restrict__ n_entries, float* __restrict__ scores,
-    uint32_t* __restrict__ hist) {
-  constexpr int kFmt = MX ? 4 : 0;
-  constexpr int kRowBytes = MX ? 64 : 128;  // bytes of one 128-dim vector
-  __shared__ uint32_t lh[HIST ? kScoreHistBins : 1];
-  const long long row = blockIdx.x / wpr;
-  const int wi = blockIdx.x % wpr;
-  const int b = static_cast<int>(row / n_q);
-  const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
-  if (wi * kBlockKeys >= vis) return;
-
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
-  const int j = lane & 31;
-  const int g = lane >> 5;
-  if (HIST) {
-    for (int i = threadIdx.x; i < kScoreHistBins; i += kWave * kIdxWaves) lh[i] = 0;
-  }
-
-  // A operand: query heads 32*ht + j, K-steps ks = 0, 1
-  v8i A[2][2];
-  int sA[2][2];
+// A operand of one query row: heads 32*ht + j, K-steps ks = 0, 1.
+template <bool MX>
+__device__ __forceinline__ void load_query(const uint8_t* qI, const uint8_t* qI_scale, long long row,
+                                           int j, int g, v8i (&A)[2][2], int (&sA)[2][2]) {
+  constexpr int kRowBytes = MX ? 64 : 128;
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
     const size_t hrow = static_cast<size_t>(row) * 64 + 32 * ht + j;
@@ -137,67 +119,320 @@ __global__ __launch_bounds__(kWave * kIdxWaves, 3) void indexer_mfma_kernel(
       }
     }
   }
-  // head weights in LDS: register r of accumulator tile ht is head
-  // 32*ht + 8*(r/4) + 4*g + (r%4), so four consecutive registers read one float4
-  __shared__ __attribute__((aligned(16))) float w_s[64];
-  if (threadIdx.x < 64) w_s[threadIdx.x] = w[static_cast<size_t>(row) * 64 + threadIdx.x];
+}
 
+// Score of key column j of a 32-key group (valid in every lane; lanes j and j+32
+// agree): the 64 heads' ReLU'd dot products weighted by w_s and summed.  Register
+// r of accumulator tile ht is head 32*ht + 8*(r/4) + 4*g + (r%4), so four
+// consecutive registers read one float4 of the weights.
+template <bool MX>
+__device__ __forceinline__ float group_score(const v8i (&A)[2][2], const int (&sA)[2][2],
+                                             const KeyGroup<MX>& cur, const float* w_s, int g) {
+  constexpr int kFmt = MX ? 4 : 0;
+  v16f acc0 = {0}, acc1 = {0};
+  acc0 = mfma<kFmt>(A[0][0], cur.b[0], acc0, sA[0][0], cur.sb[0]);
+  acc0 = mfma<kFmt>(A[0][1], cur.b[1], acc0, sA[0][1], cur.sb[1]);
+  acc1 = mfma<kFmt>(A[1][0], cur.b[0], acc1, sA[1][0], cur.sb[0]);
+  acc1 = mfma<kFmt>(A[1][1], cur.b[1], acc1, sA[1][1], cur.sb[1]);
+  float s = 0.f;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const float4 w4 = *reinterpret_cast<const float4*>(&w_s[8 * a + 4 * g]);
+    s += w4.x * fmaxf(acc0[4 * a], 0.f);
+    s += w4.y * fmaxf(acc0[4 * a + 1], 0.f);
+    s += w4.z * fmaxf(acc0[4 * a + 2], 0.f);
+    s += w4.w * fmaxf(acc0[4 * a + 3], 0.f);
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const float4 w4 = *reinterpret_cast<const float4*>(&w_s[32 + 8 * a + 4 * g]);
+    s += w4.x * fmaxf(acc1[4 * a], 0.f);
+    s += w4.y * fmaxf(acc1[4 * a + 1], 0.f);
+    s += w4.z * fmaxf(acc1[4 * a + 2], 0.f);
+    s += w4.w * fmaxf(acc1[4 * a + 3], 0.f);
+  }
+  return s + __shfl_xor(s, 32, kWave);
+}
+
+// Scores of every visible key, written to scores[row]; HIST: also add their
+// score_bin histogram into hist[row] (global, zeroed by the caller) through a
+// per-workgroup LDS histogram.  Workgroup wi of a row takes the row's 128-key
+// blocks wi, wi + wpr, ...; wave w the 32 keys at offset 32w of each.
+template <bool MX, bool HIST>
+__global__ __launch_bounds__(kWave * kIdxWaves, 3) void indexer_mfma_kernel(
+    const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qI_scale,
+    const uint8_t* __restrict__ kI, const uint8_t* __restrict__ kI_scale, int n_q, int N_cap,
+    int wpr, const float* __restrict__ w, const int32_t* __restrict__ q_pos, int m,
+    const int32_t* __restrict__ n_entries, float* __restrict__ scores,
+    uint32_t* __restrict__ hist) {
+  constexpr int kRowBytes = MX ? 64 : 128;  // bytes of one 128-dim vector
+  __shared__ uint32_t lh[HIST ? kScoreHistBins : 1];
+  __shared__ __attribute__((aligned(16))) float w_s[64];
+  const long long row = blockIdx.x / wpr;
+  const int wi = blockIdx.x % wpr;
+  const int b = static_cast<int>(row / n_q);
+  const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
+  if (wi * kBlockKeys >= vis) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 31;
+  const int g = lane >> 5;
+  if (HIST) {
+    for (int i = threadIdx.x; i < kScoreHistBins; i += kWave * kIdxWaves) lh[i] = 0;
+  }
+  v8i A[2][2];
+  int sA[2][2];
+  load_query<MX>(qI, qI_scale, row, j, g, A, sA);
+  if (threadIdx.x < 64) w_s[threadIdx.x] = w[static_cast<size_t>(row) * 64 + threadIdx.x];
   const uint8_t* kb_base = kI + static_cast<size_t>(b) * N_cap * kRowBytes;
   const uint8_t* ks_base = MX ? kI_scale + static_cast<size_t>(b) * N_cap * 4 : nullptr;
   float* out = scores + static_cast<size_t>(row) * N_cap;
   __syncthreads();
 
-  // this wave's groups: keys [kb, kb + 32) for kb = wi*128 + 32*wave + t*stride
+  // Every wave runs all n_t steps (a group past the end loads a clamped key and
+  // stores nothing).
   const int stride = kBlockKeys * wpr;
-  int kb = wi * kBlockKeys + wave * kKeysPerGroup;
-  KeyGroup<MX> buf[kPrefetch];
-#pragma unroll
-  for (int p = 0; p < kPrefetch; ++p) {
-    const int kk = kb + p * stride;
-    if (kk < vis) load_group<MX>(kb_base, ks_base, min(kk + j, vis - 1), g, buf[p]);
-  }
-  for (; kb < vis; kb += stride) {
-    KeyGroup<MX> nxt;
-    const int kn = kb + kPrefetch * stride;
-    if (kn < vis) load_group<MX>(kb_base, ks_base, min(kn + j, vis - 1), g, nxt);
-    const KeyGroup<MX>& cur = buf[0];
-    v16f acc0 = {0}, acc1 = {0};
-    acc0 = mfma<kFmt>(A[0][0], cur.b[0], acc0, sA[0][0], cur.sb[0]);
-    acc0 = mfma<kFmt>(A[0][1], cur.b[1], acc0, sA[0][1], cur.sb[1]);
-    acc1 = mfma<kFmt>(A[1][0], cur.b[0], acc1, sA[1][0], cur.sb[0]);
-    acc1 = mfma<kFmt>(A[1][1], cur.b[1], acc1, sA[1][1], cur.sb[1]);
-    float s = 0.f;
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const float4 w4 = *reinterpret_cast<const float4*>(&w_s[8 * a + 4 * g]);
-      s += w4.x * fmaxf(acc0[4 * a], 0.f);
-      s += w4.y * fmaxf(acc0[4 * a + 1], 0.f);
-      s += w4.z * fmaxf(acc0[4 * a + 2], 0.f);
-      s += w4.w * fmaxf(acc0[4 * a + 3], 0.f);
-    }
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const float4 w4 = *reinterpret_cast<const float4*>(&w_s[32 + 8 * a + 4 * g]);
-      s += w4.x * fmaxf(acc1[4 * a], 0.f);
-      s += w4.y * fmaxf(acc1[4 * a + 1], 0.f);
-      s += w4.z * fmaxf(acc1[4 * a + 2], 0.f);
-      s += w4.w * fmaxf(acc1[4 * a + 3], 0.f);
-    }
-    s += __shfl_xor(s, 32, kWave);
+  const int n_t = (vis - wi * kBlockKeys + stride - 1) / stride;
+  auto key0 = [&](int t) {
+    return (wi + min(t, n_t - 1) * wpr) * kBlockKeys + wave * kKeysPerGroup;
+  };
+  auto load = [&](KeyGroup<MX>& G, int t) {
+    load_group<MX>(kb_base, ks_base, min(key0(t) + j, vis - 1), g, G);
+  };
+  auto step = [&](const KeyGroup<MX>& cur, int t) {
+    const float s = group_score<MX>(A, sA, cur, w_s, g);
+    const int kb = key0(t);
     if (g == 0 && kb + j < vis) {
       out[kb + j] = s;
       if (HIST) atomicAdd(&lh[score_bin(score_key(s))], 1u);
     }
-#pragma unroll
-    for (int p = 0; p < kPrefetch - 1; ++p) buf[p] = buf[p + 1];
-    buf[kPrefetch - 1] = nxt;
+  };
+  // Three named buffers, unrolled by three: a load always fills the buffer whose
+  // group was consumed one step earlier, so nothing is copied between registers
+  // (a copy of a buffer still in flight would make the wave wait for it) and two
+  // groups stay in flight while one is computed.  The loads are unconditional:
+  // a load under a branch leaves the count of newer loads unknown, and the wave
+  // would then wait for all of them.  The query operands arrive first.
+  __builtin_amdgcn_s_waitcnt(0);
+  KeyGroup<MX> g0, g1, g2;
+  load(g0, 0);
+  __builtin_amdgcn_sched_barrier(0);  // g0's loads go out before g1's, as in the loop
+  load(g1, 1);
+  for (int t = 0; t < n_t; t += 3) {
+    load(g2, t + 2);
+    step(g0, t);
+    if (t + 1 >= n_t) break;
+    load(g0, t + 3);
+    step(g1, t + 1);
+    if (t + 2 >= n_t) break;
+    load(g1, t + 4);
+    step(g2, t + 2);
   }
   if (HIST) {
     __syncthreads();
     uint32_t* gh = hist + row * kScoreHistBins;
     for (int i = threadIdx.x; i < kScoreHistBins; i += kWave * kIdxWaves)
-      if (lh[i]) atomicAdd(&gh[i], lh[i]);
+      if (lh[i]) atomicAdd(&gh[hist_slot(i)], lh[i]);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Fused selection (SelectWs): the scores stay in LDS and only the entries that
+// can still be among the row's k largest leave the chip.
+
+constexpr int kSelWaves = 12;                      // one workgroup per CU
+constexpr int kSelThreads = kWave * kSelWaves;
+// LDS scores per workgroup: at most 280 blocks (140 KiB; the workgroup is alone on its CU)
+constexpr int kSelMaxBlocks = 280;
+
+// After a workgroup's scores are final: bound the row's threshold bin from
+// below, write every entry at or above the bound into the per-block lists
+// (index order), then add the rest of the workgroup's histogram (lh holds the
+// counts not flushed yet) to the row's.  Histogram counts only grow, and the
+// counts in lh are added only after the row histogram has been read, so
+// (count read) + (count in lh) never exceeds the final count of a bin: if bins
+// >= b hold >= k entries by that sum, the final k-th largest key lies in bin
+// >= b.  Every entry of the final top-k is therefore emitted, whatever the
+// order in which workgroups run, and no workgroup waits for another.  The bound
+// looks at the blockDim bins ending 32 bins above the workgroup's highest bin;
+// entries elsewhere only make it weaker.
+template <int NW>
+__device__ void select_emit(uint32_t* lh, const float* sc, int n_t, int wi, int wpr, int vis,
+                            long long row, const SelectWs& o, int k, uint32_t kmax) {
+  constexpr int NT = NW * kWave;
+  __shared__ int sh_bin, scan_sh[NW];
+  __shared__ uint32_t top_sh[NW];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  uint32_t* gh = o.hist + row * kScoreHistBins;
+  for (int off = 32; off >= 1; off >>= 1)
+    kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(kmax, off, kWave)));
+  if (lane == 0) top_sh[wave] = kmax;
+  if (tid == 0) sh_bin = -1;
+  __syncthreads();
+  uint32_t tk = 0;
+#pragma unroll
+  for (int x = 0; x < NW; ++x) tk = max(tk, top_sh[x]);
+  const int top = static_cast<int>(score_bin(tk));
+  const int hi = min(top + 32, kScoreHistBins - 1);
+  const int bin = hi - tid;
+  int v = 0;
+  if (bin >= 0)
+    v = static_cast<int>(__hip_atomic_load(&gh[hist_slot(bin)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) +
+                         lh[bin]);
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int u = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += u;
+  }
+  if (lane == kWave - 1) scan_sh[wave] = incl;
+  __syncthreads();
+  for (int x = 0; x < wave; ++x) incl += scan_sh[x];
+  // the highest bin whose cumulative count from hi reaches k (a unique thread)
+  if (incl >= k && incl - v < k) sh_bin = bin;
+  const int b_lb = __syncthreads_or(incl >= k) ? sh_bin : -1;
+  // emission: wave w takes blocks w, w + NW, ...; lane l holds keys l and l + 64
+  // of the block, so two ballots give every emitted entry its place in index order
+  for (int t = wave; t < n_t; t += NW) {
+    const int blk = wi + t * wpr;
+    const int i0 = blk * kSelBlock + lane, i1 = i0 + kWave;
+    const uint32_t k0 = i0 < vis ? score_key(sc[t * kSelBlock + lane]) : 0u;
+    const uint32_t k1 = i1 < vis ? score_key(sc[t * kSelBlock + kWave + lane]) : 0u;
+    const bool e0 = i0 < vis && static_cast<int>(score_bin(k0)) >= b_lb;
+    const bool e1 = i1 < vis && static_cast<int>(score_bin(k1)) >= b_lb;
+    const uint64_t m0 = __ballot(e0), m1 = __ballot(e1);
+    const int n0 = __popcll(m0);
+    const size_t seg = static_cast<size_t>(row) * o.n_blk + blk;
+    if (e0) {
+      const int p = lanes_below64(m0);
+      o.emit[seg * kSelBlock + p] = make_uint2(k0, static_cast<uint32_t>(i0));
+    }
+    if (e1) {
+      const int p = n0 + lanes_below64(m1);
+      o.emit[seg * kSelBlock + p] = make_uint2(k1, static_cast<uint32_t>(i1));
+    }
+    if (lane == 0) o.emit_cnt[seg] = n0 + __popcll(m1);
+  }
+  for (int bb = tid; bb < kScoreHistBins; bb += NT)
+    if (lh[bb]) atomicAdd(&gh[hist_slot(bb)], lh[bb]);
+}
+
+// One 12-wave workgroup per CU.  Rows are interleaved over the grid (row =
+// blockIdx % rows), workgroup wi of a row owns the row's blocks wi, wi + wpr,
+// ... (n_t of them, 4 groups of 32 keys each), and the workgroup's waves take
+// its groups from an LDS counter, so a wave that the CU serves faster simply
+// takes more of them and all waves end together.  Group q's scores go to
+// sc[32 q ...] (block q/4, offset 32 (q%4)).  The wave that takes the middle
+// group also flushes the histogram so far (atomic exchange on the LDS bins, no
+// barrier), which lets the row's other workgroups bound the threshold tightly.
+template <bool MX>
+__global__ __launch_bounds__(kSelThreads, 1) void indexer_select_kernel(
+    const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qI_scale,
+    const uint8_t* __restrict__ kI, const uint8_t* __restrict__ kI_scale, int n_q, int N_cap,
+    int wpr, const float* __restrict__ w, const int32_t* __restrict__ q_pos, int m,
+    const int32_t* __restrict__ n_entries, SelectWs sel, int k) {
+  constexpr int kRowBytes = MX ? 64 : 128;
+  constexpr int kFirst = 3;  // groups per wave assigned before the counter
+  __shared__ uint32_t lh[kScoreHistBins];
+  __shared__ __attribute__((aligned(16))) float w_s[64];
+  __shared__ int next_grp;
+  extern __shared__ float sc[];
+  const long long rows = gridDim.x / wpr;
+  const long long row = blockIdx.x % rows;
+  const int wi = static_cast<int>(blockIdx.x / rows);
+  const int b = static_cast<int>(row / n_q);
+  const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
+  if (wi * kBlockKeys >= vis) return;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
+  const int j = lane & 31;
+  const int g = lane >> 5;
+  for (int i = tid; i < kScoreHistBins; i += kSelThreads) lh[i] = 0;
+  if (tid == 0) next_grp = kSelWaves * kFirst;
+  v8i A[2][2];
+  int sA[2][2];
+  load_query<MX>(qI, qI_scale, row, j, g, A, sA);
+  if (tid < 64) w_s[tid] = w[static_cast<size_t>(row) * 64 + tid];
+  const uint8_t* kb_base = kI + static_cast<size_t>(b) * N_cap * kRowBytes;
+  const uint8_t* ks_base = MX ? kI_scale + static_cast<size_t>(b) * N_cap * 4 : nullptr;
+  const int stride = kBlockKeys * wpr;
+  const int n_t = (vis - wi * kBlockKeys + stride - 1) / stride;
+  const int n_grp = 4 * n_t;
+  const int mid = n_grp / 2;
+  __syncthreads();
+
+  auto key0 = [&](int q) {  // first key of group q (q past the end: the last group)
+    q = min(q, n_grp - 1);
+    return (wi + (q >> 2) * wpr) * kBlockKeys + (q & 3) * kKeysPerGroup;
+  };
+  auto load = [&](KeyGroup<MX>& G, int q) {
+    load_group<MX>(kb_base, ks_base, min(key0(q) + j, vis - 1), g, G);
+  };
+  auto grab = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&next_grp, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  uint32_t kmax = 0;  // largest score key this lane wrote
+  auto step = [&](const KeyGroup<MX>& cur, int q) {
+    const float s = group_score<MX>(A, sA, cur, w_s, g);
+    const int kb = key0(q);
+    if (g == 0 && kb + j < vis) {
+      const uint32_t key = score_key(s);
+      sc[q * kKeysPerGroup + j] = s;
+      kmax = max(kmax, key);
+      atomicAdd(&lh[score_bin(key)], 1u);
+    }
+  };
+  // Group numbers only grow along a wave (the first kFirst are static, the rest
+  // come from the counter), so the first one past the end ends the wave.  The
+  // wave holding group `mid` stops there, flushes the histogram so far and
+  // restarts: the pipelined loop itself holds no global write, which keeps the
+  // compiler's waits for the key loads exact.
+  int qa = wave, qb = wave + kSelWaves, qc = wave + 2 * kSelWaves;
+  int stop = (qa == mid || qb == mid || qc == mid) ? mid : n_grp;
+  while (true) {
+    __builtin_amdgcn_s_waitcnt(0);  // (re)start with nothing in flight
+    KeyGroup<MX> g0, g1, g2;
+    load(g0, qa);
+    __builtin_amdgcn_sched_barrier(0);  // g0's loads go out before g1's, as in the loop
+    load(g1, qb);
+    // three named buffers, unrolled by three (see indexer_mfma_kernel)
+    while (true) {
+      if (qa >= stop) break;
+      load(g2, qc);
+      const int qd = grab();
+      if (qd == mid) stop = mid;
+      step(g0, qa);
+      if (qb >= stop) {
+        qa = qb; qb = qc; qc = qd;
+        break;
+      }
+      load(g0, qd);
+      const int qe = grab();
+      if (qe == mid) stop = mid;
+      step(g1, qb);
+      if (qc >= stop) {
+        qa = qc; qb = qd; qc = qe;
+        break;
+      }
+      load(g1, qe);
+      const int qf = grab();
+      if (qf == mid) stop = mid;
+      step(g2, qc);
+      qa = qd; qb = qe; qc = qf;
+    }
+    if (qa >= n_grp) break;
+    // qa == mid: about half of the workgroup's groups are done
+    uint32_t* gh = sel.hist + row * kScoreHistBins;
+    for (int i = lane; i < kScoreHistBins; i += kWave) {
+      const uint32_t c = atomicExch(&lh[i], 0u);
+      if (c) atomicAdd(&gh[hist_slot(i)], c);
+    }
+    stop = n_grp;
+  }
+  __syncthreads();
+  select_emit<kSelWaves>(lh, sc, n_t, wi, wpr, vis, row, sel, k, kmax);
 }
 
 // Scalar fp32 path for small shapes: one thread per (query, entry).
@@ -233,14 +468,29 @@ __global__ __launch_bounds__(kF32Threads) void indexer_f32_kernel(
 
 }  // namespace
 
+static int device_cus() {
+  static int cached = 0;
+  if (cached == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      cached = cus;
+    else
+      return 256;
+  }
+  return cached;
+}
+
 hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const void* qI,
                           const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale,
                           int N_cap, const float* w, const int32_t* q_pos, int m,
                           const int32_t* n_entries, float* scores, hipStream_t s,
-                          uint32_t* hist, hipEvent_t ev_start, hipEvent_t ev_stop) {
+                          uint32_t* hist, hipEvent_t ev_start, hipEvent_t ev_stop,
+                          const SelectWs* sel, int k) {
   const long long rows = static_cast<long long>(B) * n_q;
   if (rows == 0 || N_cap == 0) return hipSuccess;
   if (idx_fmt == LCA_F32) {
+    if (sel) return hipErrorInvalidValue;  // the selecting kernel is MFMA-only
     const int n_chunks = (N_cap + kF32Threads - 1) / kF32Threads;
     const size_t lds = sizeof(float) * (static_cast<size_t>(H_I) * d_I + H_I);
     const dim3 g(static_cast<unsigned>(rows * n_chunks));
@@ -255,31 +505,61 @@ hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const v
     return hipGetLastError();
   }
   const long long max_blocks = (N_cap + kBlockKeys - 1) / kBlockKeys;
+  const uint8_t* q8 = static_cast<const uint8_t*>(qI);
+  const uint8_t* k8 = static_cast<const uint8_t*>(kI);
+  const bool mx = idx_fmt == LCA_MXFP4;
+  if (sel) {
+    // one workgroup per CU in a single round when the row's blocks fit in
+    // floor(CUs / rows) workgroups' LDS, else more workgroups (and rounds)
+    long long wpr = std::max<long long>(device_cus() / rows,
+                                        (max_blocks + kSelMaxBlocks - 1) / kSelMaxBlocks);
+    wpr = std::min(wpr, max_blocks);
+    const size_t lds = sizeof(float) * kBlockKeys * static_cast<size_t>((max_blocks + wpr - 1) / wpr);
+    const dim3 grid(static_cast<unsigned>(rows * wpr)), block(kSelThreads);
+    const int iw = static_cast<int>(wpr);
+    const SelectWs so = *sel;
+    hipError_t e = hipSuccess;
+    auto go = [&](auto kern) {
+      static bool attr_set = false;  // per kernel: LDS above the default dynamic limit
+      if (!attr_set) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                static_cast<int>(sizeof(float) * kBlockKeys * kSelMaxBlocks));
+        if (e != hipSuccess) return;
+        attr_set = true;
+      }
+      if (ev_start || ev_stop)
+        hipExtLaunchKernelGGL(kern, grid, block, lds, s, ev_start, ev_stop, 0, q8, qI_scale, k8,
+                              kI_scale, n_q, N_cap, iw, w, q_pos, m, n_entries, so, k);
+      else
+        hipLaunchKernelGGL(kern, grid, block, lds, s, q8, qI_scale, k8, kI_scale, n_q, N_cap, iw, w,
+                           q_pos, m, n_entries, so, k);
+    };
+    if (mx) go(indexer_select_kernel<true>);
+    else go(indexer_select_kernel<false>);
+    return e != hipSuccess ? e : hipGetLastError();
+  }
   long long wpr = (kTargetBlocks + rows - 1) / rows;
   wpr = wpr < 1 ? 1 : (wpr > max_blocks ? max_blocks : wpr);
   const dim3 grid(static_cast<unsigned>(rows * wpr));
   const int n_chunks = static_cast<int>(wpr);
   const dim3 block(kWave * kIdxWaves);
-  const uint8_t* q8 = static_cast<const uint8_t*>(qI);
-  const uint8_t* k8 = static_cast<const uint8_t*>(kI);
-  const bool mx = idx_fmt == LCA_MXFP4;
   // start/stop events, when given, are stamped by the dispatch itself
   auto go = [&](auto kern) {
     if (ev_start || ev_stop)
-      hipExtLaunchKernelGGL(kern, grid, block, 0, s, ev_start, ev_stop, 0, q8, qI_scale, k8, kI_scale,
-                            n_q, N_cap, n_chunks, w, q_pos, m, n_entries, scores, hist);
+      hipExtLaunchKernelGGL(kern, grid, block, 0, s, ev_start, ev_stop, 0, q8, qI_scale, k8,
+                            kI_scale, n_q, N_cap, n_chunks, w, q_pos, m, n_entries, scores, hist);
     else
-      hipLaunchKernelGGL(kern, grid, block, 0, s, q8, qI_scale, k8, kI_scale, n_q, N_cap, n_chunks, w,
-                         q_pos, m, n_entries, scores, hist);
+      hipLaunchKernelGGL(kern, grid, block, 0, s, q8, qI_scale, k8, kI_scale, n_q, N_cap, n_chunks,
+                         w, q_pos, m, n_entries, scores, hist);
   };
-  if (!mx && !hist)
-    go(indexer_mfma_kernel<false, false>);
-  else if (!mx)
-    go(indexer_mfma_kernel<false, true>);
-  else if (!hist)
-    go(indexer_mfma_kernel<true, false>);
-  else
-    go(indexer_mfma_kernel<true, true>);
+  if (!mx) {
+    if (hist) go(indexer_mfma_kernel<false, true>);
+    else go(indexer_mfma_kernel<false, false>);
+  } else {
+    if (hist) go(indexer_mfma_kernel<true, true>);
+    else go(indexer_mfma_kernel<true, false>);
+  }
   return hipGetLastError();
 }
 

@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kSegThreads) void topk_hist_kernel(
   __syncthreads();
   uint32_t* gh = ghist + row * kHistBins;
   for (int i = threadIdx.x; i < kHistBins; i += kSegThreads)
-    if (h[i]) atomicAdd(&gh[i], h[i]);
+    if (h[i]) atomicAdd(&gh[hist_slot(i)], h[i]);
 }
 
 // Threshold of a row: (bin of the k-th largest key, count of keys in higher
@@ -229,8 +229,7 @@ __device__ void row_threshold(const uint32_t* gh, uint32_t* lh, int vis, int k, 
     __syncthreads();
     return;
   }
-  const uint4* g4 = reinterpret_cast<const uint4*>(gh);
-  for (int i = threadIdx.x; i < kHistBins / 4; i += blockDim.x) reinterpret_cast<uint4*>(lh)[i] = g4[i];
+  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) lh[i] = gh[hist_slot(i)];
   __syncthreads();
   find_threshold_block(lh, k, sh_bin, sh_above, scan_sh);
 }
@@ -316,6 +315,73 @@ __global__ __launch_bounds__(kSegThreads) void topk_collect_kernel(
   }
 }
 
+
+// Radix-select the `need` largest candidates (all in one 12-bit top bin, so only
+// the low 20 key bits differ; passes of 8, 8 and 4 bits) and write their indices
+// to Ch in candidate order (ties: earlier candidates first).  The candidates are
+// in ascending index order, so Ch is ascending.  All threads of a kRowThreads
+// block call it.
+template <class KeyF, class IdxF>
+__device__ int select_candidates(int nCand, int need, KeyF cand_key, IdxF cand_idx, int32_t* Ch,
+                                 uint32_t* hist, int* sh_b2, int* sh_a2, uint32_t* wgt,
+                                 uint32_t* weq) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (need <= 0) return 0;
+  uint32_t prefix = 0, mask = 0;
+  int remaining = need;
+  const int shifts[3] = {12, 4, 0};
+  const int widths[3] = {8, 8, 4};
+  for (int pass = 0; pass < 3; ++pass) {
+    const int sh = shifts[pass];
+    const uint32_t dm = (1u << widths[pass]) - 1u;
+    for (int i = tid; i < 256; i += kRowThreads) hist[i] = 0;
+    __syncthreads();
+    for (int p = tid; p < nCand; p += kRowThreads) {
+      const uint32_t key = cand_key(p);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> sh) & dm], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) find_bin_wave(hist, 256, remaining, sh_b2, sh_a2);
+    __syncthreads();
+    prefix |= static_cast<uint32_t>(*sh_b2) << sh;
+    mask |= dm << sh;
+    remaining -= *sh_a2;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  const int need_eq = remaining;
+  int run_gt = 0, run_eq = 0;
+  for (int base = 0; base < nCand; base += kRowThreads) {
+    const int p = base + tid;
+    const uint32_t key = p < nCand ? (cand_key(p) & 0xfffffu) : 0u;
+    const bool gt = p < nCand && key > T;
+    const bool eq = p < nCand && key == T;
+    const uint64_t bg = __ballot(gt), be = __ballot(eq);
+    if (lane == 0) {
+      wgt[wv] = __popcll(bg);
+      weq[wv] = __popcll(be);
+    }
+    __syncthreads();
+    int og = run_gt, oe = run_eq, tg = 0, te = 0;
+    for (int x = 0; x < kRowThreads / 64; ++x) {
+      if (x < wv) {
+        og += wgt[x];
+        oe += weq[x];
+      }
+      tg += wgt[x];
+      te += weq[x];
+    }
+    const int gb = og + lanes_below(bg), eb = oe + lanes_below(be);
+    const int pc = gb + min(eb, need_eq);
+    if ((gt || (eq && eb < need_eq)) && pc < need) Ch[pc] = cand_idx(p);
+    run_gt += tg;
+    run_eq += te;
+    __syncthreads();
+  }
+  __syncthreads();
+  return need;
+}
+
 __device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int x) {
   int lo = 0, hi = n;
   while (lo < hi) {
@@ -323,6 +389,21 @@ __device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int x) {
     if (a[mid] < x) lo = mid + 1; else hi = mid;
   }
   return lo;
+}
+
+// Merge the ascending lists S[0..nS) and Ch[0..nC) into out[0..k), -1 after.
+__device__ void merge_to_output(const int32_t* S, int nS, const int32_t* Ch, int nC, int32_t* out,
+                                int k) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < nS; i += kRowThreads) {
+    const int pos = i + lower_bound_i32(Ch, nC, S[i]);
+    if (pos < k) out[pos] = S[i];
+  }
+  for (int i = tid; i < nC; i += kRowThreads) {
+    const int pos = i + lower_bound_i32(S, nS, Ch[i]);
+    if (pos < k) out[pos] = Ch[i];
+  }
+  for (int i = nS + nC + tid; i < k; i += kRowThreads) out[i] = -1;
 }
 
 constexpr int kMaxK = 4096;
@@ -422,76 +503,244 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
     return ws.cand_idx[(row * n_seg + s) * kSeg + (p - seg_c[s])];
   };
   const int need = vis <= k ? 0 : k - sh_above;
-  int nC = 0;
-  if (need > 0) {
-    // radix select among the candidates on the low 20 key bits (8, 8, 4)
-    uint32_t prefix = 0, mask = 0;
-    int remaining = need;
-    const int shifts[3] = {12, 4, 0};
-    const int widths[3] = {8, 8, 4};
-    for (int pass = 0; pass < 3; ++pass) {
-      const int sh = shifts[pass];
-      const uint32_t dm = (1u << widths[pass]) - 1u;
-      for (int i = tid; i < 256; i += kRowThreads) hist[i] = 0;
-      __syncthreads();
-      for (int p = tid; p < nCand; p += kRowThreads) {
-        const uint32_t key = cand_key(p);
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> sh) & dm], 1u);
-      }
-      __syncthreads();
-      if (tid < 64) find_bin_wave(hist, 256, remaining, &sh_b2, &sh_a2);
-      __syncthreads();
-      prefix |= static_cast<uint32_t>(sh_b2) << sh;
-      mask |= dm << sh;
-      remaining -= sh_a2;
-      __syncthreads();
-    }
-    // every candidate shares the top 12 bits, so compare the low 20 only
-    const uint32_t T = prefix;
-    const int need_eq = remaining;
-    int run_gt = 0, run_eq = 0;
-    for (int base = 0; base < nCand; base += kRowThreads) {
-      const int p = base + tid;
-      const uint32_t key = p < nCand ? (cand_key(p) & 0xfffffu) : 0u;
-      const bool gt = p < nCand && key > T;
-      const bool eq = p < nCand && key == T;
-      const uint64_t bg = __ballot(gt), be = __ballot(eq);
-      if (lane == 0) {
-        wgt[wv] = __popcll(bg);
-        weq[wv] = __popcll(be);
-      }
-      __syncthreads();
-      int og = run_gt, oe = run_eq, tg = 0, te = 0;
-      for (int x = 0; x < kRowThreads / 64; ++x) {
-        if (x < wv) {
-          og += wgt[x];
-          oe += weq[x];
-        }
-        tg += wgt[x];
-        te += weq[x];
-      }
-      const int gb = og + lanes_below(bg), eb = oe + lanes_below(be);
-      const int pc = gb + min(eb, need_eq);
-      if ((gt || (eq && eb < need_eq)) && pc < need) Ch[pc] = cand_idx(p);
-      run_gt += tg;
-      run_eq += te;
-      __syncthreads();
-    }
-    nC = need;
-  }
-  __syncthreads();
-  // merge the two ascending lists
-  for (int i = tid; i < nS; i += kRowThreads) {
-    const int pos = i + lower_bound_i32(Ch, nC, S[i]);
-    if (pos < k) out[pos] = S[i];
-  }
-  for (int i = tid; i < nC; i += kRowThreads) {
-    const int pos = i + lower_bound_i32(S, nS, Ch[i]);
-    if (pos < k) out[pos] = Ch[i];
-  }
-  for (int i = nS + nC + tid; i < k; i += kRowThreads) out[i] = -1;
+  const int nC = select_candidates(nCand, need, cand_key, cand_idx, Ch, hist, &sh_b2, &sh_a2, wgt, weq);
+  merge_to_output(S, nS, Ch, nC, out, k);
 }
 
+
+// ---------------------------------------------------------------------------
+// finish of the fused indexer selection (SelectWs): the indexer emitted, per
+// 128-entry block and in index order, a superset of the row's top k.  One
+// workgroup per row: the exact threshold bin b* from the final histogram, the
+// block counts' prefix sums, a gather of the emitted pairs into LDS, an ordered
+// split into "above b*" (all selected) and "in b*" (candidates), the radix
+// selection among the candidates, and the merge of the two ascending lists.
+constexpr int kMaxBlk = 8192;     // blocks per row (N_cap <= 1 Mi entries)
+constexpr int kEmitLds = 8192;    // emitted pairs held in LDS (else read from global)
+constexpr int kSegPerThread = kMaxBlk / kRowThreads;
+
+// Block-wide exclusive prefix of two per-thread counts (kRowThreads threads);
+// also returns the totals.  scan_a/scan_b hold kRowThreads/64 ints each.
+__device__ __forceinline__ void block_scan2(int a, int b, int* ea, int* eb, int* ta, int* tb,
+                                            int* scan_a, int* scan_b) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int ia = a, ib = b;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int va = __shfl_up(ia, o, 64), vb = __shfl_up(ib, o, 64);
+    if (lane >= o) {
+      ia += va;
+      ib += vb;
+    }
+  }
+  if (lane == 63) {
+    scan_a[wv] = ia;
+    scan_b[wv] = ib;
+  }
+  __syncthreads();
+  int oa = ia - a, ob = ib - b, sa = 0, sb = 0;
+  for (int x = 0; x < kRowThreads / 64; ++x) {
+    if (x < wv) {
+      oa += scan_a[x];
+      ob += scan_b[x];
+    }
+    sa += scan_a[x];
+    sb += scan_b[x];
+  }
+  *ea = oa;
+  *eb = ob;
+  *ta = sa;
+  *tb = sb;
+}
+
+constexpr int kEmitPerThread = kEmitLds / kRowThreads;  // 8
+
+__global__ __launch_bounds__(kRowThreads) void select_finish_kernel(
+    int N_cap, int n_q, const int32_t* __restrict__ q_pos, int m, const int32_t* __restrict__ n_entries,
+    int k, SelectWs ws, int32_t* __restrict__ idx) {
+  __shared__ int32_t S[kMaxK], Ch[kMaxK];
+  __shared__ int seg_off[kMaxBlk + 1];
+  __shared__ uint32_t ck[kEmitLds];
+  __shared__ int32_t ci[kEmitLds];
+  __shared__ uint32_t lh[kHistBins];
+  __shared__ uint32_t hist[256];
+  __shared__ int sh_bin, sh_above, sh_b2, sh_a2;
+  __shared__ int scan_sh[kRowThreads / 64], scan_a[kRowThreads / 64], scan_b[kRowThreads / 64];
+  __shared__ uint32_t wgt[kRowThreads / 64], weq[kRowThreads / 64];
+  const long long row = blockIdx.x;
+  const int b = static_cast<int>(row / n_q);
+  const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int32_t* out = idx + row * k;
+  const int nb = (vis + kSelBlock - 1) / kSelBlock;
+  const size_t seg0 = static_cast<size_t>(row) * ws.n_blk;
+  // the row histogram and the block counts, loaded together
+  const int q = (nb + kRowThreads - 1) / kRowThreads;  // blocks [t*q, t*q + q) of thread t
+  uint32_t hv[kHistBins / kRowThreads];
+#pragma unroll
+  for (int u = 0; u < kHistBins / kRowThreads; ++u)
+    hv[u] = ws.hist[row * kHistBins + hist_slot(tid + u * kRowThreads)];
+  int cnt[kSegPerThread];
+  int local = 0;
+#pragma unroll
+  for (int u = 0; u < kSegPerThread; ++u) {
+    const int sgi = tid * q + u;
+    cnt[u] = (u < q && sgi < nb) ? ws.emit_cnt[seg0 + sgi] : 0;
+    local += cnt[u];
+  }
+#pragma unroll
+  for (int u = 0; u < kHistBins / kRowThreads; ++u) lh[tid + u * kRowThreads] = hv[u];
+  if (tid == 0) {
+    sh_bin = -1;
+    sh_above = vis;
+  }
+  int run, dummy, E, dummy2;
+  block_scan2(local, 0, &run, &dummy, &E, &dummy2, scan_a, scan_b);
+#pragma unroll
+  for (int u = 0; u < kSegPerThread; ++u) {
+    const int sgi = tid * q + u;
+    if (u < q && sgi < nb) seg_off[sgi] = run;
+    run += cnt[u];
+  }
+  if (tid == 0) seg_off[nb] = E;
+  __syncthreads();
+  // exact threshold bin b* of the row (vis <= k: every entry is selected)
+  if (vis > k) find_threshold_block(lh, k, &sh_bin, &sh_above, scan_sh);
+  const int bstar = sh_bin;
+  const int need = vis <= k ? 0 : k - sh_above;
+  int nS = 0, nC = 0;
+  if (E <= kEmitLds) {
+    // gather: entry p = tid + 1024 u (neighbouring lanes read neighbouring slots
+    // of a block), one search and one 8-byte load each, all loads at once
+    size_t off[kEmitPerThread];
+#pragma unroll
+    for (int u = 0; u < kEmitPerThread; ++u) {
+      const int p = tid + u * kRowThreads;
+      off[u] = seg0 * kSelBlock;
+      if (p < E) {
+        const int sgp = seg_of(seg_off, nb, p);
+        off[u] = (seg0 + sgp) * kSelBlock + (p - seg_off[sgp]);
+      }
+    }
+    uint2 pr[kEmitPerThread];
+#pragma unroll
+    for (int u = 0; u < kEmitPerThread; ++u) pr[u] = ws.emit[off[u]];
+#pragma unroll
+    for (int u = 0; u < kEmitPerThread; ++u) {
+      const int p = tid + u * kRowThreads;
+      if (p < E) {
+        ck[p] = pr[u].x;
+        ci[p] = static_cast<int32_t>(pr[u].y);
+      }
+    }
+    __syncthreads();
+    // thread t then takes entries [8t, 8t + 8) in order
+    const int p0 = tid * kEmitPerThread;
+    uint32_t key[kEmitPerThread];
+    int32_t id[kEmitPerThread];
+#pragma unroll
+    for (int u = 0; u < kEmitPerThread; ++u) {
+      key[u] = p0 + u < E ? ck[p0 + u] : 0u;
+      id[u] = p0 + u < E ? ci[p0 + u] : 0;
+    }
+    int ns = 0, nc = 0;
+#pragma unroll
+    for (int u = 0; u < kEmitPerThread; ++u) {
+      const int bin = static_cast<int>(score_bin(key[u]));
+      ns += (p0 + u < E && bin > bstar) ? 1 : 0;
+      nc += (p0 + u < E && bin == bstar) ? 1 : 0;
+    }
+    int os, oc, ts, tc;
+    block_scan2(ns, nc, &os, &oc, &ts, &tc, scan_a, scan_b);  // (every read of ck/ci is done)
+#pragma unroll
+    for (int u = 0; u < kEmitPerThread; ++u) {
+      if (p0 + u >= E) continue;
+      const int bin = static_cast<int>(score_bin(key[u]));
+      if (bin > bstar) {
+        if (os < kMaxK) S[os] = id[u];
+        ++os;
+      } else if (bin == bstar) {
+        ck[oc] = key[u];
+        ci[oc] = id[u];
+        ++oc;
+      }
+    }
+    nS = min(ts, k);
+    __syncthreads();
+    auto cand_key = [&](int p) -> uint32_t { return ck[p]; };
+    auto cand_idx = [&](int p) -> int32_t { return ci[p]; };
+    nC = select_candidates(tc, need, cand_key, cand_idx, Ch, hist, &sh_b2, &sh_a2, wgt, weq);
+  } else {
+    // more emitted entries than LDS holds: ordered split straight from global
+    // memory, candidates to the row's global candidate arrays
+    uint32_t* gck = ws.cand_key + row * N_cap;
+    int32_t* gci = ws.cand_idx + row * N_cap;
+    int run_s = 0, run_c = 0;
+    for (int base = 0; base < E; base += kRowThreads) {
+      const int p = base + tid;
+      const bool valid = p < E;
+      uint32_t key = 0u;
+      int32_t id = 0;
+      if (valid) {
+        const int sgp = seg_of(seg_off, nb, p);
+        const size_t o = (seg0 + sgp) * kSelBlock + (p - seg_off[sgp]);
+        const uint2 e = ws.emit[o];
+        key = e.x;
+        id = static_cast<int32_t>(e.y);
+      }
+      const int bin = static_cast<int>(score_bin(key));
+      const bool is_s = valid && bin > bstar;
+      const bool is_c = valid && bin == bstar;
+      const uint64_t bs = __ballot(is_s), bc = __ballot(is_c);
+      if (lane == 0) {
+        wgt[wv] = __popcll(bs);
+        weq[wv] = __popcll(bc);
+      }
+      __syncthreads();
+      int os = run_s, oc = run_c, ts = 0, tc = 0;
+      for (int x = 0; x < kRowThreads / 64; ++x) {
+        if (x < wv) {
+          os += wgt[x];
+          oc += weq[x];
+        }
+        ts += wgt[x];
+        tc += weq[x];
+      }
+      const int ps = os + lanes_below(bs), pc = oc + lanes_below(bc);
+      if (is_s && ps < kMaxK) S[ps] = id;
+      if (is_c) {
+        gck[pc] = key;
+        gci[pc] = id;
+      }
+      run_s += ts;
+      run_c += tc;
+      __syncthreads();
+    }
+    nS = min(run_s, k);
+    auto cand_key = [&](int p) -> uint32_t { return gck[p]; };
+    auto cand_idx = [&](int p) -> int32_t { return gci[p]; };
+    nC = select_candidates(run_c, need, cand_key, cand_idx, Ch, hist, &sh_b2, &sh_a2, wgt, weq);
+  }
+  merge_to_output(S, nS, Ch, nC, out, k);
+}
+
+struct SelectLayout {
+  size_t hist, emit_cnt, emit, cand_key, cand_idx, total;
+};
+
+inline SelectLayout select_layout(long long rows, int N_cap) {
+  SelectLayout L;
+  const size_t r = static_cast<size_t>(rows), n = static_cast<size_t>(N_cap);
+  const size_t nb = (n + kSelBlock - 1) / kSelBlock;
+  size_t off = 0;
+  L.hist = off;     off += align256(r * kHistBins * 4);
+  L.emit_cnt = off; off += align256(r * nb * 4);
+  L.emit = off;     off += align256(r * nb * kSelBlock * 8);
+  L.cand_key = off; off += align256(r * n * 4);
+  L.cand_idx = off; off += align256(r * n * 4);
+  L.total = off;
+  return L;
+}
 }  // namespace
 
 static int n_segments(int N_cap) { return (N_cap + kSeg - 1) / kSeg; }
@@ -551,6 +800,38 @@ hipError_t launch_topk(int B, int n_q, int N_cap, const float* scores, const int
   hipLaunchKernelGGL(topk_hist_kernel, g2, dim3(kSegThreads), 0, s, scores, N_cap, n_q, q_pos, m,
                      n_entries, k, n_seg, w.hist);
   return launch_collect_finish(rows, N_cap, scores, n_q, q_pos, m, n_entries, k, idx, w, n_seg, s);
+}
+
+bool select_supported(int N_cap, int k) {
+  return N_cap > kLdsMaxRow && (N_cap + kSelBlock - 1) / kSelBlock <= kMaxBlk && k >= 1 && k <= kMaxK;
+}
+
+size_t select_workspace_bytes(long long rows, int N_cap) { return select_layout(rows, N_cap).total; }
+
+long long select_zero_words(long long rows) { return rows * kHistBins; }
+
+SelectWs select_ws_in(void* ws, long long rows, int N_cap) {
+  const SelectLayout L = select_layout(rows, N_cap);
+  char* p = static_cast<char*>(ws);
+  SelectWs w;
+  w.hist = reinterpret_cast<uint32_t*>(p + L.hist);
+  w.emit_cnt = reinterpret_cast<int32_t*>(p + L.emit_cnt);
+  w.emit = reinterpret_cast<uint2*>(p + L.emit);
+  w.cand_key = reinterpret_cast<uint32_t*>(p + L.cand_key);
+  w.cand_idx = reinterpret_cast<int32_t*>(p + L.cand_idx);
+  w.n_blk = (N_cap + kSelBlock - 1) / kSelBlock;
+  return w;
+}
+
+hipError_t launch_select_finish(int B, int n_q, int N_cap, const int32_t* q_pos, int m,
+                                const int32_t* n_entries, int k, int32_t* idx, const SelectWs& w,
+                                hipStream_t s) {
+  const long long rows = static_cast<long long>(B) * n_q;
+  if (rows == 0) return hipSuccess;
+  if (!select_supported(N_cap, k)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(select_finish_kernel, dim3(static_cast<unsigned>(rows)), dim3(kRowThreads), 0, s,
+                     N_cap, n_q, q_pos, m, n_entries, k, w, idx);
+  return hipGetLastError();
 }
 
 }  // namespace lca

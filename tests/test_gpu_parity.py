@@ -312,6 +312,44 @@ def test_csa_decode_1m_full_size_sampled():
     _decode_parity(cfg, d, [0, 7, 15])
 
 
+@pytest.mark.parametrize("case", ["constant_keys", "three_keys", "rows_shorter_than_k"])
+def test_csa_decode_selection_degenerate(case):
+    """Rows longer than the LDS top-k takes (the fused indexer selection): every
+    key equal (all scores tie: the first k entries), three distinct keys (ties
+    across the threshold: lowest indices first) and rows with fewer visible
+    entries than k (all of them, then -1)."""
+    if case == "rows_shorter_than_k":
+        cfg = CSA_DECODE_1M.with_(B=2, ctx=2048)
+        d = gen.decode_inputs(cfg, extra_entries=40000)
+    else:
+        cfg = CSA_DECODE_1M.with_(B=2, ctx=1 << 18)
+        d = gen.decode_inputs(cfg)
+        kI = d["kI"]
+        pick = np.zeros(kI.shape[1], np.int64) if case == "constant_keys" else np.arange(kI.shape[1]) % 3
+        d["kI"] = np.ascontiguousarray(kI[:, pick])
+    say(f"degenerate selection: {case}, N_cap {d['n_cap']}")
+    assert d["n_cap"] > 36864
+    layer = _decode_parity(cfg, d, range(cfg.B))
+    idx = host(layer.idx)
+    for b in range(cfg.B):
+        vis = int((d["n_tokens"][b] + 1) // d["m"])
+        if case == "constant_keys":
+            assert np.array_equal(idx[b], np.arange(cfg.k)), f"b{b}"
+        elif case == "rows_shorter_than_k":
+            assert vis < cfg.k
+            want = np.concatenate([np.arange(vis), np.full(cfg.k - vis, -1)])
+            assert np.array_equal(idx[b], want), f"b{b}"
+        else:
+            ref = OS.oracle_decode(cfg, d, b)
+            vals = np.unique(ref["scores"][:vis])
+            assert len(vals) == 3
+            kIb = O.decode(d["kI"][b, :3], cfg.idx_dtype)
+            qIb = O.decode(d["qI"][b], cfg.idx_dtype)
+            bnd = O.score_error_bound(qIb[None], kIb, d["w"][b][None].astype(np.float64))[0].max()
+            if np.diff(vals).min() > 2 * bnd:   # the three values rank the same in fp32
+                assert np.array_equal(idx[b], ref["idx"]), f"b{b}"
+
+
 def test_hca_decode_full_size():
     cfg = HCA_DECODE
     say("HCA decode B=32 131072")
