@@ -133,8 +133,9 @@ def _calibrate_copy(mib, dev):
 
 
 def _indexer_traffic():
-    """HBM bytes per fp8 indexer launch from the committed counter summary, if it
-    was taken with the current kernel source."""
+    """HBM bytes per launch of the fp8 indexer (the fused indexer + selection
+    kernel) from the committed counter summary, if it was taken with the current
+    kernel source."""
     import hashlib
     tfile = os.path.join(ROOT, "profiles", "indexer_fp8_decode_b16_1m_counters.txt")
     if not os.path.exists(tfile):
@@ -256,7 +257,8 @@ def run_decode(args, workload):
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS,
                 "traffic": _indexer_traffic() if workload == "csa_decode_1m" else None,
-                "kernel": f"indexer_mfma_kernel<{c0.idx_dtype}>"}
+                # rows of this length take the fused indexer + selection kernel
+                "kernel": f"indexer_select_kernel<{c0.idx_dtype}>"}
     else:
         # HCA only: dominant kernel is the attention over all visible entries + window
         c0, d0 = cfgs[0], ds[0]

@@ -187,6 +187,7 @@ __device__ __forceinline__ uint32_t score_bin(uint32_t key) { return key >> 20; 
 // different 128-byte lines (bin b -> line b % 32), so the few dozen bins a row's
 // scores fall in do not make one hot line for the atomics of many workgroups.
 __device__ __forceinline__ int hist_slot(int b) { return ((b & 31) << 7) | (b >> 5); }
+__device__ __forceinline__ int hist_bin_of_slot(int w) { return ((w & 127) << 5) | (w >> 7); }
 
 // Threshold of a row from its histogram in LDS (kScoreHistBins bins, bin
 // order == key order): the bin holding the want-th largest key and the count

@@ -229,7 +229,8 @@ __device__ void row_threshold(const uint32_t* gh, uint32_t* lh, int vis, int k, 
     __syncthreads();
     return;
   }
-  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) lh[i] = gh[hist_slot(i)];
+  // read in word order (coalesced), place by bin
+  for (int w = threadIdx.x; w < kHistBins; w += blockDim.x) lh[hist_bin_of_slot(w)] = gh[w];
   __syncthreads();
   find_threshold_block(lh, k, sh_bin, sh_above, scan_sh);
 }
@@ -558,7 +559,12 @@ constexpr int kEmitPerThread = kEmitLds / kRowThreads;  // 8
 __global__ __launch_bounds__(kRowThreads) void select_finish_kernel(
     int N_cap, int n_q, const int32_t* __restrict__ q_pos, int m, const int32_t* __restrict__ n_entries,
     int k, SelectWs ws, int32_t* __restrict__ idx) {
-  __shared__ int32_t S[kMaxK], Ch[kMaxK];
+  // S and Ch (the two sorted lists) first serve as the gather's block table
+  static_assert(2 * kMaxK >= kEmitLds, "block table fits in S and Ch");
+  __shared__ int32_t SCh[2 * kMaxK];
+  int32_t* S = SCh;
+  int32_t* Ch = SCh + kMaxK;
+  int32_t* blk_of = SCh;  // [E]: block of emitted entry p (gather only)
   __shared__ int seg_off[kMaxBlk + 1];
   __shared__ uint32_t ck[kEmitLds];
   __shared__ int32_t ci[kEmitLds];
@@ -578,8 +584,8 @@ __global__ __launch_bounds__(kRowThreads) void select_finish_kernel(
   const int q = (nb + kRowThreads - 1) / kRowThreads;  // blocks [t*q, t*q + q) of thread t
   uint32_t hv[kHistBins / kRowThreads];
 #pragma unroll
-  for (int u = 0; u < kHistBins / kRowThreads; ++u)
-    hv[u] = ws.hist[row * kHistBins + hist_slot(tid + u * kRowThreads)];
+  for (int u = 0; u < kHistBins / kRowThreads; ++u)  // word order (coalesced)
+    hv[u] = ws.hist[row * kHistBins + tid + u * kRowThreads];
   int cnt[kSegPerThread];
   int local = 0;
 #pragma unroll
@@ -589,7 +595,7 @@ __global__ __launch_bounds__(kRowThreads) void select_finish_kernel(
     local += cnt[u];
   }
 #pragma unroll
-  for (int u = 0; u < kHistBins / kRowThreads; ++u) lh[tid + u * kRowThreads] = hv[u];
+  for (int u = 0; u < kHistBins / kRowThreads; ++u) lh[hist_bin_of_slot(tid + u * kRowThreads)] = hv[u];
   if (tid == 0) {
     sh_bin = -1;
     sh_above = vis;
@@ -610,15 +616,23 @@ __global__ __launch_bounds__(kRowThreads) void select_finish_kernel(
   const int need = vis <= k ? 0 : k - sh_above;
   int nS = 0, nC = 0;
   if (E <= kEmitLds) {
+    // block table: every thread labels its own blocks' entries
+#pragma unroll
+    for (int u = 0; u < kSegPerThread; ++u) {
+      const int sgi = tid * q + u;
+      if (u < q && sgi < nb)
+        for (int p = seg_off[sgi]; p < seg_off[sgi + 1]; ++p) blk_of[p] = sgi;
+    }
+    __syncthreads();
     // gather: entry p = tid + 1024 u (neighbouring lanes read neighbouring slots
-    // of a block), one search and one 8-byte load each, all loads at once
+    // of a block), one 8-byte load each, all loads at once
     size_t off[kEmitPerThread];
 #pragma unroll
     for (int u = 0; u < kEmitPerThread; ++u) {
       const int p = tid + u * kRowThreads;
       off[u] = seg0 * kSelBlock;
       if (p < E) {
-        const int sgp = seg_of(seg_off, nb, p);
+        const int sgp = blk_of[p];
         off[u] = (seg0 + sgp) * kSelBlock + (p - seg_off[sgp]);
       }
     }
