@@ -229,6 +229,18 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
+// gfx950's transposing LDS read: within each 16-lane group, output lane i gets
+// element i%4 of the 8-byte chunks addressed by group lanes i/4 + 4j, j = 0..3.
+// With group lane s pointing at row r0 + s/4, dims d0 + 4 (s%4) of a row-major
+// tile, output lane i receives rows r0 .. r0+3 of dim d0 + i (checked by the
+// attention parity tests).
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 tr_rows4(const uint16_t* p) {
+  const v4s_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
 __device__ __forceinline__ v16f_t mfma_bf16(const v8bf_t& a, const v8bf_t& b, const v16f_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -353,6 +365,10 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     for (int dt = 0; dt < 4; ++dt) o[ht][dt] = v16f_t{0};
 
   const int sh = wv >> 1, sr = wv & 1;  // this wave's S tile
+  // transposing-read source of this lane: row (lane%16)/4, dims 16 (lane/16 % 2)
+  // + 4 (lane%4) within a 4-row x 32-dim block (see tr_rows4)
+  const int tr_r = (lane & 15) >> 2;
+  const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   __syncthreads();
   int cur = 0;
   for (int base = s_begin; base < s_end; base += kMT, cur ^= 1) {
@@ -450,14 +466,12 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
         A[ht] = as_v8bf(*reinterpret_cast<const uint4*>(&p_s[(32 * ht + j32) * kPS + 16 * ks + 8 * g]));
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const int dim = 128 * wv + 32 * dt + j32;
-        const uint16_t* vp = &kv_s[(16 * ks + 8 * g) * kQS + dim];
-        uint4 bv;
-        bv.x = static_cast<uint32_t>(vp[0]) | (static_cast<uint32_t>(vp[kQS]) << 16);
-        bv.y = static_cast<uint32_t>(vp[2 * kQS]) | (static_cast<uint32_t>(vp[3 * kQS]) << 16);
-        bv.z = static_cast<uint32_t>(vp[4 * kQS]) | (static_cast<uint32_t>(vp[5 * kQS]) << 16);
-        bv.w = static_cast<uint32_t>(vp[6 * kQS]) | (static_cast<uint32_t>(vp[7 * kQS]) << 16);
-        const v8bf_t Bv = as_v8bf(bv);
+        // B = V rows 16 ks + 8 g .. +8 of dim 128 wv + 32 dt + j32, read transposed
+        // from the row-major tile: two 4-row transposing reads (see tr_rows4)
+        const uint16_t* vp = &kv_s[(16 * ks + 8 * g + tr_r) * kQS + 128 * wv + 32 * dt + tr_d];
+        const uint2 lo = tr_rows4(vp);
+        const uint2 hi = tr_rows4(vp + 4 * kQS);
+        const v8bf_t Bv = as_v8bf(make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht) o[ht][dt] = mfma_bf16(A[ht], Bv, o[ht][dt]);
       }
