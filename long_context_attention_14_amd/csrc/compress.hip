@@ -180,7 +180,9 @@ __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
   load_row<CPL>(tokC + static_cast<size_t>(b) * io_row, io_fmt, c, lane, tc);
   load_row<CPL>(tokZ + static_cast<size_t>(b) * io_row, io_fmt, c, lane, tz);
   const int p = n_tokens[b];
-  if (p < 0) return;
+  if (p < 0) return;  // the same for every wave
+  // every wave has read the count before wave 0 advances it below
+  __syncthreads();
   const int blk = p / m;
   const int half = csa ? (blk & 1) : 0;
   const int row = half * m + p % m;
