@@ -22,13 +22,21 @@ CFLAGS = [
 ]
 
 
+# Per-source extra flags.  attention.hip: MFMA accumulators in VGPRs.  The
+# attention kernels rescale their O accumulators with VALU multiplies; with the
+# accumulators in AGPRs every rescale and every MFMA moves them between the
+# register files, and the decode kernel spills to scratch, whose reloads wait
+# for the KV rows in flight.
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -241,6 +241,23 @@ __device__ __forceinline__ uint2 tr_rows4(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// Loads through a global-address-space pointer.  Row pointers that went through
+// LDS or lane reads are generic to the compiler, which would emit flat loads;
+// those also count against the LDS wait counter, so every LDS wait would
+// wait for the KV rows in flight as well.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ldg16(const void* p) {
+  const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(1))) u32x4_t*>(
+      reinterpret_cast<uintptr_t>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ldg8(const void* p) {
+  const u32x2_t v = *reinterpret_cast<const __attribute__((address_space(1))) u32x2_t*>(
+      reinterpret_cast<uintptr_t>(p));
+  return make_uint2(v.x, v.y);
+}
+
 __device__ __forceinline__ v16f_t mfma_bf16(const v8bf_t& a, const v8bf_t& b, const v16f_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -294,13 +311,13 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
       raw[i] = make_uint4(0, 0, 0, 0);
       if (rp) {
         if (KVFMT == LCA_BF16) {
-          raw[i] = *reinterpret_cast<const uint4*>(rp + lane * 16);
+          raw[i] = ldg16(rp + lane * 16);
         } else if (lane < 56) {
-          const uint2 f = *reinterpret_cast<const uint2*>(rp + lane * 8);
+          const uint2 f = ldg8(rp + lane * 8);
           raw[i].x = f.x;
           raw[i].y = f.y;
         } else {
-          raw[i] = *reinterpret_cast<const uint4*>(rp + 448 + (lane - 56) * 16);
+          raw[i] = ldg16(rp + 448 + (lane - 56) * 16);
         }
       }
     }
@@ -543,6 +560,351 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode kernel (few query rows, bf16 queries, 64 heads x 512): one workgroup
+// per (query row, split) with all 64 heads; wave w covers heads 32 hg .. +32
+// (hg = w & 1) and dims 256 kh .. +256 (kh = w >> 1).
+//
+//  * The normalised query (the wave's heads and dims) stays in registers as the
+//    B operand of S^T = K Q^T (32x32x16 bf16 MFMA; lane: head 32 hg + l%32,
+//    dims 256 kh + 16 ks + 8 (l/32) .. +8 of k-step ks), so the scores read only
+//    K from LDS.  The two waves of a head half add their partial S^T (over the
+//    two dim halves) through LDS; each then holds all 64 rows of the tile, takes
+//    the maximum in registers, and writes P (bf16) of its own 32 rows to LDS.
+//  * PV: the wave accumulates O for its 32 heads and its 256 dims (V read
+//    transposed from the row-major tile).
+//  * The running maximum is raised only when a tile's maximum exceeds it by
+//    more than kLazyMax (natural-log units), so P stays below e^kLazyMax and O
+//    is rescaled only on those tiles (the normalised result is the same).
+//  * KV tiles are double-buffered in LDS.  Wave w loads the tile rows w + 4 i,
+//    i < 16, through row pointers held by lanes 0..15; the next tile's rows are
+//    in flight in registers during a tile's compute, and the row indices of
+//    the tile after it are loaded one tile ahead.  Empty rows (outside the
+//    split, past the visible entries, before the window start) are loaded from
+//    a valid row, staged as zeros and masked to -inf in S.  The partial S^T of
+//    a tile goes through the other KV buffer, which is free at that point.
+constexpr float kLazyMax = 8.0f;
+
+// Row of slot i when its index entry e has been loaded already (e unused for
+// window slots); nullptr when the slot is empty.
+__device__ __forceinline__ const uint8_t* slot_row_e(const SlotCtx& s, int i, int e) {
+  if (i < s.NS) {
+    const int lim = s.vis < s.N_cap ? s.vis : s.N_cap;
+    if (e < 0 || e >= lim) return nullptr;
+    return s.cache_b + static_cast<size_t>(e) * s.kv_row;
+  }
+  const int w = i - s.NS;
+  const long long j = static_cast<long long>(s.t) - s.n_win + 1 + w;
+  if (j < 0) return nullptr;
+  long long slot = (j - s.win_origin) % s.W_cap;
+  if (slot < 0) slot += s.W_cap;
+  return s.win_b + static_cast<size_t>(slot) * s.kv_row;
+}
+
+template <int KVFMT>
+__global__ __launch_bounds__(256) void attn_decode_kernel(
+    int n_q, const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int N_cap,
+    const int32_t* __restrict__ idx, int k, const int32_t* __restrict__ q_pos, int m,
+    const int32_t* __restrict__ n_entries, const uint8_t* __restrict__ win, int W_cap,
+    long long win_origin, int n_win, float tau, float eps, const float* __restrict__ sink,
+    int n_splits, int split_rows, uint8_t* __restrict__ out, int out_fmt, float* __restrict__ lse,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
+  __shared__ __attribute__((aligned(16))) uint16_t kv_s[2][kMT * kQS];
+  __shared__ __attribute__((aligned(16))) uint16_t p_s[kMH * kPS];
+  __shared__ float ps_s[2][kMH];
+  __shared__ __attribute__((aligned(16))) uint32_t vm_s[2][4];
+
+  const int split = blockIdx.x % n_splits;
+  const long long row = blockIdx.x / n_splits;
+  const int b = static_cast<int>(row / n_q);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hg = w & 1, kh = w >> 1;
+  const int j32 = lane & 31, g = lane >> 5;
+  const int head = 32 * hg + j32;  // the head of this lane's softmax state
+
+  // query fragments, issued before everything else
+  uint4 qf[kMC / 32];
+  {
+    const uint16_t* qh = q + (static_cast<size_t>(row) * kMH + head) * kMC + 256 * kh + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kMC / 32; ++ks) qf[ks] = *reinterpret_cast<const uint4*>(qh + 16 * ks);
+  }
+
+  SlotCtx sc;
+  sc.t = q_pos[row];
+  sc.vis = visible_entries(sc.t, m, n_entries[b], N_cap);
+  sc.idx = idx ? idx + row * k : nullptr;
+  sc.NS = idx ? k : N_cap;
+  sc.N_cap = N_cap;
+  sc.n_win = n_win;
+  sc.kv_row = row_bytes(KVFMT, kMC);
+  sc.cache_b = cache + static_cast<size_t>(b) * N_cap * sc.kv_row;
+  sc.win_b = win + static_cast<size_t>(b) * W_cap * sc.kv_row;
+  sc.W_cap = W_cap;
+  sc.win_origin = win_origin;
+  const int NT = sc.NS + n_win;
+  const int s_begin = split * split_rows;
+  const int s_end = min(s_begin + split_rows, NT);
+  const int n_tiles = (s_end - s_begin + kMT - 1) / kMT;
+
+  // lanes 0..15 (and their copies in the other lanes) hold tile row w + 4 (lane % 16)
+  const int my_r = w + 4 * (lane & 15);
+  auto entry = [&](int tile) -> int {  // index entry of my_r in a tile (clamped load)
+    const int i = s_begin + kMT * tile + my_r;
+    if (sc.idx) return sc.idx[min(i, sc.NS - 1)];
+    return i;
+  };
+  auto row_ptr = [&](int tile, int e, uint32_t& mask16) -> const uint8_t* {
+    const int i = s_begin + kMT * tile + my_r;
+    const uint8_t* p = i < s_end ? slot_row_e(sc, i, e) : nullptr;
+    mask16 = static_cast<uint32_t>(__ballot(p != nullptr)) & 0xffffu;
+    return p ? p : sc.cache_b;
+  };
+  const int lane_off = KVFMT == LCA_BF16 ? lane * 16 : (lane < 56 ? lane * 8 : 448 + (lane - 56) * 16);
+  uint4 raw[16];
+  auto load_rows = [&](const uint8_t* p) {
+    const uint64_t pv = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = static_cast<uint32_t>(pv), hi = static_cast<uint32_t>(pv >> 32);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint64_t pi =
+          (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(hi, i))) << 32) |
+          static_cast<uint32_t>(__builtin_amdgcn_readlane(lo, i));
+      raw[i] = ldg16(reinterpret_cast<const uint8_t*>(pi) + lane_off);
+    }
+  };
+  auto stage = [&](int buf, uint32_t mask16) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint4 v = raw[i];
+      if (KVFMT != LCA_BF16) {  // 8 OCP e4m3 dims -> bf16 (exact) for lanes < 56
+        const uint4 c = make_uint4(fp8x2_to_bf16x2<false>(raw[i].x), fp8x2_to_bf16x2<true>(raw[i].x),
+                                   fp8x2_to_bf16x2<false>(raw[i].y), fp8x2_to_bf16x2<true>(raw[i].y));
+        if (lane < 56) v = c;
+      }
+      if (!((mask16 >> i) & 1u)) v = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&kv_s[buf][(w + 4 * i) * kQS + lane * 8]) = v;
+    }
+    if (lane == 0) vm_s[buf][w] = mask16;
+  };
+
+  // first tile's row pointers -> its loads; the second tile's index entries
+  uint32_t mask_cur;
+  load_rows(row_ptr(0, entry(0), mask_cur));
+  int e_next = entry(1);
+
+  // RMSNorm of the query over its 512 dims: lane halves and the two waves of a
+  // head half hold a quarter each; the wave sums go through LDS
+  {
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kMC / 32; ++ks) {
+      const uint32_t w4[4] = {qf[ks].x, qf[ks].y, qf[ks].z, qf[ks].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = bf16_to_f32(static_cast<uint16_t>(w4[e] & 0xffffu));
+        const float c = bf16_to_f32(static_cast<uint16_t>(w4[e] >> 16));
+        ss = fmaf(a, a, ss);
+        ss = fmaf(c, c, ss);
+      }
+    }
+    ss += __shfl_xor(ss, 32, 64);
+    if (g == 0) ps_s[kh][head] = ss;
+    __syncthreads();
+    const float r = rsqrt_hw((ps_s[0][head] + ps_s[1][head]) / static_cast<float>(kMC) + eps);
+#pragma unroll
+    for (int ks = 0; ks < kMC / 32; ++ks) {
+      uint32_t w4[4] = {qf[ks].x, qf[ks].y, qf[ks].z, qf[ks].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w4[e] = pack_bf16(bf16_to_f32(static_cast<uint16_t>(w4[e] & 0xffffu)) * r,
+                          bf16_to_f32(static_cast<uint16_t>(w4[e] >> 16)) * r);
+      qf[ks] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;  // softmax state of `head`
+  v16f_t o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = v16f_t{0};
+  // transposing-read source of this lane: row (lane%16)/4, dims 16 (lane/16 % 2)
+  // + 4 (lane%4) within a 4-row x 32-dim block (see tr_rows4)
+  const int tr_r = (lane & 15) >> 2;
+  const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    stage(buf, mask_cur);
+    // the next tile's row pointers (entries loaded one tile ago) and the entries
+    // of the tile after it
+    uint32_t mask_next = 0;
+    const uint8_t* p_next = row_ptr(t + 1, e_next, mask_next);
+    e_next = entry(t + 2);
+    __syncthreads();  // B1: tile t staged (ps_s of the last tile read)
+    if (t + 1 < n_tiles) load_rows(p_next);  // in flight during this tile's compute
+    mask_cur = mask_next;
+
+    // partial S^T (this wave's dims) of its own rows 32 kh .. +32 (acc[0]) and
+    // of the other 32 rows (acc[1])
+    v16f_t acc[2];
+    {
+      acc[0] = v16f_t{0};
+      acc[1] = v16f_t{0};
+      const uint16_t* kb0 = &kv_s[buf][(32 * kh + j32) * kQS + 256 * kh + 8 * g];
+      const uint16_t* kb1 = &kv_s[buf][(32 * (kh ^ 1) + j32) * kQS + 256 * kh + 8 * g];
+#pragma unroll
+      for (int ks = 0; ks < kMC / 32; ++ks) {
+        const uint4 a0 = *reinterpret_cast<const uint4*>(kb0 + 16 * ks);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(kb1 + 16 * ks);
+        acc[0] = mfma_bf16(as_v8bf(a0), as_v8bf(qf[ks]), acc[0]);
+        acc[1] = mfma_bf16(as_v8bf(a1), as_v8bf(qf[ks]), acc[1]);
+      }
+    }
+    // exchange with the other dim half through the free KV buffer:
+    // sx[wave][16 blk + r][lane] (blk 0: the writer's own rows)
+    float* sx = reinterpret_cast<float*>(kv_s[buf ^ 1]);
+    {
+      float* sw = sx + w * 2048 + lane;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sw[r * 64] = acc[0][r];
+        sw[(16 + r) * 64] = acc[1][r];
+      }
+    }
+    __syncthreads();  // B2: partial scores
+    // full scores: own rows (the partner's other block) and the other rows (the
+    // partner's own block)
+    float so[16], st[16];
+    {
+      const float* pw = sx + (w ^ 2) * 2048 + lane;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        so[r] = (acc[0][r] + pw[(16 + r) * 64]) * tau;
+        st[r] = (acc[1][r] + pw[r * 64]) * tau;
+      }
+    }
+    {
+      // empty rows -> -inf.  Tile row 32 rb + 8 (r/4) + 4 g + r%4 was loaded by
+      // wave r%4 as its row number 8 rb + 2 (r/4) + g.
+      const uint4 vm = *reinterpret_cast<const uint4*>(vm_s[buf]);
+      if (((vm.x & vm.y & vm.z & vm.w) & 0xffffu) != 0xffffu) {
+        const uint32_t vmw[4] = {vm.x >> g, vm.y >> g, vm.z >> g, vm.w >> g};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int bo = 8 * kh + 2 * (r >> 2), bt = 8 * (kh ^ 1) + 2 * (r >> 2);
+          if (!((vmw[r & 3] >> bo) & 1u)) so[r] = -INFINITY;
+          if (!((vmw[r & 3] >> bt) & 1u)) st[r] = -INFINITY;
+        }
+      }
+    }
+    float tmax = so[0];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, fmaxf(so[r], st[r]));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = (m_run == -INFINITY || tmax > m_run + kLazyMax) ? tmax : m_run;
+    // O and l are zero while m_run is -inf, so no rescale is needed then
+    const float alpha = (m_run == -INFINITY || m_new == m_run) ? 1.f : __expf(m_run - m_new);
+    // every row of the head empty so far: m_new = -inf, and exp(-inf - 0) = 0
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    {
+      // P of this wave's rows 32 kh .. +32 (both waves of the head half hold all
+      // of S; each writes half of P)
+      float psum = 0.f;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        uint32_t pk[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float p0 = __expf(so[4 * q4 + 2 * u] - m_use);
+          const float p1 = __expf(so[4 * q4 + 2 * u + 1] - m_use);
+          pk[u] = pack_bf16(p0, p1);
+          psum += bf16_to_f32(static_cast<uint16_t>(pk[u] & 0xffffu)) +
+                  bf16_to_f32(static_cast<uint16_t>(pk[u] >> 16));
+        }
+        *reinterpret_cast<uint2*>(&p_s[head * kPS + 32 * kh + 8 * q4 + 4 * g]) = make_uint2(pk[0], pk[1]);
+      }
+      psum += __shfl_xor(psum, 32, 64);
+      if (g == 0) ps_s[kh][head] = psum;
+    }
+    __syncthreads();  // B3: P and the row-half sums
+    l_run = l_run * alpha + ps_s[0][head] + ps_s[1][head];
+    m_run = m_new;
+    // rescale O where the running maximum moved (rare after the first tiles)
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float al = __shfl(alpha, 8 * (r >> 2) + 4 * g + (r & 3), 64);
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[db][r] *= al;
+      }
+    }
+    // O[heads 32 hg + .., dims 256 kh + ..] += P V
+#pragma unroll
+    for (int ks = 0; ks < kMT / 16; ++ks) {
+      const v8bf_t A = as_v8bf(*reinterpret_cast<const uint4*>(&p_s[head * kPS + 16 * ks + 8 * g]));
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        // B = V rows 16 ks + 8 g .. +8 of dim 256 kh + 32 db + j32, read transposed
+        const uint16_t* vp = &kv_s[buf][(16 * ks + 8 * g + tr_r) * kQS + 256 * kh + 32 * db + tr_d];
+        const uint2 lo = tr_rows4(vp);
+        const uint2 hi = tr_rows4(vp + 4 * kQS);
+        o[db] = mfma_bf16(A, as_v8bf(make_uint4(lo.x, lo.y, hi.x, hi.y)), o[db]);
+      }
+    }
+  }
+
+  // epilogue: O / l (with the sink when this is the only split); lse = m + log l
+  float lse_v = l_run > 0.f ? m_run + __logf(l_run) : -INFINITY;
+  float f = l_run > 0.f ? 1.0f / l_run : 0.f;
+  if (n_splits == 1 && sink) {
+    const float sk = sink[head];
+    if (lse_v == -INFINITY) {
+      lse_v = sk;
+    } else {
+      const float mx = fmaxf(lse_v, sk);
+      const float tot = mx + __logf(__expf(lse_v - mx) + __expf(sk - mx));
+      f *= __expf(lse_v - tot);
+      lse_v = tot;
+    }
+  }
+  if (kh == 0 && g == 0) {
+    if (n_splits == 1) {
+      if (lse) lse[static_cast<size_t>(row) * kMH + head] = lse_v;
+    } else {
+      part_lse[(static_cast<size_t>(row) * n_splits + split) * kMH + head] = lse_v;
+    }
+  }
+  // O * f -> LDS as fp32 [64 heads][512] (over both KV buffers, once every wave
+  // is done with them), then contiguous 16-byte stores
+  float* ost = reinterpret_cast<float*>(&kv_s[0][0]);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int h = 32 * hg + 8 * (r >> 2) + 4 * g + (r & 3);
+    const float fr = __shfl(f, 8 * (r >> 2) + 4 * g + (r & 3), 64);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) ost[h * kMC + 256 * kh + 32 * db + j32] = o[db][r] * fr;
+  }
+  __syncthreads();
+  const size_t obase = n_splits == 1 ? static_cast<size_t>(row) * kMH * kMC
+                                     : (static_cast<size_t>(row) * n_splits + split) * kMH * kMC;
+  // 64 x 512 fp32 = 8192 chunks of 16 B; thread tid writes chunks tid + 256 i
+#pragma unroll 8
+  for (int i = 0; i < kMH * kMC / 4 / 256; ++i) {
+    const int c4 = (tid + 256 * i) * 4;
+    const float4 v = *reinterpret_cast<const float4*>(&ost[c4]);
+    if (n_splits > 1) {
+      *reinterpret_cast<float4*>(&part_o[obase + c4]) = v;
+    } else if (out_fmt == LCA_F32) {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + obase + c4) = v;
+    } else {
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + obase + c4) =
+          make_uint2(pack_bf16(v.x, v.y), pack_bf16(v.z, v.w));
+    }
+  }
+}
+
 // One wave per (query row, head): combine the splits in split order.  Lane s
 // reads split s's lse (wave-wide max and weights by shuffles), and every
 // split's partial row is loaded before the weighted sum.
@@ -612,7 +974,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
 
 struct Plan {
   int n_splits, split_rows;
-  bool mfma;
+  bool mfma;    // 64 heads x 512 on the MFMA kernels
+  bool decode;  // ... with the decode kernel (few rows, bf16 queries)
 };
 
 bool use_mfma(int H, int c, int q_fmt, int kv_fmt) {
@@ -625,6 +988,7 @@ Plan make_plan(long long rows, int H, int c, int q_fmt, int kv_fmt, int k, int N
   const int NT = (dense ? N_cap : k) + n_win;
   Plan p;
   p.mfma = use_mfma(H, c, q_fmt, kv_fmt);
+  p.decode = p.mfma && q_fmt == LCA_BF16 && rows < 512;
   if (rows >= 512) {
     p.n_splits = 1;
     p.split_rows = NT;
@@ -686,7 +1050,21 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
     part_o = static_cast<float*>(ws);
     part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + n * c * sizeof(float));
   }
-  if (p.mfma) {
+  if (p.decode) {
+    const dim3 grid(static_cast<unsigned>(rows * p.n_splits));
+    if (kv_fmt == LCA_BF16)
+      hipLaunchKernelGGL(attn_decode_kernel<LCA_BF16>, grid, dim3(256), 0, s, n_q,
+                         static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(cache),
+                         N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
+                         static_cast<long long>(win_origin), n_win, tau, eps, sink, p.n_splits,
+                         p.split_rows, static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
+    else
+      hipLaunchKernelGGL(attn_decode_kernel<LCA_KV_FP8_BF16ROPE>, grid, dim3(256), 0, s, n_q,
+                         static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(cache),
+                         N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
+                         static_cast<long long>(win_origin), n_win, tau, eps, sink, p.n_splits,
+                         p.split_rows, static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
+  } else if (p.mfma) {
     const dim3 grid(static_cast<unsigned>(rows * p.n_splits));
     if (kv_fmt == LCA_BF16)
       hipLaunchKernelGGL(attn_mfma_kernel<LCA_BF16>, grid, dim3(256), 0, s, n_q,

@@ -184,6 +184,103 @@ def test_rmsnorm_rows(io, kv):
 
 
 # ---------------------------------------------------------------------------
+# core attention alone at decode shapes: empty slots, ragged splits, window
+# positions before 0, a running maximum that moves on every tile
+
+
+def _as_bytes(enc_rows, fmt):
+    return np.ascontiguousarray(enc_rows).view(np.uint8)
+
+
+def _mqa_case(case, rng):
+    c, H, n_win, eps = 512, 64, 128, 1e-6
+    tau = 1.0 / np.sqrt(c)
+    kv = "fp8_bf16rope" if case.startswith("fp8") else "bf16"
+    if case == "rows300":                  # one split per row: the direct-output path
+        B, N_cap, k, m = 300, 256, 128, 4
+        q_pos = rng.integers(600, 2000, B)
+        n_entries = np.minimum((q_pos + 1) // m, N_cap)
+    elif case == "bf16_dense":             # HCA: every visible entry, many empty slots
+        B, N_cap, k, m = 2, 700, 0, 128
+        q_pos = np.array([300 * 128 + 5, 700 * 128 + 900])
+        n_entries = np.array([300, 700])
+    else:                                  # CSA: k = 200 selected, -1 padded
+        B, N_cap, k, m = 3, 5000, 200, 4
+        q_pos = np.array([5, 4000, 20000])
+        n_entries = np.array([2, 1000, 5000])
+    vis = np.minimum(np.minimum((q_pos + 1) // m, n_entries), N_cap)
+    cache_f = rng.standard_normal((B, N_cap, c))
+    win_f = rng.standard_normal((B, n_win, c))
+    q_f = rng.standard_normal((B, H, c))
+    if case == "rows300":
+        # rows aligned ever more with one query direction along the candidate
+        # list (selected entries 0..127, then the window oldest first): the
+        # logits climb by about 11 per 64-row tile, so the running maximum moves
+        # on every tile
+        u = rng.standard_normal(c)
+        u /= np.linalg.norm(u)
+        q_f = u[None, None, :] * np.sqrt(c) + 0.1 * rng.standard_normal((B, H, c))
+
+        def aligned(cosv, shape):
+            noise = rng.standard_normal(shape)
+            noise -= (noise @ u)[..., None] * u
+            noise /= np.linalg.norm(noise, axis=-1, keepdims=True)
+            return np.sqrt(c) * (cosv[..., None] * u + np.sqrt(1 - cosv ** 2)[..., None] * noise)
+
+        cache_f = aligned(np.broadcast_to(np.linspace(-1.0, 1.0, N_cap), (B, N_cap)), (B, N_cap, c))
+        age = (np.arange(n_win)[None, :] - (q_pos[:, None] - (n_win - 1))) % n_win   # slot -> window order
+        win_f = aligned(age / (n_win - 1.0), (B, n_win, c))
+    if k:
+        idx = np.full((B, k), -1, np.int32)
+        for b in range(B):
+            n = min(k, int(vis[b]))
+            idx[b, :n] = np.sort(rng.choice(int(vis[b]), n, replace=False)) if case != "rows300" \
+                else np.arange(n)
+    else:
+        idx = None
+    sink = rng.standard_normal(H).astype(np.float32) if case in ("fp8_sink", "rows300") else None
+    cache_e = enc.encode(cache_f, kv)
+    win_e = enc.encode(win_f, kv)
+    q_e = enc.to_bf16_bits(q_f)
+    return dict(B=B, N_cap=N_cap, k=k, m=m, q_pos=q_pos.astype(np.int32), n_entries=n_entries.astype(np.int32),
+                vis=vis, idx=idx, sink=sink, kv=kv, cache=cache_e, win=win_e, q=q_e, c=c, H=H,
+                n_win=n_win, tau=tau, eps=eps)
+
+
+@pytest.mark.parametrize("case", ["bf16_sparse", "fp8_sink", "bf16_dense", "rows300"])
+def test_sparse_mqa_decode_shapes(case):
+    rng = np.random.default_rng(7)
+    t = _mqa_case(case, rng)
+    B, H, c, kv = t["B"], t["H"], t["c"], t["kv"]
+    say(f"sparse MQA {case}: B={B} k={t['k']} N_cap={t['N_cap']}")
+    out = torch.zeros(B * H * c, dtype=torch.bfloat16, device=DEV)
+    lse = torch.zeros(B * H, dtype=torch.float32, device=DEV)
+    ops.lca_sparse_mqa(B, 1, H, c, T(t["q"]), "bf16", T(_as_bytes(t["cache"], kv)), kv, t["N_cap"],
+                       None if t["idx"] is None else T(t["idx"]), t["k"], T(t["q_pos"]), t["m"],
+                       T(t["n_entries"]), T(_as_bytes(t["win"], kv)), t["n_win"], 0, t["n_win"],
+                       t["tau"], t["eps"], None if t["sink"] is None else T(t["sink"]), out, "bf16",
+                       lse=lse)
+    got = out_f64(out).reshape(B, H, c)
+    got_lse = host(lse).reshape(B, H)
+    check = range(B) if B <= 8 else [0, 1, 2, 150, 298, 299]
+    for b in check:
+        tp = int(t["q_pos"][b])
+        if t["idx"] is None:
+            sel = np.arange(int(t["vis"][b]))
+        else:
+            sel = t["idx"][b][(t["idx"][b] >= 0) & (t["idx"][b] < t["vis"][b])]
+        wpos = O.window_positions(tp, t["n_win"])
+        rows = np.concatenate([O.decode(t["cache"][b, sel], kv).reshape(-1, c),
+                               O.decode(t["win"][b, wpos % t["n_win"]], kv).reshape(-1, c)])
+        qh = O.rmsnorm(O.decode(t["q"][b], "bf16"), t["eps"])
+        o_ref, lse_ref = O.merge([O.attend(qh, rows, t["tau"])], sink=t["sink"])
+        err = np.abs(got[b] - o_ref).max()
+        assert err <= OUT_TOL["bf16"], f"b{b}: out err {err:.3g}"
+        lerr = np.abs(got_lse[b] - lse_ref).max()
+        assert lerr <= LSE_TOL["bf16"], f"b{b}: lse err {lerr:.3g}"
+
+
+# ---------------------------------------------------------------------------
 # whole prefill layers
 
 
