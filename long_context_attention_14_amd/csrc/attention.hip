@@ -623,17 +623,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   const int j32 = lane & 31, g = lane >> 5;
   const int head = 32 * hg + j32;  // the head of this lane's softmax state
 
-  // query fragments, issued before everything else
-  uint4 qf[kMC / 32];
-  {
-    const uint16_t* qh = q + (static_cast<size_t>(row) * kMH + head) * kMC + 256 * kh + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < kMC / 32; ++ks) qf[ks] = *reinterpret_cast<const uint4*>(qh + 16 * ks);
-  }
-
   SlotCtx sc;
-  sc.t = q_pos[row];
-  sc.vis = visible_entries(sc.t, m, n_entries[b], N_cap);
   sc.idx = idx ? idx + row * k : nullptr;
   sc.NS = idx ? k : N_cap;
   sc.N_cap = N_cap;
@@ -689,10 +679,21 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     if (lane == 0) vm_s[buf][w] = mask16;
   };
 
-  // first tile's row pointers -> its loads; the second tile's index entries
-  uint32_t mask_cur;
-  load_rows(row_ptr(0, entry(0), mask_cur));
+  // issue order: the index entries of the first two tiles, the query fragments,
+  // then (once the entries are in) the first tile's rows.  Vector loads complete
+  // in order for the wait counter, so each wait covers only what it needs.
+  const int e_first = entry(0);
   int e_next = entry(1);
+  sc.t = q_pos[row];
+  sc.vis = visible_entries(sc.t, m, n_entries[b], N_cap);
+  uint4 qf[kMC / 32];
+  {
+    const uint16_t* qh = q + (static_cast<size_t>(row) * kMH + head) * kMC + 256 * kh + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kMC / 32; ++ks) qf[ks] = *reinterpret_cast<const uint4*>(qh + 16 * ks);
+  }
+  uint32_t mask_cur;
+  load_rows(row_ptr(0, e_first, mask_cur));
 
   // RMSNorm of the query over its 512 dims: lane halves and the two waves of a
   // head half hold a quarter each; the wave sums go through LDS
@@ -905,71 +906,75 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   }
 }
 
-// One wave per (query row, head): combine the splits in split order.  Lane s
-// reads split s's lse (wave-wide max and weights by shuffles), and every
-// split's partial row is loaded before the weighted sum.
+// Splits per query row are capped so that each split stays a few tiles long.
 constexpr int kMaxMergeSplits = 256;
 
-template <int CPL>
-__global__ __launch_bounds__(256) void attn_merge_kernel(
+// Split merge with one thread per 4 consecutive dims of a (query row, head).
+// The lse values and partial rows of up to kMergeChunk splits are loaded
+// together, so a merge of that many splits takes one memory round trip; more
+// splits go kMergeChunk at a time with a running maximum.  Splits are combined
+// in split order (deterministic).
+constexpr int kMergeChunk = 16;
+
+__global__ __launch_bounds__(256) void attn_merge4_kernel(
     long long rows, int H, int c, int n_splits, const float* __restrict__ part_o,
     const float* __restrict__ part_lse, const float* __restrict__ sink, uint8_t* __restrict__ out,
     int out_fmt, float* __restrict__ lse) {
-  const long long rh = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (rh >= rows * H) return;
-  const int lane = threadIdx.x & 63;
+  const int c4n = c / 4;
+  const long long gid = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (gid >= rows * H * c4n) return;
+  const long long rh = gid / c4n;
+  const int d4 = static_cast<int>(gid % c4n) * 4;
   const long long row = rh / H;
   const int h = static_cast<int>(rh % H);
-  // lane holds the lse of splits lane, lane + 64, ... (at most kMaxMergeSplits)
-  float my_lse[kMaxMergeSplits / 64];
-  float lmax = -INFINITY;
+  // the sink is one more logit in the denominator, with no value row
+  float m = sink ? sink[h] : -INFINITY;
+  float den = sink ? 1.f : 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < n_splits; s0 += kMergeChunk) {
+    float l[kMergeChunk];
+    float4 v[kMergeChunk];
 #pragma unroll
-  for (int u = 0; u < kMaxMergeSplits / 64; ++u) {
-    const int sp = lane + 64 * u;
-    my_lse[u] = sp < n_splits ? part_lse[(row * n_splits + sp) * H + h] : -INFINITY;
-    lmax = fmaxf(lmax, my_lse[u]);
-  }
-  float mx = fmaxf(wave_max(lmax), sink ? sink[h] : -INFINITY);
-  float acc[CPL];
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
-  float den = 0.f;
-  if (mx != -INFINITY) {
-    float my_w[kMaxMergeSplits / 64];
-#pragma unroll
-    for (int u = 0; u < kMaxMergeSplits / 64; ++u)
-      my_w[u] = my_lse[u] == -INFINITY ? 0.f : __expf(my_lse[u] - mx);
-    if (sink) den = __expf(sink[h] - mx);
-    for (int s0 = 0; s0 < n_splits; s0 += 8) {
-      float v[8][CPL];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (s0 + u < n_splits) {
-          load_row<CPL>(part_o + ((row * n_splits + s0 + u) * H + h) * c, LCA_F32, c, lane, v[u]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < CPL; ++i) v[u][i] = 0.f;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int sp = s0 + u < n_splits ? s0 + u : 0;
-        float wsel = my_w[0];
-#pragma unroll
-        for (int q = 1; q < kMaxMergeSplits / 64; ++q) wsel = (sp >> 6) == q ? my_w[q] : wsel;
-        const float wgt = __shfl(wsel, sp & 63, 64);
-        if (s0 + u >= n_splits) continue;
-        den += wgt;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) acc[i] = fmaf(wgt, v[u][i], acc[i]);
-      }
+    for (int u = 0; u < kMergeChunk; ++u) {
+      const int sp = min(s0 + u, n_splits - 1);
+      const size_t base = (static_cast<size_t>(row) * n_splits + sp) * H + h;
+      l[u] = part_lse[base];
+      v[u] = *reinterpret_cast<const float4*>(&part_o[base * c + d4]);
     }
+    float mc = m;
+#pragma unroll
+    for (int u = 0; u < kMergeChunk; ++u) {
+      if (s0 + u >= n_splits) l[u] = -INFINITY;
+      mc = fmaxf(mc, l[u]);
+    }
+    if (mc == -INFINITY) continue;  // no rows so far
+    const float sc = m == -INFINITY ? 0.f : __expf(m - mc);
+    den *= sc;
+    acc.x *= sc;
+    acc.y *= sc;
+    acc.z *= sc;
+    acc.w *= sc;
+#pragma unroll
+    for (int u = 0; u < kMergeChunk; ++u) {
+      const float wgt = l[u] == -INFINITY ? 0.f : __expf(l[u] - mc);
+      den += wgt;
+      acc.x = fmaf(wgt, v[u].x, acc.x);
+      acc.y = fmaf(wgt, v[u].y, acc.y);
+      acc.z = fmaf(wgt, v[u].z, acc.z);
+      acc.w = fmaf(wgt, v[u].w, acc.w);
+    }
+    m = mc;
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) acc[i] *= inv;
-  store_row<CPL>(out + rh * row_bytes(out_fmt, c), out_fmt, c, lane, acc);
-  if (lse && lane == 0) lse[rh] = den > 0.f ? mx + __logf(den) : -INFINITY;
+  const float4 o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  const size_t oi = static_cast<size_t>(rh) * c + d4;
+  if (out_fmt == LCA_F32) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + oi) = o;
+  } else {
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + oi) =
+        make_uint2(pack_bf16(o.x, o.y), pack_bf16(o.z, o.w));
+  }
+  if (lse && d4 == 0) lse[rh] = den > 0.f ? m + __logf(den) : -INFINITY;
 }
 
 struct Plan {
@@ -1088,9 +1093,9 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
-  const dim3 g2(static_cast<unsigned>((rows * H + 3) / 4));
-  LCA_ATTN_CPL(c, attn_merge_kernel, g2, dim3(256), rows, H, c, p.n_splits, part_o, part_lse, sink,
-               static_cast<uint8_t*>(out), out_fmt, lse);
+  const dim3 g2(static_cast<unsigned>((rows * H * (c / 4) + 255) / 256));
+  hipLaunchKernelGGL(attn_merge4_kernel, g2, dim3(256), 0, s, rows, H, c, p.n_splits, part_o,
+                     part_lse, sink, static_cast<uint8_t*>(out), out_fmt, lse);
   return hipGetLastError();
 }
 
