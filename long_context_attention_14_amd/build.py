@@ -27,7 +27,12 @@ CFLAGS = [
 # accumulators in AGPRs every rescale and every MFMA moves them between the
 # register files, and the decode kernel spills to scratch, whose reloads wait
 # for the KV rows in flight.
-EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# indexer.hip: no NaN-quieting before each ReLU.  max(x, 0) on an MFMA result
+# is otherwise two instructions (a canonicalising max, then the max); the
+# hardware max already returns 0 for a quiet NaN input, and MFMA results are
+# never signalling NaNs.  Score keys handle NaN on the bit pattern.
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "indexer.hip": ["-fno-honor-nans"]}
 
 
 def sources():

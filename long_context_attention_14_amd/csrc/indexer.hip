@@ -435,6 +435,127 @@ __global__ __launch_bounds__(kSelThreads, 1) void indexer_select_kernel(
   select_emit<kSelWaves>(lh, sc, n_t, wi, wpr, vis, row, sel, k, kmax);
 }
 
+// ---------------------------------------------------------------------------
+// Many query rows (prefill): kRowsPerWG consecutive query rows of one sequence
+// per workgroup, one per wave.  The rows' keys stream through LDS in 128-key
+// tiles (double-buffered, staged through registers), so a key leaves L2 once
+// per kRowsPerWG rows instead of once per row; each wave keeps its row's query
+// tiles in registers and runs every key group of a tile against them.  Several
+// waves per SIMD hide the MFMA -> ReLU/weights -> store chain of each wave.
+// LDS key rows are padded to 144 (fp8) / 80 (MXFP4) bytes so that the B-operand
+// reads of 8 consecutive keys hit distinct banks.
+constexpr int kRowsPerWG = 8;
+constexpr int kRowsThreads = kWave * kRowsPerWG;
+constexpr int kTileKeys = 128;
+
+template <bool MX>
+__global__ __launch_bounds__(kRowsThreads, 2) void indexer_rows_kernel(
+    const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qI_scale,
+    const uint8_t* __restrict__ kI, const uint8_t* __restrict__ kI_scale, int n_q, int N_cap,
+    int groups_per_seq, const float* __restrict__ w, const int32_t* __restrict__ q_pos, int m,
+    const int32_t* __restrict__ n_entries, float* __restrict__ scores) {
+  constexpr int kRowBytes = MX ? 64 : 128;
+  constexpr int kLdsRow = kRowBytes + 16;
+  constexpr int kChunks = kTileKeys * kRowBytes / 16;  // 16-byte chunks per tile
+  constexpr int kChunksPerThread = (kChunks + kRowsThreads - 1) / kRowsThreads;
+  __shared__ __attribute__((aligned(16))) uint8_t kt[2][kTileKeys * kLdsRow];
+  __shared__ uint32_t kts[2][MX ? kTileKeys : 1];
+  __shared__ __attribute__((aligned(16))) float w_s[kRowsPerWG][64];
+  __shared__ int vis_s[kRowsPerWG];
+  const int b = blockIdx.x / groups_per_seq;
+  const int r0 = (blockIdx.x % groups_per_seq) * kRowsPerWG;  // first row within the sequence
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 31, g = lane >> 5;
+  const long long row_base = static_cast<long long>(b) * n_q;
+  if (tid < kRowsPerWG) {
+    const int r = r0 + tid;
+    vis_s[tid] = r < n_q ? visible_entries(q_pos[row_base + r], m, n_entries[b], N_cap) : 0;
+  }
+  for (int i = tid; i < kRowsPerWG * 64; i += kRowsThreads) {
+    const int r = r0 + i / 64;
+    w_s[i / 64][i % 64] = r < n_q ? w[(row_base + r) * 64 + i % 64] : 0.f;
+  }
+  // the wave's row (a row past n_q computes on the last row and stores nothing)
+  v8i A[2][2];
+  int sA[2][2];
+  load_query<MX>(qI, qI_scale, row_base + min(r0 + wave, n_q - 1), j, g, A, sA);
+  __syncthreads();
+  int vis_max = 0;
+#pragma unroll
+  for (int u = 0; u < kRowsPerWG; ++u) vis_max = max(vis_max, vis_s[u]);
+  const int vis = vis_s[wave];
+  const int n_tiles = (vis_max + kTileKeys - 1) / kTileKeys;
+  if (n_tiles == 0) return;
+  const uint8_t* kb_base = kI + static_cast<size_t>(b) * N_cap * kRowBytes;
+  const uint8_t* ks_base = MX ? kI_scale + static_cast<size_t>(b) * N_cap * 4 : nullptr;
+  float* out = scores + static_cast<size_t>(row_base + r0 + wave) * N_cap;
+
+  // tile staging: chunk c = tid + 512 i is bytes 16 (c % (kRowBytes/16)) of key
+  // c / (kRowBytes/16); keys past vis_max load the last visible key
+  uint4 st[kChunksPerThread];
+  uint32_t sts = 0;
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < kChunksPerThread; ++i) {
+      const int c = min(tid + kRowsThreads * i, kChunks - 1);
+      const int key = min(t * kTileKeys + c / (kRowBytes / 16), vis_max - 1);
+      st[i] = *reinterpret_cast<const uint4*>(kb_base + static_cast<size_t>(key) * kRowBytes +
+                                              16 * (c % (kRowBytes / 16)));
+    }
+    if (MX) {
+      const int key = min(t * kTileKeys + (tid & (kTileKeys - 1)), vis_max - 1);
+      sts = *reinterpret_cast<const uint32_t*>(ks_base + static_cast<size_t>(key) * 4);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kChunksPerThread; ++i) {
+      const int c = tid + kRowsThreads * i;
+      if (c < kChunks)
+        *reinterpret_cast<uint4*>(&kt[buf][(c / (kRowBytes / 16)) * kLdsRow + 16 * (c % (kRowBytes / 16))]) = st[i];
+    }
+    if (MX && tid < kTileKeys) kts[buf][tid] = sts;
+  };
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  // Tile t+1 goes into the other buffer while tile t is computed: that buffer
+  // held tile t-1, which every wave finished before the barrier ending step t-1.
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) load_tile(t + 1);  // in flight during this tile
+#pragma unroll
+    for (int grp = 0; grp < kTileKeys / kKeysPerGroup; ++grp) {
+      const int kl = kKeysPerGroup * grp + j;  // key within the tile
+      const uint8_t* kp = &kt[buf][kl * kLdsRow];
+      KeyGroup<MX> G;
+      if (MX) {
+        const uint32_t sc = kts[buf][kl];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int blk = 2 * g + ks;
+          G.b[ks] = load16(kp + 16 * blk);
+          G.sb[ks] = (sc >> (8 * blk)) & 0xff;
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          G.b[ks] = load32(kp + 64 * g + 32 * ks);
+          G.sb[ks] = 127;
+        }
+      }
+      const float sv = group_score<MX>(A, sA, G, w_s[wave], g);
+      const int key = t * kTileKeys + kl;
+      if (g == 0 && key < vis) out[key] = sv;
+    }
+    if (t + 1 < n_tiles) {
+      store_tile(buf ^ 1);
+      __syncthreads();
+    }
+  }
+}
+
 // Scalar fp32 path for small shapes: one thread per (query, entry).
 constexpr int kF32Threads = 256;
 
@@ -538,6 +659,22 @@ hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const v
     if (mx) go(indexer_select_kernel<true>);
     else go(indexer_select_kernel<false>);
     return e != hipSuccess ? e : hipGetLastError();
+  }
+  if (!hist && n_q >= kRowsPerWG * 8) {
+    // many rows per sequence: row groups share each key tile through LDS
+    const int gps = (n_q + kRowsPerWG - 1) / kRowsPerWG;
+    const dim3 grid(static_cast<unsigned>(static_cast<long long>(B) * gps)), block(kRowsThreads);
+    auto go = [&](auto kern) {
+      if (ev_start || ev_stop)
+        hipExtLaunchKernelGGL(kern, grid, block, 0, s, ev_start, ev_stop, 0, q8, qI_scale, k8,
+                              kI_scale, n_q, N_cap, gps, w, q_pos, m, n_entries, scores);
+      else
+        hipLaunchKernelGGL(kern, grid, block, 0, s, q8, qI_scale, k8, kI_scale, n_q, N_cap, gps, w,
+                           q_pos, m, n_entries, scores);
+    };
+    if (mx) go(indexer_rows_kernel<true>);
+    else go(indexer_rows_kernel<false>);
+    return hipGetLastError();
   }
   long long wpr = (kTargetBlocks + rows - 1) / rows;
   wpr = wpr < 1 ? 1 : (wpr > max_blocks ? max_blocks : wpr);

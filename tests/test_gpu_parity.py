@@ -128,6 +128,44 @@ def test_indexer_scores_within_bound(fmt, HI, dI):
             assert np.all(got[b, t, vis:] == 12345.0), "entries past vis were written"
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_indexer_scores_many_rows(fmt):
+    """Many query rows per sequence (the row-group kernel): 75 rows (a ragged last
+    group of 8), 2000 entries (a ragged last tile), visible lengths from 0 to all
+    entries mixed within each group."""
+    say(f"indexer {fmt} many rows")
+    rng = np.random.default_rng(11)
+    B, n_q, N, m, HI, dI = 2, 75, 2000, 4, 64, 128
+    qf = rng.standard_normal((B, n_q, HI, dI))
+    kf = rng.standard_normal((B, N, dI))
+    w = rng.random((B, n_q, HI)).astype(np.float32)
+    if fmt == "mxfp4":
+        qb, qs = enc.to_mxfp4(qf)
+        kb, ks = enc.to_mxfp4(kf)
+        qd, kd = O.decode_mxfp4(qb, qs), O.decode_mxfp4(kb, ks)
+        qs_t, ks_t = T(qs), T(ks)
+    else:
+        qb, kb = enc.encode(qf, fmt), enc.encode(kf, fmt)
+        qd, kd = O.decode(qb, fmt), O.decode(kb, fmt)
+        qs_t = ks_t = None
+    pos = rng.integers(-1, 4 * N + 40, (B, n_q)).astype(np.int32)
+    pos[0, :8] = np.arange(8) * 3          # the first group: tiny visible lengths
+    n_ent = np.array([N, N - 17], np.int32)
+    scores = torch.full((B, n_q, N), 12345.0, dtype=torch.float32, device=DEV)
+    ops.lca_indexer_scores(B, n_q, HI, dI, fmt, T(qb), qs_t, T(kb), ks_t, N, T(w), T(pos), m,
+                           T(n_ent), scores)
+    got = host(scores)
+    for b in range(B):
+        for t in range(n_q):
+            vis = int(O.visible([pos[b, t]], m, n_ent[b])[0])
+            if vis:
+                ref = O.index_scores(qd[b, t][None], kd[b, :vis], w[b, t][None].astype(np.float64), [vis])[0]
+                bnd = O.score_error_bound(qd[b, t][None], kd[b, :vis], w[b, t][None].astype(np.float64))[0]
+                err = np.abs(got[b, t, :vis] - ref)
+                assert np.all(err <= bnd + 1e-30), f"b{b} t{t}: err {err.max():.3g}"
+            assert np.all(got[b, t, vis:] == 12345.0), f"b{b} t{t}: entries past vis were written"
+
+
 # ---------------------------------------------------------------------------
 # compressor and window KV
 
