@@ -121,37 +121,57 @@ __device__ __forceinline__ void load_query(const uint8_t* qI, const uint8_t* qI_
   }
 }
 
-// Score of key column j of a 32-key group (valid in every lane; lanes j and j+32
-// agree): the 64 heads' ReLU'd dot products weighted by w_s and summed.  Register
-// r of accumulator tile ht is head 32*ht + 8*(r/4) + 4*g + (r%4), so four
-// consecutive registers read one float4 of the weights.
+// x of lane l plus x of lane l ^ 32, with gfx950's lane-half swap (a VALU op:
+// lanes 32..63 of the first operand trade places with lanes 0..31 of the
+// second, so the two results hold the pair's values in either order).
+__device__ __forceinline__ float lane_pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(static_cast<uint32_t>(r[0])) + __uint_as_float(static_cast<uint32_t>(r[1]));
+}
+
+// A 32-key group against the query's 64 heads: accumulator tile ht holds heads
+// 32*ht + 8*(r/4) + 4*g + (r%4) in register r, key column j.
+struct GroupAcc {
+  v16f a[2];
+};
+
+template <bool MX>
+__device__ __forceinline__ GroupAcc group_mma(const v8i (&A)[2][2], const int (&sA)[2][2],
+                                              const KeyGroup<MX>& cur) {
+  constexpr int kFmt = MX ? 4 : 0;
+  GroupAcc r;
+  r.a[0] = v16f{0};
+  r.a[1] = v16f{0};
+  r.a[0] = mfma<kFmt>(A[0][0], cur.b[0], r.a[0], sA[0][0], cur.sb[0]);
+  r.a[1] = mfma<kFmt>(A[1][0], cur.b[0], r.a[1], sA[1][0], cur.sb[0]);
+  r.a[0] = mfma<kFmt>(A[0][1], cur.b[1], r.a[0], sA[0][1], cur.sb[1]);
+  r.a[1] = mfma<kFmt>(A[1][1], cur.b[1], r.a[1], sA[1][1], cur.sb[1]);
+  return r;
+}
+
+// Score of key column j (valid in every lane; lanes j and j+32 agree): the 64
+// heads' ReLU'd dot products weighted by w_s and summed, in four independent
+// partial sums; four consecutive registers read one float4 of the weights.
+__device__ __forceinline__ float group_reduce(const GroupAcc& acc, const float* w_s, int g) {
+  float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const float4 w4 = *reinterpret_cast<const float4*>(&w_s[32 * ht + 8 * a + 4 * g]);
+      p[0] = fmaf(w4.x, fmaxf(acc.a[ht][4 * a], 0.f), p[0]);
+      p[1] = fmaf(w4.y, fmaxf(acc.a[ht][4 * a + 1], 0.f), p[1]);
+      p[2] = fmaf(w4.z, fmaxf(acc.a[ht][4 * a + 2], 0.f), p[2]);
+      p[3] = fmaf(w4.w, fmaxf(acc.a[ht][4 * a + 3], 0.f), p[3]);
+    }
+  }
+  return lane_pair_sum((p[0] + p[1]) + (p[2] + p[3]));
+}
+
 template <bool MX>
 __device__ __forceinline__ float group_score(const v8i (&A)[2][2], const int (&sA)[2][2],
                                              const KeyGroup<MX>& cur, const float* w_s, int g) {
-  constexpr int kFmt = MX ? 4 : 0;
-  v16f acc0 = {0}, acc1 = {0};
-  acc0 = mfma<kFmt>(A[0][0], cur.b[0], acc0, sA[0][0], cur.sb[0]);
-  acc0 = mfma<kFmt>(A[0][1], cur.b[1], acc0, sA[0][1], cur.sb[1]);
-  acc1 = mfma<kFmt>(A[1][0], cur.b[0], acc1, sA[1][0], cur.sb[0]);
-  acc1 = mfma<kFmt>(A[1][1], cur.b[1], acc1, sA[1][1], cur.sb[1]);
-  float s = 0.f;
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const float4 w4 = *reinterpret_cast<const float4*>(&w_s[8 * a + 4 * g]);
-    s += w4.x * fmaxf(acc0[4 * a], 0.f);
-    s += w4.y * fmaxf(acc0[4 * a + 1], 0.f);
-    s += w4.z * fmaxf(acc0[4 * a + 2], 0.f);
-    s += w4.w * fmaxf(acc0[4 * a + 3], 0.f);
-  }
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const float4 w4 = *reinterpret_cast<const float4*>(&w_s[32 + 8 * a + 4 * g]);
-    s += w4.x * fmaxf(acc1[4 * a], 0.f);
-    s += w4.y * fmaxf(acc1[4 * a + 1], 0.f);
-    s += w4.z * fmaxf(acc1[4 * a + 2], 0.f);
-    s += w4.w * fmaxf(acc1[4 * a + 3], 0.f);
-  }
-  return s + __shfl_xor(s, 32, kWave);
+  return group_reduce(group_mma<MX>(A, sA, cur), w_s, g);
 }
 
 // Scores of every visible key, written to scores[row]; HIST: also add their
@@ -525,8 +545,7 @@ __global__ __launch_bounds__(kRowsThreads, 2) void indexer_rows_kernel(
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
     if (t + 1 < n_tiles) load_tile(t + 1);  // in flight during this tile
-#pragma unroll
-    for (int grp = 0; grp < kTileKeys / kKeysPerGroup; ++grp) {
+    auto lds_group = [&](int grp) {
       const int kl = kKeysPerGroup * grp + j;  // key within the tile
       const uint8_t* kp = &kt[buf][kl * kLdsRow];
       KeyGroup<MX> G;
@@ -545,8 +564,17 @@ __global__ __launch_bounds__(kRowsThreads, 2) void indexer_rows_kernel(
           G.sb[ks] = 127;
         }
       }
-      const float sv = group_score<MX>(A, sA, G, w_s[wave], g);
-      const int key = t * kTileKeys + kl;
+      return G;
+    };
+    // the next group's MFMAs are issued before this group's reduction
+    constexpr int kGroups = kTileKeys / kKeysPerGroup;
+    GroupAcc acc[kGroups];
+    acc[0] = group_mma<MX>(A, sA, lds_group(0));
+#pragma unroll
+    for (int grp = 0; grp < kGroups; ++grp) {
+      if (grp + 1 < kGroups) acc[grp + 1] = group_mma<MX>(A, sA, lds_group(grp + 1));
+      const float sv = group_reduce(acc[grp], w_s[wave], g);
+      const int key = t * kTileKeys + kKeysPerGroup * grp + j;
       if (g == 0 && key < vis) out[key] = sv;
     }
     if (t + 1 < n_tiles) {
