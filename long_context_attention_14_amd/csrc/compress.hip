@@ -63,11 +63,15 @@ __device__ __forceinline__ void load_bias(const float* P, int slot, int c, int l
   load_row<CPL>(P + static_cast<size_t>(slot) * c, LCA_F32, c, lane, pv);
 }
 
-template <int CPL>
+// IOF: the candidates' format (F32 or BF16) as a compile-time constant, so that
+// row loads carry no format branches (a load under a branch makes the compiler
+// wait for it at the branch's end, which serialises the candidate loads).
+template <int CPL, int IOF>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void compress_kernel(
-    int csa, int m, int B, int n_new, int c, const uint8_t* C, const uint8_t* Z, int io_fmt,
+    int csa, int m, int B, int n_new, int c, const uint8_t* C, const uint8_t* Z,
     const uint8_t* prevC, const uint8_t* prevZ, const float* P, uint8_t* cache, int kv_fmt,
     int N_cap, int first_entry, float eps) {
+  constexpr int io_fmt = IOF;
   const int lane = threadIdx.x & (kWave - 1);
   const int n_ent = n_new / m;
   const long long e = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
@@ -147,12 +151,13 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void rmsnorm_rows_kernel(
 // used from registers.  As a side job the workgroups clear zero_buf.
 constexpr int kAppendWaves = 8;
 
-template <int CPL>
+template <int CPL, int IOF>
 __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
-    int csa, int m, int B, int c, int n_win, const uint8_t* tokC, const uint8_t* tokZ, int io_fmt,
+    int csa, int m, int B, int c, int n_win, const uint8_t* tokC, const uint8_t* tokZ,
     uint8_t* tailC, uint8_t* tailZ, uint8_t* ring, int kv_fmt, const float* P, uint8_t* cache,
     int N_cap, int32_t* n_tokens, int32_t* q_pos, int32_t* n_entries, float eps,
     uint32_t* zero_buf, long long zero_words) {
+  constexpr int io_fmt = IOF;  // compile-time: no format branches around the row loads
   __shared__ float part[kAppendWaves][3][CPL][kWave];  // lane-contiguous: no bank conflicts
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x >> 6;
@@ -233,7 +238,7 @@ __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
         add_row(wv, rc, rz, own ? sp1 : sp0);
       }
     }
-  } else {
+  } else if (CPL > 8) {
     for (int r = wv; r < T_cap; r += kAppendWaves) {
       const bool own = !csa || (r / m) == half;
       if (!own && s == 0) continue;
@@ -251,6 +256,35 @@ __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
       float bias[CPL];
       load_bias<CPL>(P, slot, c, lane, bias);
       add_row(r, cv, pv, bias);
+    }
+  } else {
+    // rows r = wv + kAppendWaves * i, kAppendBatch of them loaded before any is
+    // pooled, so a long HCA tail pays one memory latency per batch
+    constexpr int kAppendBatch = 4;
+    for (int r0 = wv; r0 < T_cap; r0 += kAppendWaves * kAppendBatch) {
+      float bc[kAppendBatch][CPL], bz[kAppendBatch][CPL], bb[kAppendBatch][CPL];
+      bool use[kAppendBatch];
+      // unconditional loads (rows past the tail read row 0 and are not used): a
+      // load under a branch would be waited for at the branch's end
+#pragma unroll
+      for (int u = 0; u < kAppendBatch; ++u) {
+        const int r = r0 + kAppendWaves * u;
+        const int rl = r < T_cap ? r : 0;
+        const bool own = !csa || (rl / m) == half;
+        use[u] = r < T_cap && (own || s > 0);
+        const int slot = csa ? (own ? m + rl % m : rl % m) : rl;
+        load_row<CPL>(tCb + rl * io_row, io_fmt, c, lane, bc[u]);
+        load_row<CPL>(tZb + rl * io_row, io_fmt, c, lane, bz[u]);
+        load_bias<CPL>(P, slot, c, lane, bb[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kAppendBatch; ++u) {
+        const int r = r0 + kAppendWaves * u;
+        if (!use[u]) continue;  // the same for the whole wave
+        // the new token's row may not have reached memory yet: take it from registers
+        if (r == row) add_row(r, tc, tz, bb[u]);
+        else add_row(r, bc[u], bz[u], bb[u]);
+      }
     }
   }
 #pragma unroll
@@ -306,10 +340,25 @@ hipError_t launch_compress(int mode, int m, int B, int n_new, int c, const void*
   const long long n = static_cast<long long>(B) * (n_new / m);
   if (n == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((n + kWavesPerBlock - 1) / kWavesPerBlock));
-  LCA_DISPATCH_CPL(c, compress_kernel, grid, mode == LCA_CSA ? 1 : 0, m, B, n_new, c,
-                   static_cast<const uint8_t*>(C), static_cast<const uint8_t*>(Z), io_fmt,
-                   static_cast<const uint8_t*>(prevC), static_cast<const uint8_t*>(prevZ), P,
-                   static_cast<uint8_t*>(cache), kv_fmt, N_cap, first_entry, eps);
+  const int csa = mode == LCA_CSA ? 1 : 0;
+  const uint8_t* Cp = static_cast<const uint8_t*>(C);
+  const uint8_t* Zp = static_cast<const uint8_t*>(Z);
+  const uint8_t* pC = static_cast<const uint8_t*>(prevC);
+  const uint8_t* pZ = static_cast<const uint8_t*>(prevZ);
+  uint8_t* ch = static_cast<uint8_t*>(cache);
+  const dim3 block(kWave * kWavesPerBlock);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, s, csa, m, B, n_new, c, Cp, Zp, pC, pZ, P, ch, kv_fmt,
+                       N_cap, first_entry, eps);
+  };
+  const bool f32 = io_fmt == LCA_F32;
+  switch (c / kWave) {
+    case 2: f32 ? go(compress_kernel<2, LCA_F32>) : go(compress_kernel<2, LCA_BF16>); break;
+    case 4: f32 ? go(compress_kernel<4, LCA_F32>) : go(compress_kernel<4, LCA_BF16>); break;
+    case 8: f32 ? go(compress_kernel<8, LCA_F32>) : go(compress_kernel<8, LCA_BF16>); break;
+    case 16: f32 ? go(compress_kernel<16, LCA_F32>) : go(compress_kernel<16, LCA_BF16>); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -337,11 +386,16 @@ hipError_t launch_state_append(int mode, int m, int B, int c, int n_win, const v
   uint8_t* tZ = static_cast<uint8_t*>(tailZ);
   uint8_t* rg = static_cast<uint8_t*>(ring);
   uint8_t* ch = static_cast<uint8_t*>(cache);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, s, csa, m, B, c, n_win, tc, tz, tC, tZ, rg, kv_fmt, P,
+                       ch, N_cap, n_tokens, q_pos, n_entries, eps, zero_buf, zero_words);
+  };
+  const bool f32 = io_fmt == LCA_F32;
   switch (c / kWave) {
-    case 2: hipLaunchKernelGGL(state_append_kernel<2>, grid, block, 0, s, csa, m, B, c, n_win, tc, tz, io_fmt, tC, tZ, rg, kv_fmt, P, ch, N_cap, n_tokens, q_pos, n_entries, eps, zero_buf, zero_words); break;
-    case 4: hipLaunchKernelGGL(state_append_kernel<4>, grid, block, 0, s, csa, m, B, c, n_win, tc, tz, io_fmt, tC, tZ, rg, kv_fmt, P, ch, N_cap, n_tokens, q_pos, n_entries, eps, zero_buf, zero_words); break;
-    case 8: hipLaunchKernelGGL(state_append_kernel<8>, grid, block, 0, s, csa, m, B, c, n_win, tc, tz, io_fmt, tC, tZ, rg, kv_fmt, P, ch, N_cap, n_tokens, q_pos, n_entries, eps, zero_buf, zero_words); break;
-    case 16: hipLaunchKernelGGL(state_append_kernel<16>, grid, block, 0, s, csa, m, B, c, n_win, tc, tz, io_fmt, tC, tZ, rg, kv_fmt, P, ch, N_cap, n_tokens, q_pos, n_entries, eps, zero_buf, zero_words); break;
+    case 2: f32 ? go(state_append_kernel<2, LCA_F32>) : go(state_append_kernel<2, LCA_BF16>); break;
+    case 4: f32 ? go(state_append_kernel<4, LCA_F32>) : go(state_append_kernel<4, LCA_BF16>); break;
+    case 8: f32 ? go(state_append_kernel<8, LCA_F32>) : go(state_append_kernel<8, LCA_BF16>); break;
+    case 16: f32 ? go(state_append_kernel<16, LCA_F32>) : go(state_append_kernel<16, LCA_BF16>); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
