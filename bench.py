@@ -351,12 +351,45 @@ def run_prefill(args):
                    "global_batch": 1, "seq_len": cfg.ctx + cfg.n_new, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / FP8_PEAK_TFLOPS, "traffic": None,
-                     "kernel": "indexer_mfma_kernel<fp8>"},
+                     "kernel": "indexer_rows_kernel<fp8>"},
         "stages_us": {k: v * 1e6 for k, v in per.items()},
+        "bf16_selector": bf16_selector(layer, args.steps),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_prefill(cfg, d, args.cpu_seconds)
     return result, per
+
+
+def bf16_selector(layer, steps):
+    """The pages' BF16-score variant of the indexer + top-k on the same chunk:
+    its stage times, and the share of the float32 selection (layer.idx, from the
+    timed runs) that it keeps; context, not a parity claim (each selection is
+    exact for its own scores)."""
+    import numpy as np
+    import torch
+
+    layer.indexer_bf16()
+    layer.topk_bf16()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        layer.indexer_bf16()
+        e[1].record()
+        layer.topk_bf16()
+        e[2].record()
+    torch.cuda.synchronize()
+    a = layer.idx.reshape(-1, layer.idx.shape[-1]).long()
+    b = layer.idx16.reshape(-1, layer.idx16.shape[-1]).long()
+    big = 1 << 40
+    a_s = torch.where(a < 0, torch.full_like(a, big), a)
+    pos = torch.searchsorted(a_s, torch.where(b < 0, torch.full_like(b, big + 1), b)).clamp(max=a.shape[1] - 1)
+    hit = (torch.gather(a_s, 1, pos) == b) & (b >= 0)
+    recall = float(hit.sum().item() / max(1, int((a >= 0).sum().item())))
+    rows_equal = float((a == b).all(dim=1).float().mean().item())
+    return {"indexer_us": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3,
+            "topk_us": float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3,
+            "recall_vs_f32": recall, "rows_identical": rows_equal}
 
 
 def main():

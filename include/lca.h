@@ -183,6 +183,27 @@ int lca_topk(int B, int n_q, int N_cap, const float* scores, const int32_t* q_po
              size_t workspace_bytes, lca_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * The BF16-score selector ("DeepSeek V4 Architecture Tricks", section "FP4 /
+ * FP8 Quantization-Aware Training": index scores kept in BF16 make the top-k
+ * selector about twice as fast).
+ * lca_indexer_scores_bf16 -- as lca_indexer_scores, but each visible score is
+ *   stored as bf16: the round-to-nearest-even of the float32 score that
+ *   lca_indexer_scores writes for the same inputs.  scores [B, n_q, N_cap] bf16.
+ * lca_topk_bf16 -- as lca_topk over bf16 scores [B, n_q, N_cap]: the min(k, vis)
+ *   largest bf16 values, equal values lower index first (-0 counts as +0, NaN
+ *   as -inf), ascending, -1 padded; workspace lca_topk_workspace_size(...).
+ * The selection of a bf16 row can differ from the float32 selection only among
+ * scores that round to the same bf16 value.
+ * ------------------------------------------------------------------------- */
+int lca_indexer_scores_bf16(int B, int n_q, int H_I, int d_I, int idx_dtype, const void* qI,
+                            const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale,
+                            int N_cap, const float* w, const int32_t* q_pos, int m,
+                            const int32_t* n_entries, uint16_t* scores, lca_stream_t stream);
+int lca_topk_bf16(int B, int n_q, int N_cap, const uint16_t* scores, const int32_t* q_pos, int m,
+                  const int32_t* n_entries, int k, int32_t* idx, void* workspace,
+                  size_t workspace_bytes, lca_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * lca_sparse_mqa -- core attention of CSA (over idx) or HCA (idx == NULL: all
  * visible entries) plus the sliding-window branch, merged into one softmax
  * (QbitAI article, hybrid attention section: MQA over the selected compressed

@@ -44,8 +44,11 @@ SIGNATURES = {
     "lca_rmsnorm_rows": (c_int, [c_int, c_int, c_int, P, c_int, P, c_int, c_int, c_float, P]),
     "lca_indexer_scores": (c_int, [c_int, c_int, c_int, c_int, c_int, P, P, P, P, c_int, P, P,
                                    c_int, P, P, P]),
+    "lca_indexer_scores_bf16": (c_int, [c_int, c_int, c_int, c_int, c_int, P, P, P, P, c_int, P, P,
+                                        c_int, P, P, P]),
     "lca_topk_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int]),
     "lca_topk": (c_int, [c_int, c_int, c_int, P, P, c_int, P, c_int, P, P, c_size_t, P]),
+    "lca_topk_bf16": (c_int, [c_int, c_int, c_int, P, P, c_int, P, c_int, P, P, c_size_t, P]),
     "lca_sparse_mqa_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                                  c_int, c_int]),
     "lca_sparse_mqa": (c_int, [c_int, c_int, c_int, c_int, P, c_int, P, c_int, c_int, P, c_int, P,

@@ -103,10 +103,11 @@ int lca_rmsnorm_rows(int B, int n, int c, const void* x, int x_dtype, void* y, i
                     "lca_rmsnorm_rows");
 }
 
-int lca_indexer_scores(int B, int n_q, int H_I, int d_I, int idx_dtype, const void* qI,
-                       const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale, int N_cap,
-                       const float* w, const int32_t* q_pos, int m, const int32_t* n_entries,
-                       float* scores, lca_stream_t stream) {
+static int indexer_scores(int B, int n_q, int H_I, int d_I, int idx_dtype, const void* qI,
+                          const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale,
+                          int N_cap, const float* w, const int32_t* q_pos, int m,
+                          const int32_t* n_entries, void* scores, int score_fmt,
+                          lca_stream_t stream, const char* name) {
   g_last_error.clear();
   REQUIRE(B >= 0 && n_q >= 0 && N_cap >= 0, "negative sizes");
   REQUIRE(m >= 1, "m = %d < 1", m);
@@ -124,8 +125,25 @@ int lca_indexer_scores(int B, int n_q, int H_I, int d_I, int idx_dtype, const vo
   REQUIRE(qI && kI && w && q_pos && n_entries && scores, "NULL tensor pointer");
   return hip_status(lca::launch_indexer(B, n_q, H_I, d_I, idx_dtype, qI, qI_scale, kI, kI_scale,
                                         N_cap, w, q_pos, m, n_entries, scores,
-                                        reinterpret_cast<hipStream_t>(stream)),
-                    "lca_indexer_scores");
+                                        reinterpret_cast<hipStream_t>(stream), nullptr, nullptr,
+                                        nullptr, nullptr, 0, score_fmt),
+                    name);
+}
+
+int lca_indexer_scores(int B, int n_q, int H_I, int d_I, int idx_dtype, const void* qI,
+                       const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale, int N_cap,
+                       const float* w, const int32_t* q_pos, int m, const int32_t* n_entries,
+                       float* scores, lca_stream_t stream) {
+  return indexer_scores(B, n_q, H_I, d_I, idx_dtype, qI, qI_scale, kI, kI_scale, N_cap, w, q_pos, m,
+                        n_entries, scores, LCA_F32, stream, "lca_indexer_scores");
+}
+
+int lca_indexer_scores_bf16(int B, int n_q, int H_I, int d_I, int idx_dtype, const void* qI,
+                            const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale,
+                            int N_cap, const float* w, const int32_t* q_pos, int m,
+                            const int32_t* n_entries, uint16_t* scores, lca_stream_t stream) {
+  return indexer_scores(B, n_q, H_I, d_I, idx_dtype, qI, qI_scale, kI, kI_scale, N_cap, w, q_pos, m,
+                        n_entries, scores, LCA_BF16, stream, "lca_indexer_scores_bf16");
 }
 
 size_t lca_topk_workspace_size(int B, int n_q, int N_cap, int k) {
@@ -133,9 +151,9 @@ size_t lca_topk_workspace_size(int B, int n_q, int N_cap, int k) {
   return lca::topk_workspace_bytes(B, n_q, N_cap, k);
 }
 
-int lca_topk(int B, int n_q, int N_cap, const float* scores, const int32_t* q_pos, int m,
-             const int32_t* n_entries, int k, int32_t* idx, void* workspace, size_t workspace_bytes,
-             lca_stream_t stream) {
+static int topk(int B, int n_q, int N_cap, const void* scores, int score_fmt, const int32_t* q_pos,
+                int m, const int32_t* n_entries, int k, int32_t* idx, void* workspace,
+                size_t workspace_bytes, lca_stream_t stream, const char* name) {
   g_last_error.clear();
   REQUIRE(B >= 0 && n_q >= 0 && N_cap >= 0, "negative sizes");
   REQUIRE(k >= 1 && k <= 4096, "k = %d out of range [1, 4096]", k);
@@ -143,13 +161,27 @@ int lca_topk(int B, int n_q, int N_cap, const float* scores, const int32_t* q_po
   SUPPORT(N_cap <= (1 << 23), "N_cap = %d too large", N_cap);
   const size_t need = lca::topk_workspace_bytes(B, n_q, N_cap, k);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(LCA_ERR_WORKSPACE, "lca_topk needs %zu workspace bytes, got %zu", need,
+    return fail(LCA_ERR_WORKSPACE, "%s needs %zu workspace bytes, got %zu", name, need,
                 workspace ? workspace_bytes : 0);
   if (B == 0 || n_q == 0) return LCA_OK;
   REQUIRE(scores && q_pos && n_entries && idx, "NULL tensor pointer");
   return hip_status(lca::launch_topk(B, n_q, N_cap, scores, q_pos, m, n_entries, k, idx, workspace,
-                                     reinterpret_cast<hipStream_t>(stream)),
-                    "lca_topk");
+                                     reinterpret_cast<hipStream_t>(stream), score_fmt),
+                    name);
+}
+
+int lca_topk(int B, int n_q, int N_cap, const float* scores, const int32_t* q_pos, int m,
+             const int32_t* n_entries, int k, int32_t* idx, void* workspace, size_t workspace_bytes,
+             lca_stream_t stream) {
+  return topk(B, n_q, N_cap, scores, LCA_F32, q_pos, m, n_entries, k, idx, workspace,
+              workspace_bytes, stream, "lca_topk");
+}
+
+int lca_topk_bf16(int B, int n_q, int N_cap, const uint16_t* scores, const int32_t* q_pos, int m,
+                  const int32_t* n_entries, int k, int32_t* idx, void* workspace,
+                  size_t workspace_bytes, lca_stream_t stream) {
+  return topk(B, n_q, N_cap, scores, LCA_BF16, q_pos, m, n_entries, k, idx, workspace,
+              workspace_bytes, stream, "lca_topk_bf16");
 }
 
 size_t lca_sparse_mqa_workspace_size(int B, int n_q, int H, int c, int kv_dtype, int k, int N_cap,

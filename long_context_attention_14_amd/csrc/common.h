@@ -181,6 +181,21 @@ __device__ __forceinline__ uint32_t score_key(float x) {
   if (u == 0x80000000u) u = 0u;                          // -0 -> +0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+// A score as stored: fp32, or bf16 (round to nearest even of the fp32 score).
+// The key of a bf16 score keeps only its top 16 bits (the key of the bf16
+// value), so equal bf16 values have equal keys.
+__device__ __forceinline__ void store_score(float* p, float s) { *p = s; }
+__device__ __forceinline__ void store_score(uint16_t* p, float s) { *p = f32_to_bf16(s); }
+__device__ __forceinline__ uint32_t stored_key(float s) { return score_key(s); }
+__device__ __forceinline__ uint32_t stored_key(uint16_t h) {
+  return score_key(bf16_to_f32(h)) & 0xffff0000u;
+}
+// key of a computed score once stored as ST
+template <typename ST>
+__device__ __forceinline__ uint32_t key_as_stored(float s) {
+  if constexpr (sizeof(ST) == 2) return stored_key(f32_to_bf16(s));
+  else return score_key(s);
+}
 constexpr int kScoreHistBins = 4096;
 __device__ __forceinline__ uint32_t score_bin(uint32_t key) { return key >> 20; }
 // Word of bin b in a row's histogram in global memory: neighbouring bins sit in
@@ -271,12 +286,15 @@ hipError_t launch_select_finish(int B, int n_q, int N_cap, const int32_t* q_pos,
 hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const void* qI,
                           const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale,
                           int N_cap, const float* w, const int32_t* q_pos, int m,
-                          const int32_t* n_entries, float* scores, hipStream_t s,
+                          const int32_t* n_entries, void* scores, hipStream_t s,
                           uint32_t* hist = nullptr, hipEvent_t ev_start = nullptr,
-                          hipEvent_t ev_stop = nullptr, const SelectWs* sel = nullptr, int k = 0);
+                          hipEvent_t ev_stop = nullptr, const SelectWs* sel = nullptr, int k = 0,
+                          int score_fmt = LCA_F32);
 size_t topk_workspace_bytes(int B, int n_q, int N_cap, int k);
-hipError_t launch_topk(int B, int n_q, int N_cap, const float* scores, const int32_t* q_pos, int m,
-                       const int32_t* n_entries, int k, int32_t* idx, void* ws, hipStream_t s);
+// scores: [B*n_q, N_cap] float32, or bf16 bits when score_fmt == LCA_BF16
+hipError_t launch_topk(int B, int n_q, int N_cap, const void* scores, const int32_t* q_pos, int m,
+                       const int32_t* n_entries, int k, int32_t* idx, void* ws, hipStream_t s,
+                       int score_fmt = LCA_F32);
 // For rows longer than the LDS path takes: the row histogram inside the top-k
 // workspace (nullptr when the LDS path applies; its zero region is
 // topk_hist_words(rows) words), and the selection from a histogram that the

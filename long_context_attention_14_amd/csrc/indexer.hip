@@ -178,12 +178,12 @@ __device__ __forceinline__ float group_score(const v8i (&A)[2][2], const int (&s
 // score_bin histogram into hist[row] (global, zeroed by the caller) through a
 // per-workgroup LDS histogram.  Workgroup wi of a row takes the row's 128-key
 // blocks wi, wi + wpr, ...; wave w the 32 keys at offset 32w of each.
-template <bool MX, bool HIST>
+template <bool MX, bool HIST, typename ST>
 __global__ __launch_bounds__(kWave * kIdxWaves, 3) void indexer_mfma_kernel(
     const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qI_scale,
     const uint8_t* __restrict__ kI, const uint8_t* __restrict__ kI_scale, int n_q, int N_cap,
     int wpr, const float* __restrict__ w, const int32_t* __restrict__ q_pos, int m,
-    const int32_t* __restrict__ n_entries, float* __restrict__ scores,
+    const int32_t* __restrict__ n_entries, ST* __restrict__ scores,
     uint32_t* __restrict__ hist) {
   constexpr int kRowBytes = MX ? 64 : 128;  // bytes of one 128-dim vector
   __shared__ uint32_t lh[HIST ? kScoreHistBins : 1];
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kWave * kIdxWaves, 3) void indexer_mfma_kernel(
   if (threadIdx.x < 64) w_s[threadIdx.x] = w[static_cast<size_t>(row) * 64 + threadIdx.x];
   const uint8_t* kb_base = kI + static_cast<size_t>(b) * N_cap * kRowBytes;
   const uint8_t* ks_base = MX ? kI_scale + static_cast<size_t>(b) * N_cap * 4 : nullptr;
-  float* out = scores + static_cast<size_t>(row) * N_cap;
+  ST* out = scores + static_cast<size_t>(row) * N_cap;
   __syncthreads();
 
   // Every wave runs all n_t steps (a group past the end loads a clamped key and
@@ -223,8 +223,8 @@ __global__ __launch_bounds__(kWave * kIdxWaves, 3) void indexer_mfma_kernel(
     const float s = group_score<MX>(A, sA, cur, w_s, g);
     const int kb = key0(t);
     if (g == 0 && kb + j < vis) {
-      out[kb + j] = s;
-      if (HIST) atomicAdd(&lh[score_bin(score_key(s))], 1u);
+      store_score(&out[kb + j], s);
+      if (HIST) atomicAdd(&lh[score_bin(key_as_stored<ST>(s))], 1u);
     }
   };
   // Three named buffers, unrolled by three: a load always fills the buffer whose
@@ -468,12 +468,12 @@ constexpr int kRowsPerWG = 8;
 constexpr int kRowsThreads = kWave * kRowsPerWG;
 constexpr int kTileKeys = 128;
 
-template <bool MX>
+template <bool MX, typename ST>
 __global__ __launch_bounds__(kRowsThreads, 2) void indexer_rows_kernel(
     const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qI_scale,
     const uint8_t* __restrict__ kI, const uint8_t* __restrict__ kI_scale, int n_q, int N_cap,
     int groups_per_seq, const float* __restrict__ w, const int32_t* __restrict__ q_pos, int m,
-    const int32_t* __restrict__ n_entries, float* __restrict__ scores) {
+    const int32_t* __restrict__ n_entries, ST* __restrict__ scores) {
   constexpr int kRowBytes = MX ? 64 : 128;
   constexpr int kLdsRow = kRowBytes + 16;
   constexpr int kChunks = kTileKeys * kRowBytes / 16;  // 16-byte chunks per tile
@@ -509,7 +509,7 @@ __global__ __launch_bounds__(kRowsThreads, 2) void indexer_rows_kernel(
   if (n_tiles == 0) return;
   const uint8_t* kb_base = kI + static_cast<size_t>(b) * N_cap * kRowBytes;
   const uint8_t* ks_base = MX ? kI_scale + static_cast<size_t>(b) * N_cap * 4 : nullptr;
-  float* out = scores + static_cast<size_t>(row_base + r0 + wave) * N_cap;
+  ST* out = scores + static_cast<size_t>(row_base + r0 + wave) * N_cap;
 
   // tile staging: chunk c = tid + 512 i is bytes 16 (c % (kRowBytes/16)) of key
   // c / (kRowBytes/16); keys past vis_max load the last visible key
@@ -575,7 +575,7 @@ __global__ __launch_bounds__(kRowsThreads, 2) void indexer_rows_kernel(
       if (grp + 1 < kGroups) acc[grp + 1] = group_mma<MX>(A, sA, lds_group(grp + 1));
       const float sv = group_reduce(acc[grp], w_s[wave], g);
       const int key = t * kTileKeys + kKeysPerGroup * grp + j;
-      if (g == 0 && key < vis) out[key] = sv;
+      if (g == 0 && key < vis) store_score(&out[key], sv);
     }
     if (t + 1 < n_tiles) {
       store_tile(buf ^ 1);
@@ -587,10 +587,11 @@ __global__ __launch_bounds__(kRowsThreads, 2) void indexer_rows_kernel(
 // Scalar fp32 path for small shapes: one thread per (query, entry).
 constexpr int kF32Threads = 256;
 
+template <typename ST>
 __global__ __launch_bounds__(kF32Threads) void indexer_f32_kernel(
     const float* __restrict__ qI, const float* __restrict__ kI, int n_q, int H_I, int d_I,
     int N_cap, int n_chunks, const float* __restrict__ w, const int32_t* __restrict__ q_pos, int m,
-    const int32_t* __restrict__ n_entries, float* __restrict__ scores) {
+    const int32_t* __restrict__ n_entries, ST* __restrict__ scores) {
   extern __shared__ float sm[];  // [H_I * d_I] query, then [H_I] weights
   const long long row = blockIdx.x / n_chunks;
   const int chunk = blockIdx.x % n_chunks;
@@ -612,7 +613,7 @@ __global__ __launch_bounds__(kF32Threads) void indexer_f32_kernel(
     for (int i = 0; i < d_I; ++i) d = fmaf(qp[i], kp[i], d);
     acc = fmaf(sm[HD + h], fmaxf(d, 0.f), acc);
   }
-  scores[static_cast<size_t>(row) * N_cap + s] = acc;
+  store_score(&scores[static_cast<size_t>(row) * N_cap + s], acc);
 }
 
 }  // namespace
@@ -633,24 +634,32 @@ static int device_cus() {
 hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const void* qI,
                           const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale,
                           int N_cap, const float* w, const int32_t* q_pos, int m,
-                          const int32_t* n_entries, float* scores, hipStream_t s,
+                          const int32_t* n_entries, void* scores, hipStream_t s,
                           uint32_t* hist, hipEvent_t ev_start, hipEvent_t ev_stop,
-                          const SelectWs* sel, int k) {
+                          const SelectWs* sel, int k, int score_fmt) {
   const long long rows = static_cast<long long>(B) * n_q;
   if (rows == 0 || N_cap == 0) return hipSuccess;
+  if (score_fmt != LCA_F32 && score_fmt != LCA_BF16) return hipErrorInvalidValue;
+  const bool sbf = score_fmt == LCA_BF16;
+  float* sf = static_cast<float*>(scores);
+  uint16_t* sb = static_cast<uint16_t*>(scores);
   if (idx_fmt == LCA_F32) {
     if (sel) return hipErrorInvalidValue;  // the selecting kernel is MFMA-only
     const int n_chunks = (N_cap + kF32Threads - 1) / kF32Threads;
     const size_t lds = sizeof(float) * (static_cast<size_t>(H_I) * d_I + H_I);
     const dim3 g(static_cast<unsigned>(rows * n_chunks));
-    if (ev_start || ev_stop)
-      hipExtLaunchKernelGGL(indexer_f32_kernel, g, dim3(kF32Threads), lds, s, ev_start, ev_stop, 0,
-                            static_cast<const float*>(qI), static_cast<const float*>(kI), n_q, H_I,
-                            d_I, N_cap, n_chunks, w, q_pos, m, n_entries, scores);
-    else
-      hipLaunchKernelGGL(indexer_f32_kernel, g, dim3(kF32Threads), lds, s,
-                         static_cast<const float*>(qI), static_cast<const float*>(kI), n_q, H_I, d_I,
-                         N_cap, n_chunks, w, q_pos, m, n_entries, scores);
+    auto go = [&](auto kern, auto* out) {
+      if (ev_start || ev_stop)
+        hipExtLaunchKernelGGL(kern, g, dim3(kF32Threads), lds, s, ev_start, ev_stop, 0,
+                              static_cast<const float*>(qI), static_cast<const float*>(kI), n_q, H_I,
+                              d_I, N_cap, n_chunks, w, q_pos, m, n_entries, out);
+      else
+        hipLaunchKernelGGL(kern, g, dim3(kF32Threads), lds, s, static_cast<const float*>(qI),
+                           static_cast<const float*>(kI), n_q, H_I, d_I, N_cap, n_chunks, w, q_pos,
+                           m, n_entries, out);
+    };
+    if (sbf) go(indexer_f32_kernel<uint16_t>, sb);
+    else go(indexer_f32_kernel<float>, sf);
     return hipGetLastError();
   }
   const long long max_blocks = (N_cap + kBlockKeys - 1) / kBlockKeys;
@@ -692,16 +701,16 @@ hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const v
     // many rows per sequence: row groups share each key tile through LDS
     const int gps = (n_q + kRowsPerWG - 1) / kRowsPerWG;
     const dim3 grid(static_cast<unsigned>(static_cast<long long>(B) * gps)), block(kRowsThreads);
-    auto go = [&](auto kern) {
+    auto go = [&](auto kern, auto* out) {
       if (ev_start || ev_stop)
         hipExtLaunchKernelGGL(kern, grid, block, 0, s, ev_start, ev_stop, 0, q8, qI_scale, k8,
-                              kI_scale, n_q, N_cap, gps, w, q_pos, m, n_entries, scores);
+                              kI_scale, n_q, N_cap, gps, w, q_pos, m, n_entries, out);
       else
         hipLaunchKernelGGL(kern, grid, block, 0, s, q8, qI_scale, k8, kI_scale, n_q, N_cap, gps, w,
-                           q_pos, m, n_entries, scores);
+                           q_pos, m, n_entries, out);
     };
-    if (mx) go(indexer_rows_kernel<true>);
-    else go(indexer_rows_kernel<false>);
+    if (mx) sbf ? go(indexer_rows_kernel<true, uint16_t>, sb) : go(indexer_rows_kernel<true, float>, sf);
+    else sbf ? go(indexer_rows_kernel<false, uint16_t>, sb) : go(indexer_rows_kernel<false, float>, sf);
     return hipGetLastError();
   }
   long long wpr = (kTargetBlocks + rows - 1) / rows;
@@ -710,20 +719,30 @@ hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const v
   const int n_chunks = static_cast<int>(wpr);
   const dim3 block(kWave * kIdxWaves);
   // start/stop events, when given, are stamped by the dispatch itself
-  auto go = [&](auto kern) {
+  auto go = [&](auto kern, auto* out) {
     if (ev_start || ev_stop)
       hipExtLaunchKernelGGL(kern, grid, block, 0, s, ev_start, ev_stop, 0, q8, qI_scale, k8,
-                            kI_scale, n_q, N_cap, n_chunks, w, q_pos, m, n_entries, scores, hist);
+                            kI_scale, n_q, N_cap, n_chunks, w, q_pos, m, n_entries, out, hist);
     else
       hipLaunchKernelGGL(kern, grid, block, 0, s, q8, qI_scale, k8, kI_scale, n_q, N_cap, n_chunks,
-                         w, q_pos, m, n_entries, scores, hist);
+                         w, q_pos, m, n_entries, out, hist);
   };
-  if (!mx) {
-    if (hist) go(indexer_mfma_kernel<false, true>);
-    else go(indexer_mfma_kernel<false, false>);
+  if (sbf) {
+    if (!mx) {
+      if (hist) go(indexer_mfma_kernel<false, true, uint16_t>, sb);
+      else go(indexer_mfma_kernel<false, false, uint16_t>, sb);
+    } else {
+      if (hist) go(indexer_mfma_kernel<true, true, uint16_t>, sb);
+      else go(indexer_mfma_kernel<true, false, uint16_t>, sb);
+    }
   } else {
-    if (hist) go(indexer_mfma_kernel<true, true>);
-    else go(indexer_mfma_kernel<true, false>);
+    if (!mx) {
+      if (hist) go(indexer_mfma_kernel<false, true, float>, sf);
+      else go(indexer_mfma_kernel<false, false, float>, sf);
+    } else {
+      if (hist) go(indexer_mfma_kernel<true, true, float>, sf);
+      else go(indexer_mfma_kernel<true, false, float>, sf);
+    }
   }
   return hipGetLastError();
 }

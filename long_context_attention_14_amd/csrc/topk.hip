@@ -70,33 +70,102 @@ __device__ void find_bin_wave(const uint32_t* hist, int nbins, int want, int* ou
 // ---------------------------------------------------------------------------
 // LDS path
 
+// Block-wide exclusive prefix of two per-thread counts (kRowThreads threads);
+// also returns the totals.  scan_a/scan_b hold kRowThreads/64 ints each.
+__device__ __forceinline__ void block_scan2(int a, int b, int* ea, int* eb, int* ta, int* tb,
+                                            int* scan_a, int* scan_b) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int ia = a, ib = b;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int va = __shfl_up(ia, o, 64), vb = __shfl_up(ib, o, 64);
+    if (lane >= o) {
+      ia += va;
+      ib += vb;
+    }
+  }
+  if (lane == 63) {
+    scan_a[wv] = ia;
+    scan_b[wv] = ib;
+  }
+  __syncthreads();
+  int oa = ia - a, ob = ib - b, sa = 0, sb = 0;
+  for (int x = 0; x < kRowThreads / 64; ++x) {
+    if (x < wv) {
+      oa += scan_a[x];
+      ob += scan_b[x];
+    }
+    sa += scan_a[x];
+    sb += scan_b[x];
+  }
+  *ea = oa;
+  *eb = ob;
+  *ta = sa;
+  *tb = sb;
+}
+
+
+// ST: float, or uint16_t for bf16 scores (16-bit keys: two 8-bit passes).
+// One workgroup per row, the row's keys in LDS.  The radix histograms have
+// kHistCopies copies (lane l adds to copy l % kHistCopies, copies 257 words
+// apart so that a bin's copies sit in different banks): the top key bits of a
+// row of scores take very few distinct values, and LDS atomics to one address
+// within an instruction are serialised.  The index-order compaction counts
+// every round's selected entries per wave first, so one block scan gives all
+// output offsets (no barrier per 1024 entries).
+constexpr int kHistCopies = 8;
+constexpr int kHistStride = 257;
+constexpr int kMaxRounds = (kLdsMaxRow + kRowThreads - 1) / kRowThreads;  // 36
+constexpr int kRowWaves = kRowThreads / 64;
+
+template <typename ST>
 __global__ __launch_bounds__(kRowThreads) void topk_lds_kernel(
-    const float* __restrict__ scores, int N_cap, int n_q, const int32_t* __restrict__ q_pos, int m,
+    const ST* __restrict__ scores, int N_cap, int n_q, const int32_t* __restrict__ q_pos, int m,
     const int32_t* __restrict__ n_entries, int k, int32_t* __restrict__ idx) {
   extern __shared__ uint32_t keys[];
+  __shared__ uint32_t hc[kHistCopies * kHistStride];
   __shared__ uint32_t hist[256];
   __shared__ int sh_bin, sh_above;
-  __shared__ uint32_t wgt[kRowThreads / 64], weq[kRowThreads / 64];
+  __shared__ int cg[kMaxRounds * kRowWaves], ce[kMaxRounds * kRowWaves];
+  __shared__ int scan_a[kRowWaves], scan_b[kRowWaves];
   const long long row = blockIdx.x;
   const int b = static_cast<int>(row / n_q);
   const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
   int32_t* out = idx + row * k;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   if (vis <= k) {
     for (int i = tid; i < k; i += kRowThreads) out[i] = i < vis ? i : -1;
     return;
   }
-  const float* src = scores + row * N_cap;
-  for (int i = tid; i < vis; i += kRowThreads) keys[i] = score_key(src[i]);
-
+  // keys to LDS, eight loads in flight per thread (clamped addresses, unconditional)
+  const ST* src = scores + row * N_cap;
+  for (int base = 0; base < vis; base += 8 * kRowThreads) {
+    ST v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[min(base + u * kRowThreads + tid, vis - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * kRowThreads + tid;
+      if (i < vis) keys[i] = stored_key(v[u]);
+    }
+  }
   uint32_t prefix = 0, mask = 0;
   int remaining = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kRowThreads) hist[i] = 0;
+  constexpr int kLowShift = sizeof(ST) == 2 ? 16 : 0;  // bf16 keys have no low 16 bits
+  uint32_t* my_copy = hc + (lane % kHistCopies) * kHistStride;
+  for (int shift = 24; shift >= kLowShift; shift -= 8) {
+    for (int i = tid; i < kHistCopies * kHistStride; i += kRowThreads) hc[i] = 0;
     __syncthreads();
     for (int i = tid; i < vis; i += kRowThreads) {
       const uint32_t key = keys[i];
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xffu], 1u);
+      if ((key & mask) == prefix) atomicAdd(&my_copy[(key >> shift) & 0xffu], 1u);
+    }
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t t = 0;
+#pragma unroll
+      for (int c = 0; c < kHistCopies; ++c) t += hc[c * kHistStride + tid];
+      hist[tid] = t;
     }
     __syncthreads();
     if (tid < 64) find_bin_wave(hist, 256, remaining, &sh_bin, &sh_above);
@@ -104,41 +173,46 @@ __global__ __launch_bounds__(kRowThreads) void topk_lds_kernel(
     prefix |= static_cast<uint32_t>(sh_bin) << shift;
     mask |= 0xffu << shift;
     remaining -= sh_above;
-    __syncthreads();
   }
   const uint32_t T = prefix;
   const int need_eq = remaining;
 
-  // compaction in index order
-  const int lane = tid & 63, wv = tid >> 6;
-  int run_gt = 0, run_eq = 0;
-  for (int base = 0; base < vis; base += kRowThreads) {
-    const int i = base + tid;
+  // compaction in index order: entry i = 1024 r + tid.  Per-wave counts of
+  // every round, one scan over (round, wave), then the writes.
+  const int n_rounds = (vis + kRowThreads - 1) / kRowThreads;
+  for (int r = 0; r < n_rounds; ++r) {
+    const int i = r * kRowThreads + tid;
+    const uint32_t key = i < vis ? keys[i] : 0u;
+    const uint64_t bg = __ballot(i < vis && key > T), be = __ballot(i < vis && key == T);
+    if (lane == 0) {
+      cg[r * kRowWaves + wv] = __popcll(bg);
+      ce[r * kRowWaves + wv] = __popcll(be);
+    }
+  }
+  __syncthreads();
+  {
+    const int t = tid;  // n_rounds * kRowWaves <= kRowThreads entries, round-major
+    const bool in = t < n_rounds * kRowWaves;
+    const int a = in ? cg[t] : 0, c = in ? ce[t] : 0;
+    int ea, ec, ta, tc;
+    block_scan2(a, c, &ea, &ec, &ta, &tc, scan_a, scan_b);
+    __syncthreads();  // every count read before the offsets replace them
+    if (in) {
+      cg[t] = ea;
+      ce[t] = ec;
+    }
+  }
+  __syncthreads();
+  for (int r = 0; r < n_rounds; ++r) {
+    const int i = r * kRowThreads + tid;
     const uint32_t key = i < vis ? keys[i] : 0u;
     const bool gt = i < vis && key > T;
     const bool eq = i < vis && key == T;
     const uint64_t bg = __ballot(gt), be = __ballot(eq);
-    if (lane == 0) {
-      wgt[wv] = __popcll(bg);
-      weq[wv] = __popcll(be);
-    }
-    __syncthreads();
-    int off_gt = run_gt, off_eq = run_eq, tot_gt = 0, tot_eq = 0;
-    for (int x = 0; x < kRowThreads / 64; ++x) {
-      if (x < wv) {
-        off_gt += wgt[x];
-        off_eq += weq[x];
-      }
-      tot_gt += wgt[x];
-      tot_eq += weq[x];
-    }
-    const int gt_before = off_gt + lanes_below(bg);
-    const int eq_before = off_eq + lanes_below(be);
+    const int gt_before = cg[r * kRowWaves + wv] + lanes_below(bg);
+    const int eq_before = ce[r * kRowWaves + wv] + lanes_below(be);
     const int pos = gt_before + min(eq_before, need_eq);
     if ((gt || (eq && eq_before < need_eq)) && pos < k) out[pos] = i;
-    run_gt += tot_gt;
-    run_eq += tot_eq;
-    __syncthreads();
   }
 }
 
@@ -193,8 +267,9 @@ __global__ void zero_u32_kernel(uint32_t* p, long long n) {
   if (i < n) p[i] = 0u;
 }
 
+template <typename ST>
 __global__ __launch_bounds__(kSegThreads) void topk_hist_kernel(
-    const float* __restrict__ scores, int N_cap, int n_q, const int32_t* __restrict__ q_pos, int m,
+    const ST* __restrict__ scores, int N_cap, int n_q, const int32_t* __restrict__ q_pos, int m,
     const int32_t* __restrict__ n_entries, int k, int n_seg, uint32_t* __restrict__ ghist) {
   __shared__ uint32_t h[kHistBins];
   const long long row = blockIdx.x / n_seg;
@@ -207,8 +282,8 @@ __global__ __launch_bounds__(kSegThreads) void topk_hist_kernel(
   const int s1 = min(s0 + kSeg, vis);
   for (int i = threadIdx.x; i < kHistBins; i += kSegThreads) h[i] = 0;
   __syncthreads();
-  const float* src = scores + row * N_cap;
-  for (int i = s0 + threadIdx.x; i < s1; i += kSegThreads) atomicAdd(&h[score_bin(score_key(src[i]))], 1u);
+  const ST* src = scores + row * N_cap;
+  for (int i = s0 + threadIdx.x; i < s1; i += kSegThreads) atomicAdd(&h[score_bin(stored_key(src[i]))], 1u);
   __syncthreads();
   uint32_t* gh = ghist + row * kHistBins;
   for (int i = threadIdx.x; i < kHistBins; i += kSegThreads)
@@ -243,8 +318,9 @@ __device__ void row_threshold(const uint32_t* gh, uint32_t* lh, int vis, int k, 
 constexpr int kQuarter = kSeg / (kSegThreads / 64);  // 2048
 constexpr int kPerLane = kQuarter / 64;                // 32
 
+template <typename ST>
 __global__ __launch_bounds__(kSegThreads) void topk_collect_kernel(
-    const float* __restrict__ scores, int N_cap, int n_q, const int32_t* __restrict__ q_pos, int m,
+    const ST* __restrict__ scores, int N_cap, int n_q, const int32_t* __restrict__ q_pos, int m,
     const int32_t* __restrict__ n_entries, int k, int n_seg, WideWs ws) {
   __shared__ int wtot_s[kSegThreads / 64], wtot_c[kSegThreads / 64];
   __shared__ uint32_t lh[kHistBins];
@@ -258,12 +334,12 @@ __global__ __launch_bounds__(kSegThreads) void topk_collect_kernel(
   const long long rs = row * n_seg + seg;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wbase = s0 + wv * kQuarter;
-  const float* src = scores + row * N_cap;
-  float v[kPerLane];
+  const ST* src = scores + row * N_cap;
+  uint32_t kv[kPerLane];
 #pragma unroll
   for (int r = 0; r < kPerLane; ++r) {
     const int i = wbase + 64 * r + lane;
-    v[r] = i < s1 ? src[i] : 0.f;
+    kv[r] = i < s1 ? stored_key(src[i]) : 0u;
   }
   row_threshold(ws.hist + row * kHistBins, lh, vis, k, &sh_bin, &sh_above, scan_sh);
   const int bstar = sh_bin;
@@ -271,7 +347,7 @@ __global__ __launch_bounds__(kSegThreads) void topk_collect_kernel(
 #pragma unroll
   for (int r = 0; r < kPerLane; ++r) {
     const int i = wbase + 64 * r + lane;
-    const int bin = static_cast<int>(score_bin(score_key(v[r])));
+    const int bin = static_cast<int>(score_bin(kv[r]));
     ns += __popcll(__ballot(i < s1 && bin > bstar));
     nc += __popcll(__ballot(i < s1 && bin == bstar));
   }
@@ -296,7 +372,7 @@ __global__ __launch_bounds__(kSegThreads) void topk_collect_kernel(
 #pragma unroll
   for (int r = 0; r < kPerLane; ++r) {
     const int i = wbase + 64 * r + lane;
-    const uint32_t key = score_key(v[r]);
+    const uint32_t key = kv[r];
     const int bin = static_cast<int>(score_bin(key));
     const bool is_s = i < s1 && bin > bstar;
     const bool is_c = i < s1 && bin == bstar;
@@ -520,40 +596,6 @@ constexpr int kMaxBlk = 8192;     // blocks per row (N_cap <= 1 Mi entries)
 constexpr int kEmitLds = 8192;    // emitted pairs held in LDS (else read from global)
 constexpr int kSegPerThread = kMaxBlk / kRowThreads;
 
-// Block-wide exclusive prefix of two per-thread counts (kRowThreads threads);
-// also returns the totals.  scan_a/scan_b hold kRowThreads/64 ints each.
-__device__ __forceinline__ void block_scan2(int a, int b, int* ea, int* eb, int* ta, int* tb,
-                                            int* scan_a, int* scan_b) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int ia = a, ib = b;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int va = __shfl_up(ia, o, 64), vb = __shfl_up(ib, o, 64);
-    if (lane >= o) {
-      ia += va;
-      ib += vb;
-    }
-  }
-  if (lane == 63) {
-    scan_a[wv] = ia;
-    scan_b[wv] = ib;
-  }
-  __syncthreads();
-  int oa = ia - a, ob = ib - b, sa = 0, sb = 0;
-  for (int x = 0; x < kRowThreads / 64; ++x) {
-    if (x < wv) {
-      oa += scan_a[x];
-      ob += scan_b[x];
-    }
-    sa += scan_a[x];
-    sb += scan_b[x];
-  }
-  *ea = oa;
-  *eb = ob;
-  *ta = sa;
-  *tb = sb;
-}
-
 constexpr int kEmitPerThread = kEmitLds / kRowThreads;  // 8
 
 __global__ __launch_bounds__(kRowThreads) void select_finish_kernel(
@@ -766,12 +808,13 @@ uint32_t* topk_hist_in_workspace(void* ws, int B, int n_q, int N_cap, int k) {
   return wide_ws(ws, static_cast<long long>(B) * n_q, n_segments(N_cap), k).hist;
 }
 
-static hipError_t launch_collect_finish(long long rows, int N_cap, const float* scores, int n_q,
+template <typename ST>
+static hipError_t launch_collect_finish(long long rows, int N_cap, const ST* scores, int n_q,
                                         const int32_t* q_pos, int m, const int32_t* n_entries, int k,
                                         int32_t* idx, const WideWs& w, int n_seg, hipStream_t s) {
   const dim3 g2(static_cast<unsigned>(rows * n_seg));
-  hipLaunchKernelGGL(topk_collect_kernel, g2, dim3(kSegThreads), 0, s, scores, N_cap, n_q, q_pos, m,
-                     n_entries, k, n_seg, w);
+  hipLaunchKernelGGL(topk_collect_kernel<ST>, g2, dim3(kSegThreads), 0, s, scores, N_cap, n_q, q_pos,
+                     m, n_entries, k, n_seg, w);
   hipLaunchKernelGGL(topk_finish_kernel, dim3(static_cast<unsigned>(rows)), dim3(kRowThreads), 0, s,
                      N_cap, n_q, q_pos, m, n_entries, k, n_seg, w, idx);
   return hipGetLastError();
@@ -785,8 +828,8 @@ hipError_t launch_topk_from_hist(int B, int n_q, int N_cap, const float* scores,
   if (N_cap <= kLdsMaxRow) return launch_topk(B, n_q, N_cap, scores, q_pos, m, n_entries, k, idx, ws, s);
   const int n_seg = n_segments(N_cap);
   if (n_seg > kMaxSeg || k > kMaxK) return hipErrorInvalidValue;
-  return launch_collect_finish(rows, N_cap, scores, n_q, q_pos, m, n_entries, k, idx,
-                               wide_ws(ws, rows, n_seg, k), n_seg, s);
+  return launch_collect_finish<float>(rows, N_cap, scores, n_q, q_pos, m, n_entries, k, idx,
+                                      wide_ws(ws, rows, n_seg, k), n_seg, s);
 }
 
 size_t topk_workspace_bytes(int B, int n_q, int N_cap, int k) {
@@ -794,14 +837,16 @@ size_t topk_workspace_bytes(int B, int n_q, int N_cap, int k) {
   return wide_layout(static_cast<long long>(B) * n_q, n_segments(N_cap), k).total;
 }
 
-hipError_t launch_topk(int B, int n_q, int N_cap, const float* scores, const int32_t* q_pos, int m,
-                       const int32_t* n_entries, int k, int32_t* idx, void* ws, hipStream_t s) {
+template <typename ST>
+static hipError_t launch_topk_t(int B, int n_q, int N_cap, const ST* scores, const int32_t* q_pos,
+                                int m, const int32_t* n_entries, int k, int32_t* idx, void* ws,
+                                hipStream_t s) {
   const long long rows = static_cast<long long>(B) * n_q;
   if (rows == 0) return hipSuccess;
   if (N_cap <= kLdsMaxRow) {
     const size_t lds = sizeof(uint32_t) * static_cast<size_t>(N_cap > 0 ? N_cap : 1);
-    hipLaunchKernelGGL(topk_lds_kernel, dim3(static_cast<unsigned>(rows)), dim3(kRowThreads), lds, s,
-                       scores, N_cap, n_q, q_pos, m, n_entries, k, idx);
+    hipLaunchKernelGGL(topk_lds_kernel<ST>, dim3(static_cast<unsigned>(rows)), dim3(kRowThreads), lds,
+                       s, scores, N_cap, n_q, q_pos, m, n_entries, k, idx);
     return hipGetLastError();
   }
   const int n_seg = n_segments(N_cap);
@@ -811,9 +856,20 @@ hipError_t launch_topk(int B, int n_q, int N_cap, const float* scores, const int
   hipLaunchKernelGGL(zero_u32_kernel, dim3(static_cast<unsigned>((nh + 255) / 256)), dim3(256), 0, s,
                      w.hist, nh);
   const dim3 g2(static_cast<unsigned>(rows * n_seg));
-  hipLaunchKernelGGL(topk_hist_kernel, g2, dim3(kSegThreads), 0, s, scores, N_cap, n_q, q_pos, m,
+  hipLaunchKernelGGL(topk_hist_kernel<ST>, g2, dim3(kSegThreads), 0, s, scores, N_cap, n_q, q_pos, m,
                      n_entries, k, n_seg, w.hist);
-  return launch_collect_finish(rows, N_cap, scores, n_q, q_pos, m, n_entries, k, idx, w, n_seg, s);
+  return launch_collect_finish<ST>(rows, N_cap, scores, n_q, q_pos, m, n_entries, k, idx, w, n_seg, s);
+}
+
+hipError_t launch_topk(int B, int n_q, int N_cap, const void* scores, const int32_t* q_pos, int m,
+                       const int32_t* n_entries, int k, int32_t* idx, void* ws, hipStream_t s,
+                       int score_fmt) {
+  if (score_fmt == LCA_BF16)
+    return launch_topk_t<uint16_t>(B, n_q, N_cap, static_cast<const uint16_t*>(scores), q_pos, m,
+                                   n_entries, k, idx, ws, s);
+  if (score_fmt != LCA_F32) return hipErrorInvalidValue;
+  return launch_topk_t<float>(B, n_q, N_cap, static_cast<const float*>(scores), q_pos, m, n_entries,
+                              k, idx, ws, s);
 }
 
 bool select_supported(int N_cap, int k) {

@@ -88,6 +88,19 @@ def lca_indexer_scores(B, n_q, H_I, d_I, idx_fmt, qI, qI_scale, kI, kI_scale, N_
         _stream(stream)))
 
 
+def lca_indexer_scores_bf16(B, n_q, H_I, d_I, idx_fmt, qI, qI_scale, kI, kI_scale, N_cap, w, q_pos,
+                            m, n_entries, scores, stream=None):
+    vb = row_bytes(idx_fmt, d_I)
+    mx = idx_fmt == "mxfp4"
+    return check("lca_indexer_scores_bf16", lib().lca_indexer_scores_bf16(
+        B, n_q, H_I, d_I, FMT[idx_fmt], _ptr(qI, vb * B * n_q * H_I, "qI"),
+        _ptr(qI_scale, B * n_q * H_I * d_I // 32, "qI_scale", not mx),
+        _ptr(kI, vb * B * N_cap, "kI"), _ptr(kI_scale, B * N_cap * d_I // 32, "kI_scale", not mx),
+        N_cap, _ptr(w, 4 * B * n_q * H_I, "w"), _ptr(q_pos, 4 * B * n_q, "q_pos"), m,
+        _ptr(n_entries, 4 * B, "n_entries"), _ptr(scores, 2 * B * n_q * N_cap, "scores"),
+        _stream(stream)))
+
+
 def lca_topk_workspace_size(B, n_q, N_cap, k) -> int:
     return lib().lca_topk_workspace_size(B, n_q, N_cap, k)
 
@@ -98,6 +111,16 @@ def lca_topk(B, n_q, N_cap, scores, q_pos, m, n_entries, k, idx, workspace=None,
         workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
     return check("lca_topk", lib().lca_topk(
         B, n_q, N_cap, _ptr(scores, 4 * B * n_q * N_cap, "scores"), _ptr(q_pos, 4 * B * n_q, "q_pos"),
+        m, _ptr(n_entries, 4 * B, "n_entries"), k, _ptr(idx, 4 * B * n_q * k, "idx"),
+        _ptr(workspace, need, "workspace", need == 0), need, _stream(stream)))
+
+
+def lca_topk_bf16(B, n_q, N_cap, scores, q_pos, m, n_entries, k, idx, workspace=None, stream=None):
+    need = lca_topk_workspace_size(B, n_q, N_cap, k)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    return check("lca_topk_bf16", lib().lca_topk_bf16(
+        B, n_q, N_cap, _ptr(scores, 2 * B * n_q * N_cap, "scores"), _ptr(q_pos, 4 * B * n_q, "q_pos"),
         m, _ptr(n_entries, 4 * B, "n_entries"), k, _ptr(idx, 4 * B * n_q * k, "idx"),
         _ptr(workspace, need, "workspace", need == 0), need, _stream(stream)))
 

@@ -81,6 +81,21 @@ class PrefillLayer:
         ops.lca_topk(self.B, self.n, self.N_cap, self.scores, self.q_pos, self.m, self.n_entries,
                      self.cfg.k, self.idx, self.ws_topk)
 
+    # the BF16-score selector: bf16 scores and a top-k over them (own buffers)
+    def indexer_bf16(self):
+        cfg = self.cfg
+        if not hasattr(self, "scores16"):
+            self.scores16 = torch.empty((self.B, self.n, self.N_cap), dtype=torch.int16,
+                                        device=self.device)
+            self.idx16 = torch.empty_like(self.idx)
+        ops.lca_indexer_scores_bf16(self.B, self.n, cfg.H_I, cfg.d_I, cfg.idx_dtype, self.qI,
+                                    self.qI_scale, self.kI, self.kI_scale, self.N_cap, self.w,
+                                    self.q_pos, self.m, self.n_entries, self.scores16)
+
+    def topk_bf16(self):
+        ops.lca_topk_bf16(self.B, self.n, self.N_cap, self.scores16, self.q_pos, self.m,
+                          self.n_entries, self.cfg.k, self.idx16, self.ws_topk)
+
     def attention(self):
         cfg = self.cfg
         ops.lca_sparse_mqa(self.B, self.n, cfg.H, self.c, self.q, cfg.io_dtype, self.cache,

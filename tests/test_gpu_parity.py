@@ -90,6 +90,29 @@ def test_topk_select_stage_bit_exact(N, k, kind):
         assert np.array_equal(got[r], want), f"row {r} vis {vis[r]}"
 
 
+@pytest.mark.parametrize("N,k,kind", [
+    (300, 32, "ties"), (36864, 1024, "normal"), (36864, 1024, "ties"), (20000, 1024, "special"),
+    (100003, 1024, "normal"), (262148, 1024, "ties"), (70000, 1, "normal")])
+def test_topk_bf16_select_stage_bit_exact(N, k, kind):
+    """The BF16-score selector over bf16 arrays: equal to the oracle's stable
+    top-k of the same bf16 values (rounding normal scores to bf16 makes ties
+    common at the threshold)."""
+    say(f"topk bf16 N={N} k={k} kind={kind}")
+    rng = np.random.default_rng(N + 3 * k)
+    B, n_q = 2, 3
+    s16 = enc.to_bf16_bits(_scores(kind, B * n_q, N, rng))
+    s = O.decode(s16, "bf16")
+    vis = np.array([0, max(0, k - 1), k, min(N, k + 1), N, N - 3])[: B * n_q]
+    q_pos = T((vis - 1).astype(np.int32).reshape(B, n_q))
+    n_ent = T(np.full(B, N, np.int32))
+    idx = torch.full((B, n_q, k), -7, dtype=torch.int32, device=DEV)
+    ops.lca_topk_bf16(B, n_q, N, T(s16.reshape(B, n_q, N)), q_pos, 1, n_ent, k, idx)
+    got = host(idx).reshape(B * n_q, k)
+    for r in range(B * n_q):
+        want = O.topk(s[r:r + 1], [vis[r]], k)[0]
+        assert np.array_equal(got[r], want), f"row {r} vis {vis[r]}"
+
+
 # ---------------------------------------------------------------------------
 # indexer
 
@@ -164,6 +187,41 @@ def test_indexer_scores_many_rows(fmt):
                 err = np.abs(got[b, t, :vis] - ref)
                 assert np.all(err <= bnd + 1e-30), f"b{b} t{t}: err {err.max():.3g}"
             assert np.all(got[b, t, vis:] == 12345.0), f"b{b} t{t}: entries past vis were written"
+
+
+@pytest.mark.parametrize("fmt,n_q", [("fp8", 3), ("fp8", 75), ("mxfp4", 75), ("f32", 3)])
+def test_indexer_scores_bf16_is_rounded_fp32(fmt, n_q):
+    """The bf16 scores are the round-to-nearest-even of the float32 scores the
+    float32 entry point writes for the same inputs (one-row and row-group
+    kernels); entries past vis are untouched."""
+    say(f"indexer bf16 scores {fmt} n_q={n_q}")
+    rng = np.random.default_rng(5 + n_q)
+    HI, dI = (4, 32) if fmt == "f32" else (64, 128)
+    B, N, m = 2, 3001, 4
+    qf = rng.standard_normal((B, n_q, HI, dI))
+    kf = rng.standard_normal((B, N, dI))
+    w = rng.random((B, n_q, HI)).astype(np.float32)
+    if fmt == "mxfp4":
+        qb, qs = enc.to_mxfp4(qf)
+        kb, ks = enc.to_mxfp4(kf)
+        qs_t, ks_t = T(qs), T(ks)
+    else:
+        qb, kb = enc.encode(qf, fmt), enc.encode(kf, fmt)
+        qs_t = ks_t = None
+    pos = rng.integers(-1, 4 * N + 40, (B, n_q)).astype(np.int32)
+    n_ent = np.array([N, N - 17], np.int32)
+    s32 = torch.full((B, n_q, N), 12345.0, dtype=torch.float32, device=DEV)
+    s16 = torch.full((B, n_q, N), 0x1234, dtype=torch.int16, device=DEV)
+    args = (B, n_q, HI, dI, fmt, T(qb), qs_t, T(kb), ks_t, N, T(w), T(pos), m, T(n_ent))
+    ops.lca_indexer_scores(*args, s32)
+    ops.lca_indexer_scores_bf16(*args, s16)
+    g32 = host(s32)
+    g16 = host(s16).view(np.uint16)
+    for b in range(B):
+        for t in range(n_q):
+            vis = int(O.visible([pos[b, t]], m, n_ent[b])[0])
+            assert np.array_equal(g16[b, t, :vis], enc.to_bf16_bits(g32[b, t, :vis])), f"b{b} t{t}"
+            assert np.all(g16[b, t, vis:] == 0x1234), f"b{b} t{t}: entries past vis were written"
 
 
 # ---------------------------------------------------------------------------
