@@ -993,7 +993,7 @@ Plan make_plan(long long rows, int H, int c, int q_fmt, int kv_fmt, int k, int N
   const int NT = (dense ? N_cap : k) + n_win;
   Plan p;
   p.mfma = use_mfma(H, c, q_fmt, kv_fmt);
-  p.decode = p.mfma && q_fmt == LCA_BF16 && rows < 512;
+  p.decode = p.mfma && q_fmt == LCA_BF16;
   if (rows >= 512) {
     p.n_splits = 1;
     p.split_rows = NT;
