@@ -74,17 +74,36 @@ def attention(qhat_h, rows, tau, sink=None):
     return [sum(e * r[d] for e, r in zip(es, rows)) / den for d in range(c)]
 
 
+def turn(row, pos, base, rope_dims=64):
+    """Partial RoPE ("DeepSeek V4 Architecture Tricks", section "Partial RoPE 和
+    Attention Sink"): pair i of the last rope_dims dims turns by the angle
+    pos * base^(-2i/rope_dims); base 0 leaves the row as it is."""
+    out = list(row)
+    if not base:
+        return out
+    r0 = len(row) - rope_dims
+    for i in range(rope_dims // 2):
+        a = pos * math.pow(base, -2.0 * i / rope_dims)
+        x, y = row[r0 + 2 * i], row[r0 + 2 * i + 1]
+        out[r0 + 2 * i] = x * math.cos(a) - y * math.sin(a)
+        out[r0 + 2 * i + 1] = x * math.sin(a) + y * math.cos(a)
+    return out
+
+
 def layer(*, mode, m, k, n_win, tau, eps, C, Z, P, q, qI=None, kI=None, w=None,
-          round_kv=lambda row: row, sink=None):
+          round_kv=lambda row: row, sink=None, rope_base=0.0):
     """Whole prefill of a sequence from position 0.  Inputs are nested lists.
 
     round_kv is the storage cast applied to stored entries and window rows.
+    With rope_base, entry s is turned at the position of its last token
+    (s+1)m-1, window row j at j, the query of token t at t and its output at -t.
     Returns (outs [n][H][c], idx [n][k] or None, entries [N][c])."""
     n = len(C)
     nb = n // m
-    entries = [round_kv(rmsnorm_row(compress_entry(C, Z, P, m, s, mode == "csa"), eps))
+    entries = [round_kv(turn(rmsnorm_row(compress_entry(C, Z, P, m, s, mode == "csa"), eps),
+                             (s + 1) * m - 1, rope_base))
                for s in range(nb)]
-    U = [round_kv(rmsnorm_row(C[j], eps)) for j in range(n)]
+    U = [round_kv(turn(rmsnorm_row(C[j], eps), j, rope_base)) for j in range(n)]
     outs, idxs = [], []
     for t in range(n):
         vis = (t + 1) // m
@@ -97,7 +116,7 @@ def layer(*, mode, m, k, n_win, tau, eps, C, Z, P, q, qI=None, kI=None, w=None,
             S = list(range(vis))
         W = list(range(max(0, t - n_win + 1), t + 1))
         rows = [entries[s] for s in S] + [U[j] for j in W]
-        outs.append([attention(rmsnorm_row(q[t][h], eps), rows, tau,
-                               None if sink is None else sink[h])
+        outs.append([turn(attention(turn(rmsnorm_row(q[t][h], eps), t, rope_base), rows, tau,
+                                    None if sink is None else sink[h]), -t, rope_base)
                      for h in range(len(q[t]))])
     return outs, (idxs if mode == "csa" else None), entries

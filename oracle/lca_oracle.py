@@ -30,7 +30,11 @@ Readings where the pages are silent (each also listed in the design notes):
   * top-k keeps the min(k, visible) largest scores, ties to the lower index,
     -0 counted as +0, NaN counted as -inf, output ascending, padded with -1;
   * the two branches form one softmax, merged by log-sum-exp; an optional
-    per-head sink logit joins the denominator only.
+    per-head sink logit joins the denominator only;
+  * partial RoPE (off unless a base is given): adjacent pairs of the last 64
+    dims turn by pos * base^(-2i/64); a compressed entry sits at the position of
+    the last token it covers, (s+1)*m - 1; queries turn at their own position
+    and the output turns back by minus that position.
 """
 from collections import deque
 
@@ -296,6 +300,51 @@ def merge(parts, sink=None):
     return o, tot
 
 
+ROPE_DIMS = 64
+
+
+def rope(x, pos, base: float, rope_dims: int = ROPE_DIMS) -> np.ndarray:
+    """Rotary position embedding of the last `rope_dims` dims ([PT] Partial RoPE and
+    attention sink: only the last 64 dims of queries, KV entries and the attention
+    output carry positions; [QB] hybrid attention).  The pages give no frequencies
+    or pairing, so this is the original rotary embedding: pair i of the rotary part
+    (dims c-rope_dims+2i and c-rope_dims+2i+1) turns by the angle
+    pos * base^(-2i/rope_dims), the pair (x, y) becoming
+    (x cos a - y sin a, x sin a + y cos a).  `pos` broadcasts against x.shape[:-1];
+    base == 0 returns x unchanged."""
+    x = np.array(x, dtype=np.float64, copy=True)
+    if not base:
+        return x
+    c = x.shape[-1]
+    i = np.arange(rope_dims // 2, dtype=np.float64)
+    theta = float(base) ** (-2.0 * i / rope_dims)
+    a = np.asarray(pos, np.float64)[..., None] * theta
+    cs, sn = np.cos(a), np.sin(a)
+    xe = x[..., c - rope_dims::2].copy()
+    xo = x[..., c - rope_dims + 1::2].copy()
+    x[..., c - rope_dims::2] = xe * cs - xo * sn
+    x[..., c - rope_dims + 1::2] = xe * sn + xo * cs
+    return x
+
+
+def entry_position(s, m: int):
+    """Position of compressed entry s for RoPE: the last token it covers (the pages
+    leave it open; this is also the first position that sees the entry)."""
+    return (np.asarray(s, np.int64) + 1) * m - 1
+
+
+def core_attention(q, parts, tau: float, eps: float, t: int, sink=None, rope_base: float = 0.0):
+    """One query token's output over the branches' stored rows (each a [R, c] array:
+    the selected or visible entries, then the window): RMSNorm of the query per
+    head, the query turned to its position t, one softmax over all branches (their
+    partials merged by log-sum-exp, with the optional sink), and the output turned
+    back by -t so that only relative positions remain ([PT] Partial RoPE).  Returns
+    the unrounded (o [H, c], lse [H])."""
+    qhat = rope(rmsnorm(np.asarray(q, np.float64), eps), t, rope_base)
+    o, lse = merge([attend(qhat, rows, tau) for rows in parts], sink)
+    return rope(o, -t, rope_base), lse
+
+
 def window_positions(t: int, n_win: int) -> np.ndarray:
     """The query's own position and the n_win-1 before it ([PT] Sliding Window
     Branch, n_win = 128), clipped at 0."""
@@ -308,7 +357,8 @@ def window_positions(t: int, n_win: int) -> np.ndarray:
 
 def prefill_layer(*, mode, m, k, n_win, tau, eps, kv_fmt, out_fmt, pos0,
                   C, Z, P, q, cache_prefix, prevC=None, prevZ=None, win_prefix=None,
-                  qI=None, kI=None, w=None, queries=None, sink=None, idx_given=None):
+                  qI=None, kI=None, w=None, queries=None, sink=None, idx_given=None,
+                  rope_base=0.0):
     """One sequence of CSA ("csa") or HCA ("hca") prefill.
 
     New tokens occupy positions pos0 .. pos0+n-1 (pos0 % m == 0).  cache_prefix
@@ -317,21 +367,31 @@ def prefill_layer(*, mode, m, k, n_win, tau, eps, kv_fmt, out_fmt, pos0,
     new tokens to evaluate (default all); q, qI and w are indexed per query, so
     they may be lazy row accessors.  idx_given ([len(queries), k]) makes the
     attention use those selections instead of the oracle's own (the oracle's
-    scores and selections are still returned).  Returns float64 results.
+    scores and selections are still returned).  rope_base != 0 turns the new
+    entries (at their entry positions), the new window KV (at their tokens'
+    positions), the queries and the outputs; the prefix rows are taken as stored.
+    Returns float64 results.
     """
     C = np.asarray(C, np.float64)
     n, c = C.shape
     E = compress(C, Z, P, m, overlap=(mode == "csa"), prevC=prevC, prevZ=prevZ)
-    entries_new = round_to(rmsnorm(E, eps), kv_fmt)
+    n_pre = np.asarray(cache_prefix).reshape(-1, c).shape[0]
+    e_pos = entry_position(n_pre + np.arange(E.shape[0]), m)
+    entries_exact = rope(rmsnorm(E, eps), e_pos, rope_base)
+    entries_new = round_to(entries_exact, kv_fmt)
     Khat = np.concatenate([np.asarray(cache_prefix, np.float64).reshape(-1, c), entries_new], 0)
-    U_new = round_to(rmsnorm(C, eps), kv_fmt)
+    U_exact = rope(rmsnorm(C, eps), pos0 + np.arange(n), rope_base)
+    U_new = round_to(U_exact, kv_fmt)
     n_pre_win = 0 if win_prefix is None else len(win_prefix)
     bound = compress_error_bound(C, Z, P, m, mode == "csa", prevC, prevZ, eps)
+    if rope_base:
+        bound = rope_error_bound(entries_exact, bound)
     U = U_new if win_prefix is None else np.concatenate([np.asarray(win_prefix, np.float64), U_new], 0)
     win_origin = pos0 - n_pre_win
     queries = np.arange(n) if queries is None else np.asarray(queries)
     H = np.asarray(q[int(queries[0])]).shape[0] if len(queries) else 0
     res = {"entries": entries_new, "entries_bound": bound, "window": U_new,
+           "window_bound": rope_error_bound(U_exact, 0.0) if rope_base else None,
            "out": np.zeros((len(queries), H, c)),
            "lse": np.zeros((len(queries), H)), "idx": None, "scores": None}
     if mode == "csa":
@@ -352,10 +412,7 @@ def prefill_layer(*, mode, m, k, n_win, tau, eps, kv_fmt, out_fmt, pos0,
             S = np.arange(vis)
         W = window_positions(t, n_win) - win_origin
         assert W.min() >= 0, "window reaches before the provided window KV"
-        qhat = rmsnorm(np.asarray(q[i], np.float64), eps)          # per head
-        part_c = attend(qhat, Khat[S], tau)
-        part_w = attend(qhat, U[W], tau)
-        o, lse = merge([part_c, part_w], sink)
+        o, lse = core_attention(q[i], [Khat[S], U[W]], tau, eps, t, sink, rope_base)
         res["out"][r] = round_to(o, out_fmt)
         res["lse"][r] = lse
     return res
@@ -406,7 +463,7 @@ class DecodeState:
 
 
 def decode_step(st: DecodeState, *, tokC, tokZ, P, q, tau, eps, kv_fmt, out_fmt, k=0,
-                qI=None, kI=None, w=None, sink=None, idx_given=None):
+                qI=None, kI=None, w=None, sink=None, idx_given=None, rope_base=0.0):
     """Append one token and answer its query (the step of a decode loop).
 
     The token goes to the incomplete block and its normalised KV to the window;
@@ -414,14 +471,17 @@ def decode_step(st: DecodeState, *, tokC, tokZ, P, q, tau, eps, kv_fmt, out_fmt,
     previous block as overlap for CSA).  The query at the token's position then
     attends top-k (CSA) or all (HCA) visible entries plus the window.
     kI holds the indexer keys of all entries including a new one.  idx_given makes
-    the attention use that selection instead of the oracle's own."""
+    the attention use that selection instead of the oracle's own.  rope_base != 0
+    turns the token's window KV and a new entry (both at the token's position t,
+    the last token of the entry's block), the query and the output."""
     m, c = st.m, st.c
     t = st.L
     tokC = np.asarray(tokC, np.float64).reshape(c)
     tokZ = np.asarray(tokZ, np.float64).reshape(c)
     curC = np.concatenate([st.cur[0], tokC[None]], 0)
     curZ = np.concatenate([st.cur[1], tokZ[None]], 0)
-    u_t = round_to(rmsnorm(tokC, eps), kv_fmt)
+    u_exact = rope(rmsnorm(tokC, eps), t, rope_base)
+    u_t = round_to(u_exact, kv_fmt)
     win_rows = np.array(list(st.window) + [u_t]).reshape(-1, c)
     new_entry = new_bound = None
     if (t + 1) % m == 0:
@@ -430,11 +490,14 @@ def decode_step(st: DecodeState, *, tokC, tokZ, P, q, tau, eps, kv_fmt, out_fmt,
             E = compress(curC, curZ, P, m, True, pc, pz)
         else:
             E = compress(curC, curZ, P, m, False)
-        new_entry = round_to(rmsnorm(E, eps), kv_fmt)[0]
+        e_exact = rope(rmsnorm(E, eps), entry_position(st.n_entries, m), rope_base)
+        new_entry = round_to(e_exact, kv_fmt)[0]
         if st.mode == "csa":
             new_bound = compress_error_bound(curC, curZ, P, m, True, pc, pz, eps)[0]
         else:
             new_bound = compress_error_bound(curC, curZ, P, m, False, eps=eps)[0]
+        if rope_base:
+            new_bound = rope_error_bound(e_exact[0], new_bound)
         st.new.append(new_entry)
         st.prev = (curC, curZ)
         st.cur = (np.zeros((0, c)), np.zeros((0, c)))
@@ -444,9 +507,9 @@ def decode_step(st: DecodeState, *, tokC, tokZ, P, q, tau, eps, kv_fmt, out_fmt,
         st.window.append(u_t)
     st.L = t + 1
     vis = int(visible([t], m, st.n_entries)[0])
-    qhat = rmsnorm(np.asarray(q, np.float64), eps)
     res = {"new_entry": new_entry, "new_entry_bound": new_bound, "window_row": u_t, "idx": None,
-           "scores": None}
+           "scores": None,
+           "window_row_bound": rope_error_bound(u_exact, 0.0) if rope_base else None}
     if st.mode == "csa":
         I = index_scores(np.asarray(qI, np.float64)[None], np.asarray(kI, np.float64)[:vis],
                          np.asarray(w, np.float64)[None], [vis])
@@ -456,13 +519,29 @@ def decode_step(st: DecodeState, *, tokC, tokZ, P, q, tau, eps, kv_fmt, out_fmt,
         S = use[use >= 0]
     else:
         S = np.arange(vis)
-    part_c = attend(qhat, st.rows(S), tau)
-    part_w = attend(qhat, win_rows, tau)
-    o, lse = merge([part_c, part_w], sink)
+    o, lse = core_attention(q, [st.rows(S), win_rows], tau, eps, t, sink, rope_base)
     res["out"] = round_to(o, out_fmt)
     res["out_exact"] = o
     res["lse"] = lse
     return res
+
+
+def rope_error_bound(y, bound, rope_dims: int = ROPE_DIMS) -> np.ndarray:
+    """Bound on the error of an fp32 rotation of values y (exact: the rotated values;
+    the rotation preserves |pair|) whose inputs carry the error bound `bound`: a
+    rotated dim mixes both dims of its pair, so it takes both bounds, plus
+    2^-20 |pair| for the float32 cos/sin (of an angle reduced in float64) and the
+    float32 products.  Dims outside the rotary part keep their bound."""
+    y = np.asarray(y, np.float64)
+    b = np.array(np.broadcast_to(np.asarray(bound, np.float64), y.shape), copy=True)
+    c = y.shape[-1]
+    ye, yo = y[..., c - rope_dims::2], y[..., c - rope_dims + 1::2]
+    pair = np.sqrt(ye * ye + yo * yo)
+    be, bo = b[..., c - rope_dims::2].copy(), b[..., c - rope_dims + 1::2].copy()
+    extra = be + bo + 2.0 ** -20 * pair
+    b[..., c - rope_dims::2] = extra
+    b[..., c - rope_dims + 1::2] = extra
+    return b
 
 
 def gamma(n: int) -> float:

@@ -46,7 +46,8 @@ def oracle_prefill(cfg, d, b, queries, idx_given=None, sink=None):
         prevC=O.decode(d["prevC"][b], io) if "prevC" in d else None,
         prevZ=O.decode(d["prevZ"][b], io) if "prevZ" in d else None,
         win_prefix=O.decode(d["win_prefix"][b], kv) if "win_prefix" in d else None,
-        qI=qI, kI=kI, w=d["w"][b], queries=queries, idx_given=idx_given, sink=sink)
+        qI=qI, kI=kI, w=d["w"][b], queries=queries, idx_given=idx_given, sink=sink,
+        rope_base=cfg.rope_base)
 
 
 # ---------------------------------------------------------------------------
@@ -95,6 +96,6 @@ def oracle_decode(cfg, d, b, idx_given=None, sink=None):
     r = O.decode_step(st, tokC=O.decode(d["tokC"][b], io), tokZ=O.decode(d["tokZ"][b], io),
                       P=np.asarray(d["P"], np.float64), q=O.decode(d["q"][b], io), tau=cfg.tau,
                       eps=cfg.eps, kv_fmt=cfg.kv_dtype, out_fmt=io, idx_given=idx_given, sink=sink,
-                      **kw)
+                      rope_base=cfg.rope_base, **kw)
     r["state"] = st
     return r

@@ -35,6 +35,7 @@ class LayerConfig:
     seed: int = 0
     rope_dims: int = 64
     eps: float = 1e-6
+    rope_base: float = 0.0           # partial RoPE frequency base; 0: off (inputs taken as post-RoPE)
 
     @property
     def tau(self) -> float:

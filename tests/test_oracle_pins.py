@@ -293,23 +293,26 @@ def _tiny_layer_inputs(seed, n=48, c=16, H=2, HI=3, dI=8, m=4):
                 w=r.random((n, HI)))
 
 
-@pytest.mark.parametrize("mode,m,k,n_win,kv", [("csa", 4, 5, 6, "f32"), ("csa", 4, 3, 1, "bf16"),
-                                               ("hca", 8, 0, 5, "fp8"), ("csa", 2, 4, 3, "fp8_bf16rope")])
-def test_layer_matches_brute_force(mode, m, k, n_win, kv):
-    c = 80 if kv == "fp8_bf16rope" else 16
+@pytest.mark.parametrize("mode,m,k,n_win,kv,rope_base",
+                         [("csa", 4, 5, 6, "f32", 0.0), ("csa", 4, 3, 1, "bf16", 0.0),
+                          ("hca", 8, 0, 5, "fp8", 0.0), ("csa", 2, 4, 3, "fp8_bf16rope", 0.0),
+                          ("csa", 4, 5, 6, "f32", 10000.0), ("hca", 8, 0, 5, "fp8_bf16rope", 50.0)])
+def test_layer_matches_brute_force(mode, m, k, n_win, kv, rope_base):
+    c = 80 if kv == "fp8_bf16rope" or rope_base else 16
     d = _tiny_layer_inputs(20 + m + k, n=32, c=c, m=m)
     tau = 1 / math.sqrt(c)
     sink = np.array([0.3, -0.7])
     res = O.prefill_layer(mode=mode, m=m, k=k, n_win=n_win, tau=tau, eps=1e-6, kv_fmt=kv,
                           out_fmt="f32", pos0=0, C=d["C"], Z=d["Z"], P=d["P"][: 2 * m if mode == "csa" else m],
                           q=d["q"], cache_prefix=np.zeros((0, c)), qI=d["qI"], kI=d["kI"], w=d["w"],
-                          sink=sink)
+                          sink=sink, rope_base=rope_base)
     rk = (lambda row: O.round_to(np.array(row), kv).tolist())
     outs, idxs, entries = brute.layer(mode=mode, m=m, k=k, n_win=n_win, tau=tau, eps=1e-6,
                                       C=d["C"].tolist(), Z=d["Z"].tolist(),
                                       P=d["P"][: 2 * m if mode == "csa" else m].tolist(),
                                       q=d["q"].tolist(), qI=d["qI"].tolist(), kI=d["kI"].tolist(),
-                                      w=d["w"].tolist(), round_kv=rk, sink=sink.tolist())
+                                      w=d["w"].tolist(), round_kv=rk, sink=sink.tolist(),
+                                      rope_base=rope_base)
     assert np.allclose(res["entries"], entries, rtol=1e-12, atol=1e-12)
     if mode == "csa":
         assert np.array_equal(res["idx"], np.array(idxs))
@@ -375,12 +378,13 @@ def test_causality_future_perturbation():
 # decode: incremental steps reproduce the prefill
 
 
-@pytest.mark.parametrize("mode,m", [("csa", 4), ("hca", 8)])
-def test_incremental_decode_equals_prefill(mode, m):
-    n, c, H = 40, 16, 2
+@pytest.mark.parametrize("mode,m,rope_base", [("csa", 4, 0.0), ("hca", 8, 0.0), ("csa", 4, 10000.0),
+                                               ("hca", 8, 300.0)])
+def test_incremental_decode_equals_prefill(mode, m, rope_base):
+    n, c, H = 40, 80 if rope_base else 16, 2
     d = _tiny_layer_inputs(40 + m, n=n, c=c, H=H, m=m)
     P = d["P"][: 2 * m if mode == "csa" else m]
-    kw = dict(tau=0.25, eps=1e-6, kv_fmt="bf16", out_fmt="f32")
+    kw = dict(tau=0.25, eps=1e-6, kv_fmt="bf16", out_fmt="f32", rope_base=rope_base)
     pre = O.prefill_layer(mode=mode, m=m, k=3, n_win=5, pos0=0, C=d["C"], Z=d["Z"], P=P, q=d["q"],
                           cache_prefix=np.zeros((0, c)), qI=d["qI"], kI=d["kI"], w=d["w"], **kw)
     st = O.DecodeState(mode=mode, m=m, n_win=5, c=c)
@@ -391,6 +395,98 @@ def test_incremental_decode_equals_prefill(mode, m):
         if mode == "csa":
             assert np.array_equal(r["idx"], pre["idx"][t])
     assert np.array_equal(st.rows(np.arange(st.n_entries)), pre["entries"])
+
+
+# ---------------------------------------------------------------------------
+# partial RoPE: the rotation itself, its group law, relative positions only
+
+
+def test_rope_is_a_complex_rotation_of_the_last_64_dims():
+    r = rng(70)
+    x = r.standard_normal((5, 3, 160))
+    pos = r.integers(0, 1 << 21, (5, 3))
+    base = 10000.0
+    y = O.rope(x, pos, base)
+    assert np.array_equal(y[..., :96], x[..., :96])
+    # pair i as the complex number x[2i] + i x[2i+1], multiplied by e^{i pos w_i}
+    z = x[..., 96::2] + 1j * x[..., 97::2]
+    w = np.exp(-math.log(base) * np.arange(32) / 32.0)
+    zr = z * np.exp(1j * (pos[..., None] * w))
+    assert np.allclose(y[..., 96::2], zr.real, rtol=0, atol=1e-8)
+    assert np.allclose(y[..., 97::2], zr.imag, rtol=0, atol=1e-8)
+    assert np.array_equal(O.rope(x, pos, 0.0), x)
+    assert np.array_equal(O.rope(x, 0, base), x)
+    # the lowest pair turns by pos radians, the highest by pos * base^(-31/32)
+    assert np.allclose(O.rope(np.r_[np.zeros(62), 1.0, 0.0], 0.5, base)[62:],
+                       [math.cos(0.5 * base ** (-31 / 32)), math.sin(0.5 * base ** (-31 / 32))])
+    assert np.allclose(O.rope(np.r_[1.0, 0.0, np.zeros(62)], 0.5, base)[:2], [math.cos(0.5), math.sin(0.5)])
+
+
+def test_rope_group_law_and_lengths():
+    r = rng(71)
+    x = r.standard_normal((4, 128))
+    base, a, b = 500.0, 123457, -98765
+    assert np.allclose(O.rope(O.rope(x, a, base), b, base), O.rope(x, a + b, base), rtol=0, atol=1e-9)
+    assert np.allclose(O.rope(O.rope(x, a, base), -a, base), x, rtol=0, atol=1e-9)
+    y = O.rope(x, a, base)
+    assert np.allclose(y[:, 64::2] ** 2 + y[:, 65::2] ** 2, x[:, 64::2] ** 2 + x[:, 65::2] ** 2)
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    r = rng(72)
+    q, k = r.standard_normal(96), r.standard_normal(96)
+    base = 10000.0
+    for t, s in [(10, 3), (1 << 20, 17), (5, 5)]:
+        d0 = O.rope(q, t, base) @ O.rope(k, s, base)
+        for shift in (1, 1000, 777777):
+            assert abs(O.rope(q, t + shift, base) @ O.rope(k, s + shift, base) - d0) < 1e-9
+    # without the turn the score is the plain dot product at equal positions
+    assert abs(O.rope(q, 9, base) @ O.rope(k, 9, base) - q @ k) < 1e-12
+
+
+def test_core_attention_with_rope_keeps_relative_positions_only():
+    r = rng(73)
+    H, c, base, t = 3, 128, 10000.0, 23
+    q = r.standard_normal((H, c))
+    raw = [O.rmsnorm(r.standard_normal((6, c))), O.rmsnorm(r.standard_normal((4, c)))]
+    pos = [np.array([3, 7, 11, 15, 19, 23]), np.array([20, 21, 22, 23])]
+
+    def run(shift):
+        parts = [O.rope(x, p + shift, base) for x, p in zip(raw, pos)]
+        return O.core_attention(q, parts, 0.1, 1e-6, t + shift, sink=np.array([0.1, -2.0, 1.0]),
+                                rope_base=base)
+
+    o0, l0 = run(0)
+    for shift in (5, 4096, 999999):
+        o1, l1 = run(shift)
+        assert np.allclose(o1, o0, rtol=0, atol=1e-9) and np.allclose(l1, l0, rtol=0, atol=1e-9)
+    # a single row stored at position s: the output is that row turned by s - t
+    row = O.rmsnorm(r.standard_normal(c))
+    o, _ = O.core_attention(q, [O.rope(row, 40, base)[None]], 0.1, 1e-6, 55, rope_base=base)
+    assert np.allclose(o, np.broadcast_to(O.rope(row, -15, base), (H, c)), rtol=0, atol=1e-12)
+    # base 0 is the attention without positions
+    o_off, _ = O.core_attention(q, raw, 0.1, 1e-6, t)
+    o_ref, _ = O.merge([O.attend(O.rmsnorm(q), x, 0.1) for x in raw])
+    assert np.array_equal(o_off, o_ref)
+
+
+def test_rope_error_bound_covers_fp32_rotation():
+    r = rng(74)
+    x = O.rmsnorm(r.standard_normal((200, 128)))
+    pos = r.integers(0, 1 << 21, 200)
+    exact = O.rope(x, pos, 10000.0)
+    # float32 rotation with float32 cos/sin of the float64-reduced angle
+    i = np.arange(32)
+    a = pos[:, None] * 10000.0 ** (-2.0 * i / 64)
+    a = np.remainder(a + np.pi, 2 * np.pi) - np.pi
+    cs, sn = np.cos(a.astype(np.float32)).astype(np.float32), np.sin(a.astype(np.float32)).astype(np.float32)
+    xf = x.astype(np.float32)
+    ye = xf[:, 64::2] * cs - xf[:, 65::2] * sn
+    yo = xf[:, 64::2] * sn + xf[:, 65::2] * cs
+    got = xf.astype(np.float64).copy()
+    got[:, 64::2], got[:, 65::2] = ye, yo
+    bnd = O.rope_error_bound(exact, np.abs(xf.astype(np.float64) - x))
+    assert np.all(np.abs(got - exact) <= bnd)
 
 
 # ---------------------------------------------------------------------------
