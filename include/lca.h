@@ -52,6 +52,19 @@
  *   (s+1)*m - 1 <= t and s < n_entries[b] (strict causality of compressed
  *   attention: an entry that covers a future token is never visible).  Its
  *   window is positions max(0, t-n_win+1) .. t.
+ *
+ * Partial RoPE (argument rope_base; 0 = off, otherwise a finite base > 1)
+ *   "DeepSeek V4 Architecture Tricks", section "Partial RoPE 和 Attention
+ *   Sink"; QbitAI article, hybrid attention section: only the last 64 dims of
+ *   queries, KV entries and the attention output carry positions, and the
+ *   output is turned back by minus the query position so that only relative
+ *   positions remain.  Pair i of the last 64 dims (c-64+2i, c-64+2i+1) turns
+ *   by the angle pos * rope_base^(-2i/64): (x, y) -> (x cos - y sin,
+ *   x sin + y cos).  A compressed entry is turned at the position of the last
+ *   token it covers, (s+1)*m - 1; window KV at its token's position; the
+ *   query at t; the output by -t.  Rows that the caller stores directly in a
+ *   cache or ring are taken as already turned.  The angle is reduced in
+ *   float64 before a float32 sincos.
  */
 #ifndef LCA_H
 #define LCA_H
@@ -63,7 +76,7 @@
 extern "C" {
 #endif
 
-#define LCA_ABI_VERSION 1
+#define LCA_ABI_VERSION 2
 
 /* A hipStream_t. */
 typedef struct ihipStream_t* lca_stream_t;
@@ -128,11 +141,13 @@ size_t lca_kv_row_bytes(int kv_dtype, int c);
  *                first_entry .. first_entry + n_new/m - 1 are written
  *   N_cap        rows per sequence in cache; first_entry + n_new/m <= N_cap
  *   eps          RMSNorm epsilon
+ *   rope_base    partial RoPE base (0 = off): the normalised entry
+ *                first_entry + s is turned at position (first_entry+s+1)*m - 1
  * ------------------------------------------------------------------------- */
 int lca_compress(int mode, int m, int B, int n_new, int c, const void* C, const void* Z,
                  int io_dtype, const void* prevC, const void* prevZ, const float* P,
                  void* cache, int kv_dtype, int N_cap, int first_entry, float eps,
-                 lca_stream_t stream);
+                 float rope_base, lca_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * lca_rmsnorm_rows -- y[b, i] = cast(x[b, i] / sqrt(mean(x[b, i]^2) + eps)):
@@ -141,9 +156,12 @@ int lca_compress(int mode, int m, int B, int n_new, int c, const void* C, const 
  * branch over uncompressed KV).
  *   x  [B, n, c] format x_dtype (F32|BF16)
  *   y  rows (b, i) at y + (b*y_seq_rows + i) * row_bytes(y_dtype, c)
+ *   pos0, rope_base  with rope_base != 0, row i is turned at position pos0 + i
+ *                    (0 <= pos0 <= 2^40)
  * ------------------------------------------------------------------------- */
 int lca_rmsnorm_rows(int B, int n, int c, const void* x, int x_dtype, void* y, int y_dtype,
-                     int y_seq_rows, float eps, lca_stream_t stream);
+                     int y_seq_rows, float eps, int64_t pos0, float rope_base,
+                     lca_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * lca_indexer_scores -- lightning-indexer scores (QbitAI article, hybrid
@@ -225,6 +243,8 @@ int lca_topk_bf16(int B, int n_q, int N_cap, const uint16_t* scores, const int32
  *            win_origin = 0; a prefill buffer of positions p0 .. p0+W_cap-1 is
  *            win_origin = p0.  Every window position must be present.
  *   out      [B, n_q, H, c] format out_dtype (F32|BF16); lse [B, n_q, H] or NULL
+ *   rope_base  partial RoPE (0 = off): qh is turned to q_pos[b,t] and out[b,t,h]
+ *            back by -q_pos[b,t]; the stored rows are taken as turned
  * Workspace: lca_sparse_mqa_workspace_size(...) bytes (split partials).
  * ------------------------------------------------------------------------- */
 size_t lca_sparse_mqa_workspace_size(int B, int n_q, int H, int c, int kv_dtype, int k,
@@ -233,7 +253,7 @@ int lca_sparse_mqa(int B, int n_q, int H, int c, const void* q, int q_dtype, con
                    int kv_dtype, int N_cap, const int32_t* idx, int k, const int32_t* q_pos,
                    int m, const int32_t* n_entries, const void* win, int W_cap,
                    int64_t win_origin, int n_win, float tau, float eps, const float* sink,
-                   void* out, int out_dtype, float* lse, void* workspace,
+                   float rope_base, void* out, int out_dtype, float* lse, void* workspace,
                    size_t workspace_bytes, lca_stream_t stream);
 
 /* ---------------------------------------------------------------------------
@@ -251,11 +271,13 @@ int lca_sparse_mqa(int B, int n_q, int H, int c, const void* q, int q_dtype, con
  *   - n_tokens[b] = p+1, q_pos[b] = p, n_entries[b] = (p+1)/m.
  *   tailC, tailZ [B, 2m or m, c] io_dtype; ring [B, n_win, row] kv_dtype;
  *   cache [B, N_cap, row]; n_tokens, q_pos, n_entries [B] int32 device.
+ *   rope_base (0 = off): the ring row and a new entry are turned at position p
+ *   (the new entry's last token).
  * ------------------------------------------------------------------------- */
 int lca_state_append(int mode, int m, int B, int c, int n_win, const void* tokC, const void* tokZ,
                      int io_dtype, void* tailC, void* tailZ, void* ring, int kv_dtype,
                      const float* P, void* cache, int N_cap, int32_t* n_tokens, int32_t* q_pos,
-                     int32_t* n_entries, float eps, lca_stream_t stream);
+                     int32_t* n_entries, float eps, float rope_base, lca_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * lca_decode_step -- one decode step of one CSA or HCA layer for B sequences:
@@ -281,6 +303,7 @@ typedef struct lca_decode_layer {
   int k, H_I, d_I, idx_dtype;
   const void* kI;       /* [B, N_cap, d_I] (+ kI_scale for MXFP4) */
   const uint8_t* kI_scale;
+  float rope_base;      /* partial RoPE base, 0 = off (as in lca_state_append / lca_sparse_mqa) */
 } lca_decode_layer;
 
 typedef struct lca_decode_io {

@@ -25,7 +25,7 @@ class DecodeLayer(ctypes.Structure):
                 ("tailC", P), ("tailZ", P), ("ring", P), ("cache", P), ("n_tokens", P), ("P", P),
                 ("sink", P), ("tau", c_float), ("eps", c_float),
                 ("k", c_int), ("H_I", c_int), ("d_I", c_int), ("idx_dtype", c_int),
-                ("kI", P), ("kI_scale", P)]
+                ("kI", P), ("kI_scale", P), ("rope_base", c_float)]
 
 
 class DecodeIO(ctypes.Structure):
@@ -40,8 +40,9 @@ SIGNATURES = {
     "lca_last_error": (ctypes.c_char_p, []),
     "lca_kv_row_bytes": (c_size_t, [c_int, c_int]),
     "lca_compress": (c_int, [c_int, c_int, c_int, c_int, c_int, P, P, c_int, P, P, P, P, c_int,
-                             c_int, c_int, c_float, P]),
-    "lca_rmsnorm_rows": (c_int, [c_int, c_int, c_int, P, c_int, P, c_int, c_int, c_float, P]),
+                             c_int, c_int, c_float, c_float, P]),
+    "lca_rmsnorm_rows": (c_int, [c_int, c_int, c_int, P, c_int, P, c_int, c_int, c_float, c_int64,
+                                 c_float, P]),
     "lca_indexer_scores": (c_int, [c_int, c_int, c_int, c_int, c_int, P, P, P, P, c_int, P, P,
                                    c_int, P, P, P]),
     "lca_indexer_scores_bf16": (c_int, [c_int, c_int, c_int, c_int, c_int, P, P, P, P, c_int, P, P,
@@ -52,10 +53,10 @@ SIGNATURES = {
     "lca_sparse_mqa_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                                  c_int, c_int]),
     "lca_sparse_mqa": (c_int, [c_int, c_int, c_int, c_int, P, c_int, P, c_int, c_int, P, c_int, P,
-                               c_int, P, P, c_int, c_int64, c_int, c_float, c_float, P, P, c_int, P,
-                               P, c_size_t, P]),
+                               c_int, P, P, c_int, c_int64, c_int, c_float, c_float, P, c_float, P,
+                               c_int, P, P, c_size_t, P]),
     "lca_state_append": (c_int, [c_int, c_int, c_int, c_int, c_int, P, P, c_int, P, P, P, c_int, P,
-                                 P, c_int, P, P, P, c_float, P]),
+                                 P, c_int, P, P, P, c_float, c_float, P]),
     "lca_decode_workspace_size": (c_size_t, [ctypes.POINTER(DecodeLayer)]),
     "lca_decode_step": (c_int, [ctypes.POINTER(DecodeLayer), ctypes.POINTER(DecodeIO), P, c_size_t,
                                 P]),

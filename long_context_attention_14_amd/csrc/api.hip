@@ -1,6 +1,7 @@
 // C ABI of the CSA/HCA attention library: host-side validation, workspace
 // sizing and dispatch to the kernels.  Validation runs before any HIP call, so
 // a rejected call enqueues nothing; no entry point throws, aborts or prints.
+#include <cmath>
 #include <cstdio>
 #include <cstdarg>
 #include <string>
@@ -28,6 +29,10 @@ int hip_status(hipError_t e, const char* what) {
 
 bool io_fmt_ok(int f) { return f == LCA_F32 || f == LCA_BF16; }
 bool kv_fmt_ok(int f) { return f == LCA_F32 || f == LCA_BF16 || f == LCA_KV_FP8_BF16ROPE; }
+// Partial RoPE base: 0 (off) or a finite base above 1; the kernels take its log2.
+bool rope_ok(float base) { return base == 0.f || (std::isfinite(base) && base > 1.f); }
+double rope_lb(float base) { return base == 0.f ? 0.0 : std::log2(static_cast<double>(base)); }
+
 bool c_ok(int c) { return c >= 128 && c <= 1024 && c % 64 == 0 && (c / 64 == 2 || c / 64 == 4 || c / 64 == 8 || c / 64 == 16); }
 
 #define REQUIRE(cond, ...)                                         \
@@ -67,8 +72,10 @@ size_t lca_kv_row_bytes(int kv_dtype, int c) {
 
 int lca_compress(int mode, int m, int B, int n_new, int c, const void* C, const void* Z,
                  int io_dtype, const void* prevC, const void* prevZ, const float* P, void* cache,
-                 int kv_dtype, int N_cap, int first_entry, float eps, lca_stream_t stream) {
+                 int kv_dtype, int N_cap, int first_entry, float eps, float rope_base,
+                 lca_stream_t stream) {
   g_last_error.clear();
+  REQUIRE(rope_ok(rope_base), "rope_base = %g is neither 0 nor a finite value > 1", rope_base);
   REQUIRE(mode == LCA_CSA || mode == LCA_HCA, "mode %d is not LCA_CSA/LCA_HCA", mode);
   REQUIRE(m >= 1 && m <= 4096, "m = %d out of range [1, 4096]", m);
   REQUIRE(B >= 0 && n_new >= 0, "negative batch or token count");
@@ -83,15 +90,19 @@ int lca_compress(int mode, int m, int B, int n_new, int c, const void* C, const 
   if (B == 0 || n_new == 0) return LCA_OK;
   REQUIRE(C && Z && P && cache, "NULL tensor pointer");
   return hip_status(lca::launch_compress(mode, m, B, n_new, c, C, Z, io_dtype, prevC, prevZ, P, cache,
-                                         kv_dtype, N_cap, first_entry, eps,
+                                         kv_dtype, N_cap, first_entry, eps, rope_lb(rope_base),
                                          reinterpret_cast<hipStream_t>(stream)),
                     "lca_compress");
 }
 
 int lca_rmsnorm_rows(int B, int n, int c, const void* x, int x_dtype, void* y, int y_dtype,
-                     int y_seq_rows, float eps, lca_stream_t stream) {
+                     int y_seq_rows, float eps, int64_t pos0, float rope_base,
+                     lca_stream_t stream) {
   g_last_error.clear();
   REQUIRE(B >= 0 && n >= 0, "negative sizes");
+  REQUIRE(rope_ok(rope_base), "rope_base = %g is neither 0 nor a finite value > 1", rope_base);
+  REQUIRE(pos0 >= 0 && pos0 <= (INT64_C(1) << 40), "pos0 = %lld out of range",
+          static_cast<long long>(pos0));
   SUPPORT(c_ok(c), "c = %d unsupported", c);
   SUPPORT(io_fmt_ok(x_dtype), "x_dtype %d unsupported", x_dtype);
   SUPPORT(kv_fmt_ok(y_dtype), "y_dtype %d unsupported", y_dtype);
@@ -99,6 +110,7 @@ int lca_rmsnorm_rows(int B, int n, int c, const void* x, int x_dtype, void* y, i
   if (B == 0 || n == 0) return LCA_OK;
   REQUIRE(x && y, "NULL tensor pointer");
   return hip_status(lca::launch_rmsnorm_rows(B, n, c, x, x_dtype, y, y_dtype, y_seq_rows, eps,
+                                             static_cast<long long>(pos0), rope_lb(rope_base),
                                              reinterpret_cast<hipStream_t>(stream)),
                     "lca_rmsnorm_rows");
 }
@@ -193,9 +205,11 @@ size_t lca_sparse_mqa_workspace_size(int B, int n_q, int H, int c, int kv_dtype,
 int lca_sparse_mqa(int B, int n_q, int H, int c, const void* q, int q_dtype, const void* cache,
                    int kv_dtype, int N_cap, const int32_t* idx, int k, const int32_t* q_pos, int m,
                    const int32_t* n_entries, const void* win, int W_cap, int64_t win_origin,
-                   int n_win, float tau, float eps, const float* sink, void* out, int out_dtype,
-                   float* lse, void* workspace, size_t workspace_bytes, lca_stream_t stream) {
+                   int n_win, float tau, float eps, const float* sink, float rope_base, void* out,
+                   int out_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                   lca_stream_t stream) {
   g_last_error.clear();
+  REQUIRE(rope_ok(rope_base), "rope_base = %g is neither 0 nor a finite value > 1", rope_base);
   REQUIRE(B >= 0 && n_q >= 0 && N_cap >= 0, "negative sizes");
   REQUIRE(m >= 1, "m = %d < 1", m);
   SUPPORT(c == 128 || c == 256 || c == 512, "c = %d unsupported (128, 256 or 512)", c);
@@ -213,18 +227,20 @@ int lca_sparse_mqa(int B, int n_q, int H, int c, const void* q, int q_dtype, con
   if (B == 0 || n_q == 0) return LCA_OK;
   REQUIRE(q && cache && q_pos && n_entries && out, "NULL tensor pointer");
   return hip_status(lca::launch_mqa(B, n_q, H, c, q, q_dtype, cache, kv_dtype, N_cap, idx, k, q_pos,
-                                    m, n_entries, win, W_cap, win_origin, n_win, tau, eps, sink, out,
-                                    out_dtype, lse, workspace, reinterpret_cast<hipStream_t>(stream)),
+                                    m, n_entries, win, W_cap, win_origin, n_win, tau, eps, sink,
+                                    rope_lb(rope_base), out, out_dtype, lse, workspace,
+                                    reinterpret_cast<hipStream_t>(stream)),
                     "lca_sparse_mqa");
 }
 
 int lca_state_append(int mode, int m, int B, int c, int n_win, const void* tokC, const void* tokZ,
                      int io_dtype, void* tailC, void* tailZ, void* ring, int kv_dtype,
                      const float* P, void* cache, int N_cap, int32_t* n_tokens, int32_t* q_pos,
-                     int32_t* n_entries, float eps, lca_stream_t stream) {
+                     int32_t* n_entries, float eps, float rope_base, lca_stream_t stream) {
   g_last_error.clear();
   REQUIRE(mode == LCA_CSA || mode == LCA_HCA, "mode %d is not LCA_CSA/LCA_HCA", mode);
   REQUIRE(m >= 1 && m <= 4096, "m = %d out of range", m);
+  REQUIRE(rope_ok(rope_base), "rope_base = %g is neither 0 nor a finite value > 1", rope_base);
   REQUIRE(B >= 0 && N_cap >= 0, "negative sizes");
   REQUIRE(n_win >= 1, "n_win = %d < 1", n_win);
   SUPPORT(c_ok(c), "c = %d unsupported", c);
@@ -235,7 +251,7 @@ int lca_state_append(int mode, int m, int B, int c, int n_win, const void* tokC,
           "NULL tensor pointer");
   return hip_status(lca::launch_state_append(mode, m, B, c, n_win, tokC, tokZ, io_dtype, tailC,
                                              tailZ, ring, kv_dtype, P, cache, N_cap, n_tokens,
-                                             q_pos, n_entries, eps,
+                                             q_pos, n_entries, eps, rope_lb(rope_base),
                                              reinterpret_cast<hipStream_t>(stream)),
                     "lca_state_append");
 }
@@ -284,6 +300,7 @@ int check_layer(const lca_decode_layer* L) {
   REQUIRE(L->mode == LCA_CSA || L->mode == LCA_HCA, "bad mode");
   REQUIRE(L->B >= 0 && L->N_cap >= 1 && L->m >= 1, "bad sizes");
   if (L->mode == LCA_CSA) REQUIRE(L->k >= 1 && L->k <= 4096, "k = %d out of range", L->k);
+  REQUIRE(rope_ok(L->rope_base), "rope_base = %g is neither 0 nor a finite value > 1", L->rope_base);
   return LCA_OK;
 }
 
@@ -352,7 +369,7 @@ int lca_decode_step(const lca_decode_layer* L, const lca_decode_io* io, void* wo
   st = hip_status(lca::launch_state_append(L->mode, L->m, L->B, L->c, L->n_win, io->tokC, io->tokZ,
                                            L->io_dtype, L->tailC, L->tailZ, L->ring, L->kv_dtype,
                                            L->P, L->cache, L->N_cap, L->n_tokens, q_pos, n_ent,
-                                           L->eps, s, hist, zero_words),
+                                           L->eps, rope_lb(L->rope_base), s, hist, zero_words),
                   "lca_decode_step/append");
   if (st != LCA_OK) return st;
   const int32_t* sel = nullptr;
@@ -390,8 +407,9 @@ int lca_decode_step(const lca_decode_layer* L, const lca_decode_io* io, void* wo
   }
   st = hip_status(lca::launch_mqa(L->B, 1, L->H, L->c, io->q, L->io_dtype, L->cache, L->kv_dtype,
                                   L->N_cap, sel, csa ? L->k : 0, q_pos, L->m, n_ent, L->ring,
-                                  L->n_win, 0, L->n_win, L->tau, L->eps, L->sink, io->out,
-                                  io->out_dtype, io->lse, ws + d.mqa, s),
+                                  L->n_win, 0, L->n_win, L->tau, L->eps, L->sink,
+                                  rope_lb(L->rope_base), io->out, io->out_dtype, io->lse,
+                                  ws + d.mqa, s),
                   "lca_decode_step/mqa");
   if (st != LCA_OK) return st;
   return mark(4);

@@ -61,8 +61,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_generic_kernel(
     int kv_fmt, int N_cap, const int32_t* __restrict__ idx, int k, const int32_t* __restrict__ q_pos,
     int m, const int32_t* __restrict__ n_entries, const uint8_t* __restrict__ win, int W_cap,
     long long win_origin, int n_win, float tau, float eps, const float* __restrict__ sink,
-    int n_splits, int split_rows, uint8_t* __restrict__ out, int out_fmt, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_lse) {
+    double rope_lb, int n_splits, int split_rows, uint8_t* __restrict__ out, int out_fmt,
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
   constexpr int C = CPL * 64;
   constexpr int CP = C + 1;                    // padded LDS row stride (floats)
   constexpr int OPT = kHG * C / kAttnThreads;  // outputs per thread
@@ -108,7 +108,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_generic_kernel(
     ss = wave_sum(ss);
     const float r = rsqrt_hw(ss / static_cast<float>(c) + eps);
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) qs[hh * CP + lane * CPL + i] = v[i] * r;
+    for (int i = 0; i < CPL; ++i) v[i] *= r;
+    rope_lane<CPL>(v, lane, c, sc.t, rope_lb);  // the query turned to its position
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) qs[hh * CP + lane * CPL + i] = v[i];
   }
 
   const int my_h = tid / TPH;
@@ -183,7 +186,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_generic_kernel(
     const size_t orow = (static_cast<size_t>(row) * H + h) * row_bytes(out_fmt, c);
     for (int i = 0; i < OPT; ++i) {
       const int d = my_d0 + i * TPH;
-      const float v = o[i] * inv * f;
+      float v = o[i] * inv * f;
+      if (rope_lb != 0.0) {
+        // the output turned back by -t; the pair's other dim is in lane tid ^ 1
+        const float other = __shfl_xor(v, 1, 64);
+        const int pd = d - (c - kRopeDims);
+        if (pd >= 0) {
+          const float2 cs = rope_cs(-static_cast<long long>(sc.t), pd >> 1, rope_lb);
+          v = (d & 1) ? other * cs.y + v * cs.x : v * cs.x - other * cs.y;
+        }
+      }
       if (out_fmt == LCA_F32)
         reinterpret_cast<float*>(out + orow)[d] = v;
       else
@@ -268,9 +280,10 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     int N_cap, const int32_t* __restrict__ idx, int k, const int32_t* __restrict__ q_pos, int m,
     const int32_t* __restrict__ n_entries, const uint8_t* __restrict__ win, int W_cap,
     long long win_origin, int n_win, float tau, float eps, const float* __restrict__ sink,
-    int n_splits, int split_rows, uint8_t* __restrict__ out, int out_fmt, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_lse) {
+    double rope_lb, int n_splits, int split_rows, uint8_t* __restrict__ out, int out_fmt,
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(16))) uint16_t q_s[kMH * kQS];
+  __shared__ float2 rope_s[kRopeDims / 2];  // (cos, sin) of the query position's angles
   __shared__ __attribute__((aligned(16))) uint16_t kv_s[kMT * kQS];
   __shared__ float s_s[kMH * kSS];
   __shared__ __attribute__((aligned(16))) uint16_t p_s[kMH * kPS];
@@ -302,7 +315,17 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
   // row pointers of the first tile; its row loads are issued before the query
   // phase so that both latencies overlap
   if (tid < kMT) rowp_s[0][tid] = s_begin + tid < s_end ? slot_row(sc, s_begin + tid) : nullptr;
+  if (rope_lb != 0.0 && tid >= kMT && tid < kMT + kRopeDims / 2)
+    rope_s[tid - kMT] = rope_cs(sc.t, tid - kMT, rope_lb);
   __syncthreads();
+  // the rotary pairs of a lane's 8 dims [8 lane, +8) turned to the query position
+  auto rope8 = [&](float* v) {
+    if (rope_lb != 0.0 && lane >= (kMC - kRopeDims) / 8) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        rope_turn(v[2 * e], v[2 * e + 1], rope_s[4 * (lane - (kMC - kRopeDims) / 8) + e]);
+    }
+  };
   uint4 raw[kMT / 4];
   auto load_tile = [&](int buf) {
 #pragma unroll
@@ -346,11 +369,14 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
       for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
       ss = wave_sum(ss);
       const float r = rsqrt_hw(ss / static_cast<float>(kMC) + eps);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= r;
+      rope8(v);
       uint4 pk;
-      pk.x = pack_bf16(v[0] * r, v[1] * r);
-      pk.y = pack_bf16(v[2] * r, v[3] * r);
-      pk.z = pack_bf16(v[4] * r, v[5] * r);
-      pk.w = pack_bf16(v[6] * r, v[7] * r);
+      pk.x = pack_bf16(v[0], v[1]);
+      pk.y = pack_bf16(v[2], v[3]);
+      pk.z = pack_bf16(v[4], v[5]);
+      pk.w = pack_bf16(v[6], v[7]);
       *reinterpret_cast<uint4*>(&q_s[(wv + 4 * i) * kQS + lane * 8]) = pk;
     }
   } else {
@@ -362,11 +388,14 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
       for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
       ss = wave_sum(ss);
       const float r = rsqrt_hw(ss / static_cast<float>(kMC) + eps);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] *= r;
+      rope8(v);
       uint4 pk;
-      pk.x = pack_bf16(v[0] * r, v[1] * r);
-      pk.y = pack_bf16(v[2] * r, v[3] * r);
-      pk.z = pack_bf16(v[4] * r, v[5] * r);
-      pk.w = pack_bf16(v[6] * r, v[7] * r);
+      pk.x = pack_bf16(v[0], v[1]);
+      pk.y = pack_bf16(v[2], v[3]);
+      pk.z = pack_bf16(v[4], v[5]);
+      pk.w = pack_bf16(v[6], v[7]);
       *reinterpret_cast<uint4*>(&q_s[h * kQS + lane * 8]) = pk;
     }
   }
@@ -541,9 +570,15 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     for (int i = 0; i < 16; ++i) {
       const int chunk = tid + 256 * i;
       const int hl = chunk >> 7, d4 = (chunk & 127) * 4;
-      const float4 v = *reinterpret_cast<const float4*>(&ost[hl * kMC + d4]);
+      float4 v = *reinterpret_cast<const float4*>(&ost[hl * kMC + d4]);
       const int h = 32 * ht + hl;
       if (n_splits == 1) {
+        if (rope_lb != 0.0 && d4 >= kMC - kRopeDims) {  // the output turned back by -t
+          const int pr = (d4 - (kMC - kRopeDims)) >> 1;
+          const float2 c0 = rope_s[pr], c1 = rope_s[pr + 1];
+          rope_turn(v.x, v.y, make_float2(c0.x, -c0.y));
+          rope_turn(v.z, v.w, make_float2(c1.x, -c1.y));
+        }
         const size_t oi = (static_cast<size_t>(row) * kMH + h) * kMC + d4;
         if (out_fmt == LCA_F32) {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + oi) = v;
@@ -607,9 +642,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     const int32_t* __restrict__ idx, int k, const int32_t* __restrict__ q_pos, int m,
     const int32_t* __restrict__ n_entries, const uint8_t* __restrict__ win, int W_cap,
     long long win_origin, int n_win, float tau, float eps, const float* __restrict__ sink,
-    int n_splits, int split_rows, uint8_t* __restrict__ out, int out_fmt, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_lse) {
+    double rope_lb, int n_splits, int split_rows, uint8_t* __restrict__ out, int out_fmt,
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(16))) uint16_t kv_s[2][kMT * kQS];
+  __shared__ float2 rope_s[kRopeDims / 2];  // (cos, sin) of the query position's angles
   __shared__ __attribute__((aligned(16))) uint16_t p_s[kMH * kPS];
   __shared__ float ps_s[2][kMH];
   __shared__ __attribute__((aligned(16))) uint32_t vm_s[2][4];
@@ -712,15 +748,23 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     }
     ss += __shfl_xor(ss, 32, 64);
     if (g == 0) ps_s[kh][head] = ss;
+    if (rope_lb != 0.0 && w == 0 && lane < kRopeDims / 2) rope_s[lane] = rope_cs(sc.t, lane, rope_lb);
     __syncthreads();
     const float r = rsqrt_hw((ps_s[0][head] + ps_s[1][head]) / static_cast<float>(kMC) + eps);
+    // the rotary dims 448..511 (k-steps 12..15 of the kh = 1 waves) turned to the
+    // query position
+    const bool rope_q = rope_lb != 0.0 && kh == 1;
+    constexpr int kRopeStep = (kMC - kRopeDims - 256) / 16;
 #pragma unroll
     for (int ks = 0; ks < kMC / 32; ++ks) {
       uint32_t w4[4] = {qf[ks].x, qf[ks].y, qf[ks].z, qf[ks].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w4[e] = pack_bf16(bf16_to_f32(static_cast<uint16_t>(w4[e] & 0xffffu)) * r,
-                          bf16_to_f32(static_cast<uint16_t>(w4[e] >> 16)) * r);
+      for (int e = 0; e < 4; ++e) {
+        float x = bf16_to_f32(static_cast<uint16_t>(w4[e] & 0xffffu)) * r;
+        float y = bf16_to_f32(static_cast<uint16_t>(w4[e] >> 16)) * r;
+        if (ks >= kRopeStep && rope_q) rope_turn(x, y, rope_s[8 * (ks - kRopeStep) + 4 * g + e]);
+        w4[e] = pack_bf16(x, y);
+      }
       qf[ks] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
     }
   }
@@ -894,7 +938,14 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 #pragma unroll 8
   for (int i = 0; i < kMH * kMC / 4 / 256; ++i) {
     const int c4 = (tid + 256 * i) * 4;
-    const float4 v = *reinterpret_cast<const float4*>(&ost[c4]);
+    float4 v = *reinterpret_cast<const float4*>(&ost[c4]);
+    if (n_splits == 1 && rope_lb != 0.0 && (c4 & (kMC - 1)) >= kMC - kRopeDims) {
+      // the output turned back by -t (a split output is turned by the merge)
+      const int pr = ((c4 & (kMC - 1)) - (kMC - kRopeDims)) >> 1;
+      const float2 c0 = rope_s[pr], c1 = rope_s[pr + 1];
+      rope_turn(v.x, v.y, make_float2(c0.x, -c0.y));
+      rope_turn(v.z, v.w, make_float2(c1.x, -c1.y));
+    }
     if (n_splits > 1) {
       *reinterpret_cast<float4*>(&part_o[obase + c4]) = v;
     } else if (out_fmt == LCA_F32) {
@@ -919,7 +970,7 @@ constexpr int kMergeChunk = 16;
 __global__ __launch_bounds__(256) void attn_merge4_kernel(
     long long rows, int H, int c, int n_splits, const float* __restrict__ part_o,
     const float* __restrict__ part_lse, const float* __restrict__ sink, uint8_t* __restrict__ out,
-    int out_fmt, float* __restrict__ lse) {
+    int out_fmt, float* __restrict__ lse, const int32_t* __restrict__ q_pos, double rope_lb) {
   const int c4n = c / 4;
   const long long gid = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
   if (gid >= rows * H * c4n) return;
@@ -966,7 +1017,13 @@ __global__ __launch_bounds__(256) void attn_merge4_kernel(
     m = mc;
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
-  const float4 o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  float4 o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (rope_lb != 0.0 && d4 >= c - kRopeDims) {  // the output turned back by -t
+    const long long t = q_pos[row];
+    const int pr = (d4 - (c - kRopeDims)) >> 1;
+    rope_turn(o.x, o.y, rope_cs(-t, pr, rope_lb));
+    rope_turn(o.z, o.w, rope_cs(-t, pr + 1, rope_lb));
+  }
   const size_t oi = static_cast<size_t>(rh) * c + d4;
   if (out_fmt == LCA_F32) {
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + oi) = o;
@@ -1042,8 +1099,8 @@ size_t mqa_workspace_bytes(int B, int n_q, int H, int c, int kv_fmt, int k, int 
 hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, const void* cache,
                       int kv_fmt, int N_cap, const int32_t* idx, int k, const int32_t* q_pos, int m,
                       const int32_t* n_entries, const void* win, int W_cap, int64_t win_origin,
-                      int n_win, float tau, float eps, const float* sink, void* out, int out_fmt,
-                      float* lse, void* ws, hipStream_t s) {
+                      int n_win, float tau, float eps, const float* sink, double rope_lb, void* out,
+                      int out_fmt, float* lse, void* ws, hipStream_t s) {
   const long long rows = static_cast<long long>(B) * n_q;
   if (rows == 0) return hipSuccess;
   const int dense = idx == nullptr;
@@ -1061,13 +1118,13 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
       hipLaunchKernelGGL(attn_decode_kernel<LCA_BF16>, grid, dim3(256), 0, s, n_q,
                          static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(cache),
                          N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
-                         static_cast<long long>(win_origin), n_win, tau, eps, sink, p.n_splits,
+                         static_cast<long long>(win_origin), n_win, tau, eps, sink, rope_lb, p.n_splits,
                          p.split_rows, static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
     else
       hipLaunchKernelGGL(attn_decode_kernel<LCA_KV_FP8_BF16ROPE>, grid, dim3(256), 0, s, n_q,
                          static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(cache),
                          N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
-                         static_cast<long long>(win_origin), n_win, tau, eps, sink, p.n_splits,
+                         static_cast<long long>(win_origin), n_win, tau, eps, sink, rope_lb, p.n_splits,
                          p.split_rows, static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
   } else if (p.mfma) {
     const dim3 grid(static_cast<unsigned>(rows * p.n_splits));
@@ -1075,27 +1132,27 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
       hipLaunchKernelGGL(attn_mfma_kernel<LCA_BF16>, grid, dim3(256), 0, s, n_q,
                          static_cast<const uint8_t*>(q), q_fmt, static_cast<const uint8_t*>(cache),
                          N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
-                         static_cast<long long>(win_origin), n_win, tau, eps, sink, p.n_splits,
+                         static_cast<long long>(win_origin), n_win, tau, eps, sink, rope_lb, p.n_splits,
                          p.split_rows, static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
     else
       hipLaunchKernelGGL(attn_mfma_kernel<LCA_KV_FP8_BF16ROPE>, grid, dim3(256), 0, s, n_q,
                          static_cast<const uint8_t*>(q), q_fmt, static_cast<const uint8_t*>(cache),
                          N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
-                         static_cast<long long>(win_origin), n_win, tau, eps, sink, p.n_splits,
+                         static_cast<long long>(win_origin), n_win, tau, eps, sink, rope_lb, p.n_splits,
                          p.split_rows, static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
   } else {
   const dim3 grid(static_cast<unsigned>(rows * (H / kHG) * p.n_splits));
   LCA_ATTN_CPL(c, attn_generic_kernel, grid, dim3(kAttnThreads), n_q, H, c,
                static_cast<const uint8_t*>(q), q_fmt, static_cast<const uint8_t*>(cache), kv_fmt,
                N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
-               static_cast<long long>(win_origin), n_win, tau, eps, sink, p.n_splits, p.split_rows,
+               static_cast<long long>(win_origin), n_win, tau, eps, sink, rope_lb, p.n_splits, p.split_rows,
                static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
   const dim3 g2(static_cast<unsigned>((rows * H * (c / 4) + 255) / 256));
   hipLaunchKernelGGL(attn_merge4_kernel, g2, dim3(256), 0, s, rows, H, c, p.n_splits, part_o,
-                     part_lse, sink, static_cast<uint8_t*>(out), out_fmt, lse);
+                     part_lse, sink, static_cast<uint8_t*>(out), out_fmt, lse, q_pos, rope_lb);
   return hipGetLastError();
 }
 

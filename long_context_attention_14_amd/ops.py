@@ -57,22 +57,23 @@ def lca_kv_row_bytes(kv_fmt: str, c: int) -> int:
 
 
 def lca_compress(mode, m, B, n_new, c, C, Z, io_fmt, prevC, prevZ, P, cache, kv_fmt, N_cap,
-                 first_entry, eps=1e-6, stream=None):
+                 first_entry, eps=1e-6, rope_base=0.0, stream=None):
     io_b = row_bytes(io_fmt, c) * B * n_new
     W = 2 * m if mode == "csa" else m
     args = (MODE[mode], m, B, n_new, c, _ptr(C, io_b, "C"), _ptr(Z, io_b, "Z"), FMT[io_fmt],
             _ptr(prevC, row_bytes(io_fmt, c) * B * m, "prevC", True),
             _ptr(prevZ, row_bytes(io_fmt, c) * B * m, "prevZ", True),
             _ptr(P, 4 * W * c, "P"), _ptr(cache, row_bytes(kv_fmt, c) * B * N_cap, "cache"),
-            FMT[kv_fmt], N_cap, first_entry, eps, _stream(stream))
+            FMT[kv_fmt], N_cap, first_entry, eps, rope_base, _stream(stream))
     return check("lca_compress", lib().lca_compress(*args))
 
 
-def lca_rmsnorm_rows(B, n, c, x, x_fmt, y, y_fmt, y_seq_rows, eps=1e-6, stream=None):
+def lca_rmsnorm_rows(B, n, c, x, x_fmt, y, y_fmt, y_seq_rows, eps=1e-6, pos0=0, rope_base=0.0,
+                     stream=None):
     need_y = row_bytes(y_fmt, c) * ((B - 1) * y_seq_rows + n) if B and n else 0
     return check("lca_rmsnorm_rows", lib().lca_rmsnorm_rows(
         B, n, c, _ptr(x, row_bytes(x_fmt, c) * B * n, "x"), FMT[x_fmt], _ptr(y, need_y, "y"),
-        FMT[y_fmt], y_seq_rows, eps, _stream(stream)))
+        FMT[y_fmt], y_seq_rows, eps, pos0, rope_base, _stream(stream)))
 
 
 def lca_indexer_scores(B, n_q, H_I, d_I, idx_fmt, qI, qI_scale, kI, kI_scale, N_cap, w, q_pos, m,
@@ -130,8 +131,8 @@ def lca_sparse_mqa_workspace_size(B, n_q, H, c, kv_fmt, k, N_cap, n_win, dense) 
 
 
 def lca_sparse_mqa(B, n_q, H, c, q, q_fmt, cache, kv_fmt, N_cap, idx, k, q_pos, m, n_entries, win,
-                   W_cap, win_origin, n_win, tau, eps, sink, out, out_fmt, lse=None, workspace=None,
-                   stream=None):
+                   W_cap, win_origin, n_win, tau, eps, sink, rope_base, out, out_fmt, lse=None,
+                   workspace=None, stream=None):
     dense = idx is None
     need = lca_sparse_mqa_workspace_size(B, n_q, H, c, kv_fmt, k, N_cap, n_win, dense)
     if need and workspace is None:
@@ -142,14 +143,14 @@ def lca_sparse_mqa(B, n_q, H, c, q, q_fmt, cache, kv_fmt, N_cap, idx, k, q_pos, 
         _ptr(cache, kvb * B * N_cap, "cache"), FMT[kv_fmt], N_cap,
         _ptr(idx, 4 * B * n_q * k, "idx", True), k, _ptr(q_pos, 4 * B * n_q, "q_pos"), m,
         _ptr(n_entries, 4 * B, "n_entries"), _ptr(win, kvb * B * W_cap, "win", n_win == 0), W_cap,
-        win_origin, n_win, tau, eps, _ptr(sink, 4 * H, "sink", True),
+        win_origin, n_win, tau, eps, _ptr(sink, 4 * H, "sink", True), rope_base,
         _ptr(out, row_bytes(out_fmt, c) * B * n_q * H, "out"), FMT[out_fmt],
         _ptr(lse, 4 * B * n_q * H, "lse", True), _ptr(workspace, need, "workspace", need == 0), need,
         _stream(stream)))
 
 
 def lca_state_append(mode, m, B, c, n_win, tokC, tokZ, io_fmt, tailC, tailZ, ring, kv_fmt, P, cache,
-                     N_cap, n_tokens, q_pos, n_entries, eps=1e-6, stream=None):
+                     N_cap, n_tokens, q_pos, n_entries, eps=1e-6, rope_base=0.0, stream=None):
     iob = row_bytes(io_fmt, c)
     T = 2 * m if mode == "csa" else m
     kvb = row_bytes(kv_fmt, c)
@@ -158,7 +159,8 @@ def lca_state_append(mode, m, B, c, n_win, tokC, tokZ, io_fmt, tailC, tailZ, rin
         FMT[io_fmt], _ptr(tailC, iob * B * T, "tailC"), _ptr(tailZ, iob * B * T, "tailZ"),
         _ptr(ring, kvb * B * n_win, "ring"), FMT[kv_fmt], _ptr(P, 4 * T * c, "P"),
         _ptr(cache, kvb * B * N_cap, "cache"), N_cap, _ptr(n_tokens, 4 * B, "n_tokens"),
-        _ptr(q_pos, 4 * B, "q_pos"), _ptr(n_entries, 4 * B, "n_entries"), eps, _stream(stream)))
+        _ptr(q_pos, 4 * B, "q_pos"), _ptr(n_entries, 4 * B, "n_entries"), eps, rope_base,
+        _stream(stream)))
 
 
 class DecodeLayerState:
@@ -166,7 +168,7 @@ class DecodeLayerState:
 
     def __init__(self, *, mode, m, B, c, H, n_win, N_cap, io_fmt, kv_fmt, tailC, tailZ, ring, cache,
                  n_tokens, P, sink=None, tau=None, eps=1e-6, k=0, H_I=0, d_I=0, idx_fmt="fp8",
-                 kI=None, kI_scale=None):
+                 kI=None, kI_scale=None, rope_base=0.0):
         T = 2 * m if mode == "csa" else m
         iob, kvb = row_bytes(io_fmt, c), row_bytes(kv_fmt, c)
         self.keep = [tailC, tailZ, ring, cache, n_tokens, P, sink, kI, kI_scale]
@@ -183,6 +185,7 @@ class DecodeLayerState:
         s.sink = _ptr(sink, 4 * H, "sink", True)
         s.tau = c ** -0.5 if tau is None else tau
         s.eps = eps
+        s.rope_base = rope_base
         if mode == "csa":
             mx = idx_fmt == "mxfp4"
             s.k, s.H_I, s.d_I, s.idx_dtype = k, H_I, d_I, FMT[idx_fmt]

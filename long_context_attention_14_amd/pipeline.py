@@ -62,14 +62,14 @@ class PrefillLayer:
         cfg = self.cfg
         ops.lca_compress("csa", self.m, self.B, self.n, self.c, self.C, self.Z, cfg.io_dtype,
                          self.prevC, self.prevZ, self.P, self.cache, cfg.kv_dtype, self.N_cap,
-                         self.n_prefix, cfg.eps)
+                         self.n_prefix, cfg.eps, cfg.rope_base)
 
     def window_kv(self):
         cfg = self.cfg
         rb = ops.row_bytes(cfg.kv_dtype, self.c)
         y = self.win[self.n_pre_win * rb:]
         ops.lca_rmsnorm_rows(self.B, self.n, self.c, self.C, cfg.io_dtype, y, cfg.kv_dtype, self.W_cap,
-                             cfg.eps)
+                             cfg.eps, self.pos0, cfg.rope_base)
 
     def indexer(self):
         cfg = self.cfg
@@ -101,8 +101,8 @@ class PrefillLayer:
         ops.lca_sparse_mqa(self.B, self.n, cfg.H, self.c, self.q, cfg.io_dtype, self.cache,
                            cfg.kv_dtype, self.N_cap, self.idx, cfg.k, self.q_pos, self.m,
                            self.n_entries, self.win, self.W_cap, self.pos0 - self.n_pre_win,
-                           cfg.n_win, cfg.tau, cfg.eps, None, self.out, cfg.io_dtype, self.lse,
-                           self.ws_mqa)
+                           cfg.n_win, cfg.tau, cfg.eps, None, cfg.rope_base, self.out, cfg.io_dtype,
+                           self.lse, self.ws_mqa)
 
     def run(self):
         self.compress()
@@ -140,7 +140,7 @@ class DecodeLayer:
             io_fmt=cfg.io_dtype, kv_fmt=cfg.kv_dtype, tailC=self.tailC, tailZ=self.tailZ,
             ring=self.ring, cache=self.cache, n_tokens=self.n_tokens, P=self.P, sink=self.sink,
             tau=cfg.tau, eps=cfg.eps, k=cfg.k, H_I=cfg.H_I, d_I=cfg.d_I, idx_fmt=cfg.idx_dtype,
-            kI=self.kI, kI_scale=self.kI_scale)
+            kI=self.kI, kI_scale=self.kI_scale, rope_base=cfg.rope_base)
         self.workspace = _empty_bytes(self.state.workspace_size(), device)
 
     def step(self, stream=None):

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.lca_version() == 1
+    assert L.lca_version() == 2
     for st in (0, -1, -2, -3, -4):
         assert L.lca_status_string(st)
     assert L.lca_status_string(7) == b"unknown status"
@@ -56,7 +56,7 @@ def test_compress_validation(L):
         a = {**base, **kw}
         return L.lca_compress(a["mode"], a["m"], a["B"], a["n_new"], a["c"], a["C"], a["Z"], a["io"],
                               a["pc"], a["pz"], a["P"], a["cache"], a["kv"], a["N_cap"], a["first"],
-                              1e-6, None)
+                              1e-6, a.get("rope", 0.0), None)
 
     assert call(mode=5) == _lib.LCA_ERR_INVALID_ARG
     assert call(n_new=6) == _lib.LCA_ERR_INVALID_ARG
@@ -68,6 +68,16 @@ def test_compress_validation(L):
     assert call(C=None) == _lib.LCA_ERR_INVALID_ARG
     assert call(B=0) == _lib.LCA_OK            # nothing to do: no launch
     assert call(mode=1, pc=FAKE, pz=FAKE) == _lib.LCA_ERR_INVALID_ARG
+    # partial RoPE base: 0 (off) or a finite value above 1
+    assert call(rope=0.5) == _lib.LCA_ERR_INVALID_ARG
+    assert b"rope_base" in L.lca_last_error()
+    assert call(rope=float("inf")) == _lib.LCA_ERR_INVALID_ARG
+    assert call(rope=-10000.0) == _lib.LCA_ERR_INVALID_ARG
+    assert call(B=0, rope=10000.0) == _lib.LCA_OK
+    assert L.lca_rmsnorm_rows(1, 4, 128, FAKE, 0, FAKE, 0, 4, 1e-6, -1, 10000.0,
+                              None) == _lib.LCA_ERR_INVALID_ARG            # negative pos0
+    assert L.lca_rmsnorm_rows(1, 4, 128, FAKE, 0, FAKE, 0, 4, 1e-6, 0, 1.0,
+                              None) == _lib.LCA_ERR_INVALID_ARG            # base 1
 
 
 def test_indexer_topk_mqa_validation(L):
@@ -88,7 +98,7 @@ def test_indexer_topk_mqa_validation(L):
                       None) == _lib.LCA_ERR_WORKSPACE
     # attention: shape support and workspace
     args = [1, 1, 64, 512, FAKE, F["bf16"], FAKE, F["bf16"], 1024, FAKE, 1024, FAKE, 4, FAKE, FAKE,
-            128, 0, 128, 0.04, 1e-6, None, FAKE, F["bf16"], None]
+            128, 0, 128, 0.04, 1e-6, None, 0.0, FAKE, F["bf16"], None]
     need = L.lca_sparse_mqa_workspace_size(1, 1, 64, 512, F["bf16"], 1024, 1024, 128, 0)
     assert need > 0
     assert L.lca_sparse_mqa(*args, None, 0, None) == _lib.LCA_ERR_WORKSPACE
@@ -101,12 +111,15 @@ def test_indexer_topk_mqa_validation(L):
     bad = list(args)
     bad[14] = None          # window buffer missing with n_win > 0
     assert L.lca_sparse_mqa(*bad, FAKE, need, None) == _lib.LCA_ERR_INVALID_ARG
+    bad = list(args)
+    bad[21] = float("nan")  # RoPE base
+    assert L.lca_sparse_mqa(*bad, FAKE, need, None) == _lib.LCA_ERR_INVALID_ARG
 
 
 def test_state_and_decode_validation(L):
     F = _lib.FMT
     assert L.lca_state_append(0, 4, 1, 512, 0, FAKE, FAKE, F["bf16"], FAKE, FAKE, FAKE, F["bf16"],
-                              FAKE, FAKE, 8, FAKE, FAKE, FAKE, 1e-6, None) == _lib.LCA_ERR_INVALID_ARG
+                              FAKE, FAKE, 8, FAKE, FAKE, FAKE, 1e-6, 0.0, None) == _lib.LCA_ERR_INVALID_ARG
     lay = _lib.DecodeLayer()
     lay.struct_size = 3                          # wrong struct size
     assert L.lca_decode_workspace_size(ctypes.byref(lay)) == 0
@@ -121,6 +134,10 @@ def test_state_and_decode_validation(L):
                              None) == _lib.LCA_ERR_WORKSPACE
     assert L.lca_decode_step(ctypes.byref(lay), ctypes.byref(io), FAKE, need,
                              None) == _lib.LCA_ERR_INVALID_ARG       # CSA without kI/qI/w
+    lay.rope_base = 0.9
+    assert L.lca_decode_workspace_size(ctypes.byref(lay)) == 0           # bad RoPE base
+    lay.rope_base = 10000.0
+    assert L.lca_decode_workspace_size(ctypes.byref(lay)) == need
     lay.k = 0
     assert L.lca_decode_workspace_size(ctypes.byref(lay)) == 0
 

@@ -228,13 +228,16 @@ def test_indexer_scores_bf16_is_rounded_fp32(fmt, n_q):
 # compressor and window KV
 
 
-@pytest.mark.parametrize("mode,m,io,kv,prev", [("csa", 4, "bf16", "bf16", True),
-                                               ("csa", 4, "f32", "f32", False),
-                                               ("hca", 128, "bf16", "bf16", False),
-                                               ("csa", 4, "bf16", "fp8_bf16rope", True),
-                                               ("hca", 8, "f32", "fp8_bf16rope", False)])
-def test_compress_entries(mode, m, io, kv, prev):
-    say(f"compress {mode} m={m} {io}->{kv} prev={prev}")
+@pytest.mark.parametrize("mode,m,io,kv,prev,rope", [("csa", 4, "bf16", "bf16", True, 0.0),
+                                                    ("csa", 4, "f32", "f32", False, 0.0),
+                                                    ("hca", 128, "bf16", "bf16", False, 0.0),
+                                                    ("csa", 4, "bf16", "fp8_bf16rope", True, 0.0),
+                                                    ("hca", 8, "f32", "fp8_bf16rope", False, 0.0),
+                                                    ("csa", 4, "bf16", "bf16", True, 10000.0),
+                                                    ("csa", 4, "f32", "f32", False, 10000.0),
+                                                    ("hca", 128, "bf16", "fp8_bf16rope", False, 160.0)])
+def test_compress_entries(mode, m, io, kv, prev, rope):
+    say(f"compress {mode} m={m} {io}->{kv} prev={prev} rope={rope}")
     rng = np.random.default_rng(11)
     B, c, n = 2, 512 if kv != "f32" else 128, 4 * m if m > 4 else 1028
     C = enc.encode(rng.standard_normal((B, n, c)), io)
@@ -243,39 +246,50 @@ def test_compress_entries(mode, m, io, kv, prev):
     P = (rng.standard_normal((W, c)) * 0.1).astype(np.float32)
     pC = enc.encode(rng.standard_normal((B, m, c)), io) if prev else None
     pZ = enc.encode(rng.standard_normal((B, m, c)), io) if prev else None
-    first, N_cap = 3, 3 + n // m + 2
+    # with RoPE the chunk starts deep in the sequence (entry positions near 2^21)
+    first = 3 if not rope else (1 << 21) // m
+    N_cap = first + n // m + 2
     rb = ops.row_bytes(kv, c)
     cache = torch.zeros(B * N_cap * rb, dtype=torch.uint8, device=DEV)
     ops.lca_compress(mode, m, B, n, c, T(C), T(Z), io, T(pC) if prev else None,
-                     T(pZ) if prev else None, T(P), cache, kv, N_cap, first)
+                     T(pZ) if prev else None, T(P), cache, kv, N_cap, first, rope_base=rope)
     got = host(cache).reshape(B, N_cap, rb)
     assert np.all(got[:, :first] == 0) and np.all(got[:, first + n // m:] == 0)
     for b in range(B):
         E = O.compress(O.decode(C[b], io), O.decode(Z[b], io), P, m, mode == "csa",
                        O.decode(pC[b], io) if prev else None, O.decode(pZ[b], io) if prev else None)
-        want = O.round_to(O.rmsnorm(E), kv)
+        exact = O.rope(O.rmsnorm(E), O.entry_position(first + np.arange(n // m), m), rope)
+        want = O.round_to(exact, kv)
         bound = O.compress_error_bound(O.decode(C[b], io), O.decode(Z[b], io), P, m, mode == "csa",
                                        O.decode(pC[b], io) if prev else None,
                                        O.decode(pZ[b], io) if prev else None)
+        if rope:
+            bound = O.rope_error_bound(exact, bound)
         gb = got[b, first:first + n // m]
         g = O.decode(gb.view(np.float32) if kv == "f32" else gb.view(np.uint16) if kv == "bf16" else gb, kv)
         OS.assert_within_ulp(g, want, kv, slack=bound, what=f"entries b{b}")
 
 
-@pytest.mark.parametrize("io,kv", [("bf16", "bf16"), ("f32", "f32"), ("bf16", "fp8_bf16rope")])
-def test_rmsnorm_rows(io, kv):
-    say(f"rmsnorm rows {io}->{kv}")
+@pytest.mark.parametrize("io,kv,c,rope", [("bf16", "bf16", 512, 0.0), ("f32", "f32", 512, 0.0),
+                                           ("bf16", "fp8_bf16rope", 512, 0.0),
+                                           ("bf16", "bf16", 512, 10000.0), ("f32", "f32", 128, 10000.0),
+                                           ("bf16", "fp8_bf16rope", 256, 1e6)])
+def test_rmsnorm_rows(io, kv, c, rope):
+    say(f"rmsnorm rows {io}->{kv} c={c} rope={rope}")
     rng = np.random.default_rng(12)
-    B, n, c, ys = 3, 37, 512, 50
+    B, n, ys = 3, 37, 50
+    pos0 = (1 << 20) + 3 if rope else 0
     x = enc.encode(rng.standard_normal((B, n, c)) * 3, io)
     rb = ops.row_bytes(kv, c)
     y = torch.zeros(B * ys * rb, dtype=torch.uint8, device=DEV)
-    ops.lca_rmsnorm_rows(B, n, c, T(x), io, y, kv, ys)
+    ops.lca_rmsnorm_rows(B, n, c, T(x), io, y, kv, ys, pos0=pos0, rope_base=rope)
     got = host(y).reshape(B, ys, rb)
     for b in range(B):
         gb = got[b, :n]
         g = O.decode(gb.view(np.float32) if kv == "f32" else gb.view(np.uint16) if kv == "bf16" else gb, kv)
-        OS.assert_within_ulp(g, O.round_to(O.rmsnorm(O.decode(x[b], io)), kv), kv, what=f"rows b{b}")
+        exact = O.rope(O.rmsnorm(O.decode(x[b], io)), pos0 + np.arange(n), rope)
+        slack = O.rope_error_bound(exact, 0.0) if rope else None
+        OS.assert_within_ulp(g, O.round_to(exact, kv), kv, slack=slack, what=f"rows b{b}")
         assert np.all(got[b, n:] == 0)
 
 
@@ -289,12 +303,15 @@ def _as_bytes(enc_rows, fmt):
 
 
 def _mqa_case(case, rng):
-    c, H, n_win, eps = 512, 64, 128, 1e-6
+    c, H, n_win, eps = (128, 8, 128, 1e-6) if "_c128" in case else (512, 64, 128, 1e-6)
     tau = 1.0 / np.sqrt(c)
     kv = "fp8_bf16rope" if case.startswith("fp8") else "bf16"
+    rope = 10000.0 if "_rope" in case else 0.0
+    q_fmt = "f32" if "_f32q" in case else "bf16"
+    case = case.split("_rope")[0].split("_f32q")[0].split("_c128")[0]
     if case == "rows300":                  # one split per row: the direct-output path
         B, N_cap, k, m = 300, 256, 128, 4
-        q_pos = rng.integers(600, 2000, B)
+        q_pos = rng.integers(600, 2000, B) + (2 ** 21 if rope else 0)
         n_entries = np.minimum((q_pos + 1) // m, N_cap)
     elif case == "bf16_dense":             # HCA: every visible entry, many empty slots
         B, N_cap, k, m = 2, 700, 0, 128
@@ -302,7 +319,7 @@ def _mqa_case(case, rng):
         n_entries = np.array([300, 700])
     else:                                  # CSA: k = 200 selected, -1 padded
         B, N_cap, k, m = 3, 5000, 200, 4
-        q_pos = np.array([5, 4000, 20000])
+        q_pos = np.array([5, 4000, 20000]) + (2 ** 21 if rope else 0)
         n_entries = np.array([2, 1000, 5000])
     vis = np.minimum(np.minimum((q_pos + 1) // m, n_entries), N_cap)
     cache_f = rng.standard_normal((B, N_cap, c))
@@ -337,25 +354,33 @@ def _mqa_case(case, rng):
     sink = rng.standard_normal(H).astype(np.float32) if case in ("fp8_sink", "rows300") else None
     cache_e = enc.encode(cache_f, kv)
     win_e = enc.encode(win_f, kv)
-    q_e = enc.to_bf16_bits(q_f)
+    q_e = enc.encode(q_f, q_fmt)
     return dict(B=B, N_cap=N_cap, k=k, m=m, q_pos=q_pos.astype(np.int32), n_entries=n_entries.astype(np.int32),
                 vis=vis, idx=idx, sink=sink, kv=kv, cache=cache_e, win=win_e, q=q_e, c=c, H=H,
-                n_win=n_win, tau=tau, eps=eps)
+                n_win=n_win, tau=tau, eps=eps, rope=rope, q_fmt=q_fmt)
 
 
-@pytest.mark.parametrize("case", ["bf16_sparse", "fp8_sink", "bf16_dense", "rows300"])
+@pytest.mark.parametrize("case", ["bf16_sparse", "fp8_sink", "bf16_dense", "rows300",
+                                  "bf16_sparse_rope", "fp8_sink_rope", "rows300_rope",
+                                  "rows300_f32q_rope", "bf16_sparse_f32q_rope", "bf16_sparse_c128_rope",
+                                  "rows300_c128_rope"])
 def test_sparse_mqa_decode_shapes(case):
+    """Core attention alone: the decode kernel over splits with the merge, or one
+    split writing the output itself (rows300), the float32-query kernel (_f32q)
+    and the generic kernel (_c128: 8 heads x 128), with partial RoPE (_rope:
+    the query turned to its position, the output turned back, at positions
+    near 2^21)."""
     rng = np.random.default_rng(7)
     t = _mqa_case(case, rng)
     B, H, c, kv = t["B"], t["H"], t["c"], t["kv"]
-    say(f"sparse MQA {case}: B={B} k={t['k']} N_cap={t['N_cap']}")
+    say(f"sparse MQA {case}: B={B} k={t['k']} N_cap={t['N_cap']} c={c} q={t['q_fmt']} rope={t['rope']}")
     out = torch.zeros(B * H * c, dtype=torch.bfloat16, device=DEV)
     lse = torch.zeros(B * H, dtype=torch.float32, device=DEV)
-    ops.lca_sparse_mqa(B, 1, H, c, T(t["q"]), "bf16", T(_as_bytes(t["cache"], kv)), kv, t["N_cap"],
+    ops.lca_sparse_mqa(B, 1, H, c, T(t["q"]), t["q_fmt"], T(_as_bytes(t["cache"], kv)), kv, t["N_cap"],
                        None if t["idx"] is None else T(t["idx"]), t["k"], T(t["q_pos"]), t["m"],
                        T(t["n_entries"]), T(_as_bytes(t["win"], kv)), t["n_win"], 0, t["n_win"],
-                       t["tau"], t["eps"], None if t["sink"] is None else T(t["sink"]), out, "bf16",
-                       lse=lse)
+                       t["tau"], t["eps"], None if t["sink"] is None else T(t["sink"]), t["rope"], out,
+                       "bf16", lse=lse)
     got = out_f64(out).reshape(B, H, c)
     got_lse = host(lse).reshape(B, H)
     check = range(B) if B <= 8 else [0, 1, 2, 150, 298, 299]
@@ -368,8 +393,8 @@ def test_sparse_mqa_decode_shapes(case):
         wpos = O.window_positions(tp, t["n_win"])
         rows = np.concatenate([O.decode(t["cache"][b, sel], kv).reshape(-1, c),
                                O.decode(t["win"][b, wpos % t["n_win"]], kv).reshape(-1, c)])
-        qh = O.rmsnorm(O.decode(t["q"][b], "bf16"), t["eps"])
-        o_ref, lse_ref = O.merge([O.attend(qh, rows, t["tau"])], sink=t["sink"])
+        o_ref, lse_ref = O.core_attention(O.decode(t["q"][b], t["q_fmt"]), [rows], t["tau"], t["eps"], tp,
+                                          sink=t["sink"], rope_base=t["rope"])
         err = np.abs(got[b] - o_ref).max()
         assert err <= OUT_TOL["bf16"], f"b{b}: out err {err:.3g}"
         lerr = np.abs(got_lse[b] - lse_ref).max()
@@ -433,6 +458,19 @@ def test_csa_prefill_chunk_reduced():
     run_prefill_parity(cfg, q)
 
 
+def test_tiny_csa_prefill_end_to_end_rope():
+    cfg = TINY_CSA_PREFILL.with_(rope_base=10000.0)
+    say("tiny CSA prefill fp32 with partial RoPE")
+    run_prefill_parity(cfg, np.arange(cfg.n_new))
+
+
+def test_csa_prefill_chunk_reduced_rope():
+    cfg = CSA_PREFILL_CHUNK.with_(ctx=8192, n_new=1024, rope_base=10000.0)
+    say(f"prefill {cfg.ctx}+{cfg.n_new} with partial RoPE")
+    q = np.concatenate([np.arange(0, 1024, 37), [1023]])
+    run_prefill_parity(cfg, q)
+
+
 def test_csa_prefill_chunk_full_size_sampled():
     cfg = CSA_PREFILL_CHUNK
     say("prefill chunk 8192 on 131072, sampled rows")
@@ -463,7 +501,7 @@ def _decode_parity(cfg, d, seqs, layer=None):
         ref = OS.oracle_decode(cfg, d, b)
         p = int(d["n_tokens"][b])
         OS.assert_within_ulp(O.decode(_stored(ring[b, p % cfg.n_win], kv), kv), ref["window_row"], kv,
-                             what="ring row")
+                             slack=ref["window_row_bound"], what="ring row")
         if ref["new_entry"] is not None:
             s = (p + 1) // m - 1
             OS.assert_within_ulp(O.decode(_stored(cache[b, s], kv), kv), ref["new_entry"], kv,
@@ -495,6 +533,24 @@ def test_csa_decode_reduced(ctx):
     cfg = CSA_DECODE_1M.with_(B=4, ctx=ctx)
     say(f"CSA decode B=4 ctx={ctx}")
     d = gen.decode_inputs(cfg)
+    _decode_parity(cfg, d, range(cfg.B))
+
+
+@pytest.mark.parametrize("kind", ["csa", "hca", "hybrid_csa"])
+def test_decode_rope(kind):
+    """Decode steps with partial RoPE: the ring row and a completed entry turned
+    at the token's position, the query turned, the output turned back."""
+    if kind == "csa":
+        cfg = CSA_DECODE_1M.with_(B=4, ctx=1 << 14, rope_base=10000.0)
+        d = gen.decode_inputs(cfg)
+    elif kind == "hca":
+        cfg = HCA_DECODE.with_(B=4, ctx=1 << 14, rope_base=10000.0)
+        d = gen.decode_inputs(cfg)
+    else:                              # fp8 KV with bf16 RoPE dims, MXFP4 indexer
+        cfg = HYBRID_DECODE_1M.with_(ctx=1 << 16, rope_base=10000.0)
+        d = gen.hybrid_inputs(cfg)[2]
+        assert d["kind"] == "C"
+    say(f"decode with RoPE: {cfg.name} B={cfg.B} ctx={cfg.ctx}")
     _decode_parity(cfg, d, range(cfg.B))
 
 
@@ -559,9 +615,13 @@ def test_hybrid_decode_reduced_all_layers():
         _decode_parity(lc, d, range(cfg.B))
 
 
-def test_decode_multi_step_matches_oracle_stepping():
-    """Nine steps of a CSA and an HCA layer (blocks complete along the way)."""
-    for cfg in (CSA_DECODE_1M.with_(B=2, ctx=4096), HCA_DECODE.with_(B=2, ctx=1024, m=8)):
+@pytest.mark.parametrize("rope", [0.0, 10000.0])
+def test_decode_multi_step_matches_oracle_stepping(rope):
+    """Nine steps of a CSA and an HCA layer (blocks complete along the way, so
+    entries made by the steps, turned at their last token with RoPE, are
+    attended by later steps)."""
+    for cfg in (CSA_DECODE_1M.with_(B=2, ctx=4096, rope_base=rope),
+                HCA_DECODE.with_(B=2, ctx=1024, m=8, rope_base=rope)):
         say(f"multi-step {cfg.name}")
         d = gen.decode_inputs(cfg, extra_entries=4)
         layer = pipeline.DecodeLayer(cfg, d, DEV)
@@ -586,7 +646,8 @@ def test_decode_multi_step_matches_oracle_stepping():
                 r = O.decode_step(states[b], tokC=O.decode(d["tokC"][b], cfg.io_dtype),
                                   tokZ=O.decode(d["tokZ"][b], cfg.io_dtype), P=d["P"],
                                   q=O.decode(d["q"][b], cfg.io_dtype), tau=cfg.tau, eps=cfg.eps,
-                                  kv_fmt=cfg.kv_dtype, out_fmt=cfg.io_dtype, **kw)
+                                  kv_fmt=cfg.kv_dtype, out_fmt=cfg.io_dtype, rope_base=cfg.rope_base,
+                                  **kw)
                 err = np.abs(out[b] - r["out"]).max()
                 assert err <= OUT_TOL[cfg.io_dtype], f"step {step} b{b}: {err:.3g}"
 
