@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--detail", default=None, help="write per-stage timings (JSON) to this file")
+    ap.add_argument("--rope-base", type=float, default=0.0,
+                    help="partial RoPE base for every layer (0: off, as in the workloads above; "
+                         "inputs are then taken as post-RoPE)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before warmup, run one plain device-to-device copy of MIB MiB (a "
                          "kernel of known traffic for scaling rocprofv3 byte counters)")
@@ -162,11 +165,12 @@ def run_decode(args, workload):
     dev = "cuda"
     total_steps = args.warmup + args.steps
     if workload == "hybrid_decode_1m":
-        base = HYBRID_DECODE_1M
+        base = HYBRID_DECODE_1M.with_(rope_base=args.rope_base)
         ds = gen.hybrid_inputs(base, extra_entries=total_steps // base.m + 2)
         cfgs = [base if d["kind"] == "C" else base.with_(m=d["m"]) for d in ds]
     else:
-        base = CSA_DECODE_1M if workload == "csa_decode_1m" else HCA_DECODE
+        base = (CSA_DECODE_1M if workload == "csa_decode_1m" else HCA_DECODE).with_(
+            rope_base=args.rope_base)
         ds = [gen.decode_inputs(base, extra_entries=total_steps // base.m + 2)]
         cfgs = [base]
     layers = [pipeline.DecodeLayer(c, d, dev) for c, d in zip(cfgs, ds)]
@@ -286,7 +290,8 @@ def run_decode(args, workload):
                   "hybrid_decode_1m": "mxfp4 indexer / fp8+bf16 KV / fp32 accumulate"}[workload],
         "data": "synthetic (seeded; N(0,1) and RMS-normalised rows)",
         "config": {"workload": desc, "global_batch": B, "seq_len": int(base.ctx),
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   **({"rope_base": args.rope_base} if args.rope_base else {})},
         "roofline": roof,
         "dominant_kernel_us": dom_time * 1e6,
         "stages_us": {s: float(per[:, j].sum()) * 1e6 for j, s in enumerate(DECODE_STAGES)},
@@ -309,7 +314,7 @@ def run_prefill(args):
     from synth import gen
     from synth.configs import CSA_PREFILL_CHUNK
 
-    cfg = CSA_PREFILL_CHUNK
+    cfg = CSA_PREFILL_CHUNK.with_(rope_base=args.rope_base)
     dev = "cuda"
     d = gen.prefill_inputs(cfg)
     layer = pipeline.PrefillLayer(cfg, d, dev)
@@ -348,7 +353,8 @@ def run_prefill(args):
         "config": {"workload": "csa_prefill_8k_on_128k: 8192 new tokens after a 131072-token "
                                "prefix, m=4 (34816 entries), fp8 indexer 64x128, top-1024, MQA "
                                "64x512 bf16, window 128",
-                   "global_batch": 1, "seq_len": cfg.ctx + cfg.n_new, "parallelism": "single GPU"},
+                   "global_batch": 1, "seq_len": cfg.ctx + cfg.n_new, "parallelism": "single GPU",
+                   **({"rope_base": args.rope_base} if args.rope_base else {})},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / FP8_PEAK_TFLOPS, "traffic": None,
                      "kernel": "indexer_rows_kernel<fp8>"},

@@ -29,9 +29,12 @@ int hip_status(hipError_t e, const char* what) {
 
 bool io_fmt_ok(int f) { return f == LCA_F32 || f == LCA_BF16; }
 bool kv_fmt_ok(int f) { return f == LCA_F32 || f == LCA_BF16 || f == LCA_KV_FP8_BF16ROPE; }
-// Partial RoPE base: 0 (off) or a finite base above 1; the kernels take its log2.
+// Partial RoPE base: 0 (off) or a finite base above 1; the kernels take
+// base^(-2/64), the ratio of neighbouring pairs' frequencies.
 bool rope_ok(float base) { return base == 0.f || (std::isfinite(base) && base > 1.f); }
-double rope_lb(float base) { return base == 0.f ? 0.0 : std::log2(static_cast<double>(base)); }
+double rope_step(float base) {
+  return base == 0.f ? 0.0 : std::pow(static_cast<double>(base), -2.0 / lca::kRopeDims);
+}
 
 bool c_ok(int c) { return c >= 128 && c <= 1024 && c % 64 == 0 && (c / 64 == 2 || c / 64 == 4 || c / 64 == 8 || c / 64 == 16); }
 
@@ -90,7 +93,7 @@ int lca_compress(int mode, int m, int B, int n_new, int c, const void* C, const 
   if (B == 0 || n_new == 0) return LCA_OK;
   REQUIRE(C && Z && P && cache, "NULL tensor pointer");
   return hip_status(lca::launch_compress(mode, m, B, n_new, c, C, Z, io_dtype, prevC, prevZ, P, cache,
-                                         kv_dtype, N_cap, first_entry, eps, rope_lb(rope_base),
+                                         kv_dtype, N_cap, first_entry, eps, rope_step(rope_base),
                                          reinterpret_cast<hipStream_t>(stream)),
                     "lca_compress");
 }
@@ -110,7 +113,7 @@ int lca_rmsnorm_rows(int B, int n, int c, const void* x, int x_dtype, void* y, i
   if (B == 0 || n == 0) return LCA_OK;
   REQUIRE(x && y, "NULL tensor pointer");
   return hip_status(lca::launch_rmsnorm_rows(B, n, c, x, x_dtype, y, y_dtype, y_seq_rows, eps,
-                                             static_cast<long long>(pos0), rope_lb(rope_base),
+                                             static_cast<long long>(pos0), rope_step(rope_base),
                                              reinterpret_cast<hipStream_t>(stream)),
                     "lca_rmsnorm_rows");
 }
@@ -228,7 +231,7 @@ int lca_sparse_mqa(int B, int n_q, int H, int c, const void* q, int q_dtype, con
   REQUIRE(q && cache && q_pos && n_entries && out, "NULL tensor pointer");
   return hip_status(lca::launch_mqa(B, n_q, H, c, q, q_dtype, cache, kv_dtype, N_cap, idx, k, q_pos,
                                     m, n_entries, win, W_cap, win_origin, n_win, tau, eps, sink,
-                                    rope_lb(rope_base), out, out_dtype, lse, workspace,
+                                    rope_step(rope_base), out, out_dtype, lse, workspace,
                                     reinterpret_cast<hipStream_t>(stream)),
                     "lca_sparse_mqa");
 }
@@ -251,7 +254,7 @@ int lca_state_append(int mode, int m, int B, int c, int n_win, const void* tokC,
           "NULL tensor pointer");
   return hip_status(lca::launch_state_append(mode, m, B, c, n_win, tokC, tokZ, io_dtype, tailC,
                                              tailZ, ring, kv_dtype, P, cache, N_cap, n_tokens,
-                                             q_pos, n_entries, eps, rope_lb(rope_base),
+                                             q_pos, n_entries, eps, rope_step(rope_base),
                                              reinterpret_cast<hipStream_t>(stream)),
                     "lca_state_append");
 }
@@ -369,7 +372,7 @@ int lca_decode_step(const lca_decode_layer* L, const lca_decode_io* io, void* wo
   st = hip_status(lca::launch_state_append(L->mode, L->m, L->B, L->c, L->n_win, io->tokC, io->tokZ,
                                            L->io_dtype, L->tailC, L->tailZ, L->ring, L->kv_dtype,
                                            L->P, L->cache, L->N_cap, L->n_tokens, q_pos, n_ent,
-                                           L->eps, rope_lb(L->rope_base), s, hist, zero_words),
+                                           L->eps, rope_step(L->rope_base), s, hist, zero_words),
                   "lca_decode_step/append");
   if (st != LCA_OK) return st;
   const int32_t* sel = nullptr;
@@ -408,7 +411,7 @@ int lca_decode_step(const lca_decode_layer* L, const lca_decode_io* io, void* wo
   st = hip_status(lca::launch_mqa(L->B, 1, L->H, L->c, io->q, L->io_dtype, L->cache, L->kv_dtype,
                                   L->N_cap, sel, csa ? L->k : 0, q_pos, L->m, n_ent, L->ring,
                                   L->n_win, 0, L->n_win, L->tau, L->eps, L->sink,
-                                  rope_lb(L->rope_base), io->out, io->out_dtype, io->lse,
+                                  rope_step(L->rope_base), io->out, io->out_dtype, io->lse,
                                   ws + d.mqa, s),
                   "lca_decode_step/mqa");
   if (st != LCA_OK) return st;

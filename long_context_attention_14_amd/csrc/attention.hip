@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_generic_kernel(
     int kv_fmt, int N_cap, const int32_t* __restrict__ idx, int k, const int32_t* __restrict__ q_pos,
     int m, const int32_t* __restrict__ n_entries, const uint8_t* __restrict__ win, int W_cap,
     long long win_origin, int n_win, float tau, float eps, const float* __restrict__ sink,
-    double rope_lb, int n_splits, int split_rows, uint8_t* __restrict__ out, int out_fmt,
+    double rope_step, int n_splits, int split_rows, uint8_t* __restrict__ out, int out_fmt,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
   constexpr int C = CPL * 64;
   constexpr int CP = C + 1;                    // padded LDS row stride (floats)
@@ -97,6 +97,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_generic_kernel(
   const int s_begin = split * split_rows;
   const int s_end = min(s_begin + split_rows, NT);
 
+  // the query position's angles: lane l holds pair l % 32; rope_s keeps a copy
+  // for the epilogue
+  __shared__ float2 rope_s[kRopeDims / 2];
+  float2 cs_q = make_float2(1.f, 0.f);
+  if (rope_step != 0.0) {
+    cs_q = rope_cs_lane(sc.t, rope_step);
+    if (tid < kRopeDims / 2) rope_s[tid] = cs_q;
+  }
   // normalised queries of this head group (wave wv handles heads wv, wv+4)
   const size_t q_row = row_bytes(q_fmt, c);
   for (int hh = wv; hh < kHG; hh += kAttnThreads / 64) {
@@ -109,7 +117,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_generic_kernel(
     const float r = rsqrt_hw(ss / static_cast<float>(c) + eps);
 #pragma unroll
     for (int i = 0; i < CPL; ++i) v[i] *= r;
-    rope_lane<CPL>(v, lane, c, sc.t, rope_lb);  // the query turned to its position
+    if (rope_step != 0.0) rope_lane<CPL>(v, lane, c, cs_q);  // the query turned to its position
 #pragma unroll
     for (int i = 0; i < CPL; ++i) qs[hh * CP + lane * CPL + i] = v[i];
   }
@@ -184,16 +192,17 @@ __global__ __launch_bounds__(kAttnThreads) void attn_generic_kernel(
       lse_v = sink[h];
     }
     const size_t orow = (static_cast<size_t>(row) * H + h) * row_bytes(out_fmt, c);
+    if (rope_step != 0.0) __syncthreads();  // rope_s written
     for (int i = 0; i < OPT; ++i) {
       const int d = my_d0 + i * TPH;
       float v = o[i] * inv * f;
-      if (rope_lb != 0.0) {
+      if (rope_step != 0.0) {
         // the output turned back by -t; the pair's other dim is in lane tid ^ 1
         const float other = __shfl_xor(v, 1, 64);
         const int pd = d - (c - kRopeDims);
         if (pd >= 0) {
-          const float2 cs = rope_cs(-static_cast<long long>(sc.t), pd >> 1, rope_lb);
-          v = (d & 1) ? other * cs.y + v * cs.x : v * cs.x - other * cs.y;
+          const float2 cs = rope_s[pd >> 1];  // angle t; turned by -t below
+          v = (d & 1) ? v * cs.x - other * cs.y : v * cs.x + other * cs.y;
         }
       }
       if (out_fmt == LCA_F32)
@@ -280,7 +289,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     int N_cap, const int32_t* __restrict__ idx, int k, const int32_t* __restrict__ q_pos, int m,
     const int32_t* __restrict__ n_entries, const uint8_t* __restrict__ win, int W_cap,
     long long win_origin, int n_win, float tau, float eps, const float* __restrict__ sink,
-    double rope_lb, int n_splits, int split_rows, uint8_t* __restrict__ out, int out_fmt,
+    double rope_step, int n_splits, int split_rows, uint8_t* __restrict__ out, int out_fmt,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(16))) uint16_t q_s[kMH * kQS];
   __shared__ float2 rope_s[kRopeDims / 2];  // (cos, sin) of the query position's angles
@@ -315,12 +324,12 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
   // row pointers of the first tile; its row loads are issued before the query
   // phase so that both latencies overlap
   if (tid < kMT) rowp_s[0][tid] = s_begin + tid < s_end ? slot_row(sc, s_begin + tid) : nullptr;
-  if (rope_lb != 0.0 && tid >= kMT && tid < kMT + kRopeDims / 2)
-    rope_s[tid - kMT] = rope_cs(sc.t, tid - kMT, rope_lb);
+  if (rope_step != 0.0 && tid >= kMT && tid < kMT + kRopeDims / 2)
+    rope_s[tid - kMT] = rope_cs(sc.t, tid - kMT, rope_step);
   __syncthreads();
   // the rotary pairs of a lane's 8 dims [8 lane, +8) turned to the query position
   auto rope8 = [&](float* v) {
-    if (rope_lb != 0.0 && lane >= (kMC - kRopeDims) / 8) {
+    if (rope_step != 0.0 && lane >= (kMC - kRopeDims) / 8) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         rope_turn(v[2 * e], v[2 * e + 1], rope_s[4 * (lane - (kMC - kRopeDims) / 8) + e]);
@@ -573,7 +582,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
       float4 v = *reinterpret_cast<const float4*>(&ost[hl * kMC + d4]);
       const int h = 32 * ht + hl;
       if (n_splits == 1) {
-        if (rope_lb != 0.0 && d4 >= kMC - kRopeDims) {  // the output turned back by -t
+        if (rope_step != 0.0 && d4 >= kMC - kRopeDims) {  // the output turned back by -t
           const int pr = (d4 - (kMC - kRopeDims)) >> 1;
           const float2 c0 = rope_s[pr], c1 = rope_s[pr + 1];
           rope_turn(v.x, v.y, make_float2(c0.x, -c0.y));
@@ -642,7 +651,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     const int32_t* __restrict__ idx, int k, const int32_t* __restrict__ q_pos, int m,
     const int32_t* __restrict__ n_entries, const uint8_t* __restrict__ win, int W_cap,
     long long win_origin, int n_win, float tau, float eps, const float* __restrict__ sink,
-    double rope_lb, int n_splits, int split_rows, uint8_t* __restrict__ out, int out_fmt,
+    double rope_step, int n_splits, int split_rows, uint8_t* __restrict__ out, int out_fmt,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(16))) uint16_t kv_s[2][kMT * kQS];
   __shared__ float2 rope_s[kRopeDims / 2];  // (cos, sin) of the query position's angles
@@ -748,12 +757,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     }
     ss += __shfl_xor(ss, 32, 64);
     if (g == 0) ps_s[kh][head] = ss;
-    if (rope_lb != 0.0 && w == 0 && lane < kRopeDims / 2) rope_s[lane] = rope_cs(sc.t, lane, rope_lb);
+    if (rope_step != 0.0 && w == 0 && lane < kRopeDims / 2) rope_s[lane] = rope_cs(sc.t, lane, rope_step);
     __syncthreads();
     const float r = rsqrt_hw((ps_s[0][head] + ps_s[1][head]) / static_cast<float>(kMC) + eps);
     // the rotary dims 448..511 (k-steps 12..15 of the kh = 1 waves) turned to the
     // query position
-    const bool rope_q = rope_lb != 0.0 && kh == 1;
+    const bool rope_q = rope_step != 0.0 && kh == 1;
     constexpr int kRopeStep = (kMC - kRopeDims - 256) / 16;
 #pragma unroll
     for (int ks = 0; ks < kMC / 32; ++ks) {
@@ -939,7 +948,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   for (int i = 0; i < kMH * kMC / 4 / 256; ++i) {
     const int c4 = (tid + 256 * i) * 4;
     float4 v = *reinterpret_cast<const float4*>(&ost[c4]);
-    if (n_splits == 1 && rope_lb != 0.0 && (c4 & (kMC - 1)) >= kMC - kRopeDims) {
+    if (n_splits == 1 && rope_step != 0.0 && (c4 & (kMC - 1)) >= kMC - kRopeDims) {
       // the output turned back by -t (a split output is turned by the merge)
       const int pr = ((c4 & (kMC - 1)) - (kMC - kRopeDims)) >> 1;
       const float2 c0 = rope_s[pr], c1 = rope_s[pr + 1];
@@ -970,9 +979,18 @@ constexpr int kMergeChunk = 16;
 __global__ __launch_bounds__(256) void attn_merge4_kernel(
     long long rows, int H, int c, int n_splits, const float* __restrict__ part_o,
     const float* __restrict__ part_lse, const float* __restrict__ sink, uint8_t* __restrict__ out,
-    int out_fmt, float* __restrict__ lse, const int32_t* __restrict__ q_pos, double rope_lb) {
+    int out_fmt, float* __restrict__ lse, const int32_t* __restrict__ q_pos, double rope_step) {
   const int c4n = c / 4;
   const long long gid = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  // the angles of -t for the output's turn back: a block covers one query row
+  // (H * c / 4 is a multiple of 256, checked by the launcher)
+  __shared__ float2 rope_s[kRopeDims / 2];
+  if (rope_step != 0.0) {
+    const long long row0 = static_cast<long long>(blockIdx.x) * 256 / (static_cast<long long>(H) * c4n);
+    if (threadIdx.x < kRopeDims / 2)
+      rope_s[threadIdx.x] = rope_cs(-static_cast<long long>(q_pos[row0]), threadIdx.x, rope_step);
+    __syncthreads();
+  }
   if (gid >= rows * H * c4n) return;
   const long long rh = gid / c4n;
   const int d4 = static_cast<int>(gid % c4n) * 4;
@@ -1018,11 +1036,10 @@ __global__ __launch_bounds__(256) void attn_merge4_kernel(
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
   float4 o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-  if (rope_lb != 0.0 && d4 >= c - kRopeDims) {  // the output turned back by -t
-    const long long t = q_pos[row];
+  if (rope_step != 0.0 && d4 >= c - kRopeDims) {  // the output turned back by -t
     const int pr = (d4 - (c - kRopeDims)) >> 1;
-    rope_turn(o.x, o.y, rope_cs(-t, pr, rope_lb));
-    rope_turn(o.z, o.w, rope_cs(-t, pr + 1, rope_lb));
+    rope_turn(o.x, o.y, rope_s[pr]);
+    rope_turn(o.z, o.w, rope_s[pr + 1]);
   }
   const size_t oi = static_cast<size_t>(rh) * c + d4;
   if (out_fmt == LCA_F32) {
@@ -1099,7 +1116,7 @@ size_t mqa_workspace_bytes(int B, int n_q, int H, int c, int kv_fmt, int k, int 
 hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, const void* cache,
                       int kv_fmt, int N_cap, const int32_t* idx, int k, const int32_t* q_pos, int m,
                       const int32_t* n_entries, const void* win, int W_cap, int64_t win_origin,
-                      int n_win, float tau, float eps, const float* sink, double rope_lb, void* out,
+                      int n_win, float tau, float eps, const float* sink, double rope_step, void* out,
                       int out_fmt, float* lse, void* ws, hipStream_t s) {
   const long long rows = static_cast<long long>(B) * n_q;
   if (rows == 0) return hipSuccess;
@@ -1118,13 +1135,13 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
       hipLaunchKernelGGL(attn_decode_kernel<LCA_BF16>, grid, dim3(256), 0, s, n_q,
                          static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(cache),
                          N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
-                         static_cast<long long>(win_origin), n_win, tau, eps, sink, rope_lb, p.n_splits,
+                         static_cast<long long>(win_origin), n_win, tau, eps, sink, rope_step, p.n_splits,
                          p.split_rows, static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
     else
       hipLaunchKernelGGL(attn_decode_kernel<LCA_KV_FP8_BF16ROPE>, grid, dim3(256), 0, s, n_q,
                          static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(cache),
                          N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
-                         static_cast<long long>(win_origin), n_win, tau, eps, sink, rope_lb, p.n_splits,
+                         static_cast<long long>(win_origin), n_win, tau, eps, sink, rope_step, p.n_splits,
                          p.split_rows, static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
   } else if (p.mfma) {
     const dim3 grid(static_cast<unsigned>(rows * p.n_splits));
@@ -1132,27 +1149,28 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
       hipLaunchKernelGGL(attn_mfma_kernel<LCA_BF16>, grid, dim3(256), 0, s, n_q,
                          static_cast<const uint8_t*>(q), q_fmt, static_cast<const uint8_t*>(cache),
                          N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
-                         static_cast<long long>(win_origin), n_win, tau, eps, sink, rope_lb, p.n_splits,
+                         static_cast<long long>(win_origin), n_win, tau, eps, sink, rope_step, p.n_splits,
                          p.split_rows, static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
     else
       hipLaunchKernelGGL(attn_mfma_kernel<LCA_KV_FP8_BF16ROPE>, grid, dim3(256), 0, s, n_q,
                          static_cast<const uint8_t*>(q), q_fmt, static_cast<const uint8_t*>(cache),
                          N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
-                         static_cast<long long>(win_origin), n_win, tau, eps, sink, rope_lb, p.n_splits,
+                         static_cast<long long>(win_origin), n_win, tau, eps, sink, rope_step, p.n_splits,
                          p.split_rows, static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
   } else {
   const dim3 grid(static_cast<unsigned>(rows * (H / kHG) * p.n_splits));
   LCA_ATTN_CPL(c, attn_generic_kernel, grid, dim3(kAttnThreads), n_q, H, c,
                static_cast<const uint8_t*>(q), q_fmt, static_cast<const uint8_t*>(cache), kv_fmt,
                N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
-               static_cast<long long>(win_origin), n_win, tau, eps, sink, rope_lb, p.n_splits, p.split_rows,
+               static_cast<long long>(win_origin), n_win, tau, eps, sink, rope_step, p.n_splits, p.split_rows,
                static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
+  if (rope_step != 0.0 && (static_cast<long long>(H) * (c / 4)) % 256 != 0) return hipErrorInvalidValue;
   const dim3 g2(static_cast<unsigned>((rows * H * (c / 4) + 255) / 256));
   hipLaunchKernelGGL(attn_merge4_kernel, g2, dim3(256), 0, s, rows, H, c, p.n_splits, part_o,
-                     part_lse, sink, static_cast<uint8_t*>(out), out_fmt, lse, q_pos, rope_lb);
+                     part_lse, sink, static_cast<uint8_t*>(out), out_fmt, lse, q_pos, rope_step);
   return hipGetLastError();
 }
 

@@ -68,16 +68,22 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
 // only the last kRopeDims dims of queries, KV entries and the attention output
 // carry positions.  Pair i of those dims (c - 64 + 2i, c - 64 + 2i + 1) turns by
 // the angle pos * base^(-2i/64): (x, y) -> (x cos - y sin, x sin + y cos).  The
-// kernels take rope_lb = log2(base), 0 when RoPE is off.
+// kernels take rope_step = base^(-2/64) (pair i's frequency is rope_step^i), 0
+// when RoPE is off.
 constexpr int kRopeDims = 64;
 
-// (cos, sin) of pair i's angle at position pos.  The angle is formed and reduced
-// to [-pi, pi] in float64 (Cody-Waite, 2 pi in two parts): positions reach 2^21
+// (cos, sin) of pair i's angle at position pos.  The frequency rope_step^i
+// (at most 10 float64 products) and the angle are formed and reduced to
+// [-pi, pi] in float64 (Cody-Waite, 2 pi in two parts): positions reach 2^21
 // and beyond, where a float32 angle would be off by a tenth of a radian.  Then
 // float32 sincos of the reduced angle.
-__device__ inline float2 rope_cs(long long pos, int i, double rope_lb) {
-  const double theta = exp2(-static_cast<double>(i) * (2.0 / kRopeDims) * rope_lb);
-  const double a = static_cast<double>(pos) * theta;
+__device__ inline float2 rope_cs(long long pos, int i, double rope_step) {
+  double th = 1.0, sq = rope_step;
+  for (int e = i; e; e >>= 1) {
+    if (e & 1) th *= sq;
+    sq *= sq;
+  }
+  const double a = static_cast<double>(pos) * th;
   const double k = rint(a * 0.15915494309189535);  // a / (2 pi)
   double r = fma(-k, 6.283185307179586, a);
   r = fma(-k, 2.4492935982947064e-16, r);
@@ -94,16 +100,24 @@ __device__ __forceinline__ void rope_turn(float& x, float& y, float2 cs) {
   y = ny;
 }
 
+// Every lane's share of one position's angles: lane l holds pair l % 32
+// (computed once per lane, in parallel; rope_lane reads it by lane shuffles).
+__device__ __forceinline__ float2 rope_cs_lane(long long pos, double rope_step) {
+  return rope_cs(pos, threadIdx.x & 31, rope_step);
+}
+
 // The rotary pairs among a lane's CPL consecutive channels [lane*CPL, +CPL)
-// (CPL even), turned to position pos.
+// (CPL even) turned by the angles in cs_lane (rope_cs_lane of the position).
+// Called by the whole wave (the shuffles need every lane).
 template <int CPL>
-__device__ __forceinline__ void rope_lane(float* v, int lane, int c, long long pos, double rope_lb) {
+__device__ __forceinline__ void rope_lane(float* v, int lane, int c, float2 cs_lane) {
   const int ch0 = lane * CPL;
-  if (rope_lb == 0.0 || ch0 + CPL <= c - kRopeDims) return;
 #pragma unroll
   for (int j = 0; j < CPL; j += 2) {
     const int d = ch0 + j - (c - kRopeDims);
-    if (d >= 0) rope_turn(v[j], v[j + 1], rope_cs(pos, d >> 1, rope_lb));
+    const int pr = d >= 0 ? d >> 1 : 0;
+    const float2 cs = make_float2(__shfl(cs_lane.x, pr, 64), __shfl(cs_lane.y, pr, 64));
+    if (d >= 0) rope_turn(v[j], v[j + 1], cs);
   }
 }
 
@@ -289,20 +303,20 @@ __device__ inline void find_threshold_block(const uint32_t* lh, int want, int* s
 // ---------------------------------------------------------------------------
 // internal launchers (defined next to their kernels, called by the C ABI)
 
-// rope_lb: log2 of the partial-RoPE base, 0 for no RoPE (see rope_cs).
+// rope_step: base^(-2/64) of the partial RoPE, 0 for no RoPE (see rope_cs).
 hipError_t launch_compress(int mode, int m, int B, int n_new, int c, const void* C, const void* Z,
                            int io_fmt, const void* prevC, const void* prevZ, const float* P,
                            void* cache, int kv_fmt, int N_cap, int first_entry, float eps,
-                           double rope_lb, hipStream_t s);
+                           double rope_step, hipStream_t s);
 hipError_t launch_rmsnorm_rows(int B, int n, int c, const void* x, int x_fmt, void* y, int y_fmt,
-                               int y_seq_rows, float eps, long long pos0, double rope_lb,
+                               int y_seq_rows, float eps, long long pos0, double rope_step,
                                hipStream_t s);
 // zero_buf (optional): zero_words uint32 words the kernel clears as a side job.
 hipError_t launch_state_append(int mode, int m, int B, int c, int n_win, const void* tokC,
                                const void* tokZ, int io_fmt, void* tailC, void* tailZ, void* ring,
                                int kv_fmt, const float* P, void* cache, int N_cap,
                                int32_t* n_tokens, int32_t* q_pos, int32_t* n_entries, float eps,
-                               double rope_lb, hipStream_t s, uint32_t* zero_buf = nullptr,
+                               double rope_step, hipStream_t s, uint32_t* zero_buf = nullptr,
                                long long zero_words = 0);
 // Fused indexer + selection workspace (rows = B * n_q, n_blk = ceil(N_cap / 128)).
 // hist must be zero before the indexer runs (select_zero_words(rows) words).  The indexer writes, for every
@@ -356,7 +370,7 @@ size_t mqa_workspace_bytes(int B, int n_q, int H, int c, int kv_fmt, int k, int 
 hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, const void* cache,
                       int kv_fmt, int N_cap, const int32_t* idx, int k, const int32_t* q_pos, int m,
                       const int32_t* n_entries, const void* win, int W_cap, int64_t win_origin,
-                      int n_win, float tau, float eps, const float* sink, double rope_lb, void* out,
+                      int n_win, float tau, float eps, const float* sink, double rope_step, void* out,
                       int out_fmt, float* lse, void* ws, hipStream_t s);
 
 }  // namespace lca

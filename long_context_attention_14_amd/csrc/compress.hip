@@ -70,7 +70,7 @@ template <int CPL, int IOF>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void compress_kernel(
     int csa, int m, int B, int n_new, int c, const uint8_t* C, const uint8_t* Z,
     const uint8_t* prevC, const uint8_t* prevZ, const float* P, uint8_t* cache, int kv_fmt,
-    int N_cap, int first_entry, float eps, double rope_lb) {
+    int N_cap, int first_entry, float eps, double rope_step) {
   constexpr int io_fmt = IOF;
   const int lane = threadIdx.x & (kWave - 1);
   const int n_ent = n_new / m;
@@ -116,7 +116,9 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void compress_kernel(
   float out[CPL];
   pool_finish_norm<CPL>(pool, c, eps, out);
   // RoPE position of an entry: the last token it covers
-  rope_lane<CPL>(out, lane, c, (static_cast<long long>(first_entry) + s + 1) * m - 1, rope_lb);
+  if (rope_step != 0.0)
+    rope_lane<CPL>(out, lane, c,
+                   rope_cs_lane((static_cast<long long>(first_entry) + s + 1) * m - 1, rope_step));
   const size_t kv_row = row_bytes(kv_fmt, c);
   store_row<CPL>(cache + (static_cast<size_t>(b) * N_cap + first_entry + s) * kv_row, kv_fmt, c,
                  lane, out);
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void compress_kernel(
 template <int CPL>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void rmsnorm_rows_kernel(
     int B, int n, int c, const uint8_t* x, int x_fmt, uint8_t* y, int y_fmt, int y_seq_rows,
-    float eps, long long pos0, double rope_lb) {
+    float eps, long long pos0, double rope_step) {
   const int lane = threadIdx.x & (kWave - 1);
   const long long r = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
   if (r >= static_cast<long long>(B) * n) return;
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void rmsnorm_rows_kernel(
   const float rs = rsqrt_hw(ss / static_cast<float>(c) + eps);
 #pragma unroll
   for (int j = 0; j < CPL; ++j) v[j] *= rs;
-  rope_lane<CPL>(v, lane, c, pos0 + i, rope_lb);
+  if (rope_step != 0.0) rope_lane<CPL>(v, lane, c, rope_cs_lane(pos0 + i, rope_step));
   store_row<CPL>(y + (static_cast<size_t>(b) * y_seq_rows + i) * row_bytes(y_fmt, c), y_fmt, c, lane,
                  v);
 }
@@ -158,7 +160,7 @@ template <int CPL, int IOF>
 __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
     int csa, int m, int B, int c, int n_win, const uint8_t* tokC, const uint8_t* tokZ,
     uint8_t* tailC, uint8_t* tailZ, uint8_t* ring, int kv_fmt, const float* P, uint8_t* cache,
-    int N_cap, int32_t* n_tokens, int32_t* q_pos, int32_t* n_entries, float eps, double rope_lb,
+    int N_cap, int32_t* n_tokens, int32_t* q_pos, int32_t* n_entries, float eps, double rope_step,
     uint32_t* zero_buf, long long zero_words) {
   constexpr int io_fmt = IOF;  // compile-time: no format branches around the row loads
   __shared__ float part[kAppendWaves][3][CPL][kWave];  // lane-contiguous: no bank conflicts
@@ -194,6 +196,7 @@ __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
   const int blk = p / m;
   const int half = csa ? (blk & 1) : 0;
   const int row = half * m + p % m;
+  float2 rope_p = make_float2(1.f, 0.f);
   if (wv == 0) {
     store_row<CPL>(tCb + row * io_row, io_fmt, c, lane, tc);
     store_row<CPL>(tZb + row * io_row, io_fmt, c, lane, tz);
@@ -209,7 +212,10 @@ __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
     const float rs = rsqrt_hw(ss / static_cast<float>(c) + eps);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) u[j] *= rs;
-    rope_lane<CPL>(u, lane, c, p, rope_lb);
+    if (rope_step != 0.0) {
+      rope_p = rope_cs_lane(p, rope_step);  // also the angles of an entry this token completes
+      rope_lane<CPL>(u, lane, c, rope_p);
+    }
     store_row<CPL>(ring + (static_cast<size_t>(b) * n_win + p % n_win) * kv_row, kv_fmt, c, lane, u);
     if (lane == 0) {
       n_tokens[b] = p + 1;
@@ -317,7 +323,7 @@ __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
   }
   float out[CPL];
   pool_finish_norm<CPL>(tot, c, eps, out);
-  rope_lane<CPL>(out, lane, c, p, rope_lb);  // the entry's last token is the new one
+  if (rope_step != 0.0) rope_lane<CPL>(out, lane, c, rope_p);  // the entry's last token is p
   if (s < N_cap) store_row<CPL>(cache + (static_cast<size_t>(b) * N_cap + s) * kv_row, kv_fmt, c, lane, out);
 }
 
@@ -341,7 +347,7 @@ __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
 hipError_t launch_compress(int mode, int m, int B, int n_new, int c, const void* C, const void* Z,
                            int io_fmt, const void* prevC, const void* prevZ, const float* P,
                            void* cache, int kv_fmt, int N_cap, int first_entry, float eps,
-                           double rope_lb, hipStream_t s) {
+                           double rope_step, hipStream_t s) {
   const long long n = static_cast<long long>(B) * (n_new / m);
   if (n == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((n + kWavesPerBlock - 1) / kWavesPerBlock));
@@ -354,7 +360,7 @@ hipError_t launch_compress(int mode, int m, int B, int n_new, int c, const void*
   const dim3 block(kWave * kWavesPerBlock);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, block, 0, s, csa, m, B, n_new, c, Cp, Zp, pC, pZ, P, ch, kv_fmt,
-                       N_cap, first_entry, eps, rope_lb);
+                       N_cap, first_entry, eps, rope_step);
   };
   const bool f32 = io_fmt == LCA_F32;
   switch (c / kWave) {
@@ -368,13 +374,13 @@ hipError_t launch_compress(int mode, int m, int B, int n_new, int c, const void*
 }
 
 hipError_t launch_rmsnorm_rows(int B, int n, int c, const void* x, int x_fmt, void* y, int y_fmt,
-                               int y_seq_rows, float eps, long long pos0, double rope_lb,
+                               int y_seq_rows, float eps, long long pos0, double rope_step,
                                hipStream_t s) {
   const long long rows = static_cast<long long>(B) * n;
   if (rows == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((rows + kWavesPerBlock - 1) / kWavesPerBlock));
   LCA_DISPATCH_CPL(c, rmsnorm_rows_kernel, grid, B, n, c, static_cast<const uint8_t*>(x), x_fmt,
-                   static_cast<uint8_t*>(y), y_fmt, y_seq_rows, eps, pos0, rope_lb);
+                   static_cast<uint8_t*>(y), y_fmt, y_seq_rows, eps, pos0, rope_step);
   return hipGetLastError();
 }
 
@@ -382,7 +388,7 @@ hipError_t launch_state_append(int mode, int m, int B, int c, int n_win, const v
                                const void* tokZ, int io_fmt, void* tailC, void* tailZ, void* ring,
                                int kv_fmt, const float* P, void* cache, int N_cap,
                                int32_t* n_tokens, int32_t* q_pos, int32_t* n_entries, float eps,
-                               double rope_lb, hipStream_t s, uint32_t* zero_buf,
+                               double rope_step, hipStream_t s, uint32_t* zero_buf,
                                long long zero_words) {
   if (B == 0) return hipSuccess;
   const dim3 grid(B), block(kWave * kAppendWaves);
@@ -395,7 +401,7 @@ hipError_t launch_state_append(int mode, int m, int B, int c, int n_win, const v
   uint8_t* ch = static_cast<uint8_t*>(cache);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, block, 0, s, csa, m, B, c, n_win, tc, tz, tC, tZ, rg, kv_fmt, P,
-                       ch, N_cap, n_tokens, q_pos, n_entries, eps, rope_lb, zero_buf, zero_words);
+                       ch, N_cap, n_tokens, q_pos, n_entries, eps, rope_step, zero_buf, zero_words);
   };
   const bool f32 = io_fmt == LCA_F32;
   switch (c / kWave) {
