@@ -75,6 +75,8 @@ def parse():
     ap.add_argument("--rope-base", type=float, default=0.0,
                     help="partial RoPE base for every layer (0: off, as in the workloads above; "
                          "inputs are then taken as post-RoPE)")
+    ap.add_argument("--paged", action="store_true",
+                    help="compressed-KV cache in 128-token pages behind a random block table")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before warmup, run one plain device-to-device copy of MIB MiB (a "
                          "kernel of known traffic for scaling rocprofv3 byte counters)")
@@ -173,7 +175,8 @@ def run_decode(args, workload):
             rope_base=args.rope_base)
         ds = [gen.decode_inputs(base, extra_entries=total_steps // base.m + 2)]
         cfgs = [base]
-    layers = [pipeline.DecodeLayer(c, d, dev) for c, d in zip(cfgs, ds)]
+    paged = {"seed": 1} if args.paged else None
+    layers = [pipeline.DecodeLayer(c, d, dev, paged=paged) for c, d in zip(cfgs, ds)]
     B = base.B
     hip = HipEvents()
 
@@ -291,7 +294,8 @@ def run_decode(args, workload):
         "data": "synthetic (seeded; N(0,1) and RMS-normalised rows)",
         "config": {"workload": desc, "global_batch": B, "seq_len": int(base.ctx),
                    "parallelism": "single GPU",
-                   **({"rope_base": args.rope_base} if args.rope_base else {})},
+                   **({"rope_base": args.rope_base} if args.rope_base else {}),
+                   **({"kv_cache": "paged, 128-token pages"} if args.paged else {})},
         "roofline": roof,
         "dominant_kernel_us": dom_time * 1e6,
         "stages_us": {s: float(per[:, j].sum()) * 1e6 for j, s in enumerate(DECODE_STAGES)},
@@ -317,7 +321,7 @@ def run_prefill(args):
     cfg = CSA_PREFILL_CHUNK.with_(rope_base=args.rope_base)
     dev = "cuda"
     d = gen.prefill_inputs(cfg)
-    layer = pipeline.PrefillLayer(cfg, d, dev)
+    layer = pipeline.PrefillLayer(cfg, d, dev, paged={"seed": 1} if args.paged else None)
     stages = [("compress", layer.compress), ("window", layer.window_kv), ("indexer", layer.indexer),
               ("topk", layer.topk), ("attention", layer.attention)]
     _calibrate_copy(args.calibrate_copy, dev)
@@ -354,7 +358,8 @@ def run_prefill(args):
                                "prefix, m=4 (34816 entries), fp8 indexer 64x128, top-1024, MQA "
                                "64x512 bf16, window 128",
                    "global_batch": 1, "seq_len": cfg.ctx + cfg.n_new, "parallelism": "single GPU",
-                   **({"rope_base": args.rope_base} if args.rope_base else {})},
+                   **({"rope_base": args.rope_base} if args.rope_base else {}),
+                   **({"kv_cache": "paged, 128-token pages"} if args.paged else {})},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / FP8_PEAK_TFLOPS, "traffic": None,
                      "kernel": "indexer_rows_kernel<fp8>"},

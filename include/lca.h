@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define LCA_ABI_VERSION 2
+#define LCA_ABI_VERSION 3
 
 /* A hipStream_t. */
 typedef struct ihipStream_t* lca_stream_t;
@@ -101,6 +101,26 @@ enum lca_mode {
   LCA_CSA = 0, /* compressed sparse attention: overlapped m-token blocks, top-k */
   LCA_HCA = 1  /* heavily compressed attention: disjoint m'-token blocks, dense */
 };
+
+/* Paged compressed-KV cache ("DeepSeek V4 Architecture Tricks", section
+ * "Heterogeneous KV Cache Layout": the classical cache of compressed entries is
+ * kept in blocks of lcm(m, m') = 128 tokens, so that CSA and HCA layers share
+ * one block table).  With pages, a cache argument is a pool of n_pages pages of
+ * epp = page_tokens / m entries each ([n_pages, epp, row]); entry e of
+ * sequence b lives in page block_table[b * max_pages + e / epp], row e % epp.
+ * The indexer keys are not paged (they stay [B, N_cap, d_I]).  A NULL
+ * lca_kv_pages pointer (or block_table == NULL in lca_decode_layer) means the
+ * contiguous [B, N_cap, row] layout.  Requirements: page_tokens % m == 0,
+ * N_cap <= max_pages * epp.  The table is device memory the library cannot
+ * inspect on the host: an entry whose page id is outside [0, n_pages) is
+ * treated as absent (never read, never written), so a bad table cannot make a
+ * kernel touch memory outside the pool. */
+typedef struct lca_kv_pages {
+  const int32_t* block_table; /* [B, max_pages] int32 device: physical page of logical page j */
+  int max_pages;              /* logical pages per sequence (row stride of block_table) */
+  int page_tokens;            /* tokens per page (128 = lcm(4, 128) shares a table across layers) */
+  int n_pages;                /* pages in the pool */
+} lca_kv_pages;
 
 /* ABI version (LCA_ABI_VERSION of the built library). */
 int lca_version(void);
@@ -143,11 +163,12 @@ size_t lca_kv_row_bytes(int kv_dtype, int c);
  *   eps          RMSNorm epsilon
  *   rope_base    partial RoPE base (0 = off): the normalised entry
  *                first_entry + s is turned at position (first_entry+s+1)*m - 1
+ *   pages        NULL, or the paged layout of cache (see lca_kv_pages)
  * ------------------------------------------------------------------------- */
 int lca_compress(int mode, int m, int B, int n_new, int c, const void* C, const void* Z,
                  int io_dtype, const void* prevC, const void* prevZ, const float* P,
                  void* cache, int kv_dtype, int N_cap, int first_entry, float eps,
-                 float rope_base, lca_stream_t stream);
+                 float rope_base, const lca_kv_pages* pages, lca_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * lca_rmsnorm_rows -- y[b, i] = cast(x[b, i] / sqrt(mean(x[b, i]^2) + eps)):
@@ -245,6 +266,8 @@ int lca_topk_bf16(int B, int n_q, int N_cap, const uint16_t* scores, const int32
  *   out      [B, n_q, H, c] format out_dtype (F32|BF16); lse [B, n_q, H] or NULL
  *   rope_base  partial RoPE (0 = off): qh is turned to q_pos[b,t] and out[b,t,h]
  *            back by -q_pos[b,t]; the stored rows are taken as turned
+ *   pages    NULL, or the paged layout of cache (see lca_kv_pages); the gather
+ *            reads entry e through the block table
  * Workspace: lca_sparse_mqa_workspace_size(...) bytes (split partials).
  * ------------------------------------------------------------------------- */
 size_t lca_sparse_mqa_workspace_size(int B, int n_q, int H, int c, int kv_dtype, int k,
@@ -254,7 +277,7 @@ int lca_sparse_mqa(int B, int n_q, int H, int c, const void* q, int q_dtype, con
                    int m, const int32_t* n_entries, const void* win, int W_cap,
                    int64_t win_origin, int n_win, float tau, float eps, const float* sink,
                    float rope_base, void* out, int out_dtype, float* lse, void* workspace,
-                   size_t workspace_bytes, lca_stream_t stream);
+                   size_t workspace_bytes, const lca_kv_pages* pages, lca_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * lca_state_append -- decode-time state of uncompressed tokens ("DeepSeek V4
@@ -273,11 +296,13 @@ int lca_sparse_mqa(int B, int n_q, int H, int c, const void* q, int q_dtype, con
  *   cache [B, N_cap, row]; n_tokens, q_pos, n_entries [B] int32 device.
  *   rope_base (0 = off): the ring row and a new entry are turned at position p
  *   (the new entry's last token).
+ *   pages (NULL = contiguous cache): the new entry goes through the block table.
  * ------------------------------------------------------------------------- */
 int lca_state_append(int mode, int m, int B, int c, int n_win, const void* tokC, const void* tokZ,
                      int io_dtype, void* tailC, void* tailZ, void* ring, int kv_dtype,
                      const float* P, void* cache, int N_cap, int32_t* n_tokens, int32_t* q_pos,
-                     int32_t* n_entries, float eps, float rope_base, lca_stream_t stream);
+                     int32_t* n_entries, float eps, float rope_base, const lca_kv_pages* pages,
+                     lca_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * lca_decode_step -- one decode step of one CSA or HCA layer for B sequences:
@@ -304,6 +329,7 @@ typedef struct lca_decode_layer {
   const void* kI;       /* [B, N_cap, d_I] (+ kI_scale for MXFP4) */
   const uint8_t* kI_scale;
   float rope_base;      /* partial RoPE base, 0 = off (as in lca_state_append / lca_sparse_mqa) */
+  lca_kv_pages pages;   /* paged cache (pages.block_table == NULL: contiguous [B, N_cap, row]) */
 } lca_decode_layer;
 
 typedef struct lca_decode_io {
@@ -329,6 +355,18 @@ typedef struct lca_decode_io {
 size_t lca_decode_workspace_size(const lca_decode_layer* layer);
 int lca_decode_step(const lca_decode_layer* layer, const lca_decode_io* io, void* workspace,
                     size_t workspace_bytes, lca_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * lca_decode_steps -- n_steps decode steps of one layer back to back on
+ * `stream` (the serving loop over the state cache: each step appends its token,
+ * compresses a completed block and answers its query, so later steps see the
+ * entries earlier steps made).  io points to n_steps host structs, one per
+ * step (its own token, query, indexer query and outputs); the same workspace
+ * serves every step.  Equivalent to n_steps calls of lca_decode_step; all
+ * steps are validated before the first is enqueued.
+ * ------------------------------------------------------------------------- */
+int lca_decode_steps(const lca_decode_layer* layer, const lca_decode_io* io, int n_steps,
+                     void* workspace, size_t workspace_bytes, lca_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -18,6 +18,10 @@ c_int, c_float, c_void_p, c_size_t, c_int64 = (ctypes.c_int, ctypes.c_float, cty
 P = c_void_p  # every tensor pointer is passed as an address
 
 
+class KvPages(ctypes.Structure):
+    _fields_ = [("block_table", P), ("max_pages", c_int), ("page_tokens", c_int), ("n_pages", c_int)]
+
+
 class DecodeLayer(ctypes.Structure):
     _fields_ = [("struct_size", c_size_t),
                 ("mode", c_int), ("m", c_int), ("B", c_int), ("c", c_int), ("H", c_int),
@@ -25,7 +29,7 @@ class DecodeLayer(ctypes.Structure):
                 ("tailC", P), ("tailZ", P), ("ring", P), ("cache", P), ("n_tokens", P), ("P", P),
                 ("sink", P), ("tau", c_float), ("eps", c_float),
                 ("k", c_int), ("H_I", c_int), ("d_I", c_int), ("idx_dtype", c_int),
-                ("kI", P), ("kI_scale", P), ("rope_base", c_float)]
+                ("kI", P), ("kI_scale", P), ("rope_base", c_float), ("pages", KvPages)]
 
 
 class DecodeIO(ctypes.Structure):
@@ -40,7 +44,7 @@ SIGNATURES = {
     "lca_last_error": (ctypes.c_char_p, []),
     "lca_kv_row_bytes": (c_size_t, [c_int, c_int]),
     "lca_compress": (c_int, [c_int, c_int, c_int, c_int, c_int, P, P, c_int, P, P, P, P, c_int,
-                             c_int, c_int, c_float, c_float, P]),
+                             c_int, c_int, c_float, c_float, ctypes.POINTER(KvPages), P]),
     "lca_rmsnorm_rows": (c_int, [c_int, c_int, c_int, P, c_int, P, c_int, c_int, c_float, c_int64,
                                  c_float, P]),
     "lca_indexer_scores": (c_int, [c_int, c_int, c_int, c_int, c_int, P, P, P, P, c_int, P, P,
@@ -54,12 +58,14 @@ SIGNATURES = {
                                                  c_int, c_int]),
     "lca_sparse_mqa": (c_int, [c_int, c_int, c_int, c_int, P, c_int, P, c_int, c_int, P, c_int, P,
                                c_int, P, P, c_int, c_int64, c_int, c_float, c_float, P, c_float, P,
-                               c_int, P, P, c_size_t, P]),
+                               c_int, P, P, c_size_t, ctypes.POINTER(KvPages), P]),
     "lca_state_append": (c_int, [c_int, c_int, c_int, c_int, c_int, P, P, c_int, P, P, P, c_int, P,
-                                 P, c_int, P, P, P, c_float, c_float, P]),
+                                 P, c_int, P, P, P, c_float, c_float, ctypes.POINTER(KvPages), P]),
     "lca_decode_workspace_size": (c_size_t, [ctypes.POINTER(DecodeLayer)]),
     "lca_decode_step": (c_int, [ctypes.POINTER(DecodeLayer), ctypes.POINTER(DecodeIO), P, c_size_t,
                                 P]),
+    "lca_decode_steps": (c_int, [ctypes.POINTER(DecodeLayer), ctypes.POINTER(DecodeIO), c_int, P,
+                                 c_size_t, P]),
 }
 
 _LIB = None

@@ -48,6 +48,22 @@ bool c_ok(int c) { return c >= 128 && c <= 1024 && c % 64 == 0 && (c / 64 == 2 |
     if (!(cond)) return fail(LCA_ERR_UNSUPPORTED, __VA_ARGS__);    \
   } while (0)
 
+// The device view of an optional paged layout (NULL or no table: contiguous),
+// checked against the entries per sequence it must hold.
+int kv_pages(const lca_kv_pages* in, int m, int N_cap, lca::KvPages* out) {
+  *out = lca::KvPages{nullptr, 0, 1, 0};
+  if (in == nullptr || in->block_table == nullptr) return LCA_OK;
+  REQUIRE(in->page_tokens >= 1 && m >= 1 && in->page_tokens % m == 0,
+          "page_tokens = %d is not a positive multiple of m = %d", in->page_tokens, m);
+  REQUIRE(in->max_pages >= 1 && in->n_pages >= 1, "max_pages and n_pages must be >= 1");
+  const int epp = in->page_tokens / m;
+  REQUIRE(static_cast<long long>(in->max_pages) * epp >= N_cap,
+          "max_pages * entries per page = %lld < N_cap = %d",
+          static_cast<long long>(in->max_pages) * epp, N_cap);
+  *out = lca::KvPages{in->block_table, in->max_pages, epp, in->n_pages};
+  return LCA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -76,8 +92,10 @@ size_t lca_kv_row_bytes(int kv_dtype, int c) {
 int lca_compress(int mode, int m, int B, int n_new, int c, const void* C, const void* Z,
                  int io_dtype, const void* prevC, const void* prevZ, const float* P, void* cache,
                  int kv_dtype, int N_cap, int first_entry, float eps, float rope_base,
-                 lca_stream_t stream) {
+                 const lca_kv_pages* pages, lca_stream_t stream) {
   g_last_error.clear();
+  lca::KvPages pg;
+  if (int st = kv_pages(pages, m, N_cap, &pg)) return st;
   REQUIRE(rope_ok(rope_base), "rope_base = %g is neither 0 nor a finite value > 1", rope_base);
   REQUIRE(mode == LCA_CSA || mode == LCA_HCA, "mode %d is not LCA_CSA/LCA_HCA", mode);
   REQUIRE(m >= 1 && m <= 4096, "m = %d out of range [1, 4096]", m);
@@ -93,7 +111,7 @@ int lca_compress(int mode, int m, int B, int n_new, int c, const void* C, const 
   if (B == 0 || n_new == 0) return LCA_OK;
   REQUIRE(C && Z && P && cache, "NULL tensor pointer");
   return hip_status(lca::launch_compress(mode, m, B, n_new, c, C, Z, io_dtype, prevC, prevZ, P, cache,
-                                         kv_dtype, N_cap, first_entry, eps, rope_step(rope_base),
+                                         kv_dtype, N_cap, first_entry, eps, rope_step(rope_base), pg,
                                          reinterpret_cast<hipStream_t>(stream)),
                     "lca_compress");
 }
@@ -210,8 +228,11 @@ int lca_sparse_mqa(int B, int n_q, int H, int c, const void* q, int q_dtype, con
                    const int32_t* n_entries, const void* win, int W_cap, int64_t win_origin,
                    int n_win, float tau, float eps, const float* sink, float rope_base, void* out,
                    int out_dtype, float* lse, void* workspace, size_t workspace_bytes,
-                   lca_stream_t stream) {
+                   const lca_kv_pages* pages, lca_stream_t stream) {
   g_last_error.clear();
+  lca::KvPages pg;
+  REQUIRE(m >= 1, "m = %d < 1", m);
+  if (int st = kv_pages(pages, m, N_cap, &pg)) return st;
   REQUIRE(rope_ok(rope_base), "rope_base = %g is neither 0 nor a finite value > 1", rope_base);
   REQUIRE(B >= 0 && n_q >= 0 && N_cap >= 0, "negative sizes");
   REQUIRE(m >= 1, "m = %d < 1", m);
@@ -231,7 +252,7 @@ int lca_sparse_mqa(int B, int n_q, int H, int c, const void* q, int q_dtype, con
   REQUIRE(q && cache && q_pos && n_entries && out, "NULL tensor pointer");
   return hip_status(lca::launch_mqa(B, n_q, H, c, q, q_dtype, cache, kv_dtype, N_cap, idx, k, q_pos,
                                     m, n_entries, win, W_cap, win_origin, n_win, tau, eps, sink,
-                                    rope_step(rope_base), out, out_dtype, lse, workspace,
+                                    rope_step(rope_base), out, out_dtype, lse, workspace, pg,
                                     reinterpret_cast<hipStream_t>(stream)),
                     "lca_sparse_mqa");
 }
@@ -239,10 +260,13 @@ int lca_sparse_mqa(int B, int n_q, int H, int c, const void* q, int q_dtype, con
 int lca_state_append(int mode, int m, int B, int c, int n_win, const void* tokC, const void* tokZ,
                      int io_dtype, void* tailC, void* tailZ, void* ring, int kv_dtype,
                      const float* P, void* cache, int N_cap, int32_t* n_tokens, int32_t* q_pos,
-                     int32_t* n_entries, float eps, float rope_base, lca_stream_t stream) {
+                     int32_t* n_entries, float eps, float rope_base, const lca_kv_pages* pages,
+                     lca_stream_t stream) {
   g_last_error.clear();
   REQUIRE(mode == LCA_CSA || mode == LCA_HCA, "mode %d is not LCA_CSA/LCA_HCA", mode);
   REQUIRE(m >= 1 && m <= 4096, "m = %d out of range", m);
+  lca::KvPages pg;
+  if (int st = kv_pages(pages, m, N_cap, &pg)) return st;
   REQUIRE(rope_ok(rope_base), "rope_base = %g is neither 0 nor a finite value > 1", rope_base);
   REQUIRE(B >= 0 && N_cap >= 0, "negative sizes");
   REQUIRE(n_win >= 1, "n_win = %d < 1", n_win);
@@ -254,7 +278,7 @@ int lca_state_append(int mode, int m, int B, int c, int n_win, const void* tokC,
           "NULL tensor pointer");
   return hip_status(lca::launch_state_append(mode, m, B, c, n_win, tokC, tokZ, io_dtype, tailC,
                                              tailZ, ring, kv_dtype, P, cache, N_cap, n_tokens,
-                                             q_pos, n_entries, eps, rope_step(rope_base),
+                                             q_pos, n_entries, eps, rope_step(rope_base), pg,
                                              reinterpret_cast<hipStream_t>(stream)),
                     "lca_state_append");
 }
@@ -304,7 +328,8 @@ int check_layer(const lca_decode_layer* L) {
   REQUIRE(L->B >= 0 && L->N_cap >= 1 && L->m >= 1, "bad sizes");
   if (L->mode == LCA_CSA) REQUIRE(L->k >= 1 && L->k <= 4096, "k = %d out of range", L->k);
   REQUIRE(rope_ok(L->rope_base), "rope_base = %g is neither 0 nor a finite value > 1", L->rope_base);
-  return LCA_OK;
+  lca::KvPages pg;
+  return kv_pages(&L->pages, L->m, L->N_cap, &pg);
 }
 
 }  // namespace
@@ -314,9 +339,13 @@ size_t lca_decode_workspace_size(const lca_decode_layer* layer) {
   return decode_layout(layer).total;
 }
 
-int lca_decode_step(const lca_decode_layer* L, const lca_decode_io* io, void* workspace,
-                    size_t workspace_bytes, lca_stream_t stream) {
-  g_last_error.clear();
+}  // extern "C"
+
+namespace {
+
+// Every check of one decode step, before anything is enqueued.
+int decode_check(const lca_decode_layer* L, const lca_decode_io* io, const void* workspace,
+                 size_t workspace_bytes) {
   int st = check_layer(L);
   if (st != LCA_OK) return st;
   REQUIRE(io != nullptr && io->struct_size == sizeof(lca_decode_io), "bad io struct");
@@ -325,11 +354,7 @@ int lca_decode_step(const lca_decode_layer* L, const lca_decode_io* io, void* wo
     return fail(LCA_ERR_WORKSPACE, "lca_decode_step needs %zu workspace bytes, got %zu", d.total,
                 workspace ? workspace_bytes : 0);
   if (L->B == 0) return LCA_OK;
-  char* ws = static_cast<char*>(workspace);
-  int32_t* q_pos = reinterpret_cast<int32_t*>(ws + d.q_pos);
-  int32_t* n_ent = reinterpret_cast<int32_t*>(ws + d.n_entries);
   const bool csa = L->mode == LCA_CSA;
-  // validate every stage before launching the first
   SUPPORT(c_ok(L->c) && L->c <= 512, "c = %d unsupported", L->c);
   SUPPORT(io_fmt_ok(L->io_dtype) && kv_fmt_ok(L->kv_dtype) && io_fmt_ok(io->out_dtype),
           "dtype unsupported");
@@ -346,6 +371,20 @@ int lca_decode_step(const lca_decode_layer* L, const lca_decode_io* io, void* wo
     if (L->idx_dtype == LCA_MXFP4) REQUIRE(L->kI_scale && io->qI_scale, "MXFP4 needs scales");
   }
   REQUIRE(io->tokC && io->tokZ && io->q && io->out, "NULL io tensor");
+  return LCA_OK;
+}
+
+// The launches of one decode step (decode_check passed, B > 0).
+int decode_enqueue(const lca_decode_layer* L, const lca_decode_io* io, void* workspace,
+                   lca_stream_t stream) {
+  int st = LCA_OK;
+  const DecodeLayout d = decode_layout(L);
+  lca::KvPages pg;
+  kv_pages(&L->pages, L->m, L->N_cap, &pg);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* q_pos = reinterpret_cast<int32_t*>(ws + d.q_pos);
+  int32_t* n_ent = reinterpret_cast<int32_t*>(ws + d.n_entries);
+  const bool csa = L->mode == LCA_CSA;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   auto mark = [&](int i) -> int {
     if (io->stage_events[i] == nullptr) return LCA_OK;
@@ -372,7 +411,7 @@ int lca_decode_step(const lca_decode_layer* L, const lca_decode_io* io, void* wo
   st = hip_status(lca::launch_state_append(L->mode, L->m, L->B, L->c, L->n_win, io->tokC, io->tokZ,
                                            L->io_dtype, L->tailC, L->tailZ, L->ring, L->kv_dtype,
                                            L->P, L->cache, L->N_cap, L->n_tokens, q_pos, n_ent,
-                                           L->eps, rope_step(L->rope_base), s, hist, zero_words),
+                                           L->eps, rope_step(L->rope_base), pg, s, hist, zero_words),
                   "lca_decode_step/append");
   if (st != LCA_OK) return st;
   const int32_t* sel = nullptr;
@@ -412,10 +451,42 @@ int lca_decode_step(const lca_decode_layer* L, const lca_decode_io* io, void* wo
                                   L->N_cap, sel, csa ? L->k : 0, q_pos, L->m, n_ent, L->ring,
                                   L->n_win, 0, L->n_win, L->tau, L->eps, L->sink,
                                   rope_step(L->rope_base), io->out, io->out_dtype, io->lse,
-                                  ws + d.mqa, s),
+                                  ws + d.mqa, pg, s),
                   "lca_decode_step/mqa");
   if (st != LCA_OK) return st;
   return mark(4);
+}
+
+}  // namespace
+
+extern "C" {
+
+int lca_decode_step(const lca_decode_layer* L, const lca_decode_io* io, void* workspace,
+                    size_t workspace_bytes, lca_stream_t stream) {
+  g_last_error.clear();
+  const int st = decode_check(L, io, workspace, workspace_bytes);
+  if (st != LCA_OK || L->B == 0) return st;
+  return decode_enqueue(L, io, workspace, stream);
+}
+
+int lca_decode_steps(const lca_decode_layer* L, const lca_decode_io* io, int n_steps,
+                     void* workspace, size_t workspace_bytes, lca_stream_t stream) {
+  g_last_error.clear();
+  REQUIRE(n_steps >= 0, "n_steps = %d < 0", n_steps);
+  REQUIRE(n_steps == 0 || io != nullptr, "NULL io array");
+  for (int i = 0; i < n_steps; ++i) {
+    const int st = decode_check(L, io + i, workspace, workspace_bytes);
+    if (st != LCA_OK) {
+      g_last_error = "step " + std::to_string(i) + ": " + g_last_error;
+      return st;
+    }
+  }
+  if (n_steps == 0 || L->B == 0) return LCA_OK;
+  for (int i = 0; i < n_steps; ++i) {
+    const int st = decode_enqueue(L, io + i, workspace, stream);
+    if (st != LCA_OK) return st;
+  }
+  return LCA_OK;
 }
 
 }  // extern "C"

@@ -27,6 +27,8 @@ constexpr int kSplitRows = 64;  // slots per split in decode
 
 struct SlotCtx {
   const int32_t* idx;  // [k] for this row, or nullptr (dense)
+  KvPages pg;          // paged cache (pg.bt != nullptr: cache_b is the pool base)
+  int b;               // the row's sequence
   int NS;              // compressed slots
   int vis;             // visible entries
   int N_cap;
@@ -39,12 +41,18 @@ struct SlotCtx {
   size_t kv_row;
 };
 
-// Row pointer of slot i of the candidate list, or nullptr if the slot is empty.
+// Row pointer of slot i of the candidate list, or nullptr if the slot is empty
+// (or its page is outside the pool).
 __device__ __forceinline__ const uint8_t* slot_row(const SlotCtx& s, int i) {
   if (i < s.NS) {
     int e = s.idx ? s.idx[i] : i;
     const int lim = s.vis < s.N_cap ? s.vis : s.N_cap;
     if (e < 0 || e >= lim) return nullptr;
+    if (s.pg.bt) {
+      const int pid = kv_page(s.pg, s.b, e);
+      if (pid < 0) return nullptr;
+      return s.cache_b + (static_cast<size_t>(pid) * s.pg.epp + e % s.pg.epp) * s.kv_row;
+    }
     return s.cache_b + static_cast<size_t>(e) * s.kv_row;
   }
   const int w = i - s.NS;
@@ -62,7 +70,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_generic_kernel(
     int m, const int32_t* __restrict__ n_entries, const uint8_t* __restrict__ win, int W_cap,
     long long win_origin, int n_win, float tau, float eps, const float* __restrict__ sink,
     double rope_step, int n_splits, int split_rows, uint8_t* __restrict__ out, int out_fmt,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse, KvPages pg) {
   constexpr int C = CPL * 64;
   constexpr int CP = C + 1;                    // padded LDS row stride (floats)
   constexpr int OPT = kHG * C / kAttnThreads;  // outputs per thread
@@ -89,7 +97,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_generic_kernel(
   sc.N_cap = N_cap;
   sc.n_win = n_win;
   sc.kv_row = row_bytes(kv_fmt, c);
-  sc.cache_b = cache + static_cast<size_t>(b) * N_cap * sc.kv_row;
+  sc.pg = pg;
+  sc.b = b;
+  sc.cache_b = pg.bt ? cache : cache + static_cast<size_t>(b) * N_cap * sc.kv_row;
   sc.win_b = win + static_cast<size_t>(b) * W_cap * sc.kv_row;
   sc.W_cap = W_cap;
   sc.win_origin = win_origin;
@@ -290,7 +300,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     const int32_t* __restrict__ n_entries, const uint8_t* __restrict__ win, int W_cap,
     long long win_origin, int n_win, float tau, float eps, const float* __restrict__ sink,
     double rope_step, int n_splits, int split_rows, uint8_t* __restrict__ out, int out_fmt,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse, KvPages pg) {
   __shared__ __attribute__((aligned(16))) uint16_t q_s[kMH * kQS];
   __shared__ float2 rope_s[kRopeDims / 2];  // (cos, sin) of the query position's angles
   __shared__ __attribute__((aligned(16))) uint16_t kv_s[kMT * kQS];
@@ -313,7 +323,9 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
   sc.N_cap = N_cap;
   sc.n_win = n_win;
   sc.kv_row = row_bytes(KVFMT, kMC);
-  sc.cache_b = cache + static_cast<size_t>(b) * N_cap * sc.kv_row;
+  sc.pg = pg;
+  sc.b = b;
+  sc.cache_b = pg.bt ? cache : cache + static_cast<size_t>(b) * N_cap * sc.kv_row;
   sc.win_b = win + static_cast<size_t>(b) * W_cap * sc.kv_row;
   sc.W_cap = W_cap;
   sc.win_origin = win_origin;
@@ -629,12 +641,18 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
 //    a tile goes through the other KV buffer, which is free at that point.
 constexpr float kLazyMax = 8.0f;
 
-// Row of slot i when its index entry e has been loaded already (e unused for
-// window slots); nullptr when the slot is empty.
-__device__ __forceinline__ const uint8_t* slot_row_e(const SlotCtx& s, int i, int e) {
+// Row of slot i when its index entry e (and, paged, the page pid of e) has
+// been loaded already (both unused for window slots); nullptr when the slot is
+// empty.
+template <bool PAGED>
+__device__ __forceinline__ const uint8_t* slot_row_e(const SlotCtx& s, int i, int e, int pid) {
   if (i < s.NS) {
     const int lim = s.vis < s.N_cap ? s.vis : s.N_cap;
     if (e < 0 || e >= lim) return nullptr;
+    if (PAGED) {
+      if (pid < 0) return nullptr;
+      return s.cache_b + (static_cast<size_t>(pid) * s.pg.epp + e % s.pg.epp) * s.kv_row;
+    }
     return s.cache_b + static_cast<size_t>(e) * s.kv_row;
   }
   const int w = i - s.NS;
@@ -645,14 +663,14 @@ __device__ __forceinline__ const uint8_t* slot_row_e(const SlotCtx& s, int i, in
   return s.win_b + static_cast<size_t>(slot) * s.kv_row;
 }
 
-template <int KVFMT>
+template <int KVFMT, bool PAGED>
 __global__ __launch_bounds__(256) void attn_decode_kernel(
     int n_q, const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int N_cap,
     const int32_t* __restrict__ idx, int k, const int32_t* __restrict__ q_pos, int m,
     const int32_t* __restrict__ n_entries, const uint8_t* __restrict__ win, int W_cap,
     long long win_origin, int n_win, float tau, float eps, const float* __restrict__ sink,
     double rope_step, int n_splits, int split_rows, uint8_t* __restrict__ out, int out_fmt,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse, KvPages pg) {
   __shared__ __attribute__((aligned(16))) uint16_t kv_s[2][kMT * kQS];
   __shared__ float2 rope_s[kRopeDims / 2];  // (cos, sin) of the query position's angles
   __shared__ __attribute__((aligned(16))) uint16_t p_s[kMH * kPS];
@@ -674,7 +692,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   sc.N_cap = N_cap;
   sc.n_win = n_win;
   sc.kv_row = row_bytes(KVFMT, kMC);
-  sc.cache_b = cache + static_cast<size_t>(b) * N_cap * sc.kv_row;
+  sc.pg = pg;
+  sc.b = b;
+  sc.cache_b = pg.bt ? cache : cache + static_cast<size_t>(b) * N_cap * sc.kv_row;
   sc.win_b = win + static_cast<size_t>(b) * W_cap * sc.kv_row;
   sc.W_cap = W_cap;
   sc.win_origin = win_origin;
@@ -690,9 +710,14 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     if (sc.idx) return sc.idx[min(i, sc.NS - 1)];
     return i;
   };
-  auto row_ptr = [&](int tile, int e, uint32_t& mask16) -> const uint8_t* {
+  // paged: the page of an entry (clamped into the sequence's table; ignored for
+  // window slots and empty entries)
+  auto page_of = [&](int e) -> int {
+    return kv_page(sc.pg, b, min(max(e, 0), sc.N_cap - 1));
+  };
+  auto row_ptr = [&](int tile, int e, int pid, uint32_t& mask16) -> const uint8_t* {
     const int i = s_begin + kMT * tile + my_r;
-    const uint8_t* p = i < s_end ? slot_row_e(sc, i, e) : nullptr;
+    const uint8_t* p = i < s_end ? slot_row_e<PAGED>(sc, i, e, pid) : nullptr;
     mask16 = static_cast<uint32_t>(__ballot(p != nullptr)) & 0xffffu;
     return p ? p : sc.cache_b;
   };
@@ -724,11 +749,13 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     if (lane == 0) vm_s[buf][w] = mask16;
   };
 
-  // issue order: the index entries of the first two tiles, the query fragments,
-  // then (once the entries are in) the first tile's rows.  Vector loads complete
-  // in order for the wait counter, so each wait covers only what it needs.
+  // issue order: the index entries of the first two tiles (paged: three), the
+  // query fragments, (paged: the pages of the first two tiles' entries,) then the
+  // first tile's rows.  Vector loads complete in order for the wait counter, so
+  // each wait covers only what it needs.
   const int e_first = entry(0);
   int e_next = entry(1);
+  int e_next2 = PAGED ? entry(2) : 0;
   sc.t = q_pos[row];
   sc.vis = visible_entries(sc.t, m, n_entries[b], N_cap);
   uint4 qf[kMC / 32];
@@ -738,7 +765,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     for (int ks = 0; ks < kMC / 32; ++ks) qf[ks] = *reinterpret_cast<const uint4*>(qh + 16 * ks);
   }
   uint32_t mask_cur;
-  load_rows(row_ptr(0, e_first, mask_cur));
+  int pid_first = 0, pid_next = 0;
+  if constexpr (PAGED) {
+    pid_first = page_of(e_first);
+    pid_next = page_of(e_next);
+  }
+  load_rows(row_ptr(0, e_first, pid_first, mask_cur));
 
   // RMSNorm of the query over its 512 dims: lane halves and the two waves of a
   // head half hold a quarter each; the wave sums go through LDS
@@ -791,10 +823,17 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     const int buf = t & 1;
     stage(buf, mask_cur);
     // the next tile's row pointers (entries loaded one tile ago) and the entries
-    // of the tile after it
+    // of the tile after it.  Paged: entries run two tiles ahead and their pages
+    // one tile ahead, so no lookup waits.
     uint32_t mask_next = 0;
-    const uint8_t* p_next = row_ptr(t + 1, e_next, mask_next);
-    e_next = entry(t + 2);
+    const uint8_t* p_next = row_ptr(t + 1, e_next, pid_next, mask_next);
+    if constexpr (PAGED) {
+      pid_next = page_of(e_next2);
+      e_next = e_next2;
+      e_next2 = entry(t + 3);
+    } else {
+      e_next = entry(t + 2);
+    }
     __syncthreads();  // B1: tile t staged (ps_s of the last tile read)
     if (t + 1 < n_tiles) load_rows(p_next);  // in flight during this tile's compute
     mask_cur = mask_next;
@@ -1117,7 +1156,7 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
                       int kv_fmt, int N_cap, const int32_t* idx, int k, const int32_t* q_pos, int m,
                       const int32_t* n_entries, const void* win, int W_cap, int64_t win_origin,
                       int n_win, float tau, float eps, const float* sink, double rope_step, void* out,
-                      int out_fmt, float* lse, void* ws, hipStream_t s) {
+                      int out_fmt, float* lse, void* ws, const KvPages& pg, hipStream_t s) {
   const long long rows = static_cast<long long>(B) * n_q;
   if (rows == 0) return hipSuccess;
   const int dense = idx == nullptr;
@@ -1131,18 +1170,19 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
   }
   if (p.decode) {
     const dim3 grid(static_cast<unsigned>(rows * p.n_splits));
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, n_q, static_cast<const uint16_t*>(q),
+                         static_cast<const uint8_t*>(cache), N_cap, idx, k, q_pos, m, n_entries,
+                         static_cast<const uint8_t*>(win), W_cap, static_cast<long long>(win_origin),
+                         n_win, tau, eps, sink, rope_step, p.n_splits, p.split_rows,
+                         static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse, pg);
+    };
+    const bool paged = pg.bt != nullptr;
     if (kv_fmt == LCA_BF16)
-      hipLaunchKernelGGL(attn_decode_kernel<LCA_BF16>, grid, dim3(256), 0, s, n_q,
-                         static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(cache),
-                         N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
-                         static_cast<long long>(win_origin), n_win, tau, eps, sink, rope_step, p.n_splits,
-                         p.split_rows, static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
+      paged ? go(attn_decode_kernel<LCA_BF16, true>) : go(attn_decode_kernel<LCA_BF16, false>);
     else
-      hipLaunchKernelGGL(attn_decode_kernel<LCA_KV_FP8_BF16ROPE>, grid, dim3(256), 0, s, n_q,
-                         static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(cache),
-                         N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
-                         static_cast<long long>(win_origin), n_win, tau, eps, sink, rope_step, p.n_splits,
-                         p.split_rows, static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
+      paged ? go(attn_decode_kernel<LCA_KV_FP8_BF16ROPE, true>)
+            : go(attn_decode_kernel<LCA_KV_FP8_BF16ROPE, false>);
   } else if (p.mfma) {
     const dim3 grid(static_cast<unsigned>(rows * p.n_splits));
     if (kv_fmt == LCA_BF16)
@@ -1150,20 +1190,20 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
                          static_cast<const uint8_t*>(q), q_fmt, static_cast<const uint8_t*>(cache),
                          N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
                          static_cast<long long>(win_origin), n_win, tau, eps, sink, rope_step, p.n_splits,
-                         p.split_rows, static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
+                         p.split_rows, static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse, pg);
     else
       hipLaunchKernelGGL(attn_mfma_kernel<LCA_KV_FP8_BF16ROPE>, grid, dim3(256), 0, s, n_q,
                          static_cast<const uint8_t*>(q), q_fmt, static_cast<const uint8_t*>(cache),
                          N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
                          static_cast<long long>(win_origin), n_win, tau, eps, sink, rope_step, p.n_splits,
-                         p.split_rows, static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
+                         p.split_rows, static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse, pg);
   } else {
   const dim3 grid(static_cast<unsigned>(rows * (H / kHG) * p.n_splits));
   LCA_ATTN_CPL(c, attn_generic_kernel, grid, dim3(kAttnThreads), n_q, H, c,
                static_cast<const uint8_t*>(q), q_fmt, static_cast<const uint8_t*>(cache), kv_fmt,
                N_cap, idx, k, q_pos, m, n_entries, static_cast<const uint8_t*>(win), W_cap,
                static_cast<long long>(win_origin), n_win, tau, eps, sink, rope_step, p.n_splits, p.split_rows,
-               static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse);
+               static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse, pg);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;

@@ -63,6 +63,33 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
 }
 
 // ---------------------------------------------------------------------------
+// Paged compressed-KV cache ("DeepSeek V4 Architecture Tricks", section
+// "Heterogeneous KV Cache Layout"): entry e of sequence b is row e % epp of
+// page bt[b * max_pages + e / epp] of the pool.  bt == nullptr: the contiguous
+// layout, row b * N_cap + e.
+struct KvPages {
+  const int32_t* bt;
+  int max_pages;  // row stride of bt
+  int epp;        // entries per page
+  int n_pages;    // pages in the pool
+};
+
+// Physical page of entry e (0 <= e < max_pages * epp), or -1 when the table
+// names a page outside the pool.
+__device__ __forceinline__ int kv_page(const KvPages& pg, int b, int e) {
+  const int pid = pg.bt[static_cast<long long>(b) * pg.max_pages + e / pg.epp];
+  return (pid >= 0 && pid < pg.n_pages) ? pid : -1;
+}
+
+// Row index (in rows from the cache base) of entry e of sequence b, or -1 when
+// its page is outside the pool.
+__device__ __forceinline__ long long kv_row_of(const KvPages& pg, int b, int N_cap, int e) {
+  if (!pg.bt) return static_cast<long long>(b) * N_cap + e;
+  const int pid = kv_page(pg, b, e);
+  return pid < 0 ? -1 : static_cast<long long>(pid) * pg.epp + e % pg.epp;
+}
+
+// ---------------------------------------------------------------------------
 // Partial RoPE ("DeepSeek V4 Architecture Tricks", section "Partial RoPE 和
 // Attention Sink"; QbitAI article on DeepSeek-V4, hybrid attention section):
 // only the last kRopeDims dims of queries, KV entries and the attention output
@@ -307,7 +334,7 @@ __device__ inline void find_threshold_block(const uint32_t* lh, int want, int* s
 hipError_t launch_compress(int mode, int m, int B, int n_new, int c, const void* C, const void* Z,
                            int io_fmt, const void* prevC, const void* prevZ, const float* P,
                            void* cache, int kv_fmt, int N_cap, int first_entry, float eps,
-                           double rope_step, hipStream_t s);
+                           double rope_step, const KvPages& pg, hipStream_t s);
 hipError_t launch_rmsnorm_rows(int B, int n, int c, const void* x, int x_fmt, void* y, int y_fmt,
                                int y_seq_rows, float eps, long long pos0, double rope_step,
                                hipStream_t s);
@@ -316,8 +343,8 @@ hipError_t launch_state_append(int mode, int m, int B, int c, int n_win, const v
                                const void* tokZ, int io_fmt, void* tailC, void* tailZ, void* ring,
                                int kv_fmt, const float* P, void* cache, int N_cap,
                                int32_t* n_tokens, int32_t* q_pos, int32_t* n_entries, float eps,
-                               double rope_step, hipStream_t s, uint32_t* zero_buf = nullptr,
-                               long long zero_words = 0);
+                               double rope_step, const KvPages& pg, hipStream_t s,
+                               uint32_t* zero_buf = nullptr, long long zero_words = 0);
 // Fused indexer + selection workspace (rows = B * n_q, n_blk = ceil(N_cap / 128)).
 // hist must be zero before the indexer runs (select_zero_words(rows) words).  The indexer writes, for every
 // 128-entry block that holds visible entries, the (key, index) pairs of that
@@ -371,6 +398,6 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
                       int kv_fmt, int N_cap, const int32_t* idx, int k, const int32_t* q_pos, int m,
                       const int32_t* n_entries, const void* win, int W_cap, int64_t win_origin,
                       int n_win, float tau, float eps, const float* sink, double rope_step, void* out,
-                      int out_fmt, float* lse, void* ws, hipStream_t s);
+                      int out_fmt, float* lse, void* ws, const KvPages& pg, hipStream_t s);
 
 }  // namespace lca

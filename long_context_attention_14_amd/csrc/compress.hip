@@ -70,7 +70,7 @@ template <int CPL, int IOF>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void compress_kernel(
     int csa, int m, int B, int n_new, int c, const uint8_t* C, const uint8_t* Z,
     const uint8_t* prevC, const uint8_t* prevZ, const float* P, uint8_t* cache, int kv_fmt,
-    int N_cap, int first_entry, float eps, double rope_step) {
+    int N_cap, int first_entry, float eps, double rope_step, KvPages pg) {
   constexpr int io_fmt = IOF;
   const int lane = threadIdx.x & (kWave - 1);
   const int n_ent = n_new / m;
@@ -78,6 +78,9 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void compress_kernel(
   if (e >= static_cast<long long>(B) * n_ent) return;
   const int b = static_cast<int>(e / n_ent);
   const int s = static_cast<int>(e % n_ent);
+  // the entry's row in the cache (through the block table when paged), looked
+  // up before the candidate loads
+  const long long out_row = kv_row_of(pg, b, N_cap, first_entry + s);
   const size_t io_row = row_bytes(io_fmt, c);
   const uint8_t* Cb = C + static_cast<size_t>(b) * n_new * io_row;
   const uint8_t* Zb = Z + static_cast<size_t>(b) * n_new * io_row;
@@ -120,8 +123,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void compress_kernel(
     rope_lane<CPL>(out, lane, c,
                    rope_cs_lane((static_cast<long long>(first_entry) + s + 1) * m - 1, rope_step));
   const size_t kv_row = row_bytes(kv_fmt, c);
-  store_row<CPL>(cache + (static_cast<size_t>(b) * N_cap + first_entry + s) * kv_row, kv_fmt, c,
-                 lane, out);
+  if (out_row >= 0) store_row<CPL>(cache + static_cast<size_t>(out_row) * kv_row, kv_fmt, c, lane, out);
 }
 
 template <int CPL>
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
     int csa, int m, int B, int c, int n_win, const uint8_t* tokC, const uint8_t* tokZ,
     uint8_t* tailC, uint8_t* tailZ, uint8_t* ring, int kv_fmt, const float* P, uint8_t* cache,
     int N_cap, int32_t* n_tokens, int32_t* q_pos, int32_t* n_entries, float eps, double rope_step,
-    uint32_t* zero_buf, long long zero_words) {
+    KvPages pg, uint32_t* zero_buf, long long zero_words) {
   constexpr int io_fmt = IOF;  // compile-time: no format branches around the row loads
   __shared__ float part[kAppendWaves][3][CPL][kWave];  // lane-contiguous: no bank conflicts
   const int lane = threadIdx.x & (kWave - 1);
@@ -231,6 +233,9 @@ __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
   // for the first entry); HCA row r is slot r.  The new token's row is taken
   // from registers.
   const int s = (p + 1) / m - 1;
+  // the new entry's row in the cache (through the block table when paged),
+  // looked up before the candidate loads; -1: beyond N_cap or an absent page
+  const long long out_row = (wv == 0 && s < N_cap) ? kv_row_of(pg, b, N_cap, s) : -1;
   Pool pool[CPL];
   pool_init<CPL>(pool);
   float cv[CPL], zv[CPL], pv[CPL];
@@ -324,7 +329,7 @@ __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
   float out[CPL];
   pool_finish_norm<CPL>(tot, c, eps, out);
   if (rope_step != 0.0) rope_lane<CPL>(out, lane, c, rope_p);  // the entry's last token is p
-  if (s < N_cap) store_row<CPL>(cache + (static_cast<size_t>(b) * N_cap + s) * kv_row, kv_fmt, c, lane, out);
+  if (out_row >= 0) store_row<CPL>(cache + static_cast<size_t>(out_row) * kv_row, kv_fmt, c, lane, out);
 }
 
 }  // namespace
@@ -347,7 +352,7 @@ __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
 hipError_t launch_compress(int mode, int m, int B, int n_new, int c, const void* C, const void* Z,
                            int io_fmt, const void* prevC, const void* prevZ, const float* P,
                            void* cache, int kv_fmt, int N_cap, int first_entry, float eps,
-                           double rope_step, hipStream_t s) {
+                           double rope_step, const KvPages& pg, hipStream_t s) {
   const long long n = static_cast<long long>(B) * (n_new / m);
   if (n == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((n + kWavesPerBlock - 1) / kWavesPerBlock));
@@ -360,7 +365,7 @@ hipError_t launch_compress(int mode, int m, int B, int n_new, int c, const void*
   const dim3 block(kWave * kWavesPerBlock);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, block, 0, s, csa, m, B, n_new, c, Cp, Zp, pC, pZ, P, ch, kv_fmt,
-                       N_cap, first_entry, eps, rope_step);
+                       N_cap, first_entry, eps, rope_step, pg);
   };
   const bool f32 = io_fmt == LCA_F32;
   switch (c / kWave) {
@@ -388,8 +393,8 @@ hipError_t launch_state_append(int mode, int m, int B, int c, int n_win, const v
                                const void* tokZ, int io_fmt, void* tailC, void* tailZ, void* ring,
                                int kv_fmt, const float* P, void* cache, int N_cap,
                                int32_t* n_tokens, int32_t* q_pos, int32_t* n_entries, float eps,
-                               double rope_step, hipStream_t s, uint32_t* zero_buf,
-                               long long zero_words) {
+                               double rope_step, const KvPages& pg, hipStream_t s,
+                               uint32_t* zero_buf, long long zero_words) {
   if (B == 0) return hipSuccess;
   const dim3 grid(B), block(kWave * kAppendWaves);
   const int csa = mode == LCA_CSA ? 1 : 0;
@@ -401,7 +406,7 @@ hipError_t launch_state_append(int mode, int m, int B, int c, int n_win, const v
   uint8_t* ch = static_cast<uint8_t*>(cache);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, block, 0, s, csa, m, B, c, n_win, tc, tz, tC, tZ, rg, kv_fmt, P,
-                       ch, N_cap, n_tokens, q_pos, n_entries, eps, rope_step, zero_buf, zero_words);
+                       ch, N_cap, n_tokens, q_pos, n_entries, eps, rope_step, pg, zero_buf, zero_words);
   };
   const bool f32 = io_fmt == LCA_F32;
   switch (c / kWave) {

@@ -13,7 +13,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import FMT, MODE, DecodeIO, DecodeLayer, check, lib
+from ._lib import FMT, MODE, DecodeIO, DecodeLayer, KvPages, check, lib
 
 _ROW_BYTES = {"f32": lambda c: 4 * c, "bf16": lambda c: 2 * c, "fp8": lambda c: c,
               "fp8_bf16rope": lambda c: c + 64, "mxfp4": lambda c: c // 2}
@@ -48,6 +48,31 @@ def _stream(stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def kv_pages(block_table, page_tokens, n_pages, B):
+    """A paged layout of the compressed-KV cache: block_table [B, max_pages] int32
+    (physical page of each logical page), page_tokens tokens per page, n_pages
+    pages in the pool (the cache tensor is then [n_pages, page_tokens / m, row])."""
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be an int32 [B, max_pages] tensor")
+    pg = KvPages()
+    pg.block_table = _ptr(block_table, block_table.numel() * 4, "block_table")
+    pg.max_pages = block_table.shape[1]
+    pg.page_tokens = page_tokens
+    pg.n_pages = n_pages
+    return pg
+
+
+def _cache_rows(N_cap, B, pages, m):
+    """Rows the cache tensor must hold: B * N_cap, or the pool's pages x entries."""
+    if pages is None:
+        return B * N_cap
+    return pages.n_pages * (pages.page_tokens // m)
+
+
+def _pages_ref(pages):
+    return None if pages is None else ctypes.byref(pages)
+
+
 def lca_version() -> int:
     return lib().lca_version()
 
@@ -57,14 +82,14 @@ def lca_kv_row_bytes(kv_fmt: str, c: int) -> int:
 
 
 def lca_compress(mode, m, B, n_new, c, C, Z, io_fmt, prevC, prevZ, P, cache, kv_fmt, N_cap,
-                 first_entry, eps=1e-6, rope_base=0.0, stream=None):
+                 first_entry, eps=1e-6, rope_base=0.0, pages=None, stream=None):
     io_b = row_bytes(io_fmt, c) * B * n_new
     W = 2 * m if mode == "csa" else m
     args = (MODE[mode], m, B, n_new, c, _ptr(C, io_b, "C"), _ptr(Z, io_b, "Z"), FMT[io_fmt],
             _ptr(prevC, row_bytes(io_fmt, c) * B * m, "prevC", True),
             _ptr(prevZ, row_bytes(io_fmt, c) * B * m, "prevZ", True),
-            _ptr(P, 4 * W * c, "P"), _ptr(cache, row_bytes(kv_fmt, c) * B * N_cap, "cache"),
-            FMT[kv_fmt], N_cap, first_entry, eps, rope_base, _stream(stream))
+            _ptr(P, 4 * W * c, "P"), _ptr(cache, row_bytes(kv_fmt, c) * _cache_rows(N_cap, B, pages, m), "cache"),
+            FMT[kv_fmt], N_cap, first_entry, eps, rope_base, _pages_ref(pages), _stream(stream))
     return check("lca_compress", lib().lca_compress(*args))
 
 
@@ -132,7 +157,7 @@ def lca_sparse_mqa_workspace_size(B, n_q, H, c, kv_fmt, k, N_cap, n_win, dense) 
 
 def lca_sparse_mqa(B, n_q, H, c, q, q_fmt, cache, kv_fmt, N_cap, idx, k, q_pos, m, n_entries, win,
                    W_cap, win_origin, n_win, tau, eps, sink, rope_base, out, out_fmt, lse=None,
-                   workspace=None, stream=None):
+                   workspace=None, pages=None, stream=None):
     dense = idx is None
     need = lca_sparse_mqa_workspace_size(B, n_q, H, c, kv_fmt, k, N_cap, n_win, dense)
     if need and workspace is None:
@@ -140,17 +165,18 @@ def lca_sparse_mqa(B, n_q, H, c, q, q_fmt, cache, kv_fmt, N_cap, idx, k, q_pos, 
     kvb = row_bytes(kv_fmt, c)
     return check("lca_sparse_mqa", lib().lca_sparse_mqa(
         B, n_q, H, c, _ptr(q, row_bytes(q_fmt, c) * B * n_q * H, "q"), FMT[q_fmt],
-        _ptr(cache, kvb * B * N_cap, "cache"), FMT[kv_fmt], N_cap,
+        _ptr(cache, kvb * _cache_rows(N_cap, B, pages, m), "cache"), FMT[kv_fmt], N_cap,
         _ptr(idx, 4 * B * n_q * k, "idx", True), k, _ptr(q_pos, 4 * B * n_q, "q_pos"), m,
         _ptr(n_entries, 4 * B, "n_entries"), _ptr(win, kvb * B * W_cap, "win", n_win == 0), W_cap,
         win_origin, n_win, tau, eps, _ptr(sink, 4 * H, "sink", True), rope_base,
         _ptr(out, row_bytes(out_fmt, c) * B * n_q * H, "out"), FMT[out_fmt],
         _ptr(lse, 4 * B * n_q * H, "lse", True), _ptr(workspace, need, "workspace", need == 0), need,
-        _stream(stream)))
+        _pages_ref(pages), _stream(stream)))
 
 
 def lca_state_append(mode, m, B, c, n_win, tokC, tokZ, io_fmt, tailC, tailZ, ring, kv_fmt, P, cache,
-                     N_cap, n_tokens, q_pos, n_entries, eps=1e-6, rope_base=0.0, stream=None):
+                     N_cap, n_tokens, q_pos, n_entries, eps=1e-6, rope_base=0.0, pages=None,
+                     stream=None):
     iob = row_bytes(io_fmt, c)
     T = 2 * m if mode == "csa" else m
     kvb = row_bytes(kv_fmt, c)
@@ -158,9 +184,9 @@ def lca_state_append(mode, m, B, c, n_win, tokC, tokZ, io_fmt, tailC, tailZ, rin
         MODE[mode], m, B, c, n_win, _ptr(tokC, iob * B, "tokC"), _ptr(tokZ, iob * B, "tokZ"),
         FMT[io_fmt], _ptr(tailC, iob * B * T, "tailC"), _ptr(tailZ, iob * B * T, "tailZ"),
         _ptr(ring, kvb * B * n_win, "ring"), FMT[kv_fmt], _ptr(P, 4 * T * c, "P"),
-        _ptr(cache, kvb * B * N_cap, "cache"), N_cap, _ptr(n_tokens, 4 * B, "n_tokens"),
-        _ptr(q_pos, 4 * B, "q_pos"), _ptr(n_entries, 4 * B, "n_entries"), eps, rope_base,
-        _stream(stream)))
+        _ptr(cache, kvb * _cache_rows(N_cap, B, pages, m), "cache"), N_cap,
+        _ptr(n_tokens, 4 * B, "n_tokens"), _ptr(q_pos, 4 * B, "q_pos"),
+        _ptr(n_entries, 4 * B, "n_entries"), eps, rope_base, _pages_ref(pages), _stream(stream)))
 
 
 class DecodeLayerState:
@@ -168,10 +194,10 @@ class DecodeLayerState:
 
     def __init__(self, *, mode, m, B, c, H, n_win, N_cap, io_fmt, kv_fmt, tailC, tailZ, ring, cache,
                  n_tokens, P, sink=None, tau=None, eps=1e-6, k=0, H_I=0, d_I=0, idx_fmt="fp8",
-                 kI=None, kI_scale=None, rope_base=0.0):
+                 kI=None, kI_scale=None, rope_base=0.0, pages=None):
         T = 2 * m if mode == "csa" else m
         iob, kvb = row_bytes(io_fmt, c), row_bytes(kv_fmt, c)
-        self.keep = [tailC, tailZ, ring, cache, n_tokens, P, sink, kI, kI_scale]
+        self.keep = [tailC, tailZ, ring, cache, n_tokens, P, sink, kI, kI_scale, pages]
         s = DecodeLayer()
         s.struct_size = ctypes.sizeof(DecodeLayer)
         s.mode, s.m, s.B, s.c, s.H, s.n_win, s.N_cap = MODE[mode], m, B, c, H, n_win, N_cap
@@ -179,13 +205,15 @@ class DecodeLayerState:
         s.tailC = _ptr(tailC, iob * B * T, "tailC")
         s.tailZ = _ptr(tailZ, iob * B * T, "tailZ")
         s.ring = _ptr(ring, kvb * B * n_win, "ring")
-        s.cache = _ptr(cache, kvb * B * N_cap, "cache")
+        s.cache = _ptr(cache, kvb * _cache_rows(N_cap, B, pages, m), "cache")
         s.n_tokens = _ptr(n_tokens, 4 * B, "n_tokens")
         s.P = _ptr(P, 4 * T * c, "P")
         s.sink = _ptr(sink, 4 * H, "sink", True)
         s.tau = c ** -0.5 if tau is None else tau
         s.eps = eps
         s.rope_base = rope_base
+        if pages is not None:
+            s.pages = pages
         if mode == "csa":
             mx = idx_fmt == "mxfp4"
             s.k, s.H_I, s.d_I, s.idx_dtype = k, H_I, d_I, FMT[idx_fmt]
@@ -200,14 +228,8 @@ class DecodeLayerState:
         return lib().lca_decode_workspace_size(ctypes.byref(self.struct))
 
 
-def lca_decode_step(layer: DecodeLayerState, tokC, tokZ, q, out, out_fmt, qI=None, qI_scale=None,
-                    w=None, lse=None, idx_out=None, workspace=None, stream=None, stage_events=None):
-    """stage_events: optional sequence of 5 raw hipEvent_t handles (ints or None)."""
-    need = layer.workspace_size()
-    if workspace is None:
-        if layer.workspace is None or layer.workspace.numel() < need:
-            layer.workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-        workspace = layer.workspace
+def _decode_io(layer, tokC, tokZ, q, out, out_fmt, qI=None, qI_scale=None, w=None, lse=None,
+               idx_out=None, stage_events=None):
     B, c, H = layer.B, layer.c, layer.H
     iob = row_bytes(layer.io_fmt, c)
     io = DecodeIO()
@@ -227,6 +249,40 @@ def lca_decode_step(layer: DecodeLayerState, tokC, tokZ, q, out, out_fmt, qI=Non
     if stage_events is not None:
         for i, e in enumerate(stage_events):
             io.stage_events[i] = e
+    return io
+
+
+def _decode_workspace(layer, workspace, device):
+    need = layer.workspace_size()
+    if workspace is None:
+        if layer.workspace is None or layer.workspace.numel() < need:
+            layer.workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        workspace = layer.workspace
+    return workspace, need
+
+
+def lca_decode_step(layer: DecodeLayerState, tokC, tokZ, q, out, out_fmt, qI=None, qI_scale=None,
+                    w=None, lse=None, idx_out=None, workspace=None, stream=None, stage_events=None):
+    """stage_events: optional sequence of 5 raw hipEvent_t handles (ints or None)."""
+    workspace, need = _decode_workspace(layer, workspace, q.device)
+    io = _decode_io(layer, tokC, tokZ, q, out, out_fmt, qI, qI_scale, w, lse, idx_out, stage_events)
     return check("lca_decode_step", lib().lca_decode_step(
         ctypes.byref(layer.struct), ctypes.byref(io), _ptr(workspace, need, "workspace"), need,
+        _stream(stream)))
+
+
+def lca_decode_steps(layer: DecodeLayerState, steps, out_fmt, workspace=None, stream=None):
+    """n decode steps back to back: steps is a list of dicts with the per-step
+    tensors of lca_decode_step (tokC, tokZ, q, out, and qI, qI_scale, w, lse,
+    idx_out as the layer needs)."""
+    if not steps:
+        return check("lca_decode_steps", lib().lca_decode_steps(
+            ctypes.byref(layer.struct), None, 0, None, 0, _stream(stream)))
+    workspace, need = _decode_workspace(layer, workspace, steps[0]["q"].device)
+    arr = (DecodeIO * len(steps))()
+    for i, st in enumerate(steps):
+        arr[i] = _decode_io(layer, st["tokC"], st["tokZ"], st["q"], st["out"], out_fmt, st.get("qI"),
+                            st.get("qI_scale"), st.get("w"), st.get("lse"), st.get("idx_out"))
+    return check("lca_decode_steps", lib().lca_decode_steps(
+        ctypes.byref(layer.struct), arr, len(steps), _ptr(workspace, need, "workspace"), need,
         _stream(stream)))

@@ -21,10 +21,47 @@ def _empty_bytes(n, device):
     return torch.empty(max(1, int(n)), dtype=torch.uint8, device=device)
 
 
+# paged compressed-KV cache: host-side layout helpers (setup and read-back only)
+
+def to_pool(cache, epp, block_table, n_pages):
+    """cache [B, N_cap, row] bytes -> pool [n_pages, epp, row] with logical page j
+    of sequence b at physical page block_table[b, j] (unused pool rows zero)."""
+    B, N_cap, rb = cache.shape
+    max_pages = block_table.shape[1]
+    padded = np.zeros((B, max_pages * epp, rb), cache.dtype)
+    padded[:, :N_cap] = cache
+    pool = np.zeros((n_pages, epp, rb), cache.dtype)
+    pool[block_table.reshape(-1)] = padded.reshape(B * max_pages, epp, rb)
+    return pool
+
+
+def from_pool(pool, block_table, N_cap):
+    """The logical [B, N_cap, row] view of a pool."""
+    B, max_pages = block_table.shape
+    epp, rb = pool.shape[1], pool.shape[2]
+    return pool[block_table.reshape(-1)].reshape(B, max_pages * epp, rb)[:, :N_cap]
+
+
+class Paged:
+    """A block table over 128-token pages (lcm of the CSA and HCA rates) and its pool
+    size: n_pages = B * max_pages + extra unused pages."""
+
+    def __init__(self, B, N_cap, m, page_tokens=128, extra=3, seed=0):
+        from synth import gen
+        self.page_tokens, self.epp = page_tokens, page_tokens // m
+        self.max_pages = -(-N_cap // self.epp)
+        self.n_pages = B * self.max_pages + extra
+        self.table = gen.page_table(B, self.max_pages, self.n_pages, seed)
+
+    def struct(self, device):
+        self.table_dev = torch.from_numpy(self.table).to(device)
+        return ops.kv_pages(self.table_dev, self.page_tokens, self.n_pages, self.table.shape[0])
+
+
 class PrefillLayer:
     """CSA prefill of n_new tokens after a prefix of ctx tokens (one chunk)."""
 
-    def __init__(self, cfg, d, device="cuda"):
+    def __init__(self, cfg, d, device="cuda", paged=None):
         self.cfg, self.device = cfg, device
         B, c, m, n = cfg.B, cfg.c, cfg.m, cfg.n_new
         self.B, self.c, self.m, self.n = B, c, m, n
@@ -35,7 +72,16 @@ class PrefillLayer:
         self.C, self.Z, self.P, self.q, self.w = g("C"), g("Z"), g("P"), g("q"), g("w")
         self.prevC, self.prevZ = g("prevC"), g("prevZ")
         self.cache0 = d["cache"]
-        self.cache = g("cache")
+        self.paged, self.pages = None, None
+        if paged is not None:     # the compressed cache as a pool of pages (paged: dict(seed=...))
+            rb0 = ops.row_bytes(cfg.kv_dtype, c)
+            self.paged = Paged(B, self.N_cap, m, seed=paged.get("seed", 0))
+            pool = to_pool(np.ascontiguousarray(d["cache"]).view(np.uint8).reshape(B, self.N_cap, rb0),
+                           self.paged.epp, self.paged.table, self.paged.n_pages)
+            self.cache = _dev(pool, device)
+            self.pages = self.paged.struct(device)
+        else:
+            self.cache = g("cache")
         self.kI, self.qI = g("kI"), g("qI")
         self.kI_scale, self.qI_scale = g("kI_scale"), g("qI_scale")
         self.n_pre_win = 0 if "win_prefix" not in d else d["win_prefix"].shape[1]
@@ -62,7 +108,7 @@ class PrefillLayer:
         cfg = self.cfg
         ops.lca_compress("csa", self.m, self.B, self.n, self.c, self.C, self.Z, cfg.io_dtype,
                          self.prevC, self.prevZ, self.P, self.cache, cfg.kv_dtype, self.N_cap,
-                         self.n_prefix, cfg.eps, cfg.rope_base)
+                         self.n_prefix, cfg.eps, cfg.rope_base, pages=self.pages)
 
     def window_kv(self):
         cfg = self.cfg
@@ -102,7 +148,7 @@ class PrefillLayer:
                            cfg.kv_dtype, self.N_cap, self.idx, cfg.k, self.q_pos, self.m,
                            self.n_entries, self.win, self.W_cap, self.pos0 - self.n_pre_win,
                            cfg.n_win, cfg.tau, cfg.eps, None, cfg.rope_base, self.out, cfg.io_dtype,
-                           self.lse, self.ws_mqa)
+                           self.lse, self.ws_mqa, pages=self.pages)
 
     def run(self):
         self.compress()
@@ -111,11 +157,19 @@ class PrefillLayer:
         self.topk()
         self.attention()
 
+    def logical_cache(self):
+        """The compressed cache as [B, N_cap, row] bytes on the host."""
+        rb = ops.row_bytes(self.cfg.kv_dtype, self.c)
+        raw = self.cache.cpu().numpy().view(np.uint8)
+        if self.paged is None:
+            return raw.reshape(self.B, self.N_cap, rb)
+        return from_pool(raw.reshape(self.paged.n_pages, self.paged.epp, rb), self.paged.table, self.N_cap)
+
 
 class DecodeLayer:
     """One CSA ("C") or HCA ("H") layer's decode state on the GPU."""
 
-    def __init__(self, cfg, d, device="cuda", sink=None):
+    def __init__(self, cfg, d, device="cuda", sink=None, paged=None):
         self.cfg, self.device, self.d = cfg, device, d
         kind = d["kind"]
         self.mode = "csa" if kind == "C" else "hca"
@@ -123,7 +177,17 @@ class DecodeLayer:
         self.B, self.c, self.m = B, c, m
         self.N_cap = d["n_cap"]
         g = lambda name: _dev(d[name], device) if name in d else None  # noqa: E731
-        self.cache, self.ring = g("cache"), g("ring")
+        self.ring = g("ring")
+        self.paged, pages = None, None
+        if paged is not None:     # the compressed cache as a pool of pages (paged: dict(seed=...))
+            rb0 = ops.row_bytes(cfg.kv_dtype, c)
+            self.paged = Paged(B, self.N_cap, m, seed=paged.get("seed", 0))
+            pool = to_pool(np.ascontiguousarray(d["cache"]).view(np.uint8).reshape(B, self.N_cap, rb0),
+                           self.paged.epp, self.paged.table, self.paged.n_pages)
+            self.cache = _dev(pool, device)
+            pages = self.paged.struct(device)
+        else:
+            self.cache = g("cache")
         self.tailC, self.tailZ = g("tailC"), g("tailZ")
         self.n_tokens = g("n_tokens")
         self.P = g("P")
@@ -140,8 +204,16 @@ class DecodeLayer:
             io_fmt=cfg.io_dtype, kv_fmt=cfg.kv_dtype, tailC=self.tailC, tailZ=self.tailZ,
             ring=self.ring, cache=self.cache, n_tokens=self.n_tokens, P=self.P, sink=self.sink,
             tau=cfg.tau, eps=cfg.eps, k=cfg.k, H_I=cfg.H_I, d_I=cfg.d_I, idx_fmt=cfg.idx_dtype,
-            kI=self.kI, kI_scale=self.kI_scale, rope_base=cfg.rope_base)
+            kI=self.kI, kI_scale=self.kI_scale, rope_base=cfg.rope_base, pages=pages)
         self.workspace = _empty_bytes(self.state.workspace_size(), device)
+
+    def logical_cache(self):
+        """The compressed cache as [B, N_cap, row] bytes on the host."""
+        rb = ops.row_bytes(self.cfg.kv_dtype, self.c)
+        raw = self.cache.cpu().numpy().view(np.uint8)
+        if self.paged is None:
+            return raw.reshape(self.B, self.N_cap, rb)
+        return from_pool(raw.reshape(self.paged.n_pages, self.paged.epp, rb), self.paged.table, self.N_cap)
 
     def step(self, stream=None):
         csa = self.mode == "csa"

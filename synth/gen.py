@@ -207,3 +207,13 @@ def prefill_inputs(cfg: LayerConfig) -> dict:
         d["qI"] = draw_encoded(s, "qI", B, n, cfg.H_I * cfg.d_I, "normal",
                                cfg.idx_dtype).reshape(B, n, cfg.H_I, -1)
     return d
+
+
+def page_table(B: int, max_pages: int, n_pages: int, seed: int = 0) -> np.ndarray:
+    """A block table for a paged cache: [B, max_pages] int32 of distinct physical
+    pages drawn at random from a pool of n_pages >= B * max_pages (so that
+    sequences interleave in the pool and logical order never matches physical
+    order)."""
+    assert n_pages >= B * max_pages
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0x9A6E])))
+    return rng.permutation(n_pages)[: B * max_pages].reshape(B, max_pages).astype(np.int32)

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.lca_version() == 2
+    assert L.lca_version() == 3
     for st in (0, -1, -2, -3, -4):
         assert L.lca_status_string(st)
     assert L.lca_status_string(7) == b"unknown status"
@@ -56,7 +56,7 @@ def test_compress_validation(L):
         a = {**base, **kw}
         return L.lca_compress(a["mode"], a["m"], a["B"], a["n_new"], a["c"], a["C"], a["Z"], a["io"],
                               a["pc"], a["pz"], a["P"], a["cache"], a["kv"], a["N_cap"], a["first"],
-                              1e-6, a.get("rope", 0.0), None)
+                              1e-6, a.get("rope", 0.0), a.get("pages"), None)
 
     assert call(mode=5) == _lib.LCA_ERR_INVALID_ARG
     assert call(n_new=6) == _lib.LCA_ERR_INVALID_ARG
@@ -74,6 +74,19 @@ def test_compress_validation(L):
     assert call(rope=float("inf")) == _lib.LCA_ERR_INVALID_ARG
     assert call(rope=-10000.0) == _lib.LCA_ERR_INVALID_ARG
     assert call(B=0, rope=10000.0) == _lib.LCA_OK
+    # paged cache: page_tokens a multiple of m, the table covering N_cap entries
+    pg = _lib.KvPages(FAKE, 1, 6, 4)                      # 6 tokens per page, m = 4
+    assert call(pages=ctypes.byref(pg)) == _lib.LCA_ERR_INVALID_ARG
+    assert b"page_tokens" in L.lca_last_error()
+    pg = _lib.KvPages(FAKE, 1, 4, 4)                      # 1 entry per page, 1 page < N_cap = 2
+    assert call(pages=ctypes.byref(pg)) == _lib.LCA_ERR_INVALID_ARG
+    assert b"N_cap" in L.lca_last_error()
+    pg = _lib.KvPages(FAKE, 2, 4, 0)                      # empty pool
+    assert call(pages=ctypes.byref(pg)) == _lib.LCA_ERR_INVALID_ARG
+    pg = _lib.KvPages(FAKE, 2, 4, 4)
+    assert call(B=0, pages=ctypes.byref(pg)) == _lib.LCA_OK
+    pg = _lib.KvPages(None, 0, 0, 0)                      # no table: the contiguous layout
+    assert call(B=0, pages=ctypes.byref(pg)) == _lib.LCA_OK
     assert L.lca_rmsnorm_rows(1, 4, 128, FAKE, 0, FAKE, 0, 4, 1e-6, -1, 10000.0,
                               None) == _lib.LCA_ERR_INVALID_ARG            # negative pos0
     assert L.lca_rmsnorm_rows(1, 4, 128, FAKE, 0, FAKE, 0, 4, 1e-6, 0, 1.0,
@@ -101,25 +114,25 @@ def test_indexer_topk_mqa_validation(L):
             128, 0, 128, 0.04, 1e-6, None, 0.0, FAKE, F["bf16"], None]
     need = L.lca_sparse_mqa_workspace_size(1, 1, 64, 512, F["bf16"], 1024, 1024, 128, 0)
     assert need > 0
-    assert L.lca_sparse_mqa(*args, None, 0, None) == _lib.LCA_ERR_WORKSPACE
+    assert L.lca_sparse_mqa(*args, None, 0, None, None) == _lib.LCA_ERR_WORKSPACE
     bad = list(args)
     bad[2] = 12
-    assert L.lca_sparse_mqa(*bad, FAKE, need, None) == _lib.LCA_ERR_UNSUPPORTED
+    assert L.lca_sparse_mqa(*bad, FAKE, need, None, None) == _lib.LCA_ERR_UNSUPPORTED
     bad = list(args)
     bad[3] = 384
-    assert L.lca_sparse_mqa(*bad, FAKE, need, None) == _lib.LCA_ERR_UNSUPPORTED
+    assert L.lca_sparse_mqa(*bad, FAKE, need, None, None) == _lib.LCA_ERR_UNSUPPORTED
     bad = list(args)
     bad[14] = None          # window buffer missing with n_win > 0
-    assert L.lca_sparse_mqa(*bad, FAKE, need, None) == _lib.LCA_ERR_INVALID_ARG
+    assert L.lca_sparse_mqa(*bad, FAKE, need, None, None) == _lib.LCA_ERR_INVALID_ARG
     bad = list(args)
     bad[21] = float("nan")  # RoPE base
-    assert L.lca_sparse_mqa(*bad, FAKE, need, None) == _lib.LCA_ERR_INVALID_ARG
+    assert L.lca_sparse_mqa(*bad, FAKE, need, None, None) == _lib.LCA_ERR_INVALID_ARG
 
 
 def test_state_and_decode_validation(L):
     F = _lib.FMT
     assert L.lca_state_append(0, 4, 1, 512, 0, FAKE, FAKE, F["bf16"], FAKE, FAKE, FAKE, F["bf16"],
-                              FAKE, FAKE, 8, FAKE, FAKE, FAKE, 1e-6, 0.0, None) == _lib.LCA_ERR_INVALID_ARG
+                              FAKE, FAKE, 8, FAKE, FAKE, FAKE, 1e-6, 0.0, None, None) == _lib.LCA_ERR_INVALID_ARG
     lay = _lib.DecodeLayer()
     lay.struct_size = 3                          # wrong struct size
     assert L.lca_decode_workspace_size(ctypes.byref(lay)) == 0
@@ -138,6 +151,19 @@ def test_state_and_decode_validation(L):
     assert L.lca_decode_workspace_size(ctypes.byref(lay)) == 0           # bad RoPE base
     lay.rope_base = 10000.0
     assert L.lca_decode_workspace_size(ctypes.byref(lay)) == need
+    lay.pages = _lib.KvPages(FAKE, 100, 128, 10)          # 100 pages x 32 entries < N_cap
+    assert L.lca_decode_workspace_size(ctypes.byref(lay)) == 0
+    lay.pages = _lib.KvPages(FAKE, 2188, 128, 10)         # 2188 x 32 >= 70000
+    assert L.lca_decode_workspace_size(ctypes.byref(lay)) == need
+    # several steps: every step validated before any is enqueued
+    ios = (_lib.DecodeIO * 2)()
+    for i in range(2):
+        ios[i].struct_size = ctypes.sizeof(_lib.DecodeIO)
+    assert L.lca_decode_steps(ctypes.byref(lay), ios, 2, FAKE, need, None) == _lib.LCA_ERR_INVALID_ARG
+    assert L.lca_last_error().startswith(b"step 0")
+    assert L.lca_decode_steps(ctypes.byref(lay), None, 0, None, 0, None) == _lib.LCA_OK
+    assert L.lca_decode_steps(ctypes.byref(lay), None, -1, None, 0, None) == _lib.LCA_ERR_INVALID_ARG
+    lay.pages = _lib.KvPages(None, 0, 0, 0)
     lay.k = 0
     assert L.lca_decode_workspace_size(ctypes.byref(lay)) == 0
 

@@ -419,8 +419,7 @@ def run_prefill_parity(cfg, queries, check_entries=True):
     out = out_f64(layer.out)
     lse = host(layer.lse)
     kv, io = cfg.kv_dtype, cfg.io_dtype
-    rb = ops.row_bytes(kv, cfg.c)
-    cache = host(layer.cache).view(np.uint8).reshape(cfg.B, layer.N_cap, rb)
+    cache = layer.logical_cache()
     n_cert = 0
     for b in range(cfg.B):
         ref = OS.oracle_prefill(cfg, d, b, queries)
@@ -493,7 +492,7 @@ def _decode_parity(cfg, d, seqs, layer=None):
     ntok = host(layer.n_tokens)
     io, kv, m = cfg.io_dtype, cfg.kv_dtype, d["m"]
     rb = ops.row_bytes(kv, cfg.c)
-    cache = host(layer.cache).view(np.uint8).reshape(cfg.B, d["n_cap"], rb)
+    cache = layer.logical_cache()
     ring = host(layer.ring).view(np.uint8).reshape(cfg.B, cfg.n_win, rb)
     assert np.array_equal(ntok, d["n_tokens"] + 1)
     n_cert = 0
@@ -683,3 +682,170 @@ def test_sink_logit():
     for b in range(cfg.B):
         ref = OS.oracle_decode(cfg, d, b, sink=sink.astype(np.float64))
         assert np.abs(out[b] - ref["out"]).max() <= OUT_TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# paged compressed-KV cache (128-token pages, random block tables over a shared
+# pool): every result equals the contiguous layout's bit for bit, and the
+# oracle's
+
+
+def _paged_pool(cache_e, kv, m, seed=5, page_tokens=128, bad_page=None):
+    B, N_cap = cache_e.shape[0], cache_e.shape[1]
+    pg = pipeline.Paged(B, N_cap, m, page_tokens=page_tokens, seed=seed)
+    pool = pipeline.to_pool(_as_bytes(cache_e, kv).reshape(B, N_cap, -1), pg.epp, pg.table, pg.n_pages)
+    if bad_page is not None:            # (b, logical page) -> a page id outside the pool
+        pg.table[bad_page] = pg.n_pages + 7
+    return pg, pool
+
+
+@pytest.mark.parametrize("case", ["bf16_sparse", "fp8_sink", "bf16_dense", "rows300_f32q",
+                                  "bf16_sparse_c128_rope", "bf16_sparse_badpage"])
+def test_sparse_mqa_paged_equals_contiguous(case):
+    """The gather through a block table (decode kernel with its page prefetch,
+    the float32-query and generic kernels): bit-identical to the contiguous
+    cache; an entry whose page id lies outside the pool counts as absent."""
+    rng = np.random.default_rng(7)
+    bad = "_badpage" in case
+    t = _mqa_case(case.replace("_badpage", ""), rng)
+    B, H, c, kv = t["B"], t["H"], t["c"], t["kv"]
+    say(f"paged MQA {case}: B={B} k={t['k']} N_cap={t['N_cap']} m={t['m']}")
+    bad_page = (1, 3) if bad else None
+    pg, pool = _paged_pool(t["cache"], kv, t["m"], bad_page=bad_page)
+    idx = t["idx"]
+    if bad:                                   # the contiguous run without that page's entries
+        idx = idx.copy()
+        lo, hi = 3 * pg.epp, 4 * pg.epp
+        assert ((idx[1] >= lo) & (idx[1] < hi)).any()
+        idx[1][(idx[1] >= lo) & (idx[1] < hi)] = -1
+    outs = []
+    for paged in (False, True):
+        out = torch.zeros(B * H * c, dtype=torch.bfloat16, device=DEV)
+        lse = torch.zeros(B * H, dtype=torch.float32, device=DEV)
+        cache = T(pool) if paged else T(_as_bytes(t["cache"], kv))
+        pages = pg.struct(DEV) if paged else None
+        use_idx = t["idx"] if paged else idx
+        ops.lca_sparse_mqa(B, 1, H, c, T(t["q"]), t["q_fmt"], cache, kv, t["N_cap"],
+                           None if use_idx is None else T(use_idx), t["k"], T(t["q_pos"]), t["m"],
+                           T(t["n_entries"]), T(_as_bytes(t["win"], kv)), t["n_win"], 0, t["n_win"],
+                           t["tau"], t["eps"], None if t["sink"] is None else T(t["sink"]), t["rope"],
+                           out, "bf16", lse=lse, pages=pages)
+        outs.append((host(out.view(torch.int16)), host(lse)))
+    assert np.array_equal(outs[0][0], outs[1][0]), "outputs differ"
+    assert np.array_equal(outs[0][1], outs[1][1]), "lse differs"
+
+
+def _decode_cfg(kind):
+    if kind == "csa":
+        cfg = CSA_DECODE_1M.with_(B=4, ctx=1 << 14)
+        return cfg, gen.decode_inputs(cfg)
+    if kind == "hca":
+        cfg = HCA_DECODE.with_(B=4, ctx=1 << 14)
+        return cfg, gen.decode_inputs(cfg)
+    cfg = HYBRID_DECODE_1M.with_(ctx=1 << 16)       # a CSA layer: fp8+bf16-rope KV, MXFP4 keys
+    d = gen.hybrid_inputs(cfg)[2]
+    assert d["kind"] == "C"
+    return cfg, d
+
+
+@pytest.mark.parametrize("kind", ["csa", "hca", "hybrid_csa"])
+def test_decode_paged_equals_contiguous(kind):
+    cfg, d = _decode_cfg(kind)
+    say(f"paged decode {kind}: B={cfg.B} ctx={cfg.ctx}")
+    res = []
+    for paged in (None, {"seed": 11}):
+        layer = pipeline.DecodeLayer(cfg, d, DEV, paged=paged)
+        layer.step()
+        torch.cuda.synchronize()
+        res.append({"out": host(layer.out.view(torch.int16)), "lse": host(layer.lse),
+                    "cache": layer.logical_cache()})
+        if d["kind"] == "C":               # an HCA layer writes no selection
+            res[-1]["idx"] = host(layer.idx)
+    for name in res[0]:
+        assert np.array_equal(res[0][name], res[1][name]), f"{name} differs"
+    # and against the oracle (a fresh paged layer; the helper steps it once)
+    _decode_parity(cfg, d, range(cfg.B), layer=pipeline.DecodeLayer(cfg, d, DEV, paged={"seed": 11}))
+
+
+@pytest.mark.parametrize("kind", ["csa", "hca"])
+def test_decode_steps_paged_multi_step(kind):
+    """Nine steps in one lca_decode_steps call on a paged cache against nine
+    lca_decode_step calls on the contiguous cache: every step's output and
+    selection, and the cache with the entries the steps made, bit for bit; the
+    last step against the oracle stepped from the same state."""
+    if kind == "csa":
+        cfg = CSA_DECODE_1M.with_(B=2, ctx=4096)
+    else:
+        cfg = HCA_DECODE.with_(B=2, ctx=1024, m=8)
+    d = gen.decode_inputs(cfg, extra_entries=4)
+    say(f"paged multi-step {kind}")
+    n = 9
+    rng = np.random.default_rng(21)
+    toks = [{name: enc.encode(rng.standard_normal(d[name].shape), cfg.io_dtype)
+             for name in ("tokC", "tokZ", "q")} for _ in range(n)]
+    csa = kind == "csa"
+    # contiguous: one call per step
+    ref = pipeline.DecodeLayer(cfg, d, DEV)
+    ref_out, ref_idx = [], []
+    for st in toks:
+        for name in ("tokC", "tokZ", "q"):
+            getattr(ref, name).copy_(T(st[name]))
+        ref.step()
+        ref_out.append(host(ref.out.view(torch.int16)))
+        ref_idx.append(host(ref.idx))
+    # paged: all steps in one call
+    lay = pipeline.DecodeLayer(cfg, d, DEV, paged={"seed": 4})
+    steps = []
+    for st in toks:
+        e = {name: T(st[name]) for name in ("tokC", "tokZ", "q")}
+        e["out"] = torch.empty_like(lay.out)
+        e["lse"] = torch.empty_like(lay.lse)
+        if csa:
+            e.update(qI=lay.qI, qI_scale=lay.qI_scale, w=lay.w, idx_out=torch.empty_like(lay.idx))
+        steps.append(e)
+    ops.lca_decode_steps(lay.state, steps, cfg.io_dtype, workspace=lay.workspace)
+    torch.cuda.synchronize()
+    for i, e in enumerate(steps):
+        assert np.array_equal(host(e["out"].view(torch.int16)), ref_out[i]), f"step {i} out"
+        if csa:
+            assert np.array_equal(host(e["idx_out"]), ref_idx[i]), f"step {i} idx"
+    assert np.array_equal(lay.logical_cache(), ref.logical_cache())
+    assert np.array_equal(host(lay.n_tokens), host(ref.n_tokens))
+    # the oracle, stepped through the same tokens, agrees on the last output
+    states = [OS.oracle_decode_state(cfg, d, b) for b in range(cfg.B)]
+    for i, st in enumerate(toks):
+        for b in range(cfg.B):
+            kw = {}
+            if csa:
+                L = states[b].L + 1
+                kw = dict(k=cfg.k, qI=O.decode(d["qI"][b], cfg.idx_dtype),
+                          kI=O.decode(d["kI"][b, :L // d["m"]], cfg.idx_dtype), w=d["w"][b],
+                          idx_given=host(steps[i]["idx_out"])[b])
+            r = O.decode_step(states[b], tokC=O.decode(st["tokC"][b], cfg.io_dtype),
+                              tokZ=O.decode(st["tokZ"][b], cfg.io_dtype), P=d["P"],
+                              q=O.decode(st["q"][b], cfg.io_dtype), tau=cfg.tau, eps=cfg.eps,
+                              kv_fmt=cfg.kv_dtype, out_fmt=cfg.io_dtype, **kw)
+            got = out_f64(steps[i]["out"])[b]
+            err = np.abs(got - r["out"]).max()
+            assert err <= OUT_TOL[cfg.io_dtype], f"step {i} b{b}: {err:.3g}"
+
+
+@pytest.mark.parametrize("which", ["tiny", "chunk"])
+def test_prefill_paged_equals_contiguous(which):
+    """Prefill with the compressor writing through the block table and the
+    attention gathering through it: new entries and outputs bit for bit."""
+    if which == "tiny":
+        cfg = TINY_CSA_PREFILL
+    else:
+        cfg = CSA_PREFILL_CHUNK.with_(ctx=8192, n_new=1024)
+    say(f"paged prefill {cfg.name} ctx={cfg.ctx} n={cfg.n_new}")
+    d = gen.prefill_inputs(cfg)
+    res = []
+    for paged in (None, {"seed": 2}):
+        layer = pipeline.PrefillLayer(cfg, d, DEV, paged=paged)
+        layer.run()
+        torch.cuda.synchronize()
+        res.append((layer.logical_cache(), host(layer.out.view(torch.int16) if layer.out.dtype ==
+                                                torch.bfloat16 else layer.out), host(layer.idx)))
+    for a, b in zip(res[0], res[1]):
+        assert np.array_equal(a, b)
