@@ -120,3 +120,19 @@ def layer(*, mode, m, k, n_win, tau, eps, C, Z, P, q, qI=None, kI=None, w=None,
                                     None if sink is None else sink[h]), -t, rope_base)
                      for h in range(len(q[t]))])
     return outs, (idxs if mode == "csa" else None), entries
+
+
+def grouped_projection(o, W_g, W_o):
+    """The grouped output projection with scalar loops: head h belongs to group
+    h // (n_h/g); group j's input is its heads' outputs concatenated in head
+    order; z[j*d_g + r] = sum_i W_g[j][r][i] x_j[i]; out[n] = sum_q W_o[n][q] z[q].
+    o [n_h][c] for one token."""
+    n_h, c = len(o), len(o[0])
+    g, d_g = len(W_g), len(W_g[0])
+    per = n_h // g
+    z = []
+    for j in range(g):
+        x = [o[h][i] for h in range(j * per, (j + 1) * per) for i in range(c)]
+        for r in range(d_g):
+            z.append(sum(W_g[j][r][i] * x[i] for i in range(len(x))))
+    return [sum(W_o[n][q] * z[q] for q in range(len(z))) for n in range(len(W_o))], z

@@ -526,6 +526,35 @@ def decode_step(st: DecodeState, *, tokC, tokZ, P, q, tau, eps, kv_fmt, out_fmt,
     return res
 
 
+def grouped_output_projection(o, W_g, W_o, z_fmt=None):
+    """Grouped output projection ([QB] hybrid attention, the fourth step of CSA:
+    with c = 512 a direct projection of all heads back to d is expensive, so the
+    n_h heads are split into g groups, each group is projected to an intermediate
+    dim d_g, and the groups' results are projected together back to d).
+
+    o [T, n_h, c]; W_g [g, d_g, (n_h/g)*c] (group j's matrix, output x input);
+    W_o [d, g*d_g].  Group j takes heads j*n_h/g .. (j+1)*n_h/g - 1, their outputs
+    concatenated in head order.  z_fmt: the storage format of the intermediate
+    (the GPU keeps it as bf16 between its two products); None keeps it exact.
+    Returns (out [T, d], z [T, g*d_g])."""
+    o = np.asarray(o, np.float64)
+    W_g = np.asarray(W_g, np.float64)
+    T, n_h, c = o.shape
+    g, d_g, din = W_g.shape
+    assert n_h % g == 0 and din == (n_h // g) * c
+    x = o.reshape(T, g, din)
+    z = np.stack([x[:, j] @ W_g[j].T for j in range(g)], axis=1).reshape(T, g * d_g)
+    if z_fmt is not None:
+        z = round_to(z, z_fmt)
+    return z @ np.asarray(W_o, np.float64).T, z
+
+
+def matmul_error_bound(a_abs, b_abs_t, n_terms: int) -> np.ndarray:
+    """Bound on |fl32(A B^T) - A B^T| for float32 accumulation in any order of
+    n_terms products of exact (bf16) operands: gamma(n_terms) * |A| |B|^T."""
+    return gamma(n_terms) * (np.asarray(a_abs, np.float64) @ np.asarray(b_abs_t, np.float64).T)
+
+
 def rope_error_bound(y, bound, rope_dims: int = ROPE_DIMS) -> np.ndarray:
     """Bound on the error of an fp32 rotation of values y (exact: the rotated values;
     the rotation preserves |pair|) whose inputs carry the error bound `bound`: a

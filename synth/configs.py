@@ -77,6 +77,29 @@ HYBRID_DECODE_1M = LayerConfig(
     c=512, H=64, H_I=64, d_I=128, m=4, k=1024, n_win=128, io_dtype="bf16",
     kv_dtype="fp8_bf16rope", idx_dtype="mxfp4", layers=("H", "H", "C", "H", "C", "H", "C", "H"))
 
+@dataclass(frozen=True)
+class OutProjConfig:
+    """Grouped output projection after the attention: the n_h heads' outputs in
+    g groups, each projected to d_g, then all groups back to the hidden size d
+    (QbitAI article, hybrid attention section; d = 7168 is V4-Pro's hidden size,
+    same article, model architecture paragraph).  The pages give neither g nor
+    d_g: g = 8 groups of 8 heads and d_g = 1024 are readings."""
+    name: str
+    T: int                 # query tokens (decode: the batch; prefill: the chunk)
+    n_h: int = 64
+    c: int = 512
+    g: int = 8
+    d_g: int = 1024
+    d: int = 7168
+    seed: int = 0
+
+    def with_(self, **kw) -> "OutProjConfig":
+        return replace(self, **kw)
+
+
+OUT_PROJ_DECODE = OutProjConfig(name="out_proj_decode_b16", T=16)
+OUT_PROJ_PREFILL = OutProjConfig(name="out_proj_prefill_8k", T=8192)
+
 CONFIGS = {cfg.name: cfg for cfg in
            (TINY_CSA_PREFILL, HCA_DECODE, CSA_DECODE_1M, CSA_PREFILL_CHUNK, HYBRID_DECODE_1M)}
 

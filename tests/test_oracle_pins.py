@@ -490,6 +490,66 @@ def test_rope_error_bound_covers_fp32_rotation():
 
 
 # ---------------------------------------------------------------------------
+# grouped output projection
+
+
+def test_grouped_projection_matches_brute_force():
+    r = rng(80)
+    T, n_h, c, g, d_g, d = 2, 6, 4, 3, 5, 7
+    o = r.standard_normal((T, n_h, c))
+    W_g = r.standard_normal((g, d_g, (n_h // g) * c))
+    W_o = r.standard_normal((d, g * d_g))
+    out, z = O.grouped_output_projection(o, W_g, W_o)
+    for t in range(T):
+        bo, bz = brute.grouped_projection(o[t].tolist(), W_g.tolist(), W_o.tolist())
+        assert np.allclose(out[t], bo, rtol=1e-12, atol=1e-12)
+        assert np.allclose(z[t], bz, rtol=1e-12, atol=1e-12)
+
+
+def test_grouped_projection_structure():
+    r = rng(81)
+    T, n_h, c, g, d_g = 3, 8, 16, 4, 6
+    o = r.standard_normal((T, n_h, c))
+    W_g = r.standard_normal((g, d_g, (n_h // g) * c))
+    # one group: two plain matrix products of the flattened heads
+    W_o1 = r.standard_normal((9, d_g))
+    Wg1 = r.standard_normal((1, d_g, n_h * c))
+    out1, z1 = O.grouped_output_projection(o, Wg1, W_o1)
+    assert np.allclose(out1, (o.reshape(T, -1) @ Wg1[0].T) @ W_o1.T)
+    # with W_o the identity, perturbing the heads of group j moves only z's block j
+    I = np.eye(g * d_g)
+    base, zb = O.grouped_output_projection(o, W_g, I)
+    assert np.array_equal(base, zb)
+    for j in range(g):
+        o2 = o.copy()
+        o2[:, j * (n_h // g):(j + 1) * (n_h // g)] += 1.0
+        moved, _ = O.grouped_output_projection(o2, W_g, I)
+        diff = np.abs(moved - base).reshape(T, g, d_g).max(axis=(0, 2))
+        assert diff[j] > 0 and np.all(np.delete(diff, j) == 0)
+    # linear in the attention output
+    W_o = r.standard_normal((5, g * d_g))
+    a, _ = O.grouped_output_projection(o, W_g, W_o)
+    b, _ = O.grouped_output_projection(2.5 * o, W_g, W_o)
+    assert np.allclose(b, 2.5 * a)
+    # the bf16 intermediate is the round-to-nearest-even of the exact one
+    _, zx = O.grouped_output_projection(o, W_g, W_o)
+    _, zr = O.grouped_output_projection(o, W_g, W_o, z_fmt="bf16")
+    assert np.array_equal(zr, O.round_to(zx, "bf16"))
+
+
+def test_matmul_error_bound_covers_fp32_accumulation():
+    r = rng(82)
+    a = O.round_to(r.standard_normal((4, 3000)), "bf16")
+    b = O.round_to(r.standard_normal((5, 3000)), "bf16")
+    exact = a @ b.T
+    f32 = np.zeros((4, 5), np.float32)
+    for k in range(3000):          # sequential float32 accumulation
+        f32 += (a[:, k:k + 1].astype(np.float32) * b[:, k].astype(np.float32)[None, :])
+    bnd = O.matmul_error_bound(np.abs(a), np.abs(b), 3000)
+    assert np.all(np.abs(f32.astype(np.float64) - exact) <= bnd)
+
+
+# ---------------------------------------------------------------------------
 # score error bound and the pages' hyperparameters
 
 
@@ -510,7 +570,7 @@ def test_score_error_bound_covers_fp32_evaluation():
 
 
 def test_pages_hyperparameters():
-    from synth.configs import CSA_DECODE_1M, HCA_DECODE, HYBRID_DECODE_1M
+    from synth.configs import CSA_DECODE_1M, HCA_DECODE, HYBRID_DECODE_1M, OUT_PROJ_DECODE, OUT_PROJ_PREFILL
     g = json.load(open(os.path.join(GOLD, "hyperparams.json")))
     cfg = CSA_DECODE_1M
     assert cfg.m == g["csa_rate_m"]["value"] and cfg.k == g["csa_topk"]["value"]
@@ -521,6 +581,8 @@ def test_pages_hyperparameters():
     assert cfg.ctx == g["context_tokens"]["value"]
     assert np.lcm(cfg.m, HCA_DECODE.m) == g["cache_block_tokens_lcm"]["value"]
     assert cfg.k == g["entries_attended_at_1m"]["value"]
+    assert OUT_PROJ_DECODE.d == OUT_PROJ_PREFILL.d == g["hidden_dim_d_v4_pro"]["value"]
+    assert OUT_PROJ_DECODE.c == g["head_dim_c"]["value"]
     assert int(O.visible([cfg.ctx - 1], cfg.m, 10 ** 9)[0]) == 262144
 
 
