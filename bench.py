@@ -34,7 +34,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
-WORKLOADS = ("csa_decode_1m", "hca_decode", "hybrid_decode_1m", "csa_prefill_chunk")
+WORKLOADS = ("csa_decode_1m", "hca_decode", "hybrid_decode_1m", "csa_prefill_chunk",
+             "out_proj_decode", "out_proj_prefill")
+BF16_PEAK_TFLOPS = 2500.0
 
 
 class HipEvents:
@@ -371,6 +373,69 @@ def run_prefill(args):
     return result, per
 
 
+def run_out_proj(args):
+    """The grouped output projection after the attention (V4-Pro shape: 64 heads x
+    512 in 8 groups -> 8 x 1024 -> 7168) for a decode batch (16 tokens: streams the
+    184 MB of bf16 weights, HBM-bound) or a prefill chunk (8192 tokens: MFMA-bound)."""
+    import numpy as np
+    import torch
+
+    from long_context_attention_14_amd import ops
+    from synth import encode as enc
+    from synth.configs import OUT_PROJ_DECODE, OUT_PROJ_PREFILL
+
+    cfg = OUT_PROJ_DECODE if args.workload == "out_proj_decode" else OUT_PROJ_PREFILL
+    T, n_h, c, g, d_g, d = cfg.T, cfg.n_h, cfg.c, cfg.g, cfg.d_g, cfg.d
+    kin = n_h // g * c
+    rng = np.random.default_rng(cfg.seed)
+    dev = "cuda"
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    o = up(enc.to_bf16_bits(rng.standard_normal((T, n_h, c), dtype=np.float32) * 0.5))
+    W_g = up(enc.to_bf16_bits(rng.standard_normal((g, d_g, kin), dtype=np.float32) / np.sqrt(kin)))
+    W_o = up(enc.to_bf16_bits(rng.standard_normal((d, g * d_g), dtype=np.float32) / np.sqrt(g * d_g)))
+    z = torch.empty((T, g * d_g), dtype=torch.int16, device=dev)
+    out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, ops.lca_grouped_out_proj_workspace_size(T, n_h, c, g, d_g, d)),
+                     dtype=torch.uint8, device=dev)
+    call = lambda: ops.lca_grouped_out_proj(T, n_h, c, g, d_g, d, o, W_g, W_o, z, out, "bf16", ws)  # noqa: E731
+    _calibrate_copy(args.calibrate_copy, dev)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for _ in range(args.steps):
+        call()
+    ev[1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per = ev[0].elapsed_time(ev[1]) * 1e-3 / args.steps
+    flops = 2.0 * T * (g * d_g * kin + d * g * d_g)
+    wbytes = 2.0 * (g * d_g * kin + d * g * d_g)
+    io_bytes = 2.0 * T * (n_h * c + 2 * g * d_g + d)
+    if T <= 64:
+        roof = {"bound": "hbm", "achieved": (wbytes + io_bytes) / per / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / per / 1e12, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof.update(frac=roof["achieved"] / roof["peak"], traffic=None, kernel="gemm_bf16_kernel")
+    result = {
+        "metric": "grouped output projection tokens/s", "value": T * args.steps / elapsed,
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 / fp32 accumulate",
+        "data": "synthetic (seeded; N(0, 1/fan_in) weights)",
+        "config": {"workload": f"{cfg.name}: {T} tokens, {n_h} heads x {c} in {g} groups -> "
+                               f"{g} x {d_g} -> {d}", "global_batch": T, "seq_len": 0,
+                   "parallelism": "single GPU"},
+        "roofline": roof, "us_per_call": per * 1e6, "tflops": flops / per / 1e12,
+        "weight_GBs": wbytes / per / 1e9,
+    }
+    return result, {"us_per_call": per * 1e6}
+
+
 def bf16_selector(layer, steps):
     """The pages' BF16-score variant of the indexer + top-k on the same chunk:
     its stage times, and the share of the float32 selection (layer.idx, from the
@@ -412,6 +477,8 @@ def main():
         sys.exit(2)
     if args.workload == "csa_prefill_chunk":
         result, per = run_prefill(args)
+    elif args.workload.startswith("out_proj"):
+        result, per = run_out_proj(args)
     else:
         result, per = run_decode(args, args.workload)
     if args.detail:

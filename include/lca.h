@@ -280,6 +280,29 @@ int lca_sparse_mqa(int B, int n_q, int H, int c, const void* q, int q_dtype, con
                    size_t workspace_bytes, const lca_kv_pages* pages, lca_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * lca_grouped_out_proj -- the grouped output projection after the attention
+ * (QbitAI article on DeepSeek-V4, hybrid attention section, the fourth step of
+ * CSA: the n_h heads are split into g groups, each group is projected to an
+ * intermediate dim d_g, and the groups' results are projected back to d):
+ *   z[t, j*d_g + r] = bf16( sum_i W_g[j, r, i] * o[t, j*(n_h/g)*c + i] )
+ *   out[t, n]       = sum_q W_o[n, q] * z[t, q]
+ * (group j holds heads j*n_h/g .. (j+1)*n_h/g - 1, concatenated in head order).
+ *   o    [T, n_h, c] bf16 (the attention output)
+ *   W_g  [g, d_g, (n_h/g)*c] bf16 (each group's matrix, output x input)
+ *   W_o  [d, g*d_g] bf16 (output x input)
+ *   z    [T, g*d_g] bf16, written (the intermediate; an output of the call)
+ *   out  [T, d] out_dtype (F32|BF16)
+ * Products accumulate in float32.  Needs n_h % g == 0, d_g and d multiples of
+ * 128, (n_h/g)*c a multiple of 64.  Workspace: lca_grouped_out_proj_workspace_size
+ * bytes (K-split partials for small T; 0 for large T).
+ * ------------------------------------------------------------------------- */
+size_t lca_grouped_out_proj_workspace_size(int T, int n_h, int c, int g, int d_g, int d);
+int lca_grouped_out_proj(int T, int n_h, int c, int g, int d_g, int d, const uint16_t* o,
+                         const uint16_t* W_g, const uint16_t* W_o, uint16_t* z, void* out,
+                         int out_dtype, void* workspace, size_t workspace_bytes,
+                         lca_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * lca_state_append -- decode-time state of uncompressed tokens ("DeepSeek V4
  * Architecture Tricks", section "Heterogeneous KV Cache Layout": the state
  * cache keeps the window KV and the tail tokens of the block not yet

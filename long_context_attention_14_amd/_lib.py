@@ -61,6 +61,9 @@ SIGNATURES = {
                                c_int, P, P, c_size_t, ctypes.POINTER(KvPages), P]),
     "lca_state_append": (c_int, [c_int, c_int, c_int, c_int, c_int, P, P, c_int, P, P, P, c_int, P,
                                  P, c_int, P, P, P, c_float, c_float, ctypes.POINTER(KvPages), P]),
+    "lca_grouped_out_proj_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int]),
+    "lca_grouped_out_proj": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, P, P, P, P, P, c_int,
+                                     P, c_size_t, P]),
     "lca_decode_workspace_size": (c_size_t, [ctypes.POINTER(DecodeLayer)]),
     "lca_decode_step": (c_int, [ctypes.POINTER(DecodeLayer), ctypes.POINTER(DecodeIO), P, c_size_t,
                                 P]),

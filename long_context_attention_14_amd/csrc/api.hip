@@ -284,6 +284,47 @@ int lca_state_append(int mode, int m, int B, int c, int n_win, const void* tokC,
 }
 
 // ---------------------------------------------------------------------------
+// grouped output projection
+
+namespace {
+int out_proj_check(int T, int n_h, int c, int g, int d_g, int d) {
+  REQUIRE(T >= 0, "T = %d < 0", T);
+  REQUIRE(n_h >= 1 && c >= 1 && g >= 1 && d_g >= 1 && d >= 1, "sizes must be positive");
+  REQUIRE(n_h % g == 0, "n_h = %d is not a multiple of g = %d", n_h, g);
+  SUPPORT(d_g % 128 == 0 && d % 128 == 0, "d_g = %d and d = %d must be multiples of 128", d_g, d);
+  SUPPORT((n_h / g) * c % 64 == 0, "a group's input (n_h/g)*c = %d must be a multiple of 64",
+          (n_h / g) * c);
+  SUPPORT(static_cast<long long>(T) * n_h * c < (1LL << 31) &&
+              static_cast<long long>(d) * g * d_g < (1LL << 31),
+          "tensor too large");
+  return LCA_OK;
+}
+}  // namespace
+
+size_t lca_grouped_out_proj_workspace_size(int T, int n_h, int c, int g, int d_g, int d) {
+  if (out_proj_check(T, n_h, c, g, d_g, d) != LCA_OK) return 0;
+  return lca::out_proj_workspace_bytes(T, n_h, c, g, d_g, d);
+}
+
+int lca_grouped_out_proj(int T, int n_h, int c, int g, int d_g, int d, const uint16_t* o,
+                         const uint16_t* W_g, const uint16_t* W_o, uint16_t* z, void* out,
+                         int out_dtype, void* workspace, size_t workspace_bytes,
+                         lca_stream_t stream) {
+  g_last_error.clear();
+  if (int st = out_proj_check(T, n_h, c, g, d_g, d)) return st;
+  SUPPORT(io_fmt_ok(out_dtype), "out_dtype %d unsupported (F32 or BF16)", out_dtype);
+  const size_t need = lca::out_proj_workspace_bytes(T, n_h, c, g, d_g, d);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(LCA_ERR_WORKSPACE, "lca_grouped_out_proj needs %zu workspace bytes, got %zu", need,
+                workspace ? workspace_bytes : 0);
+  if (T == 0) return LCA_OK;
+  REQUIRE(o && W_g && W_o && z && out, "NULL tensor pointer");
+  return hip_status(lca::launch_out_proj(T, n_h, c, g, d_g, d, o, W_g, W_o, z, out, out_dtype,
+                                         workspace, reinterpret_cast<hipStream_t>(stream)),
+                    "lca_grouped_out_proj");
+}
+
+// ---------------------------------------------------------------------------
 // composed decode step
 
 namespace {

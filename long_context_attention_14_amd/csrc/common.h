@@ -394,6 +394,10 @@ hipError_t launch_topk_from_hist(int B, int n_q, int N_cap, const float* scores,
                                  int32_t* idx, void* ws, hipStream_t s);
 size_t mqa_workspace_bytes(int B, int n_q, int H, int c, int kv_fmt, int k, int N_cap, int n_win,
                            int dense);
+size_t out_proj_workspace_bytes(int T, int n_h, int c, int g, int d_g, int d);
+hipError_t launch_out_proj(int T, int n_h, int c, int g, int d_g, int d, const uint16_t* o,
+                           const uint16_t* W_g, const uint16_t* W_o, uint16_t* z, void* out,
+                           int out_fmt, void* ws, hipStream_t s);
 hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, const void* cache,
                       int kv_fmt, int N_cap, const int32_t* idx, int k, const int32_t* q_pos, int m,
                       const int32_t* n_entries, const void* win, int W_cap, int64_t win_origin,

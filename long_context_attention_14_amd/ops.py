@@ -189,6 +189,22 @@ def lca_state_append(mode, m, B, c, n_win, tokC, tokZ, io_fmt, tailC, tailZ, rin
         _ptr(n_entries, 4 * B, "n_entries"), eps, rope_base, _pages_ref(pages), _stream(stream)))
 
 
+def lca_grouped_out_proj_workspace_size(T, n_h, c, g, d_g, d) -> int:
+    return lib().lca_grouped_out_proj_workspace_size(T, n_h, c, g, d_g, d)
+
+
+def lca_grouped_out_proj(T, n_h, c, g, d_g, d, o, W_g, W_o, z, out, out_fmt, workspace=None,
+                         stream=None):
+    need = lca_grouped_out_proj_workspace_size(T, n_h, c, g, d_g, d)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=o.device)
+    return check("lca_grouped_out_proj", lib().lca_grouped_out_proj(
+        T, n_h, c, g, d_g, d, _ptr(o, 2 * T * n_h * c, "o"),
+        _ptr(W_g, 2 * g * d_g * (n_h // g) * c, "W_g"), _ptr(W_o, 2 * d * g * d_g, "W_o"),
+        _ptr(z, 2 * T * g * d_g, "z"), _ptr(out, row_bytes(out_fmt, d) * T, "out"), FMT[out_fmt],
+        _ptr(workspace, need, "workspace", need == 0), need, _stream(stream)))
+
+
 class DecodeLayerState:
     """Device buffers of one layer's decode state plus its lca_decode_layer struct."""
 

@@ -849,3 +849,62 @@ def test_prefill_paged_equals_contiguous(which):
                                                 torch.bfloat16 else layer.out), host(layer.idx)))
     for a, b in zip(res[0], res[1]):
         assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# grouped output projection: the bf16 intermediate within one ulp plus the fp32
+# accumulation bound of the oracle's exact value, the output within the bound of
+# the oracle's product over the GPU's own intermediate (each stage on the same
+# inputs as the oracle)
+
+
+def _out_proj_inputs(nt, n_h, c, g, d_g, d, seed):
+    rng = np.random.default_rng(seed)
+    kin = n_h // g * c
+    o = enc.to_bf16_bits(rng.standard_normal((nt, n_h, c)) * 0.5)
+    W_g = enc.to_bf16_bits(rng.standard_normal((g, d_g, kin)) / np.sqrt(kin))
+    W_o = enc.to_bf16_bits(rng.standard_normal((d, g * d_g)) / np.sqrt(g * d_g))
+    return o, W_g, W_o
+
+
+def _check_out_proj(nt, n_h, c, g, d_g, d, out_fmt, rows=None, seed=3):
+    o, W_g, W_o = _out_proj_inputs(nt, n_h, c, g, d_g, d, seed)
+    z = torch.empty((nt, g * d_g), dtype=torch.int16, device=DEV)
+    out = torch.empty((nt, d), dtype=torch.float32 if out_fmt == "f32" else torch.bfloat16, device=DEV)
+    ops.lca_grouped_out_proj(nt, n_h, c, g, d_g, d, T(o), T(W_g), T(W_o), z, out, out_fmt)
+    zg = O.decode_bf16(host(z).view(np.uint16))
+    og = out_f64(out)
+    rows = np.arange(nt) if rows is None else np.asarray(rows)
+    od, Wgd, Wod = O.decode_bf16(o[rows]), O.decode_bf16(W_g), O.decode_bf16(W_o)
+    _, z_exact = O.grouped_output_projection(od, Wgd, Wod)
+    kin = n_h // g * c
+    x = np.abs(od).reshape(len(rows), g, kin)
+    zb = np.concatenate([O.matmul_error_bound(x[:, j], np.abs(Wgd[j]), kin) for j in range(g)], axis=1)
+    OS.assert_within_ulp(zg[rows], O.round_to(z_exact, "bf16"), "bf16", slack=zb, what="z")
+    want = zg[rows] @ Wod.T
+    ob = O.matmul_error_bound(np.abs(zg[rows]), np.abs(Wod), g * d_g)
+    if out_fmt == "f32":
+        err = np.abs(og[rows] - want)
+        assert np.all(err <= ob + 1e-30), f"out err {err.max():.3g} > bound {ob.max():.3g}"
+    else:
+        OS.assert_within_ulp(og[rows], O.round_to(want, "bf16"), "bf16", slack=ob, what="out")
+    return host(z), host(out.view(torch.int16) if out.dtype == torch.bfloat16 else out)
+
+
+@pytest.mark.parametrize("nt,n_h,c,g,d_g,d,out_fmt", [
+    (16, 64, 512, 8, 1024, 7168, "bf16"),     # the decode batch at the V4-Pro shape (K split)
+    (5, 8, 128, 2, 128, 256, "f32"),          # small, K split, ragged rows
+    (40, 16, 256, 4, 256, 384, "f32"),        # 32-row tiles
+    (300, 16, 256, 8, 256, 1024, "bf16"),     # 128-row tiles with a ragged last tile
+    (1, 64, 512, 1, 128, 128, "f32"),         # one group, one token
+])
+def test_grouped_out_proj(nt, n_h, c, g, d_g, d, out_fmt):
+    say(f"grouped out proj T={nt} n_h={n_h} c={c} g={g} d_g={d_g} d={d} -> {out_fmt}")
+    a = _check_out_proj(nt, n_h, c, g, d_g, d, out_fmt)
+    b = _check_out_proj(nt, n_h, c, g, d_g, d, out_fmt)       # deterministic
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_grouped_out_proj_prefill_full_size_sampled():
+    say("grouped out proj T=8192 at the V4-Pro shape, sampled rows")
+    _check_out_proj(8192, 64, 512, 8, 1024, 7168, "bf16", rows=[0, 1, 127, 128, 4095, 8190, 8191])
