@@ -312,26 +312,40 @@ __device__ void select_emit(uint32_t* lh, const float* sc, int n_t, int wi, int 
   if (incl >= k && incl - v < k) sh_bin = bin;
   const int b_lb = __syncthreads_or(incl >= k) ? sh_bin : -1;
   // emission: wave w takes blocks w, w + NW, ...; lane l holds keys l and l + 64
-  // of the block, so two ballots give every emitted entry its place in index order
-  for (int t = wave; t < n_t; t += NW) {
-    const int blk = wi + t * wpr;
-    const int i0 = blk * kSelBlock + lane, i1 = i0 + kWave;
-    const uint32_t k0 = i0 < vis ? score_key(sc[t * kSelBlock + lane]) : 0u;
-    const uint32_t k1 = i1 < vis ? score_key(sc[t * kSelBlock + kWave + lane]) : 0u;
-    const bool e0 = i0 < vis && static_cast<int>(score_bin(k0)) >= b_lb;
-    const bool e1 = i1 < vis && static_cast<int>(score_bin(k1)) >= b_lb;
-    const uint64_t m0 = __ballot(e0), m1 = __ballot(e1);
-    const int n0 = __popcll(m0);
-    const size_t seg = static_cast<size_t>(row) * o.n_blk + blk;
-    if (e0) {
-      const int p = lanes_below64(m0);
-      o.emit[seg * kSelBlock + p] = make_uint2(k0, static_cast<uint32_t>(i0));
+  // of a block, so two ballots give every emitted entry its place in index order.
+  // The scores of kEmitBatch blocks are read (unconditionally: the LDS array
+  // holds n_t whole blocks) before any is used, so the LDS reads overlap.
+  constexpr int kEmitBatch = 4;
+  for (int t0 = wave; t0 < n_t; t0 += kEmitBatch * NW) {
+    float s0[kEmitBatch], s1[kEmitBatch];
+#pragma unroll
+    for (int u = 0; u < kEmitBatch; ++u) {
+      const int t = min(t0 + u * NW, n_t - 1);
+      s0[u] = sc[t * kSelBlock + lane];
+      s1[u] = sc[t * kSelBlock + kWave + lane];
     }
-    if (e1) {
-      const int p = n0 + lanes_below64(m1);
-      o.emit[seg * kSelBlock + p] = make_uint2(k1, static_cast<uint32_t>(i1));
+#pragma unroll
+    for (int u = 0; u < kEmitBatch; ++u) {
+      const int t = t0 + u * NW;
+      if (t >= n_t) break;  // the same for the whole wave
+      const int blk = wi + t * wpr;
+      const int i0 = blk * kSelBlock + lane, i1 = i0 + kWave;
+      const uint32_t k0 = score_key(s0[u]), k1 = score_key(s1[u]);
+      const bool e0 = i0 < vis && static_cast<int>(score_bin(k0)) >= b_lb;
+      const bool e1 = i1 < vis && static_cast<int>(score_bin(k1)) >= b_lb;
+      const uint64_t m0 = __ballot(e0), m1 = __ballot(e1);
+      const int n0 = __popcll(m0);
+      const size_t seg = static_cast<size_t>(row) * o.n_blk + blk;
+      if (e0) {
+        const int p = lanes_below64(m0);
+        o.emit[seg * kSelBlock + p] = make_uint2(k0, static_cast<uint32_t>(i0));
+      }
+      if (e1) {
+        const int p = n0 + lanes_below64(m1);
+        o.emit[seg * kSelBlock + p] = make_uint2(k1, static_cast<uint32_t>(i1));
+      }
+      if (lane == 0) o.emit_cnt[seg] = n0 + __popcll(m1);
     }
-    if (lane == 0) o.emit_cnt[seg] = n0 + __popcll(m1);
   }
   for (int bb = tid; bb < kScoreHistBins; bb += NT)
     if (lh[bb]) atomicAdd(&gh[hist_slot(bb)], lh[bb]);
