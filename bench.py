@@ -420,7 +420,8 @@ def run_out_proj(args):
     else:
         roof = {"bound": "mfma", "achieved": flops / per / 1e12, "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
-    roof.update(frac=roof["achieved"] / roof["peak"], traffic=None, kernel="gemm_bf16_kernel")
+    roof.update(frac=roof["achieved"] / roof["peak"], traffic=None,
+                kernel="gemm_skinny_kernel" if T <= 32 else "gemm_bf16_kernel<128>")
     result = {
         "metric": "grouped output projection tokens/s", "value": T * args.steps / elapsed,
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
