@@ -73,31 +73,36 @@ __global__ __launch_bounds__(kGThreads) void gemm_bf16_kernel(GemmArgs a) {
   const int k_begin = split * a.steps_per_split * kGBK;
   const int steps = a.steps_per_split;
 
-  uint4 ra[ACH], rw[WCH];
-  auto load = [&](int k0) {
+  // a step's A and W chunks in registers; two named sets, so that a step's
+  // loads go out two steps before they are stored to LDS
+  struct Stage {
+    uint4 a[ACH], w[WCH];
+  };
+  auto load = [&](Stage& R, int st) {  // steps past the end read the last one (not stored)
+    const int k0 = k_begin + min(st, steps - 1) * kGBK;
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
       const int ch = tid + kGThreads * i, r = ch >> 3, kc = ch & 7;
       const int m = min(m0 + r, a.M - 1);  // rows past M read row M-1, staged as zeros
-      ra[i] = *reinterpret_cast<const uint4*>(Ab + m * a.lda + k0 + 8 * kc);
-      if (m0 + r >= a.M) ra[i] = make_uint4(0, 0, 0, 0);
+      R.a[i] = *reinterpret_cast<const uint4*>(Ab + m * a.lda + k0 + 8 * kc);
     }
 #pragma unroll
     for (int i = 0; i < WCH; ++i) {
       const int ch = tid + kGThreads * i, r = ch >> 3, kc = ch & 7;
-      rw[i] = *reinterpret_cast<const uint4*>(Wb + static_cast<long long>(r) * a.K + k0 + 8 * kc);
+      R.w[i] = *reinterpret_cast<const uint4*>(Wb + static_cast<long long>(r) * a.K + k0 + 8 * kc);
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](const Stage& R, int buf) {
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
       const int ch = tid + kGThreads * i, r = ch >> 3, kc = ch & 7;
-      *reinterpret_cast<uint4*>(&As[buf][r * kGLds + 8 * kc]) = ra[i];
+      *reinterpret_cast<uint4*>(&As[buf][r * kGLds + 8 * kc]) =
+          m0 + r < a.M ? R.a[i] : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < WCH; ++i) {
       const int ch = tid + kGThreads * i, r = ch >> 3, kc = ch & 7;
-      *reinterpret_cast<uint4*>(&Ws[buf][r * kGLds + 8 * kc]) = rw[i];
+      *reinterpret_cast<uint4*>(&Ws[buf][r * kGLds + 8 * kc]) = R.w[i];
     }
   };
 
@@ -107,12 +112,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int y = 0; y < TN; ++y) acc[x][y] = gv16f{0};
 
-  load(k_begin);
-  store(0);
-  __syncthreads();
-  for (int st = 0; st < steps; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < steps) load(k_begin + (st + 1) * kGBK);  // in flight during this step
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < kGBK / 16; ++ks) {
       uint4 av[TM], wv[TN];
@@ -130,7 +130,23 @@ __global__ __launch_bounds__(kGThreads) void gemm_bf16_kernel(GemmArgs a) {
         for (int y = 0; y < TN; ++y)
           acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(av[x]), as8(wv[y]), acc[x][y], 0, 0, 0);
     }
-    if (st + 1 < steps) store(buf ^ 1);  // the other buffer was last read a step ago
+  };
+  // step st is computed from LDS buffer st % 2; register set P carries even
+  // steps and Q odd ones, each loaded two steps before it is stored
+  Stage P, Q;
+  load(P, 0);
+  load(Q, 1);
+  store(P, 0);
+  __syncthreads();
+  for (int st = 0; st < steps; st += 2) {
+    load(P, st + 2);          // P was stored last step
+    compute(0);
+    if (st + 1 < steps) store(Q, 1);  // buffer 1 was last read two steps ago
+    __syncthreads();
+    if (st + 1 >= steps) break;
+    load(Q, st + 3);
+    compute(1);
+    if (st + 2 < steps) store(P, 0);
     __syncthreads();
   }
 
