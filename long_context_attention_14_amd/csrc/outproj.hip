@@ -52,7 +52,7 @@ struct GemmArgs {
 __device__ __forceinline__ gv8bf as8(uint4 u) { return __builtin_bit_cast(gv8bf, u); }
 
 template <int BM>
-__global__ __launch_bounds__(kGThreads) void gemm_bf16_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int WN = BM == 128 ? 2 : 4;        // waves along N
   constexpr int WM = 4 / WN;                   // waves along M
   constexpr int TM = BM / WM / 32;             // 32-row MFMA tiles per wave
@@ -66,8 +66,27 @@ __global__ __launch_bounds__(kGThreads) void gemm_bf16_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int j32 = lane & 31, g = lane >> 5;
   const int wm = w / WN, wn = w % WN;
-  const int n0 = blockIdx.x * kGBN, m0 = blockIdx.y * BM;
-  const int batch = blockIdx.z / a.n_split, split = blockIdx.z % a.n_split;
+  // Tile order (workgroup L runs on XCD L % 8, each XCD with its own L2): the
+  // (row tile, split, batch) triples are dealt to the XCDs in eight contiguous
+  // ranges, and an XCD takes each triple's column tiles one after another, so
+  // an A tile is read from memory by one XCD and reused from its L2 (a batch's
+  // W stays on the XCDs that own its rows).
+  const int n_tiles = a.N / kGBN, m_tiles = (a.M + BM - 1) / BM;
+  const long long n_trip = static_cast<long long>(m_tiles) * a.n_split * a.batches;
+  const long long L = blockIdx.x;
+  long long nt, trip;
+  if (n_trip % 8 == 0) {
+    const long long i = L / 8;
+    nt = i % n_tiles;
+    trip = (L % 8) * (n_trip / 8) + i / n_tiles;
+  } else {
+    nt = L % n_tiles;
+    trip = L / n_tiles;
+  }
+  const int n0 = static_cast<int>(nt) * kGBN;
+  const int m0 = static_cast<int>(trip % m_tiles) * BM;
+  const int split = static_cast<int>((trip / m_tiles) % a.n_split);
+  const int batch = static_cast<int>(trip / m_tiles / a.n_split);
   const uint16_t* Ab = a.A + batch * a.a_bstride;
   const uint16_t* Wb = a.W + batch * a.w_bstride + static_cast<long long>(n0) * a.K;
   const int k_begin = split * a.steps_per_split * kGBK;
@@ -301,8 +320,8 @@ hipError_t launch_gemm(GemmArgs a, void* ws, hipStream_t s) {
   a.steps_per_split = a.K / kGBK / a.n_split;
   a.part = a.n_split > 1 ? static_cast<float*>(ws) : nullptr;
   const int bm = gemm_bm(a.M);
-  const dim3 grid(static_cast<unsigned>(a.N / kGBN), static_cast<unsigned>((a.M + bm - 1) / bm),
-                  static_cast<unsigned>(a.batches * a.n_split));
+  const dim3 grid(static_cast<unsigned>(static_cast<long long>(a.N / kGBN) * ((a.M + bm - 1) / bm) *
+                                        a.batches * a.n_split));
   hipLaunchKernelGGL(gemm_bf16_kernel<128>, grid, dim3(kGThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
