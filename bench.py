@@ -17,9 +17,11 @@ Prints ONE JSON line.  The timed loop calls lca_decode_step.  For a CSA layer
 the library launches the indexer (the dominant kernel) with two HIP events
 (lca_decode_io.stage_events[1], [2]) as its dispatch's own start and end
 stamps, on every timed step, which gives that kernel's duration for the
-roofline without extra packets on the stream.  For HCA alone the dominant kernel
-is the attention: every 4th step records two events around its stage (an event
-record costs a few microseconds of GPU time, so the other steps record none).
+roofline.  The events are created with hipEventDisableSystemFence: a default
+event writes back and invalidates the caches when it is recorded, which cost
+11 us of GPU time per step around the stamped dispatch.  For HCA alone the
+dominant kernel is the attention: every 4th step records two events around its
+stage (the other steps record none).
 The per-stage breakdown ("stages_us") comes from an untimed diagnostic loop
 that sets all five events (the recorded ones include that cost).
 """
@@ -48,9 +50,15 @@ class HipEvents:
         self.ct = ctypes
         self.lib = ctypes.CDLL("libamdhip64.so")
 
+    # hipEventDisableSystemFence: timing-only events; a default event's record
+    # writes back and invalidates the caches, which costs several microseconds of
+    # GPU time around every stamped dispatch.  The stamps are read after a device
+    # synchronisation, so nothing needs the event itself to order memory.
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
     def create(self):
         e = self.ct.c_void_p()
-        assert self.lib.hipEventCreate(self.ct.byref(e)) == 0
+        assert self.lib.hipEventCreateWithFlags(self.ct.byref(e), self.DISABLE_SYSTEM_FENCE) == 0
         return e.value
 
     def elapsed_s(self, a, b):

@@ -465,14 +465,13 @@ int decode_enqueue(const lca_decode_layer* L, const lca_decode_io* io, void* wor
                                         scores, s, fused ? nullptr : hist,
                                         reinterpret_cast<hipEvent_t>(io->stage_events[1]),
                                         reinterpret_cast<hipEvent_t>(io->stage_events[2]),
-                                        fused ? &sw : nullptr, L->k),
+                                        fused ? &sw : nullptr, L->k, LCA_F32,
+                                        fused ? idx : nullptr),
                     "lca_decode_step/indexer");
     if (st != LCA_OK) return st;
-    if (fused)
-      st = hip_status(lca::launch_select_finish(L->B, 1, L->N_cap, q_pos, L->m, n_ent, L->k, idx, sw,
-                                                s),
-                      "lca_decode_step/topk");
-    else if (hist)
+    if (fused) {
+      // the indexer launch includes the finish pass
+    } else if (hist)
       st = hip_status(lca::launch_topk_from_hist(L->B, 1, L->N_cap, scores, q_pos, L->m, n_ent, L->k,
                                                  idx, ws + d.topk, s),
                       "lca_decode_step/topk");

@@ -327,6 +327,38 @@ __device__ inline void find_threshold_block(const uint32_t* lh, int want, int* s
   __syncthreads();
 }
 
+// Given a histogram of `nbins` bins (bin index order == key order), find the bin
+// d holding the `want`-th largest element (1-based), and the number of elements
+// in bins above d.  Run by one full wave (all 64 lanes); nbins % 64 == 0.
+// Lane l owns bins nbins-1-l*per .. nbins-per-l*per (descending).
+__device__ inline void find_bin_wave(const uint32_t* hist, int nbins, int want, int* out_bin,
+                                     int* out_above) {
+  const int lane = threadIdx.x & 63;
+  const int per = nbins / 64;
+  const int top = nbins - 1 - lane * per;
+  uint32_t local = 0;
+  for (int i = 0; i < per; ++i) local += hist[top - i];
+  // exclusive prefix over lanes (lane 0 holds the highest bins)
+  uint32_t incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  uint32_t run = incl - local;
+  if (run < static_cast<uint32_t>(want) && incl >= static_cast<uint32_t>(want)) {
+    for (int i = 0; i < per; ++i) {
+      const uint32_t h = hist[top - i];
+      if (run + h >= static_cast<uint32_t>(want)) {
+        *out_bin = top - i;
+        *out_above = static_cast<int>(run);
+        break;
+      }
+      run += h;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // internal launchers (defined next to their kernels, called by the C ABI)
 
@@ -346,38 +378,46 @@ hipError_t launch_state_append(int mode, int m, int B, int c, int n_win, const v
                                double rope_step, const KvPages& pg, hipStream_t s,
                                uint32_t* zero_buf = nullptr, long long zero_words = 0);
 // Fused indexer + selection workspace (rows = B * n_q, n_blk = ceil(N_cap / 128)).
-// hist must be zero before the indexer runs (select_zero_words(rows) words).  The indexer writes, for every
-// 128-entry block that holds visible entries, the (key, index) pairs of that
-// block which can still be among the row's k largest, in index order, and their
-// count; the finish pass selects the top k from them.
+// hist must be zero before the indexer runs (select_zero_words(rows) words).  A
+// row's 128-entry blocks are dealt round-robin to its wpr workgroups;
+// workgroup wi writes the (key, index) pairs of its blocks that can still be
+// among the row's k largest into its own region of the row's emit array (in no
+// particular order; the region starts at select_region(n_blk, wpr, wi) and
+// holds 128 slots per block the workgroup owns) and their count to
+// emit_cnt[row, wi]; a finish pass selects the row's top k from those pairs.
 constexpr int kSelBlock = 128;
 struct SelectWs {
   uint32_t* hist;      // [rows, 4096] score_bin histogram (hist_slot order)
-  int32_t* emit_cnt;   // [rows, n_blk]
-  uint2* emit;         // [rows, n_blk, 128] (score key, entry index) pairs
-  uint32_t* cand_key;  // [rows, N_cap] finish pass: threshold-bin keys when LDS overflows
+  int32_t* emit_cnt;   // [rows, n_blk]: pairs emitted by workgroup wi of the row (wi < wpr)
+  uint2* emit;         // [rows, n_blk * 128] (score key, entry index) pairs
+  uint32_t* cand_key;  // [rows, N_cap] selection: threshold-bin keys when LDS overflows
   int32_t* cand_idx;   // [rows, N_cap]
   int n_blk;
 };
+// first slot of workgroup wi's region in a row's emit array: workgroups before
+// wi own n_blk / wpr blocks each, one more when they come before n_blk % wpr
+__host__ __device__ __forceinline__ size_t select_region(int n_blk, int wpr, int wi) {
+  const int a = n_blk / wpr, r = n_blk % wpr;
+  return static_cast<size_t>(wi * a + (wi < r ? wi : r)) * kSelBlock;
+}
 size_t select_workspace_bytes(long long rows, int N_cap);
 long long select_zero_words(long long rows);
 SelectWs select_ws_in(void* ws, long long rows, int N_cap);
 // whether the fused path takes rows of N_cap entries and this k
 bool select_supported(int N_cap, int k);
-hipError_t launch_select_finish(int B, int n_q, int N_cap, const int32_t* q_pos, int m,
-                                const int32_t* n_entries, int k, int32_t* idx, const SelectWs& w,
-                                hipStream_t s);
 
 // hist (optional, [B*n_q, 4096], zeroed by the caller): the MFMA path adds the
 // score_bin histogram of every row's visible scores into it.  sel (optional,
-// MFMA formats only): the fused selecting sink; scores is then not written.
+// MFMA formats only): the fused selecting sink; scores is then not written and
+// the indexer writes every row's top k to sel_idx ([B*n_q, k], ascending entry
+// indices, ties to the lower index, -1 after min(k, vis)).
 hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const void* qI,
                           const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale,
                           int N_cap, const float* w, const int32_t* q_pos, int m,
                           const int32_t* n_entries, void* scores, hipStream_t s,
                           uint32_t* hist = nullptr, hipEvent_t ev_start = nullptr,
                           hipEvent_t ev_stop = nullptr, const SelectWs* sel = nullptr, int k = 0,
-                          int score_fmt = LCA_F32);
+                          int score_fmt = LCA_F32, int32_t* sel_idx = nullptr);
 size_t topk_workspace_bytes(int B, int n_q, int N_cap, int k);
 // scores: [B*n_q, N_cap] float32, or bf16 bits when score_fmt == LCA_BF16
 hipError_t launch_topk(int B, int n_q, int N_cap, const void* scores, const int32_t* q_pos, int m,

@@ -266,13 +266,13 @@ constexpr int kSelThreads = kWave * kSelWaves;
 constexpr int kSelMaxBlocks = 280;
 
 // After a workgroup's scores are final: bound the row's threshold bin from
-// below, write every entry at or above the bound into the per-block lists
-// (index order), then add the rest of the workgroup's histogram (lh holds the
-// counts not flushed yet) to the row's.  Histogram counts only grow, and the
-// counts in lh are added only after the row histogram has been read, so
-// (count read) + (count in lh) never exceeds the final count of a bin: if bins
-// >= b hold >= k entries by that sum, the final k-th largest key lies in bin
-// >= b.  Every entry of the final top-k is therefore emitted, whatever the
+// below, write every entry at or above the bound into the workgroup's region
+// of the row's emit array, then add the rest of the workgroup's histogram (lh
+// holds the counts not flushed yet) to the row's.  Histogram counts only grow,
+// and the counts in lh are added only after the row histogram has been read,
+// so (count read) + (count in lh) never exceeds the final count of a bin: if
+// bins >= b hold >= k entries by that sum, the final k-th largest key lies in
+// bin >= b.  Every entry of the final top-k is therefore emitted, whatever the
 // order in which workgroups run, and no workgroup waits for another.  The bound
 // looks at the blockDim bins ending 32 bins above the workgroup's highest bin;
 // entries elsewhere only make it weaker.
@@ -282,12 +282,16 @@ __device__ void select_emit(uint32_t* lh, const float* sc, int n_t, int wi, int 
   constexpr int NT = NW * kWave;
   __shared__ int sh_bin, scan_sh[NW];
   __shared__ uint32_t top_sh[NW];
+  __shared__ int emit_n;  // pairs written to the region so far
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   uint32_t* gh = o.hist + row * kScoreHistBins;
   for (int off = 32; off >= 1; off >>= 1)
     kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(kmax, off, kWave)));
   if (lane == 0) top_sh[wave] = kmax;
-  if (tid == 0) sh_bin = -1;
+  if (tid == 0) {
+    sh_bin = -1;
+    emit_n = 0;
+  }
   __syncthreads();
   uint32_t tk = 0;
 #pragma unroll
@@ -312,9 +316,10 @@ __device__ void select_emit(uint32_t* lh, const float* sc, int n_t, int wi, int 
   if (incl >= k && incl - v < k) sh_bin = bin;
   const int b_lb = __syncthreads_or(incl >= k) ? sh_bin : -1;
   // emission: wave w takes blocks w, w + NW, ...; lane l holds keys l and l + 64
-  // of a block, so two ballots give every emitted entry its place in index order.
-  // The scores of kEmitBatch blocks are read (unconditionally: the LDS array
-  // holds n_t whole blocks) before any is used, so the LDS reads overlap.
+  // of a block.  The scores of kEmitBatch blocks are read (unconditionally: the
+  // LDS array holds n_t whole blocks) before any is used, so the LDS reads
+  // overlap, and one LDS atomic per batch places the batch's pairs in the region.
+  uint2* reg = o.emit + static_cast<size_t>(row) * o.n_blk * kSelBlock + select_region(o.n_blk, wpr, wi);
   constexpr int kEmitBatch = 4;
   for (int t0 = wave; t0 < n_t; t0 += kEmitBatch * NW) {
     float s0[kEmitBatch], s1[kEmitBatch];
@@ -324,31 +329,342 @@ __device__ void select_emit(uint32_t* lh, const float* sc, int n_t, int wi, int 
       s0[u] = sc[t * kSelBlock + lane];
       s1[u] = sc[t * kSelBlock + kWave + lane];
     }
+    uint32_t k0[kEmitBatch], k1[kEmitBatch];
+    uint64_t m0[kEmitBatch], m1[kEmitBatch];
+    int n_tot = 0;
 #pragma unroll
     for (int u = 0; u < kEmitBatch; ++u) {
-      const int t = t0 + u * NW;
-      if (t >= n_t) break;  // the same for the whole wave
-      const int blk = wi + t * wpr;
-      const int i0 = blk * kSelBlock + lane, i1 = i0 + kWave;
-      const uint32_t k0 = score_key(s0[u]), k1 = score_key(s1[u]);
-      const bool e0 = i0 < vis && static_cast<int>(score_bin(k0)) >= b_lb;
-      const bool e1 = i1 < vis && static_cast<int>(score_bin(k1)) >= b_lb;
-      const uint64_t m0 = __ballot(e0), m1 = __ballot(e1);
-      const int n0 = __popcll(m0);
-      const size_t seg = static_cast<size_t>(row) * o.n_blk + blk;
-      if (e0) {
-        const int p = lanes_below64(m0);
-        o.emit[seg * kSelBlock + p] = make_uint2(k0, static_cast<uint32_t>(i0));
-      }
-      if (e1) {
-        const int p = n0 + lanes_below64(m1);
-        o.emit[seg * kSelBlock + p] = make_uint2(k1, static_cast<uint32_t>(i1));
-      }
-      if (lane == 0) o.emit_cnt[seg] = n0 + __popcll(m1);
+      const int t = t0 + u * NW;  // t < n_t is the same for the whole wave
+      const int i0 = (wi + t * wpr) * kSelBlock + lane, i1 = i0 + kWave;
+      k0[u] = score_key(s0[u]);
+      k1[u] = score_key(s1[u]);
+      const bool e0 = t < n_t && i0 < vis && static_cast<int>(score_bin(k0[u])) >= b_lb;
+      const bool e1 = t < n_t && i1 < vis && static_cast<int>(score_bin(k1[u])) >= b_lb;
+      m0[u] = __ballot(e0);
+      m1[u] = __ballot(e1);
+      n_tot += __popcll(m0[u]) + __popcll(m1[u]);
+    }
+    if (n_tot == 0) continue;  // the same for the whole wave
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&emit_n, n_tot);
+    base = __shfl(base, 0, kWave);
+#pragma unroll
+    for (int u = 0; u < kEmitBatch; ++u) {
+      const int i0 = (wi + (t0 + u * NW) * wpr) * kSelBlock + lane;
+      if ((m0[u] >> lane) & 1)
+        reg[base + lanes_below64(m0[u])] = make_uint2(k0[u], static_cast<uint32_t>(i0));
+      base += __popcll(m0[u]);
+      if ((m1[u] >> lane) & 1)
+        reg[base + lanes_below64(m1[u])] = make_uint2(k1[u], static_cast<uint32_t>(i0 + kWave));
+      base += __popcll(m1[u]);
     }
   }
   for (int bb = tid; bb < kScoreHistBins; bb += NT)
     if (lh[bb]) atomicAdd(&gh[hist_slot(bb)], lh[bb]);
+  __syncthreads();  // emit_n is final
+  if (tid == 0) o.emit_cnt[row * o.n_blk + wi] = emit_n;
+}
+
+// ---------------------------------------------------------------------------
+// Finish of the fused selection: one workgroup per row selects the row's top k
+// from the pairs the row's workgroups emitted (every entry of the final top k
+// is among them).  The row's final histogram gives the bin b* of the k-th
+// largest key and the count of keys above it; every emitted entry above b* is
+// selected, and the rest come from the entries in b* (the candidates; their
+// number is the bin's count): a radix select on the low 20 key bits finds the
+// key T of the last one taken, and when more candidates than needed carry T, a
+// second radix select on the entry index takes the lowest ones.  The selected
+// indices, in no order so far, are written out in ascending order through a
+// bitmap over the row's visible entries (2^19 entries per pass).  Wave w reads
+// the pairs of regions w, w + 16, ...; the counts, the first 256 pairs of each
+// wave's first region and the histogram are loaded together, so the common case
+// takes one memory round trip before the selection.
+constexpr int kMaxWpr = 256;            // workgroups per row the finish takes
+constexpr int kFinWaves = 16;
+constexpr int kFinThreads = kFinWaves * kWave;
+constexpr int kFinSpec = 4;             // pairs per lane loaded with the counts
+constexpr int kFinMaxK = 4096;
+constexpr int kFinCand = 8192;          // candidates held in LDS (else in global memory)
+constexpr int kFinBitmapWords = 16384;  // one output pass: 2^19 entries
+constexpr uint32_t kSkipKey = 0x80000000u;
+static_assert(kFinBitmapWords <= 2 * kFinCand, "the bitmap fits in the candidates' space");
+
+// exclusive block-wide prefix of one int per thread (NW full waves); *total is
+// the sum over the block.  Ends with a barrier, so scan_sh can be reused.
+template <int NW>
+__device__ __forceinline__ int block_excl_scan(int v, int* total, int* scan_sh) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += t;
+  }
+  if (lane == kWave - 1) scan_sh[wave] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int x = 0; x < NW; ++x) {
+    const int t = scan_sh[x];
+    before += x < wave ? t : 0;
+    tot += t;
+  }
+  *total = tot;
+  __syncthreads();
+  return before + incl - v;
+}
+
+// Among the n elements whose key(e) lacks kSkipKey (keys of 20 bits), the
+// want-th largest (1 <= want <= their number), by passes over bits 19..12,
+// 11..4 and 3..0.  Returns the key prefix found and sets *mask to the bits it
+// fixes: elements with (key & mask) > prefix are all taken, *gt of them, and
+// *eq elements have (key & mask) == prefix, of which want - *gt are taken.
+// The passes stop early once every element of the chosen digit is taken
+// (*eq == want - *gt).
+template <int NW, class KeyF>
+__device__ uint32_t radix_select20(int n, int want, KeyF key, uint32_t* rh, int* sh_rb, int* sh_ra,
+                                   uint32_t* mask_out, int* gt, int* eq) {
+  constexpr int NT = NW * kWave;
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, mask = 0;
+  int remaining = want, in_bin = 0;
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int sh = pass == 0 ? 12 : (pass == 1 ? 4 : 0);
+    const uint32_t dm = pass == 2 ? 0xfu : 0xffu;
+    for (int i = tid; i < 256; i += NT) rh[i] = 0;
+    if (tid == 0) {  // (set by the bin search; defined even if it found none)
+      *sh_rb = 0;
+      *sh_ra = 0;
+    }
+    __syncthreads();
+    for (int e = tid; e < n; e += NT) {
+      const uint32_t kk = key(e);
+      if (!(kk & kSkipKey) && (kk & mask) == prefix) atomicAdd(&rh[(kk >> sh) & dm], 1u);
+    }
+    __syncthreads();
+    if (tid < kWave) find_bin_wave(rh, 256, remaining, sh_rb, sh_ra);
+    __syncthreads();
+    const int bsel = *sh_rb;
+    prefix |= static_cast<uint32_t>(bsel) << sh;
+    mask |= dm << sh;
+    remaining -= *sh_ra;
+    in_bin = static_cast<int>(rh[bsel]);
+    __syncthreads();
+    if (in_bin == remaining) break;  // the same for every thread
+  }
+  *mask_out = mask;
+  *gt = want - remaining;
+  *eq = in_bin;
+  return prefix;
+}
+
+__global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
+    int n_q, int N_cap, int wpr, const int32_t* __restrict__ q_pos, int m,
+    const int32_t* __restrict__ n_entries, int k, SelectWs o, int32_t* __restrict__ sel_idx) {
+  constexpr int NT = kFinThreads;
+  __shared__ uint32_t lh[kScoreHistBins];
+  __shared__ int32_t sel[kFinMaxK];
+  __shared__ uint32_t cand[2 * kFinCand];  // keys, indices; then the output bitmap
+  __shared__ int sh_bin, sh_above, sh_nsel, sh_ncand, sh_rb, sh_ra;
+  __shared__ int scan_sh[kFinWaves];
+  __shared__ uint32_t rh[256];
+  uint32_t* ck = cand;
+  int32_t* ci = reinterpret_cast<int32_t*>(cand + kFinCand);
+  uint32_t* bm = cand;
+  const long long row = blockIdx.x;
+  const int b = static_cast<int>(row / n_q);
+  const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
+  if (vis <= k) return;  // written by the indexer
+  int32_t* out = sel_idx + row * k;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_part = min(wpr, (vis + kBlockKeys - 1) / kBlockKeys);
+  const uint2* em = o.emit + static_cast<size_t>(row) * o.n_blk * kSelBlock;
+  // the histogram words, the count of the wave's first region and its first
+  // 256 pairs (slots clamped to the region), all in flight together
+  const uint32_t* gh = o.hist + row * kScoreHistBins;
+  constexpr int kHv = kScoreHistBins / NT;
+  uint32_t hv[kHv];
+#pragma unroll
+  for (int u = 0; u < kHv; ++u) hv[u] = gh[tid + u * NT];
+  int cnt0 = 0;
+  uint2 pr[kFinSpec];
+  size_t rb0 = 0;
+  if (wave < n_part) {
+    rb0 = select_region(o.n_blk, wpr, wave);
+    const int capc = static_cast<int>(select_region(o.n_blk, wpr, wave + 1) - rb0);
+    cnt0 = o.emit_cnt[row * o.n_blk + wave];
+#pragma unroll
+    for (int u = 0; u < kFinSpec; ++u) pr[u] = em[rb0 + min(lane + u * kWave, capc - 1)];
+  }
+#pragma unroll
+  for (int u = 0; u < kHv; ++u) lh[hist_bin_of_slot(tid + u * NT)] = hv[u];
+  if (tid == 0) {
+    sh_nsel = 0;
+    sh_ncand = 0;
+    sh_bin = 0;  // (set below; defined even if the histogram were short of k)
+    sh_above = 0;
+  }
+  __syncthreads();
+  // threshold bin b*: thread t sums bins [4095 - 4t - 3, 4095 - 4t]
+  constexpr int per = kScoreHistBins / NT;
+  const int topb = kScoreHistBins - 1 - per * tid;
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < per; ++i) local += static_cast<int>(lh[topb - i]);
+  int total;
+  int run = block_excl_scan<kFinWaves>(local, &total, scan_sh);
+  if (run < k && run + local >= k) {
+    for (int i = 0; i < per; ++i) {
+      const int h = static_cast<int>(lh[topb - i]);
+      if (run + h >= k) {
+        sh_bin = topb - i;
+        sh_above = run;
+        break;
+      }
+      run += h;
+    }
+  }
+  __syncthreads();
+  const int bstar = sh_bin, above = sh_above;
+  const int C = static_cast<int>(lh[bstar]);
+  const int need = k - above;  // 1 <= need <= C
+  const bool cand_lds = C <= kFinCand;
+  uint32_t* gck = o.cand_key + row * N_cap;
+  int32_t* gci = o.cand_idx + row * N_cap;
+  const int cap = cand_lds ? kFinCand : N_cap;
+  // above b* -> sel, in b* -> candidates; one LDS atomic per kind and wave per
+  // kFinSpec * 64 pairs
+  auto classify = [&](const uint2* p, int n_valid) {
+    uint64_t ms[kFinSpec], mc[kFinSpec];
+    int ns = 0, nc = 0;
+#pragma unroll
+    for (int u = 0; u < kFinSpec; ++u) {
+      const bool valid = lane + u * kWave < n_valid;
+      const int bin = static_cast<int>(score_bin(p[u].x));
+      ms[u] = __ballot(valid && bin > bstar);
+      mc[u] = __ballot(valid && bin == bstar);
+      ns += __popcll(ms[u]);
+      nc += __popcll(mc[u]);
+    }
+    int bs = 0, bc = 0;
+    if (lane == 0) {
+      if (ns) bs = atomicAdd(&sh_nsel, ns);
+      if (nc) bc = atomicAdd(&sh_ncand, nc);
+    }
+    bs = __shfl(bs, 0, kWave);
+    bc = __shfl(bc, 0, kWave);
+#pragma unroll
+    for (int u = 0; u < kFinSpec; ++u) {
+      if ((ms[u] >> lane) & 1) {
+        const int q = bs + lanes_below64(ms[u]);
+        if (q < k) sel[q] = static_cast<int32_t>(p[u].y);
+      }
+      bs += __popcll(ms[u]);
+      if ((mc[u] >> lane) & 1) {
+        const int q = bc + lanes_below64(mc[u]);
+        if (q < cap) {
+          if (cand_lds) {
+            ck[q] = p[u].x;
+            ci[q] = static_cast<int32_t>(p[u].y);
+          } else {
+            gck[q] = p[u].x;
+            gci[q] = static_cast<int32_t>(p[u].y);
+          }
+        }
+      }
+      bc += __popcll(mc[u]);
+    }
+  };
+  constexpr int kChunk = kFinSpec * kWave;
+  for (int sg = wave; sg < n_part; sg += kFinWaves) {  // the same for the whole wave
+    size_t rb = rb0;
+    int cnt = cnt0;
+    if (sg != wave) {
+      rb = select_region(o.n_blk, wpr, sg);
+      cnt = o.emit_cnt[row * o.n_blk + sg];
+    }
+    for (int c0 = 0; c0 < cnt; c0 += kChunk) {
+      if (sg != wave || c0 > 0) {
+#pragma unroll
+        for (int u = 0; u < kFinSpec; ++u) pr[u] = em[rb + min(c0 + lane + u * kWave, cnt - 1)];
+      }
+      classify(pr, cnt - c0);
+    }
+  }
+  __syncthreads();
+  const int nC = min(sh_ncand, cap);
+  auto ckey = [&](int e) -> uint32_t { return (cand_lds ? ck[e] : gck[e]) & 0xfffffu; };
+  auto cidx = [&](int e) -> int32_t { return cand_lds ? ci[e] : gci[e]; };
+  // the need largest candidates (low 20 key bits; ties to the lower index)
+  uint32_t T = 0, tmask = 0;
+  // candidates with (key & tmask) == T are taken when ((0xfffff - index) & xmask) >= X
+  uint32_t X = 0, xmask = 0;
+  if (need < nC) {
+    int gt, eq;
+    T = radix_select20<kFinWaves>(nC, need, ckey, rh, &sh_rb, &sh_ra, &tmask, &gt, &eq);
+    const int need_eq = need - gt;
+    if (eq > need_eq) {  // T is a whole key here: more candidates carry it than are taken
+      auto inv_idx = [&](int e) -> uint32_t {
+        return ckey(e) == T ? 0xfffffu - static_cast<uint32_t>(cidx(e)) : kSkipKey;
+      };
+      int gt2, eq2;
+      X = radix_select20<kFinWaves>(nC, need_eq, inv_idx, rh, &sh_rb, &sh_ra, &xmask, &gt2, &eq2);
+    }
+  }
+  for (int e0 = 0; e0 < nC; e0 += NT) {
+    const int e = e0 + tid;
+    bool take = false;
+    int32_t id = 0;
+    if (e < nC) {
+      const uint32_t kk = ckey(e) & tmask;
+      id = cidx(e);
+      take = need >= nC || kk > T ||
+             (kk == T && ((0xfffffu - static_cast<uint32_t>(id)) & xmask) >= X);
+    }
+    const uint64_t mt = __ballot(take);
+    int bs = 0;
+    if (lane == 0 && mt) bs = atomicAdd(&sh_nsel, __popcll(mt));
+    bs = __shfl(bs, 0, kWave);
+    if (take) {
+      const int q = bs + lanes_below64(mt);
+      if (q < k) sel[q] = id;
+    }
+  }
+  __syncthreads();
+  const int n_sel = min(sh_nsel, k);
+  // ascending output through a bitmap over the visible entries
+  int done = 0;
+  for (int base = 0; base < vis; base += 32 * kFinBitmapWords) {
+    const int nbits = min(32 * kFinBitmapWords, vis - base);
+    const int nw = (nbits + 31) >> 5;
+    for (int w = tid; w < nw; w += NT) bm[w] = 0u;
+    __syncthreads();
+    for (int i = tid; i < n_sel; i += NT) {
+      const int x = sel[i] - base;
+      if (x >= 0 && x < nbits) atomicOr(&bm[x >> 5], 1u << (x & 31));
+    }
+    __syncthreads();
+    const int wpt = (nw + NT - 1) / NT, w0 = tid * wpt;
+    int c = 0;
+    for (int j = 0; j < wpt; ++j)
+      if (w0 + j < nw) c += __popc(bm[w0 + j]);
+    int tot;
+    int at = done + block_excl_scan<kFinWaves>(c, &tot, scan_sh);
+    for (int j = 0; j < wpt; ++j) {
+      uint32_t bits = w0 + j < nw ? bm[w0 + j] : 0u;
+      while (bits) {
+        const int bit = __ffs(bits) - 1;
+        if (at < k) out[at] = base + (w0 + j) * 32 + bit;
+        ++at;
+        bits &= bits - 1u;
+      }
+    }
+    done += tot;
+    __syncthreads();  // before the next pass clears the bitmap
+  }
+  for (int i = done + tid; i < k; i += NT) out[i] = -1;  // (none when the data is consistent)
 }
 
 // One 12-wave workgroup per CU.  Rows are interleaved over the grid (row =
@@ -364,7 +680,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void indexer_select_kernel(
     const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qI_scale,
     const uint8_t* __restrict__ kI, const uint8_t* __restrict__ kI_scale, int n_q, int N_cap,
     int wpr, const float* __restrict__ w, const int32_t* __restrict__ q_pos, int m,
-    const int32_t* __restrict__ n_entries, SelectWs sel, int k) {
+    const int32_t* __restrict__ n_entries, SelectWs sel, int k, int32_t* __restrict__ sel_idx) {
   constexpr int kRowBytes = MX ? 64 : 128;
   constexpr int kFirst = 3;  // groups per wave assigned before the counter
   __shared__ uint32_t lh[kScoreHistBins];
@@ -376,6 +692,12 @@ __global__ __launch_bounds__(kSelThreads, 1) void indexer_select_kernel(
   const int wi = static_cast<int>(blockIdx.x / rows);
   const int b = static_cast<int>(row / n_q);
   const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
+  int32_t* out = sel_idx + row * k;
+  if (vis <= k) {  // every visible entry is selected: no scores needed
+    if (wi == 0)
+      for (int i = threadIdx.x; i < k; i += kSelThreads) out[i] = i < vis ? i : -1;
+    return;
+  }
   if (wi * kBlockKeys >= vis) return;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
@@ -650,7 +972,7 @@ hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const v
                           int N_cap, const float* w, const int32_t* q_pos, int m,
                           const int32_t* n_entries, void* scores, hipStream_t s,
                           uint32_t* hist, hipEvent_t ev_start, hipEvent_t ev_stop,
-                          const SelectWs* sel, int k, int score_fmt) {
+                          const SelectWs* sel, int k, int score_fmt, int32_t* sel_idx) {
   const long long rows = static_cast<long long>(B) * n_q;
   if (rows == 0 || N_cap == 0) return hipSuccess;
   if (score_fmt != LCA_F32 && score_fmt != LCA_BF16) return hipErrorInvalidValue;
@@ -686,6 +1008,7 @@ hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const v
     long long wpr = std::max<long long>(device_cus() / rows,
                                         (max_blocks + kSelMaxBlocks - 1) / kSelMaxBlocks);
     wpr = std::min(wpr, max_blocks);
+    if (wpr > kMaxWpr || k < 1 || k > kFinMaxK || sel_idx == nullptr) return hipErrorInvalidValue;
     const size_t lds = sizeof(float) * kBlockKeys * static_cast<size_t>((max_blocks + wpr - 1) / wpr);
     const dim3 grid(static_cast<unsigned>(rows * wpr)), block(kSelThreads);
     const int iw = static_cast<int>(wpr);
@@ -702,14 +1025,17 @@ hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const v
       }
       if (ev_start || ev_stop)
         hipExtLaunchKernelGGL(kern, grid, block, lds, s, ev_start, ev_stop, 0, q8, qI_scale, k8,
-                              kI_scale, n_q, N_cap, iw, w, q_pos, m, n_entries, so, k);
+                              kI_scale, n_q, N_cap, iw, w, q_pos, m, n_entries, so, k, sel_idx);
       else
         hipLaunchKernelGGL(kern, grid, block, lds, s, q8, qI_scale, k8, kI_scale, n_q, N_cap, iw, w,
-                           q_pos, m, n_entries, so, k);
+                           q_pos, m, n_entries, so, k, sel_idx);
     };
     if (mx) go(indexer_select_kernel<true>);
     else go(indexer_select_kernel<false>);
-    return e != hipSuccess ? e : hipGetLastError();
+    if (e != hipSuccess || (e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(select_finish_kernel, dim3(static_cast<unsigned>(rows)), dim3(kFinThreads), 0, s,
+                       n_q, N_cap, iw, q_pos, m, n_entries, k, so, sel_idx);
+    return hipGetLastError();
   }
   if (!hist && n_q >= kRowsPerWG * 8) {
     // many rows per sequence: row groups share each key tile through LDS

@@ -35,38 +35,6 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
 }
 
-// Given a histogram of `nbins` bins (bin index order == key order), find the bin
-// d holding the `want`-th largest element (1-based), and the number of elements
-// in bins above d.  Run by one full wave (all 64 lanes); nbins % 64 == 0.
-// Lane l owns bins nbins-1-l*per .. nbins-per-l*per (descending).
-__device__ void find_bin_wave(const uint32_t* hist, int nbins, int want, int* out_bin,
-                              int* out_above) {
-  const int lane = threadIdx.x & 63;
-  const int per = nbins / 64;
-  const int top = nbins - 1 - lane * per;
-  uint32_t local = 0;
-  for (int i = 0; i < per; ++i) local += hist[top - i];
-  // exclusive prefix over lanes (lane 0 holds the highest bins)
-  uint32_t incl = local;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t v = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += v;
-  }
-  uint32_t run = incl - local;
-  if (run < static_cast<uint32_t>(want) && incl >= static_cast<uint32_t>(want)) {
-    for (int i = 0; i < per; ++i) {
-      const uint32_t h = hist[top - i];
-      if (run + h >= static_cast<uint32_t>(want)) {
-        *out_bin = top - i;
-        *out_above = static_cast<int>(run);
-        break;
-      }
-      run += h;
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // LDS path
 
@@ -586,199 +554,9 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
 
 
 // ---------------------------------------------------------------------------
-// finish of the fused indexer selection (SelectWs): the indexer emitted, per
-// 128-entry block and in index order, a superset of the row's top k.  One
-// workgroup per row: the exact threshold bin b* from the final histogram, the
-// block counts' prefix sums, a gather of the emitted pairs into LDS, an ordered
-// split into "above b*" (all selected) and "in b*" (candidates), the radix
-// selection among the candidates, and the merge of the two ascending lists.
-constexpr int kMaxBlk = 8192;     // blocks per row (N_cap <= 1 Mi entries)
-constexpr int kEmitLds = 8192;    // emitted pairs held in LDS (else read from global)
-constexpr int kSegPerThread = kMaxBlk / kRowThreads;
-
-constexpr int kEmitPerThread = kEmitLds / kRowThreads;  // 8
-
-__global__ __launch_bounds__(kRowThreads) void select_finish_kernel(
-    int N_cap, int n_q, const int32_t* __restrict__ q_pos, int m, const int32_t* __restrict__ n_entries,
-    int k, SelectWs ws, int32_t* __restrict__ idx) {
-  // S and Ch (the two sorted lists) first serve as the gather's block table
-  static_assert(2 * kMaxK >= kEmitLds, "block table fits in S and Ch");
-  __shared__ int32_t SCh[2 * kMaxK];
-  int32_t* S = SCh;
-  int32_t* Ch = SCh + kMaxK;
-  int32_t* blk_of = SCh;  // [E]: block of emitted entry p (gather only)
-  __shared__ int seg_off[kMaxBlk + 1];
-  __shared__ uint32_t ck[kEmitLds];
-  __shared__ int32_t ci[kEmitLds];
-  __shared__ uint32_t lh[kHistBins];
-  __shared__ uint32_t hist[256];
-  __shared__ int sh_bin, sh_above, sh_b2, sh_a2;
-  __shared__ int scan_sh[kRowThreads / 64], scan_a[kRowThreads / 64], scan_b[kRowThreads / 64];
-  __shared__ uint32_t wgt[kRowThreads / 64], weq[kRowThreads / 64];
-  const long long row = blockIdx.x;
-  const int b = static_cast<int>(row / n_q);
-  const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int32_t* out = idx + row * k;
-  const int nb = (vis + kSelBlock - 1) / kSelBlock;
-  const size_t seg0 = static_cast<size_t>(row) * ws.n_blk;
-  // the row histogram and the block counts, loaded together
-  const int q = (nb + kRowThreads - 1) / kRowThreads;  // blocks [t*q, t*q + q) of thread t
-  uint32_t hv[kHistBins / kRowThreads];
-#pragma unroll
-  for (int u = 0; u < kHistBins / kRowThreads; ++u)  // word order (coalesced)
-    hv[u] = ws.hist[row * kHistBins + tid + u * kRowThreads];
-  int cnt[kSegPerThread];
-  int local = 0;
-#pragma unroll
-  for (int u = 0; u < kSegPerThread; ++u) {
-    const int sgi = tid * q + u;
-    cnt[u] = (u < q && sgi < nb) ? ws.emit_cnt[seg0 + sgi] : 0;
-    local += cnt[u];
-  }
-#pragma unroll
-  for (int u = 0; u < kHistBins / kRowThreads; ++u) lh[hist_bin_of_slot(tid + u * kRowThreads)] = hv[u];
-  if (tid == 0) {
-    sh_bin = -1;
-    sh_above = vis;
-  }
-  int run, dummy, E, dummy2;
-  block_scan2(local, 0, &run, &dummy, &E, &dummy2, scan_a, scan_b);
-#pragma unroll
-  for (int u = 0; u < kSegPerThread; ++u) {
-    const int sgi = tid * q + u;
-    if (u < q && sgi < nb) seg_off[sgi] = run;
-    run += cnt[u];
-  }
-  if (tid == 0) seg_off[nb] = E;
-  __syncthreads();
-  // exact threshold bin b* of the row (vis <= k: every entry is selected)
-  if (vis > k) find_threshold_block(lh, k, &sh_bin, &sh_above, scan_sh);
-  const int bstar = sh_bin;
-  const int need = vis <= k ? 0 : k - sh_above;
-  int nS = 0, nC = 0;
-  if (E <= kEmitLds) {
-    // block table: every thread labels its own blocks' entries
-#pragma unroll
-    for (int u = 0; u < kSegPerThread; ++u) {
-      const int sgi = tid * q + u;
-      if (u < q && sgi < nb)
-        for (int p = seg_off[sgi]; p < seg_off[sgi + 1]; ++p) blk_of[p] = sgi;
-    }
-    __syncthreads();
-    // gather: entry p = tid + 1024 u (neighbouring lanes read neighbouring slots
-    // of a block), one 8-byte load each, all loads at once
-    size_t off[kEmitPerThread];
-#pragma unroll
-    for (int u = 0; u < kEmitPerThread; ++u) {
-      const int p = tid + u * kRowThreads;
-      off[u] = seg0 * kSelBlock;
-      if (p < E) {
-        const int sgp = blk_of[p];
-        off[u] = (seg0 + sgp) * kSelBlock + (p - seg_off[sgp]);
-      }
-    }
-    uint2 pr[kEmitPerThread];
-#pragma unroll
-    for (int u = 0; u < kEmitPerThread; ++u) pr[u] = ws.emit[off[u]];
-#pragma unroll
-    for (int u = 0; u < kEmitPerThread; ++u) {
-      const int p = tid + u * kRowThreads;
-      if (p < E) {
-        ck[p] = pr[u].x;
-        ci[p] = static_cast<int32_t>(pr[u].y);
-      }
-    }
-    __syncthreads();
-    // thread t then takes entries [8t, 8t + 8) in order
-    const int p0 = tid * kEmitPerThread;
-    uint32_t key[kEmitPerThread];
-    int32_t id[kEmitPerThread];
-#pragma unroll
-    for (int u = 0; u < kEmitPerThread; ++u) {
-      key[u] = p0 + u < E ? ck[p0 + u] : 0u;
-      id[u] = p0 + u < E ? ci[p0 + u] : 0;
-    }
-    int ns = 0, nc = 0;
-#pragma unroll
-    for (int u = 0; u < kEmitPerThread; ++u) {
-      const int bin = static_cast<int>(score_bin(key[u]));
-      ns += (p0 + u < E && bin > bstar) ? 1 : 0;
-      nc += (p0 + u < E && bin == bstar) ? 1 : 0;
-    }
-    int os, oc, ts, tc;
-    block_scan2(ns, nc, &os, &oc, &ts, &tc, scan_a, scan_b);  // (every read of ck/ci is done)
-#pragma unroll
-    for (int u = 0; u < kEmitPerThread; ++u) {
-      if (p0 + u >= E) continue;
-      const int bin = static_cast<int>(score_bin(key[u]));
-      if (bin > bstar) {
-        if (os < kMaxK) S[os] = id[u];
-        ++os;
-      } else if (bin == bstar) {
-        ck[oc] = key[u];
-        ci[oc] = id[u];
-        ++oc;
-      }
-    }
-    nS = min(ts, k);
-    __syncthreads();
-    auto cand_key = [&](int p) -> uint32_t { return ck[p]; };
-    auto cand_idx = [&](int p) -> int32_t { return ci[p]; };
-    nC = select_candidates(tc, need, cand_key, cand_idx, Ch, hist, &sh_b2, &sh_a2, wgt, weq);
-  } else {
-    // more emitted entries than LDS holds: ordered split straight from global
-    // memory, candidates to the row's global candidate arrays
-    uint32_t* gck = ws.cand_key + row * N_cap;
-    int32_t* gci = ws.cand_idx + row * N_cap;
-    int run_s = 0, run_c = 0;
-    for (int base = 0; base < E; base += kRowThreads) {
-      const int p = base + tid;
-      const bool valid = p < E;
-      uint32_t key = 0u;
-      int32_t id = 0;
-      if (valid) {
-        const int sgp = seg_of(seg_off, nb, p);
-        const size_t o = (seg0 + sgp) * kSelBlock + (p - seg_off[sgp]);
-        const uint2 e = ws.emit[o];
-        key = e.x;
-        id = static_cast<int32_t>(e.y);
-      }
-      const int bin = static_cast<int>(score_bin(key));
-      const bool is_s = valid && bin > bstar;
-      const bool is_c = valid && bin == bstar;
-      const uint64_t bs = __ballot(is_s), bc = __ballot(is_c);
-      if (lane == 0) {
-        wgt[wv] = __popcll(bs);
-        weq[wv] = __popcll(bc);
-      }
-      __syncthreads();
-      int os = run_s, oc = run_c, ts = 0, tc = 0;
-      for (int x = 0; x < kRowThreads / 64; ++x) {
-        if (x < wv) {
-          os += wgt[x];
-          oc += weq[x];
-        }
-        ts += wgt[x];
-        tc += weq[x];
-      }
-      const int ps = os + lanes_below(bs), pc = oc + lanes_below(bc);
-      if (is_s && ps < kMaxK) S[ps] = id;
-      if (is_c) {
-        gck[pc] = key;
-        gci[pc] = id;
-      }
-      run_s += ts;
-      run_c += tc;
-      __syncthreads();
-    }
-    nS = min(run_s, k);
-    auto cand_key = [&](int p) -> uint32_t { return gck[p]; };
-    auto cand_idx = [&](int p) -> int32_t { return gci[p]; };
-    nC = select_candidates(run_c, need, cand_key, cand_idx, Ch, hist, &sh_b2, &sh_a2, wgt, weq);
-  }
-  merge_to_output(S, nS, Ch, nC, out, k);
-}
+// Workspace of the fused indexer selection (SelectWs; the selection itself
+// runs inside the indexer).
+constexpr int kMaxBlk = 8192;  // blocks per row (N_cap <= 1 Mi entries)
 
 struct SelectLayout {
   size_t hist, emit_cnt, emit, cand_key, cand_idx, total;
@@ -891,17 +669,6 @@ SelectWs select_ws_in(void* ws, long long rows, int N_cap) {
   w.cand_idx = reinterpret_cast<int32_t*>(p + L.cand_idx);
   w.n_blk = (N_cap + kSelBlock - 1) / kSelBlock;
   return w;
-}
-
-hipError_t launch_select_finish(int B, int n_q, int N_cap, const int32_t* q_pos, int m,
-                                const int32_t* n_entries, int k, int32_t* idx, const SelectWs& w,
-                                hipStream_t s) {
-  const long long rows = static_cast<long long>(B) * n_q;
-  if (rows == 0) return hipSuccess;
-  if (!select_supported(N_cap, k)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(select_finish_kernel, dim3(static_cast<unsigned>(rows)), dim3(kRowThreads), 0, s,
-                     N_cap, n_q, q_pos, m, n_entries, k, w, idx);
-  return hipGetLastError();
 }
 
 }  // namespace lca
