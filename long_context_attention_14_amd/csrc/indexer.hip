@@ -376,13 +376,14 @@ __device__ void select_emit(uint32_t* lh, const float* sc, int n_t, int wi, int 
 // second radix select on the entry index takes the lowest ones.  The selected
 // indices, in no order so far, are written out in ascending order through a
 // bitmap over the row's visible entries (2^19 entries per pass).  Wave w reads
-// the pairs of regions w, w + 16, ...; the counts, the first 256 pairs of each
-// wave's first region and the histogram are loaded together, so the common case
-// takes one memory round trip before the selection.
+// the pairs of regions w, w + 16, ...; the histogram, the counts and the first
+// 512 pairs of each wave's first region do not depend on the row's length, so
+// they are loaded at once with it: the common case takes one memory round trip
+// before the selection.
 constexpr int kMaxWpr = 256;            // workgroups per row the finish takes
 constexpr int kFinWaves = 16;
 constexpr int kFinThreads = kFinWaves * kWave;
-constexpr int kFinSpec = 4;             // pairs per lane loaded with the counts
+constexpr int kFinSpec = 8;             // pairs per lane loaded with the counts
 constexpr int kFinMaxK = 4096;
 constexpr int kFinCand = 8192;          // candidates held in LDS (else in global memory)
 constexpr int kFinBitmapWords = 16384;  // one output pass: 2^19 entries
@@ -465,7 +466,7 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   constexpr int NT = kFinThreads;
   __shared__ uint32_t lh[kScoreHistBins];
   __shared__ int32_t sel[kFinMaxK];
-  __shared__ uint32_t cand[2 * kFinCand];  // keys, indices; then the output bitmap
+  __shared__ __attribute__((aligned(16))) uint32_t cand[2 * kFinCand];  // keys, indices; then the output bitmap
   __shared__ int sh_bin, sh_above, sh_nsel, sh_ncand, sh_rb, sh_ra;
   __shared__ int scan_sh[kFinWaves];
   __shared__ uint32_t rh[256];
@@ -473,16 +474,12 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   int32_t* ci = reinterpret_cast<int32_t*>(cand + kFinCand);
   uint32_t* bm = cand;
   const long long row = blockIdx.x;
-  const int b = static_cast<int>(row / n_q);
-  const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
-  if (vis <= k) return;  // written by the indexer
-  int32_t* out = sel_idx + row * k;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n_part = min(wpr, (vis + kBlockKeys - 1) / kBlockKeys);
   const uint2* em = o.emit + static_cast<size_t>(row) * o.n_blk * kSelBlock;
   // the histogram words, the count of the wave's first region and its first
-  // 256 pairs (slots clamped to the region), all in flight together
+  // 512 pairs (slots clamped to the region; every one of the wpr regions
+  // exists, the row's length decides below which are used)
   const uint32_t* gh = o.hist + row * kScoreHistBins;
   constexpr int kHv = kScoreHistBins / NT;
   uint32_t hv[kHv];
@@ -491,13 +488,18 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   int cnt0 = 0;
   uint2 pr[kFinSpec];
   size_t rb0 = 0;
-  if (wave < n_part) {
+  if (wave < wpr) {
     rb0 = select_region(o.n_blk, wpr, wave);
     const int capc = static_cast<int>(select_region(o.n_blk, wpr, wave + 1) - rb0);
     cnt0 = o.emit_cnt[row * o.n_blk + wave];
 #pragma unroll
     for (int u = 0; u < kFinSpec; ++u) pr[u] = em[rb0 + min(lane + u * kWave, capc - 1)];
   }
+  const int b = static_cast<int>(row / n_q);
+  const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
+  if (vis <= k) return;  // written by the indexer
+  int32_t* out = sel_idx + row * k;
+  const int n_part = min(wpr, (vis + kBlockKeys - 1) / kBlockKeys);
 #pragma unroll
   for (int u = 0; u < kHv; ++u) lh[hist_bin_of_slot(tid + u * NT)] = hv[u];
   if (tid == 0) {
@@ -639,30 +641,43 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   for (int base = 0; base < vis; base += 32 * kFinBitmapWords) {
     const int nbits = min(32 * kFinBitmapWords, vis - base);
     const int nw = (nbits + 31) >> 5;
-    for (int w = tid; w < nw; w += NT) bm[w] = 0u;
+    const int nw4 = (nw + 3) & ~3;  // (<= kFinBitmapWords, a multiple of 4)
+    for (int w = 4 * tid; w < nw4; w += 4 * NT) *reinterpret_cast<uint4*>(bm + w) = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
     for (int i = tid; i < n_sel; i += NT) {
       const int x = sel[i] - base;
       if (x >= 0 && x < nbits) atomicOr(&bm[x >> 5], 1u << (x & 31));
     }
     __syncthreads();
-    const int wpt = (nw + NT - 1) / NT, w0 = tid * wpt;
+    // thread t: words [8t, 8t + 8) (two 16-byte LDS reads), more per thread
+    // beyond 8192 words
+    const int wpt = ((nw + NT - 1) / NT + 3) & ~3, w0 = tid * wpt;
     int c = 0;
-    for (int j = 0; j < wpt; ++j)
-      if (w0 + j < nw) c += __popc(bm[w0 + j]);
+    for (int j = 0; j < wpt; j += 4) {
+      if (w0 + j < nw) {  // (the words up to nw4 are cleared)
+        const uint4 v = *reinterpret_cast<const uint4*>(bm + w0 + j);
+        c += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
+      }
+    }
     int tot;
     int at = done + block_excl_scan<kFinWaves>(c, &tot, scan_sh);
-    for (int j = 0; j < wpt; ++j) {
-      uint32_t bits = w0 + j < nw ? bm[w0 + j] : 0u;
-      while (bits) {
-        const int bit = __ffs(bits) - 1;
-        if (at < k) out[at] = base + (w0 + j) * 32 + bit;
-        ++at;
-        bits &= bits - 1u;
+    for (int j = 0; j < wpt; j += 4) {
+      if (w0 + j >= nw) break;
+      const uint4 v = *reinterpret_cast<const uint4*>(bm + w0 + j);
+      const uint32_t words[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t bits = words[q];
+        while (bits) {
+          const int bit = __ffs(bits) - 1;
+          if (at < k) out[at] = base + (w0 + j + q) * 32 + bit;
+          ++at;
+          bits &= bits - 1u;
+        }
       }
     }
     done += tot;
-    __syncthreads();  // before the next pass clears the bitmap
+    if (base + 32 * kFinBitmapWords < vis) __syncthreads();  // the next pass clears the bitmap
   }
   for (int i = done + tid; i < k; i += NT) out[i] = -1;  // (none when the data is consistent)
 }
