@@ -377,9 +377,9 @@ __device__ void select_emit(uint32_t* lh, const float* sc, int n_t, int wi, int 
 // indices, in no order so far, are written out in ascending order through a
 // bitmap over the row's visible entries (2^19 entries per pass).  Wave w reads
 // the pairs of regions w, w + 16, ...; the histogram, the counts and the first
-// 512 pairs of each wave's first region do not depend on the row's length, so
-// they are loaded at once with it: the common case takes one memory round trip
-// before the selection.
+// 512 pairs of the wave's regions (up to 8 regions) do not depend on the row's
+// length, so they are loaded at once with it: the common case takes one memory
+// round trip before the selection.
 constexpr int kMaxWpr = 256;            // workgroups per row the finish takes
 constexpr int kFinWaves = 16;
 constexpr int kFinThreads = kFinWaves * kWave;
@@ -477,23 +477,30 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint2* em = o.emit + static_cast<size_t>(row) * o.n_blk * kSelBlock;
-  // the histogram words, the count of the wave's first region and its first
-  // 512 pairs (slots clamped to the region; every one of the wpr regions
-  // exists, the row's length decides below which are used)
+  // the histogram words, and the counts and first pairs of the wave's regions
+  // w, w + 16, ... (up to 8 of them; the 8 pair slots of a lane are shared
+  // out, 64 pairs each, slots clamped to the region; every one of the wpr
+  // regions exists, the row's length decides below which are used)
   const uint32_t* gh = o.hist + row * kScoreHistBins;
   constexpr int kHv = kScoreHistBins / NT;
   uint32_t hv[kHv];
 #pragma unroll
   for (int u = 0; u < kHv; ++u) hv[u] = gh[tid + u * NT];
-  int cnt0 = 0;
+  const int spr_lg = wpr > 4 * kFinWaves ? 0 : (wpr > 2 * kFinWaves ? 1 : (wpr > kFinWaves ? 2 : 3));
+  const int rpw = kFinSpec >> spr_lg;  // regions per wave read speculatively
+  int cu[kFinSpec];
   uint2 pr[kFinSpec];
-  size_t rb0 = 0;
-  if (wave < wpr) {
-    rb0 = select_region(o.n_blk, wpr, wave);
-    const int capc = static_cast<int>(select_region(o.n_blk, wpr, wave + 1) - rb0);
-    cnt0 = o.emit_cnt[row * o.n_blk + wave];
 #pragma unroll
-    for (int u = 0; u < kFinSpec; ++u) pr[u] = em[rb0 + min(lane + u * kWave, capc - 1)];
+  for (int u = 0; u < kFinSpec; ++u) {
+    const int sg = wave + kFinWaves * (u >> spr_lg), sl = u & ((1 << spr_lg) - 1);
+    cu[u] = 0;
+    pr[u] = make_uint2(0u, 0u);
+    if (sg < wpr) {  // the same for the whole wave
+      const size_t rb = select_region(o.n_blk, wpr, sg);
+      const int capc = static_cast<int>(select_region(o.n_blk, wpr, sg + 1) - rb);
+      cu[u] = o.emit_cnt[row * o.n_blk + sg];
+      pr[u] = em[rb + min(sl * kWave + lane, capc - 1)];
+    }
   }
   const int b = static_cast<int>(row / n_q);
   const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
@@ -538,12 +545,13 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   const int cap = cand_lds ? kFinCand : N_cap;
   // above b* -> sel, in b* -> candidates; one LDS atomic per kind and wave per
   // kFinSpec * 64 pairs
-  auto classify = [&](const uint2* p, int n_valid) {
+  // (slot u of a lane holds a pair when lane < lim[u])
+  auto classify = [&](const uint2* p, const int* lim) {
     uint64_t ms[kFinSpec], mc[kFinSpec];
     int ns = 0, nc = 0;
 #pragma unroll
     for (int u = 0; u < kFinSpec; ++u) {
-      const bool valid = lane + u * kWave < n_valid;
+      const bool valid = lane < lim[u];
       const int bin = static_cast<int>(score_bin(p[u].x));
       ms[u] = __ballot(valid && bin > bstar);
       mc[u] = __ballot(valid && bin == bstar);
@@ -580,19 +588,39 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     }
   };
   constexpr int kChunk = kFinSpec * kWave;
-  for (int sg = wave; sg < n_part; sg += kFinWaves) {  // the same for the whole wave
-    size_t rb = rb0;
-    int cnt = cnt0;
-    if (sg != wave) {
-      rb = select_region(o.n_blk, wpr, sg);
-      cnt = o.emit_cnt[row * o.n_blk + sg];
-    }
-    for (int c0 = 0; c0 < cnt; c0 += kChunk) {
-      if (sg != wave || c0 > 0) {
+  int lim[kFinSpec];
 #pragma unroll
-        for (int u = 0; u < kFinSpec; ++u) pr[u] = em[rb + min(c0 + lane + u * kWave, cnt - 1)];
+  for (int u = 0; u < kFinSpec; ++u) {
+    const int sg = wave + kFinWaves * (u >> spr_lg), sl = u & ((1 << spr_lg) - 1);
+    lim[u] = sg < n_part ? cu[u] - sl * kWave : 0;
+  }
+  classify(pr, lim);
+  // pairs of those regions past the slots they were given, then the regions
+  // past the first 8 of the wave (the same for the whole wave)
+  for (int j = 0; j < rpw; ++j) {
+    const int sg = wave + kFinWaves * j;
+    if (sg >= n_part) break;
+    const int cnt = o.emit_cnt[row * o.n_blk + sg];
+    const size_t rb = select_region(o.n_blk, wpr, sg);
+    for (int c0 = kWave << spr_lg; c0 < cnt; c0 += kChunk) {
+#pragma unroll
+      for (int u = 0; u < kFinSpec; ++u) {
+        pr[u] = em[rb + min(c0 + u * kWave + lane, cnt - 1)];
+        lim[u] = cnt - c0 - u * kWave;
       }
-      classify(pr, cnt - c0);
+      classify(pr, lim);
+    }
+  }
+  for (int sg = wave + kFinWaves * rpw; sg < n_part; sg += kFinWaves) {
+    const int cnt = o.emit_cnt[row * o.n_blk + sg];
+    const size_t rb = select_region(o.n_blk, wpr, sg);
+    for (int c0 = 0; c0 < cnt; c0 += kChunk) {
+#pragma unroll
+      for (int u = 0; u < kFinSpec; ++u) {
+        pr[u] = em[rb + min(c0 + u * kWave + lane, cnt - 1)];
+        lim[u] = cnt - c0 - u * kWave;
+      }
+      classify(pr, lim);
     }
   }
   __syncthreads();

@@ -535,6 +535,17 @@ def test_csa_decode_reduced(ctx):
     _decode_parity(cfg, d, range(cfg.B))
 
 
+def test_csa_decode_rows_longer_than_one_bitmap_pass():
+    """One sequence of about 2.1M tokens: more than 2^19 visible entries, so the
+    selection writes its ascending output in two bitmap passes, and the row's
+    256 indexer workgroups give each finish wave 16 regions to read."""
+    cfg = CSA_DECODE_1M.with_(B=1, ctx=(1 << 21) + (1 << 15))
+    say(f"CSA decode B=1 ctx={cfg.ctx}")
+    d = gen.decode_inputs(cfg)
+    assert d["n_cap"] > (1 << 19)
+    _decode_parity(cfg, d, range(cfg.B))
+
+
 @pytest.mark.parametrize("kind", ["csa", "hca", "hybrid_csa"])
 def test_decode_rope(kind):
     """Decode steps with partial RoPE: the ring row and a completed entry turned
