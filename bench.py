@@ -16,12 +16,13 @@ chunk (8192 tokens on a 131072 prefix); the default line is the 1M CSA decode.
 Prints ONE JSON line.  The timed loop calls lca_decode_step.  For a CSA layer
 the library launches the indexer (the dominant kernel) with two HIP events
 (lca_decode_io.stage_events[1], [2]) as its dispatch's own start and end
-stamps, on every timed step, which gives that kernel's duration for the
+stamps, on every 4th timed step, which gives that kernel's duration for the
 roofline.  The events are created with hipEventDisableSystemFence: a default
 event writes back and invalidates the caches when it is recorded, which cost
-11 us of GPU time per step around the stamped dispatch.  For HCA alone the
-dominant kernel is the attention: every 4th step records two events around its
-stage (the other steps record none).
+11 us of GPU time per stamped step; without the fence the stamps still leave
+about 4 us idle around the dispatch, so the other steps carry none.  For HCA
+alone the dominant kernel is the attention: every 4th step records two events
+around its stage.
 The per-stage breakdown ("stages_us") comes from an untimed diagnostic loop
 that sets all five events (the recorded ones include that cost).
 """
@@ -202,12 +203,12 @@ def run_decode(args, workload):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # Timed region: the indexer's events are its dispatch stamps (every step);
-    # the HCA attention stage is bracketed by recorded events on every 4th step.
+    # Timed region: on every 4th step, the indexer's dispatch stamps (CSA) or two
+    # events around the attention stage (HCA alone).
     csa_layers = [i for i, L in enumerate(layers) if L.mode == "csa"]
     dom_layers = csa_layers if csa_layers else [0]
     dom = (1, 2) if csa_layers else (3, 4)          # indexer or attention stage
-    SAMPLE = 1 if csa_layers else 4
+    SAMPLE = 4  # stamped steps: the event packets themselves cost GPU time
     sampled = {}
     for i in range(0, args.steps, SAMPLE):
         sampled[i] = {li: (hip.create(), hip.create()) for li in dom_layers}

@@ -405,6 +405,14 @@ long long select_zero_words(long long rows);
 SelectWs select_ws_in(void* ws, long long rows, int N_cap);
 // whether the fused path takes rows of N_cap entries and this k
 bool select_supported(int N_cap, int k);
+// workgroups per row (wpr) the finish pass takes
+constexpr int kSelMaxWpr = 256;
+// The finish pass after the fused indexer: one workgroup per row selects the
+// row's top k from the emitted pairs into idx ([rows, k], ascending, -1 after
+// min(k, vis)); rows with vis <= k were written by the indexer.
+hipError_t launch_select_finish(long long rows, int n_q, int N_cap, int wpr, const int32_t* q_pos, int m,
+                                const int32_t* n_entries, int k, const SelectWs& w, int32_t* idx,
+                                hipStream_t s);
 
 // hist (optional, [B*n_q, 4096], zeroed by the caller): the MFMA path adds the
 // score_bin histogram of every row's visible scores into it.  sel (optional,

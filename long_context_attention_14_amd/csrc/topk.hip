@@ -558,6 +558,349 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
 // runs inside the indexer).
 constexpr int kMaxBlk = 8192;  // blocks per row (N_cap <= 1 Mi entries)
 
+// ---------------------------------------------------------------------------
+// Finish of the fused selection: one workgroup per row selects the row's top k
+// from the pairs the row's workgroups emitted (every entry of the final top k
+// is among them).  The row's final histogram gives the bin b* of the k-th
+// largest key and the count of keys above it; every emitted entry above b* is
+// selected, and the rest come from the entries in b* (the candidates; their
+// number is the bin's count): a radix select on the low 20 key bits finds the
+// key T of the last one taken, and when more candidates than needed carry T, a
+// second radix select on the entry index takes the lowest ones.  The selected
+// indices, in no order so far, are written out in ascending order through a
+// bitmap over the row's visible entries (2^19 entries per pass).  Wave w reads
+// the pairs of regions w, w + 16, ...; the histogram, the counts and the first
+// 512 pairs of the wave's regions (up to 8 regions) do not depend on the row's
+// length, so they are loaded at once with it: the common case takes one memory
+// round trip before the selection.
+constexpr int kFinWaves = 16;
+constexpr int kFinThreads = kFinWaves * kWave;
+constexpr int kFinSpec = 8;             // pairs per lane loaded with the counts
+constexpr int kFinCand = 8192;          // candidates held in LDS (else in global memory)
+constexpr int kFinBitmapWords = 16384;  // one output pass: 2^19 entries
+constexpr uint32_t kSkipKey = 0x80000000u;
+static_assert(kFinBitmapWords <= 2 * kFinCand, "the bitmap fits in the candidates' space");
+
+// exclusive block-wide prefix of one int per thread (NW full waves); *total is
+// the sum over the block.  Ends with a barrier, so scan_sh can be reused.
+template <int NW>
+__device__ __forceinline__ int block_excl_scan(int v, int* total, int* scan_sh) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += t;
+  }
+  if (lane == kWave - 1) scan_sh[wave] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int x = 0; x < NW; ++x) {
+    const int t = scan_sh[x];
+    before += x < wave ? t : 0;
+    tot += t;
+  }
+  *total = tot;
+  __syncthreads();
+  return before + incl - v;
+}
+
+// Among the n elements whose key(e) lacks kSkipKey (keys of 20 bits), the
+// want-th largest (1 <= want <= their number), by passes over bits 19..12,
+// 11..4 and 3..0.  Returns the key prefix found and sets *mask to the bits it
+// fixes: elements with (key & mask) > prefix are all taken, *gt of them, and
+// *eq elements have (key & mask) == prefix, of which want - *gt are taken.
+// The passes stop early once every element of the chosen digit is taken
+// (*eq == want - *gt).
+template <int NW, class KeyF>
+__device__ uint32_t radix_select20(int n, int want, KeyF key, uint32_t* rh, int* sh_rb, int* sh_ra,
+                                   uint32_t* mask_out, int* gt, int* eq) {
+  constexpr int NT = NW * kWave;
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, mask = 0;
+  int remaining = want, in_bin = 0;
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int sh = pass == 0 ? 12 : (pass == 1 ? 4 : 0);
+    const uint32_t dm = pass == 2 ? 0xfu : 0xffu;
+    for (int i = tid; i < 256; i += NT) rh[i] = 0;
+    if (tid == 0) {  // (set by the bin search; defined even if it found none)
+      *sh_rb = 0;
+      *sh_ra = 0;
+    }
+    __syncthreads();
+    for (int e = tid; e < n; e += NT) {
+      const uint32_t kk = key(e);
+      if (!(kk & kSkipKey) && (kk & mask) == prefix) atomicAdd(&rh[(kk >> sh) & dm], 1u);
+    }
+    __syncthreads();
+    if (tid < kWave) find_bin_wave(rh, 256, remaining, sh_rb, sh_ra);
+    __syncthreads();
+    const int bsel = *sh_rb;
+    prefix |= static_cast<uint32_t>(bsel) << sh;
+    mask |= dm << sh;
+    remaining -= *sh_ra;
+    in_bin = static_cast<int>(rh[bsel]);
+    __syncthreads();
+    if (in_bin == remaining) break;  // the same for every thread
+  }
+  *mask_out = mask;
+  *gt = want - remaining;
+  *eq = in_bin;
+  return prefix;
+}
+
+__global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
+    int n_q, int N_cap, int wpr, const int32_t* __restrict__ q_pos, int m,
+    const int32_t* __restrict__ n_entries, int k, SelectWs o, int32_t* __restrict__ sel_idx) {
+  constexpr int NT = kFinThreads;
+  __shared__ uint32_t lh[kScoreHistBins];
+  __shared__ int32_t sel[kMaxK];
+  __shared__ __attribute__((aligned(16))) uint32_t cand[2 * kFinCand];  // keys, indices; then the output bitmap
+  __shared__ int sh_bin, sh_above, sh_nsel, sh_ncand, sh_rb, sh_ra;
+  __shared__ int scan_sh[kFinWaves];
+  __shared__ uint32_t rh[256];
+  uint32_t* ck = cand;
+  int32_t* ci = reinterpret_cast<int32_t*>(cand + kFinCand);
+  uint32_t* bm = cand;
+  const long long row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint2* em = o.emit + static_cast<size_t>(row) * o.n_blk * kSelBlock;
+  // the histogram words, and the counts and first pairs of the wave's regions
+  // w, w + 16, ... (up to 8 of them; the 8 pair slots of a lane are shared
+  // out, 64 pairs each, slots clamped to the region; every one of the wpr
+  // regions exists, the row's length decides below which are used)
+  const uint32_t* gh = o.hist + row * kScoreHistBins;
+  constexpr int kHv = kScoreHistBins / NT;
+  uint32_t hv[kHv];
+#pragma unroll
+  for (int u = 0; u < kHv; ++u) hv[u] = gh[tid + u * NT];
+  const int spr_lg = wpr > 4 * kFinWaves ? 0 : (wpr > 2 * kFinWaves ? 1 : (wpr > kFinWaves ? 2 : 3));
+  const int rpw = kFinSpec >> spr_lg;  // regions per wave read speculatively
+  int cu[kFinSpec];
+  uint2 pr[kFinSpec];
+#pragma unroll
+  for (int u = 0; u < kFinSpec; ++u) {
+    const int sg = wave + kFinWaves * (u >> spr_lg), sl = u & ((1 << spr_lg) - 1);
+    cu[u] = 0;
+    pr[u] = make_uint2(0u, 0u);
+    if (sg < wpr) {  // the same for the whole wave
+      const size_t rb = select_region(o.n_blk, wpr, sg);
+      const int capc = static_cast<int>(select_region(o.n_blk, wpr, sg + 1) - rb);
+      cu[u] = o.emit_cnt[row * o.n_blk + sg];
+      pr[u] = em[rb + min(sl * kWave + lane, capc - 1)];
+    }
+  }
+  const int b = static_cast<int>(row / n_q);
+  const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
+  if (vis <= k) return;  // written by the indexer
+  int32_t* out = sel_idx + row * k;
+  const int n_part = min(wpr, (vis + kSelBlock - 1) / kSelBlock);
+#pragma unroll
+  for (int u = 0; u < kHv; ++u) lh[hist_bin_of_slot(tid + u * NT)] = hv[u];
+  if (tid == 0) {
+    sh_nsel = 0;
+    sh_ncand = 0;
+    sh_bin = 0;  // (set below; defined even if the histogram were short of k)
+    sh_above = 0;
+  }
+  __syncthreads();
+  // threshold bin b*: thread t sums bins [4095 - 4t - 3, 4095 - 4t]
+  constexpr int per = kScoreHistBins / NT;
+  const int topb = kScoreHistBins - 1 - per * tid;
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < per; ++i) local += static_cast<int>(lh[topb - i]);
+  int total;
+  int run = block_excl_scan<kFinWaves>(local, &total, scan_sh);
+  if (run < k && run + local >= k) {
+    for (int i = 0; i < per; ++i) {
+      const int h = static_cast<int>(lh[topb - i]);
+      if (run + h >= k) {
+        sh_bin = topb - i;
+        sh_above = run;
+        break;
+      }
+      run += h;
+    }
+  }
+  __syncthreads();
+  const int bstar = sh_bin, above = sh_above;
+  const int C = static_cast<int>(lh[bstar]);
+  const int need = k - above;  // 1 <= need <= C
+  const bool cand_lds = C <= kFinCand;
+  uint32_t* gck = o.cand_key + row * N_cap;
+  int32_t* gci = o.cand_idx + row * N_cap;
+  const int cap = cand_lds ? kFinCand : N_cap;
+  // above b* -> sel, in b* -> candidates; one LDS atomic per kind and wave per
+  // kFinSpec * 64 pairs
+  // (slot u of a lane holds a pair when lane < lim[u])
+  auto classify = [&](const uint2* p, const int* lim) {
+    uint64_t ms[kFinSpec], mc[kFinSpec];
+    int ns = 0, nc = 0;
+#pragma unroll
+    for (int u = 0; u < kFinSpec; ++u) {
+      const bool valid = lane < lim[u];
+      const int bin = static_cast<int>(score_bin(p[u].x));
+      ms[u] = __ballot(valid && bin > bstar);
+      mc[u] = __ballot(valid && bin == bstar);
+      ns += __popcll(ms[u]);
+      nc += __popcll(mc[u]);
+    }
+    int bs = 0, bc = 0;
+    if (lane == 0) {
+      if (ns) bs = atomicAdd(&sh_nsel, ns);
+      if (nc) bc = atomicAdd(&sh_ncand, nc);
+    }
+    bs = __shfl(bs, 0, kWave);
+    bc = __shfl(bc, 0, kWave);
+#pragma unroll
+    for (int u = 0; u < kFinSpec; ++u) {
+      if ((ms[u] >> lane) & 1) {
+        const int q = bs + lanes_below(ms[u]);
+        if (q < k) sel[q] = static_cast<int32_t>(p[u].y);
+      }
+      bs += __popcll(ms[u]);
+      if ((mc[u] >> lane) & 1) {
+        const int q = bc + lanes_below(mc[u]);
+        if (q < cap) {
+          if (cand_lds) {
+            ck[q] = p[u].x;
+            ci[q] = static_cast<int32_t>(p[u].y);
+          } else {
+            gck[q] = p[u].x;
+            gci[q] = static_cast<int32_t>(p[u].y);
+          }
+        }
+      }
+      bc += __popcll(mc[u]);
+    }
+  };
+  constexpr int kChunk = kFinSpec * kWave;
+  int lim[kFinSpec];
+#pragma unroll
+  for (int u = 0; u < kFinSpec; ++u) {
+    const int sg = wave + kFinWaves * (u >> spr_lg), sl = u & ((1 << spr_lg) - 1);
+    lim[u] = sg < n_part ? cu[u] - sl * kWave : 0;
+  }
+  classify(pr, lim);
+  // pairs of those regions past the slots they were given, then the regions
+  // past the first 8 of the wave (the same for the whole wave)
+  for (int j = 0; j < rpw; ++j) {
+    const int sg = wave + kFinWaves * j;
+    if (sg >= n_part) break;
+    const int cnt = o.emit_cnt[row * o.n_blk + sg];
+    const size_t rb = select_region(o.n_blk, wpr, sg);
+    for (int c0 = kWave << spr_lg; c0 < cnt; c0 += kChunk) {
+#pragma unroll
+      for (int u = 0; u < kFinSpec; ++u) {
+        pr[u] = em[rb + min(c0 + u * kWave + lane, cnt - 1)];
+        lim[u] = cnt - c0 - u * kWave;
+      }
+      classify(pr, lim);
+    }
+  }
+  for (int sg = wave + kFinWaves * rpw; sg < n_part; sg += kFinWaves) {
+    const int cnt = o.emit_cnt[row * o.n_blk + sg];
+    const size_t rb = select_region(o.n_blk, wpr, sg);
+    for (int c0 = 0; c0 < cnt; c0 += kChunk) {
+#pragma unroll
+      for (int u = 0; u < kFinSpec; ++u) {
+        pr[u] = em[rb + min(c0 + u * kWave + lane, cnt - 1)];
+        lim[u] = cnt - c0 - u * kWave;
+      }
+      classify(pr, lim);
+    }
+  }
+  __syncthreads();
+  const int nC = min(sh_ncand, cap);
+  auto ckey = [&](int e) -> uint32_t { return (cand_lds ? ck[e] : gck[e]) & 0xfffffu; };
+  auto cidx = [&](int e) -> int32_t { return cand_lds ? ci[e] : gci[e]; };
+  // the need largest candidates (low 20 key bits; ties to the lower index)
+  uint32_t T = 0, tmask = 0;
+  // candidates with (key & tmask) == T are taken when ((0xfffff - index) & xmask) >= X
+  uint32_t X = 0, xmask = 0;
+  if (need < nC) {
+    int gt, eq;
+    T = radix_select20<kFinWaves>(nC, need, ckey, rh, &sh_rb, &sh_ra, &tmask, &gt, &eq);
+    const int need_eq = need - gt;
+    if (eq > need_eq) {  // T is a whole key here: more candidates carry it than are taken
+      auto inv_idx = [&](int e) -> uint32_t {
+        return ckey(e) == T ? 0xfffffu - static_cast<uint32_t>(cidx(e)) : kSkipKey;
+      };
+      int gt2, eq2;
+      X = radix_select20<kFinWaves>(nC, need_eq, inv_idx, rh, &sh_rb, &sh_ra, &xmask, &gt2, &eq2);
+    }
+  }
+  for (int e0 = 0; e0 < nC; e0 += NT) {
+    const int e = e0 + tid;
+    bool take = false;
+    int32_t id = 0;
+    if (e < nC) {
+      const uint32_t kk = ckey(e) & tmask;
+      id = cidx(e);
+      take = need >= nC || kk > T ||
+             (kk == T && ((0xfffffu - static_cast<uint32_t>(id)) & xmask) >= X);
+    }
+    const uint64_t mt = __ballot(take);
+    int bs = 0;
+    if (lane == 0 && mt) bs = atomicAdd(&sh_nsel, __popcll(mt));
+    bs = __shfl(bs, 0, kWave);
+    if (take) {
+      const int q = bs + lanes_below(mt);
+      if (q < k) sel[q] = id;
+    }
+  }
+  __syncthreads();
+  const int n_sel = min(sh_nsel, k);
+  // ascending output through a bitmap over the visible entries
+  int done = 0;
+  for (int base = 0; base < vis; base += 32 * kFinBitmapWords) {
+    const int nbits = min(32 * kFinBitmapWords, vis - base);
+    const int nw = (nbits + 31) >> 5;
+    const int nw4 = (nw + 3) & ~3;  // (<= kFinBitmapWords, a multiple of 4)
+    for (int w = 4 * tid; w < nw4; w += 4 * NT) *reinterpret_cast<uint4*>(bm + w) = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    for (int i = tid; i < n_sel; i += NT) {
+      const int x = sel[i] - base;
+      if (x >= 0 && x < nbits) atomicOr(&bm[x >> 5], 1u << (x & 31));
+    }
+    __syncthreads();
+    // thread t: words [8t, 8t + 8) (two 16-byte LDS reads), more per thread
+    // beyond 8192 words
+    const int wpt = ((nw + NT - 1) / NT + 3) & ~3, w0 = tid * wpt;
+    int c = 0;
+    for (int j = 0; j < wpt; j += 4) {
+      if (w0 + j < nw) {  // (the words up to nw4 are cleared)
+        const uint4 v = *reinterpret_cast<const uint4*>(bm + w0 + j);
+        c += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
+      }
+    }
+    int tot;
+    int at = done + block_excl_scan<kFinWaves>(c, &tot, scan_sh);
+    for (int j = 0; j < wpt; j += 4) {
+      if (w0 + j >= nw) break;
+      const uint4 v = *reinterpret_cast<const uint4*>(bm + w0 + j);
+      const uint32_t words[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t bits = words[q];
+        while (bits) {
+          const int bit = __ffs(bits) - 1;
+          if (at < k) out[at] = base + (w0 + j + q) * 32 + bit;
+          ++at;
+          bits &= bits - 1u;
+        }
+      }
+    }
+    done += tot;
+    if (base + 32 * kFinBitmapWords < vis) __syncthreads();  // the next pass clears the bitmap
+  }
+  for (int i = done + tid; i < k; i += NT) out[i] = -1;  // (none when the data is consistent)
+}
+
 struct SelectLayout {
   size_t hist, emit_cnt, emit, cand_key, cand_idx, total;
 };
@@ -669,6 +1012,16 @@ SelectWs select_ws_in(void* ws, long long rows, int N_cap) {
   w.cand_idx = reinterpret_cast<int32_t*>(p + L.cand_idx);
   w.n_blk = (N_cap + kSelBlock - 1) / kSelBlock;
   return w;
+}
+
+hipError_t launch_select_finish(long long rows, int n_q, int N_cap, int wpr, const int32_t* q_pos, int m,
+                                const int32_t* n_entries, int k, const SelectWs& w, int32_t* idx,
+                                hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (wpr < 1 || wpr > kSelMaxWpr || !select_supported(N_cap, k)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(select_finish_kernel, dim3(static_cast<unsigned>(rows)), dim3(kFinThreads), 0, s,
+                     n_q, N_cap, wpr, q_pos, m, n_entries, k, w, idx);
+  return hipGetLastError();
 }
 
 }  // namespace lca
