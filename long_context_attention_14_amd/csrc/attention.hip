@@ -1009,12 +1009,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 constexpr int kMaxMergeSplits = 256;
 
 // Split merge with one thread per 4 consecutive dims of a (query row, head).
-// The lse values and partial rows of up to kMergeChunk splits are loaded
-// together, so a merge of that many splits takes one memory round trip; more
-// splits go kMergeChunk at a time with a running maximum.  Splits are combined
-// in split order (deterministic).
-constexpr int kMergeChunk = 16;
-
+// The lse values and partial rows of up to CH splits are loaded together, so a
+// merge of that many splits takes one memory round trip; more splits go CH at a
+// time with a running maximum.  Splits are combined in split order
+// (deterministic).  CH (4, 8, 12 or 16) is the split count rounded up to a
+// multiple of 4, so few loads are clamped repeats of the last split.
+template <int CH>
 __global__ __launch_bounds__(256) void attn_merge4_kernel(
     long long rows, int H, int c, int n_splits, const float* __restrict__ part_o,
     const float* __restrict__ part_lse, const float* __restrict__ sink, uint8_t* __restrict__ out,
@@ -1039,11 +1039,11 @@ __global__ __launch_bounds__(256) void attn_merge4_kernel(
   float m = sink ? sink[h] : -INFINITY;
   float den = sink ? 1.f : 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < n_splits; s0 += kMergeChunk) {
-    float l[kMergeChunk];
-    float4 v[kMergeChunk];
+  for (int s0 = 0; s0 < n_splits; s0 += CH) {
+    float l[CH];
+    float4 v[CH];
 #pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u) {
+    for (int u = 0; u < CH; ++u) {
       const int sp = min(s0 + u, n_splits - 1);
       const size_t base = (static_cast<size_t>(row) * n_splits + sp) * H + h;
       l[u] = part_lse[base];
@@ -1051,7 +1051,7 @@ __global__ __launch_bounds__(256) void attn_merge4_kernel(
     }
     float mc = m;
 #pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u) {
+    for (int u = 0; u < CH; ++u) {
       if (s0 + u >= n_splits) l[u] = -INFINITY;
       mc = fmaxf(mc, l[u]);
     }
@@ -1063,7 +1063,7 @@ __global__ __launch_bounds__(256) void attn_merge4_kernel(
     acc.z *= sc;
     acc.w *= sc;
 #pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u) {
+    for (int u = 0; u < CH; ++u) {
       const float wgt = l[u] == -INFINITY ? 0.f : __expf(l[u] - mc);
       den += wgt;
       acc.x = fmaf(wgt, v[u].x, acc.x);
@@ -1209,8 +1209,14 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
   if (e != hipSuccess || p.n_splits == 1) return e;
   if (rope_step != 0.0 && (static_cast<long long>(H) * (c / 4)) % 256 != 0) return hipErrorInvalidValue;
   const dim3 g2(static_cast<unsigned>((rows * H * (c / 4) + 255) / 256));
-  hipLaunchKernelGGL(attn_merge4_kernel, g2, dim3(256), 0, s, rows, H, c, p.n_splits, part_o,
-                     part_lse, sink, static_cast<uint8_t*>(out), out_fmt, lse, q_pos, rope_step);
+  auto merge = [&](auto kern) {
+    hipLaunchKernelGGL(kern, g2, dim3(256), 0, s, rows, H, c, p.n_splits, part_o, part_lse, sink,
+                       static_cast<uint8_t*>(out), out_fmt, lse, q_pos, rope_step);
+  };
+  if (p.n_splits <= 4) merge(attn_merge4_kernel<4>);
+  else if (p.n_splits <= 8) merge(attn_merge4_kernel<8>);
+  else if (p.n_splits <= 12) merge(attn_merge4_kernel<12>);
+  else merge(attn_merge4_kernel<16>);
   return hipGetLastError();
 }
 

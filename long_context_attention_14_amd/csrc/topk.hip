@@ -679,19 +679,19 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   for (int u = 0; u < kHv; ++u) hv[u] = gh[tid + u * NT];
   const int spr_lg = wpr > 4 * kFinWaves ? 0 : (wpr > 2 * kFinWaves ? 1 : (wpr > kFinWaves ? 2 : 3));
   const int rpw = kFinSpec >> spr_lg;  // regions per wave read speculatively
-  int cu[kFinSpec];
+  // region wi: blocks [wi a + min(wi, r), +a + (wi < r)) of the row (see select_region)
+  const int ra = o.n_blk / wpr, rr = o.n_blk % wpr;
+  auto region_first = [&](int wi) -> int { return (wi * ra + min(wi, rr)) * kSelBlock; };
+  // lane l < 8 loads the count of the wave's region l (clamped to an existing
+  // region; which regions are used is decided below)
+  const int cnt_l = o.emit_cnt[row * o.n_blk + min(wave + kFinWaves * min(lane, kFinSpec - 1), wpr - 1)];
   uint2 pr[kFinSpec];
 #pragma unroll
   for (int u = 0; u < kFinSpec; ++u) {
-    const int sg = wave + kFinWaves * (u >> spr_lg), sl = u & ((1 << spr_lg) - 1);
-    cu[u] = 0;
-    pr[u] = make_uint2(0u, 0u);
-    if (sg < wpr) {  // the same for the whole wave
-      const size_t rb = select_region(o.n_blk, wpr, sg);
-      const int capc = static_cast<int>(select_region(o.n_blk, wpr, sg + 1) - rb);
-      cu[u] = o.emit_cnt[row * o.n_blk + sg];
-      pr[u] = em[rb + min(sl * kWave + lane, capc - 1)];
-    }
+    const int sgc = min(wave + kFinWaves * (u >> spr_lg), wpr - 1), sl = u & ((1 << spr_lg) - 1);
+    const int rb = region_first(sgc);
+    const int capc = (ra + (sgc < rr ? 1 : 0)) * kSelBlock;
+    pr[u] = em[rb + min(sl * kWave + lane, capc - 1)];
   }
   const int b = static_cast<int>(row / n_q);
   const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
@@ -783,7 +783,8 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
 #pragma unroll
   for (int u = 0; u < kFinSpec; ++u) {
     const int sg = wave + kFinWaves * (u >> spr_lg), sl = u & ((1 << spr_lg) - 1);
-    lim[u] = sg < n_part ? cu[u] - sl * kWave : 0;
+    const int cnt = __shfl(cnt_l, u >> spr_lg, kWave);
+    lim[u] = sg < n_part ? cnt - sl * kWave : 0;
   }
   classify(pr, lim);
   // pairs of those regions past the slots they were given, then the regions
