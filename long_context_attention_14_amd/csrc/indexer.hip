@@ -152,6 +152,23 @@ __device__ __forceinline__ GroupAcc group_mma(const v8i (&A)[2][2], const int (&
 // Score of key column j (valid in every lane; lanes j and j+32 agree): the 64
 // heads' ReLU'd dot products weighted by w_s and summed, in four independent
 // partial sums; four consecutive registers read one float4 of the weights.
+// group_reduce_reg: the same with the lane's 32 weights in registers
+// (wr[4 ht + a] = w_s[32 ht + 8 a + 4 g .. + 4]).
+__device__ __forceinline__ float group_reduce_reg(const GroupAcc& acc, const float4 (&wr)[8]) {
+  float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const float4 w4 = wr[4 * ht + a];
+      p[0] = fmaf(w4.x, fmaxf(acc.a[ht][4 * a], 0.f), p[0]);
+      p[1] = fmaf(w4.y, fmaxf(acc.a[ht][4 * a + 1], 0.f), p[1]);
+      p[2] = fmaf(w4.z, fmaxf(acc.a[ht][4 * a + 2], 0.f), p[2]);
+      p[3] = fmaf(w4.w, fmaxf(acc.a[ht][4 * a + 3], 0.f), p[3]);
+    }
+  }
+  return lane_pair_sum((p[0] + p[1]) + (p[2] + p[3]));
+}
 __device__ __forceinline__ float group_reduce(const GroupAcc& acc, const float* w_s, int g) {
   float p[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -500,7 +517,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void indexer_select_kernel(
 // reads of 8 consecutive keys hit distinct banks.
 constexpr int kRowsPerWG = 8;
 constexpr int kRowsThreads = kWave * kRowsPerWG;
-constexpr int kTileKeys = 128;
+constexpr int kTileKeys = 64;
 
 template <bool MX, typename ST>
 __global__ __launch_bounds__(kRowsThreads, 2) void indexer_rows_kernel(
@@ -538,6 +555,12 @@ __global__ __launch_bounds__(kRowsThreads, 2) void indexer_rows_kernel(
   int vis_max = 0;
 #pragma unroll
   for (int u = 0; u < kRowsPerWG; ++u) vis_max = max(vis_max, vis_s[u]);
+  // the 32 head weights this lane applies, kept in registers for every key group
+  float4 wr[8];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) wr[4 * ht + a] = *reinterpret_cast<const float4*>(&w_s[wave][32 * ht + 8 * a + 4 * g]);
   const int vis = vis_s[wave];
   const int n_tiles = (vis_max + kTileKeys - 1) / kTileKeys;
   if (n_tiles == 0) return;
@@ -607,7 +630,7 @@ __global__ __launch_bounds__(kRowsThreads, 2) void indexer_rows_kernel(
 #pragma unroll
     for (int grp = 0; grp < kGroups; ++grp) {
       if (grp + 1 < kGroups) acc[grp + 1] = group_mma<MX>(A, sA, lds_group(grp + 1));
-      const float sv = group_reduce(acc[grp], w_s[wave], g);
+      const float sv = group_reduce_reg(acc[grp], wr);
       const int key = t * kTileKeys + kKeysPerGroup * grp + j;
       if (g == 0 && key < vis) store_score(&out[key], sv);
     }
