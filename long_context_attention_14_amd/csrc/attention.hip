@@ -968,8 +968,21 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
       part_lse[(static_cast<size_t>(row) * n_splits + split) * kMH + head] = lse_v;
     }
   }
-  // O * f -> LDS as fp32 [64 heads][512] (over both KV buffers, once every wave
-  // is done with them), then contiguous 16-byte stores
+  if (n_splits > 1) {
+    // fp32 partial rows straight from the accumulators (a lane's 32 columns of
+    // a head are 128 contiguous bytes; the merge turns the output back)
+    float* pb = part_o + (static_cast<size_t>(row) * n_splits + split) * kMH * kMC + 256 * kh + j32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int h = 32 * hg + 8 * (r >> 2) + 4 * g + (r & 3);
+      const float fr = __shfl(f, 8 * (r >> 2) + 4 * g + (r & 3), 64);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) pb[h * kMC + 32 * db] = o[db][r] * fr;
+    }
+    return;
+  }
+  // one split: O * f -> LDS as fp32 [64 heads][512] (over both KV buffers, once
+  // every wave is done with them), then contiguous 16-byte stores
   float* ost = reinterpret_cast<float*>(&kv_s[0][0]);
   __syncthreads();
 #pragma unroll
