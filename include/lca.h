@@ -369,9 +369,11 @@ typedef struct lca_decode_io {
   int32_t* idx_out;     /* CSA: [B, k] selected entries, or NULL (kept in workspace) */
   /* Optional hipEvent_t handles (NULL = skip) on `stream`: [0] is recorded before
    * the state append; in a CSA layer [1] and [2] are the start and end stamps of
-   * the indexer's own dispatch (no separate event packet, so [2] - [1] is the
-   * indexer kernel's duration); [3] is recorded after the top-k and [4] after the
-   * attention.  An HCA layer records [1], [2] and [3] right after the append. */
+   * the indexer's own dispatch (given to its launch, so [2] - [1] is the indexer
+   * kernel's duration; stamped dispatches still leave a few microseconds idle on
+   * either side, so a timing caller stamps a sample of its steps); [3] is
+   * recorded after the top-k and [4] after the attention.  An HCA layer records
+   * [1], [2] and [3] right after the append. */
   void* stage_events[5];
 } lca_decode_io;
 
