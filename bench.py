@@ -285,7 +285,8 @@ def run_decode(args, workload):
         att_bytes = (vis_mean(d0) + B * c0.n_win) * rb + 2 * B * c0.H * c0.c * 2
         achieved = att_bytes / dom_time / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "attn_mfma_kernel"}
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "kernel": "attention stage: attn_decode_kernel + attn_merge4_kernel"}
     desc = {
         "csa_decode_1m": "csa_decode_b16_1m: batch 16, context 2^20 + U{0..3}, m=4 (262144 entries), "
                          "fp8 indexer 64x128, top-1024, MQA 64x512 bf16, window 128",

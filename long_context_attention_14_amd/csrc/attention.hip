@@ -618,27 +618,30 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
 
 // ---------------------------------------------------------------------------
 // Decode kernel (few query rows, bf16 queries, 64 heads x 512): one workgroup
-// per (query row, split) with all 64 heads; wave w covers heads 32 hg .. +32
-// (hg = w & 1) and dims 256 kh .. +256 (kh = w >> 1).
+// of eight waves (two per SIMD) per (query row, split) with all 64 heads; wave
+// w covers heads 32 hg .. +32 (hg = w & 1) and dims 128 kq .. +128 (kq = w >> 1).
 //
 //  * The normalised query (the wave's heads and dims) stays in registers as the
 //    B operand of S^T = K Q^T (32x32x16 bf16 MFMA; lane: head 32 hg + l%32,
-//    dims 256 kh + 16 ks + 8 (l/32) .. +8 of k-step ks), so the scores read only
-//    K from LDS.  The two waves of a head half add their partial S^T (over the
-//    two dim halves) through LDS; each then holds all 64 rows of the tile, takes
-//    the maximum in registers, and writes P (bf16) of its own 32 rows to LDS.
-//  * PV: the wave accumulates O for its 32 heads and its 256 dims (V read
+//    dims 128 kq + 16 ks + 8 (l/32) .. +8 of k-step ks), so the scores read only
+//    K from LDS.  Each wave computes the partial S^T of all 64 tile rows over
+//    its 128 dims; the four waves of a head half add their partials (in quarter
+//    order) through LDS, each keeping the rows 16 kq .. +16, agree on every
+//    head's tile maximum through LDS, and write P (bf16) of their rows to LDS.
+//  * PV: the wave accumulates O for its 32 heads and its 128 dims (V read
 //    transposed from the row-major tile).
 //  * The running maximum is raised only when a tile's maximum exceeds it by
 //    more than kLazyMax (natural-log units), so P stays below e^kLazyMax and O
 //    is rescaled only on those tiles (the normalised result is the same).
-//  * KV tiles are double-buffered in LDS.  Wave w loads the tile rows w + 4 i,
-//    i < 16, through row pointers held by lanes 0..15; the next tile's rows are
-//    in flight in registers during a tile's compute, and the row indices of
-//    the tile after it are loaded one tile ahead.  Empty rows (outside the
-//    split, past the visible entries, before the window start) are loaded from
-//    a valid row, staged as zeros and masked to -inf in S.  The partial S^T of
-//    a tile goes through the other KV buffer, which is free at that point.
+//  * KV tiles are double-buffered in LDS.  Wave w loads the tile rows w + 8 i,
+//    i < 8, through row pointers held by lanes 0..7; the next tile's rows are in
+//    flight in registers during a tile's compute, and the row indices of the
+//    tile after it are loaded one tile ahead.  Empty rows (outside the split,
+//    past the visible entries, before the window start) are loaded from a valid
+//    row, staged as zeros and masked to -inf in S.  The partial S^T of a tile
+//    goes through the other KV buffer, which is free at that point.
+//  * With two waves per SIMD one wave's barrier and LDS waits overlap the other
+//    wave's MFMA and VALU work (four waves of twice the work each took 9% longer).
 constexpr float kLazyMax = 8.0f;
 
 // Row of slot i when its index entry e (and, paged, the page pid of e) has
@@ -663,26 +666,30 @@ __device__ __forceinline__ const uint8_t* slot_row_e(const SlotCtx& s, int i, in
   return s.win_b + static_cast<size_t>(slot) * s.kv_row;
 }
 
+constexpr int kD8Waves = 8;  // waves per decode workgroup
+
 template <int KVFMT, bool PAGED>
-__global__ __launch_bounds__(256) void attn_decode_kernel(
+__global__ __launch_bounds__(64 * kD8Waves) void attn_decode_kernel(
     int n_q, const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int N_cap,
     const int32_t* __restrict__ idx, int k, const int32_t* __restrict__ q_pos, int m,
     const int32_t* __restrict__ n_entries, const uint8_t* __restrict__ win, int W_cap,
     long long win_origin, int n_win, float tau, float eps, const float* __restrict__ sink,
     double rope_step, int n_splits, int split_rows, uint8_t* __restrict__ out, int out_fmt,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse, KvPages pg) {
+  constexpr int NW = kD8Waves;
   __shared__ __attribute__((aligned(16))) uint16_t kv_s[2][kMT * kQS];
   __shared__ float2 rope_s[kRopeDims / 2];  // (cos, sin) of the query position's angles
   __shared__ __attribute__((aligned(16))) uint16_t p_s[kMH * kPS];
-  __shared__ float ps_s[2][kMH];
-  __shared__ __attribute__((aligned(16))) uint32_t vm_s[2][4];
+  __shared__ float ps_s[4][kMH];  // per dim quarter: query sums of squares; then P row sums
+  __shared__ float mx_s[4][kMH];  // per row quarter: the tile maximum of each head
+  __shared__ __attribute__((aligned(16))) uint32_t vm_s[2][NW];
 
   const int split = blockIdx.x % n_splits;
   const long long row = blockIdx.x / n_splits;
   const int b = static_cast<int>(row / n_q);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hg = w & 1, kh = w >> 1;
+  const int hg = w & 1, kq = w >> 1;
   const int j32 = lane & 31, g = lane >> 5;
   const int head = 32 * hg + j32;  // the head of this lane's softmax state
 
@@ -703,66 +710,63 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   const int s_end = min(s_begin + split_rows, NT);
   const int n_tiles = (s_end - s_begin + kMT - 1) / kMT;
 
-  // lanes 0..15 (and their copies in the other lanes) hold tile row w + 4 (lane % 16)
-  const int my_r = w + 4 * (lane & 15);
+  // lanes 0..7 (and their copies in the other lanes) hold tile row w + 8 (lane % 8)
+  const int my_r = w + NW * (lane & 7);
   auto entry = [&](int tile) -> int {  // index entry of my_r in a tile (clamped load)
     const int i = s_begin + kMT * tile + my_r;
     if (sc.idx) return sc.idx[min(i, sc.NS - 1)];
     return i;
   };
-  // paged: the page of an entry (clamped into the sequence's table; ignored for
-  // window slots and empty entries)
   auto page_of = [&](int e) -> int {
     return kv_page(sc.pg, b, min(max(e, 0), sc.N_cap - 1));
   };
-  auto row_ptr = [&](int tile, int e, int pid, uint32_t& mask16) -> const uint8_t* {
+  auto row_ptr = [&](int tile, int e, int pid, uint32_t& mask8) -> const uint8_t* {
     const int i = s_begin + kMT * tile + my_r;
     const uint8_t* p = i < s_end ? slot_row_e<PAGED>(sc, i, e, pid) : nullptr;
-    mask16 = static_cast<uint32_t>(__ballot(p != nullptr)) & 0xffffu;
+    mask8 = static_cast<uint32_t>(__ballot(p != nullptr)) & 0xffu;
     return p ? p : sc.cache_b;
   };
   const int lane_off = KVFMT == LCA_BF16 ? lane * 16 : (lane < 56 ? lane * 8 : 448 + (lane - 56) * 16);
-  uint4 raw[16];
+  uint4 raw[8];
   auto load_rows = [&](const uint8_t* p) {
     const uint64_t pv = reinterpret_cast<uint64_t>(p);
     const uint32_t lo = static_cast<uint32_t>(pv), hi = static_cast<uint32_t>(pv >> 32);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const uint64_t pi =
           (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(hi, i))) << 32) |
           static_cast<uint32_t>(__builtin_amdgcn_readlane(lo, i));
       raw[i] = ldg16(reinterpret_cast<const uint8_t*>(pi) + lane_off);
     }
   };
-  auto stage = [&](int buf, uint32_t mask16) {
+  auto stage = [&](int buf, uint32_t mask8) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
       uint4 v = raw[i];
       if (KVFMT != LCA_BF16) {  // 8 OCP e4m3 dims -> bf16 (exact) for lanes < 56
         const uint4 c = make_uint4(fp8x2_to_bf16x2<false>(raw[i].x), fp8x2_to_bf16x2<true>(raw[i].x),
                                    fp8x2_to_bf16x2<false>(raw[i].y), fp8x2_to_bf16x2<true>(raw[i].y));
         if (lane < 56) v = c;
       }
-      if (!((mask16 >> i) & 1u)) v = make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(&kv_s[buf][(w + 4 * i) * kQS + lane * 8]) = v;
+      if (!((mask8 >> i) & 1u)) v = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&kv_s[buf][(w + NW * i) * kQS + lane * 8]) = v;
     }
-    if (lane == 0) vm_s[buf][w] = mask16;
+    if (lane == 0) vm_s[buf][w] = mask8;
   };
 
   // issue order: the index entries of the first two tiles (paged: three), the
   // query fragments, (paged: the pages of the first two tiles' entries,) then the
-  // first tile's rows.  Vector loads complete in order for the wait counter, so
-  // each wait covers only what it needs.
+  // first tile's rows
   const int e_first = entry(0);
   int e_next = entry(1);
   int e_next2 = PAGED ? entry(2) : 0;
   sc.t = q_pos[row];
   sc.vis = visible_entries(sc.t, m, n_entries[b], N_cap);
-  uint4 qf[kMC / 32];
+  uint4 qf[kMC / 64];
   {
-    const uint16_t* qh = q + (static_cast<size_t>(row) * kMH + head) * kMC + 256 * kh + 8 * g;
+    const uint16_t* qh = q + (static_cast<size_t>(row) * kMH + head) * kMC + 128 * kq + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < kMC / 32; ++ks) qf[ks] = *reinterpret_cast<const uint4*>(qh + 16 * ks);
+    for (int ks = 0; ks < kMC / 64; ++ks) qf[ks] = *reinterpret_cast<const uint4*>(qh + 16 * ks);
   }
   uint32_t mask_cur;
   int pid_first = 0, pid_next = 0;
@@ -772,12 +776,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   }
   load_rows(row_ptr(0, e_first, pid_first, mask_cur));
 
-  // RMSNorm of the query over its 512 dims: lane halves and the two waves of a
-  // head half hold a quarter each; the wave sums go through LDS
+  // RMSNorm of the query over its 512 dims: lane halves and the four waves of a
+  // head half hold an eighth each; the wave sums go through LDS
   {
     float ss = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < kMC / 32; ++ks) {
+    for (int ks = 0; ks < kMC / 64; ++ks) {
       const uint32_t w4[4] = {qf[ks].x, qf[ks].y, qf[ks].z, qf[ks].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -788,16 +792,17 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
       }
     }
     ss += __shfl_xor(ss, 32, 64);
-    if (g == 0) ps_s[kh][head] = ss;
+    if (g == 0) ps_s[kq][head] = ss;
     if (rope_step != 0.0 && w == 0 && lane < kRopeDims / 2) rope_s[lane] = rope_cs(sc.t, lane, rope_step);
     __syncthreads();
-    const float r = rsqrt_hw((ps_s[0][head] + ps_s[1][head]) / static_cast<float>(kMC) + eps);
-    // the rotary dims 448..511 (k-steps 12..15 of the kh = 1 waves) turned to the
+    const float r = rsqrt_hw(((ps_s[0][head] + ps_s[1][head]) + (ps_s[2][head] + ps_s[3][head])) /
+                                 static_cast<float>(kMC) + eps);
+    // the rotary dims 448..511 (k-steps 4..7 of the kq = 3 waves) turned to the
     // query position
-    const bool rope_q = rope_step != 0.0 && kh == 1;
-    constexpr int kRopeStep = (kMC - kRopeDims - 256) / 16;
+    const bool rope_q = rope_step != 0.0 && kq == 3;
+    constexpr int kRopeStep = (kMC - kRopeDims - 384) / 16;
 #pragma unroll
-    for (int ks = 0; ks < kMC / 32; ++ks) {
+    for (int ks = 0; ks < kMC / 64; ++ks) {
       uint32_t w4[4] = {qf[ks].x, qf[ks].y, qf[ks].z, qf[ks].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -811,20 +816,16 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   }
 
   float m_run = -INFINITY, l_run = 0.f;  // softmax state of `head`
-  v16f_t o[8];
+  v16f_t o[4];
 #pragma unroll
-  for (int db = 0; db < 8; ++db) o[db] = v16f_t{0};
-  // transposing-read source of this lane: row (lane%16)/4, dims 16 (lane/16 % 2)
-  // + 4 (lane%4) within a 4-row x 32-dim block (see tr_rows4)
+  for (int db = 0; db < 4; ++db) o[db] = v16f_t{0};
   const int tr_r = (lane & 15) >> 2;
   const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int rb = kq >> 1, rh = kq & 1;  // this wave's 16 rows: block rb, registers 8 rh .. +8
 
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
     stage(buf, mask_cur);
-    // the next tile's row pointers (entries loaded one tile ago) and the entries
-    // of the tile after it.  Paged: entries run two tiles ahead and their pages
-    // one tile ahead, so no lookup waits.
     uint32_t mask_next = 0;
     const uint8_t* p_next = row_ptr(t + 1, e_next, pid_next, mask_next);
     if constexpr (PAGED) {
@@ -838,24 +839,23 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     if (t + 1 < n_tiles) load_rows(p_next);  // in flight during this tile's compute
     mask_cur = mask_next;
 
-    // partial S^T (this wave's dims) of its own rows 32 kh .. +32 (acc[0]) and
-    // of the other 32 rows (acc[1])
+    // partial S^T over this wave's 128 dims for the rows 0..31 (acc[0]) and
+    // 32..63 (acc[1])
     v16f_t acc[2];
     {
       acc[0] = v16f_t{0};
       acc[1] = v16f_t{0};
-      const uint16_t* kb0 = &kv_s[buf][(32 * kh + j32) * kQS + 256 * kh + 8 * g];
-      const uint16_t* kb1 = &kv_s[buf][(32 * (kh ^ 1) + j32) * kQS + 256 * kh + 8 * g];
+      const uint16_t* kb0 = &kv_s[buf][j32 * kQS + 128 * kq + 8 * g];
+      const uint16_t* kb1 = &kv_s[buf][(32 + j32) * kQS + 128 * kq + 8 * g];
 #pragma unroll
-      for (int ks = 0; ks < kMC / 32; ++ks) {
+      for (int ks = 0; ks < kMC / 64; ++ks) {
         const uint4 a0 = *reinterpret_cast<const uint4*>(kb0 + 16 * ks);
         const uint4 a1 = *reinterpret_cast<const uint4*>(kb1 + 16 * ks);
         acc[0] = mfma_bf16(as_v8bf(a0), as_v8bf(qf[ks]), acc[0]);
         acc[1] = mfma_bf16(as_v8bf(a1), as_v8bf(qf[ks]), acc[1]);
       }
     }
-    // exchange with the other dim half through the free KV buffer:
-    // sx[wave][16 blk + r][lane] (blk 0: the writer's own rows)
+    // exchange through the free KV buffer: sx[wave][16 blk + r][lane]
     float* sx = reinterpret_cast<float*>(kv_s[buf ^ 1]);
     {
       float* sw = sx + w * 2048 + lane;
@@ -866,80 +866,81 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
       }
     }
     __syncthreads();  // B2: partial scores
-    // full scores: own rows (the partner's other block) and the other rows (the
-    // partner's own block)
-    float so[16], st[16];
+    // full scores of this wave's rows 16 kq + 8 (i/4) + 4 g + i%4, summed over the
+    // four dim quarters in quarter order
+    // (the wave's own partial is read back from LDS too, so every row sums in the
+    // same order whichever wave holds it)
+    float s8[8];
     {
-      const float* pw = sx + (w ^ 2) * 2048 + lane;
+      float tot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        so[r] = (acc[0][r] + pw[(16 + r) * 64]) * tau;
-        st[r] = (acc[1][r] + pw[r * 64]) * tau;
+      for (int qq = 0; qq < 4; ++qq) {
+        const float* pw = sx + (hg + 2 * qq) * 2048 + (16 * rb + 8 * rh) * 64 + lane;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tot[i] += pw[i * 64];
       }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s8[i] = tot[i] * tau;
     }
     {
-      // empty rows -> -inf.  Tile row 32 rb + 8 (r/4) + 4 g + r%4 was loaded by
-      // wave r%4 as its row number 8 rb + 2 (r/4) + g.
-      const uint4 vm = *reinterpret_cast<const uint4*>(vm_s[buf]);
-      if (((vm.x & vm.y & vm.z & vm.w) & 0xffffu) != 0xffffu) {
-        const uint32_t vmw[4] = {vm.x >> g, vm.y >> g, vm.z >> g, vm.w >> g};
+      // empty rows -> -inf.  Tile row 16 kq + 8 (i/4) + 4 g + i%4 was loaded by
+      // wave 4 g + i%4 as its row number 2 kq + i/4.
+      const uint4 v0 = *reinterpret_cast<const uint4*>(&vm_s[buf][0]);
+      const uint4 v1 = *reinterpret_cast<const uint4*>(&vm_s[buf][4]);
+      if (((v0.x & v0.y & v0.z & v0.w & v1.x & v1.y & v1.z & v1.w) & 0xffu) != 0xffu) {
+        const uint32_t vmw[4] = {g ? v1.x : v0.x, g ? v1.y : v0.y, g ? v1.z : v0.z, g ? v1.w : v0.w};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int bo = 8 * kh + 2 * (r >> 2), bt = 8 * (kh ^ 1) + 2 * (r >> 2);
-          if (!((vmw[r & 3] >> bo) & 1u)) so[r] = -INFINITY;
-          if (!((vmw[r & 3] >> bt) & 1u)) st[r] = -INFINITY;
-        }
+        for (int i = 0; i < 8; ++i)
+          if (!((vmw[i & 3] >> (2 * kq + (i >> 2))) & 1u)) s8[i] = -INFINITY;
       }
     }
-    float tmax = so[0];
+    float tq = s8[0];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, fmaxf(so[r], st[r]));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    for (int i = 1; i < 8; ++i) tq = fmaxf(tq, s8[i]);
+    tq = fmaxf(tq, __shfl_xor(tq, 32, 64));
+    if (g == 0) mx_s[kq][head] = tq;
+    __syncthreads();  // B2b: the row quarters' maxima
+    const float tmax = fmaxf(fmaxf(mx_s[0][head], mx_s[1][head]), fmaxf(mx_s[2][head], mx_s[3][head]));
     const float m_new = (m_run == -INFINITY || tmax > m_run + kLazyMax) ? tmax : m_run;
-    // O and l are zero while m_run is -inf, so no rescale is needed then
     const float alpha = (m_run == -INFINITY || m_new == m_run) ? 1.f : __expf(m_run - m_new);
-    // every row of the head empty so far: m_new = -inf, and exp(-inf - 0) = 0
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     {
-      // P of this wave's rows 32 kh .. +32 (both waves of the head half hold all
-      // of S; each writes half of P)
+      // P of this wave's 16 rows
       float psum = 0.f;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
+      for (int q4 = 0; q4 < 2; ++q4) {
         uint32_t pk[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const float p0 = __expf(so[4 * q4 + 2 * u] - m_use);
-          const float p1 = __expf(so[4 * q4 + 2 * u + 1] - m_use);
+          const float p0 = __expf(s8[4 * q4 + 2 * u] - m_use);
+          const float p1 = __expf(s8[4 * q4 + 2 * u + 1] - m_use);
           pk[u] = pack_bf16(p0, p1);
           psum += bf16_to_f32(static_cast<uint16_t>(pk[u] & 0xffffu)) +
                   bf16_to_f32(static_cast<uint16_t>(pk[u] >> 16));
         }
-        *reinterpret_cast<uint2*>(&p_s[head * kPS + 32 * kh + 8 * q4 + 4 * g]) = make_uint2(pk[0], pk[1]);
+        *reinterpret_cast<uint2*>(&p_s[head * kPS + 16 * kq + 8 * q4 + 4 * g]) = make_uint2(pk[0], pk[1]);
       }
       psum += __shfl_xor(psum, 32, 64);
-      if (g == 0) ps_s[kh][head] = psum;
+      if (g == 0) ps_s[kq][head] = psum;
     }
-    __syncthreads();  // B3: P and the row-half sums
-    l_run = l_run * alpha + ps_s[0][head] + ps_s[1][head];
+    __syncthreads();  // B3: P and the row-quarter sums
+    l_run = l_run * alpha + ((ps_s[0][head] + ps_s[1][head]) + (ps_s[2][head] + ps_s[3][head]));
     m_run = m_new;
-    // rescale O where the running maximum moved (rare after the first tiles)
     if (__ballot(alpha != 1.f)) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float al = __shfl(alpha, 8 * (r >> 2) + 4 * g + (r & 3), 64);
 #pragma unroll
-        for (int db = 0; db < 8; ++db) o[db][r] *= al;
+        for (int db = 0; db < 4; ++db) o[db][r] *= al;
       }
     }
-    // O[heads 32 hg + .., dims 256 kh + ..] += P V
+    // O[heads 32 hg + .., dims 128 kq + ..] += P V
 #pragma unroll
     for (int ks = 0; ks < kMT / 16; ++ks) {
       const v8bf_t A = as_v8bf(*reinterpret_cast<const uint4*>(&p_s[head * kPS + 16 * ks + 8 * g]));
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        // B = V rows 16 ks + 8 g .. +8 of dim 256 kh + 32 db + j32, read transposed
-        const uint16_t* vp = &kv_s[buf][(16 * ks + 8 * g + tr_r) * kQS + 256 * kh + 32 * db + tr_d];
+      for (int db = 0; db < 4; ++db) {
+        const uint16_t* vp = &kv_s[buf][(16 * ks + 8 * g + tr_r) * kQS + 128 * kq + 32 * db + tr_d];
         const uint2 lo = tr_rows4(vp);
         const uint2 hi = tr_rows4(vp + 4 * kQS);
         o[db] = mfma_bf16(A, as_v8bf(make_uint4(lo.x, lo.y, hi.x, hi.y)), o[db]);
@@ -961,7 +962,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
       lse_v = tot;
     }
   }
-  if (kh == 0 && g == 0) {
+  if (kq == 0 && g == 0) {
     if (n_splits == 1) {
       if (lse) lse[static_cast<size_t>(row) * kMH + head] = lse_v;
     } else {
@@ -971,13 +972,13 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   if (n_splits > 1) {
     // fp32 partial rows straight from the accumulators (a lane's 32 columns of
     // a head are 128 contiguous bytes; the merge turns the output back)
-    float* pb = part_o + (static_cast<size_t>(row) * n_splits + split) * kMH * kMC + 256 * kh + j32;
+    float* pb = part_o + (static_cast<size_t>(row) * n_splits + split) * kMH * kMC + 128 * kq + j32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int h = 32 * hg + 8 * (r >> 2) + 4 * g + (r & 3);
       const float fr = __shfl(f, 8 * (r >> 2) + 4 * g + (r & 3), 64);
 #pragma unroll
-      for (int db = 0; db < 8; ++db) pb[h * kMC + 32 * db] = o[db][r] * fr;
+      for (int db = 0; db < 4; ++db) pb[h * kMC + 32 * db] = o[db][r] * fr;
     }
     return;
   }
@@ -990,26 +991,22 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     const int h = 32 * hg + 8 * (r >> 2) + 4 * g + (r & 3);
     const float fr = __shfl(f, 8 * (r >> 2) + 4 * g + (r & 3), 64);
 #pragma unroll
-    for (int db = 0; db < 8; ++db) ost[h * kMC + 256 * kh + 32 * db + j32] = o[db][r] * fr;
+    for (int db = 0; db < 4; ++db) ost[h * kMC + 128 * kq + 32 * db + j32] = o[db][r] * fr;
   }
   __syncthreads();
-  const size_t obase = n_splits == 1 ? static_cast<size_t>(row) * kMH * kMC
-                                     : (static_cast<size_t>(row) * n_splits + split) * kMH * kMC;
-  // 64 x 512 fp32 = 8192 chunks of 16 B; thread tid writes chunks tid + 256 i
-#pragma unroll 8
-  for (int i = 0; i < kMH * kMC / 4 / 256; ++i) {
-    const int c4 = (tid + 256 * i) * 4;
+  const size_t obase = static_cast<size_t>(row) * kMH * kMC;
+  // 64 x 512 fp32 = 8192 chunks of 16 B; thread tid writes chunks tid + 512 i
+#pragma unroll 4
+  for (int i = 0; i < kMH * kMC / 4 / (64 * NW); ++i) {
+    const int c4 = (tid + 64 * NW * i) * 4;
     float4 v = *reinterpret_cast<const float4*>(&ost[c4]);
-    if (n_splits == 1 && rope_step != 0.0 && (c4 & (kMC - 1)) >= kMC - kRopeDims) {
-      // the output turned back by -t (a split output is turned by the merge)
+    if (rope_step != 0.0 && (c4 & (kMC - 1)) >= kMC - kRopeDims) {  // the output turned back by -t
       const int pr = ((c4 & (kMC - 1)) - (kMC - kRopeDims)) >> 1;
       const float2 c0 = rope_s[pr], c1 = rope_s[pr + 1];
       rope_turn(v.x, v.y, make_float2(c0.x, -c0.y));
       rope_turn(v.z, v.w, make_float2(c1.x, -c1.y));
     }
-    if (n_splits > 1) {
-      *reinterpret_cast<float4*>(&part_o[obase + c4]) = v;
-    } else if (out_fmt == LCA_F32) {
+    if (out_fmt == LCA_F32) {
       *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + obase + c4) = v;
     } else {
       *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + obase + c4) =
@@ -1183,8 +1180,9 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
   }
   if (p.decode) {
     const dim3 grid(static_cast<unsigned>(rows * p.n_splits));
+    const dim3 block(64 * kD8Waves);
     auto go = [&](auto kern) {
-      hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, n_q, static_cast<const uint16_t*>(q),
+      hipLaunchKernelGGL(kern, grid, block, 0, s, n_q, static_cast<const uint16_t*>(q),
                          static_cast<const uint8_t*>(cache), N_cap, idx, k, q_pos, m, n_entries,
                          static_cast<const uint8_t*>(win), W_cap, static_cast<long long>(win_origin),
                          n_win, tau, eps, sink, rope_step, p.n_splits, p.split_rows,
