@@ -1022,8 +1022,9 @@ constexpr int kMaxMergeSplits = 256;
 // The lse values and partial rows of up to CH splits are loaded together, so a
 // merge of that many splits takes one memory round trip; more splits go CH at a
 // time with a running maximum.  Splits are combined in split order
-// (deterministic).  CH (4, 8, 12 or 16) is the split count rounded up to a
-// multiple of 4, so few loads are clamped repeats of the last split.
+// (deterministic).  CH (4 .. 20) is the split count rounded up to a multiple of
+// 4, so few loads are clamped repeats of the last split; more than 20 splits go
+// 16 at a time.
 template <int CH>
 __global__ __launch_bounds__(256) void attn_merge4_kernel(
     long long rows, int H, int c, int n_splits, const float* __restrict__ part_o,
@@ -1227,6 +1228,8 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
   if (p.n_splits <= 4) merge(attn_merge4_kernel<4>);
   else if (p.n_splits <= 8) merge(attn_merge4_kernel<8>);
   else if (p.n_splits <= 12) merge(attn_merge4_kernel<12>);
+  else if (p.n_splits <= 16) merge(attn_merge4_kernel<16>);
+  else if (p.n_splits <= 20) merge(attn_merge4_kernel<20>);
   else merge(attn_merge4_kernel<16>);
   return hipGetLastError();
 }
