@@ -633,6 +633,15 @@ __global__ __launch_bounds__(kRowsThreads, 2) void indexer_rows_kernel(
       const float sv = group_reduce_reg(acc[grp], wr);
       const int key = t * kTileKeys + kKeysPerGroup * grp + j;
       if (g == 0 && key < vis) store_score(&out[key], sv);
+      if (grp + 1 < kGroups) {
+        // the next group's four MFMAs spread over this group's epilogue (one per
+        // 16 VALU operations) instead of issued back to back ahead of it
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // sixteen VALU
+        }
+      }
     }
     if (t + 1 < n_tiles) {
       store_tile(buf ^ 1);
