@@ -331,9 +331,12 @@ int lca_state_append(int mode, int m, int B, int c, int n_win, const void* tokC,
  * lca_decode_step -- one decode step of one CSA or HCA layer for B sequences:
  * lca_state_append, then (CSA) lca_indexer_scores + lca_topk, then
  * lca_sparse_mqa over the ring window (W_cap = n_win, win_origin = 0).  For
- * CSA rows longer than 36864 entries with an FP8/MXFP4 indexer, the indexer
- * also builds the top-k's score histogram (the append clears it), so the
- * top-k skips its own histogram pass; results are identical.
+ * CSA rows longer than 36864 entries with an FP8/MXFP4 indexer, the indexer and
+ * the top-k are fused: the scores stay on chip, each indexer workgroup writes
+ * out the entries that can still be among the row's k largest, and a finish
+ * pass selects the k largest among them -- the indices lca_topk returns over
+ * the scores lca_indexer_scores writes for the same inputs.  Shorter rows go
+ * through a score array in the workspace and lca_topk's path.
  * ------------------------------------------------------------------------- */
 typedef struct lca_decode_layer {
   size_t struct_size;   /* sizeof(lca_decode_layer) */

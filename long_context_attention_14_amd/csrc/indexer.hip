@@ -22,6 +22,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 
@@ -684,17 +685,36 @@ __global__ __launch_bounds__(kF32Threads) void indexer_f32_kernel(
 
 }  // namespace
 
+// Compute units of the current device, asked on every call (a host-side
+// attribute lookup): the library keeps no per-process cache of it.
 static int device_cus() {
-  static int cached = 0;
-  if (cached == 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
-      cached = cus;
-    else
-      return 256;
-  }
-  return cached;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+    return cus;
+  return 256;
+}
+
+// The fused selection keeps up to kSelMaxBlocks blocks of scores in dynamic
+// LDS, above the default limit: the kernel's limit is raised once per device
+// and kernel instance (std::call_once, so concurrent first calls from several
+// host threads are safe), and the result of that call is kept with it.
+constexpr int kMaxDevices = 64;
+
+template <bool MX>
+static hipError_t select_lds_limit() {
+  static std::once_flag once[kMaxDevices];
+  static hipError_t result[kMaxDevices];
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [dev] {
+    result[dev] = hipFuncSetAttribute(reinterpret_cast<const void*>(indexer_select_kernel<MX>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      static_cast<int>(sizeof(float) * kBlockKeys * kSelMaxBlocks));
+  });
+  return result[dev];
 }
 
 hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const void* qI,
@@ -743,16 +763,9 @@ hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const v
     const dim3 grid(static_cast<unsigned>(rows * wpr)), block(kSelThreads);
     const int iw = static_cast<int>(wpr);
     const SelectWs so = *sel;
-    hipError_t e = hipSuccess;
+    hipError_t e = mx ? select_lds_limit<true>() : select_lds_limit<false>();
+    if (e != hipSuccess) return e;
     auto go = [&](auto kern) {
-      static bool attr_set = false;  // per kernel: LDS above the default dynamic limit
-      if (!attr_set) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                static_cast<int>(sizeof(float) * kBlockKeys * kSelMaxBlocks));
-        if (e != hipSuccess) return;
-        attr_set = true;
-      }
       if (ev_start || ev_stop)
         hipExtLaunchKernelGGL(kern, grid, block, lds, s, ev_start, ev_stop, 0, q8, qI_scale, k8,
                               kI_scale, n_q, N_cap, iw, w, q_pos, m, n_entries, so, k, sel_idx);

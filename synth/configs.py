@@ -82,7 +82,7 @@ class OutProjConfig:
     """Grouped output projection after the attention: the n_h heads' outputs in
     g groups, each projected to d_g, then all groups back to the hidden size d
     (QbitAI article, hybrid attention section; d = 7168 is V4-Pro's hidden size,
-    same article, model architecture paragraph).  The pages give neither g nor
+    same article, section 模型訓練 (model training)).  The pages give neither g nor
     d_g: g = 8 groups of 8 heads and d_g = 1024 are readings."""
     name: str
     T: int                 # query tokens (decode: the batch; prefill: the chunk)

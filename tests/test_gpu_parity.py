@@ -481,6 +481,42 @@ def test_csa_prefill_chunk_full_size_sampled():
 # decode steps
 
 
+def _gpu_decode_scores(layer, cfg, d, pos):
+    """Float32 index scores of each sequence's decode query at position pos[b]
+    (after the step's append), written by lca_indexer_scores from the layer's own
+    indexer inputs.  The decode step's selection (the fused indexer + selection
+    kernel for long rows, the score-writing kernel for short ones) scores every
+    entry with the same MFMA tiles and the same reduction order, so these are
+    the scores it selected from; the select stage is checked on them bit for
+    bit."""
+    m, B = d["m"], cfg.B
+    pos = np.asarray(pos, np.int64).reshape(B)
+    n_ent = ((pos + 1) // m).astype(np.int32)
+    scores = torch.full((B, 1, layer.N_cap), float("nan"), dtype=torch.float32, device=DEV)
+    ops.lca_indexer_scores(B, 1, cfg.H_I, cfg.d_I, cfg.idx_dtype, layer.qI, layer.qI_scale, layer.kI,
+                           layer.kI_scale, layer.N_cap, layer.w, T(pos.astype(np.int32).reshape(B, 1)),
+                           m, T(n_ent), scores)
+    return host(scores).reshape(B, layer.N_cap)
+
+
+def _check_decode_selection(cfg, d, b, idx_row, gpu_scores_row, oracle_scores, p, kI_rows=None,
+                            what=""):
+    """Selection parity of one decode row (every row, certified or not): the select
+    stage bit-exact on the GPU's own float32 scores, those scores within the fp32
+    evaluation bound of the oracle's, and the selection equal to the oracle's on a
+    certified row, else holding every clear winner and no clear loser.  Returns
+    True when the row was certified."""
+    m = d["m"]
+    vis = (p + 1) // m
+    sc = d.get("kI_scale")
+    if kI_rows is None:
+        kI_rows = O.decode(d["kI"][b, :vis], cfg.idx_dtype, None if sc is None else sc[b, :vis])
+    qI = O.decode(d["qI"][b], cfg.idx_dtype, None if d.get("qI_scale") is None else d["qI_scale"][b])
+    bnd = O.score_error_bound(qI[None], kI_rows[:vis], d["w"][b][None].astype(np.float64))[0]
+    return OS.check_selection(idx_row, gpu_scores_row[:vis], np.asarray(oracle_scores)[:vis], bnd, vis,
+                              cfg.k, what=what)
+
+
 def _decode_parity(cfg, d, seqs, layer=None):
     if layer is None:
         layer = pipeline.DecodeLayer(cfg, d, DEV)
@@ -495,7 +531,9 @@ def _decode_parity(cfg, d, seqs, layer=None):
     cache = layer.logical_cache()
     ring = host(layer.ring).view(np.uint8).reshape(cfg.B, cfg.n_win, rb)
     assert np.array_equal(ntok, d["n_tokens"] + 1)
-    n_cert = 0
+    csa = d["kind"] == "C"
+    gscores = _gpu_decode_scores(layer, cfg, d, d["n_tokens"]) if csa else None
+    n_cert = n_rows = 0
     for b in seqs:
         ref = OS.oracle_decode(cfg, d, b)
         p = int(d["n_tokens"][b])
@@ -505,25 +543,22 @@ def _decode_parity(cfg, d, seqs, layer=None):
             s = (p + 1) // m - 1
             OS.assert_within_ulp(O.decode(_stored(cache[b, s], kv), kv), ref["new_entry"], kv,
                                  slack=ref["new_entry_bound"], what="new entry")
-        if d["kind"] == "C":
-            vis = (p + 1) // m
-            sel = idx[b]
-            # selection: certified rows bit-exact against the oracle's own top-k
-            st = ref["state"]
-            sc = d.get("kI_scale")
-            kI = O.decode(d["kI"][b, :vis], cfg.idx_dtype, None if sc is None else sc[b, :vis])
-            qI = O.decode(d["qI"][b], cfg.idx_dtype, None if d.get("qI_scale") is None else d["qI_scale"][b])
-            bnd = O.score_error_bound(qI[None], kI, d["w"][b][None].astype(np.float64))[0]
-            osel = ref["idx"]
-            if OS.certified(ref["scores"], bnd, vis, cfg.k):
-                assert np.array_equal(sel, osel), f"b{b}: certified row selects differently"
-                n_cert += 1
-            ref = OS.oracle_decode(cfg, d, b, idx_given=sel)
+        if csa:
+            # every row's selection: select stage bit-exact on the GPU's scores,
+            # scores within bound, certified rows equal to the oracle's top-k,
+            # the others with every clear winner and no clear loser
+            n_cert += _check_decode_selection(cfg, d, b, idx[b], gscores[b], ref["scores"], p,
+                                              what=f"b{b}")
+            n_rows += 1
+            ref = OS.oracle_decode(cfg, d, b, idx_given=idx[b])
         err = np.abs(out[b] - ref["out"])
         assert err.max() <= OUT_TOL[io], f"b{b}: out err {err.max():.3g}"
         lerr = np.abs(lse[b] - ref["lse"])
         assert lerr.max() <= LSE_TOL[io], f"b{b}: lse err {lerr.max():.3g}"
-    say(f"{cfg.name}: {n_cert} of {len(seqs)} CSA rows certified")
+    if csa:
+        assert n_rows == len(list(seqs)) and n_rows > 0
+        say(f"{cfg.name}: selection checked on {n_rows} CSA rows ({n_cert} certified, "
+            f"{n_rows - n_cert} by select stage + clear winners/losers)")
     return layer
 
 
@@ -646,6 +681,8 @@ def test_decode_multi_step_matches_oracle_stepping(rope):
             layer.step()
             out = out_f64(layer.out)
             idx = host(layer.idx)
+            pos = [states[b].L for b in range(cfg.B)]
+            gsc = _gpu_decode_scores(layer, cfg, d, pos) if d["kind"] == "C" else None
             for b in range(cfg.B):
                 kw = {}
                 if d["kind"] == "C":
@@ -658,28 +695,78 @@ def test_decode_multi_step_matches_oracle_stepping(rope):
                                   q=O.decode(d["q"][b], cfg.io_dtype), tau=cfg.tau, eps=cfg.eps,
                                   kv_fmt=cfg.kv_dtype, out_fmt=cfg.io_dtype, rope_base=cfg.rope_base,
                                   **kw)
+                if d["kind"] == "C":
+                    _check_decode_selection(cfg, d, b, idx[b], gsc[b], r["scores"], pos[b],
+                                            kI_rows=kw["kI"], what=f"step {step} b{b}")
                 err = np.abs(out[b] - r["out"]).max()
                 assert err <= OUT_TOL[cfg.io_dtype], f"step {step} b{b}: {err:.3g}"
 
 
-def test_decode_deterministic_and_batch_invariant():
-    cfg = CSA_DECODE_1M.with_(B=3, ctx=1 << 16)
-    say("determinism / batch invariance")
-    d = gen.decode_inputs(cfg)
-    outs = []
-    for _ in range(2):
-        layer = pipeline.DecodeLayer(cfg, d, DEV)
-        layer.step()
-        outs.append((host(layer.out.view(torch.int16)), host(layer.idx), host(layer.lse)))
-    for a, b in zip(outs[0], outs[1]):
-        assert np.array_equal(a, b)
-    # sequence 1 alone
-    one = {k: (v[1:2] if isinstance(v, np.ndarray) and v.ndim >= 1 and v.shape[0] == cfg.B else v)
-           for k, v in d.items()}
-    layer1 = pipeline.DecodeLayer(cfg.with_(B=1), one, DEV)
-    layer1.step()
-    assert np.array_equal(host(layer1.out.view(torch.int16))[0], outs[0][0][1])
-    assert np.array_equal(host(layer1.idx)[0], outs[0][1][1])
+def _hybrid_csa_layer(ctx, B=None):
+    """The first CSA layer of the hybrid stack (layer 2: MXFP4 indexer keys, KV in
+    fp8 with bf16 RoPE dims), drawn as the stack draws it."""
+    cfg = HYBRID_DECODE_1M.with_(ctx=ctx) if B is None else HYBRID_DECODE_1M.with_(ctx=ctx, B=B)
+    d = gen.decode_layer(cfg, "C", cfg.m, gen.hybrid_lengths(cfg), layer=2)
+    return cfg, d
+
+
+@pytest.mark.parametrize("ctx", [1 << 18, 1 << 20])
+def test_hybrid_csa_decode_mxfp4_fused_selection(ctx):
+    """A CSA layer of the hybrid stack on rows longer than the LDS top-k takes
+    (65536 and 262144 entries), so the MXFP4 instance of the fused indexer +
+    selection runs; at 2^20 tokens this is the stack's own CSA layer (batch 4)."""
+    cfg, d = _hybrid_csa_layer(ctx)
+    say(f"hybrid CSA layer (MXFP4 keys, fp8+bf16 KV) B={cfg.B} ctx={ctx} N_cap={d['n_cap']}")
+    assert d["n_cap"] > 36864
+    _decode_parity(cfg, d, range(cfg.B))
+
+
+def _seq_slice(d, B, sel):
+    return {k: (np.ascontiguousarray(v[sel]) if isinstance(v, np.ndarray) and v.ndim >= 1 and
+                v.shape[0] == B else v) for k, v in d.items()}
+
+
+def _decode_bits(cfg, d):
+    layer = pipeline.DecodeLayer(cfg, d, DEV)
+    layer.step()
+    torch.cuda.synchronize()
+    return {"out": host(layer.out.view(torch.int16)), "idx": host(layer.idx), "lse": host(layer.lse),
+            "cache": layer.logical_cache(), "ring": host(layer.ring).view(np.uint8)}
+
+
+@pytest.mark.parametrize("fmt,ctx", [("fp8", 1 << 16), ("fp8", 1 << 18), ("mxfp4", 1 << 18)])
+def test_decode_deterministic_and_batch_invariant(fmt, ctx):
+    """Two runs give the same bits; sequence 1 run alone (B = 1) gives the bits it
+    gets inside a batch of 3; and other inputs for sequences 0 and 2 leave
+    sequence 1's bits unchanged.  At 2^18 tokens (65536 entries) the rows take
+    the fused indexer + selection, whose workgroup split of a row, dynamic group
+    counter and emission order all change with the batch; at 2^16 the
+    score-array path.  (B = 1 and B = 3 share the attention's split plan: it
+    depends on the batch size only through the number of query rows.)"""
+    if fmt == "fp8":
+        cfg = CSA_DECODE_1M.with_(B=3, ctx=ctx)
+        d = gen.decode_inputs(cfg)
+    else:
+        cfg, d = _hybrid_csa_layer(ctx, B=3)
+    say(f"determinism / batch invariance {fmt} ctx={ctx} N_cap={d['n_cap']}")
+    runs = [_decode_bits(cfg, d) for _ in range(2)]
+    for name in runs[0]:
+        assert np.array_equal(runs[0][name], runs[1][name]), f"{name} differs between two runs"
+    one = _decode_bits(cfg.with_(B=1), _seq_slice(d, cfg.B, slice(1, 2)))
+    for name in ("out", "idx", "lse"):
+        assert np.array_equal(one[name][0], runs[0][name][1]), f"{name}: B=1 differs from B=3"
+    assert np.array_equal(one["cache"][0], runs[0]["cache"][1])
+    # sequences 0 and 2 swap every per-sequence input: sequence 1 is unchanged
+    sw = dict(d)
+    for k, v in d.items():
+        if isinstance(v, np.ndarray) and v.ndim >= 1 and v.shape[0] == cfg.B and k not in (
+                "lengths", "n_tokens"):
+            v2 = v.copy()
+            v2[0], v2[2] = v[2], v[0]
+            sw[k] = v2
+    other = _decode_bits(cfg, sw)
+    for name in ("out", "idx", "lse"):
+        assert np.array_equal(other[name][1], runs[0][name][1]), f"{name}: depends on other sequences"
 
 
 def test_sink_logit():
@@ -822,9 +909,12 @@ def test_decode_steps_paged_multi_step(kind):
             assert np.array_equal(host(e["idx_out"]), ref_idx[i]), f"step {i} idx"
     assert np.array_equal(lay.logical_cache(), ref.logical_cache())
     assert np.array_equal(host(lay.n_tokens), host(ref.n_tokens))
-    # the oracle, stepped through the same tokens, agrees on the last output
+    # the oracle, stepped through the same tokens, agrees on every step's output
+    # and selection
     states = [OS.oracle_decode_state(cfg, d, b) for b in range(cfg.B)]
     for i, st in enumerate(toks):
+        pos = [states[b].L for b in range(cfg.B)]
+        gsc = _gpu_decode_scores(lay, cfg, d, pos) if csa else None
         for b in range(cfg.B):
             kw = {}
             if csa:
@@ -836,6 +926,9 @@ def test_decode_steps_paged_multi_step(kind):
                               tokZ=O.decode(st["tokZ"][b], cfg.io_dtype), P=d["P"],
                               q=O.decode(st["q"][b], cfg.io_dtype), tau=cfg.tau, eps=cfg.eps,
                               kv_fmt=cfg.kv_dtype, out_fmt=cfg.io_dtype, **kw)
+            if csa:
+                _check_decode_selection(cfg, d, b, kw["idx_given"], gsc[b], r["scores"], pos[b],
+                                        kI_rows=kw["kI"], what=f"step {i} b{b}")
             got = out_f64(steps[i]["out"])[b]
             err = np.abs(got - r["out"]).max()
             assert err <= OUT_TOL[cfg.io_dtype], f"step {i} b{b}: {err:.3g}"

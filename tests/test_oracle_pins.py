@@ -605,3 +605,186 @@ def test_compress_error_bound_covers_fp32_pooling():
     y32 = E32 / np.sqrt((E32 * E32).mean(-1, keepdims=True, dtype=np.float32) + np.float32(1e-6))
     assert np.all(np.abs(y32 - exact) <= bound)
     assert bound.max() < 1e-4
+
+
+# ---------------------------------------------------------------------------
+# the chunked-prefill branch and the decode state rebuilt from its physical layout
+
+
+@pytest.mark.parametrize("mode,m,rope_base", [("csa", 4, 0.0), ("csa", 4, 10000.0), ("hca", 8, 0.0),
+                                               ("hca", 8, 300.0)])
+def test_chunked_prefill_equals_one_shot_and_brute_force(mode, m, rope_base):
+    """A prefill of n1 + n2 tokens in one call equals the prefill of the last n2
+    tokens at pos0 = n1 fed the first part's stored entries (cache_prefix), its
+    last n_win - 1 stored window rows (win_prefix) and, for CSA, its last block's
+    candidates and gate logits (prevC, prevZ: the overlap with the previous block
+    reaches across the chunk boundary, "DeepSeek V4 Architecture Tricks",
+    compressed-KV tricks).  Entries, window rows, selections, outputs and lse are
+    bit-identical; the chunk also equals the brute-force twin of the whole
+    sequence (which turns entry s at (s+1)m-1 under RoPE, so the chunk's entry
+    positions carry the prefix offset)."""
+    n1, n2, H, n_win, k, kv = 24, 16, 2, 6, 3, "bf16"
+    c = 80 if rope_base else 16
+    n = n1 + n2
+    d = _tiny_layer_inputs(70 + m, n=n, c=c, H=H, m=m)
+    P = d["P"][: 2 * m if mode == "csa" else m]
+    tau = 1 / math.sqrt(c)
+    kw = dict(mode=mode, m=m, k=k, n_win=n_win, tau=tau, eps=1e-6, kv_fmt=kv, out_fmt="f32",
+              rope_base=rope_base)
+    full = O.prefill_layer(pos0=0, C=d["C"], Z=d["Z"], P=P, q=d["q"], cache_prefix=np.zeros((0, c)),
+                           qI=d["qI"], kI=d["kI"], w=d["w"], **kw)
+    csa = mode == "csa"
+    chunk = O.prefill_layer(pos0=n1, C=d["C"][n1:], Z=d["Z"][n1:], P=P, q=d["q"][n1:],
+                            cache_prefix=full["entries"][: n1 // m],
+                            prevC=d["C"][n1 - m:n1] if csa else None,
+                            prevZ=d["Z"][n1 - m:n1] if csa else None,
+                            win_prefix=full["window"][n1 - (n_win - 1):n1],
+                            qI=d["qI"][n1:], kI=d["kI"], w=d["w"][n1:], **kw)
+    assert np.array_equal(chunk["entries"], full["entries"][n1 // m:])
+    assert np.array_equal(chunk["window"], full["window"][n1:])
+    assert np.array_equal(chunk["out"], full["out"][n1:])
+    assert np.array_equal(chunk["lse"], full["lse"][n1:])
+    if csa:
+        assert np.array_equal(chunk["idx"], full["idx"][n1:])
+    rk = (lambda row: O.round_to(np.array(row), kv).tolist())
+    outs, idxs, entries = brute.layer(mode=mode, m=m, k=k, n_win=n_win, tau=tau, eps=1e-6,
+                                      C=d["C"].tolist(), Z=d["Z"].tolist(), P=P.tolist(),
+                                      q=d["q"].tolist(), qI=d["qI"].tolist(), kI=d["kI"].tolist(),
+                                      w=d["w"].tolist(), round_kv=rk, rope_base=rope_base)
+    assert np.allclose(chunk["entries"], np.array(entries)[n1 // m:], rtol=1e-12, atol=1e-12)
+    if csa:
+        assert np.array_equal(chunk["idx"], np.array(idxs)[n1:])
+    assert np.allclose(chunk["out"], np.array(outs)[n1:], rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("mode,m,L", [("csa", 4, 37), ("csa", 4, 40), ("csa", 4, 2), ("csa", 4, 5),
+                                      ("hca", 8, 45), ("hca", 8, 40), ("hca", 8, 3)])
+def test_decode_state_from_physical_layout_equals_stepped_state(mode, m, L):
+    """oracle_decode_state rebuilds a sequence's logical decode state from the
+    physical layout the library's header documents -- the token at position p
+    in tail row ((p/m) % 2) * m + p % m (CSA: the current and the previous
+    block) or p % m (HCA), its stored window row in ring slot p % n_win, entries
+    in cache rows 0 .. L/m - 1, L in the token counter.  Laid out here from
+    tokens stepped through a DecodeState from empty, it must give that state
+    back, and one more step from either state must give the same results."""
+    from oracle.workloads import oracle_decode_state
+    from synth.configs import TINY_CSA_PREFILL
+    c, n_win, H, HI, dI, k = 16, 6, 2, 3, 8, 3
+    r = rng(80 + L + m)
+    f32 = lambda a: a.astype(np.float32).astype(np.float64)  # noqa: E731  (stored exactly in f32)
+    C, Z = f32(r.standard_normal((L + 1, c))), f32(r.standard_normal((L + 1, c)))
+    q = r.standard_normal((L + 1, H, c))
+    qI, kI, w = r.standard_normal((L + 1, HI, dI)), r.standard_normal(((L + 1) // m + 1, dI)), r.random((L + 1, HI))
+    P = f32(r.standard_normal((2 * m if mode == "csa" else m, c)) * 0.1)
+    kw = dict(tau=0.25, eps=1e-6, kv_fmt="f32", out_fmt="f32")
+    ckw = (lambda t: dict(k=k, qI=qI[t], kI=kI, w=w[t])) if mode == "csa" else (lambda t: {})
+    ref = O.DecodeState(mode=mode, m=m, n_win=n_win, c=c)
+    stored_win = []
+    for t in range(L):
+        res = O.decode_step(ref, tokC=C[t], tokZ=Z[t], P=P, q=q[t], **kw, **ckw(t))
+        stored_win.append(res["window_row"])
+    # the physical layout, written from the header's formulas
+    T = 2 * m if mode == "csa" else m
+    tailC, tailZ = np.zeros((T, c), np.float32), np.zeros((T, c), np.float32)
+    ring = np.zeros((n_win, c), np.float32)
+    for p in range(L):
+        row = ((p // m) % 2) * m + p % m if mode == "csa" else p % m
+        tailC[row], tailZ[row] = C[p], Z[p]
+        ring[p % n_win] = stored_win[p]
+    n_ent = L // m
+    cache = np.zeros((n_ent + 2, c), np.float32)
+    cache[:n_ent] = ref.rows(np.arange(n_ent))
+    d = {"kind": "C" if mode == "csa" else "H", "m": m, "n_tokens": np.array([L], np.int32),
+         "tailC": tailC[None], "tailZ": tailZ[None], "ring": ring[None], "cache": cache[None]}
+    cfg = TINY_CSA_PREFILL.with_(c=c, n_win=n_win, io_dtype="f32", kv_dtype="f32")
+    st = oracle_decode_state(cfg, d, 0)
+    assert st.L == ref.L and st.n_entries == ref.n_entries
+    for a, b in zip(st.cur, ref.cur):
+        assert np.array_equal(a.reshape(-1, c), b.reshape(-1, c))
+    if mode == "csa":                    # HCA pools no previous block (its prev is unused)
+        assert (st.prev is None) == (ref.prev is None)
+    if mode == "csa" and ref.prev is not None:
+        for a, b in zip(st.prev, ref.prev):
+            assert np.array_equal(a.reshape(-1, c), b.reshape(-1, c))
+    assert np.array_equal(np.array(list(st.window)).reshape(-1, c), np.array(list(ref.window)).reshape(-1, c))
+    assert np.array_equal(st.rows(np.arange(n_ent)), ref.rows(np.arange(n_ent)))
+    a = O.decode_step(st, tokC=C[L], tokZ=Z[L], P=P, q=q[L], **kw, **ckw(L))
+    b = O.decode_step(ref, tokC=C[L], tokZ=Z[L], P=P, q=q[L], **kw, **ckw(L))
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["lse"], b["lse"])
+    assert (a["new_entry"] is None) == (b["new_entry"] is None)
+    if a["new_entry"] is not None:
+        assert np.array_equal(a["new_entry"], b["new_entry"])
+    if mode == "csa":
+        assert np.array_equal(a["idx"], b["idx"])
+
+
+def _pool_gpu_arith(C, Z, P, m, overlap, r):
+    """The compressor's float32 arithmetic with the error model of its hardware
+    functions: per channel, an online softmax over the candidates in time order
+    (running maximum; every rescale and weight through exp(x) = 2^(x log2 e) with
+    the product rounded to float32 and the exp2 result off by one ulp in a random
+    direction), the pooled value times a reciprocal of the weight sum (one ulp),
+    then RMSNorm with a reciprocal square root (one ulp).  Entry 0 of a CSA chunk
+    has no previous block."""
+    f = np.float32
+    n, c = C.shape
+    nb = n // m
+    C32, Z32, P32 = C.astype(f), Z.astype(f), P.astype(f)
+    log2e = f(1.4426950408889634)
+
+    def ulp_off(x):
+        s = r.choice([-1.0, 1.0], size=x.shape).astype(f)
+        return (x * (f(1) + s * f(2.0 ** -23))).astype(f)
+
+    def exp_hw(x):
+        y = (x.astype(f) * log2e).astype(f)
+        return ulp_off(np.exp2(y.astype(np.float64)).astype(f))
+
+    out = np.zeros((nb, c), f)
+    for s in range(nb):
+        cand = []
+        if overlap and s > 0:
+            cand += [(C32[(s - 1) * m + i], Z32[(s - 1) * m + i] + P32[i]) for i in range(m)]
+        slot0 = m if overlap else 0
+        cand += [(C32[s * m + i], (Z32[s * m + i] + P32[slot0 + i]).astype(f)) for i in range(m)]
+        mx = np.full(c, -np.inf, f)
+        sm, acc = np.zeros(c, f), np.zeros(c, f)
+        for cv, zv in cand:
+            nm = np.maximum(mx, zv)
+            with np.errstate(invalid="ignore"):
+                sc = np.where(np.isfinite(mx), exp_hw(mx - nm), f(0))
+            e = exp_hw(zv - nm)
+            sm = (sm * sc + e).astype(f)
+            acc = (acc * sc + e * cv).astype(f)
+            mx = nm
+        rcp = ulp_off((f(1) / sm).astype(f))
+        out[s] = (acc * rcp).astype(f)
+    ss = (out * out).sum(-1, dtype=f)
+    rs = ulp_off((f(1) / np.sqrt(ss / f(c) + f(1e-6))).astype(f))
+    return (out * rs[:, None]).astype(np.float64)
+
+
+@pytest.mark.parametrize("overlap,m,zscale", [(True, 4, 1.0), (False, 128, 1.0), (True, 4, 3.0),
+                                              (False, 128, 2.0)])
+def test_compress_error_bound_covers_the_kernel_arithmetic(overlap, m, zscale):
+    """compress_error_bound's gamma(2W + 32): 2W units for the W rescaling
+    multiply-adds and W products of a weight's path, plus 32 units for the
+    exponentials (exp(x) as 2^(x log2 e) carries about |x| units from the
+    rounded product, and along any weight's path the arguments of its exps sum
+    to at most twice the spread of the window's logits) and for the reciprocal
+    and reciprocal square root.  Checked against an emulation of the kernel's
+    float32 operation order with one-ulp hardware functions, at the workloads'
+    logit spread (gate logits N(0,1), bias N(0, 0.1^2)) and beyond it."""
+    r = rng(90 + m)
+    c = 256
+    n = 8 * m
+    C = r.standard_normal((n, c))
+    Z = r.standard_normal((n, c)) * zscale
+    P = r.standard_normal((2 * m if overlap else m, c)) * 0.1
+    C, Z, P = (a.astype(np.float32).astype(np.float64) for a in (C, Z, P))
+    exact = O.rmsnorm(O.compress(C, Z, P, m, overlap))
+    bound = O.compress_error_bound(C, Z, P, m, overlap)
+    for trial in range(3):
+        y = _pool_gpu_arith(C, Z, P, m, overlap, rng(trial))
+        err = np.abs(y - exact)
+        assert np.all(err <= bound), f"trial {trial}: worst err/bound {(err / bound).max():.3g}"
