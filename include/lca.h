@@ -396,6 +396,28 @@ int lca_decode_step(const lca_decode_layer* layer, const lca_decode_io* io, void
 int lca_decode_steps(const lca_decode_layer* layer, const lca_decode_io* io, int n_steps,
                      void* workspace, size_t workspace_bytes, lca_stream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * lca_decode_step_static -- lca_decode_step for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It takes no workspace: the step's scratch space is a
+ * device array of LCA_STATIC_SCRATCH_BYTES that the library owns, one copy per
+ * device, placed when the library's code object is loaded on that device and
+ * held until the process ends.  The call allocates nothing.  Same arguments,
+ * kernels and results as lca_decode_step; the caller still passes every
+ * input and output.
+ *   - Returns LCA_ERR_WORKSPACE, having enqueued nothing, when the layer needs
+ *     more scratch than that (lca_decode_workspace_size(layer) >
+ *     LCA_STATIC_SCRATCH_BYTES; 96 MiB holds a CSA layer of 16 sequences at
+ *     1M tokens, or any HCA layer of the workloads).
+ *   - Every call on a device shares that device's array, which keeps the last
+ *     call's contents; the step clears what it needs cleared.  Calls that
+ *     overlap on one device (unordered streams or host threads) race on the
+ *     array: the caller must order them.
+ * ------------------------------------------------------------------------- */
+#define LCA_STATIC_SCRATCH_BYTES ((size_t)96 << 20)
+int lca_decode_step_static(const lca_decode_layer* layer, const lca_decode_io* io,
+                           lca_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

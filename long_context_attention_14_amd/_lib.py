@@ -69,7 +69,9 @@ SIGNATURES = {
                                 P]),
     "lca_decode_steps": (c_int, [ctypes.POINTER(DecodeLayer), ctypes.POINTER(DecodeIO), c_int, P,
                                  c_size_t, P]),
+    "lca_decode_step_static": (c_int, [ctypes.POINTER(DecodeLayer), ctypes.POINTER(DecodeIO), P]),
 }
+LCA_STATIC_SCRATCH_BYTES = 96 << 20  # include/lca.h
 
 _LIB = None
 

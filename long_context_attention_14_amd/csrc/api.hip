@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstdarg>
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -384,16 +385,16 @@ size_t lca_decode_workspace_size(const lca_decode_layer* layer) {
 
 namespace {
 
-// Every check of one decode step, before anything is enqueued.
-int decode_check(const lca_decode_layer* L, const lca_decode_io* io, const void* workspace,
-                 size_t workspace_bytes) {
-  int st = check_layer(L);
+// The structs of one decode step.
+int decode_check_structs(const lca_decode_layer* L, const lca_decode_io* io) {
+  const int st = check_layer(L);
   if (st != LCA_OK) return st;
   REQUIRE(io != nullptr && io->struct_size == sizeof(lca_decode_io), "bad io struct");
-  const DecodeLayout d = decode_layout(L);
-  if (workspace == nullptr || workspace_bytes < d.total)
-    return fail(LCA_ERR_WORKSPACE, "lca_decode_step needs %zu workspace bytes, got %zu", d.total,
-                workspace ? workspace_bytes : 0);
+  return LCA_OK;
+}
+
+// The shapes, formats and tensors of one decode step (structs already checked).
+int decode_check_args(const lca_decode_layer* L, const lca_decode_io* io) {
   if (L->B == 0) return LCA_OK;
   const bool csa = L->mode == LCA_CSA;
   SUPPORT(c_ok(L->c) && L->c <= 512, "c = %d unsupported", L->c);
@@ -413,6 +414,18 @@ int decode_check(const lca_decode_layer* L, const lca_decode_io* io, const void*
   }
   REQUIRE(io->tokC && io->tokZ && io->q && io->out, "NULL io tensor");
   return LCA_OK;
+}
+
+// Every check of one decode step, before anything is enqueued.
+int decode_check(const lca_decode_layer* L, const lca_decode_io* io, const void* workspace,
+                 size_t workspace_bytes) {
+  const int st = decode_check_structs(L, io);
+  if (st != LCA_OK) return st;
+  const DecodeLayout d = decode_layout(L);
+  if (workspace == nullptr || workspace_bytes < d.total)
+    return fail(LCA_ERR_WORKSPACE, "lca_decode_step needs %zu workspace bytes, got %zu", d.total,
+                workspace ? workspace_bytes : 0);
+  return decode_check_args(L, io);
 }
 
 // The launches of one decode step (decode_check passed, B > 0).
@@ -527,6 +540,71 @@ int lca_decode_steps(const lca_decode_layer* L, const lca_decode_io* io, int n_s
     if (st != LCA_OK) return st;
   }
   return LCA_OK;
+}
+
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// lca_decode_step_static: the decode step's scratch space in a device array the
+// library owns, for callers that cannot allocate.  The array is a file-scope
+// __device__ variable: the loader gives every device that runs the library its
+// own copy, held until the process ends.  In host code its name is only a
+// host-side stand-in, so its device address is asked for once per device (with
+// that device current) and kept; kernels only ever see that address.
+
+static __device__ __align__(256) unsigned char scratch[LCA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxStaticDevices = 64;
+
+struct StaticScratch {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+
+StaticScratch g_static_scratch[kMaxStaticDevices];
+
+// The current device's copy of `scratch` (its address asked for on the first
+// call on that device; std::call_once makes concurrent first calls safe).
+int static_scratch_ptr(void** out) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "lca_decode_step_static/hipGetDevice");
+  if (dev < 0 || dev >= kMaxStaticDevices)
+    return fail(LCA_ERR_UNSUPPORTED, "lca_decode_step_static: device %d beyond the %d supported",
+                dev, kMaxStaticDevices);
+  StaticScratch& sc = g_static_scratch[dev];
+  std::call_once(sc.once, [&sc] {
+    sc.err = hipGetSymbolAddress(&sc.ptr, HIP_SYMBOL(scratch));
+    if (sc.err == hipSuccess && sc.ptr == nullptr) sc.err = hipErrorInvalidSymbol;
+  });
+  if (sc.err != hipSuccess) return hip_status(sc.err, "lca_decode_step_static/hipGetSymbolAddress");
+  *out = sc.ptr;
+  return LCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lca_decode_step_static(const lca_decode_layer* L, const lca_decode_io* io, lca_stream_t stream) {
+  g_last_error.clear();
+  int st = decode_check_structs(L, io);
+  if (st != LCA_OK) return st;
+  const size_t need = decode_layout(L).total;
+  if (need > LCA_STATIC_SCRATCH_BYTES)
+    return fail(LCA_ERR_WORKSPACE,
+                "lca_decode_step_static: this layer needs %zu scratch bytes, more than the %zu of the "
+                "library's static scratch (use lca_decode_step with a workspace)",
+                need, static_cast<size_t>(LCA_STATIC_SCRATCH_BYTES));
+  if ((st = decode_check_args(L, io)) != LCA_OK) return st;
+  if (L->B == 0) return LCA_OK;
+  void* ws = nullptr;
+  if ((st = static_scratch_ptr(&ws)) != LCA_OK) return st;
+  return decode_enqueue(L, io, ws, stream);
 }
 
 }  // extern "C"

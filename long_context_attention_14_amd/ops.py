@@ -302,3 +302,13 @@ def lca_decode_steps(layer: DecodeLayerState, steps, out_fmt, workspace=None, st
     return check("lca_decode_steps", lib().lca_decode_steps(
         ctypes.byref(layer.struct), arr, len(steps), _ptr(workspace, need, "workspace"), need,
         _stream(stream)))
+
+
+def lca_decode_step_static(layer: DecodeLayerState, tokC, tokZ, q, out, out_fmt, qI=None,
+                           qI_scale=None, w=None, lse=None, idx_out=None, stream=None,
+                           stage_events=None):
+    """lca_decode_step without a workspace: the step's scratch space is the
+    library's own per-device array (for callers that cannot allocate)."""
+    io = _decode_io(layer, tokC, tokZ, q, out, out_fmt, qI, qI_scale, w, lse, idx_out, stage_events)
+    return check("lca_decode_step_static", lib().lca_decode_step_static(
+        ctypes.byref(layer.struct), ctypes.byref(io), _stream(stream)))
