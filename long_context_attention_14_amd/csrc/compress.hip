@@ -8,10 +8,14 @@
 // the own block (m' tokens).  The entry is RMS-normalised (unit gain) and cast
 // to the cache format.
 //
-// Mapping: one 64-lane wavefront per entry; lane l owns channels
+// Mapping: one workgroup of kPoolWaves waves per entry; lane l owns channels
 // [l*CPL, (l+1)*CPL) with CPL = c/64, so every candidate row is one coalesced
-// c-wide load per wave; the softmax is computed online per channel in
-// registers and the RMSNorm sum of squares is a wavefront reduction.
+// c-wide load per wave.  Candidate slot j (time order) is pooled by wave
+// j % kPoolWaves with an online per-channel softmax in registers; the waves'
+// partial states are combined in slot order, then RMS-normalised (a wavefront
+// reduction).  The decode-time state append pools a completed block with the
+// same slot-to-wave split and combination order, so an entry made by decode
+// steps has the same bits as the entry the prefill compressor makes.
 #include "common.h"
 
 namespace lca {
@@ -58,6 +62,45 @@ __device__ __forceinline__ void pool_finish_norm(const Pool* p, int c, float eps
   for (int i = 0; i < CPL; ++i) out[i] *= r;
 }
 
+constexpr int kPoolWaves = 8;
+
+// The entry from the waves' partial pooling states: every wave stores its
+// state, then wave 0 combines them in slot order -- order[x] is the wave that
+// pooled the x-th slot group (a fixed order, so the result does not depend on
+// timing) -- and RMS-normalises.  Returns true in wave 0, whose `out` then
+// holds the entry.  Every wave of the workgroup must call it.
+template <int CPL>
+__device__ __forceinline__ bool pool_combine_norm(float (*part)[3][CPL][kWave], const Pool* pool,
+                                                  const int (&order)[kPoolWaves], int wv, int lane,
+                                                  int c, float eps, float* out) {
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    part[wv][0][j][lane] = pool[j].mx;
+    part[wv][1][j][lane] = pool[j].sum;
+    part[wv][2][j][lane] = pool[j].acc;
+  }
+  __syncthreads();
+  if (wv != 0) return false;
+  Pool tot[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < kPoolWaves; ++x) M = fmaxf(M, part[order[x]][0][j][lane]);
+    float sum = 0.f, acc = 0.f;
+#pragma unroll
+    for (int x = 0; x < kPoolWaves; ++x) {
+      const float mx = part[order[x]][0][j][lane];
+      const float f = mx == -INFINITY ? 0.f : __expf(mx - M);
+      sum += part[order[x]][1][j][lane] * f;
+      acc += part[order[x]][2][j][lane] * f;
+    }
+    tot[j] = {M, sum, acc};
+  }
+  pool_finish_norm<CPL>(tot, c, eps, out);
+  return true;
+}
+
 template <int CPL>
 __device__ __forceinline__ void load_bias(const float* P, int slot, int c, int lane, float* pv) {
   load_row<CPL>(P + static_cast<size_t>(slot) * c, LCA_F32, c, lane, pv);
@@ -66,58 +109,75 @@ __device__ __forceinline__ void load_bias(const float* P, int slot, int c, int l
 // IOF: the candidates' format (F32 or BF16) as a compile-time constant, so that
 // row loads carry no format branches (a load under a branch makes the compiler
 // wait for it at the branch's end, which serialises the candidate loads).
+// One workgroup per entry (grid = B * n_new / m); wave wv pools slots wv,
+// wv + kPoolWaves, ... in increasing order, loading kBatch slots' rows before
+// pooling any of them.
 template <int CPL, int IOF>
-__global__ __launch_bounds__(kWave * kWavesPerBlock) void compress_kernel(
+__global__ __launch_bounds__(kWave * kPoolWaves) void compress_kernel(
     int csa, int m, int B, int n_new, int c, const uint8_t* C, const uint8_t* Z,
     const uint8_t* prevC, const uint8_t* prevZ, const float* P, uint8_t* cache, int kv_fmt,
     int N_cap, int first_entry, float eps, double rope_step, KvPages pg) {
   constexpr int io_fmt = IOF;
+  constexpr int kBatch = CPL > 8 ? 1 : 4;
+  __shared__ float part[kPoolWaves][3][CPL][kWave];  // lane-contiguous: no bank conflicts
   const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x >> 6;
   const int n_ent = n_new / m;
-  const long long e = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-  if (e >= static_cast<long long>(B) * n_ent) return;
-  const int b = static_cast<int>(e / n_ent);
-  const int s = static_cast<int>(e % n_ent);
+  const int b = static_cast<int>(blockIdx.x / n_ent);
+  const int s = static_cast<int>(blockIdx.x % n_ent);
   // the entry's row in the cache (through the block table when paged), looked
   // up before the candidate loads
-  const long long out_row = kv_row_of(pg, b, N_cap, first_entry + s);
+  const long long out_row = wv == 0 ? kv_row_of(pg, b, N_cap, first_entry + s) : -1;
   const size_t io_row = row_bytes(io_fmt, c);
   const uint8_t* Cb = C + static_cast<size_t>(b) * n_new * io_row;
   const uint8_t* Zb = Z + static_cast<size_t>(b) * n_new * io_row;
-
+  const int W = csa ? 2 * m : m;
+  // CSA slots 0..m-1: the previous block (chunk rows of block s-1, prevC/prevZ
+  // for the chunk's first entry, absent without them); slots m..2m-1 and every
+  // HCA slot: the entry's own block
+  const bool have_prev = s > 0 || prevC != nullptr;
   Pool pool[CPL];
   pool_init<CPL>(pool);
-  float cv[CPL], zv[CPL], pv[CPL];
-  if (csa) {
-    // slots 0..m-1: previous block (absent for the first entry without prevC)
-    const bool have_prev = s > 0 || prevC != nullptr;
-    if (have_prev) {
-      for (int i = 0; i < m; ++i) {
-        const uint8_t* rc = s > 0 ? Cb + (static_cast<size_t>(s - 1) * m + i) * io_row
-                                  : prevC + (static_cast<size_t>(b) * m + i) * io_row;
-        const uint8_t* rz = s > 0 ? Zb + (static_cast<size_t>(s - 1) * m + i) * io_row
-                                  : prevZ + (static_cast<size_t>(b) * m + i) * io_row;
-        load_row<CPL>(rc, io_fmt, c, lane, cv);
-        load_row<CPL>(rz, io_fmt, c, lane, zv);
-        load_bias<CPL>(P, i, c, lane, pv);
+  for (int j0 = wv; j0 < W; j0 += kPoolWaves * kBatch) {
+    float bc[kBatch][CPL], bz[kBatch][CPL], bb[kBatch][CPL];
+    bool use[kBatch];
+    // unconditional loads (a slot past W reads slot j0's rows and is not used)
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) zv[j] += pv[j];
-        pool_add<CPL>(pool, cv, zv);
+    for (int u = 0; u < kBatch; ++u) {
+      const int j = j0 + kPoolWaves * u;
+      const int jl = j < W ? j : j0;
+      const bool prev = csa && jl < m;
+      const uint8_t* rc;
+      const uint8_t* rz;
+      if (prev && s == 0 && prevC != nullptr) {
+        rc = prevC + (static_cast<size_t>(b) * m + jl) * io_row;
+        rz = prevZ + (static_cast<size_t>(b) * m + jl) * io_row;
+      } else {
+        // previous block: row (s-1)*m + jl (row s*m when absent: loaded, unused)
+        const size_t r = prev ? (s > 0 ? static_cast<size_t>(s - 1) * m + jl : static_cast<size_t>(s) * m)
+                              : static_cast<size_t>(s) * m + (csa ? jl - m : jl);
+        rc = Cb + r * io_row;
+        rz = Zb + r * io_row;
       }
+      use[u] = j < W && (!prev || have_prev);
+      load_row<CPL>(rc, io_fmt, c, lane, bc[u]);
+      load_row<CPL>(rz, io_fmt, c, lane, bz[u]);
+      load_bias<CPL>(P, jl, c, lane, bb[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (!use[u]) continue;  // the same for the whole wave
+      float zv[CPL];
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) zv[i] = bz[u][i] + bb[u][i];
+      pool_add<CPL>(pool, bc[u], zv);
     }
   }
-  const int slot0 = csa ? m : 0;
-  for (int i = 0; i < m; ++i) {
-    const size_t r = static_cast<size_t>(s) * m + i;
-    load_row<CPL>(Cb + r * io_row, io_fmt, c, lane, cv);
-    load_row<CPL>(Zb + r * io_row, io_fmt, c, lane, zv);
-    load_bias<CPL>(P, slot0 + i, c, lane, pv);
+  int order[kPoolWaves];
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) zv[j] += pv[j];
-    pool_add<CPL>(pool, cv, zv);
-  }
+  for (int x = 0; x < kPoolWaves; ++x) order[x] = x;
   float out[CPL];
-  pool_finish_norm<CPL>(pool, c, eps, out);
+  if (!pool_combine_norm<CPL>(part, pool, order, wv, lane, c, eps, out)) return;
   // RoPE position of an entry: the last token it covers
   if (rope_step != 0.0)
     rope_lane<CPL>(out, lane, c,
@@ -150,13 +210,14 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void rmsnorm_rows_kernel(
 }
 
 // One workgroup of kAppendWaves waves per sequence: append the token, and
-// compress its block when the token completes it.  The block's candidates are
-// spread over the waves (candidate j goes to wave j % kAppendWaves), each wave
-// keeping an online per-channel softmax; the partial states are combined in
-// wave order through LDS, so the result does not depend on timing.  Tail rows
-// other than the new token were written by earlier steps; the new token's row is
-// used from registers.  As a side job the workgroups clear zero_buf.
-constexpr int kAppendWaves = 8;
+// compress its block when the token completes it.  The block's candidate slots
+// are pooled as in compress_kernel (slot j by one wave, each wave an online
+// per-channel softmax over its slots in increasing order, the partial states
+// combined in slot order through LDS), so the entry has the bits the prefill
+// compressor gives it and does not depend on timing.  Tail rows other than the
+// new token were written by earlier steps; the new token's row is used from
+// registers.  As a side job the workgroups clear zero_buf.
+constexpr int kAppendWaves = kPoolWaves;
 
 template <int CPL, int IOF>
 __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
@@ -228,106 +289,68 @@ __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
   }
   if ((p + 1) % m != 0) return;
 
-  // candidates, by physical tail row r: CSA rows of the current half are slots
-  // m..2m-1 (own block), the other half slots 0..m-1 (previous block, absent
-  // for the first entry); HCA row r is slot r.  The new token's row is taken
-  // from registers.
+  // candidate slots: CSA slot j < m is the previous block's token j (tail row
+  // (1-half)*m + j, absent for the first entry), slot m + j the own block's
+  // token j (row half*m + j); HCA slot j is row j.  The new token's row is
+  // taken from registers.
   const int s = (p + 1) / m - 1;
   // the new entry's row in the cache (through the block table when paged),
   // looked up before the candidate loads; -1: beyond N_cap or an absent page
   const long long out_row = (wv == 0 && s < N_cap) ? kv_row_of(pg, b, N_cap, s) : -1;
   Pool pool[CPL];
   pool_init<CPL>(pool);
-  float cv[CPL], zv[CPL], pv[CPL];
-  auto add_row = [&](int r, const float* rc, const float* rz, const float* bias) {
+  auto add_row = [&](const float* rc, const float* rz, const float* bias) {
+    float zv[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) zv[j] = rz[j] + bias[j];
     pool_add<CPL>(pool, rc, zv);
   };
+  int order[kPoolWaves];  // order[x]: the wave that pooled slot group x
   if (spec) {
+    // wave wv holds tail row wv (loaded before the count was known): its slot
+    // is m + wv % m in the own half, wv % m in the other
     if (wv < T_cap) {
       const bool own = (wv / m) == half;
-      if (own || s > 0) {
-        const float* rc = wv == row ? tc : sc;
-        const float* rz = wv == row ? tz : sz;
-        add_row(wv, rc, rz, own ? sp1 : sp0);
-      }
+      if (own || s > 0) add_row(wv == row ? tc : sc, wv == row ? tz : sz, own ? sp1 : sp0);
     }
-  } else if (CPL > 8) {
-    for (int r = wv; r < T_cap; r += kAppendWaves) {
-      const bool own = !csa || (r / m) == half;
-      if (!own && s == 0) continue;
-      const int slot = csa ? (own ? m + r % m : r % m) : r;
-      if (r == row) {
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          cv[j] = tc[j];
-          pv[j] = tz[j];
-        }
-      } else {
-        load_row<CPL>(tCb + r * io_row, io_fmt, c, lane, cv);
-        load_row<CPL>(tZb + r * io_row, io_fmt, c, lane, pv);
-      }
-      float bias[CPL];
-      load_bias<CPL>(P, slot, c, lane, bias);
-      add_row(r, cv, pv, bias);
-    }
+    for (int x = 0; x < kPoolWaves; ++x)
+      order[x] = x < T_cap ? (x < m ? (1 - half) * m + x : half * m + (x - m)) : x;
   } else {
-    // rows r = wv + kAppendWaves * i, kAppendBatch of them loaded before any is
-    // pooled, so a long HCA tail pays one memory latency per batch
-    constexpr int kAppendBatch = 4;
-    for (int r0 = wv; r0 < T_cap; r0 += kAppendWaves * kAppendBatch) {
+    // wave wv pools slots wv, wv + kAppendWaves, ... in increasing order,
+    // kAppendBatch slots' rows loaded before any is pooled, so a long HCA tail
+    // pays one memory latency per batch
+    constexpr int kAppendBatch = CPL > 8 ? 1 : 4;
+    for (int j0 = wv; j0 < T_cap; j0 += kAppendWaves * kAppendBatch) {
       float bc[kAppendBatch][CPL], bz[kAppendBatch][CPL], bb[kAppendBatch][CPL];
-      bool use[kAppendBatch];
-      // unconditional loads (rows past the tail read row 0 and are not used): a
-      // load under a branch would be waited for at the branch's end
+      bool use[kAppendBatch], mine[kAppendBatch];
+      // unconditional loads (slots past the tail read slot j0's rows and are
+      // not used): a load under a branch would be waited for at the branch's end
 #pragma unroll
       for (int u = 0; u < kAppendBatch; ++u) {
-        const int r = r0 + kAppendWaves * u;
-        const int rl = r < T_cap ? r : 0;
-        const bool own = !csa || (rl / m) == half;
-        use[u] = r < T_cap && (own || s > 0);
-        const int slot = csa ? (own ? m + rl % m : rl % m) : rl;
-        load_row<CPL>(tCb + rl * io_row, io_fmt, c, lane, bc[u]);
-        load_row<CPL>(tZb + rl * io_row, io_fmt, c, lane, bz[u]);
-        load_bias<CPL>(P, slot, c, lane, bb[u]);
+        const int j = j0 + kAppendWaves * u;
+        const int jl = j < T_cap ? j : j0;
+        const bool prev = csa && jl < m;
+        const int r = csa ? (prev ? (1 - half) * m + jl : half * m + (jl - m)) : jl;
+        use[u] = j < T_cap && (!prev || s > 0);
+        mine[u] = r == row;
+        load_row<CPL>(tCb + r * io_row, io_fmt, c, lane, bc[u]);
+        load_row<CPL>(tZb + r * io_row, io_fmt, c, lane, bz[u]);
+        load_bias<CPL>(P, jl, c, lane, bb[u]);
       }
 #pragma unroll
       for (int u = 0; u < kAppendBatch; ++u) {
-        const int r = r0 + kAppendWaves * u;
         if (!use[u]) continue;  // the same for the whole wave
         // the new token's row may not have reached memory yet: take it from registers
-        if (r == row) add_row(r, tc, tz, bb[u]);
-        else add_row(r, bc[u], bz[u], bb[u]);
+        if (mine[u]) add_row(tc, tz, bb[u]);
+        else add_row(bc[u], bz[u], bb[u]);
       }
     }
-  }
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    part[wv][0][j][lane] = pool[j].mx;
-    part[wv][1][j][lane] = pool[j].sum;
-    part[wv][2][j][lane] = pool[j].acc;
-  }
-  __syncthreads();
-  if (wv != 0) return;
-  Pool tot[CPL];
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int x = 0; x < kAppendWaves; ++x) M = fmaxf(M, part[x][0][j][lane]);
-    float sum = 0.f, acc = 0.f;
-#pragma unroll
-    for (int x = 0; x < kAppendWaves; ++x) {
-      const float mx = part[x][0][j][lane];
-      const float f = mx == -INFINITY ? 0.f : __expf(mx - M);
-      sum += part[x][1][j][lane] * f;
-      acc += part[x][2][j][lane] * f;
-    }
-    tot[j] = {M, sum, acc};
+    for (int x = 0; x < kPoolWaves; ++x) order[x] = x;
   }
   float out[CPL];
-  pool_finish_norm<CPL>(tot, c, eps, out);
+  if (!pool_combine_norm<CPL>(part, pool, order, wv, lane, c, eps, out)) return;
   if (rope_step != 0.0) rope_lane<CPL>(out, lane, c, rope_p);  // the entry's last token is p
   if (out_row >= 0) store_row<CPL>(cache + static_cast<size_t>(out_row) * kv_row, kv_fmt, c, lane, out);
 }
@@ -355,14 +378,15 @@ hipError_t launch_compress(int mode, int m, int B, int n_new, int c, const void*
                            double rope_step, const KvPages& pg, hipStream_t s) {
   const long long n = static_cast<long long>(B) * (n_new / m);
   if (n == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((n + kWavesPerBlock - 1) / kWavesPerBlock));
+  if (n > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(n));  // one workgroup per entry
   const int csa = mode == LCA_CSA ? 1 : 0;
   const uint8_t* Cp = static_cast<const uint8_t*>(C);
   const uint8_t* Zp = static_cast<const uint8_t*>(Z);
   const uint8_t* pC = static_cast<const uint8_t*>(prevC);
   const uint8_t* pZ = static_cast<const uint8_t*>(prevZ);
   uint8_t* ch = static_cast<uint8_t*>(cache);
-  const dim3 block(kWave * kWavesPerBlock);
+  const dim3 block(kWave * kPoolWaves);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, block, 0, s, csa, m, B, n_new, c, Cp, Zp, pC, pZ, P, ch, kv_fmt,
                        N_cap, first_entry, eps, rope_step, pg);

@@ -1012,3 +1012,168 @@ def test_grouped_out_proj(nt, n_h, c, g, d_g, d, out_fmt):
 def test_grouped_out_proj_prefill_full_size_sampled():
     say("grouped out proj T=8192 at the V4-Pro shape, sampled rows")
     _check_out_proj(8192, 64, 512, 8, 1024, 7168, "bf16", rows=[0, 1, 127, 128, 4095, 8190, 8191])
+
+
+# ---------------------------------------------------------------------------
+# GPU decode path == GPU prefill path, and a saved decode state resumes to the
+# same bits ("DeepSeek V4 Architecture Tricks", section "Heterogeneous KV Cache
+# Layout": the state cache holds the window KV and the tail tokens)
+
+
+def _prefill_and_decode(mode, rope, seed=31):
+    """n tokens of a layer run two ways on the GPU: one prefill call chain from
+    position 0 (lca_compress, lca_rmsnorm_rows, lca_indexer_scores, lca_topk,
+    lca_sparse_mqa) and n lca_decode_step calls from an empty state.  Returns both
+    results plus the decode state's tensors and the per-step inputs."""
+    csa = mode == "csa"
+    m = 4 if csa else 8
+    B, n, c, H, HI, dI, n_win, k = 2, 640 if csa else 256, 512, 64, 64, 128, 128, 32
+    N_cap = n // m
+    tau, eps = c ** -0.5, 1e-6
+    rng = np.random.default_rng(seed)
+    enc16 = lambda a: enc.encode(a, "bf16")  # noqa: E731
+    C, Z = enc16(rng.standard_normal((B, n, c))), enc16(rng.standard_normal((B, n, c)))
+    P = (rng.standard_normal((2 * m if csa else m, c)) * 0.1).astype(np.float32)
+    q = enc16(rng.standard_normal((B, n, H, c)))
+    qI = enc.encode(rng.standard_normal((B, n, HI, dI)), "fp8")
+    kI = enc.encode(rng.standard_normal((B, N_cap, dI)), "fp8")
+    w = rng.random((B, n, HI)).astype(np.float32)
+    rb = ops.row_bytes("bf16", c)
+    # prefill
+    cache_p = torch.zeros(B * N_cap * rb, dtype=torch.uint8, device=DEV)
+    ops.lca_compress(mode, m, B, n, c, T(C), T(Z), "bf16", None, None, T(P), cache_p, "bf16", N_cap, 0,
+                     eps, rope)
+    win_p = torch.zeros(B * n * rb, dtype=torch.uint8, device=DEV)
+    ops.lca_rmsnorm_rows(B, n, c, T(C), "bf16", win_p, "bf16", n, eps, 0, rope)
+    q_pos = T(np.tile(np.arange(n, dtype=np.int32), (B, 1)))
+    n_ent = T(np.full(B, N_cap, np.int32))
+    idx_p = None
+    if csa:
+        scores = torch.empty((B, n, N_cap), dtype=torch.float32, device=DEV)
+        ops.lca_indexer_scores(B, n, HI, dI, "fp8", T(qI), None, T(kI), None, N_cap, T(w), q_pos, m,
+                               n_ent, scores)
+        idx_p = torch.empty((B, n, k), dtype=torch.int32, device=DEV)
+        ops.lca_topk(B, n, N_cap, scores, q_pos, m, n_ent, k, idx_p)
+    out_p = torch.empty((B, n, H, c), dtype=torch.bfloat16, device=DEV)
+    lse_p = torch.empty((B, n, H), dtype=torch.float32, device=DEV)
+    ops.lca_sparse_mqa(B, n, H, c, T(q), "bf16", cache_p, "bf16", N_cap, idx_p, k if csa else 0, q_pos, m,
+                       n_ent, win_p, n, 0, n_win, tau, eps, None, rope, out_p, "bf16", lse=lse_p)
+    # decode from an empty state, one token per step
+    T_rows = 2 * m if csa else m
+    st = {"tailC": torch.zeros(B * T_rows * c, dtype=torch.int16, device=DEV),
+          "tailZ": torch.zeros(B * T_rows * c, dtype=torch.int16, device=DEV),
+          "ring": torch.zeros(B * n_win * rb, dtype=torch.uint8, device=DEV),
+          "cache": torch.zeros(B * N_cap * rb, dtype=torch.uint8, device=DEV),
+          "n_tokens": torch.zeros(B, dtype=torch.int32, device=DEV)}
+    Pd, kId = T(P), T(kI)
+    lay = ops.DecodeLayerState(mode=mode, m=m, B=B, c=c, H=H, n_win=n_win, N_cap=N_cap, io_fmt="bf16",
+                               kv_fmt="bf16", tailC=st["tailC"], tailZ=st["tailZ"], ring=st["ring"],
+                               cache=st["cache"], n_tokens=st["n_tokens"], P=Pd, tau=tau, eps=eps, k=k,
+                               H_I=HI, d_I=dI, idx_fmt="fp8", kI=kId, rope_base=rope)
+    steps = {"tokC": T(np.ascontiguousarray(C.transpose(1, 0, 2))),
+             "tokZ": T(np.ascontiguousarray(Z.transpose(1, 0, 2))),
+             "q": T(np.ascontiguousarray(q.transpose(1, 0, 2, 3))),
+             "qI": T(np.ascontiguousarray(qI.transpose(1, 0, 2, 3))),
+             "w": T(np.ascontiguousarray(w.transpose(1, 0, 2)))}
+    dec = {"out": torch.empty((n, B, H, c), dtype=torch.bfloat16, device=DEV),
+           "lse": torch.empty((n, B, H), dtype=torch.float32, device=DEV),
+           "idx": torch.empty((n, B, k), dtype=torch.int32, device=DEV)}
+    ws = torch.empty(lay.workspace_size(), dtype=torch.uint8, device=DEV)
+
+    def step(t):
+        ops.lca_decode_step(lay, steps["tokC"][t], steps["tokZ"][t], steps["q"][t], dec["out"][t], "bf16",
+                            qI=steps["qI"][t] if csa else None, w=steps["w"][t] if csa else None,
+                            lse=dec["lse"][t], idx_out=dec["idx"][t] if csa else None, workspace=ws)
+
+    return dict(B=B, n=n, m=m, c=c, k=k, n_win=n_win, N_cap=N_cap, rb=rb, csa=csa, cache_p=cache_p,
+                C=C, Z=Z, P=P, q=q, qI=qI, kI=kI, w=w,
+                win_p=win_p, idx_p=idx_p, out_p=out_p, lse_p=lse_p, st=st, dec=dec, step=step)
+
+
+@pytest.mark.parametrize("mode,rope", [("csa", 0.0), ("csa", 10000.0), ("hca", 0.0)])
+def test_gpu_decode_from_empty_equals_gpu_prefill(mode, rope):
+    """n decode steps from an empty state against one prefill of the same n
+    tokens, both on the GPU.  Bit for bit: every compressed entry (the decode
+    append pools a completed block with the prefill compressor's slot split and
+    combination order), the window rows left in the ring, and every step's
+    selection (both indexer kernels score with the same MFMA tiles and reduction
+    order, and both selections are exact).  The outputs agree within the bf16
+    output tolerance, with each other and with the oracle on sampled positions,
+    rather than bit for bit: the decode step splits a query's candidate rows
+    over several workgroups merged by log-sum-exp, the prefill call runs each
+    query row in one workgroup, so the probabilities are rounded against
+    different running maxima and the float32 sums are ordered differently (each
+    path is deterministic)."""
+    r = _prefill_and_decode(mode, rope)
+    say(f"GPU decode == GPU prefill: {mode} rope={rope} n={r['n']}")
+    for t in range(r["n"]):
+        r["step"](t)
+    torch.cuda.synchronize()
+    B, n, N_cap, rb, n_win = r["B"], r["n"], r["N_cap"], r["rb"], r["n_win"]
+    cp = host(r["cache_p"]).reshape(B, N_cap, rb)
+    cd = host(r["st"]["cache"]).reshape(B, N_cap, rb)
+    assert np.array_equal(cd, cp), f"entries differ in {(cd != cp).any(-1).sum()} rows"
+    wp = host(r["win_p"]).reshape(B, n, rb)
+    ring = host(r["st"]["ring"]).reshape(B, n_win, rb)
+    for pos in range(n - n_win, n):
+        assert np.array_equal(ring[:, pos % n_win], wp[:, pos]), f"window row {pos}"
+    assert np.array_equal(host(r["st"]["n_tokens"]), np.full(B, n))
+    if r["csa"]:
+        idx_d = host(r["dec"]["idx"]).transpose(1, 0, 2)
+        assert np.array_equal(idx_d, host(r["idx_p"])), "selections differ"
+    od = out_f64(r["dec"]["out"]).transpose(1, 0, 2, 3)
+    op = out_f64(r["out_p"])
+    err = np.abs(od - op).max()
+    # the probabilities go to the PV product as bf16, rounded against each
+    # workgroup's own running maximum, so the two paths differ by more than a
+    # rounding of the same float32 value: each is held to the oracle's
+    # tolerance, and so is their difference
+    assert err <= OUT_TOL["bf16"], f"decode vs prefill out err {err:.3g}"
+    qs = np.array([0, 1, 3, 4, 127, 128, r["n"] // 2 + 3, r["n"] - 1])
+    ref = O.prefill_layer(mode=mode, m=r["m"], k=r["k"], n_win=n_win, tau=r["c"] ** -0.5, eps=1e-6,
+                          kv_fmt="bf16", out_fmt="bf16", pos0=0, C=O.decode(r["C"][0], "bf16"),
+                          Z=O.decode(r["Z"][0], "bf16"), P=r["P"], q=O.decode(r["q"][0], "bf16"),
+                          cache_prefix=np.zeros((0, r["c"])), qI=O.decode(r["qI"][0], "fp8"),
+                          kI=O.decode(r["kI"][0], "fp8"), w=r["w"][0], queries=qs,
+                          idx_given=host(r["idx_p"])[0, qs] if r["csa"] else None, rope_base=rope)
+    for name, o in (("decode", od[0, qs]), ("prefill", op[0, qs])):
+        e = np.abs(o - ref["out"]).max()
+        assert e <= OUT_TOL["bf16"], f"{name} vs oracle: {e:.3g}"
+    lerr = np.abs(host(r["dec"]["lse"]).transpose(1, 0, 2) - host(r["lse_p"])).max()
+    assert lerr <= LSE_TOL["bf16"], f"lse err {lerr:.3g}"
+    say(f"  outputs: max |decode - prefill| = {err:.3g}, lse {lerr:.3g}")
+
+
+@pytest.mark.parametrize("mode", ["csa", "hca"])
+def test_decode_state_save_restore_resume(mode):
+    """The decode state (tail rows, window ring, compressed cache, token counts)
+    copied to host memory after some steps and written back later resumes to
+    the same bits: the steps after the restore repeat the outputs, selections
+    and final state of the steps first run after the save."""
+    r = _prefill_and_decode(mode, 0.0, seed=47)
+    n, n1 = r["n"], r["n"] // 2 + 3
+    say(f"save / restore / resume: {mode}, save after {n1} of {n} steps")
+    for t in range(n1):
+        r["step"](t)
+    torch.cuda.synchronize()
+    saved = {name: v.cpu().clone() for name, v in r["st"].items()}
+    for t in range(n1, n):
+        r["step"](t)
+    torch.cuda.synchronize()
+    bits = lambda v: host(v.view(torch.int16) if v.dtype == torch.bfloat16 else v)  # noqa: E731
+    first = {name: bits(v)[n1:].copy() for name, v in r["dec"].items()}
+    end1 = {name: bits(v).copy() for name, v in r["st"].items()}
+    for v in r["dec"].values():
+        v.zero_()
+    for name, v in r["st"].items():
+        v.fill_(0x3 if v.dtype != torch.int32 else -5)   # scribble, then restore
+        v.copy_(saved[name].to(DEV))
+    for t in range(n1, n):
+        r["step"](t)
+    torch.cuda.synchronize()
+    for name, v in r["dec"].items():
+        if name == "idx" and not r["csa"]:
+            continue
+        assert np.array_equal(bits(v)[n1:], first[name]), f"{name} differs after the restore"
+    for name, v in r["st"].items():
+        assert np.array_equal(bits(v), end1[name]), f"state {name} differs after the restore"
