@@ -7,7 +7,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liblca.so")
+# LCA_LIB names another build of the same library (the CPU-only host-sanitizer
+# build used by the tests); by default the in-tree liblca.so.
+LIB_PATH = os.environ.get("LCA_LIB") or os.path.join(HERE, "liblca.so")
 
 LCA_OK, LCA_ERR_INVALID_ARG, LCA_ERR_UNSUPPORTED, LCA_ERR_WORKSPACE, LCA_ERR_HIP = 0, -1, -2, -3, -4
 FMT = {"f32": 0, "bf16": 1, "fp8": 2, "mxfp4": 3, "fp8_bf16rope": 4}

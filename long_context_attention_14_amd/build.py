@@ -35,13 +35,25 @@ EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "indexer.hip": ["-fno-honor-nans"]}
 
 
+# The host-sanitizer variant (CPU checks only): the host half of every source is
+# built with AddressSanitizer and UndefinedBehaviorSanitizer (errors fatal);
+# device code is built as usual.  Its library is loaded only by the CPU test
+# that runs the C ABI's validation paths under the sanitizers, with the
+# sanitizer runtime preloaded; nothing on a GPU loads it.
+SAN_BUILD = os.path.join(HERE, "_build_san")
+SAN_LIB = os.path.join(SAN_BUILD, "liblca_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address,undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
+def _compile(src, out_dir=BUILD, extra=()):
+    obj = os.path.join(out_dir, os.path.basename(src)[:-4] + ".o")
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -49,22 +61,38 @@ def _compile(src):
     return obj, warn
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    out_dir, lib = (SAN_BUILD, SAN_LIB) if sanitize else (BUILD, LIB)
+    extra = SAN_FLAGS if sanitize else []
+    os.makedirs(out_dir, exist_ok=True)
     with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
-        results = list(ex.map(_compile, sources()))
+        results = list(ex.map(lambda src: _compile(src, out_dir, extra), sources()))
     for _, warn in results:
         if verbose and warn.strip():
             print(warn, file=sys.stderr)
     objs = [o for o, _ in results]
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def sanitizer_runtime() -> str:
+    """The ASan runtime of the compiler that built the sanitized library (it also
+    carries the UBSan handlers), for LD_PRELOAD into an uninstrumented Python."""
+    import glob
+    root = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    hits = sorted(glob.glob(os.path.join(root, "llvm", "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")) +
+                  glob.glob(os.path.join(root, "lib", "llvm", "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise RuntimeError("no libclang_rt.asan-x86_64.so next to hipcc")
+    return hits[-1]
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv))
