@@ -406,7 +406,7 @@ def run_out_proj(args):
     W_o = up(enc.to_bf16_bits(rng.standard_normal((d, g * d_g), dtype=np.float32) / np.sqrt(g * d_g)))
     z = torch.empty((T, g * d_g), dtype=torch.int16, device=dev)
     out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(max(1, ops.lca_grouped_out_proj_workspace_size(T, n_h, c, g, d_g, d)),
+    ws = torch.empty(max(1, ops.grouped_out_proj_workspace_size(T, n_h, c, g, d_g, d)),
                      dtype=torch.uint8, device=dev)
     call = lambda: ops.lca_grouped_out_proj(T, n_h, c, g, d_g, d, o, W_g, W_o, z, out, "bf16", ws)  # noqa: E731
     _calibrate_copy(args.calibrate_copy, dev)

@@ -19,12 +19,21 @@
  *   - queries and KV are RMS-normalised before attention.
  *
  * Conventions shared by every call
+ *   - Every entry point takes a pointer to a versioned argument struct whose
+ *     first field, struct_size, must equal sizeof() of that struct in this
+ *     header (a caller built against another layout is rejected with
+ *     LCA_ERR_INVALID_ARG, never misread), plus the stream.  Appending fields
+ *     in a later version changes sizeof() and so cannot be confused with an
+ *     older caller's struct.
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
  *     never allocates or frees device memory and keeps no pointer after a
  *     call returns.  Scratch space is a caller-provided device workspace whose
- *     size the matching *_workspace_size call returns.
- *   - Tensors are dense and row-major in the shapes given; the innermost
- *     dimension is contiguous.  Every pointer must be 16-byte aligned.
+ *     size lca_workspace_size() returns for the same arguments
+ *     (lca_decode_step_static is the one exception: see there).
+ *   - Tensors are dense and row-major in the shapes given, with no element
+ *     strides: the kernels derive every address from the shape, and the
+ *     innermost dimension is read in 16-byte pieces.  Every pointer must be
+ *     16-byte aligned.  A strided view is made contiguous by the caller.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *     default stream).  No call synchronises the host.
  *   - Arguments are validated on the host before any HIP call; a call that
@@ -32,8 +41,16 @@
  *     LCA_ERR_HIP.  lca_last_error() gives a per-thread message for the last
  *     failing call.  No call aborts, prints or throws.
  *   - Results are deterministic: the same inputs give bitwise-identical
- *     outputs, independent of the other sequences in the batch.
- *
+ *     outputs.  A sequence's outputs do not depend on the other sequences'
+ *     data; its selection does not depend on the batch at all, while its
+ *     attention output can change in the last bits when the batch size moves
+ *     the attention into another split plan (the plan follows the number of
+ *     query rows; see lca_sparse_mqa).
+ *   - The library keeps no mutable state of its own besides, per device and
+ *     kernel, a once-only record that a kernel's LDS limit was raised and the
+ *     address of lca_decode_step_static's scratch array (both set under
+ *     std::call_once, so first calls from several host threads are safe).
+
  * Stored formats (enum lca_dtype)
  *   LCA_F32              IEEE float32.
  *   LCA_BF16             bfloat16 (upper half of float32), round to nearest even.
@@ -76,17 +93,17 @@
 extern "C" {
 #endif
 
-#define LCA_ABI_VERSION 3
+#define LCA_ABI_VERSION 4
 
 /* A hipStream_t. */
 typedef struct ihipStream_t* lca_stream_t;
 
 enum lca_status {
   LCA_OK = 0,
-  LCA_ERR_INVALID_ARG = -1, /* a NULL pointer, bad size, shape or enum value      */
-  LCA_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype/shape combination) */
-  LCA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required          */
-  LCA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed          */
+  LCA_ERR_INVALID_ARG = -1, /* a NULL pointer, bad size, shape, enum value or struct_size */
+  LCA_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype/shape combination)        */
+  LCA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required                 */
+  LCA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed                 */
 };
 
 enum lca_dtype {
@@ -102,19 +119,26 @@ enum lca_mode {
   LCA_HCA = 1  /* heavily compressed attention: disjoint m'-token blocks, dense */
 };
 
+/* Operations with a workspace, for lca_workspace_size. */
+enum lca_op {
+  LCA_OP_TOPK = 1,           /* args: const lca_topk_args*            */
+  LCA_OP_SPARSE_MQA = 2,     /* args: const lca_sparse_mqa_args*      */
+  LCA_OP_GROUPED_OUT_PROJ = 3, /* args: const lca_grouped_out_proj_args* */
+  LCA_OP_DECODE_STEP = 4     /* args: const lca_decode_layer*         */
+};
+
 /* Paged compressed-KV cache ("DeepSeek V4 Architecture Tricks", section
  * "Heterogeneous KV Cache Layout": the classical cache of compressed entries is
  * kept in blocks of lcm(m, m') = 128 tokens, so that CSA and HCA layers share
  * one block table).  With pages, a cache argument is a pool of n_pages pages of
  * epp = page_tokens / m entries each ([n_pages, epp, row]); entry e of
  * sequence b lives in page block_table[b * max_pages + e / epp], row e % epp.
- * The indexer keys are not paged (they stay [B, N_cap, d_I]).  A NULL
- * lca_kv_pages pointer (or block_table == NULL in lca_decode_layer) means the
- * contiguous [B, N_cap, row] layout.  Requirements: page_tokens % m == 0,
- * N_cap <= max_pages * epp.  The table is device memory the library cannot
- * inspect on the host: an entry whose page id is outside [0, n_pages) is
- * treated as absent (never read, never written), so a bad table cannot make a
- * kernel touch memory outside the pool. */
+ * The indexer keys are not paged (they stay [B, N_cap, d_I]).  block_table ==
+ * NULL means the contiguous [B, N_cap, row] layout.  Requirements:
+ * page_tokens % m == 0, N_cap <= max_pages * epp.  The table is device memory
+ * the library cannot inspect on the host: an entry whose page id is outside
+ * [0, n_pages) is treated as absent (never read, never written), so a bad
+ * table cannot make a kernel touch memory outside the pool. */
 typedef struct lca_kv_pages {
   const int32_t* block_table; /* [B, max_pages] int32 device: physical page of logical page j */
   int max_pages;              /* logical pages per sequence (row stride of block_table) */
@@ -136,6 +160,15 @@ const char* lca_last_error(void);
 size_t lca_kv_row_bytes(int kv_dtype, int c);
 
 /* ---------------------------------------------------------------------------
+ * lca_workspace_size -- *bytes = the workspace that operation `op` (enum
+ * lca_op) needs for these arguments (0: none).  The args struct is validated
+ * as by the operation itself, except for its tensor pointers and workspace
+ * fields; an invalid one returns its error status and leaves *bytes at 0.
+ * Operations not in lca_op need no workspace.
+ * ------------------------------------------------------------------------- */
+int lca_workspace_size(int op, const void* args, size_t* bytes);
+
+/* ---------------------------------------------------------------------------
  * lca_compress -- the KV compressor on a prefill chunk.
  * "DeepSeek V4 Architecture Tricks", section "压缩 KV 的具体 trick": KV
  * candidates and compression weights come from the hidden states; weights
@@ -149,98 +182,107 @@ size_t lca_kv_row_bytes(int kv_dtype, int c);
  * block is prevC/prevZ, or absent (masked) when those are NULL); HCA -- the m
  * tokens of block s (slots 0 .. m-1).  The stored entry is
  * cast(E / sqrt(mean(E^2) + eps)) (unit-gain RMSNorm, QbitAI article, hybrid
- * attention section), written to cache[b, first_entry + s].
- *
- *   mode         LCA_CSA or LCA_HCA
- *   m            tokens per entry (>= 1); n_new % m == 0
- *   B, n_new, c  sequences, new tokens per sequence, channels (c % 64 == 0, c <= 1024)
- *   C, Z         [B, n_new, c] candidates / gate logits, format io_dtype (F32|BF16)
- *   prevC,prevZ  [B, m, c] previous block (CSA only) or both NULL
- *   P            [2m, c] (CSA) or [m, c] (HCA) float32 positional bias
- *   cache        [B, N_cap, row] stored entries, format kv_dtype; rows
- *                first_entry .. first_entry + n_new/m - 1 are written
- *   N_cap        rows per sequence in cache; first_entry + n_new/m <= N_cap
- *   eps          RMSNorm epsilon
- *   rope_base    partial RoPE base (0 = off): the normalised entry
- *                first_entry + s is turned at position (first_entry+s+1)*m - 1
- *   pages        NULL, or the paged layout of cache (see lca_kv_pages)
+ * attention section), written to cache[b, first_entry + s].  Entries have the
+ * bits lca_state_append gives an entry it compresses from the same tokens.
  * ------------------------------------------------------------------------- */
-int lca_compress(int mode, int m, int B, int n_new, int c, const void* C, const void* Z,
-                 int io_dtype, const void* prevC, const void* prevZ, const float* P,
-                 void* cache, int kv_dtype, int N_cap, int first_entry, float eps,
-                 float rope_base, const lca_kv_pages* pages, lca_stream_t stream);
+typedef struct lca_compress_args {
+  size_t struct_size;   /* sizeof(lca_compress_args) */
+  int mode;             /* LCA_CSA or LCA_HCA */
+  int m;                /* tokens per entry (1 .. 4096); n_new % m == 0 */
+  int B, n_new, c;      /* sequences, new tokens per sequence, channels (128, 256, 512 or 1024) */
+  const void* C;        /* [B, n_new, c] candidates, io_dtype */
+  const void* Z;        /* [B, n_new, c] gate logits, io_dtype */
+  int io_dtype;         /* F32 or BF16 */
+  const void* prevC;    /* [B, m, c] previous block (CSA only) or NULL ...   */
+  const void* prevZ;    /* ... both set or both NULL                         */
+  const float* P;       /* [2m, c] (CSA) or [m, c] (HCA) float32 positional bias */
+  void* cache;          /* [B, N_cap, row] in kv_dtype (or a page pool); rows first_entry ..
+                           first_entry + n_new/m - 1 are written */
+  int kv_dtype;         /* F32, BF16 or KV_FP8_BF16ROPE */
+  int N_cap;            /* rows per sequence; first_entry + n_new/m <= N_cap */
+  int first_entry;
+  float eps;            /* RMSNorm epsilon */
+  float rope_base;      /* partial RoPE base (0 = off): entry first_entry + s is turned at
+                           position (first_entry+s+1)*m - 1 */
+  lca_kv_pages pages;   /* block_table NULL: contiguous cache */
+} lca_compress_args;
+int lca_compress(const lca_compress_args* args, lca_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * lca_rmsnorm_rows -- y[b, i] = cast(x[b, i] / sqrt(mean(x[b, i]^2) + eps)):
  * the window (uncompressed) KV of new tokens, RMSNorm of their KV candidates
  * (QbitAI article, hybrid attention section: Q/KV RMSNorm; sliding-window
- * branch over uncompressed KV).
- *   x  [B, n, c] format x_dtype (F32|BF16)
- *   y  rows (b, i) at y + (b*y_seq_rows + i) * row_bytes(y_dtype, c)
- *   pos0, rope_base  with rope_base != 0, row i is turned at position pos0 + i
- *                    (0 <= pos0 <= 2^40)
+ * branch over uncompressed KV).  Rows have the bits lca_state_append writes
+ * to the window ring for the same token.
  * ------------------------------------------------------------------------- */
-int lca_rmsnorm_rows(int B, int n, int c, const void* x, int x_dtype, void* y, int y_dtype,
-                     int y_seq_rows, float eps, int64_t pos0, float rope_base,
-                     lca_stream_t stream);
+typedef struct lca_rmsnorm_rows_args {
+  size_t struct_size;   /* sizeof(lca_rmsnorm_rows_args) */
+  int B, n, c;
+  const void* x;        /* [B, n, c] in x_dtype (F32 or BF16) */
+  int x_dtype;
+  void* y;              /* row (b, i) at y + (b*y_seq_rows + i) * row_bytes(y_dtype, c) */
+  int y_dtype;          /* F32, BF16 or KV_FP8_BF16ROPE */
+  int y_seq_rows;       /* >= n */
+  float eps;
+  float rope_base;      /* 0 = off, else row i is turned at position pos0 + i */
+  int64_t pos0;         /* 0 .. 2^40 */
+} lca_rmsnorm_rows_args;
+int lca_rmsnorm_rows(const lca_rmsnorm_rows_args* args, lca_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * lca_indexer_scores -- lightning-indexer scores (QbitAI article, hybrid
  * attention section: inherited from V3.2's DSA; "DeepSeek V4 Architecture
  * Tricks", section "CSA": 64 indexer heads of dim 128; section "FP4 / FP8
- * Quantization-Aware Training": the indexer QK path in FP4):
+ * Quantization-Aware Training": the indexer QK path in FP4, and index scores
+ * kept in BF16 for an about twice faster selector):
  *   I[b,t,s] = sum_h w[b,t,h] * max(0, sum_d qI[b,t,h,d] * kI[b,s,d])
  * for s < vis(b,t) = min((q_pos[b,t]+1)/m, n_entries[b]).  Entries s >=
- * vis(b,t) are not written.  Products accumulate in float32.
- *
- *   idx_dtype  F32, FP8_E4M3 or MXFP4 (for both qI and kI)
- *   qI         [B, n_q, H_I, d_I] (MXFP4: [B, n_q, H_I, d_I/2] bytes + qI_scale
- *              [B, n_q, H_I, d_I/32]); qI_scale NULL otherwise
- *   kI         [B, N_cap, d_I] (MXFP4: bytes + kI_scale [B, N_cap, d_I/32])
- *   w          [B, n_q, H_I] float32 head weights
- *   q_pos      [B, n_q] int32 positions; n_entries [B] int32 (both device)
- *   scores     [B, n_q, N_cap] float32
- * FP8/MXFP4 need H_I == 64 and d_I == 128; F32 needs d_I <= 256, H_I <= 64.
+ * vis(b,t) are not written.  Products accumulate in float32; with score_dtype
+ * BF16 each visible score is stored as the round-to-nearest-even of that
+ * float32 score.  FP8/MXFP4 need H_I == 64 and d_I == 128; F32 needs
+ * d_I <= 256, d_I % 4 == 0, H_I <= 64.
  * ------------------------------------------------------------------------- */
-int lca_indexer_scores(int B, int n_q, int H_I, int d_I, int idx_dtype, const void* qI,
-                       const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale,
-                       int N_cap, const float* w, const int32_t* q_pos, int m,
-                       const int32_t* n_entries, float* scores, lca_stream_t stream);
+typedef struct lca_indexer_args {
+  size_t struct_size;   /* sizeof(lca_indexer_args) */
+  int B, n_q, H_I, d_I;
+  int idx_dtype;        /* F32, FP8_E4M3 or MXFP4 (for both qI and kI) */
+  const void* qI;       /* [B, n_q, H_I, d_I] (MXFP4: [B, n_q, H_I, d_I/2] bytes) */
+  const uint8_t* qI_scale; /* MXFP4: [B, n_q, H_I, d_I/32] E8M0; NULL otherwise */
+  const void* kI;       /* [B, N_cap, d_I] (MXFP4: bytes) */
+  const uint8_t* kI_scale; /* MXFP4: [B, N_cap, d_I/32]; NULL otherwise */
+  int N_cap;
+  const float* w;       /* [B, n_q, H_I] float32 head weights */
+  const int32_t* q_pos; /* [B, n_q] int32 positions (device) */
+  int m;
+  const int32_t* n_entries; /* [B] int32 (device) */
+  void* scores;         /* [B, n_q, N_cap] in score_dtype */
+  int score_dtype;      /* F32 or BF16 */
+} lca_indexer_args;
+int lca_indexer_scores(const lca_indexer_args* args, lca_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * lca_topk -- per-query top-k selection ("DeepSeek V4 Architecture Tricks",
  * section "CSA": top-k = 1024; QbitAI article: 1M tokens attend 1024
  * compressed blocks).  idx[b,t,:] holds the min(k, vis) indices s < vis(b,t)
  * with the largest scores[b,t,s] (equal scores: lower index first; -0 counts
- * as +0 and NaN as -inf), in ascending order, followed by -1 padding.
- *   scores [B, n_q, N_cap] float32, idx [B, n_q, k] int32, 1 <= k <= 4096.
- * Workspace: lca_topk_workspace_size(B, n_q, N_cap, k) bytes.
+ * as +0 and NaN as -inf), in ascending order, followed by -1 padding.  A BF16
+ * row selects among the bf16 values (its selection can differ from the
+ * float32 one only among scores that round to the same bf16 value).
  * ------------------------------------------------------------------------- */
-size_t lca_topk_workspace_size(int B, int n_q, int N_cap, int k);
-int lca_topk(int B, int n_q, int N_cap, const float* scores, const int32_t* q_pos, int m,
-             const int32_t* n_entries, int k, int32_t* idx, void* workspace,
-             size_t workspace_bytes, lca_stream_t stream);
-
-/* ---------------------------------------------------------------------------
- * The BF16-score selector ("DeepSeek V4 Architecture Tricks", section "FP4 /
- * FP8 Quantization-Aware Training": index scores kept in BF16 make the top-k
- * selector about twice as fast).
- * lca_indexer_scores_bf16 -- as lca_indexer_scores, but each visible score is
- *   stored as bf16: the round-to-nearest-even of the float32 score that
- *   lca_indexer_scores writes for the same inputs.  scores [B, n_q, N_cap] bf16.
- * lca_topk_bf16 -- as lca_topk over bf16 scores [B, n_q, N_cap]: the min(k, vis)
- *   largest bf16 values, equal values lower index first (-0 counts as +0, NaN
- *   as -inf), ascending, -1 padded; workspace lca_topk_workspace_size(...).
- * The selection of a bf16 row can differ from the float32 selection only among
- * scores that round to the same bf16 value.
- * ------------------------------------------------------------------------- */
-int lca_indexer_scores_bf16(int B, int n_q, int H_I, int d_I, int idx_dtype, const void* qI,
-                            const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale,
-                            int N_cap, const float* w, const int32_t* q_pos, int m,
-                            const int32_t* n_entries, uint16_t* scores, lca_stream_t stream);
-int lca_topk_bf16(int B, int n_q, int N_cap, const uint16_t* scores, const int32_t* q_pos, int m,
-                  const int32_t* n_entries, int k, int32_t* idx, void* workspace,
-                  size_t workspace_bytes, lca_stream_t stream);
+typedef struct lca_topk_args {
+  size_t struct_size;   /* sizeof(lca_topk_args) */
+  int B, n_q, N_cap;    /* N_cap <= 2^23 */
+  const void* scores;   /* [B, n_q, N_cap] in score_dtype */
+  int score_dtype;      /* F32 or BF16 */
+  const int32_t* q_pos; /* [B, n_q] */
+  int m;
+  const int32_t* n_entries; /* [B] */
+  int k;                /* 1 .. 4096 */
+  int32_t* idx;         /* [B, n_q, k] int32 */
+  void* workspace;      /* lca_workspace_size(LCA_OP_TOPK, ...) bytes (NULL if 0) */
+  size_t workspace_bytes;
+} lca_topk_args;
+int lca_topk(const lca_topk_args* args, lca_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * lca_sparse_mqa -- core attention of CSA (over idx) or HCA (idx == NULL: all
@@ -254,30 +296,47 @@ int lca_topk_bf16(int B, int n_q, int N_cap, const uint16_t* scores, const int32
  *   out[b,t,h] = sum_x softmax_x(tau * qh . row_x) * row_x, where the softmax
  *   denominator also holds exp(sink[h]) when sink != NULL;
  *   lse[b,t,h]  = log of that denominator.
- *   q        [B, n_q, H, c] format q_dtype (F32|BF16), not normalised
- *   cache    [B, N_cap, row] format kv_dtype (F32|BF16|KV_FP8_BF16ROPE), rows
- *            already RMS-normalised
- *   idx      [B, n_q, k] int32 ascending, -1 padded (lca_topk output), or NULL
- *   q_pos    [B, n_q], n_entries [B] int32 device
- *   win      [B, W_cap, row] window KV in kv_dtype; position j lives in slot
- *            (j - win_origin) mod W_cap.  A decode ring is W_cap = n_win,
- *            win_origin = 0; a prefill buffer of positions p0 .. p0+W_cap-1 is
- *            win_origin = p0.  Every window position must be present.
- *   out      [B, n_q, H, c] format out_dtype (F32|BF16); lse [B, n_q, H] or NULL
- *   rope_base  partial RoPE (0 = off): qh is turned to q_pos[b,t] and out[b,t,h]
- *            back by -q_pos[b,t]; the stored rows are taken as turned
- *   pages    NULL, or the paged layout of cache (see lca_kv_pages); the gather
- *            reads entry e through the block table
- * Workspace: lca_sparse_mqa_workspace_size(...) bytes (split partials).
+ * A query's candidate rows (selected entries in idx order, then the window
+ * oldest first) are split into chunks of whole 64-row tiles, one workgroup
+ * each, whose partial results are merged by log-sum-exp in chunk order.  The
+ * chunk length follows the number of query rows B*n_q (about 256 workgroups
+ * in all), so a query's output bits can depend on B*n_q, never on the other
+ * queries' data.
  * ------------------------------------------------------------------------- */
-size_t lca_sparse_mqa_workspace_size(int B, int n_q, int H, int c, int kv_dtype, int k,
-                                     int N_cap, int n_win, int dense);
-int lca_sparse_mqa(int B, int n_q, int H, int c, const void* q, int q_dtype, const void* cache,
-                   int kv_dtype, int N_cap, const int32_t* idx, int k, const int32_t* q_pos,
-                   int m, const int32_t* n_entries, const void* win, int W_cap,
-                   int64_t win_origin, int n_win, float tau, float eps, const float* sink,
-                   float rope_base, void* out, int out_dtype, float* lse, void* workspace,
-                   size_t workspace_bytes, const lca_kv_pages* pages, lca_stream_t stream);
+typedef struct lca_sparse_mqa_args {
+  size_t struct_size;   /* sizeof(lca_sparse_mqa_args) */
+  int B, n_q, H, c;     /* c in {128, 256, 512}, H a multiple of 8 */
+  const void* q;        /* [B, n_q, H, c] in q_dtype (F32 or BF16), not normalised */
+  int q_dtype;
+  const void* cache;    /* [B, N_cap, row] in kv_dtype (F32, BF16 or KV_FP8_BF16ROPE), rows
+                           already RMS-normalised (or a page pool) */
+  int kv_dtype;
+  int N_cap;
+  const int32_t* idx;   /* [B, n_q, k] ascending, -1 padded (lca_topk output), or NULL (dense) */
+  int k;                /* 1 .. 4096 when idx != NULL */
+  const int32_t* q_pos; /* [B, n_q] */
+  int m;
+  const int32_t* n_entries; /* [B] */
+  const void* win;      /* [B, W_cap, row] window KV in kv_dtype; position j lives in slot
+                           (j - win_origin) mod W_cap.  A decode ring is W_cap = n_win,
+                           win_origin = 0; a prefill buffer of positions p0 .. p0+W_cap-1 is
+                           win_origin = p0.  Every window position must be present. */
+  int W_cap;
+  int64_t win_origin;
+  int n_win;            /* 0 .. 4096 */
+  float tau, eps;
+  const float* sink;    /* [H] or NULL */
+  float rope_base;      /* 0 = off, else qh is turned to q_pos[b,t] and out[b,t,h] back by
+                           -q_pos[b,t]; the stored rows are taken as turned */
+  void* out;            /* [B, n_q, H, c] in out_dtype (F32 or BF16) */
+  int out_dtype;
+  float* lse;           /* [B, n_q, H] or NULL */
+  void* workspace;      /* lca_workspace_size(LCA_OP_SPARSE_MQA, ...) bytes (split partials) */
+  size_t workspace_bytes;
+  lca_kv_pages pages;   /* block_table NULL: contiguous cache; else the gather reads entry e
+                           through the block table */
+} lca_sparse_mqa_args;
+int lca_sparse_mqa(const lca_sparse_mqa_args* args, lca_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * lca_grouped_out_proj -- the grouped output projection after the attention
@@ -287,20 +346,23 @@ int lca_sparse_mqa(int B, int n_q, int H, int c, const void* q, int q_dtype, con
  *   z[t, j*d_g + r] = bf16( sum_i W_g[j, r, i] * o[t, j*(n_h/g)*c + i] )
  *   out[t, n]       = sum_q W_o[n, q] * z[t, q]
  * (group j holds heads j*n_h/g .. (j+1)*n_h/g - 1, concatenated in head order).
- *   o    [T, n_h, c] bf16 (the attention output)
- *   W_g  [g, d_g, (n_h/g)*c] bf16 (each group's matrix, output x input)
- *   W_o  [d, g*d_g] bf16 (output x input)
- *   z    [T, g*d_g] bf16, written (the intermediate; an output of the call)
- *   out  [T, d] out_dtype (F32|BF16)
  * Products accumulate in float32.  Needs n_h % g == 0, d_g and d multiples of
- * 128, (n_h/g)*c a multiple of 64.  Workspace: lca_grouped_out_proj_workspace_size
- * bytes (K-split partials for small T; 0 for large T).
+ * 128, (n_h/g)*c a multiple of 64.
  * ------------------------------------------------------------------------- */
-size_t lca_grouped_out_proj_workspace_size(int T, int n_h, int c, int g, int d_g, int d);
-int lca_grouped_out_proj(int T, int n_h, int c, int g, int d_g, int d, const uint16_t* o,
-                         const uint16_t* W_g, const uint16_t* W_o, uint16_t* z, void* out,
-                         int out_dtype, void* workspace, size_t workspace_bytes,
-                         lca_stream_t stream);
+typedef struct lca_grouped_out_proj_args {
+  size_t struct_size;   /* sizeof(lca_grouped_out_proj_args) */
+  int T, n_h, c, g, d_g, d;
+  const uint16_t* o;    /* [T, n_h, c] bf16 (the attention output) */
+  const uint16_t* W_g;  /* [g, d_g, (n_h/g)*c] bf16 (each group's matrix, output x input) */
+  const uint16_t* W_o;  /* [d, g*d_g] bf16 (output x input) */
+  uint16_t* z;          /* [T, g*d_g] bf16, written (the intermediate) */
+  void* out;            /* [T, d] in out_dtype (F32 or BF16) */
+  int out_dtype;
+  void* workspace;      /* lca_workspace_size(LCA_OP_GROUPED_OUT_PROJ, ...) bytes
+                           (K-split partials for small T; 0 for large T) */
+  size_t workspace_bytes;
+} lca_grouped_out_proj_args;
+int lca_grouped_out_proj(const lca_grouped_out_proj_args* args, lca_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * lca_state_append -- decode-time state of uncompressed tokens ("DeepSeek V4
@@ -312,20 +374,32 @@ int lca_grouped_out_proj(int T, int n_h, int c, int g, int d_g, int d, const uin
  *   - tokC/tokZ go to tail row  ((p/m)%2)*m + p%m  (CSA: two-block ring that
  *     also keeps the previous block for the overlap) or p%m (HCA);
  *   - ring[b, p % n_win] = cast(RMSNorm(tokC[b]));
- *   - if (p+1) % m == 0 the block is compressed (as lca_compress) into
- *     cache[b, (p+1)/m - 1] (skipped if that row is >= N_cap);
+ *   - if (p+1) % m == 0 the block is compressed (as lca_compress, same bits)
+ *     into cache[b, (p+1)/m - 1] (skipped if that row is >= N_cap);
  *   - n_tokens[b] = p+1, q_pos[b] = p, n_entries[b] = (p+1)/m.
- *   tailC, tailZ [B, 2m or m, c] io_dtype; ring [B, n_win, row] kv_dtype;
- *   cache [B, N_cap, row]; n_tokens, q_pos, n_entries [B] int32 device.
  *   rope_base (0 = off): the ring row and a new entry are turned at position p
  *   (the new entry's last token).
- *   pages (NULL = contiguous cache): the new entry goes through the block table.
  * ------------------------------------------------------------------------- */
-int lca_state_append(int mode, int m, int B, int c, int n_win, const void* tokC, const void* tokZ,
-                     int io_dtype, void* tailC, void* tailZ, void* ring, int kv_dtype,
-                     const float* P, void* cache, int N_cap, int32_t* n_tokens, int32_t* q_pos,
-                     int32_t* n_entries, float eps, float rope_base, const lca_kv_pages* pages,
-                     lca_stream_t stream);
+typedef struct lca_state_append_args {
+  size_t struct_size;   /* sizeof(lca_state_append_args) */
+  int mode, m, B, c, n_win;
+  const void* tokC;     /* [B, c] io_dtype */
+  const void* tokZ;
+  int io_dtype;         /* F32 or BF16 */
+  void* tailC;          /* [B, 2m (CSA) or m (HCA), c] io_dtype */
+  void* tailZ;
+  void* ring;           /* [B, n_win, row] kv_dtype */
+  int kv_dtype;
+  const float* P;       /* [2m or m, c] */
+  void* cache;          /* [B, N_cap, row] (or a page pool) */
+  int N_cap;
+  int32_t* n_tokens;    /* [B] int32 device, advanced by one */
+  int32_t* q_pos;       /* [B] written */
+  int32_t* n_entries;   /* [B] written */
+  float eps, rope_base;
+  lca_kv_pages pages;   /* block_table NULL: contiguous cache */
+} lca_state_append_args;
+int lca_state_append(const lca_state_append_args* args, lca_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * lca_decode_step -- one decode step of one CSA or HCA layer for B sequences:
@@ -380,7 +454,7 @@ typedef struct lca_decode_io {
   void* stage_events[5];
 } lca_decode_io;
 
-size_t lca_decode_workspace_size(const lca_decode_layer* layer);
+/* Workspace of lca_decode_step: lca_workspace_size(LCA_OP_DECODE_STEP, layer, &bytes). */
 int lca_decode_step(const lca_decode_layer* layer, const lca_decode_io* io, void* workspace,
                     size_t workspace_bytes, lca_stream_t stream);
 
@@ -406,7 +480,7 @@ int lca_decode_steps(const lca_decode_layer* layer, const lca_decode_io* io, int
  * kernels and results as lca_decode_step; the caller still passes every
  * input and output.
  *   - Returns LCA_ERR_WORKSPACE, having enqueued nothing, when the layer needs
- *     more scratch than that (lca_decode_workspace_size(layer) >
+ *     more scratch than that (the LCA_OP_DECODE_STEP workspace size >
  *     LCA_STATIC_SCRATCH_BYTES; 96 MiB holds a CSA layer of 16 sequences at
  *     1M tokens, or any HCA layer of the workloads).
  *   - Every call on a device shares that device's array, which keeps the last

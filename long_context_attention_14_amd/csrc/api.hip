@@ -49,6 +49,15 @@ bool c_ok(int c) { return c >= 128 && c <= 1024 && c % 64 == 0 && (c / 64 == 2 |
     if (!(cond)) return fail(LCA_ERR_UNSUPPORTED, __VA_ARGS__);    \
   } while (0)
 
+// Every args struct starts with its own size: NULL or another layout is rejected.
+#define CHECK_ARGS(a, T)                                                              \
+  do {                                                                                \
+    if ((a) == nullptr) return fail(LCA_ERR_INVALID_ARG, #T ": NULL argument struct"); \
+    if ((a)->struct_size != sizeof(T))                                                \
+      return fail(LCA_ERR_INVALID_ARG, #T ".struct_size = %zu, this library's is %zu", \
+                  (a)->struct_size, sizeof(T));                                       \
+  } while (0)
+
 // The device view of an optional paged layout (NULL or no table: contiguous),
 // checked against the entries per sequence it must hold.
 int kv_pages(const lca_kv_pages* in, int m, int N_cap, lca::KvPages* out) {
@@ -90,205 +99,117 @@ size_t lca_kv_row_bytes(int kv_dtype, int c) {
   return lca::row_bytes(kv_dtype, c);
 }
 
-int lca_compress(int mode, int m, int B, int n_new, int c, const void* C, const void* Z,
-                 int io_dtype, const void* prevC, const void* prevZ, const float* P, void* cache,
-                 int kv_dtype, int N_cap, int first_entry, float eps, float rope_base,
-                 const lca_kv_pages* pages, lca_stream_t stream) {
+int lca_compress(const lca_compress_args* a, lca_stream_t stream) {
   g_last_error.clear();
+  CHECK_ARGS(a, lca_compress_args);
   lca::KvPages pg;
-  if (int st = kv_pages(pages, m, N_cap, &pg)) return st;
-  REQUIRE(rope_ok(rope_base), "rope_base = %g is neither 0 nor a finite value > 1", rope_base);
-  REQUIRE(mode == LCA_CSA || mode == LCA_HCA, "mode %d is not LCA_CSA/LCA_HCA", mode);
-  REQUIRE(m >= 1 && m <= 4096, "m = %d out of range [1, 4096]", m);
-  REQUIRE(B >= 0 && n_new >= 0, "negative batch or token count");
-  REQUIRE(n_new % m == 0, "n_new = %d is not a multiple of m = %d", n_new, m);
-  SUPPORT(c_ok(c), "c = %d unsupported (need 128, 256, 512 or 1024)", c);
-  SUPPORT(io_fmt_ok(io_dtype), "io_dtype %d unsupported (F32 or BF16)", io_dtype);
-  SUPPORT(kv_fmt_ok(kv_dtype), "kv_dtype %d unsupported", kv_dtype);
-  REQUIRE((prevC == nullptr) == (prevZ == nullptr), "prevC and prevZ must both be set or both NULL");
-  REQUIRE(mode == LCA_CSA || prevC == nullptr, "prevC/prevZ only apply to CSA");
-  REQUIRE(first_entry >= 0 && N_cap >= 0 && static_cast<long long>(first_entry) + n_new / m <= N_cap,
-          "entries [%d, %d) exceed N_cap = %d", first_entry, first_entry + n_new / m, N_cap);
-  if (B == 0 || n_new == 0) return LCA_OK;
-  REQUIRE(C && Z && P && cache, "NULL tensor pointer");
-  return hip_status(lca::launch_compress(mode, m, B, n_new, c, C, Z, io_dtype, prevC, prevZ, P, cache,
-                                         kv_dtype, N_cap, first_entry, eps, rope_step(rope_base), pg,
+  if (int st = kv_pages(&a->pages, a->m, a->N_cap, &pg)) return st;
+  REQUIRE(rope_ok(a->rope_base), "rope_base = %g is neither 0 nor a finite value > 1", a->rope_base);
+  REQUIRE(a->mode == LCA_CSA || a->mode == LCA_HCA, "mode %d is not LCA_CSA/LCA_HCA", a->mode);
+  REQUIRE(a->m >= 1 && a->m <= 4096, "m = %d out of range [1, 4096]", a->m);
+  REQUIRE(a->B >= 0 && a->n_new >= 0, "negative batch or token count");
+  REQUIRE(a->n_new % a->m == 0, "n_new = %d is not a multiple of m = %d", a->n_new, a->m);
+  SUPPORT(c_ok(a->c), "c = %d unsupported (need 128, 256, 512 or 1024)", a->c);
+  SUPPORT(io_fmt_ok(a->io_dtype), "io_dtype %d unsupported (F32 or BF16)", a->io_dtype);
+  SUPPORT(kv_fmt_ok(a->kv_dtype), "kv_dtype %d unsupported", a->kv_dtype);
+  REQUIRE((a->prevC == nullptr) == (a->prevZ == nullptr), "prevC and prevZ must both be set or both NULL");
+  REQUIRE(a->mode == LCA_CSA || a->prevC == nullptr, "prevC/prevZ only apply to CSA");
+  REQUIRE(a->first_entry >= 0 && a->N_cap >= 0 &&
+              static_cast<long long>(a->first_entry) + a->n_new / a->m <= a->N_cap,
+          "entries [%d, %d) exceed N_cap = %d", a->first_entry, a->first_entry + a->n_new / a->m, a->N_cap);
+  REQUIRE(static_cast<long long>(a->B) * (a->n_new / a->m) <= 0x7fffffffLL, "too many entries");
+  if (a->B == 0 || a->n_new == 0) return LCA_OK;
+  REQUIRE(a->C && a->Z && a->P && a->cache, "NULL tensor pointer");
+  return hip_status(lca::launch_compress(a->mode, a->m, a->B, a->n_new, a->c, a->C, a->Z, a->io_dtype,
+                                         a->prevC, a->prevZ, a->P, a->cache, a->kv_dtype, a->N_cap,
+                                         a->first_entry, a->eps, rope_step(a->rope_base), pg,
                                          reinterpret_cast<hipStream_t>(stream)),
                     "lca_compress");
 }
 
-int lca_rmsnorm_rows(int B, int n, int c, const void* x, int x_dtype, void* y, int y_dtype,
-                     int y_seq_rows, float eps, int64_t pos0, float rope_base,
-                     lca_stream_t stream) {
+int lca_rmsnorm_rows(const lca_rmsnorm_rows_args* a, lca_stream_t stream) {
   g_last_error.clear();
-  REQUIRE(B >= 0 && n >= 0, "negative sizes");
-  REQUIRE(rope_ok(rope_base), "rope_base = %g is neither 0 nor a finite value > 1", rope_base);
-  REQUIRE(pos0 >= 0 && pos0 <= (INT64_C(1) << 40), "pos0 = %lld out of range",
-          static_cast<long long>(pos0));
-  SUPPORT(c_ok(c), "c = %d unsupported", c);
-  SUPPORT(io_fmt_ok(x_dtype), "x_dtype %d unsupported", x_dtype);
-  SUPPORT(kv_fmt_ok(y_dtype), "y_dtype %d unsupported", y_dtype);
-  REQUIRE(y_seq_rows >= n, "y_seq_rows = %d < n = %d", y_seq_rows, n);
-  if (B == 0 || n == 0) return LCA_OK;
-  REQUIRE(x && y, "NULL tensor pointer");
-  return hip_status(lca::launch_rmsnorm_rows(B, n, c, x, x_dtype, y, y_dtype, y_seq_rows, eps,
-                                             static_cast<long long>(pos0), rope_step(rope_base),
+  CHECK_ARGS(a, lca_rmsnorm_rows_args);
+  REQUIRE(a->B >= 0 && a->n >= 0, "negative sizes");
+  REQUIRE(rope_ok(a->rope_base), "rope_base = %g is neither 0 nor a finite value > 1", a->rope_base);
+  REQUIRE(a->pos0 >= 0 && a->pos0 <= (INT64_C(1) << 40), "pos0 = %lld out of range",
+          static_cast<long long>(a->pos0));
+  SUPPORT(c_ok(a->c), "c = %d unsupported", a->c);
+  SUPPORT(io_fmt_ok(a->x_dtype), "x_dtype %d unsupported", a->x_dtype);
+  SUPPORT(kv_fmt_ok(a->y_dtype), "y_dtype %d unsupported", a->y_dtype);
+  REQUIRE(a->y_seq_rows >= a->n, "y_seq_rows = %d < n = %d", a->y_seq_rows, a->n);
+  if (a->B == 0 || a->n == 0) return LCA_OK;
+  REQUIRE(a->x && a->y, "NULL tensor pointer");
+  return hip_status(lca::launch_rmsnorm_rows(a->B, a->n, a->c, a->x, a->x_dtype, a->y, a->y_dtype,
+                                             a->y_seq_rows, a->eps, static_cast<long long>(a->pos0),
+                                             rope_step(a->rope_base),
                                              reinterpret_cast<hipStream_t>(stream)),
                     "lca_rmsnorm_rows");
 }
 
-static int indexer_scores(int B, int n_q, int H_I, int d_I, int idx_dtype, const void* qI,
-                          const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale,
-                          int N_cap, const float* w, const int32_t* q_pos, int m,
-                          const int32_t* n_entries, void* scores, int score_fmt,
-                          lca_stream_t stream, const char* name) {
+int lca_indexer_scores(const lca_indexer_args* a, lca_stream_t stream) {
   g_last_error.clear();
-  REQUIRE(B >= 0 && n_q >= 0 && N_cap >= 0, "negative sizes");
-  REQUIRE(m >= 1, "m = %d < 1", m);
-  REQUIRE(H_I >= 1 && d_I >= 1, "H_I and d_I must be positive");
-  if (idx_dtype == LCA_F32) {
-    SUPPORT(H_I <= 64 && d_I <= 256 && d_I % 4 == 0, "F32 indexer needs H_I <= 64, d_I <= 256");
-  } else if (idx_dtype == LCA_FP8_E4M3 || idx_dtype == LCA_MXFP4) {
-    SUPPORT(H_I == 64 && d_I == 128, "FP8/MXFP4 indexer needs H_I == 64 and d_I == 128");
+  CHECK_ARGS(a, lca_indexer_args);
+  REQUIRE(a->B >= 0 && a->n_q >= 0 && a->N_cap >= 0, "negative sizes");
+  REQUIRE(a->m >= 1, "m = %d < 1", a->m);
+  REQUIRE(a->H_I >= 1 && a->d_I >= 1, "H_I and d_I must be positive");
+  if (a->idx_dtype == LCA_F32) {
+    SUPPORT(a->H_I <= 64 && a->d_I <= 256 && a->d_I % 4 == 0, "F32 indexer needs H_I <= 64, d_I <= 256");
+  } else if (a->idx_dtype == LCA_FP8_E4M3 || a->idx_dtype == LCA_MXFP4) {
+    SUPPORT(a->H_I == 64 && a->d_I == 128, "FP8/MXFP4 indexer needs H_I == 64 and d_I == 128");
   } else {
-    return fail(LCA_ERR_UNSUPPORTED, "idx_dtype %d unsupported", idx_dtype);
+    return fail(LCA_ERR_UNSUPPORTED, "idx_dtype %d unsupported", a->idx_dtype);
   }
-  if (idx_dtype == LCA_MXFP4)
-    REQUIRE(qI_scale && kI_scale, "MXFP4 needs qI_scale and kI_scale");
-  if (B == 0 || n_q == 0 || N_cap == 0) return LCA_OK;
-  REQUIRE(qI && kI && w && q_pos && n_entries && scores, "NULL tensor pointer");
-  return hip_status(lca::launch_indexer(B, n_q, H_I, d_I, idx_dtype, qI, qI_scale, kI, kI_scale,
-                                        N_cap, w, q_pos, m, n_entries, scores,
-                                        reinterpret_cast<hipStream_t>(stream), nullptr, nullptr,
-                                        nullptr, nullptr, 0, score_fmt),
-                    name);
+  SUPPORT(a->score_dtype == LCA_F32 || a->score_dtype == LCA_BF16, "score_dtype %d unsupported (F32 or BF16)",
+          a->score_dtype);
+  if (a->idx_dtype == LCA_MXFP4) REQUIRE(a->qI_scale && a->kI_scale, "MXFP4 needs qI_scale and kI_scale");
+  if (a->B == 0 || a->n_q == 0 || a->N_cap == 0) return LCA_OK;
+  REQUIRE(a->qI && a->kI && a->w && a->q_pos && a->n_entries && a->scores, "NULL tensor pointer");
+  return hip_status(lca::launch_indexer(a->B, a->n_q, a->H_I, a->d_I, a->idx_dtype, a->qI, a->qI_scale, a->kI,
+                                        a->kI_scale, a->N_cap, a->w, a->q_pos, a->m, a->n_entries, a->scores,
+                                        reinterpret_cast<hipStream_t>(stream), nullptr, nullptr, nullptr,
+                                        nullptr, 0, a->score_dtype),
+                    "lca_indexer_scores");
 }
 
-int lca_indexer_scores(int B, int n_q, int H_I, int d_I, int idx_dtype, const void* qI,
-                       const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale, int N_cap,
-                       const float* w, const int32_t* q_pos, int m, const int32_t* n_entries,
-                       float* scores, lca_stream_t stream) {
-  return indexer_scores(B, n_q, H_I, d_I, idx_dtype, qI, qI_scale, kI, kI_scale, N_cap, w, q_pos, m,
-                        n_entries, scores, LCA_F32, stream, "lca_indexer_scores");
-}
-
-int lca_indexer_scores_bf16(int B, int n_q, int H_I, int d_I, int idx_dtype, const void* qI,
-                            const uint8_t* qI_scale, const void* kI, const uint8_t* kI_scale,
-                            int N_cap, const float* w, const int32_t* q_pos, int m,
-                            const int32_t* n_entries, uint16_t* scores, lca_stream_t stream) {
-  return indexer_scores(B, n_q, H_I, d_I, idx_dtype, qI, qI_scale, kI, kI_scale, N_cap, w, q_pos, m,
-                        n_entries, scores, LCA_BF16, stream, "lca_indexer_scores_bf16");
-}
-
-size_t lca_topk_workspace_size(int B, int n_q, int N_cap, int k) {
-  if (B < 0 || n_q < 0 || N_cap < 0 || k < 1 || k > 4096) return 0;
-  return lca::topk_workspace_bytes(B, n_q, N_cap, k);
-}
-
-static int topk(int B, int n_q, int N_cap, const void* scores, int score_fmt, const int32_t* q_pos,
-                int m, const int32_t* n_entries, int k, int32_t* idx, void* workspace,
-                size_t workspace_bytes, lca_stream_t stream, const char* name) {
-  g_last_error.clear();
-  REQUIRE(B >= 0 && n_q >= 0 && N_cap >= 0, "negative sizes");
-  REQUIRE(k >= 1 && k <= 4096, "k = %d out of range [1, 4096]", k);
-  REQUIRE(m >= 1, "m = %d < 1", m);
-  SUPPORT(N_cap <= (1 << 23), "N_cap = %d too large", N_cap);
-  const size_t need = lca::topk_workspace_bytes(B, n_q, N_cap, k);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(LCA_ERR_WORKSPACE, "%s needs %zu workspace bytes, got %zu", name, need,
-                workspace ? workspace_bytes : 0);
-  if (B == 0 || n_q == 0) return LCA_OK;
-  REQUIRE(scores && q_pos && n_entries && idx, "NULL tensor pointer");
-  return hip_status(lca::launch_topk(B, n_q, N_cap, scores, q_pos, m, n_entries, k, idx, workspace,
-                                     reinterpret_cast<hipStream_t>(stream), score_fmt),
-                    name);
-}
-
-int lca_topk(int B, int n_q, int N_cap, const float* scores, const int32_t* q_pos, int m,
-             const int32_t* n_entries, int k, int32_t* idx, void* workspace, size_t workspace_bytes,
-             lca_stream_t stream) {
-  return topk(B, n_q, N_cap, scores, LCA_F32, q_pos, m, n_entries, k, idx, workspace,
-              workspace_bytes, stream, "lca_topk");
-}
-
-int lca_topk_bf16(int B, int n_q, int N_cap, const uint16_t* scores, const int32_t* q_pos, int m,
-                  const int32_t* n_entries, int k, int32_t* idx, void* workspace,
-                  size_t workspace_bytes, lca_stream_t stream) {
-  return topk(B, n_q, N_cap, scores, LCA_BF16, q_pos, m, n_entries, k, idx, workspace,
-              workspace_bytes, stream, "lca_topk_bf16");
-}
-
-size_t lca_sparse_mqa_workspace_size(int B, int n_q, int H, int c, int kv_dtype, int k, int N_cap,
-                                     int n_win, int dense) {
-  if (B < 0 || n_q < 0 || H < 1 || !c_ok(c) || N_cap < 0 || n_win < 0 || k < 0) return 0;
-  return lca::mqa_workspace_bytes(B, n_q, H, c, kv_dtype, k, N_cap, n_win, dense);
-}
-
-int lca_sparse_mqa(int B, int n_q, int H, int c, const void* q, int q_dtype, const void* cache,
-                   int kv_dtype, int N_cap, const int32_t* idx, int k, const int32_t* q_pos, int m,
-                   const int32_t* n_entries, const void* win, int W_cap, int64_t win_origin,
-                   int n_win, float tau, float eps, const float* sink, float rope_base, void* out,
-                   int out_dtype, float* lse, void* workspace, size_t workspace_bytes,
-                   const lca_kv_pages* pages, lca_stream_t stream) {
-  g_last_error.clear();
-  lca::KvPages pg;
-  REQUIRE(m >= 1, "m = %d < 1", m);
-  if (int st = kv_pages(pages, m, N_cap, &pg)) return st;
-  REQUIRE(rope_ok(rope_base), "rope_base = %g is neither 0 nor a finite value > 1", rope_base);
-  REQUIRE(B >= 0 && n_q >= 0 && N_cap >= 0, "negative sizes");
-  REQUIRE(m >= 1, "m = %d < 1", m);
-  SUPPORT(c == 128 || c == 256 || c == 512, "c = %d unsupported (128, 256 or 512)", c);
-  SUPPORT(H >= 8 && H % 8 == 0, "H = %d unsupported (multiple of 8)", H);
-  SUPPORT(io_fmt_ok(q_dtype) && io_fmt_ok(out_dtype), "q/out dtype unsupported (F32 or BF16)");
-  SUPPORT(kv_fmt_ok(kv_dtype), "kv_dtype %d unsupported", kv_dtype);
-  REQUIRE(idx == nullptr || (k >= 1 && k <= 4096), "k = %d out of range", k);
-  REQUIRE(n_win >= 0 && n_win <= 4096, "n_win = %d out of range", n_win);
-  REQUIRE(n_win == 0 || (win != nullptr && W_cap >= 1), "window buffer missing");
-  const int dense = idx == nullptr;
-  const size_t need = lca::mqa_workspace_bytes(B, n_q, H, c, kv_dtype, k, N_cap, n_win, dense);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(LCA_ERR_WORKSPACE, "lca_sparse_mqa needs %zu workspace bytes, got %zu", need,
-                workspace ? workspace_bytes : 0);
-  if (B == 0 || n_q == 0) return LCA_OK;
-  REQUIRE(q && cache && q_pos && n_entries && out, "NULL tensor pointer");
-  return hip_status(lca::launch_mqa(B, n_q, H, c, q, q_dtype, cache, kv_dtype, N_cap, idx, k, q_pos,
-                                    m, n_entries, win, W_cap, win_origin, n_win, tau, eps, sink,
-                                    rope_step(rope_base), out, out_dtype, lse, workspace, pg,
-                                    reinterpret_cast<hipStream_t>(stream)),
-                    "lca_sparse_mqa");
-}
-
-int lca_state_append(int mode, int m, int B, int c, int n_win, const void* tokC, const void* tokZ,
-                     int io_dtype, void* tailC, void* tailZ, void* ring, int kv_dtype,
-                     const float* P, void* cache, int N_cap, int32_t* n_tokens, int32_t* q_pos,
-                     int32_t* n_entries, float eps, float rope_base, const lca_kv_pages* pages,
-                     lca_stream_t stream) {
-  g_last_error.clear();
-  REQUIRE(mode == LCA_CSA || mode == LCA_HCA, "mode %d is not LCA_CSA/LCA_HCA", mode);
-  REQUIRE(m >= 1 && m <= 4096, "m = %d out of range", m);
-  lca::KvPages pg;
-  if (int st = kv_pages(pages, m, N_cap, &pg)) return st;
-  REQUIRE(rope_ok(rope_base), "rope_base = %g is neither 0 nor a finite value > 1", rope_base);
-  REQUIRE(B >= 0 && N_cap >= 0, "negative sizes");
-  REQUIRE(n_win >= 1, "n_win = %d < 1", n_win);
-  SUPPORT(c_ok(c), "c = %d unsupported", c);
-  SUPPORT(io_fmt_ok(io_dtype), "io_dtype %d unsupported", io_dtype);
-  SUPPORT(kv_fmt_ok(kv_dtype), "kv_dtype %d unsupported", kv_dtype);
-  if (B == 0) return LCA_OK;
-  REQUIRE(tokC && tokZ && tailC && tailZ && ring && P && cache && n_tokens && q_pos && n_entries,
-          "NULL tensor pointer");
-  return hip_status(lca::launch_state_append(mode, m, B, c, n_win, tokC, tokZ, io_dtype, tailC,
-                                             tailZ, ring, kv_dtype, P, cache, N_cap, n_tokens,
-                                             q_pos, n_entries, eps, rope_step(rope_base), pg,
-                                             reinterpret_cast<hipStream_t>(stream)),
-                    "lca_state_append");
-}
-
-// ---------------------------------------------------------------------------
-// grouped output projection
+}  // extern "C"
 
 namespace {
-int out_proj_check(int T, int n_h, int c, int g, int d_g, int d) {
+
+int topk_check(const lca_topk_args* a) {
+  CHECK_ARGS(a, lca_topk_args);
+  REQUIRE(a->B >= 0 && a->n_q >= 0 && a->N_cap >= 0, "negative sizes");
+  REQUIRE(a->k >= 1 && a->k <= 4096, "k = %d out of range [1, 4096]", a->k);
+  REQUIRE(a->m >= 1, "m = %d < 1", a->m);
+  SUPPORT(a->N_cap <= (1 << 23), "N_cap = %d too large", a->N_cap);
+  SUPPORT(a->score_dtype == LCA_F32 || a->score_dtype == LCA_BF16, "score_dtype %d unsupported (F32 or BF16)",
+          a->score_dtype);
+  return LCA_OK;
+}
+
+int mqa_check(const lca_sparse_mqa_args* a, lca::KvPages* pg) {
+  CHECK_ARGS(a, lca_sparse_mqa_args);
+  REQUIRE(a->m >= 1, "m = %d < 1", a->m);
+  if (int st = kv_pages(&a->pages, a->m, a->N_cap, pg)) return st;
+  REQUIRE(rope_ok(a->rope_base), "rope_base = %g is neither 0 nor a finite value > 1", a->rope_base);
+  REQUIRE(a->B >= 0 && a->n_q >= 0 && a->N_cap >= 0, "negative sizes");
+  SUPPORT(a->c == 128 || a->c == 256 || a->c == 512, "c = %d unsupported (128, 256 or 512)", a->c);
+  SUPPORT(a->H >= 8 && a->H % 8 == 0, "H = %d unsupported (multiple of 8)", a->H);
+  SUPPORT(io_fmt_ok(a->q_dtype) && io_fmt_ok(a->out_dtype), "q/out dtype unsupported (F32 or BF16)");
+  SUPPORT(kv_fmt_ok(a->kv_dtype), "kv_dtype %d unsupported", a->kv_dtype);
+  REQUIRE(a->idx == nullptr || (a->k >= 1 && a->k <= 4096), "k = %d out of range", a->k);
+  REQUIRE(a->n_win >= 0 && a->n_win <= 4096, "n_win = %d out of range", a->n_win);
+  return LCA_OK;
+}
+
+size_t mqa_ws(const lca_sparse_mqa_args* a) {
+  return lca::mqa_workspace_bytes(a->B, a->n_q, a->H, a->c, a->kv_dtype, a->k, a->N_cap, a->n_win,
+                                  a->idx == nullptr);
+}
+
+int out_proj_check(const lca_grouped_out_proj_args* a) {
+  CHECK_ARGS(a, lca_grouped_out_proj_args);
+  const int T = a->T, n_h = a->n_h, c = a->c, g = a->g, d_g = a->d_g, d = a->d;
   REQUIRE(T >= 0, "T = %d < 0", T);
   REQUIRE(n_h >= 1 && c >= 1 && g >= 1 && d_g >= 1 && d >= 1, "sizes must be positive");
   REQUIRE(n_h % g == 0, "n_h = %d is not a multiple of g = %d", n_h, g);
@@ -298,30 +219,84 @@ int out_proj_check(int T, int n_h, int c, int g, int d_g, int d) {
   SUPPORT(static_cast<long long>(T) * n_h * c < (1LL << 31) &&
               static_cast<long long>(d) * g * d_g < (1LL << 31),
           "tensor too large");
+  SUPPORT(io_fmt_ok(a->out_dtype), "out_dtype %d unsupported (F32 or BF16)", a->out_dtype);
   return LCA_OK;
 }
-}  // namespace
 
-size_t lca_grouped_out_proj_workspace_size(int T, int n_h, int c, int g, int d_g, int d) {
-  if (out_proj_check(T, n_h, c, g, d_g, d) != LCA_OK) return 0;
-  return lca::out_proj_workspace_bytes(T, n_h, c, g, d_g, d);
+int workspace_ok(const char* name, size_t need, const void* ws, size_t have) {
+  if (need > 0 && (ws == nullptr || have < need))
+    return fail(LCA_ERR_WORKSPACE, "%s needs %zu workspace bytes, got %zu", name, need, ws ? have : 0);
+  return LCA_OK;
 }
 
-int lca_grouped_out_proj(int T, int n_h, int c, int g, int d_g, int d, const uint16_t* o,
-                         const uint16_t* W_g, const uint16_t* W_o, uint16_t* z, void* out,
-                         int out_dtype, void* workspace, size_t workspace_bytes,
-                         lca_stream_t stream) {
+}  // namespace
+
+extern "C" {
+
+int lca_topk(const lca_topk_args* a, lca_stream_t stream) {
   g_last_error.clear();
-  if (int st = out_proj_check(T, n_h, c, g, d_g, d)) return st;
-  SUPPORT(io_fmt_ok(out_dtype), "out_dtype %d unsupported (F32 or BF16)", out_dtype);
-  const size_t need = lca::out_proj_workspace_bytes(T, n_h, c, g, d_g, d);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(LCA_ERR_WORKSPACE, "lca_grouped_out_proj needs %zu workspace bytes, got %zu", need,
-                workspace ? workspace_bytes : 0);
-  if (T == 0) return LCA_OK;
-  REQUIRE(o && W_g && W_o && z && out, "NULL tensor pointer");
-  return hip_status(lca::launch_out_proj(T, n_h, c, g, d_g, d, o, W_g, W_o, z, out, out_dtype,
-                                         workspace, reinterpret_cast<hipStream_t>(stream)),
+  if (int st = topk_check(a)) return st;
+  const size_t need = lca::topk_workspace_bytes(a->B, a->n_q, a->N_cap, a->k);
+  if (int st = workspace_ok("lca_topk", need, a->workspace, a->workspace_bytes)) return st;
+  if (a->B == 0 || a->n_q == 0) return LCA_OK;
+  REQUIRE(a->scores && a->q_pos && a->n_entries && a->idx, "NULL tensor pointer");
+  return hip_status(lca::launch_topk(a->B, a->n_q, a->N_cap, a->scores, a->q_pos, a->m, a->n_entries, a->k,
+                                     a->idx, a->workspace, reinterpret_cast<hipStream_t>(stream),
+                                     a->score_dtype),
+                    "lca_topk");
+}
+
+int lca_sparse_mqa(const lca_sparse_mqa_args* a, lca_stream_t stream) {
+  g_last_error.clear();
+  lca::KvPages pg;
+  if (int st = mqa_check(a, &pg)) return st;
+  REQUIRE(a->n_win == 0 || (a->win != nullptr && a->W_cap >= 1), "window buffer missing");
+  if (int st = workspace_ok("lca_sparse_mqa", mqa_ws(a), a->workspace, a->workspace_bytes)) return st;
+  if (a->B == 0 || a->n_q == 0) return LCA_OK;
+  REQUIRE(a->q && a->cache && a->q_pos && a->n_entries && a->out, "NULL tensor pointer");
+  return hip_status(lca::launch_mqa(a->B, a->n_q, a->H, a->c, a->q, a->q_dtype, a->cache, a->kv_dtype, a->N_cap,
+                                    a->idx, a->k, a->q_pos, a->m, a->n_entries, a->win, a->W_cap,
+                                    a->win_origin, a->n_win, a->tau, a->eps, a->sink,
+                                    rope_step(a->rope_base), a->out, a->out_dtype, a->lse, a->workspace,
+                                    pg, reinterpret_cast<hipStream_t>(stream)),
+                    "lca_sparse_mqa");
+}
+
+int lca_state_append(const lca_state_append_args* a, lca_stream_t stream) {
+  g_last_error.clear();
+  CHECK_ARGS(a, lca_state_append_args);
+  REQUIRE(a->mode == LCA_CSA || a->mode == LCA_HCA, "mode %d is not LCA_CSA/LCA_HCA", a->mode);
+  REQUIRE(a->m >= 1 && a->m <= 4096, "m = %d out of range", a->m);
+  lca::KvPages pg;
+  if (int st = kv_pages(&a->pages, a->m, a->N_cap, &pg)) return st;
+  REQUIRE(rope_ok(a->rope_base), "rope_base = %g is neither 0 nor a finite value > 1", a->rope_base);
+  REQUIRE(a->B >= 0 && a->N_cap >= 0, "negative sizes");
+  REQUIRE(a->n_win >= 1, "n_win = %d < 1", a->n_win);
+  SUPPORT(c_ok(a->c), "c = %d unsupported", a->c);
+  SUPPORT(io_fmt_ok(a->io_dtype), "io_dtype %d unsupported", a->io_dtype);
+  SUPPORT(kv_fmt_ok(a->kv_dtype), "kv_dtype %d unsupported", a->kv_dtype);
+  if (a->B == 0) return LCA_OK;
+  REQUIRE(a->tokC && a->tokZ && a->tailC && a->tailZ && a->ring && a->P && a->cache && a->n_tokens &&
+              a->q_pos && a->n_entries,
+          "NULL tensor pointer");
+  return hip_status(lca::launch_state_append(a->mode, a->m, a->B, a->c, a->n_win, a->tokC, a->tokZ, a->io_dtype,
+                                             a->tailC, a->tailZ, a->ring, a->kv_dtype, a->P, a->cache,
+                                             a->N_cap, a->n_tokens, a->q_pos, a->n_entries, a->eps,
+                                             rope_step(a->rope_base), pg,
+                                             reinterpret_cast<hipStream_t>(stream)),
+                    "lca_state_append");
+}
+
+int lca_grouped_out_proj(const lca_grouped_out_proj_args* a, lca_stream_t stream) {
+  g_last_error.clear();
+  if (int st = out_proj_check(a)) return st;
+  const size_t need = lca::out_proj_workspace_bytes(a->T, a->n_h, a->c, a->g, a->d_g, a->d);
+  if (int st = workspace_ok("lca_grouped_out_proj", need, a->workspace, a->workspace_bytes)) return st;
+  if (a->T == 0) return LCA_OK;
+  REQUIRE(a->o && a->W_g && a->W_o && a->z && a->out, "NULL tensor pointer");
+  return hip_status(lca::launch_out_proj(a->T, a->n_h, a->c, a->g, a->d_g, a->d, a->o, a->W_g, a->W_o, a->z,
+                                         a->out, a->out_dtype, a->workspace,
+                                         reinterpret_cast<hipStream_t>(stream)),
                     "lca_grouped_out_proj");
 }
 
@@ -376,9 +351,39 @@ int check_layer(const lca_decode_layer* L) {
 
 }  // namespace
 
-size_t lca_decode_workspace_size(const lca_decode_layer* layer) {
-  if (check_layer(layer) != LCA_OK) return 0;
-  return decode_layout(layer).total;
+int lca_workspace_size(int op, const void* args, size_t* bytes) {
+  g_last_error.clear();
+  REQUIRE(bytes != nullptr, "NULL bytes pointer");
+  *bytes = 0;
+  switch (op) {
+    case LCA_OP_TOPK: {
+      const auto* a = static_cast<const lca_topk_args*>(args);
+      if (int st = topk_check(a)) return st;
+      *bytes = lca::topk_workspace_bytes(a->B, a->n_q, a->N_cap, a->k);
+      return LCA_OK;
+    }
+    case LCA_OP_SPARSE_MQA: {
+      const auto* a = static_cast<const lca_sparse_mqa_args*>(args);
+      lca::KvPages pg;
+      if (int st = mqa_check(a, &pg)) return st;
+      *bytes = mqa_ws(a);
+      return LCA_OK;
+    }
+    case LCA_OP_GROUPED_OUT_PROJ: {
+      const auto* a = static_cast<const lca_grouped_out_proj_args*>(args);
+      if (int st = out_proj_check(a)) return st;
+      *bytes = lca::out_proj_workspace_bytes(a->T, a->n_h, a->c, a->g, a->d_g, a->d);
+      return LCA_OK;
+    }
+    case LCA_OP_DECODE_STEP: {
+      const auto* L = static_cast<const lca_decode_layer*>(args);
+      if (int st = check_layer(L)) return st;
+      *bytes = decode_layout(L).total;
+      return LCA_OK;
+    }
+    default:
+      return fail(LCA_ERR_INVALID_ARG, "op %d has no workspace (enum lca_op)", op);
+  }
 }
 
 }  // extern "C"

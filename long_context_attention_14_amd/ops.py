@@ -13,7 +13,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import FMT, MODE, DecodeIO, DecodeLayer, KvPages, check, lib
+from ._lib import FMT, MODE, OP, DecodeIO, DecodeLayer, KvPages, check, lib
 
 _ROW_BYTES = {"f32": lambda c: 4 * c, "bf16": lambda c: 2 * c, "fp8": lambda c: c,
               "fp8_bf16rope": lambda c: c + 64, "mxfp4": lambda c: c // 2}
@@ -69,10 +69,6 @@ def _cache_rows(N_cap, B, pages, m):
     return pages.n_pages * (pages.page_tokens // m)
 
 
-def _pages_ref(pages):
-    return None if pages is None else ctypes.byref(pages)
-
-
 def lca_version() -> int:
     return lib().lca_version()
 
@@ -81,97 +77,120 @@ def lca_kv_row_bytes(kv_fmt: str, c: int) -> int:
     return lib().lca_kv_row_bytes(FMT[kv_fmt], c)
 
 
+def _pages_field(pages):
+    return KvPages() if pages is None else pages
+
+
+def _call(name, args, stream):
+    return check(name, getattr(lib(), name)(ctypes.byref(args), _stream(stream)))
+
+
+def lca_workspace_size(op: str, args) -> int:
+    """Workspace bytes of operation `op` ("topk", "sparse_mqa", "grouped_out_proj",
+    "decode_step") for its argument struct."""
+    n = ctypes.c_size_t(0)
+    check("lca_workspace_size", lib().lca_workspace_size(OP[op], ctypes.byref(args), ctypes.byref(n)))
+    return n.value
+
+
 def lca_compress(mode, m, B, n_new, c, C, Z, io_fmt, prevC, prevZ, P, cache, kv_fmt, N_cap,
                  first_entry, eps=1e-6, rope_base=0.0, pages=None, stream=None):
     io_b = row_bytes(io_fmt, c) * B * n_new
     W = 2 * m if mode == "csa" else m
-    args = (MODE[mode], m, B, n_new, c, _ptr(C, io_b, "C"), _ptr(Z, io_b, "Z"), FMT[io_fmt],
-            _ptr(prevC, row_bytes(io_fmt, c) * B * m, "prevC", True),
-            _ptr(prevZ, row_bytes(io_fmt, c) * B * m, "prevZ", True),
-            _ptr(P, 4 * W * c, "P"), _ptr(cache, row_bytes(kv_fmt, c) * _cache_rows(N_cap, B, pages, m), "cache"),
-            FMT[kv_fmt], N_cap, first_entry, eps, rope_base, _pages_ref(pages), _stream(stream))
-    return check("lca_compress", lib().lca_compress(*args))
+    a = _lib.CompressArgs(
+        mode=MODE[mode], m=m, B=B, n_new=n_new, c=c, C=_ptr(C, io_b, "C"), Z=_ptr(Z, io_b, "Z"),
+        io_dtype=FMT[io_fmt], prevC=_ptr(prevC, row_bytes(io_fmt, c) * B * m, "prevC", True),
+        prevZ=_ptr(prevZ, row_bytes(io_fmt, c) * B * m, "prevZ", True), P=_ptr(P, 4 * W * c, "P"),
+        cache=_ptr(cache, row_bytes(kv_fmt, c) * _cache_rows(N_cap, B, pages, m), "cache"),
+        kv_dtype=FMT[kv_fmt], N_cap=N_cap, first_entry=first_entry, eps=eps, rope_base=rope_base,
+        pages=_pages_field(pages))
+    return _call("lca_compress", a, stream)
 
 
 def lca_rmsnorm_rows(B, n, c, x, x_fmt, y, y_fmt, y_seq_rows, eps=1e-6, pos0=0, rope_base=0.0,
                      stream=None):
     need_y = row_bytes(y_fmt, c) * ((B - 1) * y_seq_rows + n) if B and n else 0
-    return check("lca_rmsnorm_rows", lib().lca_rmsnorm_rows(
-        B, n, c, _ptr(x, row_bytes(x_fmt, c) * B * n, "x"), FMT[x_fmt], _ptr(y, need_y, "y"),
-        FMT[y_fmt], y_seq_rows, eps, pos0, rope_base, _stream(stream)))
+    a = _lib.RmsnormRowsArgs(B=B, n=n, c=c, x=_ptr(x, row_bytes(x_fmt, c) * B * n, "x"),
+                             x_dtype=FMT[x_fmt], y=_ptr(y, need_y, "y"), y_dtype=FMT[y_fmt],
+                             y_seq_rows=y_seq_rows, eps=eps, rope_base=rope_base, pos0=pos0)
+    return _call("lca_rmsnorm_rows", a, stream)
 
 
 def lca_indexer_scores(B, n_q, H_I, d_I, idx_fmt, qI, qI_scale, kI, kI_scale, N_cap, w, q_pos, m,
-                       n_entries, scores, stream=None):
+                       n_entries, scores, score_fmt="f32", stream=None):
+    """score_fmt "f32", or "bf16" (the BF16-score selector: each score stored as the
+    round-to-nearest-even of its float32 value)."""
     vb = row_bytes(idx_fmt, d_I)
     mx = idx_fmt == "mxfp4"
-    return check("lca_indexer_scores", lib().lca_indexer_scores(
-        B, n_q, H_I, d_I, FMT[idx_fmt], _ptr(qI, vb * B * n_q * H_I, "qI"),
-        _ptr(qI_scale, B * n_q * H_I * d_I // 32, "qI_scale", not mx),
-        _ptr(kI, vb * B * N_cap, "kI"), _ptr(kI_scale, B * N_cap * d_I // 32, "kI_scale", not mx),
-        N_cap, _ptr(w, 4 * B * n_q * H_I, "w"), _ptr(q_pos, 4 * B * n_q, "q_pos"), m,
-        _ptr(n_entries, 4 * B, "n_entries"), _ptr(scores, 4 * B * n_q * N_cap, "scores"),
-        _stream(stream)))
+    sb = 4 if score_fmt == "f32" else 2
+    a = _lib.IndexerArgs(
+        B=B, n_q=n_q, H_I=H_I, d_I=d_I, idx_dtype=FMT[idx_fmt], qI=_ptr(qI, vb * B * n_q * H_I, "qI"),
+        qI_scale=_ptr(qI_scale, B * n_q * H_I * d_I // 32, "qI_scale", not mx),
+        kI=_ptr(kI, vb * B * N_cap, "kI"), kI_scale=_ptr(kI_scale, B * N_cap * d_I // 32, "kI_scale", not mx),
+        N_cap=N_cap, w=_ptr(w, 4 * B * n_q * H_I, "w"), q_pos=_ptr(q_pos, 4 * B * n_q, "q_pos"), m=m,
+        n_entries=_ptr(n_entries, 4 * B, "n_entries"), scores=_ptr(scores, sb * B * n_q * N_cap, "scores"),
+        score_dtype=FMT[score_fmt])
+    return _call("lca_indexer_scores", a, stream)
 
 
-def lca_indexer_scores_bf16(B, n_q, H_I, d_I, idx_fmt, qI, qI_scale, kI, kI_scale, N_cap, w, q_pos,
-                            m, n_entries, scores, stream=None):
-    vb = row_bytes(idx_fmt, d_I)
-    mx = idx_fmt == "mxfp4"
-    return check("lca_indexer_scores_bf16", lib().lca_indexer_scores_bf16(
-        B, n_q, H_I, d_I, FMT[idx_fmt], _ptr(qI, vb * B * n_q * H_I, "qI"),
-        _ptr(qI_scale, B * n_q * H_I * d_I // 32, "qI_scale", not mx),
-        _ptr(kI, vb * B * N_cap, "kI"), _ptr(kI_scale, B * N_cap * d_I // 32, "kI_scale", not mx),
-        N_cap, _ptr(w, 4 * B * n_q * H_I, "w"), _ptr(q_pos, 4 * B * n_q, "q_pos"), m,
-        _ptr(n_entries, 4 * B, "n_entries"), _ptr(scores, 2 * B * n_q * N_cap, "scores"),
-        _stream(stream)))
+def _topk_args(B, n_q, N_cap, scores, q_pos, m, n_entries, k, idx, score_fmt):
+    return _lib.TopkArgs(B=B, n_q=n_q, N_cap=N_cap, scores=scores, score_dtype=FMT[score_fmt],
+                         q_pos=q_pos, m=m, n_entries=n_entries, k=k, idx=idx)
 
 
-def lca_topk_workspace_size(B, n_q, N_cap, k) -> int:
-    return lib().lca_topk_workspace_size(B, n_q, N_cap, k)
+def topk_workspace_size(B, n_q, N_cap, k, score_fmt="f32") -> int:
+    return lca_workspace_size("topk", _topk_args(B, n_q, N_cap, None, None, 1, None, k, None, score_fmt))
 
 
-def lca_topk(B, n_q, N_cap, scores, q_pos, m, n_entries, k, idx, workspace=None, stream=None):
-    need = lca_topk_workspace_size(B, n_q, N_cap, k)
+def lca_topk(B, n_q, N_cap, scores, q_pos, m, n_entries, k, idx, workspace=None, score_fmt="f32",
+             stream=None):
+    """score_fmt "f32", or "bf16" (top-k over bf16 scores)."""
+    sb = 4 if score_fmt == "f32" else 2
+    a = _topk_args(B, n_q, N_cap, _ptr(scores, sb * B * n_q * N_cap, "scores"),
+                   _ptr(q_pos, 4 * B * n_q, "q_pos"), m, _ptr(n_entries, 4 * B, "n_entries"), k,
+                   _ptr(idx, 4 * B * n_q * k, "idx"), score_fmt)
+    need = lca_workspace_size("topk", a)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
-    return check("lca_topk", lib().lca_topk(
-        B, n_q, N_cap, _ptr(scores, 4 * B * n_q * N_cap, "scores"), _ptr(q_pos, 4 * B * n_q, "q_pos"),
-        m, _ptr(n_entries, 4 * B, "n_entries"), k, _ptr(idx, 4 * B * n_q * k, "idx"),
-        _ptr(workspace, need, "workspace", need == 0), need, _stream(stream)))
+    a.workspace = _ptr(workspace, need, "workspace", need == 0)
+    a.workspace_bytes = need
+    return _call("lca_topk", a, stream)
 
 
-def lca_topk_bf16(B, n_q, N_cap, scores, q_pos, m, n_entries, k, idx, workspace=None, stream=None):
-    need = lca_topk_workspace_size(B, n_q, N_cap, k)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
-    return check("lca_topk_bf16", lib().lca_topk_bf16(
-        B, n_q, N_cap, _ptr(scores, 2 * B * n_q * N_cap, "scores"), _ptr(q_pos, 4 * B * n_q, "q_pos"),
-        m, _ptr(n_entries, 4 * B, "n_entries"), k, _ptr(idx, 4 * B * n_q * k, "idx"),
-        _ptr(workspace, need, "workspace", need == 0), need, _stream(stream)))
+def _mqa_args(B, n_q, H, c, q_fmt, kv_fmt, N_cap, idx, k, m, n_win, pages):
+    return _lib.SparseMqaArgs(B=B, n_q=n_q, H=H, c=c, q_dtype=FMT[q_fmt], kv_dtype=FMT[kv_fmt],
+                              N_cap=N_cap, idx=idx, k=k, m=m, n_win=n_win, out_dtype=FMT["bf16"],
+                              pages=_pages_field(pages))
 
 
-def lca_sparse_mqa_workspace_size(B, n_q, H, c, kv_fmt, k, N_cap, n_win, dense) -> int:
-    return lib().lca_sparse_mqa_workspace_size(B, n_q, H, c, FMT[kv_fmt], k, N_cap, n_win, int(dense))
+def sparse_mqa_workspace_size(B, n_q, H, c, kv_fmt, k, N_cap, n_win, dense) -> int:
+    # any non-NULL idx address marks the sparse (top-k) form; it is not read
+    return lca_workspace_size("sparse_mqa", _mqa_args(B, n_q, H, c, "bf16", kv_fmt, N_cap,
+                                                      None if dense else 1, k, 1, n_win, None))
 
 
 def lca_sparse_mqa(B, n_q, H, c, q, q_fmt, cache, kv_fmt, N_cap, idx, k, q_pos, m, n_entries, win,
                    W_cap, win_origin, n_win, tau, eps, sink, rope_base, out, out_fmt, lse=None,
                    workspace=None, pages=None, stream=None):
-    dense = idx is None
-    need = lca_sparse_mqa_workspace_size(B, n_q, H, c, kv_fmt, k, N_cap, n_win, dense)
+    kvb = row_bytes(kv_fmt, c)
+    a = _mqa_args(B, n_q, H, c, q_fmt, kv_fmt, N_cap, _ptr(idx, 4 * B * n_q * k, "idx", True), k, m,
+                  n_win, pages)
+    a.q = _ptr(q, row_bytes(q_fmt, c) * B * n_q * H, "q")
+    a.cache = _ptr(cache, kvb * _cache_rows(N_cap, B, pages, m), "cache")
+    a.q_pos = _ptr(q_pos, 4 * B * n_q, "q_pos")
+    a.n_entries = _ptr(n_entries, 4 * B, "n_entries")
+    a.win = _ptr(win, kvb * B * W_cap, "win", n_win == 0)
+    a.W_cap, a.win_origin, a.tau, a.eps, a.rope_base = W_cap, win_origin, tau, eps, rope_base
+    a.sink = _ptr(sink, 4 * H, "sink", True)
+    a.out = _ptr(out, row_bytes(out_fmt, c) * B * n_q * H, "out")
+    a.out_dtype = FMT[out_fmt]
+    a.lse = _ptr(lse, 4 * B * n_q * H, "lse", True)
+    need = lca_workspace_size("sparse_mqa", a)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    kvb = row_bytes(kv_fmt, c)
-    return check("lca_sparse_mqa", lib().lca_sparse_mqa(
-        B, n_q, H, c, _ptr(q, row_bytes(q_fmt, c) * B * n_q * H, "q"), FMT[q_fmt],
-        _ptr(cache, kvb * _cache_rows(N_cap, B, pages, m), "cache"), FMT[kv_fmt], N_cap,
-        _ptr(idx, 4 * B * n_q * k, "idx", True), k, _ptr(q_pos, 4 * B * n_q, "q_pos"), m,
-        _ptr(n_entries, 4 * B, "n_entries"), _ptr(win, kvb * B * W_cap, "win", n_win == 0), W_cap,
-        win_origin, n_win, tau, eps, _ptr(sink, 4 * H, "sink", True), rope_base,
-        _ptr(out, row_bytes(out_fmt, c) * B * n_q * H, "out"), FMT[out_fmt],
-        _ptr(lse, 4 * B * n_q * H, "lse", True), _ptr(workspace, need, "workspace", need == 0), need,
-        _pages_ref(pages), _stream(stream)))
+    a.workspace = _ptr(workspace, need, "workspace", need == 0)
+    a.workspace_bytes = need
+    return _call("lca_sparse_mqa", a, stream)
 
 
 def lca_state_append(mode, m, B, c, n_win, tokC, tokZ, io_fmt, tailC, tailZ, ring, kv_fmt, P, cache,
@@ -180,29 +199,40 @@ def lca_state_append(mode, m, B, c, n_win, tokC, tokZ, io_fmt, tailC, tailZ, rin
     iob = row_bytes(io_fmt, c)
     T = 2 * m if mode == "csa" else m
     kvb = row_bytes(kv_fmt, c)
-    return check("lca_state_append", lib().lca_state_append(
-        MODE[mode], m, B, c, n_win, _ptr(tokC, iob * B, "tokC"), _ptr(tokZ, iob * B, "tokZ"),
-        FMT[io_fmt], _ptr(tailC, iob * B * T, "tailC"), _ptr(tailZ, iob * B * T, "tailZ"),
-        _ptr(ring, kvb * B * n_win, "ring"), FMT[kv_fmt], _ptr(P, 4 * T * c, "P"),
-        _ptr(cache, kvb * _cache_rows(N_cap, B, pages, m), "cache"), N_cap,
-        _ptr(n_tokens, 4 * B, "n_tokens"), _ptr(q_pos, 4 * B, "q_pos"),
-        _ptr(n_entries, 4 * B, "n_entries"), eps, rope_base, _pages_ref(pages), _stream(stream)))
+    a = _lib.StateAppendArgs(
+        mode=MODE[mode], m=m, B=B, c=c, n_win=n_win, tokC=_ptr(tokC, iob * B, "tokC"),
+        tokZ=_ptr(tokZ, iob * B, "tokZ"), io_dtype=FMT[io_fmt], tailC=_ptr(tailC, iob * B * T, "tailC"),
+        tailZ=_ptr(tailZ, iob * B * T, "tailZ"), ring=_ptr(ring, kvb * B * n_win, "ring"),
+        kv_dtype=FMT[kv_fmt], P=_ptr(P, 4 * T * c, "P"),
+        cache=_ptr(cache, kvb * _cache_rows(N_cap, B, pages, m), "cache"), N_cap=N_cap,
+        n_tokens=_ptr(n_tokens, 4 * B, "n_tokens"), q_pos=_ptr(q_pos, 4 * B, "q_pos"),
+        n_entries=_ptr(n_entries, 4 * B, "n_entries"), eps=eps, rope_base=rope_base,
+        pages=_pages_field(pages))
+    return _call("lca_state_append", a, stream)
 
 
-def lca_grouped_out_proj_workspace_size(T, n_h, c, g, d_g, d) -> int:
-    return lib().lca_grouped_out_proj_workspace_size(T, n_h, c, g, d_g, d)
+def _out_proj_args(T, n_h, c, g, d_g, d, out_fmt="bf16"):
+    return _lib.GroupedOutProjArgs(T=T, n_h=n_h, c=c, g=g, d_g=d_g, d=d, out_dtype=FMT[out_fmt])
+
+
+def grouped_out_proj_workspace_size(T, n_h, c, g, d_g, d) -> int:
+    return lca_workspace_size("grouped_out_proj", _out_proj_args(T, n_h, c, g, d_g, d))
 
 
 def lca_grouped_out_proj(T, n_h, c, g, d_g, d, o, W_g, W_o, z, out, out_fmt, workspace=None,
                          stream=None):
-    need = lca_grouped_out_proj_workspace_size(T, n_h, c, g, d_g, d)
+    a = _out_proj_args(T, n_h, c, g, d_g, d, out_fmt)
+    a.o = _ptr(o, 2 * T * n_h * c, "o")
+    a.W_g = _ptr(W_g, 2 * g * d_g * (n_h // g) * c, "W_g")
+    a.W_o = _ptr(W_o, 2 * d * g * d_g, "W_o")
+    a.z = _ptr(z, 2 * T * g * d_g, "z")
+    a.out = _ptr(out, row_bytes(out_fmt, d) * T, "out")
+    need = lca_workspace_size("grouped_out_proj", a)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=o.device)
-    return check("lca_grouped_out_proj", lib().lca_grouped_out_proj(
-        T, n_h, c, g, d_g, d, _ptr(o, 2 * T * n_h * c, "o"),
-        _ptr(W_g, 2 * g * d_g * (n_h // g) * c, "W_g"), _ptr(W_o, 2 * d * g * d_g, "W_o"),
-        _ptr(z, 2 * T * g * d_g, "z"), _ptr(out, row_bytes(out_fmt, d) * T, "out"), FMT[out_fmt],
-        _ptr(workspace, need, "workspace", need == 0), need, _stream(stream)))
+    a.workspace = _ptr(workspace, need, "workspace", need == 0)
+    a.workspace_bytes = need
+    return _call("lca_grouped_out_proj", a, stream)
 
 
 class DecodeLayerState:
@@ -241,7 +271,7 @@ class DecodeLayerState:
         self.workspace = None
 
     def workspace_size(self) -> int:
-        return lib().lca_decode_workspace_size(ctypes.byref(self.struct))
+        return lca_workspace_size("decode_step", self.struct)
 
 
 def _decode_io(layer, tokC, tokZ, q, out, out_fmt, qI=None, qI_scale=None, w=None, lse=None,

@@ -100,8 +100,8 @@ class PrefillLayer:
         out_t = torch.float32 if cfg.io_dtype == "f32" else torch.bfloat16
         self.out = torch.empty((B, n, cfg.H, c), dtype=out_t, device=device)
         self.lse = torch.empty((B, n, cfg.H), dtype=torch.float32, device=device)
-        self.ws_topk = _empty_bytes(ops.lca_topk_workspace_size(B, n, self.N_cap, cfg.k), device)
-        self.ws_mqa = _empty_bytes(ops.lca_sparse_mqa_workspace_size(
+        self.ws_topk = _empty_bytes(ops.topk_workspace_size(B, n, self.N_cap, cfg.k), device)
+        self.ws_mqa = _empty_bytes(ops.sparse_mqa_workspace_size(
             B, n, cfg.H, c, cfg.kv_dtype, cfg.k, self.N_cap, cfg.n_win, False), device)
 
     def compress(self):
@@ -134,13 +134,13 @@ class PrefillLayer:
             self.scores16 = torch.empty((self.B, self.n, self.N_cap), dtype=torch.int16,
                                         device=self.device)
             self.idx16 = torch.empty_like(self.idx)
-        ops.lca_indexer_scores_bf16(self.B, self.n, cfg.H_I, cfg.d_I, cfg.idx_dtype, self.qI,
-                                    self.qI_scale, self.kI, self.kI_scale, self.N_cap, self.w,
-                                    self.q_pos, self.m, self.n_entries, self.scores16)
+        ops.lca_indexer_scores(self.B, self.n, cfg.H_I, cfg.d_I, cfg.idx_dtype, self.qI,
+                               self.qI_scale, self.kI, self.kI_scale, self.N_cap, self.w,
+                               self.q_pos, self.m, self.n_entries, self.scores16, score_fmt="bf16")
 
     def topk_bf16(self):
-        ops.lca_topk_bf16(self.B, self.n, self.N_cap, self.scores16, self.q_pos, self.m,
-                          self.n_entries, self.cfg.k, self.idx16, self.ws_topk)
+        ops.lca_topk(self.B, self.n, self.N_cap, self.scores16, self.q_pos, self.m,
+                     self.n_entries, self.cfg.k, self.idx16, self.ws_topk, score_fmt="bf16")
 
     def attention(self):
         cfg = self.cfg

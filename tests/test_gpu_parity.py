@@ -106,7 +106,7 @@ def test_topk_bf16_select_stage_bit_exact(N, k, kind):
     q_pos = T((vis - 1).astype(np.int32).reshape(B, n_q))
     n_ent = T(np.full(B, N, np.int32))
     idx = torch.full((B, n_q, k), -7, dtype=torch.int32, device=DEV)
-    ops.lca_topk_bf16(B, n_q, N, T(s16.reshape(B, n_q, N)), q_pos, 1, n_ent, k, idx)
+    ops.lca_topk(B, n_q, N, T(s16.reshape(B, n_q, N)), q_pos, 1, n_ent, k, idx, score_fmt="bf16")
     got = host(idx).reshape(B * n_q, k)
     for r in range(B * n_q):
         want = O.topk(s[r:r + 1], [vis[r]], k)[0]
@@ -214,7 +214,7 @@ def test_indexer_scores_bf16_is_rounded_fp32(fmt, n_q):
     s16 = torch.full((B, n_q, N), 0x1234, dtype=torch.int16, device=DEV)
     args = (B, n_q, HI, dI, fmt, T(qb), qs_t, T(kb), ks_t, N, T(w), T(pos), m, T(n_ent))
     ops.lca_indexer_scores(*args, s32)
-    ops.lca_indexer_scores_bf16(*args, s16)
+    ops.lca_indexer_scores(*args, s16, score_fmt="bf16")
     g32 = host(s32)
     g16 = host(s16).view(np.uint16)
     for b in range(B):

@@ -81,7 +81,9 @@ def test_static_scratch_rejects_a_layer_too_large():
     lay.struct_size = ctypes.sizeof(_lib.DecodeLayer)
     lay.mode, lay.m, lay.B, lay.c, lay.H, lay.n_win, lay.N_cap = 0, 4, 64, 512, 64, 128, 262150
     lay.io_dtype, lay.kv_dtype, lay.k, lay.H_I, lay.d_I, lay.idx_dtype = 1, 1, 1024, 64, 128, 2
-    assert L.lca_decode_workspace_size(ctypes.byref(lay)) > _lib.LCA_STATIC_SCRATCH_BYTES
+    need = ctypes.c_size_t(0)
+    assert L.lca_workspace_size(_lib.OP["decode_step"], ctypes.byref(lay), ctypes.byref(need)) == _lib.LCA_OK
+    assert need.value > _lib.LCA_STATIC_SCRATCH_BYTES
     io = _lib.DecodeIO()
     io.struct_size = ctypes.sizeof(_lib.DecodeIO)
     FAKE = 0x1000
