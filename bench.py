@@ -13,6 +13,11 @@ Other workloads (--workload): HCA decode at 128K (batch 32), the 8-layer hybrid
 decode stack at 1M (batch 4, MXFP4 indexer, fp8+bf16 KV) and the CSA prefill
 chunk (8192 tokens on a 131072 prefix); the default line is the 1M CSA decode.
 
+Decode steps run with cold caches by default: they rotate over enough copies of
+every layer's state that more than 1 GiB (four times the 256 MB Infinity Cache)
+is touched between two uses of a copy; --warm runs every step on one copy.  The
+line's config.caches says which.
+
 Prints ONE JSON line.  The timed loop calls lca_decode_step.  For a CSA layer
 the library launches the indexer (the dominant kernel) with two HIP events
 (lca_decode_io.stage_events[1], [2]) as its dispatch's own start and end
@@ -88,6 +93,10 @@ def parse():
                          "inputs are then taken as post-RoPE)")
     ap.add_argument("--paged", action="store_true",
                     help="compressed-KV cache in 128-token pages behind a random block table")
+    ap.add_argument("--warm", action="store_true",
+                    help="decode: run every step on one copy of the layer state (warm Infinity "
+                         "Cache); by default the steps rotate over enough copies to touch more "
+                         "than 1 GiB between two uses of a copy (cold)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before warmup, run one plain device-to-device copy of MIB MiB (a "
                          "kernel of known traffic for scaling rocprofv3 byte counters)")
@@ -188,12 +197,33 @@ def run_decode(args, workload):
         ds = [gen.decode_inputs(base, extra_entries=total_steps // base.m + 2)]
         cfgs = [base]
     paged = {"seed": 1} if args.paged else None
-    layers = [pipeline.DecodeLayer(c, d, dev, paged=paged) for c, d in zip(cfgs, ds)]
     B = base.B
+
+    def touched_bytes(c, d):
+        """HBM bytes one decode step of this layer reads or writes (algorithmic)."""
+        rb = ops.row_bytes(c.kv_dtype, c.c)
+        vis = float((d["lengths"] // d["m"]).sum())
+        n = (B * c.k if d["kind"] == "C" else vis) + B * c.n_win
+        b = n * rb + 2 * B * c.H * c.c * 2
+        if d["kind"] == "C":
+            b += vis * (ops.row_bytes(c.idx_dtype, c.d_I) + (4 if c.idx_dtype == "mxfp4" else 0))
+        return b
+
+    # Cold caches: the steps rotate over n_copies copies of every layer's state,
+    # so that more than 1 GiB -- four times the 256 MB Infinity Cache -- is touched
+    # between two uses of the same copy and no step finds its inputs cached.
+    est = sum(touched_bytes(c, d) for c, d in zip(cfgs, ds))
+    n_copies = 1 if args.warm else max(2, int(np.ceil(float(1 << 30) / est)) + 1)
+    sets = [[pipeline.DecodeLayer(c, d, dev, paged=paged) for c, d in zip(cfgs, ds)]
+            for _ in range(n_copies)]
+    layers = sets[0]
     hip = HipEvents()
+    it = [0]
 
     def step(evs=None):
-        for i, (c, L) in enumerate(zip(cfgs, layers)):
+        ls = sets[it[0] % n_copies]
+        it[0] += 1
+        for i, (c, L) in enumerate(zip(cfgs, ls)):
             csa = L.mode == "csa"
             ops.lca_decode_step(L.state, L.tokC, L.tokZ, L.q, L.out, c.io_dtype,
                                 qI=L.qI if csa else None, qI_scale=L.qI_scale if csa else None,
@@ -254,7 +284,8 @@ def run_decode(args, workload):
                 hip.destroy(e)
     ms_per_step = elapsed / args.steps * 1e3
     value = B * args.steps / elapsed
-    steps_done = np.arange(args.steps) + args.warmup
+    # tokens each copy's sequences have when a timed step runs (the copies advance in turn)
+    steps_done = (np.arange(args.steps) + args.warmup) // n_copies
 
     def vis_mean(d):
         return float(np.mean([((d["lengths"] + s) // d["m"]).sum() for s in steps_done]))
@@ -308,7 +339,11 @@ def run_decode(args, workload):
         "config": {"workload": desc, "global_batch": B, "seq_len": int(base.ctx),
                    "parallelism": "single GPU",
                    **({"rope_base": args.rope_base} if args.rope_base else {}),
-                   **({"kv_cache": "paged, 128-token pages"} if args.paged else {})},
+                   **({"kv_cache": "paged, 128-token pages"} if args.paged else {}),
+                   "caches": (f"cold: steps rotate over {n_copies} copies of the layer state, "
+                              f"{(n_copies - 1) * est / 2 ** 30:.2f} GiB touched between two uses of a "
+                              "copy (the Infinity Cache holds 256 MB)") if n_copies > 1 else
+                             "warm: one copy of the layer state, steps back to back"},
         "roofline": roof,
         "dominant_kernel_us": dom_time * 1e6,
         "stages_us": {s: float(per[:, j].sum()) * 1e6 for j, s in enumerate(DECODE_STAGES)},
