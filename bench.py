@@ -43,7 +43,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 WORKLOADS = ("csa_decode_1m", "hca_decode", "hybrid_decode_1m", "csa_prefill_chunk",
-             "out_proj_decode", "out_proj_prefill")
+             "out_proj_decode", "out_proj_prefill", "hbm_ceiling")
 BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -483,6 +483,53 @@ def run_out_proj(args):
     return result, {"us_per_call": per * 1e6}
 
 
+def run_hbm_ceiling(args):
+    """The achievable HBM bandwidth on this GPU, for context beside the roofline
+    fractions (which are quoted against the 8 TB/s specification): the library's
+    read probe (every byte of a 512 MiB buffer read once; the buffer is twice the
+    256 MB Infinity Cache, so repeated reads stream from HBM) and, for
+    comparison, a 512 MiB device-to-device copy by torch (read + write)."""
+    import torch
+
+    from long_context_attention_14_amd import ops
+
+    dev = "cuda"
+    nbytes = 512 << 20
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(buf)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(args.steps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e-3 / args.steps
+
+    t_read = timed(lambda: ops.lca_read_bandwidth_probe(buf, sink))
+    t_copy = timed(lambda: dst.copy_(buf))
+    read_gbs = nbytes / t_read / 1e9
+    copy_gbs = 2 * nbytes / t_copy / 1e9
+    result = {
+        "metric": "achievable HBM bandwidth (context for the roofline fractions)", "value": read_gbs,
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": t_read * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u8", "data": "synthetic (a 512 MiB buffer)",
+        "config": {"workload": "hbm_ceiling: 512 MiB read once per step by lca_read_bandwidth_probe "
+                               "(256 workgroups x 768 threads, two 16-byte loads per lane in flight)",
+                   "global_batch": 1, "seq_len": 0, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": read_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": read_gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "read_probe_kernel"},
+        "read_us": t_read * 1e6, "copy_us": t_copy * 1e6, "copy_GBs_read_plus_write": copy_gbs,
+    }
+    return result, {"read_us": t_read * 1e6, "copy_us": t_copy * 1e6}
+
+
 def bf16_selector(layer, steps):
     """The pages' BF16-score variant of the indexer + top-k on the same chunk:
     its stage times, and the share of the float32 selection (layer.idx, from the
@@ -526,6 +573,8 @@ def main():
         result, per = run_prefill(args)
     elif args.workload.startswith("out_proj"):
         result, per = run_out_proj(args)
+    elif args.workload == "hbm_ceiling":
+        result, per = run_hbm_ceiling(args)
     else:
         result, per = run_decode(args, args.workload)
     if args.detail:

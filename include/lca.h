@@ -402,6 +402,17 @@ typedef struct lca_state_append_args {
 int lca_state_append(const lca_state_append_args* args, lca_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * lca_read_bandwidth_probe -- measurement only, not a step of the method: reads
+ * `bytes` (a multiple of 16) of device memory at buf once, with the launch
+ * shape that read fastest on MI355X (grid-stride 16-byte loads, two per lane in
+ * flight, 256 workgroups of 768 threads), and writes nothing (sink, one
+ * uint32 of device memory, is written only if the buffer's XOR equals a fixed
+ * constant).  Timing it gives the achievable HBM read bandwidth that the
+ * decode kernels' roofline fractions are set beside.
+ * ------------------------------------------------------------------------- */
+int lca_read_bandwidth_probe(const void* buf, size_t bytes, uint32_t* sink, lca_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * lca_decode_step -- one decode step of one CSA or HCA layer for B sequences:
  * lca_state_append, then (CSA) lca_indexer_scores + lca_topk, then
  * lca_sparse_mqa over the ring window (W_cap = n_win, win_origin = 0).  For

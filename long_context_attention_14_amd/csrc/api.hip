@@ -287,6 +287,15 @@ int lca_state_append(const lca_state_append_args* a, lca_stream_t stream) {
                     "lca_state_append");
 }
 
+int lca_read_bandwidth_probe(const void* buf, size_t bytes, uint32_t* sink, lca_stream_t stream) {
+  g_last_error.clear();
+  REQUIRE(bytes % 16 == 0, "bytes = %zu is not a multiple of 16", bytes);
+  if (bytes == 0) return LCA_OK;
+  REQUIRE(buf && sink, "NULL pointer");
+  return hip_status(lca::launch_read_probe(buf, bytes, sink, reinterpret_cast<hipStream_t>(stream)),
+                    "lca_read_bandwidth_probe");
+}
+
 int lca_grouped_out_proj(const lca_grouped_out_proj_args* a, lca_stream_t stream) {
   g_last_error.clear();
   if (int st = out_proj_check(a)) return st;

@@ -235,6 +235,13 @@ def lca_grouped_out_proj(T, n_h, c, g, d_g, d, o, W_g, W_o, z, out, out_fmt, wor
     return _call("lca_grouped_out_proj", a, stream)
 
 
+def lca_read_bandwidth_probe(buf, sink, stream=None):
+    """Read every byte of `buf` once (measurement of the achievable read bandwidth)."""
+    n = buf.numel() * buf.element_size()
+    return check("lca_read_bandwidth_probe", lib().lca_read_bandwidth_probe(
+        _ptr(buf, n, "buf"), n - n % 16, _ptr(sink, 4, "sink"), _stream(stream)))
+
+
 class DecodeLayerState:
     """Device buffers of one layer's decode state plus its lca_decode_layer struct."""
 
