@@ -44,8 +44,8 @@
  *     outputs.  A sequence's outputs do not depend on the other sequences'
  *     data; its selection does not depend on the batch at all, while its
  *     attention output can change in the last bits when the batch size moves
- *     the attention into another split plan (the plan follows the number of
- *     query rows; see lca_sparse_mqa).
+ *     the attention into another split plan, unless the caller fixes the
+ *     plan with split_rows (see lca_sparse_mqa).
  *   - The library keeps no mutable state of its own besides, per device and
  *     kernel, a once-only record that a kernel's LDS limit was raised and the
  *     address of lca_decode_step_static's scratch array (both set under
@@ -298,10 +298,12 @@ int lca_topk(const lca_topk_args* args, lca_stream_t stream);
  *   lse[b,t,h]  = log of that denominator.
  * A query's candidate rows (selected entries in idx order, then the window
  * oldest first) are split into chunks of whole 64-row tiles, one workgroup
- * each, whose partial results are merged by log-sum-exp in chunk order.  The
- * chunk length follows the number of query rows B*n_q (about 256 workgroups
- * in all), so a query's output bits can depend on B*n_q, never on the other
- * queries' data.
+ * each, whose partial results are merged by log-sum-exp in chunk order.  With
+ * split_rows == 0 the chunk length follows the number of query rows B*n_q
+ * (about 256 workgroups in all), so a query's output bits can depend on B*n_q,
+ * never on the other queries' data; a fixed split_rows (a multiple of 64)
+ * makes every query's bits independent of the batch ("DeepSeek-V4：迈向高效的
+ * 百万Token上下文智能", 引言: batch-invariant, deterministic kernels).
  * ------------------------------------------------------------------------- */
 typedef struct lca_sparse_mqa_args {
   size_t struct_size;   /* sizeof(lca_sparse_mqa_args) */
@@ -335,6 +337,8 @@ typedef struct lca_sparse_mqa_args {
   size_t workspace_bytes;
   lca_kv_pages pages;   /* block_table NULL: contiguous cache; else the gather reads entry e
                            through the block table */
+  int split_rows;       /* 0: automatic chunk length; else candidate rows per chunk, a multiple
+                           of 64 leaving at most 256 chunks per query (batch-invariant bits) */
 } lca_sparse_mqa_args;
 int lca_sparse_mqa(const lca_sparse_mqa_args* args, lca_stream_t stream);
 
@@ -441,6 +445,8 @@ typedef struct lca_decode_layer {
   const uint8_t* kI_scale;
   float rope_base;      /* partial RoPE base, 0 = off (as in lca_state_append / lca_sparse_mqa) */
   lca_kv_pages pages;   /* paged cache (pages.block_table == NULL: contiguous [B, N_cap, row]) */
+  int split_rows;       /* the attention's chunk length (see lca_sparse_mqa): 0 = automatic,
+                           else fixed, which makes every sequence's bits independent of B */
 } lca_decode_layer;
 
 typedef struct lca_decode_io {

@@ -67,7 +67,7 @@ class SparseMqaArgs(_Args):
                 ("win", P), ("W_cap", c_int), ("win_origin", c_int64), ("n_win", c_int),
                 ("tau", c_float), ("eps", c_float), ("sink", P), ("rope_base", c_float),
                 ("out", P), ("out_dtype", c_int), ("lse", P), ("workspace", P),
-                ("workspace_bytes", c_size_t), ("pages", KvPages)]
+                ("workspace_bytes", c_size_t), ("pages", KvPages), ("split_rows", c_int)]
 
 
 class GroupedOutProjArgs(_Args):
@@ -91,7 +91,8 @@ class DecodeLayer(ctypes.Structure):
                 ("tailC", P), ("tailZ", P), ("ring", P), ("cache", P), ("n_tokens", P), ("P", P),
                 ("sink", P), ("tau", c_float), ("eps", c_float),
                 ("k", c_int), ("H_I", c_int), ("d_I", c_int), ("idx_dtype", c_int),
-                ("kI", P), ("kI_scale", P), ("rope_base", c_float), ("pages", KvPages)]
+                ("kI", P), ("kI_scale", P), ("rope_base", c_float), ("pages", KvPages),
+                ("split_rows", c_int)]
 
 
 class DecodeIO(ctypes.Structure):

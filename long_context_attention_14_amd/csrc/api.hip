@@ -49,6 +49,17 @@ bool c_ok(int c) { return c >= 128 && c <= 1024 && c % 64 == 0 && (c / 64 == 2 |
     if (!(cond)) return fail(LCA_ERR_UNSUPPORTED, __VA_ARGS__);    \
   } while (0)
 
+// A fixed split length for the attention: 0 (the automatic plan) or a positive
+// multiple of 64 that leaves at most 256 splits per query.
+int split_rows_ok(int split_rows, int k, int N_cap, int n_win, int dense) {
+  if (split_rows == 0) return LCA_OK;
+  REQUIRE(split_rows > 0 && split_rows % 64 == 0, "split_rows = %d is not 0 or a positive multiple of 64",
+          split_rows);
+  SUPPORT(lca::mqa_splits(k, N_cap, n_win, dense, split_rows) <= lca::kMaxSplits,
+          "split_rows = %d gives more than %d splits per query", split_rows, lca::kMaxSplits);
+  return LCA_OK;
+}
+
 // Every args struct starts with its own size: NULL or another layout is rejected.
 #define CHECK_ARGS(a, T)                                                              \
   do {                                                                                \
@@ -199,12 +210,14 @@ int mqa_check(const lca_sparse_mqa_args* a, lca::KvPages* pg) {
   SUPPORT(kv_fmt_ok(a->kv_dtype), "kv_dtype %d unsupported", a->kv_dtype);
   REQUIRE(a->idx == nullptr || (a->k >= 1 && a->k <= 4096), "k = %d out of range", a->k);
   REQUIRE(a->n_win >= 0 && a->n_win <= 4096, "n_win = %d out of range", a->n_win);
+  if (int st = split_rows_ok(a->split_rows, a->idx ? a->k : 0, a->N_cap, a->n_win, a->idx == nullptr))
+    return st;
   return LCA_OK;
 }
 
 size_t mqa_ws(const lca_sparse_mqa_args* a) {
   return lca::mqa_workspace_bytes(a->B, a->n_q, a->H, a->c, a->kv_dtype, a->k, a->N_cap, a->n_win,
-                                  a->idx == nullptr);
+                                  a->idx == nullptr, a->split_rows);
 }
 
 int out_proj_check(const lca_grouped_out_proj_args* a) {
@@ -258,7 +271,7 @@ int lca_sparse_mqa(const lca_sparse_mqa_args* a, lca_stream_t stream) {
                                     a->idx, a->k, a->q_pos, a->m, a->n_entries, a->win, a->W_cap,
                                     a->win_origin, a->n_win, a->tau, a->eps, a->sink,
                                     rope_step(a->rope_base), a->out, a->out_dtype, a->lse, a->workspace,
-                                    pg, reinterpret_cast<hipStream_t>(stream)),
+                                    pg, reinterpret_cast<hipStream_t>(stream), a->split_rows),
                     "lca_sparse_mqa");
 }
 
@@ -341,7 +354,7 @@ DecodeLayout decode_layout(const lca_decode_layer* L) {
   else if (csa) off += al(lca::topk_workspace_bytes(L->B, 1, L->N_cap, L->k));
   d.mqa = off;
   off += al(lca::mqa_workspace_bytes(L->B, 1, L->H, L->c, L->kv_dtype, csa ? L->k : 0, L->N_cap,
-                                     L->n_win, csa ? 0 : 1));
+                                     L->n_win, csa ? 0 : 1, L->split_rows));
   d.total = off;
   return d;
 }
@@ -354,6 +367,8 @@ int check_layer(const lca_decode_layer* L) {
   REQUIRE(L->B >= 0 && L->N_cap >= 1 && L->m >= 1, "bad sizes");
   if (L->mode == LCA_CSA) REQUIRE(L->k >= 1 && L->k <= 4096, "k = %d out of range", L->k);
   REQUIRE(rope_ok(L->rope_base), "rope_base = %g is neither 0 nor a finite value > 1", L->rope_base);
+  const bool csa = L->mode == LCA_CSA;
+  if (int st = split_rows_ok(L->split_rows, csa ? L->k : 0, L->N_cap, L->n_win, csa ? 0 : 1)) return st;
   lca::KvPages pg;
   return kv_pages(&L->pages, L->m, L->N_cap, &pg);
 }
@@ -518,7 +533,7 @@ int decode_enqueue(const lca_decode_layer* L, const lca_decode_io* io, void* wor
                                   L->N_cap, sel, csa ? L->k : 0, q_pos, L->m, n_ent, L->ring,
                                   L->n_win, 0, L->n_win, L->tau, L->eps, L->sink,
                                   rope_step(L->rope_base), io->out, io->out_dtype, io->lse,
-                                  ws + d.mqa, pg, s),
+                                  ws + d.mqa, pg, s, L->split_rows),
                   "lca_decode_step/mqa");
   if (st != LCA_OK) return st;
   return mark(4);

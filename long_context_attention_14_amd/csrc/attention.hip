@@ -1112,12 +1112,21 @@ bool use_mfma(int H, int c, int q_fmt, int kv_fmt) {
          (kv_fmt == LCA_BF16 || kv_fmt == LCA_KV_FP8_BF16ROPE);
 }
 
+// fixed_split > 0 (a multiple of kMT): that many candidate rows per split,
+// whatever the number of query rows, so a query's result does not depend on
+// the batch; 0: the automatic plan below.
 Plan make_plan(long long rows, int H, int c, int q_fmt, int kv_fmt, int k, int N_cap, int n_win,
-               int dense) {
+               int dense, int fixed_split) {
   const int NT = (dense ? N_cap : k) + n_win;
   Plan p;
   p.mfma = use_mfma(H, c, q_fmt, kv_fmt);
   p.decode = p.mfma && q_fmt == LCA_BF16;
+  if (fixed_split > 0) {
+    p.split_rows = fixed_split < NT ? fixed_split : NT;
+    p.n_splits = (NT + fixed_split - 1) / fixed_split;
+    if (p.n_splits < 1) p.n_splits = 1;
+    return p;
+  }
   if (rows >= 512) {
     p.n_splits = 1;
     p.split_rows = NT;
@@ -1143,11 +1152,16 @@ Plan make_plan(long long rows, int H, int c, int q_fmt, int kv_fmt, int k, int N
 
 }  // namespace
 
+int mqa_splits(int k, int N_cap, int n_win, int dense, int fixed_split) {
+  const int NT = (dense ? N_cap : k) + n_win;
+  return fixed_split > 0 ? (NT + fixed_split - 1) / fixed_split : 0;
+}
+
 size_t mqa_workspace_bytes(int B, int n_q, int H, int c, int kv_fmt, int k, int N_cap, int n_win,
-                           int dense) {
+                           int dense, int fixed_split) {
   const long long rows = static_cast<long long>(B) * n_q;
   // the plan does not depend on q_fmt beyond F32/BF16, which both allow the MFMA path
-  const Plan p = make_plan(rows, H, c, LCA_BF16, kv_fmt, k, N_cap, n_win, dense);
+  const Plan p = make_plan(rows, H, c, LCA_BF16, kv_fmt, k, N_cap, n_win, dense, fixed_split);
   if (p.n_splits == 1) return 0;
   const size_t n = static_cast<size_t>(rows) * p.n_splits * H;
   return n * c * sizeof(float) + ((n * sizeof(float) + 255) & ~static_cast<size_t>(255)) + 256;
@@ -1167,11 +1181,12 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
                       int kv_fmt, int N_cap, const int32_t* idx, int k, const int32_t* q_pos, int m,
                       const int32_t* n_entries, const void* win, int W_cap, int64_t win_origin,
                       int n_win, float tau, float eps, const float* sink, double rope_step, void* out,
-                      int out_fmt, float* lse, void* ws, const KvPages& pg, hipStream_t s) {
+                      int out_fmt, float* lse, void* ws, const KvPages& pg, hipStream_t s,
+                      int fixed_split) {
   const long long rows = static_cast<long long>(B) * n_q;
   if (rows == 0) return hipSuccess;
   const int dense = idx == nullptr;
-  const Plan p = make_plan(rows, H, c, q_fmt, kv_fmt, k, N_cap, n_win, dense);
+  const Plan p = make_plan(rows, H, c, q_fmt, kv_fmt, k, N_cap, n_win, dense, fixed_split);
   float* part_o = nullptr;
   float* part_lse = nullptr;
   if (p.n_splits > 1) {

@@ -440,8 +440,13 @@ uint32_t* topk_hist_in_workspace(void* ws, int B, int n_q, int N_cap, int k);
 hipError_t launch_topk_from_hist(int B, int n_q, int N_cap, const float* scores,
                                  const int32_t* q_pos, int m, const int32_t* n_entries, int k,
                                  int32_t* idx, void* ws, hipStream_t s);
+// fixed_split: candidate rows per split (a multiple of 64), or 0 for the plan
+// that follows the number of query rows.
 size_t mqa_workspace_bytes(int B, int n_q, int H, int c, int kv_fmt, int k, int N_cap, int n_win,
-                           int dense);
+                           int dense, int fixed_split);
+// splits per query of a fixed plan (0 for the automatic one)
+int mqa_splits(int k, int N_cap, int n_win, int dense, int fixed_split);
+constexpr int kMaxSplits = 256;
 size_t out_proj_workspace_bytes(int T, int n_h, int c, int g, int d_g, int d);
 hipError_t launch_out_proj(int T, int n_h, int c, int g, int d_g, int d, const uint16_t* o,
                            const uint16_t* W_g, const uint16_t* W_o, uint16_t* z, void* out,
@@ -453,6 +458,7 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
                       int kv_fmt, int N_cap, const int32_t* idx, int k, const int32_t* q_pos, int m,
                       const int32_t* n_entries, const void* win, int W_cap, int64_t win_origin,
                       int n_win, float tau, float eps, const float* sink, double rope_step, void* out,
-                      int out_fmt, float* lse, void* ws, const KvPages& pg, hipStream_t s);
+                      int out_fmt, float* lse, void* ws, const KvPages& pg, hipStream_t s,
+                      int fixed_split = 0);
 
 }  // namespace lca

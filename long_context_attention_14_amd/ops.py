@@ -157,24 +157,27 @@ def lca_topk(B, n_q, N_cap, scores, q_pos, m, n_entries, k, idx, workspace=None,
     return _call("lca_topk", a, stream)
 
 
-def _mqa_args(B, n_q, H, c, q_fmt, kv_fmt, N_cap, idx, k, m, n_win, pages):
+def _mqa_args(B, n_q, H, c, q_fmt, kv_fmt, N_cap, idx, k, m, n_win, pages, split_rows=0):
     return _lib.SparseMqaArgs(B=B, n_q=n_q, H=H, c=c, q_dtype=FMT[q_fmt], kv_dtype=FMT[kv_fmt],
                               N_cap=N_cap, idx=idx, k=k, m=m, n_win=n_win, out_dtype=FMT["bf16"],
-                              pages=_pages_field(pages))
+                              pages=_pages_field(pages), split_rows=split_rows)
 
 
-def sparse_mqa_workspace_size(B, n_q, H, c, kv_fmt, k, N_cap, n_win, dense) -> int:
+def sparse_mqa_workspace_size(B, n_q, H, c, kv_fmt, k, N_cap, n_win, dense, split_rows=0) -> int:
     # any non-NULL idx address marks the sparse (top-k) form; it is not read
     return lca_workspace_size("sparse_mqa", _mqa_args(B, n_q, H, c, "bf16", kv_fmt, N_cap,
-                                                      None if dense else 1, k, 1, n_win, None))
+                                                      None if dense else 1, k, 1, n_win, None,
+                                                      split_rows))
 
 
 def lca_sparse_mqa(B, n_q, H, c, q, q_fmt, cache, kv_fmt, N_cap, idx, k, q_pos, m, n_entries, win,
                    W_cap, win_origin, n_win, tau, eps, sink, rope_base, out, out_fmt, lse=None,
-                   workspace=None, pages=None, stream=None):
+                   workspace=None, pages=None, split_rows=0, stream=None):
+    """split_rows: 0 for the automatic split plan, else candidate rows per split (a
+    multiple of 64): results then do not depend on the batch size."""
     kvb = row_bytes(kv_fmt, c)
     a = _mqa_args(B, n_q, H, c, q_fmt, kv_fmt, N_cap, _ptr(idx, 4 * B * n_q * k, "idx", True), k, m,
-                  n_win, pages)
+                  n_win, pages, split_rows)
     a.q = _ptr(q, row_bytes(q_fmt, c) * B * n_q * H, "q")
     a.cache = _ptr(cache, kvb * _cache_rows(N_cap, B, pages, m), "cache")
     a.q_pos = _ptr(q_pos, 4 * B * n_q, "q_pos")
@@ -247,7 +250,7 @@ class DecodeLayerState:
 
     def __init__(self, *, mode, m, B, c, H, n_win, N_cap, io_fmt, kv_fmt, tailC, tailZ, ring, cache,
                  n_tokens, P, sink=None, tau=None, eps=1e-6, k=0, H_I=0, d_I=0, idx_fmt="fp8",
-                 kI=None, kI_scale=None, rope_base=0.0, pages=None):
+                 kI=None, kI_scale=None, rope_base=0.0, pages=None, split_rows=0):
         T = 2 * m if mode == "csa" else m
         iob, kvb = row_bytes(io_fmt, c), row_bytes(kv_fmt, c)
         self.keep = [tailC, tailZ, ring, cache, n_tokens, P, sink, kI, kI_scale, pages]
@@ -265,6 +268,7 @@ class DecodeLayerState:
         s.tau = c ** -0.5 if tau is None else tau
         s.eps = eps
         s.rope_base = rope_base
+        s.split_rows = split_rows
         if pages is not None:
             s.pages = pages
         if mode == "csa":

@@ -169,7 +169,7 @@ class PrefillLayer:
 class DecodeLayer:
     """One CSA ("C") or HCA ("H") layer's decode state on the GPU."""
 
-    def __init__(self, cfg, d, device="cuda", sink=None, paged=None):
+    def __init__(self, cfg, d, device="cuda", sink=None, paged=None, split_rows=0):
         self.cfg, self.device, self.d = cfg, device, d
         kind = d["kind"]
         self.mode = "csa" if kind == "C" else "hca"
@@ -204,7 +204,8 @@ class DecodeLayer:
             io_fmt=cfg.io_dtype, kv_fmt=cfg.kv_dtype, tailC=self.tailC, tailZ=self.tailZ,
             ring=self.ring, cache=self.cache, n_tokens=self.n_tokens, P=self.P, sink=self.sink,
             tau=cfg.tau, eps=cfg.eps, k=cfg.k, H_I=cfg.H_I, d_I=cfg.d_I, idx_fmt=cfg.idx_dtype,
-            kI=self.kI, kI_scale=self.kI_scale, rope_base=cfg.rope_base, pages=pages)
+            kI=self.kI, kI_scale=self.kI_scale, rope_base=cfg.rope_base, pages=pages,
+            split_rows=split_rows)
         self.workspace = _empty_bytes(self.state.workspace_size(), device)
 
     def logical_cache(self):

@@ -199,6 +199,14 @@ def test_indexer_topk_mqa_validation(L):
     # dense HCA (idx NULL) needs its own workspace size
     st, need_dense = ws_size(L, "sparse_mqa", mqa(idx=None, k=0))
     assert st == _lib.LCA_OK and need_dense > 0
+    # a fixed split length: a positive multiple of 64, at most 256 splits per query
+    assert ws_size(L, "sparse_mqa", mqa(split_rows=100))[0] == _lib.LCA_ERR_INVALID_ARG
+    assert ws_size(L, "sparse_mqa", mqa(split_rows=-64))[0] == _lib.LCA_ERR_INVALID_ARG
+    assert ws_size(L, "sparse_mqa", mqa(idx=None, k=0, N_cap=20000, split_rows=64))[0] == \
+        _lib.LCA_ERR_UNSUPPORTED                                    # 315 splits
+    st, need_fixed = ws_size(L, "sparse_mqa", mqa(split_rows=128))  # 1152 rows: 9 splits
+    assert st == _lib.LCA_OK and need_fixed > 0
+    assert ws_size(L, "sparse_mqa", mqa(split_rows=2048)) == (_lib.LCA_OK, 0)   # one split: no partials
     # out projection
     a = _valid_args()["lca_grouped_out_proj"]
     st, need = ws_size(L, "grouped_out_proj", a)
@@ -249,6 +257,11 @@ def test_state_and_decode_validation(L):
     assert L.lca_decode_steps(ref(lay), None, 0, None, 0, None) == _lib.LCA_OK
     assert L.lca_decode_steps(ref(lay), None, -1, None, 0, None) == _lib.LCA_ERR_INVALID_ARG
     lay.pages = _lib.KvPages(None, 0, 0, 0)
+    lay.split_rows = 96
+    assert ws_size(L, "decode_step", lay)[0] == _lib.LCA_ERR_INVALID_ARG
+    lay.split_rows = 128
+    assert ws_size(L, "decode_step", lay)[0] == _lib.LCA_OK
+    lay.split_rows = 0
     lay.k = 0
     assert ws_size(L, "decode_step", lay)[0] == _lib.LCA_ERR_INVALID_ARG
 

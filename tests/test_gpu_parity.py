@@ -769,6 +769,37 @@ def test_decode_deterministic_and_batch_invariant(fmt, ctx):
         assert np.array_equal(other[name][1], runs[0][name][1]), f"{name}: depends on other sequences"
 
 
+@pytest.mark.parametrize("kind,split_rows", [("csa", 128), ("hca", 192)])
+def test_decode_fixed_split_rows_is_batch_invariant(kind, split_rows):
+    """With a fixed attention split length (lca_decode_layer.split_rows) a
+    sequence's bits do not depend on the batch size: sequence 5 alone equals
+    sequence 5 in a batch of 16 (whose automatic plan would use other splits),
+    and the batch agrees with the oracle.  CSA at 2^18 tokens takes the fused
+    selection."""
+    if kind == "csa":
+        cfg = CSA_DECODE_1M.with_(B=16, ctx=1 << 18)
+    else:
+        cfg = HCA_DECODE.with_(B=16, ctx=1 << 16)
+    d = gen.decode_inputs(cfg)
+    say(f"fixed split_rows={split_rows}: {kind} B=16 vs B=1, N_cap {d['n_cap']}")
+
+    def bits(c, dd):
+        layer = pipeline.DecodeLayer(c, dd, DEV, split_rows=split_rows)
+        layer.step()
+        torch.cuda.synchronize()
+        r = {"out": host(layer.out.view(torch.int16)), "lse": host(layer.lse)}
+        if kind == "csa":
+            r["idx"] = host(layer.idx)
+        return r
+
+    full = bits(cfg, d)
+    one = bits(cfg.with_(B=1), _seq_slice(d, cfg.B, slice(5, 6)))
+    for name in full:
+        assert np.array_equal(one[name][0], full[name][5]), f"{name}: B=1 differs from B=16"
+    _decode_parity(cfg, d, [0, 5, 15],
+                   layer=pipeline.DecodeLayer(cfg, d, DEV, split_rows=split_rows))
+
+
 def test_sink_logit():
     cfg = HCA_DECODE.with_(B=2, ctx=4096, m=128)
     say("sink")
