@@ -344,7 +344,11 @@ def run_decode(args, workload):
                               f"{(n_copies - 1) * est / 2 ** 30:.2f} GiB touched between two uses of a "
                               "copy (the Infinity Cache holds 256 MB)") if n_copies > 1 else
                              "warm: one copy of the layer state, steps back to back"},
-        "roofline": roof,
+        "roofline": {**roof,
+                     # the whole step's algorithmic bytes over its time, beside the
+                     # dominant kernel's own fraction
+                     "step_achieved": step_bytes / (ms_per_step * 1e-3) / 1e9,
+                     "step_frac": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "dominant_kernel_us": dom_time * 1e6,
         "stages_us": {s: float(per[:, j].sum()) * 1e6 for j, s in enumerate(DECODE_STAGES)},
         "step_algorithmic_GBs": step_bytes / (ms_per_step * 1e-3) / 1e9,
