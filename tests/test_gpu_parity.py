@@ -721,6 +721,19 @@ def test_hybrid_csa_decode_mxfp4_fused_selection(ctx):
     _decode_parity(cfg, d, range(cfg.B))
 
 
+def test_hybrid_hca_layer_full_size():
+    """An HCA layer of the hybrid stack at its own size (batch 4, 2^20 tokens:
+    8192 compressed entries in fp8 with bf16 RoPE dims, dense attention over all
+    of them plus the window; about 44 attention splits per row, merged 16 at a
+    time), drawn as the stack draws its layer 0."""
+    cfg = HYBRID_DECODE_1M
+    d = gen.decode_layer(cfg, "H", cfg.m_hca, gen.hybrid_lengths(cfg), layer=0)
+    lc = cfg.with_(m=d["m"])
+    say(f"hybrid HCA layer (fp8+bf16 KV) B={cfg.B} ctx={cfg.ctx} N_cap={d['n_cap']}")
+    assert d["n_cap"] > 8192
+    _decode_parity(lc, d, range(cfg.B))
+
+
 def _seq_slice(d, B, sel):
     return {k: (np.ascontiguousarray(v[sel]) if isinstance(v, np.ndarray) and v.ndim >= 1 and
                 v.shape[0] == B else v) for k, v in d.items()}
