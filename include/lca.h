@@ -417,6 +417,20 @@ int lca_state_append(const lca_state_append_args* args, lca_stream_t stream);
 int lca_read_bandwidth_probe(const void* buf, size_t bytes, uint32_t* sink, lca_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * lca_device_checks -- debug builds only (the library built with device checks,
+ * build.py --device-checks), not a step of the method: the number of violated
+ * invariants the kernels have counted on the current device since the library
+ * was loaded or last reset, over the index data they gather through -- a
+ * selected entry that is neither -1 nor visible to its query, a page id outside
+ * the pool -- and the selections they produce (min(k, vis) ascending visible
+ * entries, then -1).  The kernels treat such data as the release build does (an
+ * absent row, a skipped write); only the counting differs.  reset != 0 sets
+ * the counters to 0.  Synchronises the device.  A release build returns
+ * LCA_ERR_UNSUPPORTED with *violations = 0; NULL violations -> INVALID_ARG.
+ * ------------------------------------------------------------------------- */
+int lca_device_checks(uint64_t* violations, int reset);
+
+/* ---------------------------------------------------------------------------
  * lca_decode_step -- one decode step of one CSA or HCA layer for B sequences:
  * lca_state_append, then (CSA) lca_indexer_scores + lca_topk, then
  * lca_sparse_mqa over the ring window (W_cap = n_win, win_origin = 0).  For

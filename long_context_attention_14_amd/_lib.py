@@ -117,6 +117,7 @@ SIGNATURES = {
     "lca_grouped_out_proj": (c_int, [_ptr(GroupedOutProjArgs), P]),
     "lca_state_append": (c_int, [_ptr(StateAppendArgs), P]),
     "lca_read_bandwidth_probe": (c_int, [P, c_size_t, P, P]),
+    "lca_device_checks": (c_int, [P, c_int]),
     "lca_decode_step": (c_int, [_ptr(DecodeLayer), _ptr(DecodeIO), P, c_size_t, P]),
     "lca_decode_steps": (c_int, [_ptr(DecodeLayer), _ptr(DecodeIO), c_int, P, c_size_t, P]),
     "lca_decode_step_static": (c_int, [_ptr(DecodeLayer), _ptr(DecodeIO), P]),

@@ -47,6 +47,15 @@ SAN_FLAGS = ["-Xarch_host", "-fsanitize=address,undefined",
              "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
 
 
+# The device-check variant (a debug build): the same sources with
+# LCA_DEVICE_CHECKS=1, so that the kernels count index data that breaks the
+# interface's rules and malformed selections (lca_device_checks reads the
+# count).  Loaded only by the test that runs it in a child process.
+DBG_BUILD = os.path.join(HERE, "_build_dbg")
+DBG_LIB = os.path.join(DBG_BUILD, "liblca_dbg.so")
+DBG_FLAGS = ["-DLCA_DEVICE_CHECKS=1"]
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
@@ -61,9 +70,13 @@ def _compile(src, out_dir=BUILD, extra=()):
     return obj, warn
 
 
-def build(verbose: bool = False, sanitize: bool = False) -> str:
-    out_dir, lib = (SAN_BUILD, SAN_LIB) if sanitize else (BUILD, LIB)
-    extra = SAN_FLAGS if sanitize else []
+def build(verbose: bool = False, sanitize: bool = False, device_checks: bool = False) -> str:
+    if sanitize:
+        out_dir, lib, extra = SAN_BUILD, SAN_LIB, SAN_FLAGS
+    elif device_checks:
+        out_dir, lib, extra = DBG_BUILD, DBG_LIB, DBG_FLAGS
+    else:
+        out_dir, lib, extra = BUILD, LIB, []
     os.makedirs(out_dir, exist_ok=True)
     with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
         results = list(ex.map(lambda src: _compile(src, out_dir, extra), sources()))
@@ -95,4 +108,5 @@ def sanitizer_runtime() -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True, sanitize="--sanitize" in sys.argv))
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv,
+                device_checks="--device-checks" in sys.argv))

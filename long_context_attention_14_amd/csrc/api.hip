@@ -309,6 +309,25 @@ int lca_read_bandwidth_probe(const void* buf, size_t bytes, uint32_t* sink, lca_
                     "lca_read_bandwidth_probe");
 }
 
+int lca_device_checks(uint64_t* violations, int reset) {
+  g_last_error.clear();
+  REQUIRE(violations, "NULL pointer");
+  *violations = 0;
+  if (!LCA_DEVICE_CHECKS)
+    return fail(LCA_ERR_UNSUPPORTED, "lca_device_checks: this build has no device checks "
+                                     "(build.py --device-checks)");
+  int st = hip_status(hipDeviceSynchronize(), "lca_device_checks/hipDeviceSynchronize");
+  if (st != LCA_OK) return st;
+  unsigned long long a = 0, c = 0, t = 0;
+  const bool rs = reset != 0;
+  if ((st = hip_status(lca::dbg_violations_attention(&a, rs), "lca_device_checks/attention")) != LCA_OK ||
+      (st = hip_status(lca::dbg_violations_compress(&c, rs), "lca_device_checks/compress")) != LCA_OK ||
+      (st = hip_status(lca::dbg_violations_topk(&t, rs), "lca_device_checks/topk")) != LCA_OK)
+    return st;
+  *violations = a + c + t;
+  return LCA_OK;
+}
+
 int lca_grouped_out_proj(const lca_grouped_out_proj_args* a, lca_stream_t stream) {
   g_last_error.clear();
   if (int st = out_proj_check(a)) return st;

@@ -63,6 +63,25 @@ __device__ __forceinline__ const uint8_t* slot_row(const SlotCtx& s, int i) {
   return s.win_b + static_cast<size_t>(slot) * s.kv_row;
 }
 
+// Device checks of compressed slot i < NS whose index entry is e (and, paged,
+// page pid of e): e is -1 or a visible entry, and a visible entry's page is in
+// the pool (one call per slot and workgroup).
+__device__ __forceinline__ void dbg_slot(const SlotCtx& s, int e, int pid) {
+  const int lim = s.vis < s.N_cap ? s.vis : s.N_cap;
+  const bool vis_e = e >= 0 && e < lim;
+  if (s.idx) dbg_check(e == -1 || vis_e);
+  if (s.pg.bt && vis_e) dbg_check(pid >= 0);
+}
+__device__ __forceinline__ void dbg_slot_i(const SlotCtx& s, int i) {
+  if constexpr (LCA_DEVICE_CHECKS) {
+    if (i < s.NS) {
+      const int e = s.idx ? s.idx[i] : i;
+      const int lim = s.vis < s.N_cap ? s.vis : s.N_cap;
+      dbg_slot(s, e, (s.pg.bt && e >= 0 && e < lim) ? kv_page(s.pg, s.b, e) : 0);
+    }
+  }
+}
+
 template <int CPL>
 __global__ __launch_bounds__(kAttnThreads) void attn_generic_kernel(
     int n_q, int H, int c, const uint8_t* __restrict__ q, int q_fmt, const uint8_t* __restrict__ cache,
@@ -145,6 +164,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_generic_kernel(
     for (int r = wv; r < kRT; r += kAttnThreads / 64) {
       const int slot = base + r;
       const uint8_t* rp = slot < s_end ? slot_row(sc, slot) : nullptr;
+      if (LCA_DEVICE_CHECKS && lane == 0 && slot < s_end) dbg_slot_i(sc, slot);
       float v[CPL];
       if (rp) {
         load_row<CPL>(rp, kv_fmt, c, lane, v);
@@ -336,6 +356,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
   // row pointers of the first tile; its row loads are issued before the query
   // phase so that both latencies overlap
   if (tid < kMT) rowp_s[0][tid] = s_begin + tid < s_end ? slot_row(sc, s_begin + tid) : nullptr;
+  if (LCA_DEVICE_CHECKS && tid < kMT && s_begin + tid < s_end) dbg_slot_i(sc, s_begin + tid);
   if (rope_step != 0.0 && tid >= kMT && tid < kMT + kRopeDims / 2)
     rope_s[tid - kMT] = rope_cs(sc.t, tid - kMT, rope_step);
   __syncthreads();
@@ -453,6 +474,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     }
     const int nbase = base + kMT;
     if (tid < kMT) rowp_s[cur ^ 1][tid] = nbase + tid < s_end ? slot_row(sc, nbase + tid) : nullptr;
+    if (LCA_DEVICE_CHECKS && tid < kMT && nbase + tid < s_end) dbg_slot_i(sc, nbase + tid);
     __syncthreads();
     if (nbase < s_end) load_tile(cur ^ 1);  // in flight during this tile's compute
     // S tile of this wave (two accumulator chains)
@@ -723,6 +745,7 @@ __global__ __launch_bounds__(64 * kD8Waves) void attn_decode_kernel(
   auto row_ptr = [&](int tile, int e, int pid, uint32_t& mask8) -> const uint8_t* {
     const int i = s_begin + kMT * tile + my_r;
     const uint8_t* p = i < s_end ? slot_row_e<PAGED>(sc, i, e, pid) : nullptr;
+    if (LCA_DEVICE_CHECKS && lane < 8 && i < s_end && i < sc.NS) dbg_slot(sc, e, pid);
     mask8 = static_cast<uint32_t>(__ballot(p != nullptr)) & 0xffu;
     return p ? p : sc.cache_b;
   };
@@ -1248,5 +1271,7 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
   else merge(attn_merge4_kernel<16>);
   return hipGetLastError();
 }
+
+LCA_DBG_ACCESSOR(dbg_violations_attention)
 
 }  // namespace lca

@@ -13,6 +13,43 @@ namespace lca {
 constexpr int kWave = 64;
 
 // ---------------------------------------------------------------------------
+// Device checks (a debug build: LCA_DEVICE_CHECKS = 1, build.py --device-checks).
+// The kernels count the data they gather through that breaks the interface's
+// rules -- a selected entry that is neither -1 nor a visible entry, a page id
+// outside the pool -- and selections of the library's own that are not
+// ascending visible entries followed by -1, in a counter of each source file.
+// They handle such data exactly as the release build does (an absent row, a
+// skipped write); the release build compiles the checks away.
+#ifndef LCA_DEVICE_CHECKS
+#define LCA_DEVICE_CHECKS 0
+#endif
+[[maybe_unused]] static __device__ unsigned int g_dbg_violations;
+__device__ __forceinline__ void dbg_check(bool ok) {
+  if constexpr (LCA_DEVICE_CHECKS) {
+    if (!ok) atomicAdd(&g_dbg_violations, 1u);
+  }
+}
+// Host side of one source file's counter: its value (0 without device checks)
+// and, with reset, the counter set to 0.  Every source file that counts defines
+// one with LCA_DBG_ACCESSOR(name).
+#define LCA_DBG_ACCESSOR(name)                                                              \
+  hipError_t name(unsigned long long* v, bool reset) {                                      \
+    *v = 0;                                                                                 \
+    if constexpr (!LCA_DEVICE_CHECKS) return hipSuccess;                                    \
+    unsigned int x = 0;                                                                     \
+    hipError_t e = hipMemcpyFromSymbol(&x, HIP_SYMBOL(g_dbg_violations), sizeof(x));        \
+    if (e == hipSuccess && reset) {                                                         \
+      const unsigned int z = 0;                                                             \
+      e = hipMemcpyToSymbol(HIP_SYMBOL(g_dbg_violations), &z, sizeof(z));                   \
+    }                                                                                       \
+    *v = x;                                                                                 \
+    return e;                                                                               \
+  }
+hipError_t dbg_violations_attention(unsigned long long* v, bool reset);
+hipError_t dbg_violations_compress(unsigned long long* v, bool reset);
+hipError_t dbg_violations_topk(unsigned long long* v, bool reset);
+
+// ---------------------------------------------------------------------------
 // stored formats
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {

@@ -128,6 +128,7 @@ __global__ __launch_bounds__(kWave * kPoolWaves) void compress_kernel(
   // the entry's row in the cache (through the block table when paged), looked
   // up before the candidate loads
   const long long out_row = wv == 0 ? kv_row_of(pg, b, N_cap, first_entry + s) : -1;
+  if (LCA_DEVICE_CHECKS && wv == 0 && lane == 0) dbg_check(out_row >= 0);
   const size_t io_row = row_bytes(io_fmt, c);
   const uint8_t* Cb = C + static_cast<size_t>(b) * n_new * io_row;
   const uint8_t* Zb = Z + static_cast<size_t>(b) * n_new * io_row;
@@ -297,6 +298,7 @@ __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
   // the new entry's row in the cache (through the block table when paged),
   // looked up before the candidate loads; -1: beyond N_cap or an absent page
   const long long out_row = (wv == 0 && s < N_cap) ? kv_row_of(pg, b, N_cap, s) : -1;
+  if (LCA_DEVICE_CHECKS && wv == 0 && lane == 0 && s < N_cap) dbg_check(out_row >= 0);
   Pool pool[CPL];
   pool_init<CPL>(pool);
   auto add_row = [&](const float* rc, const float* rz, const float* bias) {
@@ -442,5 +444,7 @@ hipError_t launch_state_append(int mode, int m, int B, int c, int n_win, const v
   }
   return hipGetLastError();
 }
+
+LCA_DBG_ACCESSOR(dbg_violations_compress)
 
 }  // namespace lca

@@ -919,6 +919,34 @@ inline SelectLayout select_layout(long long rows, int N_cap) {
   L.total = off;
   return L;
 }
+// Device checks of a finished selection (debug build): row r of idx holds
+// min(k, vis) ascending visible entries, then -1.  One thread per element.
+__global__ void dbg_selection_kernel(long long rows, int n_q, int N_cap, const int32_t* __restrict__ q_pos,
+                                     int m, const int32_t* __restrict__ n_entries, int k,
+                                     const int32_t* __restrict__ idx) {
+  const long long gid = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= rows * k) return;
+  const long long row = gid / k;
+  const int i = static_cast<int>(gid % k);
+  const int vis = visible_entries(q_pos[row], m, n_entries[row / n_q], N_cap);
+  const int v = idx[gid];
+  if (i < (vis < k ? vis : k))
+    dbg_check(v >= 0 && v < vis && (i == 0 || idx[gid - 1] < v));
+  else
+    dbg_check(v == -1);
+}
+
+hipError_t dbg_selection(long long rows, int n_q, int N_cap, const int32_t* q_pos, int m,
+                         const int32_t* n_entries, int k, const int32_t* idx, hipStream_t s) {
+  if constexpr (LCA_DEVICE_CHECKS) {
+    const long long n = rows * k;
+    if (n > 0)
+      hipLaunchKernelGGL(dbg_selection_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+                         rows, n_q, N_cap, q_pos, m, n_entries, k, idx);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 static int n_segments(int N_cap) { return (N_cap + kSeg - 1) / kSeg; }
@@ -939,7 +967,7 @@ static hipError_t launch_collect_finish(long long rows, int N_cap, const ST* sco
                      m, n_entries, k, n_seg, w);
   hipLaunchKernelGGL(topk_finish_kernel, dim3(static_cast<unsigned>(rows)), dim3(kRowThreads), 0, s,
                      N_cap, n_q, q_pos, m, n_entries, k, n_seg, w, idx);
-  return hipGetLastError();
+  return dbg_selection(rows, n_q, N_cap, q_pos, m, n_entries, k, idx, s);
 }
 
 hipError_t launch_topk_from_hist(int B, int n_q, int N_cap, const float* scores,
@@ -969,7 +997,7 @@ static hipError_t launch_topk_t(int B, int n_q, int N_cap, const ST* scores, con
     const size_t lds = sizeof(uint32_t) * static_cast<size_t>(N_cap > 0 ? N_cap : 1);
     hipLaunchKernelGGL(topk_lds_kernel<ST>, dim3(static_cast<unsigned>(rows)), dim3(kRowThreads), lds,
                        s, scores, N_cap, n_q, q_pos, m, n_entries, k, idx);
-    return hipGetLastError();
+    return dbg_selection(rows, n_q, N_cap, q_pos, m, n_entries, k, idx, s);
   }
   const int n_seg = n_segments(N_cap);
   if (n_seg > kMaxSeg || k > kMaxK) return hipErrorInvalidValue;
@@ -1022,7 +1050,9 @@ hipError_t launch_select_finish(long long rows, int n_q, int N_cap, int wpr, con
   if (wpr < 1 || wpr > kSelMaxWpr || !select_supported(N_cap, k)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(select_finish_kernel, dim3(static_cast<unsigned>(rows)), dim3(kFinThreads), 0, s,
                      n_q, N_cap, wpr, q_pos, m, n_entries, k, w, idx);
-  return hipGetLastError();
+  return dbg_selection(rows, n_q, N_cap, q_pos, m, n_entries, k, idx, s);
 }
+
+LCA_DBG_ACCESSOR(dbg_violations_topk)
 
 }  // namespace lca

@@ -238,6 +238,14 @@ def lca_grouped_out_proj(T, n_h, c, g, d_g, d, o, W_g, W_o, z, out, out_fmt, wor
     return _call("lca_grouped_out_proj", a, stream)
 
 
+def lca_device_checks(reset: bool = False) -> int:
+    """Violations counted by a library built with device checks (see lca.h);
+    raises LcaError (LCA_ERR_UNSUPPORTED) on a release build."""
+    v = ctypes.c_uint64(0)
+    check("lca_device_checks", lib().lca_device_checks(ctypes.addressof(v), 1 if reset else 0))
+    return int(v.value)
+
+
 def lca_read_bandwidth_probe(buf, sink, stream=None):
     """Read every byte of `buf` once (measurement of the achievable read bandwidth)."""
     n = buf.numel() * buf.element_size()

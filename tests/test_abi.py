@@ -273,3 +273,15 @@ def test_no_cpu_fallback_in_binding():
         assert name not in src
     src = open(os.path.join(ROOT, "long_context_attention_14_amd", "_lib.py")).read()
     assert "no fallback" in src
+
+
+def test_device_checks_entry_point_is_debug_only():
+    """The release library exports lca_device_checks but has no device checks: it
+    returns LCA_ERR_UNSUPPORTED with the count set to 0, and rejects NULL."""
+    import ctypes
+    from long_context_attention_14_amd import _lib
+    L = _lib.lib()
+    v = ctypes.c_uint64(123)
+    assert L.lca_device_checks(ctypes.addressof(v), 0) == _lib.LCA_ERR_UNSUPPORTED
+    assert v.value == 0
+    assert L.lca_device_checks(None, 0) == _lib.LCA_ERR_INVALID_ARG
