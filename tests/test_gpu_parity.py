@@ -113,6 +113,45 @@ def test_topk_bf16_select_stage_bit_exact(N, k, kind):
         assert np.array_equal(got[r], want), f"row {r} vis {vis[r]}"
 
 
+def test_topk_random_shapes_bit_exact():
+    """Seeded random shapes for both score formats and both top-k paths: N from
+    1 to 300000, k from 1 to 4096, visible lengths anywhere in [0, N], scores
+    drawn from tie-heavy distributions (small integers, a few distinct values,
+    normal values rounded to a coarse grid) as well as plain normal ones; every
+    row equal to the oracle's stable top-k."""
+    rng = np.random.default_rng(2024)
+    for case in range(30):
+        N = int(rng.choice([int(rng.integers(1, 2000)), int(rng.integers(2000, 40000)),
+                            int(rng.integers(40000, 300000))]))
+        k = int(rng.integers(1, 4097))
+        rows = int(rng.integers(1, 5))
+        kind = ["ints", "few", "grid", "normal"][case % 4]
+        if kind == "ints":
+            s = rng.integers(-5, 6, (rows, N)).astype(np.float32)
+        elif kind == "few":
+            s = rng.choice(np.array([-1.5, 0.25, 3.0], np.float32), (rows, N))
+        elif kind == "grid":
+            s = (np.round(rng.standard_normal((rows, N)) * 8) / 8).astype(np.float32)
+        else:
+            s = rng.standard_normal((rows, N)).astype(np.float32)
+        fmt = "bf16" if case % 3 == 0 else "f32"
+        if fmt == "bf16":
+            s_dev = enc.to_bf16_bits(s)
+            s_ref = O.decode(s_dev, "bf16")
+        else:
+            s_dev, s_ref = s, s.astype(np.float64)
+        vis = rng.integers(0, N + 1, rows)
+        vis[0] = N
+        say(f"random topk case {case}: N={N} k={k} rows={rows} {kind} {fmt}")
+        idx = torch.full((1, rows, k), -7, dtype=torch.int32, device=DEV)
+        ops.lca_topk(1, rows, N, T(s_dev.reshape(1, rows, N)), T((vis - 1).astype(np.int32).reshape(1, rows)),
+                     1, T(np.array([N], np.int32)), k, idx, score_fmt=fmt)
+        got = host(idx).reshape(rows, k)
+        for r in range(rows):
+            want = O.topk(s_ref[r:r + 1], [int(vis[r])], k)[0]
+            assert np.array_equal(got[r], want), f"case {case} row {r}: N={N} k={k} vis={vis[r]} {kind} {fmt}"
+
+
 # ---------------------------------------------------------------------------
 # indexer
 
@@ -579,6 +618,22 @@ def test_csa_decode_rows_longer_than_one_bitmap_pass():
     d = gen.decode_inputs(cfg)
     assert d["n_cap"] > (1 << 19)
     _decode_parity(cfg, d, range(cfg.B))
+
+
+def test_csa_decode_random_batches_fused_selection():
+    """Seeded random batch sizes and context lengths in the fused selection's
+    range (more than 36864 entries per row), fp8 keys: every row's selection
+    bit-exact on the select stage (and against the oracle's when certified),
+    with every clear winner and no clear loser, and the outputs within tolerance."""
+    rng = np.random.default_rng(77)
+    for case in range(4):
+        B = int(rng.choice([1, 2, 3]))
+        ctx = int(rng.integers(150000, 420000))
+        cfg = CSA_DECODE_1M.with_(B=B, ctx=ctx, seed=100 + case)
+        say(f"random fused decode case {case}: B={B} ctx={ctx}")
+        d = gen.decode_inputs(cfg)
+        assert d["n_cap"] > 36864
+        _decode_parity(cfg, d, range(B))
 
 
 @pytest.mark.parametrize("kind", ["csa", "hca", "hybrid_csa"])
