@@ -311,7 +311,9 @@ typedef struct lca_sparse_mqa_args {
   const void* q;        /* [B, n_q, H, c] in q_dtype (F32 or BF16), not normalised */
   int q_dtype;
   const void* cache;    /* [B, N_cap, row] in kv_dtype (F32, BF16 or KV_FP8_BF16ROPE), rows
-                           already RMS-normalised (or a page pool) */
+                           already RMS-normalised (or a page pool); the few-row kernel keeps
+                           its per-chunk partial outputs, convex combinations of such rows
+                           (|value| <= sqrt(c)), in fp16 */
   int kv_dtype;
   int N_cap;
   const int32_t* idx;   /* [B, n_q, k] ascending, -1 padded (lca_topk output), or NULL (dense) */

@@ -15,6 +15,8 @@
 // partial (o, lse).  A merge kernel combines the splits of a row in a fixed
 // order (deterministic).  With a single split (prefill: many query rows) the
 // workgroup writes the final output directly.
+#include <type_traits>
+
 #include "common.h"
 
 namespace lca {
@@ -993,15 +995,18 @@ __global__ __launch_bounds__(64 * kD8Waves) void attn_decode_kernel(
     }
   }
   if (n_splits > 1) {
-    // fp32 partial rows straight from the accumulators (a lane's 32 columns of
-    // a head are 128 contiguous bytes; the merge turns the output back)
-    float* pb = part_o + (static_cast<size_t>(row) * n_splits + split) * kMH * kMC + 128 * kq + j32;
+    // fp16 partial rows straight from the accumulators (a lane's 32 columns of
+    // a head are 64 contiguous bytes; the merge turns the output back).  A
+    // split's normalised O is a convex combination of RMS-normalised rows, so
+    // |O| <= sqrt(512) and fp16 holds it to 2^-11 relative (round to nearest)
+    _Float16* pb = reinterpret_cast<_Float16*>(part_o) +
+                   (static_cast<size_t>(row) * n_splits + split) * kMH * kMC + 128 * kq + j32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int h = 32 * hg + 8 * (r >> 2) + 4 * g + (r & 3);
       const float fr = __shfl(f, 8 * (r >> 2) + 4 * g + (r & 3), 64);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) pb[h * kMC + 32 * db] = o[db][r] * fr;
+      for (int db = 0; db < 4; ++db) pb[h * kMC + 32 * db] = static_cast<_Float16>(o[db][r] * fr);
     }
     return;
   }
@@ -1047,10 +1052,11 @@ constexpr int kMaxMergeSplits = 256;
 // time with a running maximum.  Splits are combined in split order
 // (deterministic).  CH (4 .. 20) is the split count rounded up to a multiple of
 // 4, so few loads are clamped repeats of the last split; more than 20 splits go
-// 16 at a time.
-template <int CH>
+// 16 at a time.  H16: the partial rows are fp16 (the decode kernel's), else fp32.
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+template <int CH, bool H16>
 __global__ __launch_bounds__(256) void attn_merge4_kernel(
-    long long rows, int H, int c, int n_splits, const float* __restrict__ part_o,
+    long long rows, int H, int c, int n_splits, const void* __restrict__ part_o,
     const float* __restrict__ part_lse, const float* __restrict__ sink, uint8_t* __restrict__ out,
     int out_fmt, float* __restrict__ lse, const int32_t* __restrict__ q_pos, double rope_step) {
   const int c4n = c / 4;
@@ -1081,7 +1087,13 @@ __global__ __launch_bounds__(256) void attn_merge4_kernel(
       const int sp = min(s0 + u, n_splits - 1);
       const size_t base = (static_cast<size_t>(row) * n_splits + sp) * H + h;
       l[u] = part_lse[base];
-      v[u] = *reinterpret_cast<const float4*>(&part_o[base * c + d4]);
+      if (H16) {
+        const h4_t x = *reinterpret_cast<const h4_t*>(static_cast<const _Float16*>(part_o) + base * c + d4);
+        v[u] = make_float4(static_cast<float>(x[0]), static_cast<float>(x[1]), static_cast<float>(x[2]),
+                           static_cast<float>(x[3]));
+      } else {
+        v[u] = *reinterpret_cast<const float4*>(static_cast<const float*>(part_o) + base * c + d4);
+      }
     }
     float mc = m;
 #pragma unroll
@@ -1260,15 +1272,21 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
   if (rope_step != 0.0 && (static_cast<long long>(H) * (c / 4)) % 256 != 0) return hipErrorInvalidValue;
   const dim3 g2(static_cast<unsigned>((rows * H * (c / 4) + 255) / 256));
   auto merge = [&](auto kern) {
-    hipLaunchKernelGGL(kern, g2, dim3(256), 0, s, rows, H, c, p.n_splits, part_o, part_lse, sink,
-                       static_cast<uint8_t*>(out), out_fmt, lse, q_pos, rope_step);
+    hipLaunchKernelGGL(kern, g2, dim3(256), 0, s, rows, H, c, p.n_splits, static_cast<const void*>(part_o),
+                       part_lse, sink, static_cast<uint8_t*>(out), out_fmt, lse, q_pos, rope_step);
   };
-  if (p.n_splits <= 4) merge(attn_merge4_kernel<4>);
-  else if (p.n_splits <= 8) merge(attn_merge4_kernel<8>);
-  else if (p.n_splits <= 12) merge(attn_merge4_kernel<12>);
-  else if (p.n_splits <= 16) merge(attn_merge4_kernel<16>);
-  else if (p.n_splits <= 20) merge(attn_merge4_kernel<20>);
-  else merge(attn_merge4_kernel<16>);
+  // the decode kernel writes fp16 partials, the other kernels fp32
+  auto merge_ch = [&](auto h16) {
+    constexpr bool H16 = decltype(h16)::value;
+    if (p.n_splits <= 4) merge(attn_merge4_kernel<4, H16>);
+    else if (p.n_splits <= 8) merge(attn_merge4_kernel<8, H16>);
+    else if (p.n_splits <= 12) merge(attn_merge4_kernel<12, H16>);
+    else if (p.n_splits <= 16) merge(attn_merge4_kernel<16, H16>);
+    else if (p.n_splits <= 20) merge(attn_merge4_kernel<20, H16>);
+    else merge(attn_merge4_kernel<16, H16>);
+  };
+  if (p.decode) merge_ch(std::true_type{});
+  else merge_ch(std::false_type{});
   return hipGetLastError();
 }
 
