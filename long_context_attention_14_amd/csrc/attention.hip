@@ -1052,7 +1052,9 @@ constexpr int kMaxMergeSplits = 256;
 // time with a running maximum.  Splits are combined in split order
 // (deterministic).  CH (4 .. 20) is the split count rounded up to a multiple of
 // 4, so few loads are clamped repeats of the last split; more than 20 splits go
-// 16 at a time.  H16: the partial rows are fp16 (the decode kernel's), else fp32.
+// 16 at a time.  H16: the partial rows are fp16 (the decode kernel's), else
+// fp32; fp16 rows stay packed until used, which leaves registers for 32- and
+// 48-split instances.
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 template <int CH, bool H16>
 __global__ __launch_bounds__(256) void attn_merge4_kernel(
@@ -1081,19 +1083,17 @@ __global__ __launch_bounds__(256) void attn_merge4_kernel(
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s0 = 0; s0 < n_splits; s0 += CH) {
     float l[CH];
-    float4 v[CH];
+    [[maybe_unused]] float4 v[H16 ? 1 : CH];
+    [[maybe_unused]] h4_t vh[H16 ? CH : 1];  // fp16 rows kept packed until used
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
       const int sp = min(s0 + u, n_splits - 1);
       const size_t base = (static_cast<size_t>(row) * n_splits + sp) * H + h;
       l[u] = part_lse[base];
-      if (H16) {
-        const h4_t x = *reinterpret_cast<const h4_t*>(static_cast<const _Float16*>(part_o) + base * c + d4);
-        v[u] = make_float4(static_cast<float>(x[0]), static_cast<float>(x[1]), static_cast<float>(x[2]),
-                           static_cast<float>(x[3]));
-      } else {
+      if constexpr (H16)
+        vh[u] = *reinterpret_cast<const h4_t*>(static_cast<const _Float16*>(part_o) + base * c + d4);
+      else
         v[u] = *reinterpret_cast<const float4*>(static_cast<const float*>(part_o) + base * c + d4);
-      }
     }
     float mc = m;
 #pragma unroll
@@ -1112,10 +1112,16 @@ __global__ __launch_bounds__(256) void attn_merge4_kernel(
     for (int u = 0; u < CH; ++u) {
       const float wgt = l[u] == -INFINITY ? 0.f : __expf(l[u] - mc);
       den += wgt;
-      acc.x = fmaf(wgt, v[u].x, acc.x);
-      acc.y = fmaf(wgt, v[u].y, acc.y);
-      acc.z = fmaf(wgt, v[u].z, acc.z);
-      acc.w = fmaf(wgt, v[u].w, acc.w);
+      float4 vu;
+      if constexpr (H16)
+        vu = make_float4(static_cast<float>(vh[u][0]), static_cast<float>(vh[u][1]),
+                         static_cast<float>(vh[u][2]), static_cast<float>(vh[u][3]));
+      else
+        vu = v[u];
+      acc.x = fmaf(wgt, vu.x, acc.x);
+      acc.y = fmaf(wgt, vu.y, acc.y);
+      acc.z = fmaf(wgt, vu.z, acc.z);
+      acc.w = fmaf(wgt, vu.w, acc.w);
     }
     m = mc;
   }
@@ -1283,6 +1289,8 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
     else if (p.n_splits <= 12) merge(attn_merge4_kernel<12, H16>);
     else if (p.n_splits <= 16) merge(attn_merge4_kernel<16, H16>);
     else if (p.n_splits <= 20) merge(attn_merge4_kernel<20, H16>);
+    else if (H16 && p.n_splits <= 32) merge(attn_merge4_kernel<32, H16>);
+    else if (H16 && p.n_splits <= 48) merge(attn_merge4_kernel<48, H16>);
     else merge(attn_merge4_kernel<16, H16>);
   };
   if (p.decode) merge_ch(std::true_type{});
