@@ -661,8 +661,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
 //    i < 8, through row pointers held by lanes 0..7; the next tile's rows are in
 //    flight in registers during a tile's compute, and the row indices of the
 //    tile after it are loaded one tile ahead.  Empty rows (outside the split,
-//    past the visible entries, before the window start) are loaded from a valid
-//    row, staged as zeros and masked to -inf in S.  The partial S^T of a tile
+//    past the visible entries, before the window start) load the query row,
+//    are staged as zeros and masked to -inf in S.  The partial S^T of a tile
 //    goes through the other KV buffer, which is free at that point.
 //  * With two waves per SIMD one wave's barrier and LDS waits overlap the other
 //    wave's MFMA and VALU work (four waves of twice the work each took 9% longer).
@@ -744,12 +744,15 @@ __global__ __launch_bounds__(64 * kD8Waves) void attn_decode_kernel(
   auto page_of = [&](int e) -> int {
     return kv_page(sc.pg, b, min(max(e, 0), sc.N_cap - 1));
   };
+  // empty rows read the query row instead (64 KiB, always there and already in
+  // the cache), so that no load depends on the cache or the window holding a row
+  const uint8_t* q_bytes = reinterpret_cast<const uint8_t*>(q + static_cast<size_t>(row) * kMH * kMC);
   auto row_ptr = [&](int tile, int e, int pid, uint32_t& mask8) -> const uint8_t* {
     const int i = s_begin + kMT * tile + my_r;
     const uint8_t* p = i < s_end ? slot_row_e<PAGED>(sc, i, e, pid) : nullptr;
     if (LCA_DEVICE_CHECKS && lane < 8 && i < s_end && i < sc.NS) dbg_slot(sc, e, pid);
     mask8 = static_cast<uint32_t>(__ballot(p != nullptr)) & 0xffu;
-    return p ? p : sc.cache_b;
+    return p ? p : q_bytes;
   };
   const int lane_off = KVFMT == LCA_BF16 ? lane * 16 : (lane < 56 ? lane * 8 : 448 + (lane - 56) * 16);
   uint4 raw[8];

@@ -356,12 +356,16 @@ def _mqa_case(case, rng):
         B, N_cap, k, m = 2, 700, 0, 128
         q_pos = np.array([300 * 128 + 5, 700 * 128 + 900])
         n_entries = np.array([300, 700])
+    elif case.endswith("window_only"):     # no compressed entries at all (N_cap = 0), and
+        B, N_cap, k, m = 3, 0, 0, 4        # windows that start before position 0
+        q_pos = np.array([5, 70, 3000])
+        n_entries = np.zeros(B, np.int64)
     else:                                  # CSA: k = 200 selected, -1 padded
         B, N_cap, k, m = 3, 5000, 200, 4
         q_pos = np.array([5, 4000, 20000]) + (2 ** 21 if rope else 0)
         n_entries = np.array([2, 1000, 5000])
     vis = np.minimum(np.minimum((q_pos + 1) // m, n_entries), N_cap)
-    cache_f = rng.standard_normal((B, N_cap, c))
+    cache_f = rng.standard_normal((B, max(N_cap, 1), c))   # one unused row when N_cap = 0
     win_f = rng.standard_normal((B, n_win, c))
     q_f = rng.standard_normal((B, H, c))
     if case == "rows300":
@@ -399,8 +403,8 @@ def _mqa_case(case, rng):
                 n_win=n_win, tau=tau, eps=eps, rope=rope, q_fmt=q_fmt)
 
 
-@pytest.mark.parametrize("case", ["bf16_sparse", "fp8_sink", "bf16_dense", "rows300",
-                                  "bf16_sparse_rope", "fp8_sink_rope", "rows300_rope",
+@pytest.mark.parametrize("case", ["bf16_sparse", "fp8_sink", "bf16_dense", "rows300", "window_only",
+                                  "fp8_window_only", "bf16_sparse_rope", "fp8_sink_rope", "rows300_rope",
                                   "rows300_f32q_rope", "bf16_sparse_f32q_rope", "bf16_sparse_c128_rope",
                                   "rows300_c128_rope"])
 def test_sparse_mqa_decode_shapes(case):
