@@ -1058,19 +1058,23 @@ constexpr int kMaxMergeSplits = 256;
 // 16 at a time.  H16: the partial rows are fp16 (the decode kernel's), else
 // fp32; fp16 rows stay packed until used, which leaves registers for 32- and
 // 48-split instances.
+// One-wave workgroups: a small batch's merge (4 query rows: 32K threads) then
+// spreads over every CU instead of half of them (256-thread groups made the
+// hybrid stack's merges 2.4 us slower per step).
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+constexpr int kMergeThreads = 64;
 template <int CH, bool H16>
-__global__ __launch_bounds__(256) void attn_merge4_kernel(
+__global__ __launch_bounds__(kMergeThreads) void attn_merge4_kernel(
     long long rows, int H, int c, int n_splits, const void* __restrict__ part_o,
     const float* __restrict__ part_lse, const float* __restrict__ sink, uint8_t* __restrict__ out,
     int out_fmt, float* __restrict__ lse, const int32_t* __restrict__ q_pos, double rope_step) {
   const int c4n = c / 4;
-  const long long gid = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  const long long gid = static_cast<long long>(blockIdx.x) * kMergeThreads + threadIdx.x;
   // the angles of -t for the output's turn back: a block covers one query row
   // (H * c / 4 is a multiple of 256, checked by the launcher)
   __shared__ float2 rope_s[kRopeDims / 2];
   if (rope_step != 0.0) {
-    const long long row0 = static_cast<long long>(blockIdx.x) * 256 / (static_cast<long long>(H) * c4n);
+    const long long row0 = static_cast<long long>(blockIdx.x) * kMergeThreads / (static_cast<long long>(H) * c4n);
     if (threadIdx.x < kRopeDims / 2)
       rope_s[threadIdx.x] = rope_cs(-static_cast<long long>(q_pos[row0]), threadIdx.x, rope_step);
     __syncthreads();
@@ -1279,9 +1283,9 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
   if (rope_step != 0.0 && (static_cast<long long>(H) * (c / 4)) % 256 != 0) return hipErrorInvalidValue;
-  const dim3 g2(static_cast<unsigned>((rows * H * (c / 4) + 255) / 256));
+  const dim3 g2(static_cast<unsigned>((rows * H * (c / 4) + kMergeThreads - 1) / kMergeThreads));
   auto merge = [&](auto kern) {
-    hipLaunchKernelGGL(kern, g2, dim3(256), 0, s, rows, H, c, p.n_splits, static_cast<const void*>(part_o),
+    hipLaunchKernelGGL(kern, g2, dim3(kMergeThreads), 0, s, rows, H, c, p.n_splits, static_cast<const void*>(part_o),
                        part_lse, sink, static_cast<uint8_t*>(out), out_fmt, lse, q_pos, rope_step);
   };
   // the decode kernel writes fp16 partials, the other kernels fp32
