@@ -16,7 +16,9 @@ chunk (8192 tokens on a 131072 prefix); the default line is the 1M CSA decode.
 Decode steps run with cold caches by default: they rotate over enough copies of
 every layer's state that more than 1 GiB (four times the 256 MB Infinity Cache)
 is touched between two uses of a copy; --warm runs every step on one copy.  The
-line's config.caches says which.
+line's config.caches says which.  Before the warmup every page of every copy is
+read once (so that no copy is used for the first time inside the timed region)
+and then 1 GiB of scratch memory is written, which empties the caches again.
 
 Prints ONE JSON line.  The timed loop calls lca_decode_step.  For a CSA layer
 the library launches the indexer (the dominant kernel) with two HIP events
@@ -84,7 +86,13 @@ def parse():
                          "design notes")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--stamp-every", type=int, default=4,
+                    help="stamp the dominant kernel (or stage) on every n-th timed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-touch", action="store_true",
+                    help="decode: skip the pass that makes every copy of the layer state resident "
+                         "(one read per 4 KiB page, then a 1 GiB write that empties the caches) "
+                         "before the warmup")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--detail", default=None, help="write per-stage timings (JSON) to this file")
@@ -156,6 +164,35 @@ def _calibrate_copy(mib, dev):
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
+
+
+def _touch_pages(objs, dev):
+    """Make the inputs resident before the untimed warmup: read one byte of every
+    4 KiB of every device tensor the layer objects hold (the decode workloads
+    rotate over up to 27 copies of the layer state, most of which a short warmup
+    never reaches, so their first use, with its page-table walks, fell inside the
+    timed region), then write 1 GiB of scratch memory so that the caches are cold
+    again when the steps start."""
+    import torch
+    seen = set()
+
+    def visit(o, depth=0):
+        if isinstance(o, torch.Tensor):
+            if o.is_cuda and o.numel() and o.data_ptr() not in seen:
+                seen.add(o.data_ptr())
+                b = o.view(-1).view(torch.uint8) if o.is_contiguous() else None
+                if b is not None:
+                    b[::4096].sum()
+        elif isinstance(o, (list, tuple)):
+            for x in o:
+                visit(x, depth)
+        elif hasattr(o, "__dict__") and depth < 3:
+            for x in vars(o).values():
+                visit(x, depth + 1)
+    visit(objs)
+    scratch = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)  # > 4x the 256 MB Infinity Cache
+    torch.cuda.synchronize()
+    del scratch
 
 
 def _indexer_traffic():
@@ -231,6 +268,8 @@ def run_decode(args, workload):
                                 workspace=L.workspace, stage_events=evs[i] if evs else None)
 
     _calibrate_copy(args.calibrate_copy, dev)
+    if not args.no_touch:
+        _touch_pages(sets, dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -239,7 +278,7 @@ def run_decode(args, workload):
     csa_layers = [i for i, L in enumerate(layers) if L.mode == "csa"]
     dom_layers = csa_layers if csa_layers else [0]
     dom = (1, 2) if csa_layers else (3, 4)          # indexer or attention stage
-    SAMPLE = 4  # stamped steps: the event packets themselves cost GPU time
+    SAMPLE = args.stamp_every  # stamped steps: the event packets themselves cost GPU time
     sampled = {}
     for i in range(0, args.steps, SAMPLE):
         sampled[i] = {li: (hip.create(), hip.create()) for li in dom_layers}
@@ -342,7 +381,9 @@ def run_decode(args, workload):
                    **({"kv_cache": "paged, 128-token pages"} if args.paged else {}),
                    "caches": (f"cold: steps rotate over {n_copies} copies of the layer state, "
                               f"{(n_copies - 1) * est / 2 ** 30:.2f} GiB touched between two uses of a "
-                              "copy (the Infinity Cache holds 256 MB)") if n_copies > 1 else
+                              "copy (the Infinity Cache holds 256 MB)"
+                              + ("" if args.no_touch else "; every copy made resident and the caches "
+                                 "emptied before the warmup")) if n_copies > 1 else
                              "warm: one copy of the layer state, steps back to back"},
         "roofline": {**roof,
                      # the whole step's algorithmic bytes over its time, beside the
