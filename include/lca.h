@@ -441,7 +441,12 @@ int lca_device_checks(uint64_t* violations, int reset);
  * out the entries that can still be among the row's k largest, and a finish
  * pass selects the k largest among them -- the indices lca_topk returns over
  * the scores lca_indexer_scores writes for the same inputs.  Shorter rows go
- * through a score array in the workspace and lca_topk's path.
+ * through a score array in the workspace and lca_topk's path.  An HCA step
+ * whose attention runs on the few-row decode kernel (bf16 io, H = 64, c = 512,
+ * fewer than 512 sequences) does the state append inside the attention launch:
+ * the workgroups that hold the new window row and the entry a completed block
+ * makes write them, and use them for this step's query, and the split merge
+ * advances n_tokens -- the bits of lca_state_append followed by lca_sparse_mqa.
  * ------------------------------------------------------------------------- */
 typedef struct lca_decode_layer {
   size_t struct_size;   /* sizeof(lca_decode_layer) */
@@ -483,7 +488,8 @@ typedef struct lca_decode_io {
    * kernel's duration; stamped dispatches still leave a few microseconds idle on
    * either side, so a timing caller stamps a sample of its steps); [3] is
    * recorded after the top-k and [4] after the attention.  An HCA layer records
-   * [1], [2] and [3] right after the append. */
+   * [1], [2] and [3] right after the append (right after [0] when the append
+   * runs inside the attention launch). */
   void* stage_events[5];
 } lca_decode_io;
 

@@ -510,12 +510,31 @@ int decode_enqueue(const lca_decode_layer* L, const lca_decode_io* io, void* wor
     zero_words = hist ? lca::topk_hist_words(L->B) : 0;
   }
   if ((st = mark(0)) != LCA_OK) return st;
-  st = hip_status(lca::launch_state_append(L->mode, L->m, L->B, L->c, L->n_win, io->tokC, io->tokZ,
-                                           L->io_dtype, L->tailC, L->tailZ, L->ring, L->kv_dtype,
-                                           L->P, L->cache, L->N_cap, L->n_tokens, q_pos, n_ent,
-                                           L->eps, rope_step(L->rope_base), pg, s, hist, zero_words),
-                  "lca_decode_step/append");
-  if (st != LCA_OK) return st;
+  // HCA steps whose attention runs on the few-row decode kernel append the token
+  // inside that launch (same rows, entries and counts, one launch fewer)
+  const bool fused_append = !csa && L->io_dtype == LCA_BF16 &&
+                            lca::mqa_can_append(L->B, L->H, L->c, L->io_dtype, L->kv_dtype, L->N_cap,
+                                                L->n_win, L->split_rows);
+  lca::DecodeAppend ap{};
+  if (fused_append) {
+    ap.tokC = static_cast<const uint8_t*>(io->tokC);
+    ap.tokZ = static_cast<const uint8_t*>(io->tokZ);
+    ap.tailC = static_cast<uint8_t*>(L->tailC);
+    ap.tailZ = static_cast<uint8_t*>(L->tailZ);
+    ap.P = L->P;
+    ap.ring = static_cast<uint8_t*>(L->ring);
+    ap.cache = static_cast<uint8_t*>(L->cache);
+    ap.n_tokens = L->n_tokens;
+    ap.q_pos = q_pos;
+    ap.n_entries = n_ent;
+  } else {
+    st = hip_status(lca::launch_state_append(L->mode, L->m, L->B, L->c, L->n_win, io->tokC, io->tokZ,
+                                             L->io_dtype, L->tailC, L->tailZ, L->ring, L->kv_dtype,
+                                             L->P, L->cache, L->N_cap, L->n_tokens, q_pos, n_ent,
+                                             L->eps, rope_step(L->rope_base), pg, s, hist, zero_words),
+                    "lca_decode_step/append");
+    if (st != LCA_OK) return st;
+  }
   const int32_t* sel = nullptr;
   if (csa) {
     float* scores = fused ? nullptr : reinterpret_cast<float*>(ws + d.scores);
@@ -552,7 +571,7 @@ int decode_enqueue(const lca_decode_layer* L, const lca_decode_io* io, void* wor
                                   L->N_cap, sel, csa ? L->k : 0, q_pos, L->m, n_ent, L->ring,
                                   L->n_win, 0, L->n_win, L->tau, L->eps, L->sink,
                                   rope_step(L->rope_base), io->out, io->out_dtype, io->lse,
-                                  ws + d.mqa, pg, s, L->split_rows),
+                                  ws + d.mqa, pg, s, L->split_rows, fused_append ? &ap : nullptr),
                   "lca_decode_step/mqa");
   if (st != LCA_OK) return st;
   return mark(4);

@@ -18,6 +18,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "pool.h"
 
 namespace lca {
 namespace {
@@ -692,16 +693,29 @@ __device__ __forceinline__ const uint8_t* slot_row_e(const SlotCtx& s, int i, in
 
 constexpr int kD8Waves = 8;  // waves per decode workgroup
 
-template <int KVFMT, bool PAGED>
+// APPEND (HCA decode steps, dense rows, n_q = 1): the step's state append runs
+// here (DecodeAppend).  Every workgroup takes the query position p from
+// n_tokens.  The one that holds the window slot of position p RMS-normalises
+// the new token into the ring and writes its tail rows and the step's q_pos and
+// n_entries; the one that holds entry (p+1)/m - 1, when the token completes a
+// block, pools the block into the cache (the append's slot split and
+// combination order, so the same bits).  Both keep the row they made in LDS
+// and put it in place of the row loaded for that slot (which they cannot wait
+// to read back).  The pooling's scratch is the second KV buffer, free before
+// the first tile.
+template <int KVFMT, bool PAGED, bool APPEND>
 __global__ __launch_bounds__(64 * kD8Waves) void attn_decode_kernel(
     int n_q, const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int N_cap,
     const int32_t* __restrict__ idx, int k, const int32_t* __restrict__ q_pos, int m,
     const int32_t* __restrict__ n_entries, const uint8_t* __restrict__ win, int W_cap,
     long long win_origin, int n_win, float tau, float eps, const float* __restrict__ sink,
     double rope_step, int n_splits, int split_rows, uint8_t* __restrict__ out, int out_fmt,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse, KvPages pg) {
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse, KvPages pg,
+    DecodeAppend ap) {
   constexpr int NW = kD8Waves;
   __shared__ __attribute__((aligned(16))) uint16_t kv_s[2][kMT * kQS];
+  // APPEND: the stored bytes of the new window row [0] and of the new entry [1]
+  __shared__ __attribute__((aligned(16))) uint4 app_s[APPEND ? 2 : 1][APPEND ? kMC * 2 / 16 : 1];
   __shared__ float2 rope_s[kRopeDims / 2];  // (cos, sin) of the query position's angles
   __shared__ __attribute__((aligned(16))) uint16_t p_s[kMH * kPS];
   __shared__ float ps_s[4][kMH];  // per dim quarter: query sums of squares; then P row sums
@@ -767,7 +781,8 @@ __global__ __launch_bounds__(64 * kD8Waves) void attn_decode_kernel(
       raw[i] = ldg16(reinterpret_cast<const uint8_t*>(pi) + lane_off);
     }
   };
-  auto stage = [&](int buf, uint32_t mask8) {
+  int sp_new = -1, sp_ent = -1;  // APPEND: the slots whose rows this workgroup made
+  auto stage = [&](int buf, uint32_t mask8, int tile) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       uint4 v = raw[i];
@@ -779,6 +794,28 @@ __global__ __launch_bounds__(64 * kD8Waves) void attn_decode_kernel(
       if (!((mask8 >> i) & 1u)) v = make_uint4(0, 0, 0, 0);
       *reinterpret_cast<uint4*>(&kv_s[buf][(w + NW * i) * kQS + lane * 8]) = v;
     }
+    if constexpr (APPEND) {
+      // the rows this workgroup made replace what was loaded for their slots
+      // (the same wave staged that row just above; the stored bytes are read at
+      // lane_off and widened as a loaded row is)
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int sp = a ? sp_ent : sp_new;
+        const int r = sp - (s_begin + kMT * tile);
+        if (sp >= 0 && r >= 0 && r < kMT && (r & (NW - 1)) == w) {
+          const uint8_t* src = reinterpret_cast<const uint8_t*>(app_s[a]) + lane_off;
+          uint4 v;
+          if (KVFMT == LCA_BF16 || lane >= 56) {
+            v = *reinterpret_cast<const uint4*>(src);
+          } else {
+            const uint2 h = *reinterpret_cast<const uint2*>(src);
+            v = make_uint4(fp8x2_to_bf16x2<false>(h.x), fp8x2_to_bf16x2<true>(h.x),
+                           fp8x2_to_bf16x2<false>(h.y), fp8x2_to_bf16x2<true>(h.y));
+          }
+          *reinterpret_cast<uint4*>(&kv_s[buf][r * kQS + lane * 8]) = v;
+        }
+      }
+    }
     if (lane == 0) vm_s[buf][w] = mask8;
   };
 
@@ -788,8 +825,13 @@ __global__ __launch_bounds__(64 * kD8Waves) void attn_decode_kernel(
   const int e_first = entry(0);
   int e_next = entry(1);
   int e_next2 = PAGED ? entry(2) : 0;
-  sc.t = q_pos[row];
-  sc.vis = visible_entries(sc.t, m, n_entries[b], N_cap);
+  if constexpr (APPEND) {
+    sc.t = ap.n_tokens[b];  // the new token's position p (n_q = 1: row == b)
+    sc.vis = visible_entries(sc.t, m, sc.t < 0 ? 0 : min((sc.t + 1) / m, N_cap), N_cap);
+  } else {
+    sc.t = q_pos[row];
+    sc.vis = visible_entries(sc.t, m, n_entries[b], N_cap);
+  }
   uint4 qf[kMC / 64];
   {
     const uint16_t* qh = q + (static_cast<size_t>(row) * kMH + head) * kMC + 128 * kq + 8 * g;
@@ -803,6 +845,63 @@ __global__ __launch_bounds__(64 * kD8Waves) void attn_decode_kernel(
     pid_next = page_of(e_next);
   }
   load_rows(row_ptr(0, e_first, pid_first, mask_cur));
+
+  if constexpr (APPEND) {
+    // the state append of the step (while the first tile's rows are in flight)
+    const int p = sc.t;
+    const int s_new = p >= 0 && (p + 1) % m == 0 ? (p + 1) / m - 1 : -1;  // the entry p completes
+    if (p >= 0 && NT - 1 >= s_begin && NT - 1 < s_end) sp_new = NT - 1;      // window slot of p
+    if (s_new >= 0 && s_new < N_cap && s_new >= s_begin && s_new < s_end) sp_ent = s_new;
+    constexpr int CPL = kMC / kWave;
+    const size_t io_row = row_bytes(LCA_BF16, kMC);
+    float tc[CPL], tz[CPL];
+    if (sp_new >= 0 || sp_ent >= 0) {
+      load_row<CPL>(ap.tokC + static_cast<size_t>(b) * io_row, LCA_BF16, kMC, lane, tc);
+      load_row<CPL>(ap.tokZ + static_cast<size_t>(b) * io_row, LCA_BF16, kMC, lane, tz);
+    }
+    const float2 rope_p = rope_step != 0.0 ? rope_cs_lane(p, rope_step) : make_float2(1.f, 0.f);
+    uint8_t* tCb = ap.tailC + static_cast<size_t>(b) * m * io_row;
+    uint8_t* tZb = ap.tailZ + static_cast<size_t>(b) * m * io_row;
+    if (sp_new >= 0) {
+      if (w == 0) {  // window row: into the ring and into LDS
+        float u[CPL];
+        window_row<CPL>(tc, kMC, eps, u);
+        if (rope_step != 0.0) rope_lane<CPL>(u, lane, kMC, rope_p);
+        store_row<CPL>(ap.ring + (static_cast<size_t>(b) * W_cap + p % n_win) * sc.kv_row, KVFMT, kMC,
+                       lane, u);
+        store_row<CPL>(app_s[0], KVFMT, kMC, lane, u);
+        if (lane == 0) {
+          ap.q_pos[b] = p;
+          ap.n_entries[b] = min((p + 1) / m, N_cap);
+        }
+      } else if (w == 1) {  // the token's tail rows
+        store_row<CPL>(tCb + static_cast<size_t>(p % m) * io_row, LCA_BF16, kMC, lane, tc);
+      } else if (w == 2) {
+        store_row<CPL>(tZb + static_cast<size_t>(p % m) * io_row, LCA_BF16, kMC, lane, tz);
+      }
+    }
+    if (sp_ent >= 0) {  // the completed block, pooled by all eight waves
+      Pool pool[CPL];
+      pool_init<CPL>(pool);
+      pool_tail<CPL, LCA_BF16>(0, m, m, 0, s_new, p % m, tCb, tZb, ap.P, kMC, lane, w, tc, tz, pool);
+      int order[kPoolWaves];
+#pragma unroll
+      for (int x = 0; x < kPoolWaves; ++x) order[x] = x;
+      static_assert(kPoolWaves == NW, "one pooling wave per decode wave");
+      static_assert(sizeof(float) * kPoolWaves * 3 * CPL * kWave <= sizeof(kv_s[1]), "pool scratch");
+      auto part = reinterpret_cast<float (*)[3][CPL][kWave]>(&kv_s[1][0]);
+      float e[CPL];
+      if (pool_combine_norm<CPL>(part, pool, order, w, lane, kMC, eps, e)) {
+        if (rope_step != 0.0) rope_lane<CPL>(e, lane, kMC, rope_p);  // the entry's last token is p
+        const long long out_row = kv_row_of(pg, b, N_cap, s_new);
+        if (LCA_DEVICE_CHECKS && lane == 0) dbg_check(out_row >= 0);
+        if (out_row >= 0)
+          store_row<CPL>(ap.cache + static_cast<size_t>(out_row) * sc.kv_row, KVFMT, kMC, lane, e);
+        store_row<CPL>(app_s[1], KVFMT, kMC, lane, e);
+      }
+    }
+    // app_s is read after the query's normalisation barrier below
+  }
 
   // RMSNorm of the query over its 512 dims: lane halves and the four waves of a
   // head half hold an eighth each; the wave sums go through LDS
@@ -853,7 +952,7 @@ __global__ __launch_bounds__(64 * kD8Waves) void attn_decode_kernel(
 
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
-    stage(buf, mask_cur);
+    stage(buf, mask_cur, t);
     uint32_t mask_next = 0;
     const uint8_t* p_next = row_ptr(t + 1, e_next, pid_next, mask_next);
     if constexpr (PAGED) {
@@ -1017,6 +1116,9 @@ __global__ __launch_bounds__(64 * kD8Waves) void attn_decode_kernel(
   // every wave is done with them), then contiguous 16-byte stores
   float* ost = reinterpret_cast<float*>(&kv_s[0][0]);
   __syncthreads();
+  // APPEND with one split: no merge follows, and every wave read n_tokens
+  // before the barriers behind it
+  if (APPEND && tid == 0 && sc.t >= 0) ap.n_tokens[b] = sc.t + 1;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int h = 32 * hg + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -1067,7 +1169,8 @@ template <int CH, bool H16>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge4_kernel(
     long long rows, int H, int c, int n_splits, const void* __restrict__ part_o,
     const float* __restrict__ part_lse, const float* __restrict__ sink, uint8_t* __restrict__ out,
-    int out_fmt, float* __restrict__ lse, const int32_t* __restrict__ q_pos, double rope_step) {
+    int out_fmt, float* __restrict__ lse, const int32_t* __restrict__ q_pos, double rope_step,
+    int32_t* __restrict__ advance) {
   const int c4n = c / 4;
   const long long gid = static_cast<long long>(blockIdx.x) * kMergeThreads + threadIdx.x;
   // the angles of -t for the output's turn back: a block covers one query row
@@ -1079,6 +1182,9 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge4_kernel(
       rope_s[threadIdx.x] = rope_cs(-static_cast<long long>(q_pos[row0]), threadIdx.x, rope_step);
     __syncthreads();
   }
+  // a decode step whose attention appended the token: n_tokens[row] += 1 (no
+  // other launch of the step reads it any more; a negative count stays)
+  if (advance && gid < rows && advance[gid] >= 0) advance[gid] += 1;
   if (gid >= rows * H * c4n) return;
   const long long rh = gid / c4n;
   const int d4 = static_cast<int>(gid % c4n) * 4;
@@ -1200,6 +1306,11 @@ Plan make_plan(long long rows, int H, int c, int q_fmt, int kv_fmt, int k, int N
 
 }  // namespace
 
+bool mqa_can_append(long long rows, int H, int c, int q_fmt, int kv_fmt, int N_cap, int n_win,
+                    int fixed_split) {
+  return n_win >= 1 && make_plan(rows, H, c, q_fmt, kv_fmt, 0, N_cap, n_win, 1, fixed_split).decode;
+}
+
 int mqa_splits(int k, int N_cap, int n_win, int dense, int fixed_split) {
   const int NT = (dense ? N_cap : k) + n_win;
   return fixed_split > 0 ? (NT + fixed_split - 1) / fixed_split : 0;
@@ -1230,11 +1341,17 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
                       const int32_t* n_entries, const void* win, int W_cap, int64_t win_origin,
                       int n_win, float tau, float eps, const float* sink, double rope_step, void* out,
                       int out_fmt, float* lse, void* ws, const KvPages& pg, hipStream_t s,
-                      int fixed_split) {
+                      int fixed_split, const DecodeAppend* append) {
   const long long rows = static_cast<long long>(B) * n_q;
   if (rows == 0) return hipSuccess;
   const int dense = idx == nullptr;
   const Plan p = make_plan(rows, H, c, q_fmt, kv_fmt, k, N_cap, n_win, dense, fixed_split);
+  // the in-kernel append: the decode kernel over dense rows, one query per
+  // sequence, the ring as the window (W_cap = n_win, origin 0)
+  if (append && (!p.decode || !dense || n_q != 1 || W_cap != n_win || win_origin != 0 || n_win < 1 ||
+                 win != append->ring || cache != append->cache))
+    return hipErrorInvalidValue;
+  const DecodeAppend ap = append ? *append : DecodeAppend{};
   float* part_o = nullptr;
   float* part_lse = nullptr;
   if (p.n_splits > 1) {
@@ -1250,14 +1367,21 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
                          static_cast<const uint8_t*>(cache), N_cap, idx, k, q_pos, m, n_entries,
                          static_cast<const uint8_t*>(win), W_cap, static_cast<long long>(win_origin),
                          n_win, tau, eps, sink, rope_step, p.n_splits, p.split_rows,
-                         static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse, pg);
+                         static_cast<uint8_t*>(out), out_fmt, lse, part_o, part_lse, pg, ap);
     };
     const bool paged = pg.bt != nullptr;
-    if (kv_fmt == LCA_BF16)
-      paged ? go(attn_decode_kernel<LCA_BF16, true>) : go(attn_decode_kernel<LCA_BF16, false>);
-    else
-      paged ? go(attn_decode_kernel<LCA_KV_FP8_BF16ROPE, true>)
-            : go(attn_decode_kernel<LCA_KV_FP8_BF16ROPE, false>);
+    if (append) {
+      if (kv_fmt == LCA_BF16)
+        paged ? go(attn_decode_kernel<LCA_BF16, true, true>) : go(attn_decode_kernel<LCA_BF16, false, true>);
+      else
+        paged ? go(attn_decode_kernel<LCA_KV_FP8_BF16ROPE, true, true>)
+              : go(attn_decode_kernel<LCA_KV_FP8_BF16ROPE, false, true>);
+    } else if (kv_fmt == LCA_BF16) {
+      paged ? go(attn_decode_kernel<LCA_BF16, true, false>) : go(attn_decode_kernel<LCA_BF16, false, false>);
+    } else {
+      paged ? go(attn_decode_kernel<LCA_KV_FP8_BF16ROPE, true, false>)
+            : go(attn_decode_kernel<LCA_KV_FP8_BF16ROPE, false, false>);
+    }
   } else if (p.mfma) {
     const dim3 grid(static_cast<unsigned>(rows * p.n_splits));
     if (kv_fmt == LCA_BF16)
@@ -1283,10 +1407,12 @@ hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, co
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
   if (rope_step != 0.0 && (static_cast<long long>(H) * (c / 4)) % 256 != 0) return hipErrorInvalidValue;
+  int32_t* advance = append ? append->n_tokens : nullptr;
   const dim3 g2(static_cast<unsigned>((rows * H * (c / 4) + kMergeThreads - 1) / kMergeThreads));
   auto merge = [&](auto kern) {
     hipLaunchKernelGGL(kern, g2, dim3(kMergeThreads), 0, s, rows, H, c, p.n_splits, static_cast<const void*>(part_o),
-                       part_lse, sink, static_cast<uint8_t*>(out), out_fmt, lse, q_pos, rope_step);
+                       part_lse, sink, static_cast<uint8_t*>(out), out_fmt, lse, q_pos, rope_step,
+                       advance);
   };
   // the decode kernel writes fp16 partials, the other kernels fp32
   auto merge_ch = [&](auto h16) {

@@ -491,11 +491,34 @@ hipError_t launch_out_proj(int T, int n_h, int c, int g, int d_g, int d, const u
 // Reads bytes (a multiple of 16) of device memory once; sink receives at most
 // one word.
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
+// An HCA decode step's state append done inside the attention launch (the
+// decode kernel's workgroups that hold the new token's window row or the entry
+// the token completes make them, write them to the state and use them from
+// LDS; the split merge, or the single workgroup, then advances n_tokens).  The
+// same rows, entries and counts as launch_state_append followed by the
+// attention, in one launch fewer.  m is the HCA rate; the tail has m rows;
+// io is bf16; the window is the ring (W_cap = n_win, origin 0).
+struct DecodeAppend {
+  const uint8_t* tokC;  // [B, c] bf16: the new token's KV candidate
+  const uint8_t* tokZ;  // [B, c] bf16: its gate logits
+  uint8_t* tailC;       // [B, m, c] bf16
+  uint8_t* tailZ;
+  const float* P;       // [m, c] positional bias of the gate logits
+  uint8_t* ring;        // the window ring (the attention's window) and the cache (or
+  uint8_t* cache;       // page pool) it reads, for the rows the append writes
+  int32_t* n_tokens;    // [B]: read, then advanced by one
+  int32_t* q_pos;       // [B] written (the query position p = n_tokens)
+  int32_t* n_entries;   // [B] written
+};
+// Whether launch_mqa can take a DecodeAppend for this shape (the few-row decode
+// kernel runs the attention).
+bool mqa_can_append(long long rows, int H, int c, int q_fmt, int kv_fmt, int N_cap, int n_win,
+                    int fixed_split);
 hipError_t launch_mqa(int B, int n_q, int H, int c, const void* q, int q_fmt, const void* cache,
                       int kv_fmt, int N_cap, const int32_t* idx, int k, const int32_t* q_pos, int m,
                       const int32_t* n_entries, const void* win, int W_cap, int64_t win_origin,
                       int n_win, float tau, float eps, const float* sink, double rope_step, void* out,
                       int out_fmt, float* lse, void* ws, const KvPages& pg, hipStream_t s,
-                      int fixed_split = 0);
+                      int fixed_split = 0, const DecodeAppend* append = nullptr);
 
 }  // namespace lca

@@ -17,94 +17,12 @@
 // same slot-to-wave split and combination order, so an entry made by decode
 // steps has the same bits as the entry the prefill compressor makes.
 #include "common.h"
+#include "pool.h"
 
 namespace lca {
 namespace {
 
 constexpr int kWavesPerBlock = 4;
-
-struct Pool {
-  float mx, sum, acc;
-};
-
-template <int CPL>
-__device__ __forceinline__ void pool_init(Pool* p) {
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) p[i] = {-INFINITY, 0.f, 0.f};
-}
-
-// Online softmax update of one candidate (KV values c, logits z).
-template <int CPL>
-__device__ __forceinline__ void pool_add(Pool* p, const float* cv, const float* zv) {
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const float nm = fmaxf(p[i].mx, zv[i]);
-    const float sc = __expf(p[i].mx - nm);
-    const float e = __expf(zv[i] - nm);
-    p[i].sum = p[i].sum * sc + e;
-    p[i].acc = p[i].acc * sc + e * cv[i];
-    p[i].mx = nm;
-  }
-}
-
-// E / sqrt(mean(E^2) + eps) across the wave's c channels.
-template <int CPL>
-__device__ __forceinline__ void pool_finish_norm(const Pool* p, int c, float eps, float* out) {
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    out[i] = p[i].acc * __builtin_amdgcn_rcpf(p[i].sum);
-    ss += out[i] * out[i];
-  }
-  ss = wave_sum(ss);
-  const float r = rsqrt_hw(ss / static_cast<float>(c) + eps);
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) out[i] *= r;
-}
-
-constexpr int kPoolWaves = 8;
-
-// The entry from the waves' partial pooling states: every wave stores its
-// state, then wave 0 combines them in slot order -- order[x] is the wave that
-// pooled the x-th slot group (a fixed order, so the result does not depend on
-// timing) -- and RMS-normalises.  Returns true in wave 0, whose `out` then
-// holds the entry.  Every wave of the workgroup must call it.
-template <int CPL>
-__device__ __forceinline__ bool pool_combine_norm(float (*part)[3][CPL][kWave], const Pool* pool,
-                                                  const int (&order)[kPoolWaves], int wv, int lane,
-                                                  int c, float eps, float* out) {
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    part[wv][0][j][lane] = pool[j].mx;
-    part[wv][1][j][lane] = pool[j].sum;
-    part[wv][2][j][lane] = pool[j].acc;
-  }
-  __syncthreads();
-  if (wv != 0) return false;
-  Pool tot[CPL];
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int x = 0; x < kPoolWaves; ++x) M = fmaxf(M, part[order[x]][0][j][lane]);
-    float sum = 0.f, acc = 0.f;
-#pragma unroll
-    for (int x = 0; x < kPoolWaves; ++x) {
-      const float mx = part[order[x]][0][j][lane];
-      const float f = mx == -INFINITY ? 0.f : __expf(mx - M);
-      sum += part[order[x]][1][j][lane] * f;
-      acc += part[order[x]][2][j][lane] * f;
-    }
-    tot[j] = {M, sum, acc};
-  }
-  pool_finish_norm<CPL>(tot, c, eps, out);
-  return true;
-}
-
-template <int CPL>
-__device__ __forceinline__ void load_bias(const float* P, int slot, int c, int lane, float* pv) {
-  load_row<CPL>(P + static_cast<size_t>(slot) * c, LCA_F32, c, lane, pv);
-}
 
 // IOF: the candidates' format (F32 or BF16) as a compile-time constant, so that
 // row loads carry no format branches (a load under a branch makes the compiler
@@ -266,16 +184,7 @@ __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
     store_row<CPL>(tZb + row * io_row, io_fmt, c, lane, tz);
     // window KV of the new token
     float u[CPL];
-    float ss = 0.f;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      u[j] = tc[j];
-      ss += u[j] * u[j];
-    }
-    ss = wave_sum(ss);
-    const float rs = rsqrt_hw(ss / static_cast<float>(c) + eps);
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) u[j] *= rs;
+    window_row<CPL>(tc, c, eps, u);
     if (rope_step != 0.0) {
       rope_p = rope_cs_lane(p, rope_step);  // also the angles of an entry this token completes
       rope_lane<CPL>(u, lane, c, rope_p);
@@ -319,35 +228,7 @@ __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
     for (int x = 0; x < kPoolWaves; ++x)
       order[x] = x < T_cap ? (x < m ? (1 - half) * m + x : half * m + (x - m)) : x;
   } else {
-    // wave wv pools slots wv, wv + kAppendWaves, ... in increasing order,
-    // kAppendBatch slots' rows loaded before any is pooled, so a long HCA tail
-    // pays one memory latency per batch
-    constexpr int kAppendBatch = CPL > 8 ? 1 : 4;
-    for (int j0 = wv; j0 < T_cap; j0 += kAppendWaves * kAppendBatch) {
-      float bc[kAppendBatch][CPL], bz[kAppendBatch][CPL], bb[kAppendBatch][CPL];
-      bool use[kAppendBatch], mine[kAppendBatch];
-      // unconditional loads (slots past the tail read slot j0's rows and are
-      // not used): a load under a branch would be waited for at the branch's end
-#pragma unroll
-      for (int u = 0; u < kAppendBatch; ++u) {
-        const int j = j0 + kAppendWaves * u;
-        const int jl = j < T_cap ? j : j0;
-        const bool prev = csa && jl < m;
-        const int r = csa ? (prev ? (1 - half) * m + jl : half * m + (jl - m)) : jl;
-        use[u] = j < T_cap && (!prev || s > 0);
-        mine[u] = r == row;
-        load_row<CPL>(tCb + r * io_row, io_fmt, c, lane, bc[u]);
-        load_row<CPL>(tZb + r * io_row, io_fmt, c, lane, bz[u]);
-        load_bias<CPL>(P, jl, c, lane, bb[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < kAppendBatch; ++u) {
-        if (!use[u]) continue;  // the same for the whole wave
-        // the new token's row may not have reached memory yet: take it from registers
-        if (mine[u]) add_row(tc, tz, bb[u]);
-        else add_row(bc[u], bz[u], bb[u]);
-      }
-    }
+    pool_tail<CPL, IOF>(csa, m, T_cap, half, s, row, tCb, tZb, P, c, lane, wv, tc, tz, pool);
 #pragma unroll
     for (int x = 0; x < kPoolWaves; ++x) order[x] = x;
   }

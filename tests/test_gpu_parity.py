@@ -841,13 +841,14 @@ def test_decode_deterministic_and_batch_invariant(fmt, ctx):
         assert np.array_equal(other[name][1], runs[0][name][1]), f"{name}: depends on other sequences"
 
 
-@pytest.mark.parametrize("kind,split_rows", [("csa", 128), ("hca", 192)])
+@pytest.mark.parametrize("kind,split_rows", [("csa", 128), ("hca", 192), ("hca", 1024)])
 def test_decode_fixed_split_rows_is_batch_invariant(kind, split_rows):
     """With a fixed attention split length (lca_decode_layer.split_rows) a
     sequence's bits do not depend on the batch size: sequence 5 alone equals
     sequence 5 in a batch of 16 (whose automatic plan would use other splits),
     and the batch agrees with the oracle.  CSA at 2^18 tokens takes the fused
-    selection."""
+    selection; HCA with 1024 rows per split runs one split per sequence, so no
+    merge follows the attention (which then advances the token count itself)."""
     if kind == "csa":
         cfg = CSA_DECODE_1M.with_(B=16, ctx=1 << 18)
     else:
@@ -870,6 +871,55 @@ def test_decode_fixed_split_rows_is_batch_invariant(kind, split_rows):
         assert np.array_equal(one[name][0], full[name][5]), f"{name}: B=1 differs from B=16"
     _decode_parity(cfg, d, [0, 5, 15],
                    layer=pipeline.DecodeLayer(cfg, d, DEV, split_rows=split_rows))
+
+
+@pytest.mark.parametrize("case", ["bf16", "fp8_rope_paged", "bf16_one_split"])
+def test_hca_decode_step_equals_append_then_attention(case):
+    """An HCA decode step on the few-row decode kernel appends the token inside
+    the attention launch.  It must give the bits of lca_state_append followed by
+    lca_sparse_mqa (same split plan) on a copy of the same state, step after step
+    over 140 steps (every sequence completes a block; with RoPE, a paged cache
+    and fp8 rows; with one split per sequence, where no merge follows): outputs,
+    lse, ring, tail rows, compressed cache and token counts."""
+    if case == "bf16":
+        cfg, paged, split_rows = HCA_DECODE.with_(B=8, ctx=1 << 15), None, 0
+    elif case == "fp8_rope_paged":
+        cfg = HCA_DECODE.with_(B=4, ctx=1 << 16, kv_dtype="fp8_bf16rope", rope_base=10000.0)
+        paged, split_rows = {"seed": 2}, 0
+    else:
+        cfg, paged, split_rows = HCA_DECODE.with_(B=3, ctx=1 << 15), None, 4096
+    d = gen.decode_inputs(cfg, extra_entries=4)
+    say(f"HCA step == append + attention: {case}, B={cfg.B}, N_cap {d['n_cap']}")
+    fused = pipeline.DecodeLayer(cfg, d, DEV, paged=paged, split_rows=split_rows)
+    ref = pipeline.DecodeLayer(cfg, d, DEV, paged=paged, split_rows=split_rows)
+    B, m, c, H = cfg.B, d["m"], cfg.c, cfg.H
+    q_pos = torch.empty(B, dtype=torch.int32, device=DEV)
+    n_ent = torch.empty(B, dtype=torch.int32, device=DEV)
+    ws = torch.empty(max(1, ops.sparse_mqa_workspace_size(B, 1, H, c, cfg.kv_dtype, 0, d["n_cap"],
+                                                          cfg.n_win, True, split_rows)),
+                     dtype=torch.uint8, device=DEV)
+    out_r = torch.empty_like(ref.out)
+    lse_r = torch.empty_like(ref.lse)
+    pages = ref.paged.struct(DEV) if paged else None
+    bits = lambda v: host(v.view(torch.int16) if v.dtype == torch.bfloat16 else v)  # noqa: E731
+    for st in range(140):
+        fused.step()
+        ops.lca_state_append("hca", m, B, c, cfg.n_win, ref.tokC, ref.tokZ, cfg.io_dtype, ref.tailC,
+                             ref.tailZ, ref.ring, cfg.kv_dtype, ref.P, ref.cache, d["n_cap"], ref.n_tokens,
+                             q_pos, n_ent, cfg.eps, cfg.rope_base, pages=pages)
+        ops.lca_sparse_mqa(B, 1, H, c, ref.q, cfg.io_dtype, ref.cache, cfg.kv_dtype, d["n_cap"], None, 0,
+                           q_pos, m, n_ent, ref.ring, cfg.n_win, 0, cfg.n_win, cfg.tau, cfg.eps, None,
+                           cfg.rope_base, out_r, cfg.io_dtype, lse=lse_r, workspace=ws, pages=pages,
+                           split_rows=split_rows)
+        if st % 20 == 0 or st == 139:
+            torch.cuda.synchronize()
+            assert np.array_equal(bits(fused.out), bits(out_r)), f"step {st}: out"
+            assert np.array_equal(bits(fused.lse), bits(lse_r)), f"step {st}: lse"
+    torch.cuda.synchronize()
+    for name in ("ring", "tailC", "tailZ", "cache", "n_tokens"):
+        assert np.array_equal(bits(getattr(fused, name)), bits(getattr(ref, name))), f"state {name}"
+    assert np.array_equal(host(fused.n_tokens), d["n_tokens"] + 140)
+    assert ((d["n_tokens"] + 140) // m > (d["n_tokens"] + 1) // m).all(), "every sequence completes a block"
 
 
 def test_sink_logit():
