@@ -447,6 +447,10 @@ int lca_device_checks(uint64_t* violations, int reset);
  * the workgroups that hold the new window row and the entry a completed block
  * makes write them, and use them for this step's query, and the split merge
  * advances n_tokens -- the bits of lca_state_append followed by lca_sparse_mqa.
+ * A CSA step with the fused selection (bf16 io, c = 512) runs the append as
+ * extra workgroups of the selection's finish launch, one per sequence, and a
+ * light launch before the indexer writes the query positions and clears the
+ * selection's histogram -- again the bits of the separate calls.
  * ------------------------------------------------------------------------- */
 typedef struct lca_decode_layer {
   size_t struct_size;   /* sizeof(lca_decode_layer) */

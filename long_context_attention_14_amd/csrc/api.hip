@@ -515,8 +515,34 @@ int decode_enqueue(const lca_decode_layer* L, const lca_decode_io* io, void* wor
   const bool fused_append = !csa && L->io_dtype == LCA_BF16 &&
                             lca::mqa_can_append(L->B, L->H, L->c, L->io_dtype, L->kv_dtype, L->N_cap,
                                                 L->n_win, L->split_rows);
+  // CSA steps with the fused selection run the append as extra workgroups of the
+  // selection's finish launch, beside its one workgroup per row, and give the
+  // indexer its positions and cleared histogram from a light launch instead
+  const bool finish_append = fused && L->io_dtype == LCA_BF16 && L->c == 512;
+  lca::StateAppend app{};
   lca::DecodeAppend ap{};
-  if (fused_append) {
+  if (finish_append) {
+    app.m = L->m;
+    app.B = L->B;
+    app.n_win = L->n_win;
+    app.kv_fmt = L->kv_dtype;
+    app.N_cap = L->N_cap;
+    app.tokC = static_cast<const uint8_t*>(io->tokC);
+    app.tokZ = static_cast<const uint8_t*>(io->tokZ);
+    app.tailC = static_cast<uint8_t*>(L->tailC);
+    app.tailZ = static_cast<uint8_t*>(L->tailZ);
+    app.ring = static_cast<uint8_t*>(L->ring);
+    app.P = L->P;
+    app.cache = static_cast<uint8_t*>(L->cache);
+    app.n_tokens = L->n_tokens;
+    app.eps = L->eps;
+    app.rope_step = rope_step(L->rope_base);
+    app.pg = pg;
+    st = hip_status(lca::launch_decode_prep(L->m, L->B, L->N_cap, L->n_tokens, q_pos, n_ent, hist,
+                                            zero_words, s),
+                    "lca_decode_step/prep");
+    if (st != LCA_OK) return st;
+  } else if (fused_append) {
     ap.tokC = static_cast<const uint8_t*>(io->tokC);
     ap.tokZ = static_cast<const uint8_t*>(io->tokZ);
     ap.tailC = static_cast<uint8_t*>(L->tailC);
@@ -546,7 +572,7 @@ int decode_enqueue(const lca_decode_layer* L, const lca_decode_io* io, void* wor
                                         reinterpret_cast<hipEvent_t>(io->stage_events[1]),
                                         reinterpret_cast<hipEvent_t>(io->stage_events[2]),
                                         fused ? &sw : nullptr, L->k, LCA_F32,
-                                        fused ? idx : nullptr),
+                                        fused ? idx : nullptr, finish_append ? &app : nullptr),
                     "lca_decode_step/indexer");
     if (st != LCA_OK) return st;
     if (fused) {

@@ -444,12 +444,38 @@ SelectWs select_ws_in(void* ws, long long rows, int N_cap);
 bool select_supported(int N_cap, int k);
 // workgroups per row (wpr) the finish pass takes
 constexpr int kSelMaxWpr = 256;
+// A CSA decode step's state append run by the selection finish launch: one
+// more workgroup per sequence beside the finish's, on CUs the finish leaves
+// idle (the indexer before it got the query positions and the cleared
+// histogram from launch_decode_prep).  Same rows, entries and counts as
+// launch_state_append; bf16 io, c = 512, tail of 2m rows.
+struct StateAppend {
+  int m, B, n_win, kv_fmt, N_cap;
+  const uint8_t* tokC;  // [B, 512] bf16
+  const uint8_t* tokZ;
+  uint8_t* tailC;       // [B, 2m, 512] bf16
+  uint8_t* tailZ;
+  uint8_t* ring;        // [B, n_win, row]
+  const float* P;       // [2m, 512]
+  uint8_t* cache;       // [B, N_cap, row] or a page pool
+  int32_t* n_tokens;    // [B], advanced by one
+  float eps;
+  double rope_step;
+  KvPages pg;
+};
 // The finish pass after the fused indexer: one workgroup per row selects the
 // row's top k from the emitted pairs into idx ([rows, k], ascending, -1 after
-// min(k, vis)); rows with vis <= k were written by the indexer.
+// min(k, vis)); rows with vis <= k were written by the indexer.  app: the step's
+// state append, run beside it (n_q = 1), or NULL.
 hipError_t launch_select_finish(long long rows, int n_q, int N_cap, int wpr, const int32_t* q_pos, int m,
                                 const int32_t* n_entries, int k, const SelectWs& w, int32_t* idx,
-                                hipStream_t s);
+                                hipStream_t s, const StateAppend* app = nullptr);
+// What the indexer of such a step needs first: q_pos[b] = p = n_tokens[b],
+// n_entries[b] = min((p+1)/m, N_cap) (a negative count is left alone), and
+// zero_buf cleared.
+hipError_t launch_decode_prep(int m, int B, int N_cap, const int32_t* n_tokens, int32_t* q_pos,
+                              int32_t* n_entries, uint32_t* zero_buf, long long zero_words,
+                              hipStream_t s);
 
 // hist (optional, [B*n_q, 4096], zeroed by the caller): the MFMA path adds the
 // score_bin histogram of every row's visible scores into it.  sel (optional,
@@ -462,7 +488,8 @@ hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const v
                           const int32_t* n_entries, void* scores, hipStream_t s,
                           uint32_t* hist = nullptr, hipEvent_t ev_start = nullptr,
                           hipEvent_t ev_stop = nullptr, const SelectWs* sel = nullptr, int k = 0,
-                          int score_fmt = LCA_F32, int32_t* sel_idx = nullptr);
+                          int score_fmt = LCA_F32, int32_t* sel_idx = nullptr,
+                          const StateAppend* app = nullptr);
 size_t topk_workspace_bytes(int B, int n_q, int N_cap, int k);
 // scores: [B*n_q, N_cap] float32, or bf16 bits when score_fmt == LCA_BF16
 hipError_t launch_topk(int B, int n_q, int N_cap, const void* scores, const int32_t* q_pos, int m,

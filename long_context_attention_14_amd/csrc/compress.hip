@@ -16,6 +16,8 @@
 // reduction).  The decode-time state append pools a completed block with the
 // same slot-to-wave split and combination order, so an entry made by decode
 // steps has the same bits as the entry the prefill compressor makes.
+#include <algorithm>
+
 #include "common.h"
 #include "pool.h"
 
@@ -128,117 +130,53 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void rmsnorm_rows_kernel(
                  v);
 }
 
-// One workgroup of kAppendWaves waves per sequence: append the token, and
-// compress its block when the token completes it.  The block's candidate slots
-// are pooled as in compress_kernel (slot j by one wave, each wave an online
-// per-channel softmax over its slots in increasing order, the partial states
-// combined in slot order through LDS), so the entry has the bits the prefill
-// compressor gives it and does not depend on timing.  Tail rows other than the
-// new token were written by earlier steps; the new token's row is used from
-// registers.  As a side job the workgroups clear zero_buf.
-constexpr int kAppendWaves = kPoolWaves;
-
+// One workgroup of kAppendWaves waves per sequence (state_append_body).
 template <int CPL, int IOF>
 __global__ __launch_bounds__(kWave * kAppendWaves) void state_append_kernel(
     int csa, int m, int B, int c, int n_win, const uint8_t* tokC, const uint8_t* tokZ,
     uint8_t* tailC, uint8_t* tailZ, uint8_t* ring, int kv_fmt, const float* P, uint8_t* cache,
     int N_cap, int32_t* n_tokens, int32_t* q_pos, int32_t* n_entries, float eps, double rope_step,
     KvPages pg, uint32_t* zero_buf, long long zero_words) {
-  constexpr int io_fmt = IOF;  // compile-time: no format branches around the row loads
   __shared__ float part[kAppendWaves][3][CPL][kWave];  // lane-contiguous: no bank conflicts
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wv = threadIdx.x >> 6;
-  const int b = blockIdx.x;
+  state_append_body<CPL, IOF>(blockIdx.x, gridDim.x, part, csa, m, c, n_win, tokC, tokZ, tailC, tailZ,
+                              ring, kv_fmt, P, cache, N_cap, n_tokens, q_pos, n_entries, eps, rope_step,
+                              pg, zero_buf, zero_words);
+}
+
+// The part of a decode step's state append that the indexer needs first, for a
+// step whose attention appends the token itself: the query position p =
+// n_tokens[b] and the visible entry count, and the cleared zero_buf (the
+// selection's row histogram).  n_tokens is advanced after the attention.
+__global__ __launch_bounds__(256) void decode_prep_kernel(int m, int B, int N_cap,
+                                                          const int32_t* n_tokens, int32_t* q_pos,
+                                                          int32_t* n_entries, uint32_t* zero_buf,
+                                                          long long zero_words) {
   for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; i < zero_words;
        i += static_cast<long long>(gridDim.x) * blockDim.x)
     zero_buf[i] = 0u;
-  const size_t io_row = row_bytes(io_fmt, c);
-  const size_t kv_row = row_bytes(kv_fmt, c);
-  const int T_cap = csa ? 2 * m : m;
-  uint8_t* tCb = tailC + static_cast<size_t>(b) * T_cap * io_row;
-  uint8_t* tZb = tailZ + static_cast<size_t>(b) * T_cap * io_row;
-  // A CSA tail of at most kAppendWaves rows is read speculatively (one row per
-  // wave, with the bias rows of both slots that row can take) before the token
-  // count arrives, so that the step pays one memory latency.
-  const bool spec = CPL <= 8 && csa && T_cap <= kAppendWaves;
-  float sc[CPL], sz[CPL], sp0[CPL], sp1[CPL];
-  if (spec && wv < T_cap) {
-    load_row<CPL>(tCb + wv * io_row, io_fmt, c, lane, sc);
-    load_row<CPL>(tZb + wv * io_row, io_fmt, c, lane, sz);
-    load_bias<CPL>(P, wv % m, c, lane, sp0);
-    load_bias<CPL>(P, m + wv % m, c, lane, sp1);
-  }
-  float tc[CPL], tz[CPL];
-  load_row<CPL>(tokC + static_cast<size_t>(b) * io_row, io_fmt, c, lane, tc);
-  load_row<CPL>(tokZ + static_cast<size_t>(b) * io_row, io_fmt, c, lane, tz);
-  const int p = n_tokens[b];
-  if (p < 0) return;  // the same for every wave
-  // every wave has read the count before wave 0 advances it below
-  __syncthreads();
-  const int blk = p / m;
-  const int half = csa ? (blk & 1) : 0;
-  const int row = half * m + p % m;
-  float2 rope_p = make_float2(1.f, 0.f);
-  if (wv == 0) {
-    store_row<CPL>(tCb + row * io_row, io_fmt, c, lane, tc);
-    store_row<CPL>(tZb + row * io_row, io_fmt, c, lane, tz);
-    // window KV of the new token
-    float u[CPL];
-    window_row<CPL>(tc, c, eps, u);
-    if (rope_step != 0.0) {
-      rope_p = rope_cs_lane(p, rope_step);  // also the angles of an entry this token completes
-      rope_lane<CPL>(u, lane, c, rope_p);
-    }
-    store_row<CPL>(ring + (static_cast<size_t>(b) * n_win + p % n_win) * kv_row, kv_fmt, c, lane, u);
-    if (lane == 0) {
-      n_tokens[b] = p + 1;
+  const int b = static_cast<int>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (b < B) {
+    const int p = n_tokens[b];
+    if (p >= 0) {  // a negative count: the sequence is left as it is
       q_pos[b] = p;
       const int ne = (p + 1) / m;
       n_entries[b] = ne < N_cap ? ne : N_cap;
     }
   }
-  if ((p + 1) % m != 0) return;
-
-  // candidate slots: CSA slot j < m is the previous block's token j (tail row
-  // (1-half)*m + j, absent for the first entry), slot m + j the own block's
-  // token j (row half*m + j); HCA slot j is row j.  The new token's row is
-  // taken from registers.
-  const int s = (p + 1) / m - 1;
-  // the new entry's row in the cache (through the block table when paged),
-  // looked up before the candidate loads; -1: beyond N_cap or an absent page
-  const long long out_row = (wv == 0 && s < N_cap) ? kv_row_of(pg, b, N_cap, s) : -1;
-  if (LCA_DEVICE_CHECKS && wv == 0 && lane == 0 && s < N_cap) dbg_check(out_row >= 0);
-  Pool pool[CPL];
-  pool_init<CPL>(pool);
-  auto add_row = [&](const float* rc, const float* rz, const float* bias) {
-    float zv[CPL];
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) zv[j] = rz[j] + bias[j];
-    pool_add<CPL>(pool, rc, zv);
-  };
-  int order[kPoolWaves];  // order[x]: the wave that pooled slot group x
-  if (spec) {
-    // wave wv holds tail row wv (loaded before the count was known): its slot
-    // is m + wv % m in the own half, wv % m in the other
-    if (wv < T_cap) {
-      const bool own = (wv / m) == half;
-      if (own || s > 0) add_row(wv == row ? tc : sc, wv == row ? tz : sz, own ? sp1 : sp0);
-    }
-#pragma unroll
-    for (int x = 0; x < kPoolWaves; ++x)
-      order[x] = x < T_cap ? (x < m ? (1 - half) * m + x : half * m + (x - m)) : x;
-  } else {
-    pool_tail<CPL, IOF>(csa, m, T_cap, half, s, row, tCb, tZb, P, c, lane, wv, tc, tz, pool);
-#pragma unroll
-    for (int x = 0; x < kPoolWaves; ++x) order[x] = x;
-  }
-  float out[CPL];
-  if (!pool_combine_norm<CPL>(part, pool, order, wv, lane, c, eps, out)) return;
-  if (rope_step != 0.0) rope_lane<CPL>(out, lane, c, rope_p);  // the entry's last token is p
-  if (out_row >= 0) store_row<CPL>(cache + static_cast<size_t>(out_row) * kv_row, kv_fmt, c, lane, out);
 }
 
 }  // namespace
+
+hipError_t launch_decode_prep(int m, int B, int N_cap, const int32_t* n_tokens, int32_t* q_pos,
+                              int32_t* n_entries, uint32_t* zero_buf, long long zero_words,
+                              hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const long long want = std::max<long long>((B + 255) / 256, (zero_words + 1023) / 1024);
+  const unsigned grid = static_cast<unsigned>(std::min<long long>(std::max<long long>(want, 1), 1024));
+  hipLaunchKernelGGL(decode_prep_kernel, dim3(grid), dim3(256), 0, s, m, B, N_cap, n_tokens, q_pos,
+                     n_entries, zero_buf, zero_words);
+  return hipGetLastError();
+}
 
 #define LCA_DISPATCH_CPL(c, KERNEL, GRID, ...)                                              \
   do {                                                                                      \

@@ -722,7 +722,8 @@ hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const v
                           int N_cap, const float* w, const int32_t* q_pos, int m,
                           const int32_t* n_entries, void* scores, hipStream_t s,
                           uint32_t* hist, hipEvent_t ev_start, hipEvent_t ev_stop,
-                          const SelectWs* sel, int k, int score_fmt, int32_t* sel_idx) {
+                          const SelectWs* sel, int k, int score_fmt, int32_t* sel_idx,
+                          const StateAppend* app) {
   const long long rows = static_cast<long long>(B) * n_q;
   if (rows == 0 || N_cap == 0) return hipSuccess;
   if (score_fmt != LCA_F32 && score_fmt != LCA_BF16) return hipErrorInvalidValue;
@@ -776,8 +777,9 @@ hipError_t launch_indexer(int B, int n_q, int H_I, int d_I, int idx_fmt, const v
     if (mx) go(indexer_select_kernel<true>);
     else go(indexer_select_kernel<false>);
     if (e != hipSuccess || (e = hipGetLastError()) != hipSuccess) return e;
-    return launch_select_finish(rows, n_q, N_cap, iw, q_pos, m, n_entries, k, so, sel_idx, s);
+    return launch_select_finish(rows, n_q, N_cap, iw, q_pos, m, n_entries, k, so, sel_idx, s, app);
   }
+  if (app) return hipErrorInvalidValue;  // the append rides on the finish pass only
   if (!hist && n_q >= kRowsPerWG * 8) {
     // many rows per sequence: row groups share each key tile through LDS
     const int gps = (n_q + kRowsPerWG - 1) / kRowsPerWG;

@@ -20,6 +20,7 @@
 //    order; a last one-workgroup-per-row pass radix-selects among the
 //    candidates on the remaining 20 bits and merges the two sorted lists.
 #include "common.h"
+#include "pool.h"
 
 namespace lca {
 namespace {
@@ -651,13 +652,28 @@ __device__ uint32_t radix_select20(int n, int want, KeyF key, uint32_t* rh, int*
   return prefix;
 }
 
+// Workgroups rows .. rows + B - 1 (when app.tokC is set) run the decode step's
+// state append of sequence blockIdx.x - rows instead, with the candidates' LDS
+// as the pooling scratch.
 __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     int n_q, int N_cap, int wpr, const int32_t* __restrict__ q_pos, int m,
-    const int32_t* __restrict__ n_entries, int k, SelectWs o, int32_t* __restrict__ sel_idx) {
+    const int32_t* __restrict__ n_entries, int k, SelectWs o, int32_t* __restrict__ sel_idx,
+    long long rows, StateAppend app) {
   constexpr int NT = kFinThreads;
   __shared__ uint32_t lh[kScoreHistBins];
   __shared__ int32_t sel[kMaxK];
   __shared__ __attribute__((aligned(16))) uint32_t cand[2 * kFinCand];  // keys, indices; then the output bitmap
+  if (app.tokC && static_cast<long long>(blockIdx.x) >= rows) {
+    constexpr int CPL = 512 / kWave;
+    static_assert(sizeof(float) * kAppendWaves * 3 * CPL * kWave <= sizeof(cand), "append scratch");
+    static_assert(kFinThreads >= kWave * kAppendWaves, "append waves");
+    state_append_body<CPL, LCA_BF16, true>(static_cast<int>(blockIdx.x - rows), app.B,
+                                     reinterpret_cast<float (*)[3][CPL][kWave]>(cand), 1, app.m, 512,
+                                     app.n_win, app.tokC, app.tokZ, app.tailC, app.tailZ, app.ring,
+                                     app.kv_fmt, app.P, app.cache, app.N_cap, app.n_tokens, nullptr,
+                                     nullptr, app.eps, app.rope_step, app.pg, nullptr, 0);
+    return;
+  }
   __shared__ int sh_bin, sh_above, sh_nsel, sh_ncand, sh_rb, sh_ra;
   __shared__ int scan_sh[kFinWaves];
   __shared__ uint32_t rh[256];
@@ -1045,11 +1061,14 @@ SelectWs select_ws_in(void* ws, long long rows, int N_cap) {
 
 hipError_t launch_select_finish(long long rows, int n_q, int N_cap, int wpr, const int32_t* q_pos, int m,
                                 const int32_t* n_entries, int k, const SelectWs& w, int32_t* idx,
-                                hipStream_t s) {
+                                hipStream_t s, const StateAppend* app) {
   if (rows == 0) return hipSuccess;
   if (wpr < 1 || wpr > kSelMaxWpr || !select_supported(N_cap, k)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(select_finish_kernel, dim3(static_cast<unsigned>(rows)), dim3(kFinThreads), 0, s,
-                     n_q, N_cap, wpr, q_pos, m, n_entries, k, w, idx);
+  if (app && (n_q != 1 || app->B != rows || app->tokC == nullptr)) return hipErrorInvalidValue;
+  const StateAppend a = app ? *app : StateAppend{};
+  const long long grid = rows + (app ? app->B : 0);
+  hipLaunchKernelGGL(select_finish_kernel, dim3(static_cast<unsigned>(grid)), dim3(kFinThreads), 0, s,
+                     n_q, N_cap, wpr, q_pos, m, n_entries, k, w, idx, rows, a);
   return dbg_selection(rows, n_q, N_cap, q_pos, m, n_entries, k, idx, s);
 }
 
