@@ -922,6 +922,58 @@ def test_hca_decode_step_equals_append_then_attention(case):
     assert ((d["n_tokens"] + 140) // m > (d["n_tokens"] + 1) // m).all(), "every sequence completes a block"
 
 
+@pytest.mark.parametrize("case", ["fp8", "mxfp4_fp8kv_paged_rope"])
+def test_csa_decode_step_equals_separate_calls(case):
+    """A CSA decode step with the fused selection runs its state append beside
+    the selection's finish pass (after a light launch that gives the indexer its
+    positions).  It must give the bits of the separate calls on a copy of the
+    same state: lca_state_append, lca_indexer_scores + lca_topk and
+    lca_sparse_mqa, step after step over 40 steps (a block completes every 4):
+    outputs, lse, selections, ring, tail rows, compressed cache, token counts."""
+    if case == "fp8":
+        cfg, paged = CSA_DECODE_1M.with_(B=4, ctx=1 << 18), None
+    else:
+        cfg = CSA_DECODE_1M.with_(B=2, ctx=1 << 18, idx_dtype="mxfp4", kv_dtype="fp8_bf16rope",
+                                  rope_base=10000.0)
+        paged = {"seed": 4}
+    d = gen.decode_inputs(cfg, extra_entries=12)
+    say(f"CSA step == separate calls: {case}, B={cfg.B}, N_cap {d['n_cap']}")
+    fused = pipeline.DecodeLayer(cfg, d, DEV, paged=paged)
+    ref = pipeline.DecodeLayer(cfg, d, DEV, paged=paged)
+    B, m, c, H, N_cap, k = cfg.B, d["m"], cfg.c, cfg.H, d["n_cap"], cfg.k
+    q_pos = torch.empty(B, dtype=torch.int32, device=DEV)
+    n_ent = torch.empty(B, dtype=torch.int32, device=DEV)
+    scores = torch.empty((B, N_cap), dtype=torch.float32, device=DEV)
+    idx_r = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    ws_t = torch.empty(max(1, ops.topk_workspace_size(B, 1, N_cap, k)), dtype=torch.uint8, device=DEV)
+    ws_a = torch.empty(max(1, ops.sparse_mqa_workspace_size(B, 1, H, c, cfg.kv_dtype, k, N_cap, cfg.n_win,
+                                                            False)), dtype=torch.uint8, device=DEV)
+    out_r = torch.empty_like(ref.out)
+    lse_r = torch.empty_like(ref.lse)
+    pages = ref.paged.struct(DEV) if paged else None
+    bits = lambda v: host(v.view(torch.int16) if v.dtype == torch.bfloat16 else v)  # noqa: E731
+    for st in range(40):
+        fused.step()
+        ops.lca_state_append("csa", m, B, c, cfg.n_win, ref.tokC, ref.tokZ, cfg.io_dtype, ref.tailC,
+                             ref.tailZ, ref.ring, cfg.kv_dtype, ref.P, ref.cache, N_cap, ref.n_tokens,
+                             q_pos, n_ent, cfg.eps, cfg.rope_base, pages=pages)
+        ops.lca_indexer_scores(B, 1, cfg.H_I, cfg.d_I, cfg.idx_dtype, ref.qI, ref.qI_scale, ref.kI,
+                               ref.kI_scale, N_cap, ref.w, q_pos, m, n_ent, scores)
+        ops.lca_topk(B, 1, N_cap, scores, q_pos, m, n_ent, k, idx_r, ws_t)
+        ops.lca_sparse_mqa(B, 1, H, c, ref.q, cfg.io_dtype, ref.cache, cfg.kv_dtype, N_cap, idx_r, k,
+                           q_pos, m, n_ent, ref.ring, cfg.n_win, 0, cfg.n_win, cfg.tau, cfg.eps, None,
+                           cfg.rope_base, out_r, cfg.io_dtype, lse=lse_r, workspace=ws_a, pages=pages)
+        if st % 8 == 0 or st == 39:
+            torch.cuda.synchronize()
+            assert np.array_equal(host(fused.idx), host(idx_r)), f"step {st}: selection"
+            assert np.array_equal(bits(fused.out), bits(out_r)), f"step {st}: out"
+            assert np.array_equal(bits(fused.lse), bits(lse_r)), f"step {st}: lse"
+    torch.cuda.synchronize()
+    for name in ("ring", "tailC", "tailZ", "cache", "n_tokens"):
+        assert np.array_equal(bits(getattr(fused, name)), bits(getattr(ref, name))), f"state {name}"
+    assert np.array_equal(host(fused.n_tokens), d["n_tokens"] + 40)
+
+
 def test_sink_logit():
     cfg = HCA_DECODE.with_(B=2, ctx=4096, m=128)
     say("sink")
