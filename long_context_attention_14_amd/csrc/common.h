@@ -156,10 +156,13 @@ __device__ inline float2 rope_cs(long long pos, int i, double rope_step) {
   return make_float2(cs, sn);
 }
 
-// Turn the pair (x, y) by the angle with cosine cs.x and sine cs.y.
+// Turn the pair (x, y) by the angle with cosine cs.x and sine cs.y.  The fused
+// multiply-adds are written out: a sum of two products can be contracted either
+// way round, and kernels that turn the same row (the state append and the
+// attention that appends itself) must round it alike.
 __device__ __forceinline__ void rope_turn(float& x, float& y, float2 cs) {
-  const float nx = x * cs.x - y * cs.y;
-  const float ny = x * cs.y + y * cs.x;
+  const float nx = fmaf(x, cs.x, -(y * cs.y));
+  const float ny = fmaf(x, cs.y, y * cs.x);
   x = nx;
   y = ny;
 }

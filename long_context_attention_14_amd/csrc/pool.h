@@ -29,8 +29,8 @@ __device__ __forceinline__ void pool_add(Pool* p, const float* cv, const float* 
     const float nm = fmaxf(p[i].mx, zv[i]);
     const float sc = __expf(p[i].mx - nm);
     const float e = __expf(zv[i] - nm);
-    p[i].sum = p[i].sum * sc + e;
-    p[i].acc = p[i].acc * sc + e * cv[i];
+    p[i].sum = fmaf(p[i].sum, sc, e);
+    p[i].acc = fmaf(p[i].acc, sc, e * cv[i]);  // written out: two products, one sum
     p[i].mx = nm;
   }
 }

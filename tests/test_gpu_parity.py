@@ -873,7 +873,8 @@ def test_decode_fixed_split_rows_is_batch_invariant(kind, split_rows):
                    layer=pipeline.DecodeLayer(cfg, d, DEV, split_rows=split_rows))
 
 
-@pytest.mark.parametrize("case", ["bf16", "fp8_rope_paged", "bf16_one_split"])
+@pytest.mark.parametrize("case", ["bf16", "fp8_rope_paged", "bf16_one_split", "random0", "random1",
+                                  "random2"])
 def test_hca_decode_step_equals_append_then_attention(case):
     """An HCA decode step on the few-row decode kernel appends the token inside
     the attention launch.  It must give the bits of lca_state_append followed by
@@ -881,7 +882,15 @@ def test_hca_decode_step_equals_append_then_attention(case):
     over 140 steps (every sequence completes a block; with RoPE, a paged cache
     and fp8 rows; with one split per sequence, where no merge follows): outputs,
     lse, ring, tail rows, compressed cache and token counts."""
-    if case == "bf16":
+    if case.startswith("random"):
+        # seeded shapes: the split plan, and so which splits hold the new rows, varies
+        rng = np.random.default_rng(100 + int(case[-1]))
+        cfg = HCA_DECODE.with_(B=int(rng.integers(1, 40)), ctx=int(rng.integers(1 << 12, 1 << 18)),
+                               kv_dtype=["bf16", "fp8_bf16rope"][int(rng.integers(0, 2))],
+                               rope_base=[0.0, 10000.0][int(rng.integers(0, 2))], seed=int(rng.integers(0, 99)))
+        paged = {"seed": 7} if rng.integers(0, 2) else None
+        split_rows = [0, 0, 64 * int(rng.integers(1, 9))][int(rng.integers(0, 3))]
+    elif case == "bf16":
         cfg, paged, split_rows = HCA_DECODE.with_(B=8, ctx=1 << 15), None, 0
     elif case == "fp8_rope_paged":
         cfg = HCA_DECODE.with_(B=4, ctx=1 << 16, kv_dtype="fp8_bf16rope", rope_base=10000.0)
@@ -889,7 +898,8 @@ def test_hca_decode_step_equals_append_then_attention(case):
     else:
         cfg, paged, split_rows = HCA_DECODE.with_(B=3, ctx=1 << 15), None, 4096
     d = gen.decode_inputs(cfg, extra_entries=4)
-    say(f"HCA step == append + attention: {case}, B={cfg.B}, N_cap {d['n_cap']}")
+    say(f"HCA step == append + attention: {case}, B={cfg.B}, ctx={cfg.ctx}, kv={cfg.kv_dtype}, "
+        f"rope={cfg.rope_base}, paged={paged is not None}, split_rows={split_rows}, N_cap {d['n_cap']}")
     fused = pipeline.DecodeLayer(cfg, d, DEV, paged=paged, split_rows=split_rows)
     ref = pipeline.DecodeLayer(cfg, d, DEV, paged=paged, split_rows=split_rows)
     B, m, c, H = cfg.B, d["m"], cfg.c, cfg.H
