@@ -932,7 +932,7 @@ def test_hca_decode_step_equals_append_then_attention(case):
     assert ((d["n_tokens"] + 140) // m > (d["n_tokens"] + 1) // m).all(), "every sequence completes a block"
 
 
-@pytest.mark.parametrize("case", ["fp8", "mxfp4_fp8kv_paged_rope"])
+@pytest.mark.parametrize("case", ["fp8", "mxfp4_fp8kv_paged_rope", "random0", "random1"])
 def test_csa_decode_step_equals_separate_calls(case):
     """A CSA decode step with the fused selection runs its state append beside
     the selection's finish pass (after a light launch that gives the indexer its
@@ -940,14 +940,24 @@ def test_csa_decode_step_equals_separate_calls(case):
     same state: lca_state_append, lca_indexer_scores + lca_topk and
     lca_sparse_mqa, step after step over 40 steps (a block completes every 4):
     outputs, lse, selections, ring, tail rows, compressed cache, token counts."""
-    if case == "fp8":
+    if case.startswith("random"):
+        # seeded shapes in the fused selection's range (more than 36864 entries)
+        rng = np.random.default_rng(200 + int(case[-1]))
+        cfg = CSA_DECODE_1M.with_(B=int(rng.integers(1, 13)), ctx=int(rng.integers(150_000, 1 << 20)),
+                                  idx_dtype=["fp8", "mxfp4"][int(rng.integers(0, 2))],
+                                  kv_dtype=["bf16", "fp8_bf16rope"][int(rng.integers(0, 2))],
+                                  rope_base=[0.0, 10000.0][int(rng.integers(0, 2))],
+                                  seed=int(rng.integers(0, 99)))
+        paged = {"seed": 9} if rng.integers(0, 2) else None
+    elif case == "fp8":
         cfg, paged = CSA_DECODE_1M.with_(B=4, ctx=1 << 18), None
     else:
         cfg = CSA_DECODE_1M.with_(B=2, ctx=1 << 18, idx_dtype="mxfp4", kv_dtype="fp8_bf16rope",
                                   rope_base=10000.0)
         paged = {"seed": 4}
     d = gen.decode_inputs(cfg, extra_entries=12)
-    say(f"CSA step == separate calls: {case}, B={cfg.B}, N_cap {d['n_cap']}")
+    say(f"CSA step == separate calls: {case}, B={cfg.B}, ctx={cfg.ctx}, idx={cfg.idx_dtype}, "
+        f"kv={cfg.kv_dtype}, rope={cfg.rope_base}, paged={paged is not None}, N_cap {d['n_cap']}")
     fused = pipeline.DecodeLayer(cfg, d, DEV, paged=paged)
     ref = pipeline.DecodeLayer(cfg, d, DEV, paged=paged)
     B, m, c, H, N_cap, k = cfg.B, d["m"], cfg.c, cfg.H, d["n_cap"], cfg.k
