@@ -693,6 +693,19 @@ __device__ __forceinline__ const uint8_t* slot_row_e(const SlotCtx& s, int i, in
 
 constexpr int kD8Waves = 8;  // waves per decode workgroup
 
+// The decode kernel's KV tile rows are 1 KiB apart with no padding; the
+// 16-byte chunks of row r are permuted by chunk ^ dswz(r) (a function of r mod
+// 16).  Both reads of a tile then spread over all 64 LDS banks: the Sᵀ reads
+// (16 lanes, 16 consecutive rows, one chunk each) and the transposing V reads
+// (32 lanes: 4 rows x 8 pieces of 8 bytes, two chunks per row), which with the
+// padded rows met 2-way bank conflicts (a third of the kernel's LDS cycles).
+constexpr int kDQS = kMC;  // LDS row stride of the decode kernel's KV tiles (bf16 elements)
+__device__ __forceinline__ int dswz(int r) { return (4 * (r & 3)) ^ ((r >> 2) & 3); }
+// element index of chunk-aligned column col (a multiple of 4) of row r
+__device__ __forceinline__ int dkv(int r, int col) {
+  return r * kDQS + ((((col >> 3) ^ dswz(r)) << 3) | (col & 7));
+}
+
 // APPEND (HCA decode steps, dense rows, n_q = 1): the step's state append runs
 // here (DecodeAppend).  Every workgroup takes the query position p from
 // n_tokens.  The one that holds the window slot of position p RMS-normalises
@@ -713,7 +726,7 @@ __global__ __launch_bounds__(64 * kD8Waves) void attn_decode_kernel(
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse, KvPages pg,
     DecodeAppend ap) {
   constexpr int NW = kD8Waves;
-  __shared__ __attribute__((aligned(16))) uint16_t kv_s[2][kMT * kQS];
+  __shared__ __attribute__((aligned(16))) uint16_t kv_s[2][kMT * kDQS];
   // APPEND: the stored bytes of the new window row [0] and of the new entry [1]
   __shared__ __attribute__((aligned(16))) uint4 app_s[APPEND ? 2 : 1][APPEND ? kMC * 2 / 16 : 1];
   __shared__ float2 rope_s[kRopeDims / 2];  // (cos, sin) of the query position's angles
@@ -792,7 +805,7 @@ __global__ __launch_bounds__(64 * kD8Waves) void attn_decode_kernel(
         if (lane < 56) v = c;
       }
       if (!((mask8 >> i) & 1u)) v = make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(&kv_s[buf][(w + NW * i) * kQS + lane * 8]) = v;
+      *reinterpret_cast<uint4*>(&kv_s[buf][dkv(w + NW * i, lane * 8)]) = v;
     }
     if constexpr (APPEND) {
       // the rows this workgroup made replace what was loaded for their slots
@@ -812,7 +825,7 @@ __global__ __launch_bounds__(64 * kD8Waves) void attn_decode_kernel(
             v = make_uint4(fp8x2_to_bf16x2<false>(h.x), fp8x2_to_bf16x2<true>(h.x),
                            fp8x2_to_bf16x2<false>(h.y), fp8x2_to_bf16x2<true>(h.y));
           }
-          *reinterpret_cast<uint4*>(&kv_s[buf][r * kQS + lane * 8]) = v;
+          *reinterpret_cast<uint4*>(&kv_s[buf][dkv(r, lane * 8)]) = v;
         }
       }
     }
@@ -972,12 +985,15 @@ __global__ __launch_bounds__(64 * kD8Waves) void attn_decode_kernel(
     {
       acc[0] = v16f_t{0};
       acc[1] = v16f_t{0};
-      const uint16_t* kb0 = &kv_s[buf][j32 * kQS + 128 * kq + 8 * g];
-      const uint16_t* kb1 = &kv_s[buf][(32 + j32) * kQS + 128 * kq + 8 * g];
+      // rows j32 and 32 + j32 share their swizzle (it depends on r mod 16)
+      const uint16_t* kb0 = &kv_s[buf][j32 * kDQS];
+      const uint16_t* kb1 = &kv_s[buf][(32 + j32) * kDQS];
+      const int kc = 16 * kq + g, sw = dswz(j32);
 #pragma unroll
       for (int ks = 0; ks < kMC / 64; ++ks) {
-        const uint4 a0 = *reinterpret_cast<const uint4*>(kb0 + 16 * ks);
-        const uint4 a1 = *reinterpret_cast<const uint4*>(kb1 + 16 * ks);
+        const int off = ((kc + 2 * ks) ^ sw) << 3;  // chunk 16 kq + g + 2 ks, permuted
+        const uint4 a0 = *reinterpret_cast<const uint4*>(kb0 + off);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(kb1 + off);
         acc[0] = mfma_bf16(as_v8bf(a0), as_v8bf(qf[ks]), acc[0]);
         acc[1] = mfma_bf16(as_v8bf(a1), as_v8bf(qf[ks]), acc[1]);
       }
@@ -1067,9 +1083,9 @@ __global__ __launch_bounds__(64 * kD8Waves) void attn_decode_kernel(
       const v8bf_t A = as_v8bf(*reinterpret_cast<const uint4*>(&p_s[head * kPS + 16 * ks + 8 * g]));
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const uint16_t* vp = &kv_s[buf][(16 * ks + 8 * g + tr_r) * kQS + 128 * kq + 32 * db + tr_d];
-        const uint2 lo = tr_rows4(vp);
-        const uint2 hi = tr_rows4(vp + 4 * kQS);
+        const int vr = 16 * ks + 8 * g + tr_r, vc = 128 * kq + 32 * db + tr_d;
+        const uint2 lo = tr_rows4(&kv_s[buf][dkv(vr, vc)]);
+        const uint2 hi = tr_rows4(&kv_s[buf][dkv(vr + 4, vc)]);
         o[db] = mfma_bf16(A, as_v8bf(make_uint4(lo.x, lo.y, hi.x, hi.y)), o[db]);
       }
     }
