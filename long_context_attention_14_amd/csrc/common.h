@@ -329,10 +329,17 @@ __device__ __forceinline__ uint32_t score_bin(uint32_t key) { return key >> 20; 
 // scores fall in do not make one hot line for the atomics of many workgroups.
 __device__ __forceinline__ int hist_slot(int b) { return ((b & 31) << 7) | (b >> 5); }
 __device__ __forceinline__ int hist_bin_of_slot(int w) { return ((w & 127) << 5) | (w >> 7); }
+// LDS word of bin b in a row histogram copied out of global memory: one pad
+// word per 64 bins.  The coalesced copy has the 64 lanes of a wave write bins
+// 32 apart (two banks without the pad) and the threshold scans read bins
+// 4096 / blockDim.x apart; with the pad both touch 64 distinct banks.
+constexpr int kHistLdsWords = kScoreHistBins + kScoreHistBins / 64;
+__device__ __forceinline__ int hist_lds(int b) { return b + (b >> 6); }
 
 // Threshold of a row from its histogram in LDS (kScoreHistBins bins, bin
-// order == key order): the bin holding the want-th largest key and the count
-// of keys in higher bins.  All threads of the block call it; blockDim.x must
+// order == key order, bin b at word hist_lds(b)): the bin holding the want-th
+// largest key and the count of keys in higher bins.  All threads of the block
+// call it; blockDim.x must
 // divide kScoreHistBins and be a multiple of 64; scan_sh holds blockDim.x/64
 // ints.  Thread t owns bins [4095 - per*t - per + 1, 4095 - per*t].
 __device__ inline void find_threshold_block(const uint32_t* lh, int want, int* sh_bin,
@@ -341,7 +348,7 @@ __device__ inline void find_threshold_block(const uint32_t* lh, int want, int* s
   const int per = kScoreHistBins / nt;
   const int top = kScoreHistBins - 1 - per * t;
   int local = 0;
-  for (int i = 0; i < per; ++i) local += static_cast<int>(lh[top - i]);
+  for (int i = 0; i < per; ++i) local += static_cast<int>(lh[hist_lds(top - i)]);
   int incl = local;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -355,7 +362,7 @@ __device__ inline void find_threshold_block(const uint32_t* lh, int want, int* s
   int run = before + incl - local;
   if (run < want && run + local >= want) {
     for (int i = 0; i < per; ++i) {
-      const int h = static_cast<int>(lh[top - i]);
+      const int h = static_cast<int>(lh[hist_lds(top - i)]);
       if (run + h >= want) {
         *sh_bin = top - i;
         *sh_above = run;

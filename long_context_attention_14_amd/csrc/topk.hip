@@ -274,7 +274,7 @@ __device__ void row_threshold(const uint32_t* gh, uint32_t* lh, int vis, int k, 
     return;
   }
   // read in word order (coalesced), place by bin
-  for (int w = threadIdx.x; w < kHistBins; w += blockDim.x) lh[hist_bin_of_slot(w)] = gh[w];
+  for (int w = threadIdx.x; w < kHistBins; w += blockDim.x) lh[hist_lds(hist_bin_of_slot(w))] = gh[w];
   __syncthreads();
   find_threshold_block(lh, k, sh_bin, sh_above, scan_sh);
 }
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kSegThreads) void topk_collect_kernel(
     const ST* __restrict__ scores, int N_cap, int n_q, const int32_t* __restrict__ q_pos, int m,
     const int32_t* __restrict__ n_entries, int k, int n_seg, WideWs ws) {
   __shared__ int wtot_s[kSegThreads / 64], wtot_c[kSegThreads / 64];
-  __shared__ uint32_t lh[kHistBins];
+  __shared__ uint32_t lh[kHistLdsWords];
   __shared__ int sh_bin, sh_above, scan_sh[kSegThreads / 64];
   const long long row = blockIdx.x / n_seg;
   const int seg = blockIdx.x % n_seg;
@@ -479,7 +479,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
   __shared__ uint32_t hist[256];
   __shared__ int sh_bin, sh_above, sh_b2, sh_a2;
   __shared__ uint32_t wgt[kRowThreads / 64], weq[kRowThreads / 64];
-  __shared__ uint32_t lh[kHistBins];
+  __shared__ uint32_t lh[kHistLdsWords];
   __shared__ int scan_sh[kRowThreads / 64];
   __shared__ uint32_t ck_s[kCandLds];
   __shared__ int32_t ci_s[kCandLds];
@@ -660,7 +660,7 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     const int32_t* __restrict__ n_entries, int k, SelectWs o, int32_t* __restrict__ sel_idx,
     long long rows, StateAppend app) {
   constexpr int NT = kFinThreads;
-  __shared__ uint32_t lh[kScoreHistBins];
+  __shared__ uint32_t lh[kHistLdsWords];
   __shared__ int32_t sel[kMaxK];
   __shared__ __attribute__((aligned(16))) uint32_t cand[2 * kFinCand];  // keys, indices; then the output bitmap
   if (app.tokC && static_cast<long long>(blockIdx.x) >= rows) {
@@ -715,7 +715,7 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   int32_t* out = sel_idx + row * k;
   const int n_part = min(wpr, (vis + kSelBlock - 1) / kSelBlock);
 #pragma unroll
-  for (int u = 0; u < kHv; ++u) lh[hist_bin_of_slot(tid + u * NT)] = hv[u];
+  for (int u = 0; u < kHv; ++u) lh[hist_lds(hist_bin_of_slot(tid + u * NT))] = hv[u];
   if (tid == 0) {
     sh_nsel = 0;
     sh_ncand = 0;
@@ -728,12 +728,12 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   const int topb = kScoreHistBins - 1 - per * tid;
   int local = 0;
 #pragma unroll
-  for (int i = 0; i < per; ++i) local += static_cast<int>(lh[topb - i]);
+  for (int i = 0; i < per; ++i) local += static_cast<int>(lh[hist_lds(topb - i)]);
   int total;
   int run = block_excl_scan<kFinWaves>(local, &total, scan_sh);
   if (run < k && run + local >= k) {
     for (int i = 0; i < per; ++i) {
-      const int h = static_cast<int>(lh[topb - i]);
+      const int h = static_cast<int>(lh[hist_lds(topb - i)]);
       if (run + h >= k) {
         sh_bin = topb - i;
         sh_above = run;
@@ -744,7 +744,7 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   }
   __syncthreads();
   const int bstar = sh_bin, above = sh_above;
-  const int C = static_cast<int>(lh[bstar]);
+  const int C = static_cast<int>(lh[hist_lds(bstar)]);
   const int need = k - above;  // 1 <= need <= C
   const bool cand_lds = C <= kFinCand;
   uint32_t* gck = o.cand_key + row * N_cap;
