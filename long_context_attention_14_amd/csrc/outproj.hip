@@ -17,12 +17,10 @@
 // stay deterministic).
 // Few tokens (M <= 32, a decode batch; HBM-bound: the V4-Pro shape streams
 // 176 MiB of weights for 16 tokens): a workgroup owns 32 output columns, its
-// waves take interleaved 64-wide K steps and load their operands straight from
-// memory into MFMA registers, two steps ahead in two named register sets (no
-// LDS staging, no barrier in the loop); the waves' partial tiles are summed in
-// wave order through LDS at the end.  It reaches about 45% of HBM peak; a third
-// step in flight did not raise that (each step of a wave reads 128-byte segments
-// of 32 different weight rows).
+// waves take interleaved 64-wide K steps, the weight rows reach LDS in long
+// contiguous segments a few chunks ahead, each workgroup starts at its own
+// point of K (see gemm_skinny_kernel), and the waves' partial tiles are summed
+// in wave order through LDS at the end.
 #include "common.h"
 
 namespace lca {
@@ -50,6 +48,8 @@ struct GemmArgs {
 };
 
 __device__ __forceinline__ gv8bf as8(uint4 u) { return __builtin_bit_cast(gv8bf, u); }
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ gv8bf as8v(u32x4 u) { return __builtin_bit_cast(gv8bf, u); }
 
 template <int BM>
 __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a) {
@@ -218,64 +218,127 @@ __global__ __launch_bounds__(256) void gemm_split_sum_kernel(GemmArgs a) {
   }
 }
 
-// Few tokens: see the file comment.  NW waves per workgroup, 32 columns.
+// Few tokens: see the file comment.  NW waves per workgroup, 32 columns.  K
+// goes in chunks of NW 64-wide steps, step c NW + w of chunk c belonging to
+// wave w.  A chunk's 32 weight rows are loaded as whole row segments (64 NW
+// consecutive 16-byte pieces per row: one load instruction of a wave covers
+// 0.5 or 1 KiB of memory), three chunks ahead in named register sets, stored to
+// double-buffered LDS (rows padded by 16 bytes) and read from there as MFMA
+// operands; the tokens' operands come straight from memory (they stay in L2).
 template <int NW>
 __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmArgs a) {
+  constexpr int NT = 64 * NW;
+  constexpr int CK = kGBK * NW;               // K of a chunk
+  constexpr int kRowPieces = CK / 8;          // 16-byte pieces of a row in a chunk
+  constexpr int PPT = 32 * kRowPieces / NT;   // pieces a thread loads per chunk
+  constexpr int kSRow = CK + 8;               // LDS row stride (bf16)
+  static_assert(PPT * NT == 32 * kRowPieces, "whole pieces per thread");
+  __shared__ __attribute__((aligned(16))) uint16_t wt[2][32 * kSRow];
   __shared__ float red[NW][32][33];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j32 = lane & 31, g = lane >> 5;
   const int n0 = blockIdx.x * 32;
   const int batch = blockIdx.y;
-  // lane (j32, g): B operand = W row n0 + j32, A operand = A row j32 (rows past
-  // M read row M-1 and are zeroed), 8 K values at 16 ks + 8 g of each step
-  const uint16_t* Wr = a.W + batch * a.w_bstride + static_cast<long long>(n0 + j32) * a.K + 8 * g;
-  const bool arow = j32 < a.M;
+  const uint16_t* Wb = a.W + batch * a.w_bstride + static_cast<long long>(n0) * a.K;
+  // lane (j32, g): A operand = A row j32 (rows past M read row M-1: they only
+  // reach output rows past M, which are not stored), B operand = W row
+  // n0 + j32; 8 K values at 16 ks + 8 g of a step
   const uint16_t* Ar = a.A + batch * a.a_bstride + static_cast<long long>(min(j32, a.M - 1)) * a.lda + 8 * g;
   const int steps = a.K / kGBK;
-  struct Ops {
-    uint4 w[4], x[4];
+  const int nch = (steps + NW - 1) / NW;
+  static_assert(PPT == 4, "four pieces a thread per chunk");
+  // (plain vector types: copies of HIP's uint4 struct between address spaces
+  // become memcpy calls that keep the sets in scratch memory)
+  struct WSet {
+    u32x4 v0, v1, v2, v3;
   };
-  auto load = [&](Ops& o, int st) {  // steps past the end read the last one (not used)
-    const int k0 = min(st, steps - 1) * kGBK;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) o.w[ks] = *reinterpret_cast<const uint4*>(Wr + k0 + 16 * ks);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) o.x[ks] = *reinterpret_cast<const uint4*>(Ar + k0 + 16 * ks);
+  struct ASet {
+    u32x4 x0, x1, x2, x3;
+  };
+  // piece p = tid + NT i of chunk c: row p / kRowPieces, columns
+  // c CK + 8 (p % kRowPieces) .. + 7 (chunks past the last read column K - 8
+  // and are never multiplied)
+  // Workgroup L takes the chunks in the order L, L + 1, ... (mod nch): the
+  // rows of a weight matrix are a power-of-two number of bytes apart, and with
+  // every workgroup at the same K offset the reads crowd onto a fraction of the
+  // HBM channels (same work in the same order: 47 against 40 us for the
+  // 16-token projection).  phys(c) is the chunk taken c-th; nch for the
+  // clamped loads past the last one.
+  const int rot = static_cast<int>((blockIdx.x + static_cast<long long>(blockIdx.y) * gridDim.x) % nch);
+  auto phys = [&](int c) { return c < nch ? (c + rot) % nch : nch; };
+  auto wptr = [&](int c, int i) {
+    const int p = tid + NT * i;
+    const int col = min(phys(c) * CK + 8 * (p % kRowPieces), a.K - 8);
+    return reinterpret_cast<const u32x4*>(Wb + static_cast<long long>(p / kRowPieces) * a.K + col);
+  };
+  auto load_w = [&](WSet& s, int c) {
+    s.v0 = *wptr(c, 0);
+    s.v1 = *wptr(c, 1);
+    s.v2 = *wptr(c, 2);
+    s.v3 = *wptr(c, 3);
+  };
+  auto wlds = [&](int buf, int i) {
+    const int p = tid + NT * i;
+    return reinterpret_cast<u32x4*>(&wt[buf][(p / kRowPieces) * kSRow + 8 * (p % kRowPieces)]);
+  };
+  auto store_w = [&](const WSet& s, int buf) {
+    *wlds(buf, 0) = s.v0;
+    *wlds(buf, 1) = s.v1;
+    *wlds(buf, 2) = s.v2;
+    *wlds(buf, 3) = s.v3;
+  };
+  auto load_a = [&](ASet& s, int c) {  // the wave's step of chunk c (clamped)
+    const u32x4* ap = reinterpret_cast<const u32x4*>(Ar + min(phys(c) * NW + w, steps - 1) * kGBK);
+    s.x0 = ap[0];
+    s.x1 = ap[2];
+    s.x2 = ap[4];
+    s.x3 = ap[6];
   };
   gv16f acc = gv16f{0};
-  auto mma = [&](const Ops& o) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint4 x = arow ? o.x[ks] : make_uint4(0, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8(x), as8(o.w[ks]), acc, 0, 0, 0);
-    }
+  auto mma = [&](const ASet& s, int c) {
+    if (phys(c) * NW + w >= steps) return;  // (the same for the whole wave)
+    const u32x4* wr = reinterpret_cast<const u32x4*>(&wt[c & 1][j32 * kSRow + kGBK * w + 8 * g]);
+    const u32x4 b0 = wr[0], b1 = wr[2], b2 = wr[4], b3 = wr[6];
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8v(s.x0), as8v(b0), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8v(s.x1), as8v(b1), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8v(s.x2), as8v(b2), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as8v(s.x3), as8v(b3), acc, 0, 0, 0);
   };
-  // wave w takes steps w, w + NW, ...; two named operand sets of two steps
-  // each, so two steps are in flight while two are multiplied (vector loads
-  // complete in order: each product waits only for its own set)
-  Ops p0, p1, q0, q1;
-  int st = w;
-  load(p0, st);
-  load(p1, st + NW);
-  while (true) {
-    if (st >= steps) break;
-    load(q0, st + 2 * NW);
-    load(q1, st + 3 * NW);
-    mma(p0);
-    if (st + NW < steps) mma(p1);
-    st += 2 * NW;
-    if (st >= steps) break;
-    load(p0, st + 2 * NW);
-    load(p1, st + 3 * NW);
-    mma(q0);
-    if (st + NW < steps) mma(q1);
-    st += 2 * NW;
+  // The j-th chunk taken lives in the sets (wj, aj), j mod 3: the weights of
+  // chunk j + 1 are stored to LDS after chunk j's products, into the buffer
+  // that chunk j - 1 used (every wave was done with it before the barrier that
+  // ended step j - 1), and that set is refilled with chunk j + 4.  Loads and
+  // stores past the last chunk are clamped and unused: with no branch around
+  // them, each wait covers exactly its own set.
+  WSet w0, w1, w2;
+  ASet a0, a1, a2;
+  load_a(a0, 0);
+  load_w(w0, 0);
+  load_a(a1, 1);
+  load_w(w1, 1);
+  load_a(a2, 2);
+  load_w(w2, 2);
+  store_w(w0, 0);
+  load_w(w0, 3);
+  __syncthreads();
+  for (int c = 0; c < nch; c += 3) {
+#define LCA_SKINNY_STEP(AC, WN, C) \
+  mma(AC, C);                      \
+  load_a(AC, (C) + 3);             \
+  store_w(WN, ((C) + 1) & 1);      \
+  load_w(WN, (C) + 4);             \
+  __syncthreads();
+    LCA_SKINNY_STEP(a0, w1, c)
+    LCA_SKINNY_STEP(a1, w2, c + 1)
+    LCA_SKINNY_STEP(a2, w0, c + 2)
+#undef LCA_SKINNY_STEP
   }
   // register r of lane (j32, g): output row 8 (r/4) + 4 g + r%4, column n0 + j32
 #pragma unroll
   for (int r = 0; r < 16; ++r) red[w][8 * (r >> 2) + 4 * g + (r & 3)][j32] = acc[r];
   __syncthreads();
-  for (int i = tid; i < a.M * 32; i += 64 * NW) {
+  for (int i = tid; i < a.M * 32; i += NT) {
     const int m = i >> 5, nn = i & 31;
     float v = 0.f;
 #pragma unroll
