@@ -220,9 +220,9 @@ __global__ __launch_bounds__(256) void gemm_split_sum_kernel(GemmArgs a) {
 
 // Few tokens: see the file comment.  NW waves per workgroup, 32 columns.  K
 // goes in chunks of NW 64-wide steps, step c NW + w of chunk c belonging to
-// wave w.  A chunk's 32 weight rows are loaded as whole row segments (64 NW
-// consecutive 16-byte pieces per row: one load instruction of a wave covers
-// 0.5 or 1 KiB of memory), three chunks ahead in named register sets, stored to
+// wave w.  A chunk's 32 weight rows are loaded as whole row segments (8 NW
+// consecutive 16-byte pieces per row: with four waves one load instruction of
+// a wave covers two rows' 512 bytes), three chunks ahead in named register sets, stored to
 // double-buffered LDS (rows padded by 16 bytes) and read from there as MFMA
 // operands; the tokens' operands come straight from memory (they stay in L2).
 template <int NW>
@@ -371,12 +371,11 @@ size_t gemm_ws_bytes(int M, int N, int K, int batches) {
 
 hipError_t launch_gemm(GemmArgs a, void* ws, hipStream_t s) {
   if (a.M <= kSkinnyM) {
-    // eight waves per workgroup when the column tiles alone leave CUs idle
+    // four waves per workgroup (the 16-token batch: 37.0 us against 51.3 with
+    // two and 44.7 with eight waves where the column tiles are fewer than the
+    // CUs; the output stage's 224 workgroups take 19.4 us with four)
     const dim3 grid(static_cast<unsigned>(a.N / 32), static_cast<unsigned>(a.batches));
-    if (static_cast<long long>(a.N / 32) * a.batches >= 256)
-      hipLaunchKernelGGL(gemm_skinny_kernel<4>, grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL(gemm_skinny_kernel<8>, grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL(gemm_skinny_kernel<4>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
   }
   a.n_split = gemm_splits(a.M, a.N, a.K, a.batches);

@@ -1226,9 +1226,9 @@ def _check_out_proj(nt, n_h, c, g, d_g, d, out_fmt, rows=None, seed=3):
     (40, 16, 256, 4, 256, 384, "f32"),        # 32-row tiles
     (300, 16, 256, 8, 256, 1024, "bf16"),     # 128-row tiles with a ragged last tile
     (1, 64, 512, 1, 128, 128, "f32"),         # one group, one token
-    # few-token kernel: K chunks taken from a per-workgroup start, the last one partial
-    (7, 6, 128, 1, 128, 256, "f32"),          # 8 waves: 12 K steps in chunks of 8
-    (3, 24, 128, 8, 1024, 256, "bf16"),       # 4 waves (256 workgroups): 6 K steps in chunks of 4
+    # few-token kernel: K chunks of four steps taken from a per-workgroup start
+    (7, 5, 128, 1, 128, 256, "f32"),          # 10 and 2 K steps: last chunk partial
+    (3, 24, 128, 8, 1024, 256, "bf16"),       # 6 K steps (256 workgroups), then 128
     (32, 16, 256, 4, 256, 384, "f32"),        # the most tokens the few-token kernel takes
 ])
 def test_grouped_out_proj(nt, n_h, c, g, d_g, d, out_fmt):
