@@ -106,28 +106,39 @@ __global__ __launch_bounds__(kRowThreads) void topk_lds_kernel(
     for (int i = tid; i < k; i += kRowThreads) out[i] = i < vis ? i : -1;
     return;
   }
-  // keys to LDS, eight loads in flight per thread (clamped addresses, unconditional)
+  // keys to LDS: every load of the row goes out at once (at most kMaxRounds
+  // per thread; with eight at a time the row took four to five dependent
+  // memory round trips), and the first radix pass (the top 8 bits of every
+  // key) is counted as the keys are stored
   const ST* src = scores + row * N_cap;
-  for (int base = 0; base < vis; base += 8 * kRowThreads) {
-    ST v[8];
+  const int n_rounds = (vis + kRowThreads - 1) / kRowThreads;
+  ST v[kMaxRounds];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = src[min(base + u * kRowThreads + tid, vis - 1)];
+  for (int u = 0; u < kMaxRounds; ++u)
+    if (u < n_rounds) v[u] = src[min(u * kRowThreads + tid, vis - 1)];
+  for (int i = tid; i < kHistCopies * kHistStride; i += kRowThreads) hc[i] = 0;
+  __syncthreads();
+  uint32_t* my_copy = hc + (lane % kHistCopies) * kHistStride;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = base + u * kRowThreads + tid;
-      if (i < vis) keys[i] = stored_key(v[u]);
+  for (int u = 0; u < kMaxRounds; ++u) {
+    const int i = u * kRowThreads + tid;
+    if (u < n_rounds && i < vis) {
+      const uint32_t key = stored_key(v[u]);
+      keys[i] = key;
+      atomicAdd(&my_copy[key >> 24], 1u);
     }
   }
   uint32_t prefix = 0, mask = 0;
   int remaining = k;
   constexpr int kLowShift = sizeof(ST) == 2 ? 16 : 0;  // bf16 keys have no low 16 bits
-  uint32_t* my_copy = hc + (lane % kHistCopies) * kHistStride;
   for (int shift = 24; shift >= kLowShift; shift -= 8) {
-    for (int i = tid; i < kHistCopies * kHistStride; i += kRowThreads) hc[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < vis; i += kRowThreads) {
-      const uint32_t key = keys[i];
-      if ((key & mask) == prefix) atomicAdd(&my_copy[(key >> shift) & 0xffu], 1u);
+    if (shift != 24) {  // (the first pass was counted with the loads)
+      for (int i = tid; i < kHistCopies * kHistStride; i += kRowThreads) hc[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < vis; i += kRowThreads) {
+        const uint32_t key = keys[i];
+        if ((key & mask) == prefix) atomicAdd(&my_copy[(key >> shift) & 0xffu], 1u);
+      }
     }
     __syncthreads();
     if (tid < 256) {
@@ -148,7 +159,6 @@ __global__ __launch_bounds__(kRowThreads) void topk_lds_kernel(
 
   // compaction in index order: entry i = 1024 r + tid.  Per-wave counts of
   // every round, one scan over (round, wave), then the writes.
-  const int n_rounds = (vis + kRowThreads - 1) / kRowThreads;
   for (int r = 0; r < n_rounds; ++r) {
     const int i = r * kRowThreads + tid;
     const uint32_t key = i < vis ? keys[i] : 0u;
