@@ -222,9 +222,10 @@ __global__ __launch_bounds__(256) void gemm_split_sum_kernel(GemmArgs a) {
 // goes in chunks of NW 64-wide steps, step c NW + w of chunk c belonging to
 // wave w.  A chunk's 32 weight rows are loaded as whole row segments (8 NW
 // consecutive 16-byte pieces per row: with four waves one load instruction of
-// a wave covers two rows' 512 bytes), three chunks ahead in named register sets, stored to
-// double-buffered LDS (rows padded by 16 bytes) and read from there as MFMA
-// operands; the tokens' operands come straight from memory (they stay in L2).
+// a wave covers 512 bytes of each of two rows), three chunks ahead in named
+// register sets, stored to double-buffered LDS (rows padded by 16 bytes) and
+// read from there as MFMA operands; the tokens' operands come straight from
+// memory (they stay in L2).
 template <int NW>
 __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmArgs a) {
   constexpr int NT = 64 * NW;
@@ -256,9 +257,6 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmArgs a) {
   struct ASet {
     u32x4 x0, x1, x2, x3;
   };
-  // piece p = tid + NT i of chunk c: row p / kRowPieces, columns
-  // c CK + 8 (p % kRowPieces) .. + 7 (chunks past the last read column K - 8
-  // and are never multiplied)
   // Workgroup L takes the chunks in the order L, L + 1, ... (mod nch): the
   // rows of a weight matrix are a power-of-two number of bytes apart, and with
   // every workgroup at the same K offset the reads crowd onto a fraction of the
@@ -267,6 +265,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmArgs a) {
   // clamped loads past the last one.
   const int rot = static_cast<int>((blockIdx.x + static_cast<long long>(blockIdx.y) * gridDim.x) % nch);
   auto phys = [&](int c) { return c < nch ? (c + rot) % nch : nch; };
+  // piece p = tid + NT i of the c-th chunk: row p / kRowPieces, columns
+  // phys(c) CK + 8 (p % kRowPieces) .. + 7 (past the last chunk: column K - 8,
+  // never multiplied)
   auto wptr = [&](int c, int i) {
     const int p = tid + NT * i;
     const int col = min(phys(c) * CK + 8 * (p % kRowPieces), a.K - 8);
