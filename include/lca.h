@@ -93,7 +93,7 @@
 extern "C" {
 #endif
 
-#define LCA_ABI_VERSION 4
+#define LCA_ABI_VERSION 5
 
 /* A hipStream_t. */
 typedef struct ihipStream_t* lca_stream_t;
@@ -450,7 +450,10 @@ int lca_device_checks(uint64_t* violations, int reset);
  * A CSA step with the fused selection (bf16 io, c = 512) runs the append as
  * extra workgroups of the selection's finish launch, one per sequence, and a
  * light launch before the indexer writes the query positions and clears the
- * selection's histogram -- again the bits of the separate calls.
+ * selection's histogram -- again the bits of the separate calls.  With a
+ * sel_hist state buffer (below) that light launch goes: the indexer takes the
+ * positions from n_tokens itself and the finish pass leaves the histogram
+ * cleared for the next step.
  * ------------------------------------------------------------------------- */
 typedef struct lca_decode_layer {
   size_t struct_size;   /* sizeof(lca_decode_layer) */
@@ -472,6 +475,14 @@ typedef struct lca_decode_layer {
   lca_kv_pages pages;   /* paged cache (pages.block_table == NULL: contiguous [B, N_cap, row]) */
   int split_rows;       /* the attention's chunk length (see lca_sparse_mqa): 0 = automatic,
                            else fixed, which makes every sequence's bits independent of B */
+  /* (ABI version 5) */
+  uint32_t* sel_hist;   /* CSA: [B, 4096] uint32 device, or NULL.  The fused selection's row
+                           histogram kept with the layer's state: zero-filled by the caller
+                           before the layer's first step (and after any step that failed to
+                           enqueue in full), left zero-filled by every step.  Used only by steps
+                           that take the fused selection; with it the step needs no launch to
+                           clear a histogram before the indexer.  NULL: the histogram lives in
+                           the workspace and every step clears it first. */
 } lca_decode_layer;
 
 typedef struct lca_decode_io {

@@ -92,7 +92,7 @@ class DecodeLayer(ctypes.Structure):
                 ("sink", P), ("tau", c_float), ("eps", c_float),
                 ("k", c_int), ("H_I", c_int), ("d_I", c_int), ("idx_dtype", c_int),
                 ("kI", P), ("kI_scale", P), ("rope_base", c_float), ("pages", KvPages),
-                ("split_rows", c_int)]
+                ("split_rows", c_int), ("sel_hist", P)]
 
 
 class DecodeIO(ctypes.Structure):

@@ -501,10 +501,18 @@ int decode_enqueue(const lca_decode_layer* L, const lca_decode_io* io, void* wor
   lca::SelectWs sw{};
   uint32_t* hist = nullptr;
   long long zero_words = 0;
+  // sel_hist: the histogram kept (zero-filled) with the layer's state instead,
+  // which the finish pass leaves cleared, so nothing clears it before the indexer
+  const bool state_hist = fused && L->sel_hist != nullptr;
   if (fused) {
     sw = lca::select_ws_in(ws + d.topk, L->B, L->N_cap);
-    hist = sw.hist;
-    zero_words = lca::select_zero_words(L->B);
+    if (state_hist) {
+      sw.hist = L->sel_hist;
+      sw.clear_hist = 1;
+    } else {
+      hist = sw.hist;
+      zero_words = lca::select_zero_words(L->B);
+    }
   } else if (csa && L->idx_dtype != LCA_F32) {
     hist = lca::topk_hist_in_workspace(ws + d.topk, L->B, 1, L->N_cap, L->k);
     zero_words = hist ? lca::topk_hist_words(L->B) : 0;
@@ -538,10 +546,16 @@ int decode_enqueue(const lca_decode_layer* L, const lca_decode_io* io, void* wor
     app.eps = L->eps;
     app.rope_step = rope_step(L->rope_base);
     app.pg = pg;
-    st = hip_status(lca::launch_decode_prep(L->m, L->B, L->N_cap, L->n_tokens, q_pos, n_ent, hist,
-                                            zero_words, s),
-                    "lca_decode_step/prep");
-    if (st != LCA_OK) return st;
+    if (state_hist) {  // the indexer takes the positions from n_tokens itself
+      sw.n_tokens = L->n_tokens;
+      sw.q_pos_out = q_pos;
+      sw.n_entries_out = n_ent;
+    } else {
+      st = hip_status(lca::launch_decode_prep(L->m, L->B, L->N_cap, L->n_tokens, q_pos, n_ent, hist,
+                                              zero_words, s),
+                      "lca_decode_step/prep");
+      if (st != LCA_OK) return st;
+    }
   } else if (fused_append) {
     ap.tokC = static_cast<const uint8_t*>(io->tokC);
     ap.tokZ = static_cast<const uint8_t*>(io->tokZ);

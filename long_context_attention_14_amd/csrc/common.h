@@ -440,6 +440,17 @@ struct SelectWs {
   uint32_t* cand_key;  // [rows, N_cap] selection: threshold-bin keys when LDS overflows
   int32_t* cand_idx;   // [rows, N_cap]
   int n_blk;
+  // clear_hist != 0: the finish pass zero-fills each row's histogram once it has
+  // read it, so the next launch on the same hist needs no clearing first
+  int clear_hist;
+  // decode steps (n_q = 1) only, or NULL: the indexer takes each row's position
+  // from n_tokens (p = n_tokens[b]; n_entries = min((p+1)/m, N_cap)) instead of
+  // from q_pos / n_entries, and its workgroup 0 of the row writes both there for
+  // the launches after it (a negative count: q_pos / n_entries are read and left
+  // as they are)
+  const int32_t* n_tokens;
+  int32_t* q_pos_out;
+  int32_t* n_entries_out;
 };
 // first slot of workgroup wi's region in a row's emit array: workgroups before
 // wi own n_blk / wpr blocks each, one more when they come before n_blk % wpr

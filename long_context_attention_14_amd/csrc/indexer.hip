@@ -407,7 +407,25 @@ __global__ __launch_bounds__(kSelThreads, 1) void indexer_select_kernel(
   const long long row = blockIdx.x % rows;
   const int wi = static_cast<int>(blockIdx.x / rows);
   const int b = static_cast<int>(row / n_q);
-  const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
+  int qp, ne;
+  if (sel.n_tokens) {  // a decode step's position, straight from the token count
+    const int p = sel.n_tokens[b];
+    if (p >= 0) {
+      qp = p;
+      ne = min((p + 1) / m, N_cap);
+      if (wi == 0 && threadIdx.x == 0) {
+        sel.q_pos_out[row] = qp;
+        sel.n_entries_out[b] = ne;
+      }
+    } else {
+      qp = q_pos[row];
+      ne = n_entries[b];
+    }
+  } else {
+    qp = q_pos[row];
+    ne = n_entries[b];
+  }
+  const int vis = visible_entries(qp, m, ne, N_cap);
   int32_t* out = sel_idx + row * k;
   if (vis <= k) {  // every visible entry is selected: no scores needed
     if (wi == 0)

@@ -726,6 +726,11 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   const int n_part = min(wpr, (vis + kSelBlock - 1) / kSelBlock);
 #pragma unroll
   for (int u = 0; u < kHv; ++u) lh[hist_lds(hist_bin_of_slot(tid + u * NT))] = hv[u];
+  if (o.clear_hist) {  // (after the words' own loads: their values were used just above)
+    uint32_t* ghw = o.hist + row * kScoreHistBins;
+#pragma unroll
+    for (int u = 0; u < kHv; ++u) ghw[tid + u * NT] = 0u;
+  }
   if (tid == 0) {
     sh_nsel = 0;
     sh_ncand = 0;
@@ -1059,7 +1064,7 @@ long long select_zero_words(long long rows) { return rows * kHistBins; }
 SelectWs select_ws_in(void* ws, long long rows, int N_cap) {
   const SelectLayout L = select_layout(rows, N_cap);
   char* p = static_cast<char*>(ws);
-  SelectWs w;
+  SelectWs w{};
   w.hist = reinterpret_cast<uint32_t*>(p + L.hist);
   w.emit_cnt = reinterpret_cast<int32_t*>(p + L.emit_cnt);
   w.emit = reinterpret_cast<uint2*>(p + L.emit);

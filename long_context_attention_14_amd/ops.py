@@ -15,6 +15,8 @@ import torch
 from . import _lib
 from ._lib import FMT, MODE, OP, DecodeIO, DecodeLayer, KvPages, check, lib
 
+SEL_HIST_BINS = 4096  # words per sequence of a decode layer's sel_hist buffer
+
 _ROW_BYTES = {"f32": lambda c: 4 * c, "bf16": lambda c: 2 * c, "fp8": lambda c: c,
               "fp8_bf16rope": lambda c: c + 64, "mxfp4": lambda c: c // 2}
 
@@ -258,10 +260,10 @@ class DecodeLayerState:
 
     def __init__(self, *, mode, m, B, c, H, n_win, N_cap, io_fmt, kv_fmt, tailC, tailZ, ring, cache,
                  n_tokens, P, sink=None, tau=None, eps=1e-6, k=0, H_I=0, d_I=0, idx_fmt="fp8",
-                 kI=None, kI_scale=None, rope_base=0.0, pages=None, split_rows=0):
+                 kI=None, kI_scale=None, rope_base=0.0, pages=None, split_rows=0, sel_hist=None):
         T = 2 * m if mode == "csa" else m
         iob, kvb = row_bytes(io_fmt, c), row_bytes(kv_fmt, c)
-        self.keep = [tailC, tailZ, ring, cache, n_tokens, P, sink, kI, kI_scale, pages]
+        self.keep = [tailC, tailZ, ring, cache, n_tokens, P, sink, kI, kI_scale, pages, sel_hist]
         s = DecodeLayer()
         s.struct_size = ctypes.sizeof(DecodeLayer)
         s.mode, s.m, s.B, s.c, s.H, s.n_win, s.N_cap = MODE[mode], m, B, c, H, n_win, N_cap
@@ -284,6 +286,8 @@ class DecodeLayerState:
             s.k, s.H_I, s.d_I, s.idx_dtype = k, H_I, d_I, FMT[idx_fmt]
             s.kI = _ptr(kI, row_bytes(idx_fmt, d_I) * B * N_cap, "kI")
             s.kI_scale = _ptr(kI_scale, B * N_cap * d_I // 32, "kI_scale", not mx)
+            # the fused selection's histogram kept zero-filled with the state (or NULL)
+            s.sel_hist = _ptr(sel_hist, 4 * SEL_HIST_BINS * B, "sel_hist", True)
         self.struct = s
         self.mode, self.B, self.c, self.H, self.k, self.H_I, self.d_I = mode, B, c, H, k, H_I, d_I
         self.io_fmt, self.idx_fmt = io_fmt, idx_fmt

@@ -169,7 +169,7 @@ class PrefillLayer:
 class DecodeLayer:
     """One CSA ("C") or HCA ("H") layer's decode state on the GPU."""
 
-    def __init__(self, cfg, d, device="cuda", sink=None, paged=None, split_rows=0):
+    def __init__(self, cfg, d, device="cuda", sink=None, paged=None, split_rows=0, sel_hist=True):
         self.cfg, self.device, self.d = cfg, device, d
         kind = d["kind"]
         self.mode = "csa" if kind == "C" else "hca"
@@ -199,13 +199,17 @@ class DecodeLayer:
         self.out = torch.empty((B, cfg.H, c), dtype=out_t, device=device)
         self.lse = torch.empty((B, cfg.H), dtype=torch.float32, device=device)
         self.idx = torch.empty((B, max(1, cfg.k)), dtype=torch.int32, device=device)
+        # CSA: the fused selection's histogram kept zero-filled with the state
+        # (sel_hist=False: the step clears one in its workspace instead)
+        self.sel_hist = (torch.zeros(B * ops.SEL_HIST_BINS, dtype=torch.int32, device=device)
+                         if sel_hist and self.mode == "csa" else None)
         self.state = ops.DecodeLayerState(
             mode=self.mode, m=m, B=B, c=c, H=cfg.H, n_win=cfg.n_win, N_cap=self.N_cap,
             io_fmt=cfg.io_dtype, kv_fmt=cfg.kv_dtype, tailC=self.tailC, tailZ=self.tailZ,
             ring=self.ring, cache=self.cache, n_tokens=self.n_tokens, P=self.P, sink=self.sink,
             tau=cfg.tau, eps=cfg.eps, k=cfg.k, H_I=cfg.H_I, d_I=cfg.d_I, idx_fmt=cfg.idx_dtype,
             kI=self.kI, kI_scale=self.kI_scale, rope_base=cfg.rope_base, pages=pages,
-            split_rows=split_rows)
+            split_rows=split_rows, sel_hist=self.sel_hist)
         self.workspace = _empty_bytes(self.state.workspace_size(), device)
 
     def logical_cache(self):

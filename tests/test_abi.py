@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.lca_version() == 4
+    assert L.lca_version() == 5
     for st in (0, -1, -2, -3, -4):
         assert L.lca_status_string(st)
     assert L.lca_status_string(7) == b"unknown status"

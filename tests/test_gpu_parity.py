@@ -935,9 +935,10 @@ def test_hca_decode_step_equals_append_then_attention(case):
 @pytest.mark.parametrize("case", ["fp8", "mxfp4_fp8kv_paged_rope", "random0", "random1"])
 def test_csa_decode_step_equals_separate_calls(case):
     """A CSA decode step with the fused selection runs its state append beside
-    the selection's finish pass (after a light launch that gives the indexer its
-    positions).  It must give the bits of the separate calls on a copy of the
-    same state: lca_state_append, lca_indexer_scores + lca_topk and
+    the selection's finish pass (the indexer takes its positions from the token
+    counts, the histogram is the layer's sel_hist).  It must give the bits of the
+    separate calls on a copy of the same state: lca_state_append,
+    lca_indexer_scores + lca_topk and
     lca_sparse_mqa, step after step over 40 steps (a block completes every 4):
     outputs, lse, selections, ring, tail rows, compressed cache, token counts."""
     if case.startswith("random"):
@@ -992,6 +993,40 @@ def test_csa_decode_step_equals_separate_calls(case):
     for name in ("ring", "tailC", "tailZ", "cache", "n_tokens"):
         assert np.array_equal(bits(getattr(fused, name)), bits(getattr(ref, name))), f"state {name}"
     assert np.array_equal(host(fused.n_tokens), d["n_tokens"] + 40)
+
+
+@pytest.mark.parametrize("idx_dtype", ["fp8", "mxfp4"])
+def test_csa_decode_sel_hist_equals_workspace_histogram(idx_dtype):
+    """The fused selection's histogram kept with the layer's state (sel_hist:
+    no launch before the indexer; the finish pass leaves it zero-filled) gives
+    the bits of the step that clears a workspace histogram first, step after
+    step, and sel_hist is all zeros after every step.  One sequence starts with
+    at most k visible entries (the indexer writes its selection directly)."""
+    cfg = CSA_DECODE_1M.with_(B=3, ctx=1 << 18, idx_dtype=idx_dtype)
+    d = gen.decode_inputs(cfg, extra_entries=12)
+    d["n_tokens"] = d["n_tokens"].copy()
+    d["n_tokens"][1] = 4 * cfg.k - 9  # vis <= k for the first steps, then k + 1, ...
+    say(f"sel_hist == workspace histogram: idx={idx_dtype}, N_cap {d['n_cap']}, "
+        f"n_tokens {d['n_tokens'].tolist()}")
+    a = pipeline.DecodeLayer(cfg, d, DEV)
+    b = pipeline.DecodeLayer(cfg, d, DEV, sel_hist=False)
+    assert a.sel_hist is not None and b.sel_hist is None
+    bits = lambda v: host(v.view(torch.int16) if v.dtype == torch.bfloat16 else v)  # noqa: E731
+    for st in range(24):
+        a.step()
+        b.step()
+        torch.cuda.synchronize()
+        assert not host(a.sel_hist).any(), f"step {st}: sel_hist left non-zero"
+        if st == 0:  # sequence 1 sees 1022 entries: all of them, then -1
+            want = np.concatenate([np.arange(cfg.k - 2), [-1, -1]])
+            assert np.array_equal(host(a.idx)[1], want), "step 0: short row's selection"
+        if st % 4 == 0 or st == 23:
+            assert np.array_equal(host(a.idx), host(b.idx)), f"step {st}: selection"
+            assert np.array_equal(bits(a.out), bits(b.out)), f"step {st}: out"
+            assert np.array_equal(bits(a.lse), bits(b.lse)), f"step {st}: lse"
+    for name in ("ring", "tailC", "tailZ", "cache", "n_tokens"):
+        assert np.array_equal(bits(getattr(a, name)), bits(getattr(b, name))), f"state {name}"
+    assert (host(a.idx)[1] >= 0).sum() == cfg.k  # 1027 visible by the last step
 
 
 def test_sink_logit():
