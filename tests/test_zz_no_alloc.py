@@ -55,16 +55,20 @@ def _case(name):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("first,second", [("csa_fused_b4_2e18", "csa_b2_2e14"),
-                                          ("hybrid_csa_b2_2e18", "hca_b3_2e14")])
-def test_static_scratch_step_equals_workspace_step(first, second):
+@pytest.mark.parametrize("first,second,sel_hist", [("csa_fused_b4_2e18", "csa_b2_2e14", True),
+                                                   ("csa_fused_b4_2e18", "csa_b2_2e14", False),
+                                                   ("hybrid_csa_b2_2e18", "hca_b3_2e14", True)])
+def test_static_scratch_step_equals_workspace_step(first, second, sel_hist):
+    """sel_hist=False: the fused selection's histogram lives in the scratch array
+    (cleared by each step's first launch) rather than in the layer's state."""
     for name in (first, second):           # the second call is smaller than the first
         cfg, d = _case(name)
-        ref = pipeline.DecodeLayer(cfg, d, DEV)
-        sta = pipeline.DecodeLayer(cfg, d, DEV)
+        ref = pipeline.DecodeLayer(cfg, d, DEV, sel_hist=sel_hist)
+        sta = pipeline.DecodeLayer(cfg, d, DEV, sel_hist=sel_hist)
         need = ref.state.workspace_size()
         assert 0 < need <= _lib.LCA_STATIC_SCRATCH_BYTES
-        say(f"no-alloc decode step {name}: B={cfg.B} N_cap={d['n_cap']} scratch {need >> 20} MiB")
+        say(f"no-alloc decode step {name}: B={cfg.B} N_cap={d['n_cap']} scratch {need >> 20} MiB, "
+            f"sel_hist {sel_hist}")
         for step in range(2):             # two steps each: the second sees the first's entries
             ref.step()
             _static_step(sta)
