@@ -887,44 +887,54 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   }
   __syncthreads();
   const int n_sel = min(sh_nsel, k);
-  // ascending output through a bitmap over the visible entries
+  // ascending output through a bitmap over the visible entries (2^19 per pass)
+  // and a count per 128-entry block (in the histogram's LDS, free by now): a
+  // selected entry's position is its block's exclusive prefix plus the set
+  // bits below it in its block's four words
   int done = 0;
+  uint32_t* bcnt = lh;
+  static_assert(32 * kFinBitmapWords / 128 <= kHistLdsWords, "block counts fit the histogram's LDS");
   for (int base = 0; base < vis; base += 32 * kFinBitmapWords) {
     const int nbits = min(32 * kFinBitmapWords, vis - base);
     const int nw = (nbits + 31) >> 5;
     const int nw4 = (nw + 3) & ~3;  // (<= kFinBitmapWords, a multiple of 4)
+    const int nb = (nbits + 127) >> 7;
     for (int w = 4 * tid; w < nw4; w += 4 * NT) *reinterpret_cast<uint4*>(bm + w) = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = tid; i < nb; i += NT) bcnt[i] = 0u;
     __syncthreads();
     for (int i = tid; i < n_sel; i += NT) {
       const int x = sel[i] - base;
-      if (x >= 0 && x < nbits) atomicOr(&bm[x >> 5], 1u << (x & 31));
+      if (x >= 0 && x < nbits) {
+        atomicOr(&bm[x >> 5], 1u << (x & 31));
+        atomicAdd(&bcnt[x >> 7], 1u);
+      }
     }
     __syncthreads();
-    // thread t: words [8t, 8t + 8) (two 16-byte LDS reads), more per thread
-    // beyond 8192 words
-    const int wpt = ((nw + NT - 1) / NT + 3) & ~3, w0 = tid * wpt;
+    // thread t: blocks [bpt t, bpt t + bpt), turned into exclusive prefixes
+    const int bpt = (nb + NT - 1) / NT;
     int c = 0;
-    for (int j = 0; j < wpt; j += 4) {
-      if (w0 + j < nw) {  // (the words up to nw4 are cleared)
-        const uint4 v = *reinterpret_cast<const uint4*>(bm + w0 + j);
-        c += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
-      }
+    for (int j = 0; j < bpt; ++j) {
+      const int bb = bpt * tid + j;
+      if (bb < nb) c += static_cast<int>(bcnt[bb]);
     }
     int tot;
     int at = done + block_excl_scan<kFinWaves>(c, &tot, scan_sh);
-    for (int j = 0; j < wpt; j += 4) {
-      if (w0 + j >= nw) break;
-      const uint4 v = *reinterpret_cast<const uint4*>(bm + w0 + j);
-      const uint32_t words[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t bits = words[q];
-        while (bits) {
-          const int bit = __ffs(bits) - 1;
-          if (at < k) out[at] = base + (w0 + j + q) * 32 + bit;
-          ++at;
-          bits &= bits - 1u;
-        }
+    for (int j = 0; j < bpt; ++j) {
+      const int bb = bpt * tid + j;
+      if (bb < nb) {
+        const int v = static_cast<int>(bcnt[bb]);
+        bcnt[bb] = static_cast<uint32_t>(at);
+        at += v;
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < n_sel; i += NT) {
+      const int x = sel[i] - base;
+      if (x >= 0 && x < nbits) {
+        const int wx = x >> 5;
+        int pos = static_cast<int>(bcnt[x >> 7]) + __popc(bm[wx] & ((1u << (x & 31)) - 1u));
+        for (int wy = wx & ~3; wy < wx; ++wy) pos += __popc(bm[wy]);
+        if (pos < k) out[pos] = base + x;
       }
     }
     done += tot;
