@@ -734,6 +734,7 @@ __global__ __launch_bounds__(64 * kD8Waves) void attn_decode_kernel(
   __shared__ float ps_s[4][kMH];  // per dim quarter: query sums of squares; then P row sums
   __shared__ float mx_s[4][kMH];  // per row quarter: the tile maximum of each head
   __shared__ __attribute__((aligned(16))) uint32_t vm_s[2][NW];
+  __shared__ int raise_s[2];  // tile t & 1: some head's row-quarter maximum passed the lazy bound
 
   const int split = blockIdx.x % n_splits;
   const long long row = blockIdx.x / n_splits;
@@ -934,6 +935,7 @@ __global__ __launch_bounds__(64 * kD8Waves) void attn_decode_kernel(
     ss += __shfl_xor(ss, 32, 64);
     if (g == 0) ps_s[kq][head] = ss;
     if (rope_step != 0.0 && w == 0 && lane < kRopeDims / 2) rope_s[lane] = rope_cs(sc.t, lane, rope_step);
+    if (tid == 0) raise_s[0] = 0;
     __syncthreads();
     const float r = rsqrt_hw(((ps_s[0][head] + ps_s[1][head]) + (ps_s[2][head] + ps_s[3][head])) /
                                  static_cast<float>(kMC) + eps);
@@ -1041,13 +1043,15 @@ __global__ __launch_bounds__(64 * kD8Waves) void attn_decode_kernel(
 #pragma unroll
     for (int i = 1; i < 8; ++i) tq = fmaxf(tq, s8[i]);
     tq = fmaxf(tq, __shfl_xor(tq, 32, 64));
-    if (g == 0) mx_s[kq][head] = tq;
-    __syncthreads();  // B2b: the row quarters' maxima
-    const float tmax = fmaxf(fmaxf(mx_s[0][head], mx_s[1][head]), fmaxf(mx_s[2][head], mx_s[3][head]));
-    const float m_new = (m_run == -INFINITY || tmax > m_run + kLazyMax) ? tmax : m_run;
-    const float alpha = (m_run == -INFINITY || m_new == m_run) ? 1.f : __expf(m_run - m_new);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    {
+    // The running maximum moves only when a head's tile maximum passes it by
+    // more than kLazyMax (always on a split's first tile with a visible row).
+    // The first tile exchanges the row quarters' maxima as the rule needs.
+    // Later tiles: each wave checks its own row quarter and raises a flag, P is
+    // written with the running maximum, and only a raised flag (seen by every
+    // wave after B3) costs the exchange and a second P pass -- the same maxima,
+    // P and sums as exchanging on every tile, one barrier fewer on the tiles
+    // that do not raise it.
+    auto write_p = [&](float m_use) {
       // P of this wave's 16 rows
       float psum = 0.f;
 #pragma unroll
@@ -1065,8 +1069,25 @@ __global__ __launch_bounds__(64 * kD8Waves) void attn_decode_kernel(
       }
       psum += __shfl_xor(psum, 32, 64);
       if (g == 0) ps_s[kq][head] = psum;
+    };
+    bool exchange = t == 0;
+    if (!exchange) {  // (t is the same for every thread)
+      if (__ballot(tq > m_run + kLazyMax) && lane == 0) raise_s[t & 1] = 1;
+      write_p(m_run == -INFINITY ? 0.f : m_run);
+      __syncthreads();  // B3: P and the row-quarter sums (and the flag)
+      exchange = raise_s[t & 1] != 0;
     }
-    __syncthreads();  // B3: P and the row-quarter sums
+    float m_new = m_run, alpha = 1.f;
+    if (exchange) {  // (the same for every thread)
+      if (g == 0) mx_s[kq][head] = tq;
+      __syncthreads();  // B3a: the row quarters' maxima
+      const float tmax = fmaxf(fmaxf(mx_s[0][head], mx_s[1][head]), fmaxf(mx_s[2][head], mx_s[3][head]));
+      m_new = (m_run == -INFINITY || tmax > m_run + kLazyMax) ? tmax : m_run;
+      alpha = (m_run == -INFINITY || m_new == m_run) ? 1.f : __expf(m_run - m_new);
+      write_p(m_new == -INFINITY ? 0.f : m_new);
+      __syncthreads();  // B3b: P and the sums again
+    }
+    if (tid == 0) raise_s[(t + 1) & 1] = 0;  // (read again after tile t + 1's B3 only)
     l_run = l_run * alpha + ((ps_s[0][head] + ps_s[1][head]) + (ps_s[2][head] + ps_s[3][head]));
     m_run = m_new;
     if (__ballot(alpha != 1.f)) {
