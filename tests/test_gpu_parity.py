@@ -640,6 +640,19 @@ def test_csa_decode_random_batches_fused_selection():
         _decode_parity(cfg, d, range(B))
 
 
+@pytest.mark.parametrize("k", [1, 7, 2048, 4096])
+def test_csa_decode_fused_selection_k_range(k):
+    """The fused selection at the ends of the interface's k range (1 .. 4096):
+    every row's selection bit-exact on the select stage (the oracle's top-k of
+    the GPU's own scores), with every clear winner and no clear loser, and the
+    outputs within tolerance (k + 128 attended rows)."""
+    cfg = CSA_DECODE_1M.with_(B=2, ctx=1 << 18, k=k, seed=40 + k % 13)
+    say(f"fused decode selection with k={k}")
+    d = gen.decode_inputs(cfg)
+    assert d["n_cap"] > 36864
+    _decode_parity(cfg, d, range(cfg.B))
+
+
 @pytest.mark.parametrize("kind", ["csa", "hca", "hybrid_csa"])
 def test_decode_rope(kind):
     """Decode steps with partial RoPE: the ring row and a completed entry turned
