@@ -587,10 +587,9 @@ constexpr int kMaxBlk = 8192;  // blocks per row (N_cap <= 1 Mi entries)
 constexpr int kFinWaves = 16;
 constexpr int kFinThreads = kFinWaves * kWave;
 constexpr int kFinSpec = 8;             // pairs per lane loaded with the counts
-constexpr int kFinCand = 8192;          // candidates held in LDS (else in global memory)
+constexpr int kFinCand = 4096;          // candidates held in LDS (else in global memory)
 constexpr int kFinBitmapWords = 16384;  // one output pass: 2^19 entries
 constexpr uint32_t kSkipKey = 0x80000000u;
-static_assert(kFinBitmapWords <= 2 * kFinCand, "the bitmap fits in the candidates' space");
 
 // exclusive block-wide prefix of one int per thread (NW full waves); *total is
 // the sum over the block.  Ends with a barrier, so scan_sh can be reused.
@@ -672,13 +671,16 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   constexpr int NT = kFinThreads;
   __shared__ uint32_t lh[kHistLdsWords];
   __shared__ int32_t sel[kMaxK];
-  __shared__ __attribute__((aligned(16))) uint32_t cand[2 * kFinCand];  // keys, indices; then the output bitmap
+  __shared__ __attribute__((aligned(16))) uint32_t cand[2 * kFinCand];  // keys, indices
+  // the output bitmap (one pass: 2^19 entries) and its counts per 128 entries
+  __shared__ __attribute__((aligned(16))) uint32_t obm[kFinBitmapWords];
+  __shared__ __attribute__((aligned(16))) uint32_t bcnt[kFinBitmapWords / 4];
   if (app.tokC && static_cast<long long>(blockIdx.x) >= rows) {
     constexpr int CPL = 512 / kWave;
-    static_assert(sizeof(float) * kAppendWaves * 3 * CPL * kWave <= sizeof(cand), "append scratch");
+    static_assert(sizeof(float) * kAppendWaves * 3 * CPL * kWave <= sizeof(obm), "append scratch");
     static_assert(kFinThreads >= kWave * kAppendWaves, "append waves");
     state_append_body<CPL, LCA_BF16, true>(static_cast<int>(blockIdx.x - rows), app.B,
-                                     reinterpret_cast<float (*)[3][CPL][kWave]>(cand), 1, app.m, 512,
+                                     reinterpret_cast<float (*)[3][CPL][kWave]>(obm), 1, app.m, 512,
                                      app.n_win, app.tokC, app.tokZ, app.tailC, app.tailZ, app.ring,
                                      app.kv_fmt, app.P, app.cache, app.N_cap, app.n_tokens, nullptr,
                                      nullptr, app.eps, app.rope_step, app.pg, nullptr, 0);
@@ -689,7 +691,6 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   __shared__ uint32_t rh[256];
   uint32_t* ck = cand;
   int32_t* ci = reinterpret_cast<int32_t*>(cand + kFinCand);
-  uint32_t* bm = cand;
   const long long row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -719,10 +720,25 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     const int capc = (ra + (sgc < rr ? 1 : 0)) * kSelBlock;
     pr[u] = em[rb + min(sl * kWave + lane, capc - 1)];
   }
+  // the output bitmap and block counts start cleared (while the loads above
+  // are in flight; ordered before their first use by the barrier below)
+  for (int w = 4 * tid; w < kFinBitmapWords; w += 4 * NT)
+    *reinterpret_cast<uint4*>(obm + w) = make_uint4(0u, 0u, 0u, 0u);
+  for (int w = 4 * tid; w < kFinBitmapWords / 4; w += 4 * NT)
+    *reinterpret_cast<uint4*>(bcnt + w) = make_uint4(0u, 0u, 0u, 0u);
   const int b = static_cast<int>(row / n_q);
   const int vis = visible_entries(q_pos[row], m, n_entries[b], N_cap);
   if (vis <= k) return;  // written by the indexer
   int32_t* out = sel_idx + row * k;
+  // one output pass: every selected entry sets its bitmap bit and counts in
+  // its 128-entry block as it is selected
+  const bool inl = vis <= 32 * kFinBitmapWords;
+  auto mark = [&](int32_t x) {
+    if (inl) {
+      atomicOr(&obm[x >> 5], 1u << (x & 31));
+      atomicAdd(&bcnt[x >> 7], 1u);
+    }
+  };
   const int n_part = min(wpr, (vis + kSelBlock - 1) / kSelBlock);
 #pragma unroll
   for (int u = 0; u < kHv; ++u) lh[hist_lds(hist_bin_of_slot(tid + u * NT))] = hv[u];
@@ -791,7 +807,10 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     for (int u = 0; u < kFinSpec; ++u) {
       if ((ms[u] >> lane) & 1) {
         const int q = bs + lanes_below(ms[u]);
-        if (q < k) sel[q] = static_cast<int32_t>(p[u].y);
+        if (q < k) {
+          sel[q] = static_cast<int32_t>(p[u].y);
+          mark(static_cast<int32_t>(p[u].y));
+        }
       }
       bs += __popcll(ms[u]);
       if ((mc[u] >> lane) & 1) {
@@ -882,34 +901,39 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     bs = __shfl(bs, 0, kWave);
     if (take) {
       const int q = bs + lanes_below(mt);
-      if (q < k) sel[q] = id;
+      if (q < k) {
+        sel[q] = id;
+        mark(id);
+      }
     }
   }
   __syncthreads();
   const int n_sel = min(sh_nsel, k);
   // ascending output through a bitmap over the visible entries (2^19 per pass)
-  // and a count per 128-entry block (in the histogram's LDS, free by now): a
-  // selected entry's position is its block's exclusive prefix plus the set
-  // bits below it in its block's four words
+  // and a count per 128-entry block: a selected entry's position is its
+  // block's exclusive prefix plus the set bits below it in its block's four
+  // words.  One pass (inl): bits and counts were set as entries were
+  // selected; more passes (rows over 2^19 entries) set them pass by pass.
   int done = 0;
-  uint32_t* bcnt = lh;
-  static_assert(32 * kFinBitmapWords / 128 <= kHistLdsWords, "block counts fit the histogram's LDS");
+  uint32_t* bm = obm;
   for (int base = 0; base < vis; base += 32 * kFinBitmapWords) {
     const int nbits = min(32 * kFinBitmapWords, vis - base);
     const int nw = (nbits + 31) >> 5;
     const int nw4 = (nw + 3) & ~3;  // (<= kFinBitmapWords, a multiple of 4)
     const int nb = (nbits + 127) >> 7;
-    for (int w = 4 * tid; w < nw4; w += 4 * NT) *reinterpret_cast<uint4*>(bm + w) = make_uint4(0u, 0u, 0u, 0u);
-    for (int i = tid; i < nb; i += NT) bcnt[i] = 0u;
-    __syncthreads();
-    for (int i = tid; i < n_sel; i += NT) {
-      const int x = sel[i] - base;
-      if (x >= 0 && x < nbits) {
-        atomicOr(&bm[x >> 5], 1u << (x & 31));
-        atomicAdd(&bcnt[x >> 7], 1u);
+    if (!inl) {  // (the same for every thread)
+      for (int w = 4 * tid; w < nw4; w += 4 * NT) *reinterpret_cast<uint4*>(bm + w) = make_uint4(0u, 0u, 0u, 0u);
+      for (int i = tid; i < nb; i += NT) bcnt[i] = 0u;
+      __syncthreads();
+      for (int i = tid; i < n_sel; i += NT) {
+        const int x = sel[i] - base;
+        if (x >= 0 && x < nbits) {
+          atomicOr(&bm[x >> 5], 1u << (x & 31));
+          atomicAdd(&bcnt[x >> 7], 1u);
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
     // thread t: blocks [bpt t, bpt t + bpt), turned into exclusive prefixes
     const int bpt = (nb + NT - 1) / NT;
     int c = 0;
