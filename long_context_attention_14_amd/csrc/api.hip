@@ -524,8 +524,9 @@ int decode_enqueue(const lca_decode_layer* L, const lca_decode_io* io, void* wor
                             lca::mqa_can_append(L->B, L->H, L->c, L->io_dtype, L->kv_dtype, L->N_cap,
                                                 L->n_win, L->split_rows);
   // CSA steps with the fused selection run the append as extra workgroups of the
-  // selection's finish launch, beside its one workgroup per row, and give the
-  // indexer its positions and cleared histogram from a light launch instead
+  // selection's finish launch, beside its one workgroup per row; the indexer
+  // takes its positions from n_tokens (sel_hist given) or from a light launch
+  // that also clears the workspace histogram
   const bool finish_append = fused && L->io_dtype == LCA_BF16 && L->c == 512;
   lca::StateAppend app{};
   lca::DecodeAppend ap{};

@@ -467,9 +467,10 @@ bool select_supported(int N_cap, int k);
 constexpr int kSelMaxWpr = 256;
 // A CSA decode step's state append run by the selection finish launch: one
 // more workgroup per sequence beside the finish's, on CUs the finish leaves
-// idle (the indexer before it got the query positions and the cleared
-// histogram from launch_decode_prep).  Same rows, entries and counts as
-// launch_state_append; bf16 io, c = 512, tail of 2m rows.
+// idle (the indexer before it took the query positions from n_tokens itself,
+// or from launch_decode_prep, which also cleared a workspace histogram).  Same
+// rows, entries and counts as launch_state_append; bf16 io, c = 512, tail of
+// 2m rows.
 struct StateAppend {
   int m, B, n_win, kv_fmt, N_cap;
   const uint8_t* tokC;  // [B, 512] bf16
